@@ -1,0 +1,313 @@
+"""Pins for the CPU oracle: what the pages and plain mathematics fix.
+
+Each test checks the oracle against something other than itself -- the
+smoothing identity and its balance property, rounding rules from IEEE 754,
+textbook integer matrix products, brute force on tiny inputs and hand-worked
+cases -- so that a dropped term, a wrong sign, a swapped operand or a wrong
+rounding step in the oracle fails at least one of them.
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import quasar_oracle as orc
+from w8a8_quantized_speculative_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bf16(a):
+    return synth.to_bf16_bits(np.asarray(a, np.float32))
+
+
+def f(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# ---------------------------------------------------------------- formats
+def test_bf16_rounding_matches_ieee_cases():
+    cases = json.load(open(os.path.join(GOLDEN, "rounding_ieee754.json")))["f32_to_bf16_hex"]
+    for src, want, _why in cases:
+        x = np.array([int(src, 16)], np.uint32).view(np.float32)
+        assert orc.f32_to_bf16(x)[0] == int(want, 16), (src, want)
+
+
+def test_bf16_rounding_matches_torch_on_random_and_tie_values():
+    g = np.random.default_rng(3)
+    u = g.integers(0, 2**32, 200000, dtype=np.uint64).astype(np.uint32)
+    u[:5000] = (u[:5000] & np.uint32(0xFFFF0000)) | np.uint32(0x8000)  # exact ties
+    x = u.view(np.float32)
+    x = x[np.isfinite(x) & (np.abs(x) < 3.0e38)]
+    want = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(orc.f32_to_bf16(x), want)
+
+
+def test_bf16_widening_is_exact():
+    bits = np.arange(0, 2**16, dtype=np.uint32).astype(np.uint16)
+    want = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    got = orc.bf16_to_f32(bits)
+    fin = np.isfinite(want)
+    assert np.array_equal(got[fin].view(np.uint32), want[fin].view(np.uint32))
+
+
+def test_reciprocal_is_correctly_rounded():
+    g = np.random.default_rng(4)
+    s = g.uniform(0.01, 100, 20000).astype(np.float32)
+    r = orc.rn32_reciprocal(s)
+    exact = 1.0 / s.astype(np.float64)
+    err = np.abs(r.astype(np.float64) - exact)
+    half_ulp = np.spacing(r).astype(np.float64) / 2
+    assert np.all(err <= half_ulp * (1 + 1e-12))
+
+
+# ---------------------------------------------------------------- P1 / P2: smoothing identity
+def test_smoothing_identity_holds_in_float64():
+    """(X diag s)(W diag s^-1)^T == X W^T: the same s enters reciprocally on the two sides."""
+    g = np.random.default_rng(5)
+    for M, N, K in [(3, 4, 16), (6, 16, 64), (1, 1, 16)]:
+        x = bf16(g.standard_normal((M, K)))
+        w = bf16(g.standard_normal((N, K)) * 0.02)
+        s = np.exp(g.uniform(np.log(0.1), np.log(10), K)).astype(np.float32)
+        xs = orc.smooth_activations(x, s).astype(np.float64)
+        ws = orc.smooth_weights(w, s).astype(np.float64)
+        exact = f(x).astype(np.float64) @ f(w).astype(np.float64).T
+        smooth = xs @ ws.T
+        # each term carries at most three binary32 roundings (x*s, 1/s, w*r)
+        bound = 4 * 2.0**-24 * (np.abs(f(x)).astype(np.float64) @ np.abs(f(w)).astype(np.float64).T)
+        assert np.all(np.abs(smooth - exact) <= bound + 1e-300)
+        # a wrong orientation (s on both sides) breaks the identity
+        wrong = xs @ (f(w).astype(np.float64) * s[None, :]).T
+        assert not np.allclose(wrong, exact, rtol=1e-3, atol=0)
+
+
+def test_smoothed_activation_is_one_binary32_rounding_of_x_times_s():
+    g = np.random.default_rng(6)
+    x = bf16(g.standard_normal((4, 256)) * 10)
+    s = g.uniform(0.05, 20, 256).astype(np.float32)
+    xs = orc.smooth_activations(x, s)
+    exact = f(x).astype(np.float64) * s.astype(np.float64)[None, :]
+    assert xs.dtype == np.float32
+    rel = np.abs(xs.astype(np.float64) - exact) / np.maximum(np.abs(exact), 1e-300)
+    assert np.all(rel <= 2.0**-24)
+    assert np.all(rel <= 1e-6)
+
+
+@pytest.mark.parametrize("literal", [False, True])
+def test_smoothing_balances_channel_maxima(literal):
+    """With s_j = sqrt(wmax_j / xmax_j) the smoothed maxima meet at sqrt(xmax_j wmax_j).
+
+    This pins the direction of s: activations are multiplied by s and weights
+    divided by it.  The literal reading of the calibration ratio fails it.
+    """
+    M, K, N = 6, 1024, 512
+    x = synth.activations(M, K, (0, 0), n_outliers=4, fixed_scale=50.0)
+    w = synth.weights(N, K, (0, 0))
+    xm, wm = synth.col_absmax_bf16(x), synth.col_absmax_bf16(w)
+    s = synth.smoothing_vector(xm, wm, literal=literal)
+    xs_max = np.abs(orc.smooth_activations(x, s)).max(axis=0).astype(np.float64)
+    ws_max = np.abs(orc.smooth_weights(w, s)).max(axis=0).astype(np.float64)
+    geo = np.sqrt(xm * wm)
+    ulp = np.spacing(geo.astype(np.float32)).astype(np.float64)
+    balanced = np.all(np.abs(xs_max - geo) <= 4 * ulp) and np.all(np.abs(ws_max - geo) <= 4 * ulp)
+    assert balanced != literal
+    if not literal:
+        # smoothing shrinks the activation outlier ratio (difficulty moves to weights)
+        raw = f(x).astype(np.float64)
+        ratio_raw = np.abs(raw).max() / np.median(np.abs(raw).max(axis=0))
+        ratio_s = xs_max.max() / np.median(xs_max)
+        assert ratio_s < ratio_raw / 4
+
+
+# ---------------------------------------------------------------- P3 / P4: quantizer
+def test_quantizer_invariants():
+    g = np.random.default_rng(7)
+    v = (g.standard_normal((50, 333)) * g.uniform(0.01, 100, (50, 1))).astype(np.float32)
+    v[3] = 0.0
+    q, sc = orc.quantize_rows(v)
+    assert q.dtype == np.int8 and sc.dtype == np.float32
+    assert q.min() >= -127 and q.max() <= 127
+    for r in range(v.shape[0]):
+        if not np.any(v[r]):
+            assert sc[r] == 0 and not np.any(q[r])
+            continue
+        assert np.max(np.abs(q[r].astype(np.int32))) == 127
+        err = np.abs(q[r].astype(np.float64) * np.float64(sc[r]) - v[r].astype(np.float64))
+        assert np.all(err <= np.float64(sc[r]) * (0.5 + 2.0**-14))
+        order = np.argsort(v[r], kind="stable")
+        assert np.all(np.diff(q[r][order].astype(np.int32)) >= 0)       # monotone
+        assert np.all(q[r].astype(np.int32) * np.sign(v[r]) >= 0)         # sign-consistent
+
+
+def test_quantizer_rounds_half_to_even_when_scale_is_one():
+    """absmax = 127 makes inv = 1 and scale = 1, so the code is round-half-even(v)."""
+    cases = json.load(open(os.path.join(GOLDEN, "rounding_ieee754.json")))["round_to_integer"]
+    vals = np.array([127.0] + [c[0] for c in cases], np.float32)
+    q, sc = orc.quantize_rows(vals[None, :])
+    assert sc[0] == 1.0
+    assert q[0, 0] == 127
+    assert list(q[0, 1:].astype(int)) == [c[1] for c in cases]
+
+
+def test_hand_worked_linear():
+    """Powers of two keep every step exact; values worked by hand.
+
+    x = [2, -4, 0.5, 8], s = [0.5, 2, 4, 0.25] -> xs = [1, -8, 2, 2], A = 8,
+    inv = 127/8 = 15.875, xs*inv = [15.875, -127, 31.75, 31.75] -> [16, -127, 32, 32].
+    w = [1, 0.5, -0.25, 2], 1/s = [2, 0.5, 0.25, 4] -> w' = [2, 0.25, -0.0625, 8],
+    A = 8 -> [31.75, 3.96875, -0.9921875, 127] -> [32, 4, -1, 127].
+    acc = 16*32 - 127*4 - 32 + 32*127 = 4036; Y = 4036 * (8/127)^2 = 16.0148.. -> bf16 16.0.
+    """
+    x = bf16([[2, -4, 0.5, 8]])
+    s = np.array([0.5, 2, 4, 0.25], np.float32)
+    w = bf16([[1, 0.5, -0.25, 2]])
+    qw, sw = orc.quantize_weights(w, s)
+    out = orc.w8a8_linear(x, s, qw, sw)
+    assert out["qx"].tolist() == [[16, -127, 32, 32]]
+    assert qw.tolist() == [[32, 4, -1, 127]]
+    assert out["sx"][0] == np.float32(8 / 127) and sw[0] == np.float32(8 / 127)
+    assert out["acc"].tolist() == [[4036]]
+    assert f(out["y"])[0, 0] == 16.0
+
+
+# ---------------------------------------------------------------- P5-P8: GEMM and dequant
+def test_textbook_case_unit_smoothing_integer_inputs():
+    """s = 1 and integer inputs with row absmax 127: codes are the inputs, scales 1,
+    acc is numpy's integer matrix product and Y is its bf16 rounding."""
+    g = np.random.default_rng(8)
+    M, N, K = 5, 37, 96
+    xi = g.integers(-127, 128, (M, K)); xi[:, 0] = 127
+    wi = g.integers(-127, 128, (N, K)); wi[:, 1] = -127
+    s = np.ones(K, np.float32)
+    qw, sw = orc.quantize_weights(bf16(wi), s)
+    out = orc.w8a8_linear(bf16(xi), s, qw, sw)
+    assert np.array_equal(out["qx"], xi.astype(np.int8))
+    assert np.array_equal(qw, wi.astype(np.int8))
+    assert np.all(out["sx"] == 1) and np.all(sw == 1)
+    want = xi.astype(np.int64) @ wi.astype(np.int64).T
+    assert np.array_equal(out["acc"], want)
+    assert np.array_equal(out["y"], torch.from_numpy(want.astype(np.float32)).to(torch.bfloat16)
+                          .view(torch.int16).numpy().view(np.uint16))
+
+
+def test_int_matmul_matches_brute_force_and_bound():
+    g = np.random.default_rng(9)
+    for M, N, K in [(1, 1, 1), (3, 5, 7), (6, 16, 64)]:
+        a = g.integers(-127, 128, (M, K)).astype(np.int8)
+        b = g.integers(-127, 128, (N, K)).astype(np.int8)
+        acc = orc.int_matmul(a, b)
+        for m in range(M):
+            for n in range(N):
+                assert acc[m, n] == sum(int(a[m, k]) * int(b[n, k]) for k in range(K))
+    # extreme codes at the largest K the library accepts stay exact and in int32
+    K = 65536
+    a = np.full((1, K), 127, np.int8)
+    b = np.full((2, K), -127, np.int8)
+    acc = orc.int_matmul(a, b)
+    assert acc[0, 0] == -K * 127 * 127 and abs(acc[0, 0]) < 2**31
+
+
+def test_split_k_partition_invariance():
+    g = np.random.default_rng(10)
+    a = g.integers(-127, 128, (6, 1000)).astype(np.int8)
+    b = g.integers(-127, 128, (9, 1000)).astype(np.int8)
+    full = orc.int_matmul(a, b)
+    cuts = [0, 64, 65, 500, 999, 1000]
+    parts = sum(orc.int_matmul(a[:, lo:hi], b[:, lo:hi]) for lo, hi in zip(cuts[:-1], cuts[1:]))
+    assert np.array_equal(parts, full)
+
+
+def test_dequant_within_one_bf16_ulp_of_exact_product():
+    g = np.random.default_rng(11)
+    acc = g.integers(-2**30, 2**30, (8, 300))
+    sx = g.uniform(1e-4, 1, 8).astype(np.float32)
+    sw = g.uniform(1e-5, 1e-2, 300).astype(np.float32)
+    y = f(orc.dequantize(acc, sx, sw)).astype(np.float64)
+    exact = orc.dequantize_f64(acc, sx, sw)
+    ulp = 2.0 ** (np.floor(np.log2(np.abs(exact))) - 7)
+    assert np.all(np.abs(y - exact) <= ulp)
+    # zero accumulators and zero scales give exact zeros
+    z = orc.dequantize(np.zeros((2, 3), np.int64), np.array([0.5, 0], np.float32),
+                       np.ones(3, np.float32))
+    assert not np.any(f(z))
+
+
+def test_dequant_rounds_in_the_stated_order():
+    """RN32(acc) first: 2^24 + 1 is not a binary32, it rounds to 2^24 before scaling."""
+    acc = np.array([[2**24 + 1]], np.int64)
+    y = orc.dequantize(acc, np.array([1.0], np.float32), np.array([1.0], np.float32))
+    assert f(y)[0, 0] == 2.0**24
+
+
+def test_all_zero_activation_row_gives_zero_outputs():
+    g = np.random.default_rng(12)
+    x = bf16(g.standard_normal((3, 64)))
+    x[1] = 0
+    w = bf16(g.standard_normal((10, 64)) * 0.02)
+    s = np.ones(64, np.float32)
+    qw, sw = orc.quantize_weights(w, s)
+    out = orc.w8a8_linear(x, s, qw, sw)
+    assert out["sx"][1] == 0 and not np.any(out["qx"][1]) and not np.any(f(out["y"][1]))
+
+
+def test_quantized_output_tracks_float_product():
+    """Diagnostic sanity: W8A8 output stays close to the float product on smoothed data."""
+    x, w, s = synth.linear_case(6, 1024, 256, (0, 1), n_outliers=4, fixed_scale=50.0)
+    qw, sw = orc.quantize_weights(w, s)
+    out = orc.w8a8_linear(x, s, qw, sw)
+    ref = f(x).astype(np.float64) @ f(w).astype(np.float64).T
+    err = np.abs(f(out["y"]).astype(np.float64) - ref)
+    assert np.median(err) / np.median(np.abs(ref)) < 0.1
+
+
+# ---------------------------------------------------------------- P10 / P11: greedy verify
+def test_argmax_lowest_index_on_ties():
+    v = np.zeros((4, 50), np.float32) - 1
+    v[0, [7, 3, 40]] = 5.0                       # tie -> 3
+    v[1, [0, 49]] = 2.0                          # tie -> 0
+    v[2, :] = 0.0; v[2, 10] = -0.0               # +0 and -0 compare equal -> 0
+    v[3, 49] = 1e-3                              # unique max at the end
+    got = orc.argmax_lowest(bf16(v))
+    assert got.tolist() == [3, 0, 0, 49]
+
+
+def test_argmax_matches_brute_force_on_random_bf16():
+    g = np.random.default_rng(13)
+    bits = bf16(np.round(g.standard_normal((20, 300)) * 4) / 4)   # many exact ties
+    vals = f(bits)
+    got = orc.argmax_lowest(bits)
+    for r in range(20):
+        best = 0
+        for j in range(1, 300):
+            if vals[r, j] > vals[r, best]:
+                best = j
+        assert got[r] == best
+
+
+def test_greedy_accept_all_match_patterns():
+    """Every one of the 2^k match patterns: L is the first mismatch, next = g_L."""
+    k, V = 5, 64
+    g_true = np.array([11, 22, 33, 44, 55, 60])   # distinct argmax per position
+    lg = np.zeros((1, k + 1, V), np.float32)
+    lg[0, np.arange(k + 1), g_true] = 10.0
+    bits = bf16(lg)
+    for pattern in itertools.product([0, 1], repeat=k):
+        draft = np.array([[g_true[i] if pattern[i] else (g_true[i] + 1) % V for i in range(k)]])
+        L, nxt, g = orc.greedy_accept(bits, draft)
+        want_L = next((i for i in range(k) if not pattern[i]), k)
+        assert L[0] == want_L and nxt[0] == g_true[want_L]
+        assert g[0].tolist() == g_true.tolist()
+    # k = 0: nothing to accept, the next token is the argmax of the only position
+    L, nxt, _ = orc.greedy_accept(bits[:, :1], np.zeros((1, 0), np.int32))
+    assert L[0] == 0 and nxt[0] == 11
+
+
+def test_greedy_out_of_range_draft_is_a_mismatch():
+    lg = np.zeros((1, 3, 8), np.float32); lg[0, :, 2] = 1
+    L, nxt, _ = orc.greedy_accept(bf16(lg), np.array([[2, 99]]))
+    assert L[0] == 1 and nxt[0] == 2
+    L, _, _ = orc.greedy_accept(bf16(lg), np.array([[-1, 2]]))
+    assert L[0] == 0
