@@ -1,0 +1,367 @@
+"""Benchmark: one W8A8 verify step of a Qwen3-8B-shaped target on one MI355X.
+
+A step is the whole hot path over one verify window of M = B * (1 + k) tokens:
+the 36 layers' four W8A8 SmoothQuant linears (QKV 4096->6144, O 4096->4096,
+gate_up 4096->24576, down 12288->4096), the W8A8 LM head 4096->151936 and the
+greedy accept over its logits.  Attention, norms, embeddings and the drafter
+are outside the measured path.
+
+Inputs are seeded and synthetic: random-init BF16 weights ~ N(0, 0.02)
+quantized offline, per-linear activations ~ N(0, 1) with 0.1 % outlier
+channels x U[30, 100], smoothing vectors calibrated on them, drafts equal to
+the verifier's argmax with probability 0.3 each.  All inputs are resident in
+HBM before the timed region; each step reads 7.6 GB of INT8 weights.
+
+Prints one JSON line.  `value` is the algorithmic HBM bytes of a step divided
+by the step time (GB/s); tokens/s = B * mean(accepted + 1) / step time.
+
+    python bench.py [--steps 20] [--warmup 3] [--m 6] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("W8A8 verify-linear HBM GB/s (% of peak) + verified tokens/s at M=6, "
+          "Qwen3-8B shape")
+PEAK_HBM_GBS = 8000.0
+PMC_FILE = os.path.join(ROOT, "profiles", "gemm_w8a8_qwen3_stack_m6_pmc.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "w8a8_quantized_speculative_amd", "csrc", f)
+                  for f in ("gemm.hip", "quant.hip", "quasar_device.hpp")]
+
+
+def algorithmic_bytes(M: int, N: int, K: int) -> int:
+    """INT8 weights + weight scales + smoothing vector + BF16 input + BF16 output."""
+    return N * K + 4 * N + 4 * K + 2 * M * K + 2 * M * N
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--m", type=int, default=6, help="verify-window rows: B*(1+k), k=5")
+    ap.add_argument("--layers", type=int, default=36)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bf16", action="store_true", help="skip the BF16-weight comparator")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
+    return ap.parse_args()
+
+
+class Stack:
+    """Resident W8A8 weights, activations and outputs of one verify step."""
+
+    def __init__(self, M: int, layers: int, keep_bf16: bool):
+        import numpy as np
+        import torch
+        from w8a8_quantized_speculative_amd import binding, synth
+
+        self.M, self.B, self.k = M, M // 6, 5
+        self.linears = []     # dicts: name, N, K, x, s, wq, sw, y, (w_bf16)
+        shapes = [(l, name, K, N) for l in range(layers) for (name, K, N) in synth.QWEN3_8B_LINEARS]
+        shapes.append((layers, "lm_head", 4096, synth.QWEN3_8B_VOCAB))
+        for li, (layer, name, K, N) in enumerate(shapes):
+            key = (4, layer, li % 4 if name != "lm_head" else 4)
+            x_bits = synth.activations(M, K, key)
+            g = torch.Generator(device="cuda")
+            g.manual_seed(1_000_003 * (layer + 1) + 7919 * (li % 5) + M)
+            w = (torch.randn((N, K), generator=g, device="cuda", dtype=torch.float32) * 0.02).to(torch.bfloat16)
+            w_colmax = w.abs().amax(dim=0).float().cpu().numpy().astype(np.float64)
+            s = synth.smoothing_vector(synth.col_absmax_bf16(x_bits), w_colmax)
+            s_d = torch.from_numpy(s).cuda()
+            wq, sw = binding.quasar_quantize_weights(w, s_d)
+            x = torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+            ent = dict(layer=layer, name=name, N=N, K=K, x=x, s=s_d, wq=wq, sw=sw,
+                       y=torch.empty((M, N), dtype=torch.bfloat16, device="cuda"))
+            if keep_bf16:
+                ent["w_bf16"] = w
+            else:
+                del w
+            self.linears.append(ent)
+        torch.cuda.synchronize()
+        self.ws = binding.new_workspace(max(binding.workspace_bytes_linear(M, e["N"], e["K"])
+                                            for e in self.linears))
+        V = synth.QWEN3_8B_VOCAB
+        self.V = V
+        self.logits = self.linears[-1]["y"].view(self.B, self.k + 1, V)
+        self.acc_ws = binding.new_workspace(binding.workspace_bytes_accept(self.B, self.k, V))
+        self.draft = torch.zeros((self.B, self.k), dtype=torch.int32, device="cuda")
+        self.accept_len = torch.zeros((self.B,), dtype=torch.int32, device="cuda")
+        self.next_token = torch.zeros((self.B,), dtype=torch.int32, device="cuda")
+        self.argmax = torch.zeros((self.B, self.k + 1), dtype=torch.int32, device="cuda")
+        self.bytes_linear = [algorithmic_bytes(M, e["N"], e["K"]) for e in self.linears]
+        self.bytes_step = sum(self.bytes_linear) + 2 * M * V + 4 * self.B * self.k + 8 * self.B
+
+    def linear_call(self, e):
+        from w8a8_quantized_speculative_amd import binding
+        binding.quasar_w8a8_linear(e["x"], e["s"], e["wq"], e["sw"], out=e["y"], workspace=self.ws)
+
+    def accept_call(self):
+        import ctypes
+        from w8a8_quantized_speculative_amd import binding
+        L = binding.lib()
+        st = L.quasar_verify_accept(
+            ctypes.c_void_p(self.logits.data_ptr()), ctypes.c_void_p(self.draft.data_ptr()),
+            self.B, self.k, self.V, 0.0, None, ctypes.c_void_p(self.accept_len.data_ptr()),
+            ctypes.c_void_p(self.next_token.data_ptr()), ctypes.c_void_p(self.argmax.data_ptr()),
+            None, ctypes.c_void_p(self.acc_ws.data_ptr()), self.acc_ws.numel(), binding._stream())
+        if st != 0:
+            raise binding.QuasarError("quasar_verify_accept", st)
+
+    def step(self):
+        for e in self.linears:
+            self.linear_call(e)
+        self.accept_call()
+
+
+def plant_drafts(stack, n_sets: int):
+    """Seeded draft sets planted against the verifier's argmax (p = 0.3 each)."""
+    import numpy as np
+    import torch
+    from w8a8_quantized_speculative_amd import synth
+    stack.step()
+    torch.cuda.synchronize()
+    g = stack.argmax.cpu().numpy()
+    sets = [synth.draft_tokens(g[:, :stack.k], stack.V, 0.3, (5, i)) for i in range(n_sets)]
+    return torch.from_numpy(np.stack(sets)).cuda()
+
+
+def time_graph_steps(stack, drafts, warmup: int, steps: int):
+    """Capture one step in a HIP graph; replay it `steps` times (new drafts each)."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        stack.step()  # prime everything once outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        stack.step()
+    lens = torch.zeros((warmup + steps, stack.B), dtype=torch.int32, device="cuda")
+    for i in range(warmup):
+        stack.draft.copy_(drafts[i])
+        graph.replay()
+        lens[i].copy_(stack.accept_len)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(warmup, warmup + steps):
+        stack.draft.copy_(drafts[i])
+        graph.replay()
+        lens[i].copy_(stack.accept_len)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    tau = (lens[warmup:].float() + 1).mean().item()
+    return ms, tau, graph
+
+
+def time_eager_calls(stack, steps: int):
+    """Eager steps with a HIP event pair around every linear call (same stream)."""
+    import torch
+    n = len(stack.linears)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n * steps)]
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for st in range(steps):
+        for i, e in enumerate(stack.linears):
+            a, b = ev[st * n + i]
+            a.record()
+            stack.linear_call(e)
+            b.record()
+        stack.accept_call()
+    t1.record()
+    torch.cuda.synchronize()
+    durs = [a.elapsed_time(b) for a, b in ev]
+    return t0.elapsed_time(t1) / steps, durs
+
+
+def time_bf16_comparator(stack, warmup: int, steps: int):
+    """Same linear shapes with BF16 weights through torch.matmul (hipBLASLt)."""
+    import torch
+    outs = [torch.empty((stack.M, e["N"]), dtype=torch.bfloat16, device="cuda") for e in stack.linears]
+
+    def step():
+        for e, o in zip(stack.linears, outs):
+            torch.matmul(e["x"], e["w_bf16"].t(), out=o)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    bf16_bytes = sum(2 * e["N"] * e["K"] + 2 * stack.M * e["K"] + 2 * stack.M * e["N"]
+                     for e in stack.linears)
+    return ms, bf16_bytes
+
+
+def cpu_oracle_baseline(M: int, budget_s: float):
+    """The CPU oracle as it stands on a bounded sample: the four linears of one
+    Qwen3-8B-shaped layer at the same M, repeated until the budget is spent."""
+    import numpy as np
+    from oracle import quasar_oracle as orc
+    from w8a8_quantized_speculative_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    cases = []
+    for li, (name, K, N) in enumerate(synth.QWEN3_8B_LINEARS):
+        key = (6, 0, li)
+        x = synth.activations(M, K, key)
+        w = synth.weights(N, K, key)
+        s = synth.smoothing_vector(synth.col_absmax_bf16(x), synth.col_absmax_bf16(w))
+        qw, sw = orc.quantize_weights(w, s)
+        del w
+        cases.append((x, s, qw, sw, algorithmic_bytes(M, N, K)))
+    done_bytes, reps = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        for x, s, qw, sw, nb in cases:
+            orc.w8a8_linear(x, s, qw, sw)
+            done_bytes += nb
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(done_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{reps} pass(es) over one Qwen3-8B-shaped layer's 4 W8A8 linears at M={M} "
+                      f"(weights pre-quantized, untimed), {dt:.1f} s",
+            "ms_per_layer": round(dt / reps * 1e3, 2)}
+
+
+def read_traffic(per_launch_bytes: float):
+    """HBM traffic per launch from committed rocprofv3 PMC runs, when they were
+    taken on the current kernel sources."""
+    try:
+        with open(PMC_FILE) as f:
+            pmc = json.load(f)
+    except (OSError, ValueError):
+        return None, None
+    if pmc.get("kernel_source_hash") != kernel_source_hash():
+        return None, "stale"
+    return pmc.get("traffic_bytes_per_launch"), pmc.get("note")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    if args.m % 6 != 0 or not 6 <= args.m <= 96:
+        sys.exit("--m must be B*(1+5) with 1 <= B <= 16")
+
+    print(f"[bench] building stack: M={args.m} layers={args.layers}", file=sys.stderr, flush=True)
+    stack = Stack(args.m, args.layers, keep_bf16=not args.no_bf16)
+    drafts = plant_drafts(stack, args.warmup + args.steps)
+    print("[bench] graph replay timing", file=sys.stderr, flush=True)
+    ms, tau, _graph = time_graph_steps(stack, drafts, args.warmup, args.steps)
+    print("[bench] eager per-call timing", file=sys.stderr, flush=True)
+    eager_ms, durs = time_eager_calls(stack, args.steps)
+
+    n = len(stack.linears)
+    per_launch_ms = sum(durs) / len(durs)
+    per_launch_bytes = sum(stack.bytes_linear) / n
+    achieved = per_launch_bytes / (per_launch_ms * 1e-3) / 1e9
+    traffic, traffic_note = read_traffic(per_launch_bytes)
+
+    value = stack.bytes_step / (ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": f"qwen3-8b-shaped W8A8 verify step, {args.layers} layers + LM head + greedy accept, M={args.m}",
+            "M": args.m, "B": stack.B, "k": stack.k, "layers": args.layers, "hidden": 4096,
+            "intermediate": 12288, "vocab": stack.V, "linears_per_step": n,
+            "weights_int8_gb": round(sum(e["N"] * e["K"] for e in stack.linears) / 1e9, 3),
+            "timing": "HIP-graph replay of the whole step, new drafts per step",
+        },
+        "hbm_frac_of_peak": round(value / PEAK_HBM_GBS, 4),
+        "verified_tokens_per_s": round(stack.B * tau / (ms * 1e-3), 1),
+        "mean_tau": round(tau, 4),
+        "bytes_per_step": stack.bytes_step,
+        "eager_ms_per_step": round(eager_ms, 4),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "kernel": "quasar_w8a8_linear (activation quantize + INT8 MFMA GEMM + dequant)",
+            "launch_avg_us": round(per_launch_ms * 1e3, 2),
+            "algorithmic_bytes_per_launch": int(per_launch_bytes),
+            "launches_per_step": n,
+            "traffic_note": traffic_note,
+        },
+    }
+    if not args.no_bf16:
+        print("[bench] bf16 comparator", file=sys.stderr, flush=True)
+        bms, bbytes = time_bf16_comparator(stack, args.warmup, args.steps)
+        lin_ms = ms  # the W8A8 step also includes the accept kernel (tiny)
+        out["bf16_comparator"] = {
+            "what": "same linear stack + LM head, BF16 weights, torch.matmul (hipBLASLt), HIP graph",
+            "ms_per_step": round(bms, 4),
+            "gbs": round(bbytes / (bms * 1e-3) / 1e9, 1),
+            "w8a8_speedup": round(bms / lin_ms, 3),
+        }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_oracle_baseline(args.m, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

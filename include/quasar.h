@@ -1,0 +1,187 @@
+/*
+ * quasar.h -- C ABI of libquasar.so, the MI355X (gfx950) hot path of Quasar's
+ * quantized verification: the W8A8 SmoothQuant linear that the target model
+ * runs over the 1+k draft tokens of a verify step, and the accept step that
+ * turns the verifier's logits into an accepted-prefix length.
+ *
+ * Source of the method: "Quasar: Quantized Self-Speculative Acceleration for
+ * Rapid Inference via Memory-Efficient Verification" (gist.science summaries of
+ * arXiv 2603.01399; pt, nl, zh and ko pages).  Citations below name the page
+ * and the numbered section of its technical summary.
+ *
+ * Conventions for every call
+ *   - Tensors are row-major and contiguous.  BF16 values travel as uint16_t bit
+ *     patterns.  Every tensor pointer is a DEVICE pointer (hipMalloc or torch
+ *     CUDA memory) unless stated otherwise; sizes are element counts.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
+ *     validate their arguments on the host, then enqueue kernels on `stream`
+ *     and return without synchronising.  Nothing is allocated and no state is
+ *     kept between calls: the caller owns every buffer, including workspaces
+ *     sized by the *_workspace_bytes queries.  Two calls may run concurrently
+ *     on different streams only with different workspaces.
+ *   - Argument errors are reported before any launch, as a status code; the
+ *     outputs are then untouched.  A launch failure returns QUASAR_ERR_HIP.
+ *     Device faults surface at the caller's next synchronisation.
+ *   - Inputs must be finite.  A non-finite input is outside the contract.
+ */
+#ifndef QUASAR_H
+#define QUASAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum quasar_status {
+  QUASAR_OK = 0,
+  QUASAR_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size or value  */
+  QUASAR_ERR_UNSUPPORTED = 2, /* valid in principle, outside this build's limits */
+  QUASAR_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required  */
+  QUASAR_ERR_HIP = 4          /* the HIP runtime rejected a launch           */
+} quasar_status;
+
+/* Limits of this build. */
+#define QUASAR_MAX_M 128      /* verify-window rows per linear call            */
+#define QUASAR_MAX_K 65536    /* keeps |acc| <= K*127^2 < 2^31                 */
+#define QUASAR_MAX_DRAFT 63   /* k, drafts per sequence in quasar_verify_accept */
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* quasar_status_string(quasar_status status);
+
+/* ABI version of this library (bumped on any signature change). */
+int quasar_abi_version(void);
+
+/*
+ * quasar_quantize_weights -- offline weight preparation.
+ *
+ * The weights are smoothed by diag(s)^-1 and quantized to INT8 once, then stay
+ * resident in GPU memory [Quasar, pt page §2 execution pipeline item 1; ko page
+ * §2 pipeline "offline"; zh page §2 item 2 gives Y = (W diag(s)^-1)(diag(s) X)].
+ * Quantization is symmetric and uniform [pt page §2], one scale per output
+ * channel:
+ *     r_k  = RN32(1 / s_k)
+ *     w'   = RN32(W[n,k] * r_k)                    (binary32)
+ *     A_n  = max_k |w'[n,k]|
+ *     w_scale[n] = RN32(A_n / 127)
+ *     wq[n,k]    = clamp(rint(RN32(w' * RN32(127 / A_n))), -127, 127)
+ * (rint = round half to even; a row with A_n == 0 gets codes 0 and scale 0.)
+ *
+ *   w        [N, K] bf16 bits, 16-byte aligned        (in)
+ *   s        [K]    float32, all > 0, 16-byte aligned (in)
+ *   N, K     N >= 0; 16 <= K <= QUASAR_MAX_K, K % 16 == 0
+ *   wq       [N, K] int8, 16-byte aligned             (out)
+ *   w_scale  [N]    float32, 4-byte aligned           (out)
+ * N == 0 is a no-op.  Errors: QUASAR_ERR_INVALID_ARG for null/misaligned
+ * pointers or bad sizes, QUASAR_ERR_UNSUPPORTED for K > QUASAR_MAX_K.
+ */
+quasar_status quasar_quantize_weights(const uint16_t* w, const float* s, int64_t N, int64_t K,
+                                      int8_t* wq, float* w_scale, void* stream);
+
+/*
+ * quasar_quantize_activations -- the online half of one linear, on its own.
+ *
+ * BF16 activations are smoothed by diag(s) and quantized dynamically, one
+ * scale per token [Quasar, pt page §2 execution pipeline item 2; nl page §2
+ * pipeline "online"]:
+ *     xs[m,k]    = RN32(X[m,k] * s_k)               (binary32, never rounded to BF16)
+ *     A_m        = max_k |xs[m,k]|
+ *     x_scale[m] = RN32(A_m / 127)
+ *     qx[m,k]    = clamp(rint(RN32(xs * RN32(127 / A_m))), -127, 127)
+ * This is exactly what quasar_w8a8_linear computes internally; it is exported
+ * for inspection and testing.
+ *
+ *   x        [M, K] bf16 bits, 16-byte aligned (in)
+ *   s        [K] float32, 16-byte aligned      (in)
+ *   M, K     0 <= M; 16 <= K <= QUASAR_MAX_K, K % 16 == 0
+ *   qx       [M, K] int8, 16-byte aligned      (out)
+ *   x_scale  [M] float32                       (out)
+ *   xs_out   [M, K] float32 or NULL, 16-byte aligned (out, optional)
+ */
+quasar_status quasar_quantize_activations(const uint16_t* x, const float* s, int64_t M, int64_t K,
+                                          int8_t* qx, float* x_scale, float* xs_out, void* stream);
+
+/* Workspace bytes quasar_w8a8_linear needs for this shape (0 allowed for an
+ * empty call).  Pure host function; deterministic in (M, N, K). */
+size_t quasar_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * quasar_w8a8_linear -- one W8A8 SmoothQuant linear over the verify window.
+ *
+ * Online smoothing and dynamic per-token INT8 quantization of the BF16 input
+ * (as quasar_quantize_activations), an INT8 x INT8 -> INT32 product on the
+ * matrix cores against the offline INT8 weights [Quasar, pt page §2 item 3;
+ * zh page §2 item 3], and dequantization back to BF16 [pt page §2 item 4;
+ * ko page §2 "dequantization"]:
+ *     acc[m,n] = sum_k qx[m,k] * wq[n,k]               (exact int32)
+ *     y[m,n]   = BF16(RN32(RN32(RN32(acc) * x_scale[m]) * w_scale[n]))
+ * No bias is added.
+ *
+ *   x        [M, K] bf16 bits, 16-byte aligned         (in)
+ *   s        [K] float32 smoothing vector, 16-byte aligned (in)
+ *   wq       [N, K] int8 from quasar_quantize_weights, 16-byte aligned (in)
+ *   w_scale  [N] float32 from quasar_quantize_weights  (in)
+ *   M, N, K  0 <= M <= QUASAR_MAX_M, N >= 0, 16 <= K <= QUASAR_MAX_K, K % 16 == 0
+ *   y        [M, N] bf16 bits, 4-byte aligned          (out)
+ *   acc_out  [M, N] int32 or NULL                      (out, optional: the exact
+ *            accumulators, for tests)
+ *   workspace, workspace_bytes: device scratch of at least
+ *            quasar_w8a8_workspace_bytes(M, N, K) bytes, 256-byte aligned; any
+ *            contents; overwritten.  May be NULL when that size is 0.
+ * M == 0 or N == 0 is a no-op.  Errors: INVALID_ARG, UNSUPPORTED (M or K
+ * beyond the limits), WORKSPACE, HIP.
+ */
+quasar_status quasar_w8a8_linear(const uint16_t* x, const float* s, const int8_t* wq,
+                                 const float* w_scale, int64_t M, int64_t N, int64_t K,
+                                 uint16_t* y, int32_t* acc_out, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* Workspace bytes quasar_verify_accept needs (pure host function). */
+size_t quasar_accept_workspace_bytes(int64_t B, int64_t k, int64_t V);
+
+/*
+ * quasar_verify_accept -- turn the verifier's BF16 logits into accepted drafts.
+ *
+ * The logits of the 1+k verify positions are dequantized BF16 values; they
+ * feed either greedy verification at T = 0 [Quasar, ko page §4 "Qwen3 (Greedy,
+ * T=0)"] or rejection sampling, which keeps the verifier's distribution exactly
+ * [pt page §2 item 4; zh page §2 "lossless rejection sampling"].
+ *
+ * Greedy (temperature == 0): g[b,i] = lowest index of the maximum of
+ *   logits[b,i,:] (compared as reals); accept_len[b] = largest L <= k with
+ *   draft[b,i] == g[b,i] for all i < L; next_token[b] = g[b, L].
+ * Rejection (temperature > 0): p_i = softmax(logits[b,i,:] / T); draft i is
+ *   accepted while uniforms[b,i] < p_i(draft[b,i]); at the first rejection L
+ *   the next token is drawn from p_L with the rejected draft removed and
+ *   renormalised, otherwise from p_k, by inverse CDF in index order with
+ *   uniforms[b,k]: the smallest j with cumsum_j > uniforms[b,k] * total.
+ *   Arithmetic is binary32 (expf of the device library).
+ * A draft id outside [0, V) is a mismatch (greedy) or has p = 0 (rejection).
+ *
+ *   logits      [B, k+1, V] bf16 bits (in)
+ *   draft       [B, k] int32 (in; may be NULL when k == 0)
+ *   B, k, V     B >= 0, 0 <= k <= QUASAR_MAX_DRAFT, V >= 1
+ *   temperature 0 (greedy) or finite > 0
+ *   uniforms    [B, k+1] float32 in [0, 1) (in; required when temperature > 0)
+ *   accept_len  [B] int32 (out)
+ *   next_token  [B] int32 (out)
+ *   argmax_out  [B, k+1] int32 or NULL (out, greedy only: g)
+ *   p_draft_out [B, k] float32 or NULL (out, rejection only: p_i(draft i))
+ *   workspace   at least quasar_accept_workspace_bytes(B, k, V) bytes,
+ *               256-byte aligned, any contents
+ * B == 0 is a no-op.  Errors: INVALID_ARG (including temperature < 0 or NaN),
+ * UNSUPPORTED (k too large), WORKSPACE, HIP.
+ */
+quasar_status quasar_verify_accept(const uint16_t* logits, const int32_t* draft, int64_t B,
+                                   int64_t k, int64_t V, float temperature,
+                                   const float* uniforms, int32_t* accept_len,
+                                   int32_t* next_token, int32_t* argmax_out,
+                                   float* p_draft_out, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QUASAR_H */

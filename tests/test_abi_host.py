@@ -1,0 +1,128 @@
+"""The C ABI on the host: the library loads, exports every symbol the header
+declares, and rejects bad arguments with the documented status before any
+launch (no GPU is touched by these calls)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from w8a8_quantized_speculative_amd import binding, build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "quasar.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = 0x10000  # a 256-byte aligned non-null address; never dereferenced on these paths
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(binding.LIB_PATH):
+        build.build()
+    return binding.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(quasar_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls_and_diagnostics():
+    names = declared_functions()
+    for must in ("quasar_quantize_weights", "quasar_w8a8_linear", "quasar_verify_accept",
+                 "quasar_quantize_activations", "quasar_w8a8_workspace_bytes",
+                 "quasar_accept_workspace_bytes", "quasar_status_string"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (quasar_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(L, name)
+    assert set(binding._SIGNATURES) == set(declared_functions())
+
+
+def test_status_strings(L):
+    for code in range(5):
+        assert L.quasar_status_string(code).decode().startswith("QUASAR_")
+    assert b"UNKNOWN" in L.quasar_status_string(99)
+    assert L.quasar_abi_version() == 1
+
+
+def test_workspace_queries_are_pure_host_and_monotone(L):
+    assert L.quasar_w8a8_workspace_bytes(0, 100, 64) == 0
+    assert L.quasar_w8a8_workspace_bytes(6, 0, 64) == 0
+    assert L.quasar_w8a8_workspace_bytes(6, 100, 60) == 0          # K % 16 != 0
+    for M, N, K in [(6, 6144, 4096), (96, 4096, 12288), (1, 16, 16), (128, 151936, 4096)]:
+        b = L.quasar_w8a8_workspace_bytes(M, N, K)
+        assert b >= M * K + 4 * M and b % 256 == 0
+    assert L.quasar_accept_workspace_bytes(0, 5, 10) == 0
+    assert L.quasar_accept_workspace_bytes(1, 5, 151936) > 0
+    assert L.quasar_accept_workspace_bytes(1, 64, 10) == 0          # k > QUASAR_MAX_DRAFT
+
+
+def linear(L, x=FAKE, s=FAKE, wq=FAKE, sw=FAKE, M=6, N=32, K=64, y=FAKE, acc=None, ws=FAKE,
+           wsb=1 << 20):
+    return L.quasar_w8a8_linear(x, s, wq, sw, M, N, K, y, acc, ws, wsb, None)
+
+
+def test_linear_argument_errors(L):
+    assert linear(L, M=-1) == INVALID
+    assert linear(L, K=0) == INVALID
+    assert linear(L, K=72) == INVALID                      # not a multiple of 16
+    assert linear(L, K=65536 + 16) == UNSUPPORTED
+    assert linear(L, M=129) == UNSUPPORTED
+    assert linear(L, M=0) == OK and linear(L, N=0) == OK   # empty calls are no-ops
+    assert linear(L, x=None) == INVALID
+    assert linear(L, y=None) == INVALID
+    assert linear(L, x=FAKE + 8) == INVALID                # not 16-byte aligned
+    assert linear(L, wq=FAKE + 4) == INVALID
+    assert linear(L, sw=FAKE + 2) == INVALID
+    assert linear(L, acc=FAKE + 2) == INVALID
+    need = L.quasar_w8a8_workspace_bytes(6, 32, 64)
+    assert need > 0
+    assert linear(L, ws=None) == WORKSPACE
+    assert linear(L, wsb=need - 1) == WORKSPACE
+    assert linear(L, ws=FAKE + 16) == WORKSPACE            # not 256-byte aligned
+
+
+def test_quantizer_argument_errors(L):
+    qw = L.quasar_quantize_weights
+    assert qw(FAKE, FAKE, -1, 64, FAKE, FAKE, None) == INVALID
+    assert qw(FAKE, FAKE, 10, 8, FAKE, FAKE, None) == INVALID
+    assert qw(FAKE, FAKE, 10, 1 << 17, FAKE, FAKE, None) == UNSUPPORTED
+    assert qw(FAKE, FAKE, 0, 64, None, None, None) == OK
+    assert qw(None, FAKE, 10, 64, FAKE, FAKE, None) == INVALID
+    assert qw(FAKE, FAKE + 4, 10, 64, FAKE, FAKE, None) == INVALID
+    qa = L.quasar_quantize_activations
+    assert qa(FAKE, FAKE, 3, 64, FAKE, None, None, None) == INVALID
+    assert qa(FAKE, FAKE, 3, 64, FAKE, FAKE, FAKE + 4, None) == INVALID
+    assert qa(FAKE, FAKE, 0, 64, None, None, None, None) == OK
+
+
+def accept(L, logits=FAKE, draft=FAKE, B=1, k=5, V=100, T=0.0, u=None, acc=FAKE, nxt=FAKE,
+           ws=FAKE, wsb=1 << 20):
+    return L.quasar_verify_accept(logits, draft, B, k, V, T, u, acc, nxt, None, None, ws, wsb, None)
+
+
+def test_accept_argument_errors(L):
+    assert accept(L, B=-1) == INVALID
+    assert accept(L, V=0) == INVALID
+    assert accept(L, k=-1) == INVALID
+    assert accept(L, k=64) == UNSUPPORTED
+    assert accept(L, T=-1.0) == INVALID
+    assert accept(L, T=float("nan")) == INVALID
+    assert accept(L, T=float("inf")) == INVALID
+    assert accept(L, T=1.0, u=None) == INVALID             # rejection needs uniforms
+    assert accept(L, draft=None) == INVALID                # k > 0 needs drafts
+    assert accept(L, B=0) == OK
+    assert accept(L, logits=None) == INVALID
+    assert accept(L, nxt=FAKE + 2) == INVALID
+    assert accept(L, ws=None) == WORKSPACE
+    assert accept(L, wsb=16) == WORKSPACE

@@ -1,0 +1,147 @@
+"""GPU parity of the W8A8 verify linear against the oracle.
+
+Small and ragged shapes are checked on every element; the Qwen3-8B-shaped
+linears and the LM head at full size (the shapes the benchmark times, in the
+same launch configuration) are checked on sampled output channels, which the
+oracle quantizes and multiplies row by row exactly as inside the full matrix.
+The bar: INT32 accumulators and INT8-derived BF16 outputs bit-identical to the
+oracle, and every output within 1 bf16 ulp of acc * sx * sw taken in float64.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import quasar_oracle as orc
+from w8a8_quantized_speculative_amd import binding, synth
+from tests.gpu_helpers import announce, dev, dev_bf16, host, host_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(x, s, w):
+    wq, sw = binding.quasar_quantize_weights(dev_bf16(w), dev(s))
+    xd = dev_bf16(x)
+    acc = torch.empty((x.shape[0], w.shape[0]), dtype=torch.int32, device="cuda")
+    y = binding.quasar_w8a8_linear(xd, dev(s), wq, sw, acc_out=acc)
+    torch.cuda.synchronize()
+    return host_bf16(y), host(acc), wq, sw
+
+
+def check_against_oracle(x, s, w, y, acc, cols=None):
+    if cols is None:
+        cols = np.arange(w.shape[0])
+        ref = orc.w8a8_linear_rows(x, s, w)
+    else:
+        ref = orc.w8a8_linear_rows(x, s, w[cols] if w.shape[0] > len(cols) else w)
+    assert np.array_equal(acc[:, cols], ref["acc"].astype(np.int32))
+    assert np.array_equal(y[:, cols], ref["y"])
+    exact = orc.dequantize_f64(ref["acc"], ref["sx"], ref["sw"])
+    got = orc.bf16_to_f32(y[:, cols]).astype(np.float64)
+    nz = exact != 0
+    ulp = np.zeros_like(exact)
+    ulp[nz] = 2.0 ** (np.floor(np.log2(np.abs(exact[nz]))) - 7)
+    assert np.all(np.abs(got - exact) <= ulp)
+    return ref
+
+
+def test_single_linear_1024_m6_every_element():
+    """One W8A8 linear, M = 6 (1 sequence x 1+5 drafts), K = N = 1024, four
+    outlier channels x50, W ~ N(0, 0.02)."""
+    announce("linear", 6, 1024, 1024)
+    x, w, s = synth.linear_case(6, 1024, 1024, (0, 0), n_outliers=4, fixed_scale=50.0)
+    y, acc, _, _ = run_gpu(x, s, w)
+    check_against_oracle(x, s, w, y, acc)
+
+
+RAGGED = [
+    (1, 16, 16), (6, 1000, 1040), (16, 257, 4096), (17, 300, 1024), (48, 513, 2048),
+    (96, 129, 4096), (128, 64, 512), (5, 33, 12288), (2, 7, 3072), (6, 4096, 192),
+]
+
+
+@pytest.mark.parametrize("M,N,K", RAGGED)
+@pytest.mark.parametrize("literal", [False, True])
+def test_linear_ragged_every_element(M, N, K, literal):
+    announce("linear", M, N, K, "literal" if literal else "smoothing")
+    x, w, s = synth.linear_case(M, K, N, (1, M, N, K), literal=literal)
+    y, acc, _, _ = run_gpu(x, s, w)
+    check_against_oracle(x, s, w, y, acc)
+
+
+def test_zero_rows_and_channels():
+    announce("linear_zero_rows", 6, 200, 256)
+    x, w, s = synth.linear_case(6, 256, 200, (2, 0))
+    x[3] = 0
+    w[17] = 0
+    y, acc, _, _ = run_gpu(x, s, w)
+    check_against_oracle(x, s, w, y, acc)
+    assert not np.any(acc[3]) and not np.any(orc.bf16_to_f32(y[3]))
+    assert not np.any(acc[:, 17])
+
+
+def test_empty_linear_is_a_noop():
+    announce("linear_empty")
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    s = torch.ones(64, dtype=torch.float32, device="cuda")
+    wq = torch.zeros((8, 64), dtype=torch.int8, device="cuda")
+    sw = torch.ones(8, dtype=torch.float32, device="cuda")
+    y = binding.quasar_w8a8_linear(x, s, wq, sw)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 8)
+
+
+@functools.lru_cache(maxsize=4)
+def qwen3_weights(N, K, key):
+    w = synth.weights(N, K, key)
+    return w, synth.col_absmax_bf16(w)
+
+
+def sampled_cols(N, n_random, seed):
+    g = np.random.default_rng(seed)
+    cols = np.concatenate([np.arange(min(32, N)), np.arange(max(0, N - 32), N),
+                           g.choice(N, size=min(n_random, N), replace=False)])
+    return np.unique(cols)
+
+
+@pytest.mark.parametrize("M", [6, 48, 96])
+@pytest.mark.parametrize("name,K,N", synth.QWEN3_8B_LINEARS)
+def test_qwen3_layer_linear_full_size_sampled(name, K, N, M):
+    """Qwen3-8B layer linears at the verify window (M = 6, 48, 96), 0.1 %
+    outlier channels x U[30, 100]; sampled channels checked exactly."""
+    announce("qwen3_linear", name, M, N, K)
+    key = (1, 0, ["qkv", "o", "gate_up", "down"].index(name))
+    x = synth.activations(M, K, key)
+    w, w_colmax = qwen3_weights(N, K, key)
+    s = synth.smoothing_vector(synth.col_absmax_bf16(x), w_colmax)
+    y, acc, wq, sw = run_gpu(x, s, w)
+    cols = sampled_cols(N, 256, N + M)
+    ref = check_against_oracle(x, s, w, y, acc, cols)
+    assert np.array_equal(host(wq[torch.from_numpy(cols).cuda()]), ref["qw"])
+
+
+def test_lm_head_full_size_sampled():
+    """W8A8 LM head 4096 -> 151936 at M = 6."""
+    K, N, M = 4096, synth.QWEN3_8B_VOCAB, 6
+    announce("lm_head", M, N, K)
+    key = (3, 0, 0)
+    x = synth.activations(M, K, key)
+    w = synth.weights(N, K, key)
+    s = synth.smoothing_vector(synth.col_absmax_bf16(x), synth.col_absmax_bf16(w))
+    y, acc, _, _ = run_gpu(x, s, w)
+    cols = sampled_cols(N, 512, 7)
+    check_against_oracle(x, s, w, y, acc, cols)
+
+
+def test_repeated_calls_are_bit_identical():
+    """Split-K partials and LDS reductions are integer sums: no run-to-run drift."""
+    announce("linear_determinism", 5, 33, 12288)
+    x, w, s = synth.linear_case(5, 12288, 33, (4, 0))
+    wq, sw = binding.quasar_quantize_weights(dev_bf16(w), dev(s))
+    xd, sd = dev_bf16(x), dev(s)
+    ws = binding.new_workspace(binding.workspace_bytes_linear(5, 33, 12288))
+    first = binding.quasar_w8a8_linear(xd, sd, wq, sw, workspace=ws).clone()
+    for _ in range(50):
+        again = binding.quasar_w8a8_linear(xd, sd, wq, sw, workspace=ws)
+        assert torch.equal(again.view(torch.int16), first.view(torch.int16))

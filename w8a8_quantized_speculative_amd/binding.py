@@ -1,0 +1,184 @@
+"""Thin Python binding over libquasar.so (include/quasar.h).
+
+Argument marshalling only: torch tensors are checked for dtype, shape and
+device, their device pointers and torch's current HIP stream are handed to the
+C ABI, and a non-OK status becomes an exception.  Every step of the verify path
+runs in the library's HIP kernels; there is no Python or CPU fallback -- if the
+library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads torch's HIP runtime first; libquasar binds to the same one
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libquasar.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "quasar.h")
+
+QUASAR_OK = 0
+QUASAR_ERR_INVALID_ARG = 1
+QUASAR_ERR_UNSUPPORTED = 2
+QUASAR_ERR_WORKSPACE = 3
+QUASAR_ERR_HIP = 4
+QUASAR_MAX_M = 128
+QUASAR_MAX_K = 65536
+QUASAR_MAX_DRAFT = 63
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_SIGNATURES = {
+    "quasar_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "quasar_abi_version": (ctypes.c_int, []),
+    "quasar_quantize_weights": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P]),
+    "quasar_quantize_activations": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P, _P]),
+    "quasar_w8a8_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "quasar_w8a8_linear": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _SZ, _P]),
+    "quasar_accept_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "quasar_verify_accept": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P,
+                                            _P, _P, _P, _SZ, _P]),
+}
+
+
+class QuasarError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {lib().quasar_status_string(status).decode()}")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build the HIP library first "
+                "(python -m w8a8_quantized_speculative_amd.build)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != QUASAR_OK:
+        raise QuasarError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, dtype, shape, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def workspace_bytes_linear(M: int, N: int, K: int) -> int:
+    return int(lib().quasar_w8a8_workspace_bytes(M, N, K))
+
+
+def workspace_bytes_accept(B: int, k: int, V: int) -> int:
+    return int(lib().quasar_accept_workspace_bytes(B, k, V))
+
+
+def new_workspace(nbytes: int, device=None) -> torch.Tensor:
+    """A device byte buffer for the *_workspace_bytes sizes (256-byte aligned)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8,
+                       device=device if device is not None else "cuda")
+
+
+# ------------------------------------------------------------------ calls
+def quasar_quantize_weights(w: torch.Tensor, s: torch.Tensor):
+    """W [N, K] bf16, s [K] f32 -> (wq int8 [N, K], w_scale f32 [N])."""
+    N, K = w.shape
+    _need(w, torch.bfloat16, (N, K), "w")
+    _need(s, torch.float32, (K,), "s")
+    wq = torch.empty((N, K), dtype=torch.int8, device=w.device)
+    sw = torch.empty((N,), dtype=torch.float32, device=w.device)
+    _check("quasar_quantize_weights", lib().quasar_quantize_weights(
+        _ptr(w), _ptr(s), N, K, _ptr(wq), _ptr(sw), _stream()))
+    return wq, sw
+
+
+def quasar_quantize_activations(x: torch.Tensor, s: torch.Tensor, want_xs: bool = False):
+    """X [M, K] bf16 -> (qx int8 [M, K], x_scale f32 [M], xs f32 [M, K] or None)."""
+    M, K = x.shape
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(s, torch.float32, (K,), "s")
+    qx = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    sx = torch.empty((M,), dtype=torch.float32, device=x.device)
+    xs = torch.empty((M, K), dtype=torch.float32, device=x.device) if want_xs else None
+    _check("quasar_quantize_activations", lib().quasar_quantize_activations(
+        _ptr(x), _ptr(s), M, K, _ptr(qx), _ptr(sx), _ptr(xs), _stream()))
+    return qx, sx, xs
+
+
+def quasar_w8a8_linear(x: torch.Tensor, s: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,
+                       out: torch.Tensor | None = None, acc_out: torch.Tensor | None = None,
+                       workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Y [M, N] bf16 = dequant(quant(X diag(s)) @ wq^T) for X [M, K] bf16."""
+    M, K = x.shape
+    N = wq.shape[0]
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(s, torch.float32, (K,), "s")
+    _need(wq, torch.int8, (N, K), "wq")
+    _need(w_scale, torch.float32, (N,), "w_scale")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(out, torch.bfloat16, (M, N), "out")
+    if acc_out is not None:
+        _need(acc_out, torch.int32, (M, N), "acc_out")
+    need = workspace_bytes_linear(M, N, K)
+    if workspace is None and need > 0:
+        workspace = new_workspace(need, x.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("quasar_w8a8_linear", lib().quasar_w8a8_linear(
+        _ptr(x), _ptr(s), _ptr(wq), _ptr(w_scale), M, N, K, _ptr(out), _ptr(acc_out),
+        _ptr(workspace), nbytes, _stream()))
+    return out
+
+
+def quasar_verify_accept(logits: torch.Tensor, draft: torch.Tensor | None, temperature: float = 0.0,
+                         uniforms: torch.Tensor | None = None, want_argmax: bool = False,
+                         want_p_draft: bool = False, workspace: torch.Tensor | None = None):
+    """logits [B, k+1, V] bf16, draft [B, k] int32 ->
+    (accept_len int32 [B], next_token int32 [B], argmax [B, k+1] or None, p_draft [B, k] or None)."""
+    B, kp1, V = logits.shape
+    k = kp1 - 1
+    _need(logits, torch.bfloat16, (B, kp1, V), "logits")
+    if k > 0 or draft is not None:
+        _need(draft, torch.int32, (B, k), "draft")
+    if uniforms is not None:
+        _need(uniforms, torch.float32, (B, kp1), "uniforms")
+    dev = logits.device
+    acc_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    nxt = torch.empty((B,), dtype=torch.int32, device=dev)
+    g = torch.empty((B, kp1), dtype=torch.int32, device=dev) if want_argmax else None
+    pd = torch.empty((B, k), dtype=torch.float32, device=dev) if want_p_draft else None
+    if workspace is None:
+        workspace = new_workspace(workspace_bytes_accept(B, k, V), dev)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("quasar_verify_accept", lib().quasar_verify_accept(
+        _ptr(logits), _ptr(draft), B, k, V, float(temperature), _ptr(uniforms), _ptr(acc_len),
+        _ptr(nxt), _ptr(g), _ptr(pd), _ptr(workspace), nbytes, _stream()))
+    return acc_len, nxt, g, pd

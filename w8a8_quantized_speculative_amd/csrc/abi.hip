@@ -1,0 +1,134 @@
+// extern "C" entry points of libquasar.so (declared in include/quasar.h).
+// Every call validates its arguments on the host first, so an argument error
+// never reaches the GPU, then enqueues its kernels on the caller's stream.
+#include "../../include/quasar.h"
+#include "quasar_internal.hpp"
+
+#include <math.h>
+
+using namespace quasar;
+
+namespace {
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline quasar_status hip_status(hipError_t e) { return e == hipSuccess ? QUASAR_OK : QUASAR_ERR_HIP; }
+
+// Shape rules shared by the quantizers and the linear.
+quasar_status check_k(int64_t K) {
+  if (K <= 0 || K % 16 != 0) return QUASAR_ERR_INVALID_ARG;
+  if (K > QUASAR_MAX_K) return QUASAR_ERR_UNSUPPORTED;
+  return QUASAR_OK;
+}
+
+constexpr int64_t kMaxRowsPerCall = (int64_t)1 << 30;
+
+}  // namespace
+
+extern "C" {
+
+const char* quasar_status_string(quasar_status status) {
+  switch (status) {
+    case QUASAR_OK: return "QUASAR_OK";
+    case QUASAR_ERR_INVALID_ARG: return "QUASAR_ERR_INVALID_ARG: null or misaligned pointer, or bad size/value";
+    case QUASAR_ERR_UNSUPPORTED: return "QUASAR_ERR_UNSUPPORTED: size outside this build's limits";
+    case QUASAR_ERR_WORKSPACE: return "QUASAR_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case QUASAR_ERR_HIP: return "QUASAR_ERR_HIP: the HIP runtime rejected a launch";
+  }
+  return "QUASAR_ERR_UNKNOWN";
+}
+
+int quasar_abi_version(void) { return 1; }
+
+quasar_status quasar_quantize_weights(const uint16_t* w, const float* s, int64_t N, int64_t K,
+                                      int8_t* wq, float* w_scale, void* stream) {
+  if (N < 0) return QUASAR_ERR_INVALID_ARG;
+  quasar_status st = check_k(K);
+  if (st != QUASAR_OK) return st;
+  if (N > kMaxRowsPerCall) return QUASAR_ERR_UNSUPPORTED;
+  if (N == 0) return QUASAR_OK;
+  if (!w || !s || !wq || !w_scale) return QUASAR_ERR_INVALID_ARG;
+  if (!aligned(w, 16) || !aligned(s, 16) || !aligned(wq, 16) || !aligned(w_scale, 4))
+    return QUASAR_ERR_INVALID_ARG;
+  return hip_status(launch_quantize_weights(w, s, N, K, wq, w_scale, (hipStream_t)stream));
+}
+
+quasar_status quasar_quantize_activations(const uint16_t* x, const float* s, int64_t M, int64_t K,
+                                          int8_t* qx, float* x_scale, float* xs_out, void* stream) {
+  if (M < 0) return QUASAR_ERR_INVALID_ARG;
+  quasar_status st = check_k(K);
+  if (st != QUASAR_OK) return st;
+  if (M > kMaxRowsPerCall) return QUASAR_ERR_UNSUPPORTED;
+  if (M == 0) return QUASAR_OK;
+  if (!x || !s || !qx || !x_scale) return QUASAR_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(s, 16) || !aligned(qx, 16) || !aligned(x_scale, 4) ||
+      (xs_out && !aligned(xs_out, 16)))
+    return QUASAR_ERR_INVALID_ARG;
+  return hip_status(launch_quantize_activations(x, s, M, K, qx, x_scale, xs_out, nullptr, 0,
+                                                (hipStream_t)stream));
+}
+
+size_t quasar_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || check_k(K) != QUASAR_OK || M > QUASAR_MAX_M || N > kMaxRowsPerCall)
+    return 0;
+  return plan_linear(M, N, K).bytes;
+}
+
+quasar_status quasar_w8a8_linear(const uint16_t* x, const float* s, const int8_t* wq,
+                                 const float* w_scale, int64_t M, int64_t N, int64_t K,
+                                 uint16_t* y, int32_t* acc_out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (M < 0 || N < 0) return QUASAR_ERR_INVALID_ARG;
+  quasar_status st = check_k(K);
+  if (st != QUASAR_OK) return st;
+  if (M > QUASAR_MAX_M || N > kMaxRowsPerCall) return QUASAR_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return QUASAR_OK;
+  if (!x || !s || !wq || !w_scale || !y) return QUASAR_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(s, 16) || !aligned(wq, 16) || !aligned(w_scale, 4) ||
+      !aligned(y, 2) || (acc_out && !aligned(acc_out, 4)))
+    return QUASAR_ERR_INVALID_ARG;
+  const LinearPlan p = plan_linear(M, N, K);
+  if (p.bytes > 0 && (!workspace || workspace_bytes < p.bytes || !aligned(workspace, kWsAlign)))
+    return QUASAR_ERR_WORKSPACE;
+  hipStream_t hs = (hipStream_t)stream;
+  char* ws = static_cast<char*>(workspace);
+  int8_t* qx = reinterpret_cast<int8_t*>(ws + p.off_qx);
+  float* sx = reinterpret_cast<float*>(ws + p.off_sx);
+  int32_t* counters = p.splits > 1 ? reinterpret_cast<int32_t*>(ws + p.off_counters) : nullptr;
+  int32_t* partials = p.splits > 1 ? reinterpret_cast<int32_t*>(ws + p.off_partials) : nullptr;
+  hipError_t e = launch_quantize_activations(x, s, M, K, qx, sx, nullptr, counters,
+                                             counters ? p.tiles : 0, hs);
+  if (e != hipSuccess) return QUASAR_ERR_HIP;
+  return hip_status(launch_gemm(p, qx, sx, wq, w_scale, y, acc_out, counters, partials, hs));
+}
+
+size_t quasar_accept_workspace_bytes(int64_t B, int64_t k, int64_t V) {
+  if (B <= 0 || k < 0 || k > QUASAR_MAX_DRAFT || V <= 0 || V > kMaxRowsPerCall) return 0;
+  return plan_accept(B, k, V).bytes;
+}
+
+quasar_status quasar_verify_accept(const uint16_t* logits, const int32_t* draft, int64_t B,
+                                   int64_t k, int64_t V, float temperature,
+                                   const float* uniforms, int32_t* accept_len,
+                                   int32_t* next_token, int32_t* argmax_out,
+                                   float* p_draft_out, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (B < 0 || k < 0 || V <= 0) return QUASAR_ERR_INVALID_ARG;
+  if (!(temperature >= 0.0f) || isinf(temperature)) return QUASAR_ERR_INVALID_ARG;  // NaN too
+  if (k > QUASAR_MAX_DRAFT || V > kMaxRowsPerCall || B > kMaxRowsPerCall) return QUASAR_ERR_UNSUPPORTED;
+  if (B == 0) return QUASAR_OK;
+  if (!logits || !accept_len || !next_token) return QUASAR_ERR_INVALID_ARG;
+  if (k > 0 && !draft) return QUASAR_ERR_INVALID_ARG;
+  if (temperature > 0.0f && !uniforms) return QUASAR_ERR_INVALID_ARG;
+  if (!aligned(logits, 2) || (draft && !aligned(draft, 4)) || !aligned(accept_len, 4) ||
+      !aligned(next_token, 4) || (uniforms && !aligned(uniforms, 4)) ||
+      (argmax_out && !aligned(argmax_out, 4)) || (p_draft_out && !aligned(p_draft_out, 4)))
+    return QUASAR_ERR_INVALID_ARG;
+  const AcceptPlan p = plan_accept(B, k, V);
+  if (!workspace || workspace_bytes < p.bytes || !aligned(workspace, kWsAlign))
+    return QUASAR_ERR_WORKSPACE;
+  return hip_status(launch_accept(p, logits, draft, temperature, uniforms, accept_len, next_token,
+                                  argmax_out, p_draft_out, workspace, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,322 @@
+// Verification decision over the dequantized BF16 logits of the 1+k verify
+// positions: greedy at T = 0 [Quasar, ko page §4, "Qwen3 (Greedy, T=0)"] or
+// rejection sampling that keeps the verifier's distribution [pt page §2 item 4;
+// zh page §2 "lossless rejection sampling"].
+//
+// Pass 1 (grid chunks x rows): every workgroup scans one chunk of one logits
+// row and writes the chunk's (max, lowest argmax) and, for T > 0, the chunk's
+// sum of exp((l - max_chunk) / T).
+// Pass 2 (grid B): one workgroup per sequence merges the chunk partials of its
+// k+1 rows, takes the accept decisions in draft order and picks the next token
+// (argmax, or an inverse-CDF draw over the residual in index order).
+#include <float.h>
+#include <limits.h>
+
+#include "quasar_device.hpp"
+#include "quasar_internal.hpp"
+
+namespace quasar {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunk = 2048;  // logits per pass-1 workgroup (8 per thread)
+constexpr int kMaxRows = 64;  // k + 1 <= 64
+
+struct ArgMax {
+  float v;
+  int idx;
+};
+
+// larger value wins; equal values (as reals, so -0 == +0) go to the lower index
+__device__ __forceinline__ ArgMax better(ArgMax a, ArgMax b) {
+  if (b.v > a.v || (b.v == a.v && b.idx < a.idx)) return b;
+  return a;
+}
+
+__device__ __forceinline__ ArgMax wave_argmax(ArgMax a) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    ArgMax o;
+    o.v = __shfl_xor(a.v, off, kWave);
+    o.idx = __shfl_xor(a.idx, off, kWave);
+    a = better(a, o);
+  }
+  return a;
+}
+
+__device__ ArgMax block_argmax(ArgMax a, float* sv, int* si) {
+  a = wave_argmax(a);
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  if (lane == 0) {
+    sv[wave] = a.v;
+    si[wave] = a.idx;
+  }
+  __syncthreads();
+  ArgMax r{sv[0], si[0]};
+  for (int w = 1; w < kThreads / kWave; ++w) r = better(r, ArgMax{sv[w], si[w]});
+  __syncthreads();
+  return r;
+}
+
+__device__ float block_sum(float v, float* sv) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  if (lane == 0) sv[wave] = v;
+  __syncthreads();
+  float r = 0.0f;
+  for (int w = 0; w < kThreads / kWave; ++w) r += sv[w];
+  __syncthreads();
+  return r;
+}
+
+template <bool kSample>
+__global__ __launch_bounds__(kThreads) void accept_partial_kernel(
+    const uint16_t* __restrict__ logits, int64_t V, int chunks, float inv_t,
+    float* __restrict__ pmax, int32_t* __restrict__ pidx, float* __restrict__ psum) {
+  __shared__ float sv[kThreads / kWave];
+  __shared__ int si[kThreads / kWave];
+  const int c = blockIdx.x;
+  const int64_t row = blockIdx.y;
+  const uint16_t* lr = logits + row * V;
+  const int64_t j0 = (int64_t)c * kChunk;
+  const int64_t j1 = min(V, j0 + kChunk);
+  ArgMax best{-FLT_MAX, INT_MAX};
+  float vals[kChunk / kThreads];
+#pragma unroll
+  for (int e = 0; e < kChunk / kThreads; ++e) {
+    const int64_t j = j0 + (int64_t)e * kThreads + threadIdx.x;
+    vals[e] = -FLT_MAX;
+    if (j < j1) {
+      vals[e] = bf16_to_f32(lr[j]);
+      best = better(best, ArgMax{vals[e], (int)j});
+    }
+  }
+  best = block_argmax(best, sv, si);
+  const int64_t slot = row * chunks + c;
+  if (kSample) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int e = 0; e < kChunk / kThreads; ++e) {
+      const int64_t j = j0 + (int64_t)e * kThreads + threadIdx.x;
+      if (j < j1) sum += expf((vals[e] - best.v) * inv_t);
+    }
+    sum = block_sum(sum, sv);
+    if (threadIdx.x == 0) psum[slot] = sum;
+  }
+  if (threadIdx.x == 0) {
+    pmax[slot] = best.v;
+    pidx[slot] = best.idx;
+  }
+}
+
+template <bool kSample>
+__global__ __launch_bounds__(kThreads) void accept_finalize_kernel(
+    const uint16_t* __restrict__ logits, const int32_t* __restrict__ draft, int k, int64_t V,
+    int chunks, float inv_t, const float* __restrict__ uniforms, const float* __restrict__ pmax,
+    const int32_t* __restrict__ pidx, const float* __restrict__ psum,
+    int32_t* __restrict__ accept_len, int32_t* __restrict__ next_token,
+    int32_t* __restrict__ argmax_out, float* __restrict__ p_draft_out) {
+  __shared__ float sv[kThreads / kWave];
+  __shared__ int si[kThreads / kWave];
+  __shared__ int s_g[kMaxRows];
+  __shared__ float s_m[kMaxRows], s_z[kMaxRows];
+  __shared__ int s_L, s_cstar, s_found, s_fallback;
+  __shared__ float s_before, s_target;
+  __shared__ float s_run[kThreads];
+
+  const int b = blockIdx.x;
+  const int kp1 = k + 1;
+  // ---- merge the chunk partials of every verify position
+  for (int i = 0; i < kp1; ++i) {
+    const int64_t row = (int64_t)b * kp1 + i;
+    ArgMax a{-FLT_MAX, INT_MAX};
+    for (int c = threadIdx.x; c < chunks; c += kThreads)
+      a = better(a, ArgMax{pmax[row * chunks + c], pidx[row * chunks + c]});
+    a = block_argmax(a, sv, si);
+    float z = 0.0f;
+    if (kSample) {
+      float part = 0.0f;
+      for (int c = threadIdx.x; c < chunks; c += kThreads)
+        part += psum[row * chunks + c] * expf((pmax[row * chunks + c] - a.v) * inv_t);
+      z = block_sum(part, sv);
+    }
+    if (threadIdx.x == 0) {
+      s_g[i] = a.idx;
+      s_m[i] = a.v;
+      s_z[i] = z;
+    }
+  }
+  __syncthreads();
+
+  if (!kSample) {
+    if (threadIdx.x == 0) {
+      int L = 0;
+      while (L < k && draft[(int64_t)b * k + L] == s_g[L]) ++L;
+      accept_len[b] = L;
+      next_token[b] = s_g[L];
+    }
+    if (argmax_out)
+      for (int i = threadIdx.x; i < kp1; i += kThreads) argmax_out[(int64_t)b * kp1 + i] = s_g[i];
+    return;
+  }
+
+  // ---- rejection: accept decisions in draft order
+  if (threadIdx.x == 0) {
+    int L = k;
+    for (int i = 0; i < k; ++i) {
+      const int d = draft[(int64_t)b * k + i];
+      float p = 0.0f;
+      if (d >= 0 && d < V) {
+        const float l = bf16_to_f32(logits[((int64_t)b * kp1 + i) * V + d]);
+        p = expf((l - s_m[i]) * inv_t) / s_z[i];
+      }
+      if (p_draft_out) p_draft_out[(int64_t)b * k + i] = p;
+      if (L == k && !(uniforms[(int64_t)b * kp1 + i] < p)) L = i;
+    }
+    s_L = L;
+  }
+  __syncthreads();
+  const int L = s_L;
+  const int64_t row = (int64_t)b * kp1 + L;
+  const float m = s_m[L];
+  int d_ex = -1;  // token removed from the residual (the rejected draft)
+  if (L < k) {
+    const int d = draft[(int64_t)b * k + L];
+    if (d >= 0 && d < V) d_ex = d;
+  }
+  const int c_ex = d_ex >= 0 ? d_ex / kChunk : -1;
+  // the chunk holding the rejected draft: its sum without that token
+  float ex_sum = 0.0f;
+  if (c_ex >= 0) {
+    float part = 0.0f;
+    const int64_t j1 = min(V, (int64_t)(c_ex + 1) * kChunk);
+    for (int64_t j = (int64_t)c_ex * kChunk + threadIdx.x; j < j1; j += kThreads)
+      if (j != d_ex) part += expf((bf16_to_f32(logits[row * V + j]) - m) * inv_t);
+    ex_sum = block_sum(part, sv);
+  }
+  // ---- walk the chunk sums (rescaled to the row max) to the chunk holding the draw
+  if (threadIdx.x == 0) {
+    float total = 0.0f;
+    for (int c = 0; c < chunks; ++c)
+      total += (c == c_ex) ? ex_sum : psum[row * chunks + c] * expf((pmax[row * chunks + c] - m) * inv_t);
+    const float target = uniforms[(int64_t)b * kp1 + k] * total;
+    float cum = 0.0f;
+    int cstar = -1, last_nz = 0;
+    float before = 0.0f;
+    for (int c = 0; c < chunks; ++c) {
+      const float sc = (c == c_ex) ? ex_sum : psum[row * chunks + c] * expf((pmax[row * chunks + c] - m) * inv_t);
+      if (sc > 0.0f) last_nz = c;
+      if (cstar < 0 && cum + sc > target) {
+        cstar = c;
+        before = cum;
+      }
+      cum += sc;
+    }
+    if (cstar < 0) {  // rounding pushed the target past the last chunk
+      cstar = last_nz;
+      before = cum;
+    }
+    s_cstar = cstar;
+    s_before = before;
+    s_target = target;
+    s_found = INT_MAX;
+    s_fallback = -1;
+  }
+  __syncthreads();
+  // ---- scan the chosen chunk in index order: thread t owns 8 consecutive logits
+  const int64_t base = (int64_t)s_cstar * kChunk;
+  constexpr int E = kChunk / kThreads;
+  float rr[E];
+  float run = 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int64_t j = base + (int64_t)threadIdx.x * E + e;
+    rr[e] = 0.0f;
+    if (j < V && j != d_ex) rr[e] = expf((bf16_to_f32(logits[row * V + j]) - m) * inv_t);
+    run += rr[e];
+  }
+  s_run[threadIdx.x] = run;
+  __syncthreads();
+  if (threadIdx.x == 0) {  // exclusive prefix of the per-thread sums
+    float acc = 0.0f;
+    for (int t = 0; t < kThreads; ++t) {
+      const float v = s_run[t];
+      s_run[t] = acc;
+      acc += v;
+    }
+  }
+  __syncthreads();
+  float cum = s_before + s_run[threadIdx.x];
+  const float target = s_target;
+  int found = INT_MAX, nz = -1;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = (int)(base + threadIdx.x * E + e);
+    cum += rr[e];
+    if (rr[e] > 0.0f) {
+      nz = j;
+      if (found == INT_MAX && cum > target) found = j;
+    }
+  }
+  if (found != INT_MAX) atomicMin(&s_found, found);
+  if (nz >= 0) atomicMax(&s_fallback, nz);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    accept_len[b] = L;
+    next_token[b] = s_found != INT_MAX ? s_found : (s_fallback >= 0 ? s_fallback : 0);
+  }
+}
+
+}  // namespace
+
+AcceptPlan plan_accept(int64_t B, int64_t k, int64_t V) {
+  AcceptPlan p{};
+  p.B = B;
+  p.k = k;
+  p.V = V;
+  p.rows = B * (k + 1);
+  p.chunk_len = kChunk;
+  p.chunks = (int)((V + kChunk - 1) / kChunk);
+  const size_t slots = (size_t)p.rows * p.chunks;
+  size_t off = 0;
+  p.off_max = off;
+  off = align_up(off + slots * sizeof(float), kWsAlign);
+  p.off_idx = off;
+  off = align_up(off + slots * sizeof(int32_t), kWsAlign);
+  p.off_sum = off;
+  off = align_up(off + slots * sizeof(float), kWsAlign);
+  p.bytes = B == 0 ? 0 : off;
+  return p;
+}
+
+hipError_t launch_accept(const AcceptPlan& p, const uint16_t* logits, const int32_t* draft,
+                         float temperature, const float* uniforms, int32_t* accept_len,
+                         int32_t* next_token, int32_t* argmax_out, float* p_draft_out,
+                         void* workspace, hipStream_t st) {
+  char* ws = static_cast<char*>(workspace);
+  float* pmax = reinterpret_cast<float*>(ws + p.off_max);
+  int32_t* pidx = reinterpret_cast<int32_t*>(ws + p.off_idx);
+  float* psum = reinterpret_cast<float*>(ws + p.off_sum);
+  const bool sample = temperature > 0.0f;
+  const float inv_t = sample ? 1.0f / temperature : 0.0f;
+  const dim3 g1((unsigned)p.chunks, (unsigned)p.rows), blk(kThreads);
+  if (sample)
+    accept_partial_kernel<true><<<g1, blk, 0, st>>>(logits, p.V, p.chunks, inv_t, pmax, pidx, psum);
+  else
+    accept_partial_kernel<false><<<g1, blk, 0, st>>>(logits, p.V, p.chunks, inv_t, pmax, pidx, psum);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 g2((unsigned)p.B);
+  if (sample)
+    accept_finalize_kernel<true><<<g2, blk, 0, st>>>(logits, draft, (int)p.k, p.V, p.chunks, inv_t,
+                                                     uniforms, pmax, pidx, psum, accept_len,
+                                                     next_token, argmax_out, p_draft_out);
+  else
+    accept_finalize_kernel<false><<<g2, blk, 0, st>>>(logits, draft, (int)p.k, p.V, p.chunks, inv_t,
+                                                      uniforms, pmax, pidx, psum, accept_len,
+                                                      next_token, argmax_out, p_draft_out);
+  return hipGetLastError();
+}
+
+}  // namespace quasar

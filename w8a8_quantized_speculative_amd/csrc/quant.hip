@@ -1,0 +1,159 @@
+// Row quantizers: offline weight preparation and the online activation step.
+//
+// Weights: w' = RN32(W * RN32(1/s)), one INT8 scale per output channel
+// [Quasar, pt page §2 execution pipeline item 1; zh page §2 item 2].
+// Activations: xs = RN32(X * s), one dynamic INT8 scale per token
+// [pt page §2 item 2; nl page §2 pipeline "online"].
+// Both are symmetric uniform quantizers [pt page §2].
+//
+// One workgroup of 256 threads owns one row.  Each thread handles 8-element
+// units (16 bytes of bf16, 32 bytes of s); the row absmax is a wavefront
+// max-reduction followed by a 4-entry LDS reduction.
+#include "quasar_device.hpp"
+#include "quasar_internal.hpp"
+
+namespace quasar {
+namespace {
+
+constexpr int kRowThreads = 256;
+
+template <bool kWeights>
+__device__ __forceinline__ void load_unit(const uint16_t* __restrict__ row,
+                                          const float* __restrict__ s, int64_t q, float v[8]) {
+  const uint4 xv = *reinterpret_cast<const uint4*>(row + q * 8);
+  const float4 s0 = *reinterpret_cast<const float4*>(s + q * 8);
+  const float4 s1 = *reinterpret_cast<const float4*>(s + q * 8 + 4);
+  float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t bits = (e & 1) ? (xw[e >> 1] >> 16) : (xw[e >> 1] & 0xffffu);
+    // weights are divided by s (as a multiply by the rounded reciprocal),
+    // activations multiplied by s
+    const float f = kWeights ? 1.0f / sv[e] : sv[e];
+    v[e] = bf16_to_f32(bits) * f;
+  }
+}
+
+__device__ __forceinline__ void store_unit(int8_t* __restrict__ codes, float* __restrict__ xs_out,
+                                           int64_t q, const float v[8], float inv) {
+  int c[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c[e] = quant_code(v[e], inv);
+  uint2 pk;
+  pk.x = pack4_i8(c[0], c[1], c[2], c[3]);
+  pk.y = pack4_i8(c[4], c[5], c[6], c[7]);
+  *reinterpret_cast<uint2*>(codes + q * 8) = pk;
+  if (xs_out) {
+    *reinterpret_cast<float4*>(xs_out + q * 8) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(xs_out + q * 8 + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+// Register-resident variant: the smoothed row stays in registers between the
+// absmax pass and the quantize pass (K <= kUPT * 256 * 8).
+template <bool kWeights, int kUPT>
+__global__ __launch_bounds__(kRowThreads) void quantize_rows_reg_kernel(
+    const uint16_t* __restrict__ src, const float* __restrict__ s, int64_t K,
+    int8_t* __restrict__ codes, float* __restrict__ scales, float* __restrict__ xs_out,
+    int32_t* __restrict__ zero_ptr, int64_t zero_words) {
+  __shared__ float red[kRowThreads / kWave];
+  const int64_t row = blockIdx.x;
+  const int64_t units = K / 8;
+  const uint16_t* xr = src + row * K;
+  float v[kUPT][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kUPT; ++u) {
+    const int64_t q = (int64_t)u * kRowThreads + threadIdx.x;
+    if (q < units) {
+      load_unit<kWeights>(xr, s, q, v[u]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[u][e]));
+    }
+  }
+  amax = block_max(amax, red);
+  const QParams qp = row_qparams(amax);
+  int8_t* cr = codes + row * K;
+  float* xo = xs_out ? xs_out + row * K : nullptr;
+#pragma unroll
+  for (int u = 0; u < kUPT; ++u) {
+    const int64_t q = (int64_t)u * kRowThreads + threadIdx.x;
+    if (q < units) store_unit(cr, xo, q, v[u], qp.inv);
+  }
+  if (threadIdx.x == 0) scales[row] = qp.scale;
+  if (zero_ptr) {
+    for (int64_t i = (int64_t)blockIdx.x * kRowThreads + threadIdx.x; i < zero_words;
+         i += (int64_t)gridDim.x * kRowThreads)
+      zero_ptr[i] = 0;
+  }
+}
+
+// Streaming variant for long rows: two passes over global memory.
+template <bool kWeights>
+__global__ __launch_bounds__(kRowThreads) void quantize_rows_stream_kernel(
+    const uint16_t* __restrict__ src, const float* __restrict__ s, int64_t K,
+    int8_t* __restrict__ codes, float* __restrict__ scales, float* __restrict__ xs_out,
+    int32_t* __restrict__ zero_ptr, int64_t zero_words) {
+  __shared__ float red[kRowThreads / kWave];
+  const int64_t row = blockIdx.x;
+  const int64_t units = K / 8;
+  const uint16_t* xr = src + row * K;
+  float amax = 0.0f;
+  for (int64_t q = threadIdx.x; q < units; q += kRowThreads) {
+    float v[8];
+    load_unit<kWeights>(xr, s, q, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+  }
+  amax = block_max(amax, red);
+  const QParams qp = row_qparams(amax);
+  int8_t* cr = codes + row * K;
+  float* xo = xs_out ? xs_out + row * K : nullptr;
+  for (int64_t q = threadIdx.x; q < units; q += kRowThreads) {
+    float v[8];
+    load_unit<kWeights>(xr, s, q, v);
+    store_unit(cr, xo, q, v, qp.inv);
+  }
+  if (threadIdx.x == 0) scales[row] = qp.scale;
+  if (zero_ptr) {
+    for (int64_t i = (int64_t)blockIdx.x * kRowThreads + threadIdx.x; i < zero_words;
+         i += (int64_t)gridDim.x * kRowThreads)
+      zero_ptr[i] = 0;
+  }
+}
+
+template <bool kWeights>
+hipError_t launch_rows(const uint16_t* src, const float* s, int64_t rows, int64_t K, int8_t* codes,
+                       float* scales, float* xs_out, int32_t* zero_ptr, int64_t zero_words,
+                       hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  const dim3 grid((unsigned)rows), block(kRowThreads);
+  const int64_t upt = (K / 8 + kRowThreads - 1) / kRowThreads;
+  if (upt <= 1)
+    quantize_rows_reg_kernel<kWeights, 1><<<grid, block, 0, st>>>(src, s, K, codes, scales, xs_out, zero_ptr, zero_words);
+  else if (upt <= 2)
+    quantize_rows_reg_kernel<kWeights, 2><<<grid, block, 0, st>>>(src, s, K, codes, scales, xs_out, zero_ptr, zero_words);
+  else if (upt <= 4)
+    quantize_rows_reg_kernel<kWeights, 4><<<grid, block, 0, st>>>(src, s, K, codes, scales, xs_out, zero_ptr, zero_words);
+  else if (upt <= 8)
+    quantize_rows_reg_kernel<kWeights, 8><<<grid, block, 0, st>>>(src, s, K, codes, scales, xs_out, zero_ptr, zero_words);
+  else
+    quantize_rows_stream_kernel<kWeights><<<grid, block, 0, st>>>(src, s, K, codes, scales, xs_out, zero_ptr, zero_words);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_weights(const uint16_t* w, const float* s, int64_t N, int64_t K,
+                                   int8_t* wq, float* w_scale, hipStream_t st) {
+  return launch_rows<true>(w, s, N, K, wq, w_scale, nullptr, nullptr, 0, st);
+}
+
+hipError_t launch_quantize_activations(const uint16_t* x, const float* s, int64_t M, int64_t K,
+                                       int8_t* qx, float* sx, float* xs_out, int32_t* zero_ptr,
+                                       int64_t zero_words, hipStream_t st) {
+  return launch_rows<false>(x, s, M, K, qx, sx, xs_out, zero_ptr, zero_words, st);
+}
+
+}  // namespace quasar

@@ -1,0 +1,91 @@
+// Device-side building blocks shared by the gfx950 kernels of libquasar.
+//
+// Everything here is binary32 arithmetic with one rounding per operation: the
+// library is compiled with -ffp-contract=off, so no multiply-add is fused, and
+// fp32 division is the correctly rounded default of hipcc.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace quasar {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;    // CDNA wavefront width
+constexpr float kQmax = 127.0f;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Round-to-nearest-even binary32 -> bfloat16 for finite inputs (the path never
+// produces NaN): add 0x7FFF plus the lowest kept bit, drop the low half.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Per-row symmetric INT8 parameters from a row's absolute maximum:
+// scale = RN32(A / 127), inv = RN32(127 / A); an all-zero row gets 0 and 0.
+struct QParams {
+  float scale;
+  float inv;
+};
+
+__device__ __forceinline__ QParams row_qparams(float amax) {
+  QParams p;
+  if (amax == 0.0f) {
+    p.scale = 0.0f;
+    p.inv = 0.0f;
+  } else {
+    p.scale = amax / kQmax;
+    p.inv = kQmax / amax;
+  }
+  return p;
+}
+
+// code = clamp(rint(RN32(v * inv)), -127, 127), rint rounding half to even.
+__device__ __forceinline__ int quant_code(float v, float inv) {
+  float r = __builtin_rintf(v * inv);
+  r = fminf(fmaxf(r, -kQmax), kQmax);
+  return (int)r;
+}
+
+__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
+  return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
+         ((uint32_t)(d & 0xff) << 24);
+}
+
+// Max over the 64 lanes of a wavefront (all lanes receive the result).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+// Block-wide max; `red` must hold blockDim.x / 64 floats.  Ends with a barrier
+// so `red` can be reused afterwards.
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int nw = blockDim.x / kWave;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int w = 1; w < nw; ++w) r = fmaxf(r, red[w]);
+  __syncthreads();
+  return r;
+}
+
+// v_mfma_i32_16x16x64_i8: D[16x16] += A[16x64] * B[64x16], int8 operands, int32
+// accumulators.  Lane l holds row (l % 16) of A and column (l % 16) of B, each as
+// 16 consecutive K positions of one K-group (l / 16); the hardware pairs the
+// same byte of A and B, so any consistent K order gives the same dot products.
+// Result: lane l, register r holds D[4 * (l / 16) + r][l % 16].
+__device__ __forceinline__ v4i mfma_i8_16x16x64(v4i a, v4i b, v4i c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+}  // namespace quasar
