@@ -54,6 +54,13 @@ const char* quasar_status_string(quasar_status status);
 int quasar_abi_version(void);
 
 /*
+ * quasar_packed_weight_bytes -- size of the INT8 weight buffer of an N x K
+ * linear: ceil(N/16) * ceil(K/64) * 1024 bytes.  Pure host function; 0 for
+ * invalid sizes.
+ */
+size_t quasar_packed_weight_bytes(int64_t N, int64_t K);
+
+/*
  * quasar_quantize_weights -- offline weight preparation.
  *
  * The weights are smoothed by diag(s)^-1 and quantized to INT8 once, then stay
@@ -65,14 +72,21 @@ int quasar_abi_version(void);
  *     w'   = RN32(W[n,k] * r_k)                    (binary32)
  *     A_n  = max_k |w'[n,k]|
  *     w_scale[n] = RN32(A_n / 127)
- *     wq[n,k]    = clamp(rint(RN32(w' * RN32(127 / A_n))), -127, 127)
+ *     code[n,k]  = clamp(rint(RN32(w' * RN32(127 / A_n))), -127, 127)
  * (rint = round half to even; a row with A_n == 0 gets codes 0 and scale 0.)
  *
- *   w        [N, K] bf16 bits, 16-byte aligned        (in)
- *   s        [K]    float32, all > 0, 16-byte aligned (in)
+ * Layout of wq (tile-packed, the order the MFMA A operand is loaded in):
+ * code[n,k] is stored at byte
+ *     ((t * C + c) * 64 + g * 16 + r) * 16 + b
+ * with t = n / 16, r = n % 16, c = k / 64, g = (k % 64) / 16, b = k % 16 and
+ * C = ceil(K / 64): each 16-row x 64-column block is one contiguous 1 KB.
+ * Rows n >= N of the last block and columns k >= K of the last chunk hold 0.
+ *
+ *   w        [N, K] bf16 bits, row-major, 16-byte aligned (in)
+ *   s        [K]    float32, all > 0, 16-byte aligned     (in)
  *   N, K     N >= 0; 16 <= K <= QUASAR_MAX_K, K % 16 == 0
- *   wq       [N, K] int8, 16-byte aligned             (out)
- *   w_scale  [N]    float32, 4-byte aligned           (out)
+ *   wq       quasar_packed_weight_bytes(N, K) bytes, 16-byte aligned (out)
+ *   w_scale  [N]    float32, 4-byte aligned               (out)
  * N == 0 is a no-op.  Errors: QUASAR_ERR_INVALID_ARG for null/misaligned
  * pointers or bad sizes, QUASAR_ERR_UNSUPPORTED for K > QUASAR_MAX_K.
  */
@@ -102,8 +116,11 @@ quasar_status quasar_quantize_weights(const uint16_t* w, const float* s, int64_t
 quasar_status quasar_quantize_activations(const uint16_t* x, const float* s, int64_t M, int64_t K,
                                           int8_t* qx, float* x_scale, float* xs_out, void* stream);
 
-/* Workspace bytes quasar_w8a8_linear needs for this shape (0 allowed for an
- * empty call).  Pure host function; deterministic in (M, N, K). */
+/* Workspace bytes quasar_w8a8_linear needs for this shape.  Pure host
+ * function, deterministic in (M, N, K).  It is 0 for an empty call and for
+ * verify windows of M <= 8 tokens with K <= 12288, which run as a single
+ * kernel; other shapes stage the quantized activations (and, when K is split
+ * across workgroups, INT32 partial sums) in the workspace. */
 size_t quasar_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
@@ -120,15 +137,18 @@ size_t quasar_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *
  *   x        [M, K] bf16 bits, 16-byte aligned         (in)
  *   s        [K] float32 smoothing vector, 16-byte aligned (in)
- *   wq       [N, K] int8 from quasar_quantize_weights, 16-byte aligned (in)
+ *   wq       tile-packed INT8 weights from quasar_quantize_weights (in)
  *   w_scale  [N] float32 from quasar_quantize_weights  (in)
  *   M, N, K  0 <= M <= QUASAR_MAX_M, N >= 0, 16 <= K <= QUASAR_MAX_K, K % 16 == 0
- *   y        [M, N] bf16 bits, 4-byte aligned          (out)
+ *   y        [M, N] bf16 bits, 2-byte aligned          (out)
  *   acc_out  [M, N] int32 or NULL                      (out, optional: the exact
  *            accumulators, for tests)
  *   workspace, workspace_bytes: device scratch of at least
  *            quasar_w8a8_workspace_bytes(M, N, K) bytes, 256-byte aligned; any
  *            contents; overwritten.  May be NULL when that size is 0.
+ * M <= 8 with K <= 12288 runs as one kernel launch (quantize, GEMM and dequant
+ * fused); other shapes launch the activation quantizer, the GEMM and, for
+ * split K, a reduce kernel, all on `stream`.
  * M == 0 or N == 0 is a no-op.  Errors: INVALID_ARG, UNSUPPORTED (M or K
  * beyond the limits), WORKSPACE, HIP.
  */

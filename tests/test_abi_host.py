@@ -52,14 +52,18 @@ def test_status_strings(L):
     for code in range(5):
         assert L.quasar_status_string(code).decode().startswith("QUASAR_")
     assert b"UNKNOWN" in L.quasar_status_string(99)
-    assert L.quasar_abi_version() == 1
+    assert L.quasar_abi_version() == 2
 
 
 def test_workspace_queries_are_pure_host_and_monotone(L):
     assert L.quasar_w8a8_workspace_bytes(0, 100, 64) == 0
     assert L.quasar_w8a8_workspace_bytes(6, 0, 64) == 0
     assert L.quasar_w8a8_workspace_bytes(6, 100, 60) == 0          # K % 16 != 0
-    for M, N, K in [(6, 6144, 4096), (96, 4096, 12288), (1, 16, 16), (128, 151936, 4096)]:
+    # the one-launch kernel (M <= 8, K <= 12288) needs no workspace
+    for M, N, K in [(6, 6144, 4096), (8, 4096, 12288), (1, 16, 16), (6, 151936, 4096)]:
+        assert L.quasar_w8a8_workspace_bytes(M, N, K) == 0
+    # the multi-kernel path stages the quantized activations
+    for M, N, K in [(96, 4096, 12288), (9, 16, 16), (128, 151936, 4096), (6, 64, 16384)]:
         b = L.quasar_w8a8_workspace_bytes(M, N, K)
         assert b >= M * K + 4 * M and b % 256 == 0
     assert L.quasar_accept_workspace_bytes(0, 5, 10) == 0
@@ -67,7 +71,7 @@ def test_workspace_queries_are_pure_host_and_monotone(L):
     assert L.quasar_accept_workspace_bytes(1, 64, 10) == 0          # k > QUASAR_MAX_DRAFT
 
 
-def linear(L, x=FAKE, s=FAKE, wq=FAKE, sw=FAKE, M=6, N=32, K=64, y=FAKE, acc=None, ws=FAKE,
+def linear(L, x=FAKE, s=FAKE, wq=FAKE, sw=FAKE, M=16, N=32, K=64, y=FAKE, acc=None, ws=FAKE,
            wsb=1 << 20):
     return L.quasar_w8a8_linear(x, s, wq, sw, M, N, K, y, acc, ws, wsb, None)
 
@@ -85,7 +89,7 @@ def test_linear_argument_errors(L):
     assert linear(L, wq=FAKE + 4) == INVALID
     assert linear(L, sw=FAKE + 2) == INVALID
     assert linear(L, acc=FAKE + 2) == INVALID
-    need = L.quasar_w8a8_workspace_bytes(6, 32, 64)
+    need = L.quasar_w8a8_workspace_bytes(16, 32, 64)
     assert need > 0
     assert linear(L, ws=None) == WORKSPACE
     assert linear(L, wsb=need - 1) == WORKSPACE
@@ -126,3 +130,11 @@ def test_accept_argument_errors(L):
     assert accept(L, nxt=FAKE + 2) == INVALID
     assert accept(L, ws=None) == WORKSPACE
     assert accept(L, wsb=16) == WORKSPACE
+
+
+def test_packed_weight_bytes(L):
+    assert L.quasar_packed_weight_bytes(4096, 4096) == 4096 * 4096
+    assert L.quasar_packed_weight_bytes(17, 80) == 2 * 2 * 1024     # padded to 16 rows x 64 cols
+    assert L.quasar_packed_weight_bytes(151936, 4096) == 151936 * 4096
+    assert L.quasar_packed_weight_bytes(0, 64) == 0
+    assert L.quasar_packed_weight_bytes(16, 72) == 0                # K % 16 != 0

@@ -15,7 +15,7 @@ import torch
 
 from oracle import quasar_oracle as orc
 from w8a8_quantized_speculative_amd import binding, synth
-from tests.gpu_helpers import announce, dev, dev_bf16, host, host_bf16
+from tests.gpu_helpers import announce, dev, dev_bf16, host, host_bf16, unpack_weights
 
 pytestmark = pytest.mark.gpu
 
@@ -85,8 +85,7 @@ def test_empty_linear_is_a_noop():
     announce("linear_empty")
     x = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
     s = torch.ones(64, dtype=torch.float32, device="cuda")
-    wq = torch.zeros((8, 64), dtype=torch.int8, device="cuda")
-    sw = torch.ones(8, dtype=torch.float32, device="cuda")
+    wq, sw = binding.quasar_quantize_weights(torch.zeros((8, 64), dtype=torch.bfloat16, device="cuda"), s)
     y = binding.quasar_w8a8_linear(x, s, wq, sw)
     torch.cuda.synchronize()
     assert y.shape == (0, 8)
@@ -118,7 +117,7 @@ def test_qwen3_layer_linear_full_size_sampled(name, K, N, M):
     y, acc, wq, sw = run_gpu(x, s, w)
     cols = sampled_cols(N, 256, N + M)
     ref = check_against_oracle(x, s, w, y, acc, cols)
-    assert np.array_equal(host(wq[torch.from_numpy(cols).cuda()]), ref["qw"])
+    assert np.array_equal(unpack_weights(wq, N, K)[cols], ref["qw"])
 
 
 def test_lm_head_full_size_sampled():

@@ -6,7 +6,7 @@ import torch
 
 from oracle import quasar_oracle as orc
 from w8a8_quantized_speculative_amd import binding, synth
-from tests.gpu_helpers import announce, dev, dev_bf16, f32_bits, host
+from tests.gpu_helpers import announce, dev, dev_bf16, f32_bits, host, unpack_weights
 
 pytestmark = pytest.mark.gpu
 
@@ -34,7 +34,7 @@ def test_quantize_activations_bit_exact(M, K):
     assert np.all(np.abs(got - exact) <= 1e-6 * np.abs(exact))
 
 
-W_SHAPES = [(1024, 1024), (37, 80), (100, 4096), (64, 12288), (5, 65536), (2, 16)]
+W_SHAPES = [(1024, 1024), (37, 80), (100, 4096), (64, 12288), (5, 65536), (2, 16), (17, 1040)]
 
 
 @pytest.mark.parametrize("N,K", W_SHAPES)
@@ -48,7 +48,9 @@ def test_quantize_weights_bit_exact(N, K):
     wq, sw = binding.quasar_quantize_weights(dev_bf16(w), dev(s))
     torch.cuda.synchronize()
     q_ref, sw_ref = orc.quantize_weights(w, s)
-    assert np.array_equal(host(wq), q_ref)
+    full = unpack_weights(wq, N, K, keep_padding=True)
+    assert np.array_equal(full[:N, :K], q_ref)
+    assert not np.any(full[N:]) and not np.any(full[:, K:])   # zero padding
     assert np.array_equal(f32_bits(host(sw)), f32_bits(sw_ref))
 
 
@@ -59,4 +61,4 @@ def test_quantize_empty_is_a_noop():
     qx, sx, _ = binding.quasar_quantize_activations(x, s)
     wq, sw = binding.quasar_quantize_weights(x, s)
     torch.cuda.synchronize()
-    assert qx.shape == (0, 64) and wq.shape == (0, 64)
+    assert qx.shape == (0, 64) and wq.N == 0 and sw.shape == (0,)

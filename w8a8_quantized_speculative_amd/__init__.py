@@ -6,9 +6,11 @@ hand-written gfx950 HIP kernels inside ``libquasar.so`` (C ABI in
 ``synth`` draws the seeded synthetic inputs.
 """
 from .binding import (  # noqa: F401
+    PackedWeights,
     QuasarError,
     lib,
     new_workspace,
+    packed_weight_bytes,
     quasar_quantize_activations,
     quasar_quantize_weights,
     quasar_verify_accept,

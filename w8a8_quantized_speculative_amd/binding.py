@@ -36,6 +36,7 @@ _SIGNATURES = {
     "quasar_abi_version": (ctypes.c_int, []),
     "quasar_quantize_weights": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P]),
     "quasar_quantize_activations": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P, _P]),
+    "quasar_packed_weight_bytes": (_SZ, [_I64, _I64]),
     "quasar_w8a8_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "quasar_w8a8_linear": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _SZ, _P]),
     "quasar_accept_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
@@ -108,12 +109,28 @@ def new_workspace(nbytes: int, device=None) -> torch.Tensor:
 
 
 # ------------------------------------------------------------------ calls
+def packed_weight_bytes(N: int, K: int) -> int:
+    return int(lib().quasar_packed_weight_bytes(N, K))
+
+
+class PackedWeights:
+    """Tile-packed INT8 codes of an N x K linear (layout in include/quasar.h)."""
+
+    def __init__(self, codes: torch.Tensor, N: int, K: int):
+        self.codes, self.N, self.K = codes, N, K
+
+    def data_ptr(self):
+        return self.codes.data_ptr()
+
+
 def quasar_quantize_weights(w: torch.Tensor, s: torch.Tensor):
-    """W [N, K] bf16, s [K] f32 -> (wq int8 [N, K], w_scale f32 [N])."""
+    """W [N, K] bf16, s [K] f32 -> (PackedWeights, w_scale f32 [N])."""
     N, K = w.shape
     _need(w, torch.bfloat16, (N, K), "w")
     _need(s, torch.float32, (K,), "s")
-    wq = torch.empty((N, K), dtype=torch.int8, device=w.device)
+    nbytes = packed_weight_bytes(N, K) if N > 0 else 0
+    codes = torch.empty((max(nbytes, 16),), dtype=torch.int8, device=w.device)
+    wq = PackedWeights(codes, N, K)
     sw = torch.empty((N,), dtype=torch.float32, device=w.device)
     _check("quasar_quantize_weights", lib().quasar_quantize_weights(
         _ptr(w), _ptr(s), N, K, _ptr(wq), _ptr(sw), _stream()))
@@ -133,15 +150,16 @@ def quasar_quantize_activations(x: torch.Tensor, s: torch.Tensor, want_xs: bool 
     return qx, sx, xs
 
 
-def quasar_w8a8_linear(x: torch.Tensor, s: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,
+def quasar_w8a8_linear(x: torch.Tensor, s: torch.Tensor, wq: PackedWeights, w_scale: torch.Tensor,
                        out: torch.Tensor | None = None, acc_out: torch.Tensor | None = None,
                        workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """Y [M, N] bf16 = dequant(quant(X diag(s)) @ wq^T) for X [M, K] bf16."""
+    """Y [M, N] bf16 = dequant(quant(X diag(s)) @ W8^T) for X [M, K] bf16."""
     M, K = x.shape
-    N = wq.shape[0]
+    N = wq.N
+    if not isinstance(wq, PackedWeights) or wq.K != K:
+        raise ValueError("wq must be the PackedWeights of a linear with the same K")
     _need(x, torch.bfloat16, (M, K), "x")
     _need(s, torch.float32, (K,), "s")
-    _need(wq, torch.int8, (N, K), "wq")
     _need(w_scale, torch.float32, (N,), "w_scale")
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)

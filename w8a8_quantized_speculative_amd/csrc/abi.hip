@@ -38,7 +38,7 @@ const char* quasar_status_string(quasar_status status) {
   return "QUASAR_ERR_UNKNOWN";
 }
 
-int quasar_abi_version(void) { return 1; }
+int quasar_abi_version(void) { return 2; }
 
 quasar_status quasar_quantize_weights(const uint16_t* w, const float* s, int64_t N, int64_t K,
                                       int8_t* wq, float* w_scale, void* stream) {
@@ -64,8 +64,13 @@ quasar_status quasar_quantize_activations(const uint16_t* x, const float* s, int
   if (!aligned(x, 16) || !aligned(s, 16) || !aligned(qx, 16) || !aligned(x_scale, 4) ||
       (xs_out && !aligned(xs_out, 16)))
     return QUASAR_ERR_INVALID_ARG;
-  return hip_status(launch_quantize_activations(x, s, M, K, qx, x_scale, xs_out, nullptr, 0,
+  return hip_status(launch_quantize_activations(x, s, M, K, qx, x_scale, xs_out,
                                                 (hipStream_t)stream));
+}
+
+size_t quasar_packed_weight_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || check_k(K) != QUASAR_OK || N > kMaxRowsPerCall) return 0;
+  return packed_weight_bytes(N, K);
 }
 
 size_t quasar_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
@@ -88,18 +93,18 @@ quasar_status quasar_w8a8_linear(const uint16_t* x, const float* s, const int8_t
       !aligned(y, 2) || (acc_out && !aligned(acc_out, 4)))
     return QUASAR_ERR_INVALID_ARG;
   const LinearPlan p = plan_linear(M, N, K);
-  if (p.bytes > 0 && (!workspace || workspace_bytes < p.bytes || !aligned(workspace, kWsAlign)))
-    return QUASAR_ERR_WORKSPACE;
   hipStream_t hs = (hipStream_t)stream;
+  if (p.fused)  // one launch, no workspace
+    return hip_status(launch_fused(plan_fused(M, N, K), x, s, wq, w_scale, y, acc_out, hs));
+  if (!workspace || workspace_bytes < p.bytes || !aligned(workspace, kWsAlign))
+    return QUASAR_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   int8_t* qx = reinterpret_cast<int8_t*>(ws + p.off_qx);
   float* sx = reinterpret_cast<float*>(ws + p.off_sx);
-  int32_t* counters = p.splits > 1 ? reinterpret_cast<int32_t*>(ws + p.off_counters) : nullptr;
   int32_t* partials = p.splits > 1 ? reinterpret_cast<int32_t*>(ws + p.off_partials) : nullptr;
-  hipError_t e = launch_quantize_activations(x, s, M, K, qx, sx, nullptr, counters,
-                                             counters ? p.tiles : 0, hs);
+  hipError_t e = launch_quantize_activations(x, s, M, K, qx, sx, nullptr, hs);
   if (e != hipSuccess) return QUASAR_ERR_HIP;
-  return hip_status(launch_gemm(p, qx, sx, wq, w_scale, y, acc_out, counters, partials, hs));
+  return hip_status(launch_gemm(p, qx, sx, wq, w_scale, y, acc_out, partials, hs));
 }
 
 size_t quasar_accept_workspace_bytes(int64_t B, int64_t k, int64_t V) {

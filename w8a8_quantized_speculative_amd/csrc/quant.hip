@@ -35,19 +35,30 @@ __device__ __forceinline__ void load_unit(const uint16_t* __restrict__ row,
   }
 }
 
+// Codes of 8-element unit q of a row: activations are stored row-major
+// (row_base = row start), weights at their tile-packed position.
+template <bool kWeights>
 __device__ __forceinline__ void store_unit(int8_t* __restrict__ codes, float* __restrict__ xs_out,
-                                           int64_t q, const float v[8], float inv) {
+                                           int64_t row, int64_t nch, int64_t q, const float v[8],
+                                           float inv) {
   int c[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) c[e] = quant_code(v[e], inv);
   uint2 pk;
   pk.x = pack4_i8(c[0], c[1], c[2], c[3]);
   pk.y = pack4_i8(c[4], c[5], c[6], c[7]);
-  *reinterpret_cast<uint2*>(codes + q * 8) = pk;
+  *reinterpret_cast<uint2*>(codes + (kWeights ? packed_offset(row, q * 8, nch) : q * 8)) = pk;
   if (xs_out) {
     *reinterpret_cast<float4*>(xs_out + q * 8) = make_float4(v[0], v[1], v[2], v[3]);
     *reinterpret_cast<float4*>(xs_out + q * 8 + 4) = make_float4(v[4], v[5], v[6], v[7]);
   }
+}
+
+// K positions in [K, 64 * nch) of a packed weight row hold zero codes.
+__device__ __forceinline__ void zero_k_padding(int8_t* __restrict__ wq, int64_t row, int64_t K,
+                                               int64_t nch) {
+  for (int64_t k = K + (int64_t)threadIdx.x * 16; k < nch * 64; k += kRowThreads * 16)
+    *reinterpret_cast<uint4*>(wq + packed_offset(row, k, nch)) = make_uint4(0, 0, 0, 0);
 }
 
 // Register-resident variant: the smoothed row stays in registers between the
@@ -55,8 +66,7 @@ __device__ __forceinline__ void store_unit(int8_t* __restrict__ codes, float* __
 template <bool kWeights, int kUPT>
 __global__ __launch_bounds__(kRowThreads) void quantize_rows_reg_kernel(
     const uint16_t* __restrict__ src, const float* __restrict__ s, int64_t K,
-    int8_t* __restrict__ codes, float* __restrict__ scales, float* __restrict__ xs_out,
-    int32_t* __restrict__ zero_ptr, int64_t zero_words) {
+    int8_t* __restrict__ codes, float* __restrict__ scales, float* __restrict__ xs_out) {
   __shared__ float red[kRowThreads / kWave];
   const int64_t row = blockIdx.x;
   const int64_t units = K / 8;
@@ -74,27 +84,23 @@ __global__ __launch_bounds__(kRowThreads) void quantize_rows_reg_kernel(
   }
   amax = block_max(amax, red);
   const QParams qp = row_qparams(amax);
-  int8_t* cr = codes + row * K;
+  const int64_t nch = (K + 63) / 64;
+  int8_t* cr = kWeights ? codes : codes + row * K;
   float* xo = xs_out ? xs_out + row * K : nullptr;
 #pragma unroll
   for (int u = 0; u < kUPT; ++u) {
     const int64_t q = (int64_t)u * kRowThreads + threadIdx.x;
-    if (q < units) store_unit(cr, xo, q, v[u], qp.inv);
+    if (q < units) store_unit<kWeights>(cr, xo, row, nch, q, v[u], qp.inv);
   }
+  if (kWeights) zero_k_padding(codes, row, K, nch);
   if (threadIdx.x == 0) scales[row] = qp.scale;
-  if (zero_ptr) {
-    for (int64_t i = (int64_t)blockIdx.x * kRowThreads + threadIdx.x; i < zero_words;
-         i += (int64_t)gridDim.x * kRowThreads)
-      zero_ptr[i] = 0;
-  }
 }
 
 // Streaming variant for long rows: two passes over global memory.
 template <bool kWeights>
 __global__ __launch_bounds__(kRowThreads) void quantize_rows_stream_kernel(
     const uint16_t* __restrict__ src, const float* __restrict__ s, int64_t K,
-    int8_t* __restrict__ codes, float* __restrict__ scales, float* __restrict__ xs_out,
-    int32_t* __restrict__ zero_ptr, int64_t zero_words) {
+    int8_t* __restrict__ codes, float* __restrict__ scales, float* __restrict__ xs_out) {
   __shared__ float red[kRowThreads / kWave];
   const int64_t row = blockIdx.x;
   const int64_t units = K / 8;
@@ -108,38 +114,42 @@ __global__ __launch_bounds__(kRowThreads) void quantize_rows_stream_kernel(
   }
   amax = block_max(amax, red);
   const QParams qp = row_qparams(amax);
-  int8_t* cr = codes + row * K;
+  const int64_t nch = (K + 63) / 64;
+  int8_t* cr = kWeights ? codes : codes + row * K;
   float* xo = xs_out ? xs_out + row * K : nullptr;
   for (int64_t q = threadIdx.x; q < units; q += kRowThreads) {
     float v[8];
     load_unit<kWeights>(xr, s, q, v);
-    store_unit(cr, xo, q, v, qp.inv);
+    store_unit<kWeights>(cr, xo, row, nch, q, v, qp.inv);
   }
+  if (kWeights) zero_k_padding(codes, row, K, nch);
   if (threadIdx.x == 0) scales[row] = qp.scale;
-  if (zero_ptr) {
-    for (int64_t i = (int64_t)blockIdx.x * kRowThreads + threadIdx.x; i < zero_words;
-         i += (int64_t)gridDim.x * kRowThreads)
-      zero_ptr[i] = 0;
-  }
+}
+
+// Rows past N in the last 16-row tile of the packed weights hold zero codes.
+__global__ __launch_bounds__(kRowThreads) void zero_pad_rows_kernel(int8_t* __restrict__ wq,
+                                                                    int64_t N, int64_t nch) {
+  const int64_t row = N + blockIdx.x;  // N <= row < 16 * tiles
+  for (int64_t k = (int64_t)threadIdx.x * 16; k < nch * 64; k += kRowThreads * 16)
+    *reinterpret_cast<uint4*>(wq + packed_offset(row, k, nch)) = make_uint4(0, 0, 0, 0);
 }
 
 template <bool kWeights>
 hipError_t launch_rows(const uint16_t* src, const float* s, int64_t rows, int64_t K, int8_t* codes,
-                       float* scales, float* xs_out, int32_t* zero_ptr, int64_t zero_words,
-                       hipStream_t st) {
+                       float* scales, float* xs_out, hipStream_t st) {
   if (rows == 0) return hipSuccess;
   const dim3 grid((unsigned)rows), block(kRowThreads);
   const int64_t upt = (K / 8 + kRowThreads - 1) / kRowThreads;
   if (upt <= 1)
-    quantize_rows_reg_kernel<kWeights, 1><<<grid, block, 0, st>>>(src, s, K, codes, scales, xs_out, zero_ptr, zero_words);
+    quantize_rows_reg_kernel<kWeights, 1><<<grid, block, 0, st>>>(src, s, K, codes, scales, xs_out);
   else if (upt <= 2)
-    quantize_rows_reg_kernel<kWeights, 2><<<grid, block, 0, st>>>(src, s, K, codes, scales, xs_out, zero_ptr, zero_words);
+    quantize_rows_reg_kernel<kWeights, 2><<<grid, block, 0, st>>>(src, s, K, codes, scales, xs_out);
   else if (upt <= 4)
-    quantize_rows_reg_kernel<kWeights, 4><<<grid, block, 0, st>>>(src, s, K, codes, scales, xs_out, zero_ptr, zero_words);
+    quantize_rows_reg_kernel<kWeights, 4><<<grid, block, 0, st>>>(src, s, K, codes, scales, xs_out);
   else if (upt <= 8)
-    quantize_rows_reg_kernel<kWeights, 8><<<grid, block, 0, st>>>(src, s, K, codes, scales, xs_out, zero_ptr, zero_words);
+    quantize_rows_reg_kernel<kWeights, 8><<<grid, block, 0, st>>>(src, s, K, codes, scales, xs_out);
   else
-    quantize_rows_stream_kernel<kWeights><<<grid, block, 0, st>>>(src, s, K, codes, scales, xs_out, zero_ptr, zero_words);
+    quantize_rows_stream_kernel<kWeights><<<grid, block, 0, st>>>(src, s, K, codes, scales, xs_out);
   return hipGetLastError();
 }
 
@@ -147,13 +157,16 @@ hipError_t launch_rows(const uint16_t* src, const float* s, int64_t rows, int64_
 
 hipError_t launch_quantize_weights(const uint16_t* w, const float* s, int64_t N, int64_t K,
                                    int8_t* wq, float* w_scale, hipStream_t st) {
-  return launch_rows<true>(w, s, N, K, wq, w_scale, nullptr, nullptr, 0, st);
+  hipError_t e = launch_rows<true>(w, s, N, K, wq, w_scale, nullptr, st);
+  const int64_t pad_rows = (N + 15) / 16 * 16 - N;
+  if (e != hipSuccess || pad_rows == 0) return e;
+  zero_pad_rows_kernel<<<dim3((unsigned)pad_rows), dim3(kRowThreads), 0, st>>>(wq, N, (K + 63) / 64);
+  return hipGetLastError();
 }
 
 hipError_t launch_quantize_activations(const uint16_t* x, const float* s, int64_t M, int64_t K,
-                                       int8_t* qx, float* sx, float* xs_out, int32_t* zero_ptr,
-                                       int64_t zero_words, hipStream_t st) {
-  return launch_rows<false>(x, s, M, K, qx, sx, xs_out, zero_ptr, zero_words, st);
+                                       int8_t* qx, float* sx, float* xs_out, hipStream_t st) {
+  return launch_rows<false>(x, s, M, K, qx, sx, xs_out, st);
 }
 
 }  // namespace quasar

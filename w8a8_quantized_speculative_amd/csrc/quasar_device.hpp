@@ -65,6 +65,38 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Max over the 64 lanes of a wavefront for NON-NEGATIVE floats, on their bit
+// patterns (which order like unsigned integers), with DPP row operations
+// instead of LDS permutes: butterflies within each row of 16 lanes, then the
+// row broadcasts carry the maxima to lane 63, which is read back as a scalar.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kCtrl, kRowMask, 0xf, false);
+  return v > o ? v : o;
+}
+
+__device__ __forceinline__ float wave_max_nonneg(float f) {
+  uint32_t v = __float_as_uint(f);
+  v = dpp_umax<0xB1, 0xf>(v);   // quad_perm [1,0,3,2]
+  v = dpp_umax<0x4E, 0xf>(v);   // quad_perm [2,3,0,1]
+  v = dpp_umax<0x141, 0xf>(v);  // row_half_mirror
+  v = dpp_umax<0x140, 0xf>(v);  // row_mirror: every lane holds its row's max
+  v = dpp_umax<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_umax<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3: lane 63 has the max
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)v, 63));
+}
+
+// Tile-packed INT8 weight layout.  The weights are stored in the exact order
+// the MFMA A operand is loaded: for each 16-row tile t and 64-wide K chunk c, a
+// 1 KB block holds lane l's 16 bytes at l*16, where lane l = 16*g + r carries
+// row 16t + r, K positions 64c + 16g .. 64c + 16g + 15.  A wavefront thus reads
+// one chunk of one tile as a single contiguous 1 KB.  Rows past N and K past K
+// are zero padding.
+__host__ __device__ __forceinline__ int64_t packed_offset(int64_t n, int64_t k, int64_t nch) {
+  const int64_t t = n >> 4, r = n & 15, c = k >> 6, g = (k >> 4) & 3, b = k & 15;
+  return ((t * nch + c) * 64 + g * 16 + r) * 16 + b;
+}
+
 // Block-wide max; `red` must hold blockDim.x / 64 floats.  Ends with a barrier
 // so `red` can be reused afterwards.
 __device__ __forceinline__ float block_max(float v, float* red) {
@@ -86,6 +118,28 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 // Result: lane l, register r holds D[4 * (l / 16) + r][l % 16].
 __device__ __forceinline__ v4i mfma_i8_16x16x64(v4i a, v4i b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// Raw buffer resource (stride 0): loads at byte offsets >= num_bytes return
+// zero without touching memory.  Word 3 selects 32-bit untyped data, as the
+// gfx9 family expects for raw buffer access.
+typedef __amdgpu_buffer_rsrc_t buffer_rsrc;
+constexpr int kOutOfRange = 0x7ffffff0;  // an offset past every resource this library builds
+constexpr int kNonTemporal = 2;          // cache-policy bit: streaming (nt) access
+
+__device__ __forceinline__ buffer_rsrc make_rsrc(const void* base, uint32_t num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes,
+                                           0x00020000);
+}
+
+template <int kAux = 0>
+__device__ __forceinline__ int load4(buffer_rsrc rs, int offset) {
+  return __builtin_amdgcn_raw_buffer_load_b32(rs, offset, 0, kAux);
+}
+
+template <int kAux = 0>
+__device__ __forceinline__ v4i load16(buffer_rsrc rs, int offset) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, offset, 0, kAux));
 }
 
 }  // namespace quasar

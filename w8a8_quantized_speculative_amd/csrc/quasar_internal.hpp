@@ -13,8 +13,34 @@ constexpr size_t kWsAlign = 256;     // alignment of every workspace sub-buffer
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Bytes of the tile-packed INT8 weights of an N x K linear: ceil(N/16) tiles
+// of ceil(K/64) chunks of 1 KB (see packed_offset in quasar_device.hpp).
+inline size_t packed_weight_bytes(int64_t N, int64_t K) {
+  return (size_t)((N + 15) / 16) * (size_t)((K + 63) / 64) * 1024u;
+}
+
 // ---------------------------------------------------------------------------
-// W8A8 linear plan.
+// One-launch plan (M <= 8, K <= 12288): quantize + GEMM + dequant in one
+// kernel, persistent over 16-channel tiles.  No workspace.
+// ---------------------------------------------------------------------------
+struct FusedPlan {
+  int64_t M, N, K;
+  int tiles, nch;
+  int mt;     // token rows compiled for (2, 4, 6 or 8 >= M)
+  int cfg;    // 0: 8 chunks x 8 wavefronts; 1: 16 chunks (2 phases) x 12 wavefronts
+  int waves, ch;
+  int grid;   // persistent workgroups
+  int lds;    // dynamic LDS bytes
+};
+
+bool fused_supported(int64_t M, int64_t K);
+FusedPlan plan_fused(int64_t M, int64_t N, int64_t K);
+hipError_t launch_fused(const FusedPlan& p, const uint16_t* x, const float* s, const int8_t* wq,
+                        const float* w_scale, uint16_t* y, int32_t* acc_out, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// Multi-kernel W8A8 linear plan (any M <= 128): activation quantize kernel,
+// then the GEMM kernel below, then (only when K is split) a reduce kernel.
 //
 // The output is cut into 16-channel tiles (one MFMA row block).  K is cut into
 // 64-wide chunks (one MFMA K step).  A workgroup owns one (tile, K-split) pair;
@@ -22,7 +48,7 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // that split, stream the matching INT8 weight rows straight into MFMA operand
 // registers, and reduce their partial sums in LDS.  When a tile is split
 // across `splits` workgroups, each writes its exact INT32 partial to the
-// workspace and the last one to arrive (per-tile counter) sums and dequantizes.
+// workspace and a reduce kernel sums the partials and dequantizes.
 // ---------------------------------------------------------------------------
 struct LinearPlan {
   int64_t M, N, K;
@@ -33,8 +59,9 @@ struct LinearPlan {
   int splits;           // workgroups per tile along K
   int chunks_per_split;
   int waves;            // wavefronts per workgroup
+  bool fused;           // the one-launch kernel applies (then no workspace)
   // workspace layout (byte offsets)
-  size_t off_qx, off_sx, off_counters, off_partials, bytes;
+  size_t off_qx, off_sx, off_partials, bytes;
 };
 
 LinearPlan plan_linear(int64_t M, int64_t N, int64_t K);
@@ -56,15 +83,12 @@ AcceptPlan plan_accept(int64_t B, int64_t k, int64_t V);
 hipError_t launch_quantize_weights(const uint16_t* w, const float* s, int64_t N, int64_t K,
                                    int8_t* wq, float* w_scale, hipStream_t st);
 
-// Smooth + quantize activations; also zeroes `zero_words` int32 words at
-// `zero_ptr` (the split-K counters of the following GEMM), when non-null.
 hipError_t launch_quantize_activations(const uint16_t* x, const float* s, int64_t M, int64_t K,
-                                       int8_t* qx, float* sx, float* xs_out, int32_t* zero_ptr,
-                                       int64_t zero_words, hipStream_t st);
+                                       int8_t* qx, float* sx, float* xs_out, hipStream_t st);
 
 hipError_t launch_gemm(const LinearPlan& p, const int8_t* qx, const float* sx, const int8_t* wq,
-                       const float* w_scale, uint16_t* y, int32_t* acc_out, int32_t* counters,
-                       int32_t* partials, hipStream_t st);
+                       const float* w_scale, uint16_t* y, int32_t* acc_out, int32_t* partials,
+                       hipStream_t st);
 
 hipError_t launch_accept(const AcceptPlan& p, const uint16_t* logits, const int32_t* draft,
                          float temperature, const float* uniforms, int32_t* accept_len,
