@@ -53,6 +53,13 @@ __device__ __forceinline__ int quant_code(float v, float inv) {
   return (int)r;
 }
 
+// The same code without the clamp, for |v| <= A and inv = RN32(127 / A): then
+// |v * inv| <= 127 * (1 + 2^-24), whose binary32 rounding is at most 127 + 2^-17,
+// and rint of that is 127, so the clamp can never act.
+__device__ __forceinline__ int quant_code_in_range(float v, float inv) {
+  return (int)__builtin_rintf(v * inv);
+}
+
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
   return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
          ((uint32_t)(d & 0xff) << 24);

@@ -27,7 +27,7 @@ struct FusedPlan {
   int64_t M, N, K;
   int tiles, nch;
   int mt;     // token rows compiled for (2, 4, 6 or 8 >= M)
-  int cfg;    // 0: 8 chunks x 8 wavefronts; 1: 16 chunks (2 phases) x 12 wavefronts
+  int cfg;    // 0: wave-specialized (K <= 4096); 1: 16 chunks (2 phases) x 12 wavefronts
   int waves, ch;
   int grid;   // persistent workgroups
   int lds;    // dynamic LDS bytes
