@@ -60,6 +60,23 @@ __device__ __forceinline__ int quant_code_in_range(float v, float inv) {
   return (int)__builtin_rintf(v * inv);
 }
 
+// The same code as the low byte of a binary32 encoding: for |q| <= 127 + 2^-17
+// (q = RN32(v * inv) as above), q + 1.5 * 2^23 lies in [2^23, 2^24), where
+// consecutive binary32 values are 1 apart, so the addition's round-to-nearest-
+// even result is exactly 1.5 * 2^23 + rint(q).  Its encoding is 0x4B400000 +
+// rint(q), whose low 8 bits are rint(q) in two's complement.  Two operations
+// per code instead of a round, a convert and a mask.
+__device__ __forceinline__ uint32_t quant_code_biased(float v, float inv) {
+  const float q = v * inv;
+  return __float_as_uint(q + 12582912.0f);
+}
+
+// Bytes 0 of four words into one word (byte i from word i).
+__device__ __forceinline__ uint32_t pack4_low_bytes(uint32_t a, uint32_t b, uint32_t c,
+                                                    uint32_t d) {
+  return (a & 0xffu) | ((b & 0xffu) << 8) | ((c & 0xffu) << 16) | (d << 24);
+}
+
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
   return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
          ((uint32_t)(d & 0xff) << 24);

@@ -27,8 +27,8 @@ struct FusedPlan {
   int64_t M, N, K;
   int tiles, nch;
   int mt;     // token rows compiled for (2, 4, 6 or 8 >= M)
-  int cfg;    // 0: wave-specialized (K <= 4096); 1: 16 chunks (2 phases) x 12 wavefronts
-  int waves, ch;
+  int nph;    // weight phases of 8 chunks per streamer wavefront and tile (2, 4 or 6)
+  int waves;  // 4 streamer + 4 or 8 helper wavefronts
   int grid;   // persistent workgroups
   int lds;    // dynamic LDS bytes
 };
