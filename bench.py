@@ -20,7 +20,6 @@ by the step time (GB/s); tokens/s = B * mean(accepted + 1) / step time.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -33,22 +32,18 @@ if ROOT not in sys.path:
 METRIC = ("W8A8 verify-linear HBM GB/s (% of peak) + verified tokens/s at M=6, "
           "Qwen3-8B shape")
 PEAK_HBM_GBS = 8000.0
-PMC_FILE = os.path.join(ROOT, "profiles", "gemm_w8a8_qwen3_stack_m6_pmc.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "w8a8_quantized_speculative_amd", "csrc", f)
-                  for f in ("gemm.hip", "quant.hip", "quasar_device.hpp")]
+PROFILES = os.path.join(ROOT, "profiles")
+COPY_BYTES = 512 << 20  # calibration copy: plain copy kernel of a known size
+BLOCKER_COPIES = 100    # copies queued ahead of each event-timed step (~20 ms of GPU work)
+
+
+def pmc_file(M: int) -> str:
+    return os.path.join(PROFILES, f"w8a8_linear_fused_kernel_qwen3_stack_m{M}_pmc.json")
 
 
 def algorithmic_bytes(M: int, N: int, K: int) -> int:
     """INT8 weights + weight scales + smoothing vector + BF16 input + BF16 output."""
     return N * K + 4 * N + 4 * K + 2 * M * K + 2 * M * N
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def parse():
@@ -61,6 +56,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true", help="skip the BF16-weight comparator")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
+    ap.add_argument("--tau-sets", type=int, default=2048,
+                    help="seeded draft sets for the mean accepted length")
     return ap.parse_args()
 
 
@@ -192,27 +189,53 @@ def measure_tau(stack, n_sets: int):
     return (lens.float() + 1).mean().item()
 
 
-def time_eager_calls(stack, steps: int):
-    """Eager steps with a HIP event pair around every linear call (same stream)."""
+def time_eager_step(stack, steps: int) -> float:
+    """Plain eager step time (host-issued calls, no graph)."""
     import torch
-    n = len(stack.linears)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n * steps)]
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
-    for st in range(steps):
-        for i, e in enumerate(stack.linears):
-            a, b = ev[st * n + i]
-            a.record()
-            stack.linear_call(e)
-            b.record()
-        stack.accept_call()
+    for _ in range(steps):
+        stack.step()
     t1.record()
     torch.cuda.synchronize()
-    durs = [a.elapsed_time(b) for a, b in ev]
-    return t0.elapsed_time(t1) / steps, durs
+    return t0.elapsed_time(t1) / steps
+
+
+def time_kernels(stack, reps: int):
+    """Per-launch time of every linear shape of the step, with HIP events on the
+    launch stream.  Each batch -- `reps` passes over all linears of one shape,
+    rotating through the layers' weights so nothing is re-read from a cache --
+    is queued behind ~20 ms of plain copies, so the GPU reaches it only after
+    the host has enqueued all of it and runs the launches back to back: the
+    events then time the kernels, not the host's submission latency."""
+    import torch
+    from w8a8_quantized_speculative_amd import binding
+    blk_src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    blk_dst = torch.empty_like(blk_src)
+
+    def batch(launch, count):
+        for _ in range(BLOCKER_COPIES):
+            binding.quasar_stream_copy(blk_src, blk_dst)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(count):
+            launch(i)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / count
+
+    shapes = {}
+    for e in stack.linears:
+        shapes.setdefault((e["N"], e["K"]), []).append(e)
+    per_shape = {}
+    for (N, K), ents in shapes.items():
+        ms = batch(lambda i, ents=ents: stack.linear_call(ents[i % len(ents)]), reps * len(ents))
+        per_shape[(N, K)] = ms
+    del blk_src, blk_dst
+    return per_shape
 
 
 def time_bf16_comparator(stack, warmup: int, steps: int):
@@ -286,17 +309,47 @@ def cpu_oracle_baseline(M: int, budget_s: float):
             "ms_per_layer": round(dt / reps * 1e3, 2)}
 
 
-def read_traffic(per_launch_bytes: float):
-    """HBM traffic per launch from committed rocprofv3 PMC runs, when they were
-    taken on the current kernel sources."""
+def read_traffic(M: int, kernel: str):
+    """HBM traffic per launch from the committed rocprofv3 PMC summary, when it
+    was taken on the current kernel sources and for this kernel."""
+    from w8a8_quantized_speculative_amd.profiling import kernel_source_hash
     try:
-        with open(PMC_FILE) as f:
+        with open(pmc_file(M)) as f:
             pmc = json.load(f)
     except (OSError, ValueError):
-        return None, None
+        return None, "no PMC summary for this workload"
+    if pmc.get("kernel") != kernel:
+        return None, "PMC summary is for another kernel"
     if pmc.get("kernel_source_hash") != kernel_source_hash():
-        return None, "stale"
-    return pmc.get("traffic_bytes_per_launch"), pmc.get("note")
+        return None, "kernel sources changed since the PMC runs"
+    return pmc.get("traffic_bytes_per_launch"), (
+        f"FETCH_SIZE + WRITE_SIZE per launch, scaled by a plain copy; "
+        f"{pmc.get('traffic_over_algorithmic')} x the algorithmic bytes")
+
+
+def copy_calibration():
+    """A plain 16-byte-vector copy of COPY_BYTES: the reference the PMC byte
+    counters are scaled by (reported with its rate)."""
+    import torch
+    from w8a8_quantized_speculative_amd import binding
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    binding.quasar_stream_copy(src, dst)
+    torch.cuda.synchronize()
+    reps = 10
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        binding.quasar_stream_copy(src, dst)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"kernel": "stream_copy_kernel", "bytes": COPY_BYTES,
+            "read_plus_write_gbs": round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 1),
+            "us": round(ms * 1e3, 2)}
 
 
 def main():
@@ -311,20 +364,42 @@ def main():
     if args.m % 6 != 0 or not 6 <= args.m <= 96:
         sys.exit("--m must be B*(1+5) with 1 <= B <= 16")
 
+    print("[bench] calibration copy", file=sys.stderr, flush=True)
+    copy_cal = copy_calibration()
     print(f"[bench] building stack: M={args.m} layers={args.layers}", file=sys.stderr, flush=True)
     stack = Stack(args.m, args.layers, keep_bf16=not args.no_bf16)
     drafts = plant_drafts(stack, args.warmup + args.steps)
     print("[bench] graph replay timing", file=sys.stderr, flush=True)
     ms, tau, _graph = time_graph_steps(stack, drafts, args.warmup, args.steps)
-    print("[bench] eager per-call timing", file=sys.stderr, flush=True)
-    eager_ms, durs = time_eager_calls(stack, args.steps)
-    tau_many = measure_tau(stack, 2048)
+    print("[bench] eager step and per-kernel timing", file=sys.stderr, flush=True)
+    eager_ms = time_eager_step(stack, args.steps)
+    per_shape = time_kernels(stack, max(2, args.steps // 4))
+    tau_many = measure_tau(stack, args.tau_sets)
 
+    # per kernel symbol: launches of one step, their algorithmic bytes and time
+    from w8a8_quantized_speculative_amd import binding
     n = len(stack.linears)
-    per_launch_ms = sum(durs) / len(durs)
-    per_launch_bytes = sum(stack.bytes_linear) / n
-    achieved = per_launch_bytes / (per_launch_ms * 1e-3) / 1e9
-    traffic, traffic_note = read_traffic(per_launch_bytes)
+    groups = {}
+    for i, e in enumerate(stack.linears):
+        name = binding.w8a8_kernel_name(args.m, e["N"], e["K"])
+        g = groups.setdefault(name, {"launches_per_step": 0, "bytes": 0, "ms": 0.0})
+        g["launches_per_step"] += 1
+        g["bytes"] += stack.bytes_linear[i]
+        g["ms"] += per_shape[(e["N"], e["K"])]
+    kernels = []
+    for name, g in groups.items():
+        n_l = g["launches_per_step"]
+        launch_ms = g["ms"] / n_l
+        bpl = g["bytes"] / n_l
+        kernels.append({"kernel": name, "launches_per_step": n_l,
+                        "algorithmic_bytes_per_launch": int(bpl),
+                        "launch_avg_us": round(launch_ms * 1e3, 2),
+                        "gbs": round(bpl / (launch_ms * 1e-3) / 1e9, 1),
+                        "bytes_share": round(g["bytes"] / sum(stack.bytes_linear), 4)})
+    kernels.sort(key=lambda k: -k["bytes_share"])
+    dom = kernels[0]
+    achieved = dom["gbs"]
+    traffic, traffic_note = read_traffic(args.m, dom["kernel"])
 
     value = stack.bytes_step / (ms * 1e-3) / 1e9
     out = {
@@ -351,25 +426,27 @@ def main():
         "verified_tokens_per_s": round(stack.B * tau_many / (ms * 1e-3), 1),
         "mean_tau": round(tau_many, 4),
         "mean_tau_timed_steps": round(tau, 4),
-        "tau_note": "tau = accepted drafts + 1; mean over 2048 seeded draft sets (p=0.3, k=5; "
-                    "closed form 1.4275), greedy accept kernel on the step's logits",
+        "tau_note": f"tau = accepted drafts + 1; mean over {args.tau_sets} seeded draft sets "
+                    "(p=0.3, k=5; closed form 1.4275), greedy accept kernel on the step's logits",
         "bytes_per_step": stack.bytes_step,
         "eager_ms_per_step": round(eager_ms, 4),
         "roofline": {
             "bound": "hbm",
-            "achieved": round(achieved, 1),
+            "achieved": achieved,
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "kernel": ("w8a8_linear_fused_kernel (one launch per linear: smooth + per-token "
-                       "INT8 quantize + INT8 MFMA GEMM + BF16 dequant)" if args.m <= 8 else
-                       "quasar_w8a8_linear (activation quantize kernel + INT8 MFMA GEMM kernel)"),
-            "launch_avg_us": round(per_launch_ms * 1e3, 2),
-            "algorithmic_bytes_per_launch": int(per_launch_bytes),
-            "launches_per_step": n,
+            "kernel": dom["kernel"],
+            "launch_avg_us": dom["launch_avg_us"],
+            "algorithmic_bytes_per_launch": dom["algorithmic_bytes_per_launch"],
+            "launches_per_step": dom["launches_per_step"],
+            "timing": ("HIP events on the launch stream around back-to-back batches of the "
+                       "kernel's launches, in the step's mix of shapes"),
             "traffic_note": traffic_note,
         },
+        "kernels": kernels,
+        "copy_calibration": copy_cal,
     }
     if not args.no_bf16:
         print("[bench] bf16 comparator", file=sys.stderr, flush=True)

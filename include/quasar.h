@@ -50,7 +50,7 @@ typedef enum quasar_status {
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* quasar_status_string(quasar_status status);
 
-/* ABI version of this library (bumped on any signature change). */
+/* ABI version of this library (bumped on any change of the exported set). */
 int quasar_abi_version(void);
 
 /*
@@ -122,6 +122,11 @@ quasar_status quasar_quantize_activations(const uint16_t* x, const float* s, int
  * kernel; other shapes stage the quantized activations (and, when K is split
  * across workgroups, INT32 partial sums) in the workspace. */
 size_t quasar_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* Diagnostic: the kernel(s) quasar_w8a8_linear launches for an M x N x K
+ * call, as the profiler names them (static storage; "" for invalid or
+ * unsupported sizes).  Pure host function. */
+const char* quasar_w8a8_kernel_name(int64_t M, int64_t N, int64_t K);
 
 /*
  * quasar_w8a8_linear -- one W8A8 SmoothQuant linear over the verify window.
@@ -199,6 +204,15 @@ quasar_status quasar_verify_accept(const uint16_t* logits, const int32_t* draft,
                                    int32_t* next_token, int32_t* argmax_out,
                                    float* p_draft_out, void* workspace,
                                    size_t workspace_bytes, void* stream);
+
+/*
+ * quasar_stream_copy -- diagnostic, not part of the method: copies `bytes`
+ * bytes from src to dst (device pointers, 16-byte aligned, bytes a multiple of
+ * 16, non-overlapping) with 16-byte streaming loads and stores.  A copy of B
+ * bytes moves exactly B bytes each way, which makes it the reference for
+ * reading the hardware's memory byte counters.  Errors: INVALID_ARG, HIP.
+ */
+quasar_status quasar_stream_copy(const void* src, void* dst, size_t bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -52,7 +52,7 @@ def test_status_strings(L):
     for code in range(5):
         assert L.quasar_status_string(code).decode().startswith("QUASAR_")
     assert b"UNKNOWN" in L.quasar_status_string(99)
-    assert L.quasar_abi_version() == 2
+    assert L.quasar_abi_version() == 3
 
 
 def test_workspace_queries_are_pure_host_and_monotone(L):
@@ -138,3 +138,27 @@ def test_packed_weight_bytes(L):
     assert L.quasar_packed_weight_bytes(151936, 4096) == 151936 * 4096
     assert L.quasar_packed_weight_bytes(0, 64) == 0
     assert L.quasar_packed_weight_bytes(16, 72) == 0                # K % 16 != 0
+
+
+def test_kernel_name_names_the_launch_plan(L):
+    name = lambda M, N, K: L.quasar_w8a8_kernel_name(M, N, K).decode()
+    # one-launch kernel: template <token rows compiled for, weight phases per streamer>
+    assert name(6, 4096, 4096) == "w8a8_linear_fused_kernel<6, 2>"
+    assert name(6, 4096, 12288) == "w8a8_linear_fused_kernel<6, 6>"
+    assert name(1, 16, 16) == "w8a8_linear_fused_kernel<2, 2>"
+    assert name(8, 4096, 8192) == "w8a8_linear_fused_kernel<8, 4>"
+    # wider windows: quantizer + GEMM over ceil(M / 16) token blocks
+    assert name(48, 4096, 4096).startswith("quantize_rows + gemm_w8a8_kernel<3>")
+    assert name(96, 4096, 12288).startswith("quantize_rows + gemm_w8a8_kernel<6>")
+    # invalid or unsupported sizes
+    assert name(0, 16, 16) == "" and name(6, 16, 17) == "" and name(129, 16, 16) == ""
+
+
+def test_stream_copy_argument_errors(L):
+    buf = ctypes.create_string_buffer(64)
+    base = ctypes.addressof(buf)
+    aligned = base + (-base % 16)
+    assert L.quasar_stream_copy(None, None, 0, None) == 0              # empty copy is a no-op
+    assert L.quasar_stream_copy(None, aligned, 16, None) == 1          # null source
+    assert L.quasar_stream_copy(aligned, aligned, 15, None) == 1       # not a multiple of 16
+    assert L.quasar_stream_copy(aligned + 1, aligned, 16, None) == 1   # misaligned

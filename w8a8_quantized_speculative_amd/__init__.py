@@ -13,8 +13,10 @@ from .binding import (  # noqa: F401
     packed_weight_bytes,
     quasar_quantize_activations,
     quasar_quantize_weights,
+    quasar_stream_copy,
     quasar_verify_accept,
     quasar_w8a8_linear,
     workspace_bytes_accept,
+    w8a8_kernel_name,
     workspace_bytes_linear,
 )

@@ -42,6 +42,8 @@ _SIGNATURES = {
     "quasar_accept_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "quasar_verify_accept": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P,
                                             _P, _P, _P, _SZ, _P]),
+    "quasar_w8a8_kernel_name": (ctypes.c_char_p, [_I64, _I64, _I64]),
+    "quasar_stream_copy": (ctypes.c_int, [_P, _P, _SZ, _P]),
 }
 
 
@@ -106,6 +108,21 @@ def new_workspace(nbytes: int, device=None) -> torch.Tensor:
     """A device byte buffer for the *_workspace_bytes sizes (256-byte aligned)."""
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8,
                        device=device if device is not None else "cuda")
+
+
+def w8a8_kernel_name(M: int, N: int, K: int) -> str:
+    """Profiler name of the kernel(s) quasar_w8a8_linear launches for M x N x K."""
+    return lib().quasar_w8a8_kernel_name(M, N, K).decode()
+
+
+def quasar_stream_copy(src: torch.Tensor, dst: torch.Tensor) -> None:
+    """Diagnostic plain device copy of src's bytes into dst (same byte size)."""
+    nbytes = src.numel() * src.element_size()
+    if not (src.is_cuda and dst.is_cuda and src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("src and dst must be contiguous GPU tensors")
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must hold the same number of bytes")
+    _check("quasar_stream_copy", lib().quasar_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream()))
 
 
 # ------------------------------------------------------------------ calls

@@ -38,7 +38,7 @@ const char* quasar_status_string(quasar_status status) {
   return "QUASAR_ERR_UNKNOWN";
 }
 
-int quasar_abi_version(void) { return 2; }
+int quasar_abi_version(void) { return 3; }
 
 quasar_status quasar_quantize_weights(const uint16_t* w, const float* s, int64_t N, int64_t K,
                                       int8_t* wq, float* w_scale, void* stream) {
@@ -77,6 +77,34 @@ size_t quasar_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || check_k(K) != QUASAR_OK || M > QUASAR_MAX_M || N > kMaxRowsPerCall)
     return 0;
   return plan_linear(M, N, K).bytes;
+}
+
+const char* quasar_w8a8_kernel_name(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || check_k(K) != QUASAR_OK || M > QUASAR_MAX_M || N > kMaxRowsPerCall)
+    return "";
+  const LinearPlan p = plan_linear(M, N, K);
+  if (p.fused) return fused_kernel_name(plan_fused(M, N, K));
+  static const char* const names[2][8] = {
+      {"quantize_rows + gemm_w8a8_kernel<1>", "quantize_rows + gemm_w8a8_kernel<2>",
+       "quantize_rows + gemm_w8a8_kernel<3>", "quantize_rows + gemm_w8a8_kernel<4>",
+       "quantize_rows + gemm_w8a8_kernel<5>", "quantize_rows + gemm_w8a8_kernel<6>",
+       "quantize_rows + gemm_w8a8_kernel<7>", "quantize_rows + gemm_w8a8_kernel<8>"},
+      {"quantize_rows + gemm_w8a8_kernel<1> + splitk_dequant",
+       "quantize_rows + gemm_w8a8_kernel<2> + splitk_dequant",
+       "quantize_rows + gemm_w8a8_kernel<3> + splitk_dequant",
+       "quantize_rows + gemm_w8a8_kernel<4> + splitk_dequant",
+       "quantize_rows + gemm_w8a8_kernel<5> + splitk_dequant",
+       "quantize_rows + gemm_w8a8_kernel<6> + splitk_dequant",
+       "quantize_rows + gemm_w8a8_kernel<7> + splitk_dequant",
+       "quantize_rows + gemm_w8a8_kernel<8> + splitk_dequant"}};
+  return names[p.splits > 1 ? 1 : 0][p.mb - 1];
+}
+
+quasar_status quasar_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (bytes == 0) return QUASAR_OK;
+  if (!src || !dst || bytes % 16 != 0 || !aligned(src, 16) || !aligned(dst, 16))
+    return QUASAR_ERR_INVALID_ARG;
+  return hip_status(launch_stream_copy(src, dst, bytes, (hipStream_t)stream));
 }
 
 quasar_status quasar_w8a8_linear(const uint16_t* x, const float* s, const int8_t* wq,

@@ -410,6 +410,19 @@ FusedPlan plan_fused(int64_t M, int64_t N, int64_t K) {
   return p;
 }
 
+const char* fused_kernel_name(const FusedPlan& p) {
+  static const char* const names[4][3] = {
+      {"w8a8_linear_fused_kernel<2, 2>", "w8a8_linear_fused_kernel<2, 4>",
+       "w8a8_linear_fused_kernel<2, 6>"},
+      {"w8a8_linear_fused_kernel<4, 2>", "w8a8_linear_fused_kernel<4, 4>",
+       "w8a8_linear_fused_kernel<4, 6>"},
+      {"w8a8_linear_fused_kernel<6, 2>", "w8a8_linear_fused_kernel<6, 4>",
+       "w8a8_linear_fused_kernel<6, 6>"},
+      {"w8a8_linear_fused_kernel<8, 2>", "w8a8_linear_fused_kernel<8, 4>",
+       "w8a8_linear_fused_kernel<8, 6>"}};
+  return names[p.mt / 2 - 1][p.nph / 2 - 1];
+}
+
 hipError_t launch_fused(const FusedPlan& p, const uint16_t* x, const float* s, const int8_t* wq,
                         const float* w_scale, uint16_t* y, int32_t* acc_out, hipStream_t st) {
   switch (p.mt) {

@@ -34,6 +34,8 @@ struct FusedPlan {
 };
 
 bool fused_supported(int64_t M, int64_t K);
+// Name of the kernel of a one-launch plan (static storage).
+const char* fused_kernel_name(const FusedPlan& p);
 FusedPlan plan_fused(int64_t M, int64_t N, int64_t K);
 hipError_t launch_fused(const FusedPlan& p, const uint16_t* x, const float* s, const int8_t* wq,
                         const float* w_scale, uint16_t* y, int32_t* acc_out, hipStream_t st);
@@ -94,5 +96,8 @@ hipError_t launch_accept(const AcceptPlan& p, const uint16_t* logits, const int3
                          float temperature, const float* uniforms, int32_t* accept_len,
                          int32_t* next_token, int32_t* argmax_out, float* p_draft_out,
                          void* workspace, hipStream_t st);
+
+// Diagnostic plain copy (16-byte vectors), bytes % 16 == 0.
+hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
 
 }  // namespace quasar

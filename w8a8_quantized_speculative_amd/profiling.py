@@ -1,0 +1,219 @@
+"""Summaries of rocprofv3 runs of ``bench.py`` for the ``profiles/`` folder.
+
+Two kinds of run are summarised (the commands are recorded in each summary):
+
+* ``stats``: ``rocprofv3 --kernel-trace --stats -f csv ... -- python3 bench.py``.
+  The summary lists every kernel's call count and mean duration, and puts the
+  mean duration rocprofv3 measured for the roofline kernel next to the mean
+  the bench measured with HIP events in the same run.
+* ``pmc``: two ``rocprofv3 --pmc`` runs of the bench, one with ``FETCH_SIZE``
+  and one with ``WRITE_SIZE``.  Each counter is scaled by what it reads for the
+  bench's calibration copy (``stream_copy_kernel``, a plain copy of a known
+  number of bytes), and the scaled HBM bytes per launch of the roofline kernel
+  are written to a JSON file that ``bench.py`` reports as ``roofline.traffic``
+  while the kernel sources still hash to the recorded value.
+
+    python -m w8a8_quantized_speculative_amd.profiling stats STATS_CSV BENCH_JSON OUT_MD --command CMD
+    python -m w8a8_quantized_speculative_amd.profiling pmc FETCH_CSV WRITE_CSV BENCH_JSON OUT_JSON OUT_MD \\
+        --command-fetch CMD --command-write CMD
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import shlex
+import sys
+import hashlib
+import json
+import os
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+# sources of the one-launch linear kernel (the roofline kernel at M <= 8)
+KERNEL_SOURCES = [os.path.join(PKG, "csrc", f)
+                  for f in ("fused.hip", "quasar_device.hpp", "quasar_internal.hpp")]
+COPY_KERNEL = "stream_copy_kernel"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _short(name: str) -> str:
+    """'void ns::(anonymous namespace)::foo<6, 2>(args)' -> 'foo<6, 2>': drop the
+    argument list and the qualifiers at template depth 0."""
+    depth, cut, last_sep = 0, len(name), 0
+    i = 0
+    while i < len(name):
+        ch = name[i]
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif depth == 0 and name.startswith("(anonymous namespace)", i):
+            i += len("(anonymous namespace)")
+            continue
+        elif depth == 0 and ch == "(":
+            cut = i
+            break
+        elif depth == 0 and name.startswith("::", i):
+            last_sep = i + 2
+            i += 2
+            continue
+        i += 1
+    head = name[last_sep:cut]
+    if head.startswith("void "):
+        head = head[5:]
+    return head.strip()
+
+
+def _cell(name: str, width: int = 72) -> str:
+    return name if len(name) <= width else name[:width - 3] + "..."
+
+
+def _bench_line(path: str) -> dict:
+    with open(path) as f:
+        lines = [ln for ln in f.read().splitlines() if ln.startswith("{")]
+    return json.loads(lines[-1])
+
+
+def _self_command() -> str:
+    return "python -m w8a8_quantized_speculative_amd.profiling " + " ".join(
+        shlex.quote(a) for a in sys.argv[1:])
+
+
+def summarize_stats(stats_csv: str, bench_json: str, out_md: str, command: str) -> dict:
+    rows = []
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            rows.append((_short(r["Name"]), int(r["Calls"]), float(r["TotalDurationNs"]),
+                         float(r["AverageNs"]), float(r["MinNs"]), float(r["MaxNs"])))
+    rows.sort(key=lambda r: -r[2])
+    bench = _bench_line(bench_json)
+    roof = bench["roofline"]
+    kname = roof["kernel"]
+    prof = [r for r in rows if r[0] == kname]
+    prof_avg_us = prof[0][3] / 1e3 if prof else None
+    out = ["# rocprofv3 kernel statistics: " + bench["config"]["workload"], "",
+           "Profiled command (paths relative to the repository root of the GPU run):", "",
+           "```", command, "```", "", "Summary written by:", "", "```", _self_command(), "```", "",
+           f"Bench line of the same run: value {bench['value']} {bench['unit']}, "
+           f"{bench['ms_per_step']} ms per step, roofline kernel `{kname}`.", "",
+           "| kernel | calls | total ms | mean us | min us | max us |",
+           "|---|---:|---:|---:|---:|---:|"]
+    for name, calls, tot, avg, mn, mx in rows[:20]:
+        out.append(f"| `{_cell(name)}` | {calls} | {tot / 1e6:.3f} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | "
+                   f"{mx / 1e3:.2f} |")
+    out += ["", "Roofline kernel, mean duration per launch:", "",
+            f"- rocprofv3 (all launches in the run, graph replays and eager calls): "
+            f"{prof_avg_us:.2f} us" if prof_avg_us is not None else "- rocprofv3: kernel not found",
+            f"- bench.py, HIP events around back-to-back batches of its launches, same run: "
+            f"{roof['launch_avg_us']} us",
+            f"- algorithmic bytes per launch: {roof['algorithmic_bytes_per_launch']} "
+            f"-> {roof['achieved']} GB/s by the events, "
+            + (f"{roof['algorithmic_bytes_per_launch'] / (prof_avg_us * 1e3):.1f} GB/s by rocprofv3"
+               if prof_avg_us else "n/a"),
+            ""]
+    with open(out_md, "w") as f:
+        f.write("\n".join(out))
+    return {"rocprof_avg_us": prof_avg_us, "events_avg_us": roof["launch_avg_us"]}
+
+
+def _counter_means(path: str, counter: str) -> dict:
+    """Mean counter value per dispatch, by short kernel name."""
+    acc = defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name", "").strip() != counter:
+                continue
+            acc[_short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, bench_json: str, out_json: str, out_md: str,
+                  command_fetch: str, command_write: str) -> dict:
+    bench = _bench_line(bench_json)
+    kname = bench["roofline"]["kernel"]
+    copy_bytes = bench["copy_calibration"]["bytes"]
+    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
+    write = _counter_means(write_csv, "WRITE_SIZE")
+    cf, cw = fetch[COPY_KERNEL][0], write[COPY_KERNEL][0]
+    f_scale, w_scale = copy_bytes / cf, copy_bytes / cw  # bytes per counter unit
+    kf, nf = fetch[kname]
+    kw, nw = write[kname]
+    traffic = kf * f_scale + kw * w_scale
+    alg = bench["roofline"]["algorithmic_bytes_per_launch"]
+    res = {
+        "kernel": kname,
+        "kernel_source_hash": kernel_source_hash(),
+        "traffic_bytes_per_launch": round(traffic),
+        "fetch_bytes_per_launch": round(kf * f_scale),
+        "write_bytes_per_launch": round(kw * w_scale),
+        "algorithmic_bytes_per_launch": alg,
+        "traffic_over_algorithmic": round(traffic / alg, 4),
+        "dispatches_averaged": {"FETCH_SIZE": nf, "WRITE_SIZE": nw},
+        "calibration": {"kernel": COPY_KERNEL, "bytes": copy_bytes,
+                        "FETCH_SIZE": cf, "WRITE_SIZE": cw,
+                        "bytes_per_unit_fetch": round(f_scale, 4),
+                        "bytes_per_unit_write": round(w_scale, 4)},
+        "commands": [command_fetch, command_write],
+        "note": "FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by its reading for a "
+                "plain copy of a known size; mean over every launch of the kernel in the run",
+    }
+    with open(out_json, "w") as f:
+        json.dump(res, f, indent=1)
+    out = ["# HBM traffic (rocprofv3 PMC): " + bench["config"]["workload"], "",
+           "Profiled commands (paths relative to the repository root of the GPU run):", "",
+           "```", command_fetch, command_write, "```", "", "Summary written by:", "", "```",
+           _self_command(), "```", "",
+           f"Calibration: `{COPY_KERNEL}` copies {copy_bytes} bytes; it reads FETCH_SIZE {cf:.1f} "
+           f"and WRITE_SIZE {cw:.1f}, i.e. {f_scale:.2f} and {w_scale:.2f} bytes per counter unit.",
+           "",
+           "| kernel | dispatches | FETCH bytes/launch | WRITE bytes/launch | traffic | algorithmic | ratio |",
+           "|---|---:|---:|---:|---:|---:|---:|",
+           f"| `{kname}` | {nf} | {kf * f_scale:.0f} | {kw * w_scale:.0f} | {traffic:.0f} | {alg} | "
+           f"{traffic / alg:.4f} |", "",
+           "Other kernels of the run (scaled the same way, bytes per dispatch):", "",
+           "| kernel | dispatches | FETCH | WRITE |", "|---|---:|---:|---:|"]
+    for name in sorted(set(fetch) & set(write), key=lambda n: -fetch[n][0] * fetch[n][1])[:12]:
+        out.append(f"| `{_cell(name)}` | {fetch[name][1]} | {fetch[name][0] * f_scale:.0f} | "
+                   f"{write[name][0] * w_scale:.0f} |")
+    out.append("")
+    with open(out_md, "w") as f:
+        f.write("\n".join(out))
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("stats_csv")
+    a.add_argument("bench_json")
+    a.add_argument("out_md")
+    a.add_argument("--command", required=True)
+    b = sub.add_parser("pmc")
+    b.add_argument("fetch_csv")
+    b.add_argument("write_csv")
+    b.add_argument("bench_json")
+    b.add_argument("out_json")
+    b.add_argument("out_md")
+    b.add_argument("--command-fetch", required=True)
+    b.add_argument("--command-write", required=True)
+    args = ap.parse_args()
+    if args.cmd == "stats":
+        print(json.dumps(summarize_stats(args.stats_csv, args.bench_json, args.out_md,
+                                         args.command)))
+    else:
+        print(json.dumps(summarize_pmc(args.fetch_csv, args.write_csv, args.bench_json,
+                                       args.out_json, args.out_md, args.command_fetch,
+                                       args.command_write)))
+
+
+if __name__ == "__main__":
+    main()
