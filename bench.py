@@ -156,9 +156,10 @@ def time_graph_steps(stack, drafts, warmup: int, steps: int):
         stack.draft.copy_(drafts[i])
         graph.replay()
         lens[i].copy_(stack.accept_len)
-    torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
     t0.record()
     for i in range(warmup, warmup + steps):
         stack.draft.copy_(drafts[i])
@@ -166,9 +167,22 @@ def time_graph_steps(stack, drafts, warmup: int, steps: int):
         lens[i].copy_(stack.accept_len)
     t1.record()
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
+    ms = (time.perf_counter() - w0) * 1e3 / steps
+    ms_events = t0.elapsed_time(t1) / steps
     tau = (lens[warmup:].float() + 1).mean().item()
-    return ms, tau, graph
+    # the replay must recompute the step: clear the first and the last linear's
+    # outputs, replay once, and require both to be written again
+    probes = (stack.linears[0]["y"], stack.linears[-1]["y"])
+    for y in probes:
+        y.zero_()
+    graph.replay()
+    torch.cuda.synchronize()
+    if not all(bool((y != 0).any()) for y in probes):
+        raise RuntimeError("the captured step did not recompute its outputs on replay")
+    if abs(ms - ms_events) > 0.1 * ms:
+        raise RuntimeError(f"step time disagrees between host clock ({ms:.4f} ms) and "
+                           f"HIP events ({ms_events:.4f} ms)")
+    return ms, ms_events, tau, graph
 
 
 def measure_tau(stack, n_sets: int):
@@ -370,7 +384,7 @@ def main():
     stack = Stack(args.m, args.layers, keep_bf16=not args.no_bf16)
     drafts = plant_drafts(stack, args.warmup + args.steps)
     print("[bench] graph replay timing", file=sys.stderr, flush=True)
-    ms, tau, _graph = time_graph_steps(stack, drafts, args.warmup, args.steps)
+    ms, ms_events, tau, _graph = time_graph_steps(stack, drafts, args.warmup, args.steps)
     print("[bench] eager step and per-kernel timing", file=sys.stderr, flush=True)
     eager_ms = time_eager_step(stack, args.steps)
     per_shape = time_kernels(stack, max(2, args.steps // 4))
@@ -398,6 +412,14 @@ def main():
                         "bytes_share": round(g["bytes"] / sum(stack.bytes_linear), 4)})
     kernels.sort(key=lambda k: -k["bytes_share"])
     dom = kernels[0]
+    linears = []
+    for (N, K), shape_ms in per_shape.items():
+        e = next(x for x in stack.linears if (x["N"], x["K"]) == (N, K))
+        nb = algorithmic_bytes(args.m, N, K)
+        linears.append({"linear": e["name"], "N": N, "K": K,
+                        "launch_us": round(shape_ms * 1e3, 2),
+                        "gbs": round(nb / (shape_ms * 1e-3) / 1e9, 1),
+                        "kernel": binding.w8a8_kernel_name(args.m, N, K)})
     achieved = dom["gbs"]
     traffic, traffic_note = read_traffic(args.m, dom["kernel"])
 
@@ -410,6 +432,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_events": round(ms_events, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -420,7 +443,8 @@ def main():
             "M": args.m, "B": stack.B, "k": stack.k, "layers": args.layers, "hidden": 4096,
             "intermediate": 12288, "vocab": stack.V, "linears_per_step": n,
             "weights_int8_gb": round(sum(e["N"] * e["K"] for e in stack.linears) / 1e9, 3),
-            "timing": "HIP-graph replay of the whole step, new drafts per step",
+            "timing": "HIP-graph replay of the whole step, new drafts per step; host clock "
+                      "between torch.cuda.synchronize() calls",
         },
         "hbm_frac_of_peak": round(value / PEAK_HBM_GBS, 4),
         "verified_tokens_per_s": round(stack.B * tau_many / (ms * 1e-3), 1),
@@ -446,6 +470,7 @@ def main():
             "traffic_note": traffic_note,
         },
         "kernels": kernels,
+        "linears": linears,
         "copy_calibration": copy_cal,
     }
     if not args.no_bf16:

@@ -58,6 +58,10 @@ def test_single_linear_1024_m6_every_element():
 RAGGED = [
     (1, 16, 16), (6, 1000, 1040), (16, 257, 4096), (17, 300, 1024), (48, 513, 2048),
     (96, 129, 4096), (128, 64, 512), (5, 33, 12288), (2, 7, 3072), (6, 4096, 192),
+    # one-launch kernel: every token-row variant (2, 4, 6, 8) and every K variant
+    # (<= 4096, <= 8192, <= 12288), with ragged N and partial last streamer ranges
+    (4, 48, 4096), (8, 300, 4096), (3, 40, 6144), (7, 100, 8000), (8, 64, 10000),
+    (4, 520, 12288),
 ]
 
 
