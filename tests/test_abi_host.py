@@ -142,11 +142,11 @@ def test_packed_weight_bytes(L):
 
 def test_kernel_name_names_the_launch_plan(L):
     name = lambda M, N, K: L.quasar_w8a8_kernel_name(M, N, K).decode()
-    # one-launch kernel: template <token rows compiled for, weight phases per streamer>
-    assert name(6, 4096, 4096) == "w8a8_linear_fused_kernel<6, 2>"
-    assert name(6, 4096, 12288) == "w8a8_linear_fused_kernel<6, 6>"
-    assert name(1, 16, 16) == "w8a8_linear_fused_kernel<2, 2>"
-    assert name(8, 4096, 8192) == "w8a8_linear_fused_kernel<8, 4>"
+    # one-launch kernel: <token rows compiled for, streamer wavefronts, phases per streamer>
+    assert name(6, 4096, 4096) == "w8a8_linear_fused_kernel<6, 4, 2>"
+    assert name(6, 4096, 12288) == "w8a8_linear_fused_kernel<6, 4, 6>"
+    assert name(1, 16, 16) == "w8a8_linear_fused_kernel<2, 4, 2>"
+    assert name(8, 4096, 8192) == "w8a8_linear_fused_kernel<8, 4, 4>"
     # wider windows: quantizer + GEMM over ceil(M / 16) token blocks
     assert name(48, 4096, 4096).startswith("quantize_rows + gemm_w8a8_kernel<3>")
     assert name(96, 4096, 12288).startswith("quantize_rows + gemm_w8a8_kernel<6>")

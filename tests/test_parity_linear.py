@@ -62,6 +62,8 @@ RAGGED = [
     # (<= 4096, <= 8192, <= 12288), with ragged N and partial last streamer ranges
     (4, 48, 4096), (8, 300, 4096), (3, 40, 6144), (7, 100, 8000), (8, 64, 10000),
     (4, 520, 12288),
+    # many tiles per compute unit: uneven contiguous tile ranges per workgroup
+    (6, 9000, 1024), (2, 8336, 80), (8, 12000, 256),
 ]
 
 
@@ -148,3 +150,4 @@ def test_repeated_calls_are_bit_identical():
     for _ in range(50):
         again = binding.quasar_w8a8_linear(xd, sd, wq, sw, workspace=ws)
         assert torch.equal(again.view(torch.int16), first.view(torch.int16))
+

@@ -27,8 +27,8 @@ struct FusedPlan {
   int64_t M, N, K;
   int tiles, nch;
   int mt;     // token rows compiled for (2, 4, 6 or 8 >= M)
-  int nph;    // weight phases of 8 chunks per streamer wavefront and tile (2, 4 or 6)
-  int waves;  // 4 streamer + 4 or 8 helper wavefronts
+  int variant;  // 0: K <= 4096, 1: K <= 8192, 2: K <= 12288 (streamer/helper split)
+  int waves;    // streamer + helper wavefronts per workgroup
   int grid;   // persistent workgroups
   int lds;    // dynamic LDS bytes
 };
