@@ -19,9 +19,11 @@
 //   * wavefronts are specialized.  A compute unit keeps only ~32-64 KB of
 //     vector-memory misses in flight, and a wavefront that issues beyond that
 //     stalls at issue until data returns.  So S *streamer* wavefronts own the
-//     weight stream: streamer w owns chunks [w*8*NPH, (w+1)*8*NPH) of 64 K
-//     positions, in NPH phases of 8 chunks rotating through NBUF register
-//     buffers (later phases are in flight while earlier ones are multiplied).
+//     weight stream, in NPH phases of 8 chunks of 64 K positions per tile:
+//     phase p of streamer w is chunks p*8S + 8w .. p*8S + 8w + 7, so a phase
+//     of all streamers is one contiguous K range.  Phases rotate through NBUF
+//     register buffers (later phases are in flight while earlier ones are
+//     multiplied).
 //     Each chunk is one
 //     contiguous 1 KB of the tile-packed weights (one 128-bit load per lane,
 //     already in MFMA A-operand order), loaded with the streaming (nt) policy.
@@ -32,8 +34,10 @@
 //     xs = RN32(x * s), reduce the per-token absmax (DPP within a wavefront,
 //     then an LDS counter among the helpers -- not a workgroup barrier, which
 //     would wait for the stalled streamers) and write the INT8 codes into an
-//     LDS matrix that feeds the MFMA B operand.  Helpers issue no load behind
-//     the weight stream;
+//     LDS matrix that feeds the MFMA B operand, in K order, announcing each
+//     finished K range on an LDS counter: the streamers start multiplying a
+//     phase as soon as its codes exist.  Helpers issue no load behind the
+//     weight stream;
 //   * per tile the streamers' 16x16 INT32 partials (and the tile's weight
 //     scales, fetched by streamer 0 with its last phase) go to LDS, and 64
 //     helper threads apply the dequant epilogue, 4 channels (8 bytes) per
@@ -74,6 +78,8 @@ static_assert(Variant<0>::NH * 64 * Variant<0>::UP * 8 >= Variant<0>::KMAX &&
                   Variant<1>::NH * 64 * Variant<1>::UP * 8 >= Variant<1>::KMAX &&
                   Variant<2>::NH * 64 * Variant<2>::UP * 8 >= Variant<2>::KMAX,
               "helpers cover K");
+static_assert(Variant<0>::UP <= 4 && Variant<1>::UP <= 4 && Variant<2>::UP <= 4,
+              "one readiness counter per quantization step");
 
 struct Smem {
   // byte offsets into dynamic LDS
@@ -83,6 +89,7 @@ struct Smem {
   int amax;   // float [kMaxHelpers][kMaxMT] per-helper token maxima
   int qp;     // float [kMaxMT] token scales
   int cnt;    // int: helper wavefronts that published their maxima
+  int ready;  // int [4]: per quantization step, helper wavefronts that completed it
   int bytes;
 };
 
@@ -94,7 +101,8 @@ __host__ __device__ inline Smem smem_layout(int K, int MT, int S) {
   s.amax = s.wsl + 2 * 16 * 4;
   s.qp = s.amax + kMaxHelpers * kMaxMT * 4;
   s.cnt = s.qp + kMaxMT * 4;
-  s.bytes = s.cnt + 16;
+  s.ready = s.cnt + 16;
+  s.bytes = s.ready + 4 * 4;
   return s;
 }
 
@@ -109,15 +117,20 @@ __host__ __device__ inline Smem smem_layout(int K, int MT, int S) {
 // exact.  Units past the last tile are issued (as zero reads) but never
 // consumed, and only real tiles take the per-tile barrier, so the barrier
 // count matches the helpers'.
-template <int MT, int S, int NPH, int NBUF>
+template <int MT, int S, int NPH, int NBUF, int NH>
 __device__ __forceinline__ void streamer(const int8_t* __restrict__ wq,
                                          const float* __restrict__ wscale, int N, int K,
                                          int first, int T, int wave, int lane,
-                                         const int8_t* codes, int Ks, int32_t* red, float* wsl) {
+                                         const int8_t* codes, int Ks, int32_t* red, float* wsl,
+                                         const int* ready) {
   static_assert(NPH % NBUF == 0, "phase p of every tile uses buffer p % NBUF");
+  // helper quantization step u covers K positions [u * 512 NH, (u + 1) * 512 NH):
+  // PPS = NH / 4 phases of 8S chunks of 64
+  constexpr int PPS = NH * 512 / (S * kPH * 64);
+  static_assert(PPS * S * kPH * 64 == NH * 512, "a quantization step covers whole phases");
   const int r = lane & 15, g = lane >> 4;
   const int nch = (K + 63) >> 6;
-  const int cw = wave * (NPH * kPH);  // first chunk of this wavefront
+  const int cw = wave * kPH;  // chunk of phase 0 of this wavefront; phase p adds p * 8S
   v4i a[NBUF][kPH];
   float wsv[NBUF];  // wavefront 0, lanes 0..15: weight scales if the buffer holds a last phase
 
@@ -131,7 +144,7 @@ __device__ __forceinline__ void streamer(const int8_t* __restrict__ wq,
     const int8_t* tbase = wq + (size_t)tl * nch * 1024;
 #pragma unroll
     for (int j = 0; j < kPH; ++j) {
-      const int c = cw + ph * kPH + j;
+      const int c = cw + ph * (S * kPH) + j;
       const buffer_rsrc rs =
           make_rsrc(tbase + (size_t)c * 1024, (valid && c < nch) ? 1024u : 0u);
       a[b][j] = load16<kNonTemporal>(rs, voff);
@@ -144,7 +157,9 @@ __device__ __forceinline__ void streamer(const int8_t* __restrict__ wq,
   __syncthreads();  // (1) the helpers' activation loads are queued first
 #pragma unroll
   for (int b = 0; b < NBUF; ++b) issue(b, first, b);
-  __syncthreads();  // (2) code matrix complete
+  // keep the tile loop from being rotated into the issue above: the in-order
+  // wait counts are exact only with the loop entered after all NBUF issues
+  __builtin_amdgcn_sched_barrier(0);
 
   // MFMA B operand: 16 code bytes of token row r at K position 64c + 16g.  No
   // masking is needed: the packed weights are zero past K, so whatever the code
@@ -155,6 +170,24 @@ __device__ __forceinline__ void streamer(const int8_t* __restrict__ wq,
   auto bfrag = [&](int c) -> v4i {
     return *reinterpret_cast<const v4i*>(brow + min(c, nch - 1) * 64);
   };
+  // Before a phase of the first tile is multiplied, its codes must exist: per
+  // quantization step, the helpers count the wavefronts that finished it (each
+  // after its LDS writes have completed), so wait until all NH have finished
+  // the step holding this phase.  (One counter per step: a helper with no
+  // pieces in a step finishes it at once, so a single running total could
+  // reach a step's share while another helper is still writing it.)  The counter orders LDS accesses only, and LDS
+  // executes a wavefront's accesses in order, so a relaxed load plus a
+  // compiler barrier suffices; an acquire would also wait for this
+  // wavefront's weight loads in flight.  All helpers are resident and finish
+  // every step unconditionally; the spin is bounded all the same.
+  auto wait_codes = [&](int ph) {
+    const int* step_done = ready + ph / PPS;
+    for (int spin = 0; spin < (1 << 22); ++spin) {
+      if (__hip_atomic_load(step_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= NH) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");  // keep the code reads below the wait
+  };
   v4i acc = {0, 0, 0, 0};
   for (int t = 0; t < T; ++t) {
     const int tile = first + t;
@@ -163,8 +196,10 @@ __device__ __forceinline__ void streamer(const int8_t* __restrict__ wq,
     for (int ph = 0; ph < NPH; ++ph) {
       constexpr int kNB = NBUF;
       const int b = ph % kNB;
+      if (t == 0 && ph % PPS == 0) wait_codes(ph);
 #pragma unroll
-      for (int i = 0; i < kPH; ++i) acc = mfma_i8_16x16x64(a[b][i], bfrag(cw + ph * kPH + i), acc);
+      for (int i = 0; i < kPH; ++i)
+        acc = mfma_i8_16x16x64(a[b][i], bfrag(cw + ph * (S * kPH) + i), acc);
       // the unit this buffer streams next: a later phase of this tile, or of the next
       const bool same = ph + kNB < NPH;
       const int ntile = same ? tile : next;
@@ -194,7 +229,7 @@ __device__ __forceinline__ void helper(const uint16_t* __restrict__ x, const flo
                                        int M, int N, int K, int first, int T, int ht, int hwave,
                                        int lane,
                                        int8_t* codes, int Ks, const int32_t* red, const float* wsl,
-                                       float* amax_part, float* qp, int* cnt,
+                                       float* amax_part, float* qp, int* cnt, int* ready,
                                        uint16_t* __restrict__ y, int32_t* __restrict__ acc_out) {
   constexpr int HT = 64 * NH;  // helper threads
   const int units = K >> 3;    // pieces of 8 K positions per token row
@@ -309,8 +344,10 @@ __device__ __forceinline__ void helper(const uint16_t* __restrict__ x, const flo
         *reinterpret_cast<uint2*>(codes + m * Ks + q * 8) = pk;
       }
     }
+    // step u (K positions [u * 8 HT, (u + 1) * 8 HT)) of this wavefront is in LDS
+    if (lane == 0)
+      __hip_atomic_fetch_add(ready + u, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
-  __syncthreads();  // (2)
 
   for (int t = 0; t < T; ++t) {
     const int tile = first + t;
@@ -351,7 +388,7 @@ __device__ __forceinline__ void helper(const uint16_t* __restrict__ x, const flo
 }
 
 // The two roles run as separate wavefront-uniform branches.  Both execute the
-// same sequence of workgroup barriers: two in the prologue, then one per tile
+// same sequence of workgroup barriers: one in the prologue, then one per tile
 // (the streamers after writing a tile's partials, the helpers before reading
 // them).  The partial-sum buffers are double-buffered by tile parity: a buffer
 // is rewritten two tiles later, after the helpers have passed the barrier of
@@ -371,19 +408,24 @@ __global__ __launch_bounds__(64 * (S + (NPH == 2 ? 4 : 8))) void w8a8_linear_fus
   float* amax_part = reinterpret_cast<float*>(smem + L.amax);
   float* qp = reinterpret_cast<float*>(smem + L.qp);
   int* cnt = reinterpret_cast<int*>(smem + L.cnt);
+  int* ready = reinterpret_cast<int*>(smem + L.ready);
   const int Ks = K + 16;  // padded LDS row: spreads the token rows over the banks
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wavefront
-  if (tid == 0) *cnt = 0;  // ordered before use by the first barrier
+  if (tid < 4) {  // ordered before use by the first barrier
+    if (tid == 0) *cnt = 0;
+    ready[tid] = 0;
+  }
   const int G = gridDim.x;  // <= tiles, so every workgroup has at least one tile
   const int first = (int)((int64_t)blockIdx.x * tiles / G);
   const int T = (int)((int64_t)(blockIdx.x + 1) * tiles / G) - first;
   if (wave < S) {
-    streamer<MT, S, NPH, Var::NBUF>(wq, wscale, N, K, first, T, wave, lane, codes, Ks, red, wsl);
+    streamer<MT, S, NPH, Var::NBUF, Var::NH>(wq, wscale, N, K, first, T, wave, lane, codes, Ks,
+                                             red, wsl, ready);
   } else {
     helper<MT, S, Var::NH, Var::UP>(x, s, M, N, K, first, T, tid - 64 * S, wave - S, lane, codes,
-                                    Ks, red, wsl, amax_part, qp, cnt, y, acc_out);
+                                    Ks, red, wsl, amax_part, qp, cnt, ready, y, acc_out);
   }
 }
 
