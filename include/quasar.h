@@ -15,10 +15,13 @@
  *     CUDA memory) unless stated otherwise; sizes are element counts.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
  *     validate their arguments on the host, then enqueue kernels on `stream`
- *     and return without synchronising.  Nothing is allocated and no state is
- *     kept between calls: the caller owns every buffer, including workspaces
- *     sized by the *_workspace_bytes queries.  Two calls may run concurrently
- *     on different streams only with different workspaces.
+ *     and return without synchronising.  Nothing is allocated, and no state
+ *     is kept between calls apart from the launch counters of the wide linear
+ *     kernel (device words of this library, one per workgroup): the caller owns
+ *     every buffer, including workspaces sized by the *_workspace_bytes
+ *     queries.  Two calls may run concurrently
+ *     on different streams only with different workspaces (and see
+ *     quasar_w8a8_linear for the one kind of call that must not overlap).
  *   - Argument errors are reported before any launch, as a status code; the
  *     outputs are then untouched.  A launch failure returns QUASAR_ERR_HIP.
  *     Device faults surface at the caller's next synchronisation.
@@ -118,9 +121,11 @@ quasar_status quasar_quantize_activations(const uint16_t* x, const float* s, int
 
 /* Workspace bytes quasar_w8a8_linear needs for this shape.  Pure host
  * function, deterministic in (M, N, K).  It is 0 for an empty call and for
- * verify windows of M <= 8 tokens with K <= 12288, which run as a single
- * kernel; other shapes stage the quantized activations (and, when K is split
- * across workgroups, INT32 partial sums) in the workspace. */
+ * verify windows of M <= 8 tokens with K <= 12288, which keep the quantized
+ * activations in on-chip memory; other shapes stage the quantized activations
+ * and the INT32 partial sums of output groups shared by two workgroups in the
+ * workspace (M*K + 4*M bytes plus 4 KB per 16-token block and compute unit,
+ * each part rounded up to 256). */
 size_t quasar_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Diagnostic: the kernel(s) quasar_w8a8_linear launches for an M x N x K
@@ -151,11 +156,18 @@ const char* quasar_w8a8_kernel_name(int64_t M, int64_t N, int64_t K);
  *   workspace, workspace_bytes: device scratch of at least
  *            quasar_w8a8_workspace_bytes(M, N, K) bytes, 256-byte aligned; any
  *            contents; overwritten.  May be NULL when that size is 0.
- * M <= 8 with K <= 12288 runs as one kernel launch (quantize, GEMM and dequant
- * fused); other shapes launch the activation quantizer, the GEMM and, for
- * split K, a reduce kernel, all on `stream`.
+ * Every shape runs as one kernel launch on `stream` (quantize, GEMM and
+ * dequant fused).  Windows of M <= 8 tokens with K <= 12288 use a kernel that
+ * keeps the codes in on-chip memory.  Other shapes use a kernel whose grid is
+ * one workgroup per compute unit, all resident at once: its workgroups hand the
+ * quantized token rows and partial sums to each other through the workspace
+ * and through per-workgroup launch counters kept in the library's device
+ * memory.  Two such calls on one device must not run at the same time (each
+ * needs every compute unit); calls ordered on one stream never do.  The result
+ * does not depend on the workspace's previous contents.
  * M == 0 or N == 0 is a no-op.  Errors: INVALID_ARG, UNSUPPORTED (M or K
- * beyond the limits), WORKSPACE, HIP.
+ * beyond the limits, or a device with fewer than M compute units),
+ * WORKSPACE, HIP.
  */
 quasar_status quasar_w8a8_linear(const uint16_t* x, const float* s, const int8_t* wq,
                                  const float* w_scale, int64_t M, int64_t N, int64_t K,

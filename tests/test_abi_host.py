@@ -52,7 +52,7 @@ def test_status_strings(L):
     for code in range(5):
         assert L.quasar_status_string(code).decode().startswith("QUASAR_")
     assert b"UNKNOWN" in L.quasar_status_string(99)
-    assert L.quasar_abi_version() == 3
+    assert L.quasar_abi_version() == 4
 
 
 def test_workspace_queries_are_pure_host_and_monotone(L):
@@ -62,7 +62,7 @@ def test_workspace_queries_are_pure_host_and_monotone(L):
     # the one-launch kernel (M <= 8, K <= 12288) needs no workspace
     for M, N, K in [(6, 6144, 4096), (8, 4096, 12288), (1, 16, 16), (6, 151936, 4096)]:
         assert L.quasar_w8a8_workspace_bytes(M, N, K) == 0
-    # the multi-kernel path stages the quantized activations
+    # the wide path stages the quantized activations and INT32 partial sums
     for M, N, K in [(96, 4096, 12288), (9, 16, 16), (128, 151936, 4096), (6, 64, 16384)]:
         b = L.quasar_w8a8_workspace_bytes(M, N, K)
         assert b >= M * K + 4 * M and b % 256 == 0
@@ -147,9 +147,12 @@ def test_kernel_name_names_the_launch_plan(L):
     assert name(6, 4096, 12288) == "w8a8_linear_fused_kernel<6, 4, 6>"
     assert name(1, 16, 16) == "w8a8_linear_fused_kernel<2, 4, 2>"
     assert name(8, 4096, 8192) == "w8a8_linear_fused_kernel<8, 4, 4>"
-    # wider windows: quantizer + GEMM over ceil(M / 16) token blocks
-    assert name(48, 4096, 4096).startswith("quantize_rows + gemm_w8a8_kernel<3>")
-    assert name(96, 4096, 12288).startswith("quantize_rows + gemm_w8a8_kernel<6>")
+    # wider windows (or K > 12288): one launch over ceil(M / 16) token blocks
+    assert name(48, 4096, 4096) == "w8a8_linear_wide_kernel<3>"
+    assert name(96, 4096, 12288) == "w8a8_linear_wide_kernel<6>"
+    assert name(9, 16, 16) == "w8a8_linear_wide_kernel<1>"
+    assert name(6, 64, 16384) == "w8a8_linear_wide_kernel<1>"
+    assert name(128, 151936, 4096) == "w8a8_linear_wide_kernel<8>"
     # invalid or unsupported sizes
     assert name(0, 16, 16) == "" and name(6, 16, 17) == "" and name(129, 16, 16) == ""
 

@@ -64,6 +64,12 @@ RAGGED = [
     (4, 520, 12288),
     # many tiles per compute unit: uneven contiguous tile ranges per workgroup
     (6, 9000, 1024), (2, 8336, 80), (8, 12000, 256),
+    # wide windows: every 16-token block count (1..8), ragged N and K, groups
+    # shared by several workgroups (partial sums), and ranges that are empty
+    (9, 100, 1024), (20, 64, 4096), (33, 1000, 2112), (64, 520, 4096), (80, 260, 1040),
+    (112, 77, 3072), (128, 300, 4096), (16, 64, 4096), (40, 8000, 512), (24, 6144, 4096),
+    # K beyond the one-launch small-window kernel, up to the largest supported K
+    (6, 64, 16384), (1, 40, 65536), (50, 48, 20480),
 ]
 
 
@@ -139,15 +145,63 @@ def test_lm_head_full_size_sampled():
     check_against_oracle(x, s, w, y, acc, cols)
 
 
-def test_repeated_calls_are_bit_identical():
-    """Split-K partials and LDS reductions are integer sums: no run-to-run drift."""
-    announce("linear_determinism", 5, 33, 12288)
-    x, w, s = synth.linear_case(5, 12288, 33, (4, 0))
+@pytest.mark.parametrize("M,N,K", [(5, 33, 12288), (96, 300, 4096), (48, 6144, 4096)])
+def test_repeated_calls_are_bit_identical(M, N, K):
+    """Partial sums shared between workgroups and LDS reductions are integer
+    sums, and every launch of the wide kernel waits for its own token rows:
+    no run-to-run drift, including back-to-back launches on one workspace."""
+    announce("linear_determinism", M, N, K)
+    x, w, s = synth.linear_case(M, K, N, (4, M))
     wq, sw = binding.quasar_quantize_weights(dev_bf16(w), dev(s))
     xd, sd = dev_bf16(x), dev(s)
-    ws = binding.new_workspace(binding.workspace_bytes_linear(5, 33, 12288))
+    ws = binding.new_workspace(binding.workspace_bytes_linear(M, N, K))
     first = binding.quasar_w8a8_linear(xd, sd, wq, sw, workspace=ws).clone()
     for _ in range(50):
         again = binding.quasar_w8a8_linear(xd, sd, wq, sw, workspace=ws)
         assert torch.equal(again.view(torch.int16), first.view(torch.int16))
+    y = host_bf16(first)
+    ref = orc.w8a8_linear_rows(x, s, w)
+    assert np.array_equal(y, ref["y"])
+
+
+def test_alternating_inputs_on_one_workspace():
+    """Back-to-back launches on one workspace with two different inputs of the
+    same shape: every launch must read the token rows and partial sums of its
+    own input, never those a previous launch left at the same addresses."""
+    M, N, K = 96, 700, 4096
+    ws = binding.new_workspace(binding.workspace_bytes_linear(M, N, K))
+    sets = []
+    for i in range(2):
+        x, w, s = synth.linear_case(M, K, N, (6, i))
+        wq, sw = binding.quasar_quantize_weights(dev_bf16(w), dev(s))
+        sets.append((x, s, w, dev_bf16(x), dev(s), wq, sw))
+    announce("linear_alternating", M, N, K)
+    outs = []
+    for r in range(20):
+        x, s, w, xd, sd, wq, sw = sets[r % 2]
+        outs.append(binding.quasar_w8a8_linear(xd, sd, wq, sw, workspace=ws))
+    torch.cuda.synchronize()
+    refs = [orc.w8a8_linear_rows(x, s, w)["y"] for x, s, w, *_ in sets]
+    for r, y in enumerate(outs):
+        assert np.array_equal(host_bf16(y), refs[r % 2]), f"launch {r}"
+
+
+def test_interleaved_wide_shapes_on_one_stream():
+    """Wide launches of different token-block counts and shapes, back to back
+    with no synchronisation between them, each against the oracle; a second
+    round with new activations checks that no launch reads the rows of the
+    one before it."""
+    cases = [(48, 500, 4096), (96, 130, 2048), (17, 2000, 1024), (128, 64, 4096), (9, 40, 12288)]
+    for rnd in range(2):
+        outs = []
+        for i, (M, N, K) in enumerate(cases):
+            announce("linear_interleaved", rnd, M, N, K)
+            x, w, s = synth.linear_case(M, K, N, (5, rnd, i))
+            wq, sw = binding.quasar_quantize_weights(dev_bf16(w), dev(s))
+            acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+            y = binding.quasar_w8a8_linear(dev_bf16(x), dev(s), wq, sw, acc_out=acc)
+            outs.append((x, s, w, y, acc))
+        torch.cuda.synchronize()
+        for x, s, w, y, acc in outs:
+            check_against_oracle(x, s, w, host_bf16(y), host(acc))
 

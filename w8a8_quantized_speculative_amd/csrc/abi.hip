@@ -38,7 +38,7 @@ const char* quasar_status_string(quasar_status status) {
   return "QUASAR_ERR_UNKNOWN";
 }
 
-int quasar_abi_version(void) { return 3; }
+int quasar_abi_version(void) { return 4; }
 
 quasar_status quasar_quantize_weights(const uint16_t* w, const float* s, int64_t N, int64_t K,
                                       int8_t* wq, float* w_scale, void* stream) {
@@ -76,28 +76,15 @@ size_t quasar_packed_weight_bytes(int64_t N, int64_t K) {
 size_t quasar_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || check_k(K) != QUASAR_OK || M > QUASAR_MAX_M || N > kMaxRowsPerCall)
     return 0;
-  return plan_linear(M, N, K).bytes;
+  if (fused_supported(M, K)) return 0;
+  return plan_wide(M, N, K, kWideMaxGrid).bytes;
 }
 
 const char* quasar_w8a8_kernel_name(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || check_k(K) != QUASAR_OK || M > QUASAR_MAX_M || N > kMaxRowsPerCall)
     return "";
-  const LinearPlan p = plan_linear(M, N, K);
-  if (p.fused) return fused_kernel_name(plan_fused(M, N, K));
-  static const char* const names[2][8] = {
-      {"quantize_rows + gemm_w8a8_kernel<1>", "quantize_rows + gemm_w8a8_kernel<2>",
-       "quantize_rows + gemm_w8a8_kernel<3>", "quantize_rows + gemm_w8a8_kernel<4>",
-       "quantize_rows + gemm_w8a8_kernel<5>", "quantize_rows + gemm_w8a8_kernel<6>",
-       "quantize_rows + gemm_w8a8_kernel<7>", "quantize_rows + gemm_w8a8_kernel<8>"},
-      {"quantize_rows + gemm_w8a8_kernel<1> + splitk_dequant",
-       "quantize_rows + gemm_w8a8_kernel<2> + splitk_dequant",
-       "quantize_rows + gemm_w8a8_kernel<3> + splitk_dequant",
-       "quantize_rows + gemm_w8a8_kernel<4> + splitk_dequant",
-       "quantize_rows + gemm_w8a8_kernel<5> + splitk_dequant",
-       "quantize_rows + gemm_w8a8_kernel<6> + splitk_dequant",
-       "quantize_rows + gemm_w8a8_kernel<7> + splitk_dequant",
-       "quantize_rows + gemm_w8a8_kernel<8> + splitk_dequant"}};
-  return names[p.splits > 1 ? 1 : 0][p.mb - 1];
+  if (fused_supported(M, K)) return fused_kernel_name(plan_fused(M, N, K));
+  return wide_kernel_name(plan_wide(M, N, K, kWideMaxGrid).mb);
 }
 
 quasar_status quasar_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
@@ -120,19 +107,15 @@ quasar_status quasar_w8a8_linear(const uint16_t* x, const float* s, const int8_t
   if (!aligned(x, 16) || !aligned(s, 16) || !aligned(wq, 16) || !aligned(w_scale, 4) ||
       !aligned(y, 2) || (acc_out && !aligned(acc_out, 4)))
     return QUASAR_ERR_INVALID_ARG;
-  const LinearPlan p = plan_linear(M, N, K);
   hipStream_t hs = (hipStream_t)stream;
-  if (p.fused)  // one launch, no workspace
+  if (fused_supported(M, K))  // one launch, no workspace
     return hip_status(launch_fused(plan_fused(M, N, K), x, s, wq, w_scale, y, acc_out, hs));
+  WidePlan p = plan_wide(M, N, K, kWideMaxGrid);
   if (!workspace || workspace_bytes < p.bytes || !aligned(workspace, kWsAlign))
     return QUASAR_ERR_WORKSPACE;
-  char* ws = static_cast<char*>(workspace);
-  int8_t* qx = reinterpret_cast<int8_t*>(ws + p.off_qx);
-  float* sx = reinterpret_cast<float*>(ws + p.off_sx);
-  int32_t* partials = p.splits > 1 ? reinterpret_cast<int32_t*>(ws + p.off_partials) : nullptr;
-  hipError_t e = launch_quantize_activations(x, s, M, K, qx, sx, nullptr, hs);
-  if (e != hipSuccess) return QUASAR_ERR_HIP;
-  return hip_status(launch_gemm(p, qx, sx, wq, w_scale, y, acc_out, partials, hs));
+  p.grid = wide_grid_for_current_device();
+  if (p.grid < M) return QUASAR_ERR_UNSUPPORTED;  // one resident workgroup per token row
+  return hip_status(launch_wide(p, x, s, wq, w_scale, y, acc_out, workspace, hs));
 }
 
 size_t quasar_accept_workspace_bytes(int64_t B, int64_t k, int64_t V) {

@@ -41,32 +41,38 @@ hipError_t launch_fused(const FusedPlan& p, const uint16_t* x, const float* s, c
                         const float* w_scale, uint16_t* y, int32_t* acc_out, hipStream_t st);
 
 // ---------------------------------------------------------------------------
-// Multi-kernel W8A8 linear plan (any M <= 128): activation quantize kernel,
-// then the GEMM kernel below, then (only when K is split) a reduce kernel.
-//
-// The output is cut into 16-channel tiles (one MFMA row block).  K is cut into
-// 64-wide chunks (one MFMA K step).  A workgroup owns one (tile, K-split) pair;
-// its `waves` wavefronts each own up to `chunks_per_wave` consecutive chunks of
-// that split, stream the matching INT8 weight rows straight into MFMA operand
-// registers, and reduce their partial sums in LDS.  When a tile is split
-// across `splits` workgroups, each writes its exact INT32 partial to the
-// workspace and a reduce kernel sums the partials and dequantizes.
+// Wide-window plan (9 <= M <= 128, or K > 12288): one launch of a persistent
+// grid (one workgroup per compute unit, all resident at once) that quantizes
+// the token rows into the workspace, passes a one-way grid barrier, and
+// streams (group of 64 channels, 256 K positions) items in equal contiguous
+// ranges per workgroup, finishing groups shared by two ranges through INT32
+// partial sums in the workspace.
 // ---------------------------------------------------------------------------
-struct LinearPlan {
+constexpr int kWideMaxGrid = 256;
+
+struct WidePlan {
   int64_t M, N, K;
-  int mb;               // 16-token column blocks: ceil(M / 16)
-  int tiles;            // ceil(N / 16)
-  int nch;              // ceil(K / 64)
-  int chunks_per_wave;  // compile-time unroll of the weight stream (kernel template)
-  int splits;           // workgroups per tile along K
-  int chunks_per_split;
-  int waves;            // wavefronts per workgroup
-  bool fused;           // the one-launch kernel applies (then no workspace)
+  int mb;      // 16-token blocks: ceil(M / 16), 1..8
+  int tiles;   // ceil(N / 16)
+  int nch;     // ceil(K / 64)
+  int groups;  // ceil(tiles / 4)
+  int P;       // items per group: ceil(nch / 4)
+  int U;       // groups * P
+  int grid;    // workgroups (<= kWideMaxGrid, >= M)
+  int lds;     // dynamic LDS bytes
   // workspace layout (byte offsets)
   size_t off_qx, off_sx, off_partials, bytes;
 };
 
-LinearPlan plan_linear(int64_t M, int64_t N, int64_t K);
+// `grid` only enters the launch; the workspace is sized for kWideMaxGrid.
+WidePlan plan_wide(int64_t M, int64_t N, int64_t K, int grid);
+const char* wide_kernel_name(int mb);
+int wide_lds_bytes(int mb);
+// Workgroups of a wide launch on the current device (0: cannot run there).
+int wide_grid_for_current_device();
+hipError_t launch_wide(const WidePlan& p, const uint16_t* x, const float* s, const int8_t* wq,
+                       const float* w_scale, uint16_t* y, int32_t* acc_out, void* workspace,
+                       hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // Accept plan: each logits row is cut into `chunks` pieces of `chunk_len`.
@@ -87,10 +93,6 @@ hipError_t launch_quantize_weights(const uint16_t* w, const float* s, int64_t N,
 
 hipError_t launch_quantize_activations(const uint16_t* x, const float* s, int64_t M, int64_t K,
                                        int8_t* qx, float* sx, float* xs_out, hipStream_t st);
-
-hipError_t launch_gemm(const LinearPlan& p, const int8_t* qx, const float* sx, const int8_t* wq,
-                       const float* w_scale, uint16_t* y, int32_t* acc_out, int32_t* partials,
-                       hipStream_t st);
 
 hipError_t launch_accept(const AcceptPlan& p, const uint16_t* logits, const int32_t* draft,
                          float temperature, const float* uniforms, int32_t* accept_len,

@@ -1,0 +1,745 @@
+// One-launch W8A8 SmoothQuant linear for wide verify windows (9..128 tokens,
+// or any window with K > 12288): online smoothing and dynamic per-token INT8
+// quantization of the BF16 activations, the INT8 x INT8 -> INT32 product on
+// the matrix cores against the resident INT8 weights, and BF16 dequantization
+// [Quasar, pt page §2 execution pipeline items 2-4; zh page §2 items 2-3].
+//
+// A wide window is too large for the one-launch kernel of small windows,
+// which keeps the whole quantized activation matrix in every compute unit's
+// LDS (96 tokens x 4096 K positions is 384 KB; LDS is 160 KB).  Here the
+// quantized activations go to global memory once and are streamed through a
+// small LDS ring next to the weights:
+//
+//   1. Rows.  Workgroup m < M smooths and quantizes token row m
+//      (xs = RN32(x * s), absmax, scale, codes) into the workspace, then
+//      publishes a per-workgroup flag.  Every workgroup waits until the M row
+//      flags are set -- a one-way grid barrier.  Meanwhile its streamer
+//      wavefronts already have their first weights in flight.
+//   2. Items.  The output channels are cut into groups of 4 tiles of 16
+//      channels (64 channels) and K into items of 256 positions (4 chunks of
+//      64, one per streamer wavefront).  The (group, item) sequence, group
+//      major, is divided into G equal contiguous ranges, one per workgroup
+//      (stream-K): every workgroup streams the same number of weight bytes
+//      whatever N and K are.
+//   3. Per item, each of the 4 streamer wavefronts loads one 1 KB chunk of
+//      each of the group's 4 tiles (16 KB in flight per wavefront over 4
+//      register buffers) and multiplies it against the item's activation
+//      codes: 16 x 64 fragments of the M-token matrix, one per 16-token
+//      block, read from the LDS ring and reused for the 4 tiles.  Two loader
+//      wavefronts fill the ring with direct-to-LDS buffer loads from the
+//      workspace, several items ahead.
+//   4. At the end of a group (or of the range) the streamers hand their
+//      partial sums to two epilogue wavefronts, one tile at a time through a
+//      double-buffered LDS area.  The epilogue sums the 4 partials (exact
+//      INT32) and either dequantizes to BF16, or -- for a group whose first
+//      item belongs to another workgroup -- stores the INT32 partial to the
+//      workspace and raises a flag.  The workgroup that owns a group's first
+//      item finishes that group, adding the partials of the workgroups that
+//      own its later items.
+//
+// Synchronisation inside a workgroup uses monotonic LDS counters (no
+// workgroup barrier after the first), so a stalled role never stalls
+// another.  Across workgroups it uses one flag word per workgroup in module
+// memory: each launch bumps every workgroup's flag by exactly one, so a flag
+// equal to its owner's pre-launch value plus one marks this launch's data.
+// The grid is one workgroup per compute unit and all of them must be resident
+// at once; every wait is bounded, so a grid that cannot be co-resident ends
+// (with undefined outputs) instead of hanging.
+#include "quasar_device.hpp"
+#include "quasar_internal.hpp"
+
+namespace quasar {
+
+// Per-workgroup launch counters: row flags (the workgroup's token row is in
+// the workspace) and partial flags (its partial sum of a shared group is).
+// Zero at module load; launch e (0-based) leaves both at e + 1 for every
+// workgroup b < grid (the partial flag only for workgroups that wrote one).
+__device__ uint32_t g_wide_row_flag[kWideMaxGrid];
+__device__ uint32_t g_wide_part_flag[kWideMaxGrid];
+
+namespace {
+
+constexpr int kS = 4;          // streamer wavefronts (one 64-wide K chunk each per item)
+constexpr int kTG = 4;         // 16-channel tiles per group
+constexpr int kNBUF = 4;       // items of weights in flight per streamer (4 x 4 KB)
+constexpr int kLoadWaves = 2;  // loader wavefronts
+constexpr int kEpiWaves = 2;   // epilogue wavefronts
+constexpr int kHelpers = kLoadWaves + kEpiWaves;
+constexpr int kThreads = 64 * (kS + kHelpers);
+constexpr int kRowPieces = 8;  // 8-element pieces per helper thread kept in registers
+constexpr int kSpinLds = 1 << 22;
+constexpr int kSpinGlobal = 1 << 20;
+
+// s_waitcnt immediate for "at most n vector-memory operations outstanding"
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt at their
+// maxima so they are not waited for).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Ring depth by 16-token blocks: the ring (NW windows of 4 MB KB) and the
+// partial-sum area (2 x 4 MB KB) stay within 144 KB of LDS.
+template <int MB>
+struct Wide {
+  static constexpr int NW = MB <= 3 ? 8 : (MB == 4 ? 6 : (MB == 5 ? 5 : (MB == 6 ? 4 : (MB == 7 ? 3 : 2))));
+  static constexpr int FRAGS = kS * MB;          // 1 KB fragments per window (item)
+  static constexpr int NF = FRAGS / kLoadWaves;  // fragments per loader wavefront
+  static constexpr int RING = NW * FRAGS * 1024;
+  static constexpr int RED = 2 * kS * MB * 1024;
+  static constexpr int SYNC = 256;
+  static constexpr int LDS = RING + RED + SYNC;
+};
+static_assert(Wide<6>::LDS <= 150 * 1024 && Wide<8>::LDS <= 150 * 1024 &&
+                  Wide<4>::LDS <= 150 * 1024 && Wide<5>::LDS <= 150 * 1024,
+              "LDS budget");
+static_assert((Wide<3>::NW - 1) * Wide<3>::NF <= 63 && (Wide<6>::NW - 1) * Wide<6>::NF <= 63 &&
+                  (Wide<4>::NW - 1) * Wide<4>::NF <= 63 && (Wide<8>::NW - 1) * Wide<8>::NF <= 63,
+              "loader waits fit the 6-bit vmcnt");
+
+// LDS synchronisation words (int indices into the SYNC area)
+enum : int {
+  kFilled = 0,     // [8] per ring slot: loader wavefronts that filled it (monotonic)
+  kConsumed = 8,   // [8] per ring slot: streamers that finished reading it
+  kRedReady = 16,  // [2] per parity: streamers that published a tile round
+  kRedFree = 18,   // [2] per parity: epilogue wavefronts that consumed a round
+  kRowDone = 20,   // helper wavefronts whose row codes are stored
+  kAmaxCnt = 21,   // helper wavefronts that published their row maximum
+  kGate = 22,      // 1 once every token row of the launch is in the workspace
+  kPartDone = 23,  // epilogue wavefronts whose partial sums are stored
+  kAmax = 24,      // float [4] per-helper row maxima
+  kSyncWords = 32
+};
+
+// LDS word read for the wavefronts that also issue direct-to-LDS loads: the
+// compiler cannot tell these words from the ring the loads write, and would
+// wait for every load in flight before a plain read.  LDS executes a
+// wavefront's accesses in order, so no wait is needed.
+__device__ __forceinline__ int lds_read_asm(const int* p) {
+  const uint32_t addr = (uint32_t)reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const int*)p);
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+
+// LDS counter increment for the same wavefronts (no compiler-inserted wait for
+// the direct-to-LDS loads in flight).
+__device__ __forceinline__ void lds_add_asm(int* p, int v) {
+  const uint32_t addr = (uint32_t)reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) int*)p);
+  asm volatile("ds_add_u32 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
+__device__ __forceinline__ int lds_load(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+__device__ __forceinline__ void lds_add(int* p, int v) {
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Stores another workgroup reads during the same launch: device-scope
+// (write-through) stores, so a workgroup on another XCD -- whose L2 does not
+// hold the line, as every launch starts with invalidated caches and the line is
+// read only after its flag -- fetches the new value.
+__device__ __forceinline__ void store8_device(void* p, uint2 v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p),
+                     (uint64_t)v.x | ((uint64_t)v.y << 32), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store16_device(int32_t* p, v4i v) {
+  store8_device(p, make_uint2((uint32_t)v.x, (uint32_t)v.y));
+  store8_device(p + 2, make_uint2((uint32_t)v.z, (uint32_t)v.w));
+}
+
+// Wait until every store this wavefront issued has completed, i.e. is visible
+// device-wide for the device-scope stores above; flags are raised after it.
+__device__ __forceinline__ void wait_stores_done() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  asm volatile("" ::: "memory");
+}
+
+// Bounded wait until an LDS counter reaches `target` (plain-read wavefronts).
+__device__ __forceinline__ void lds_wait_ge(const int* p, int target) {
+  for (int spin = 0; spin < kSpinLds; ++spin) {
+    if (lds_load(p) >= target) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");  // later LDS reads stay below the wait
+}
+
+// Item ranges: the (group, item) sequence of U items is split into G equal
+// contiguous ranges.
+__host__ __device__ inline int range_start(int b, int U, int G) {
+  return (int)((int64_t)b * U / G);
+}
+
+// ---------------------------------------------------------------------------
+// Streamer role: weights -> MFMA against the ring -> per-tile partial rounds.
+// ---------------------------------------------------------------------------
+template <int MB>
+__device__ __forceinline__ void wide_streamer(const int8_t* __restrict__ wq, int tiles, int nch,
+                                              int P, int i0, int n, int w, int lane,
+                                              const char* ring, int32_t* red, int* sync) {
+  using C = Wide<MB>;
+  v4i a[kNBUF][kTG];
+  // issue pointer: item i0 + j as (group, item within group)
+  int ig = i0 / P, ip = i0 - (i0 / P) * P;
+  int issued = 0;
+  const int voff = lane * 16;
+  auto issue = [&](int bb) {
+    const bool live = issued < n;
+    const int c = ip * kS + w;
+#pragma unroll
+    for (int tt = 0; tt < kTG; ++tt) {
+      const int t = ig * kTG + tt;
+      const bool ok = live && t < tiles && c < nch;
+      const buffer_rsrc rs =
+          make_rsrc(wq + ((size_t)(ok ? t : 0) * nch + (ok ? c : 0)) * 1024, ok ? 1024u : 0u);
+      a[bb][tt] = load16<kNonTemporal>(rs, voff);
+    }
+    ++issued;
+    if (++ip == P) {
+      ip = 0;
+      ++ig;
+    }
+  };
+
+  __syncthreads();  // (1) the row quantizer's activation loads are queued first
+#pragma unroll
+  for (int bb = 0; bb < kNBUF; ++bb) issue(bb);
+  __builtin_amdgcn_sched_barrier(0);  // keep the loop below from rotating into the issues
+
+  v4i acc[kTG][MB];
+#pragma unroll
+  for (int tt = 0; tt < kTG; ++tt)
+#pragma unroll
+    for (int tb = 0; tb < MB; ++tb) acc[tt][tb] = (v4i){0, 0, 0, 0};
+
+  int cp = i0 - (i0 / P) * P;  // consume pointer: item within its group
+  int round = 0;
+  for (int jb = 0; jb < n; jb += kNBUF) {
+#pragma unroll
+    for (int bb = 0; bb < kNBUF; ++bb) {
+      const int j = jb + bb;
+      if (j < n) {
+        const int slot = j % C::NW;
+        lds_wait_ge(sync + kFilled + slot, kLoadWaves * (j / C::NW + 1));
+        const char* frag = ring + (slot * C::FRAGS + w * MB) * 1024 + lane * 16;
+        v4i bf[MB];
+#pragma unroll
+        for (int tb = 0; tb < MB; ++tb) bf[tb] = *reinterpret_cast<const v4i*>(frag + tb * 1024);
+#pragma unroll
+        for (int tt = 0; tt < kTG; ++tt)
+#pragma unroll
+          for (int tb = 0; tb < MB; ++tb) acc[tt][tb] = mfma_i8_16x16x64(a[bb][tt], bf[tb], acc[tt][tb]);
+        // the fragment reads above precede this count in LDS order
+        asm volatile("" ::: "memory");
+        if (lane == 0) lds_add(sync + kConsumed + slot, 1);
+      }
+      issue(bb);  // item j + kNBUF, or zeros past the range
+      if (j < n) {
+        const bool group_end = cp == P - 1 || j == n - 1;
+        if (group_end) {
+#pragma unroll
+          for (int tt = 0; tt < kTG; ++tt) {
+            const int par = round & 1;
+            if (round >= 2) lds_wait_ge(sync + kRedFree + par, kEpiWaves * (round >> 1));
+            int32_t* dst = red + ((par * kS + w) * MB) * 256 + lane * 4;
+#pragma unroll
+            for (int tb = 0; tb < MB; ++tb) {
+              *reinterpret_cast<v4i*>(dst + tb * 256) = acc[tt][tb];
+              acc[tt][tb] = (v4i){0, 0, 0, 0};
+            }
+            asm volatile("" ::: "memory");
+            if (lane == 0) lds_add(sync + kRedReady + par, 1);
+            ++round;
+          }
+        }
+        if (++cp == P) cp = 0;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Helper prologue: smooth and quantize token row `m` into the workspace.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void quantize_row_compute(const uint16_t* __restrict__ x,
+                                                     const float* __restrict__ s, int m, int K,
+                                                     int ht, int hw, int lane, const v4i (&xv)[kRowPieces],
+                                                     const v4i (&sv)[kRowPieces][2], bool in_regs,
+                                                     int8_t* __restrict__ qx, float* __restrict__ sx,
+                                                     int* sync) {
+  const int units = K >> 3;
+  const buffer_rsrc xrs = make_rsrc(x + (size_t)m * K, (uint32_t)K * 2u);
+  const buffer_rsrc srs = make_rsrc(s, (uint32_t)K * 4u);
+  auto piece = [&](const v4i& xq, const v4i& s0, const v4i& s1, float v[8]) {
+    const float sf[8] = {__int_as_float(s0.x), __int_as_float(s0.y), __int_as_float(s0.z),
+                         __int_as_float(s0.w), __int_as_float(s1.x), __int_as_float(s1.y),
+                         __int_as_float(s1.z), __int_as_float(s1.w)};
+    const uint32_t w4[4] = {(uint32_t)xq.x, (uint32_t)xq.y, (uint32_t)xq.z, (uint32_t)xq.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t bits = (e & 1) ? (w4[e >> 1] >> 16) : (w4[e >> 1] & 0xffffu);
+      v[e] = bf16_to_f32(bits) * sf[e];  // xs = RN32(x * s)
+    }
+  };
+  // absmax of the row (pieces past K read as zero)
+  float amax = 0.0f;
+  if (in_regs) {
+#pragma unroll
+    for (int u = 0; u < kRowPieces; ++u) {
+      float v[8];
+      piece(xv[u], sv[u][0], sv[u][1], v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    }
+  } else {
+    for (int q = ht; q < units; q += 64 * kHelpers) {
+      float v[8];
+      piece(load16(xrs, q * 16), load16(srs, q * 32), load16(srs, q * 32 + 16), v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    }
+  }
+  const float wmax = wave_max_nonneg(amax);
+  float* amax_part = reinterpret_cast<float*>(sync + kAmax);
+  if (lane == 0) {
+    amax_part[hw] = wmax;
+    asm volatile("" ::: "memory");
+    lds_add(sync + kAmaxCnt, 1);
+  }
+  lds_wait_ge(sync + kAmaxCnt, kHelpers);
+  float row_amax = 0.0f;
+#pragma unroll
+  for (int h = 0; h < kHelpers; ++h) row_amax = fmaxf(row_amax, amax_part[h]);
+  const QParams qp = row_qparams(row_amax);
+
+  int8_t* qrow = qx + (size_t)m * K;
+  auto emit = [&](int q, const float v[8]) {
+    uint32_t cb[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cb[e] = quant_code_biased(v[e], qp.inv);
+    uint2 pk;
+    pk.x = pack4_low_bytes(cb[0], cb[1], cb[2], cb[3]);
+    pk.y = pack4_low_bytes(cb[4], cb[5], cb[6], cb[7]);
+    store8_device(qrow + q * 8, pk);
+  };
+  if (in_regs) {
+#pragma unroll
+    for (int u = 0; u < kRowPieces; ++u) {
+      const int q = ht + u * 64 * kHelpers;
+      if (q < units) {
+        float v[8];
+        piece(xv[u], sv[u][0], sv[u][1], v);
+        emit(q, v);
+      }
+    }
+  } else {
+    for (int q = ht; q < units; q += 64 * kHelpers) {
+      float v[8];
+      piece(load16(xrs, q * 16), load16(srs, q * 32), load16(srs, q * 32 + 16), v);
+      emit(q, v);
+    }
+  }
+  if (ht == 0)
+    __hip_atomic_store(sx + m, qp.scale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// Loader role: fill ring slots with the item's activation fragments.
+// Fragment f = jc * MB + tb of an item holds token block tb at K chunk
+// (item * 4 + jc): lane l = 16 g + r reads 16 codes of token 16 tb + r at K
+// positions 64 c + 16 g, and the direct-to-LDS load stores them at l * 16.
+// Token rows >= M read as zero (buffer bound); K positions past K read the
+// next row's codes or zero, which meet zero weights.
+// ---------------------------------------------------------------------------
+template <int MB>
+__device__ __forceinline__ void wide_loader(const int8_t* __restrict__ qx, int M, int K, int P,
+                                            int i0, int n, int lw, int lane, char* ring,
+                                            int* sync) {
+  using C = Wide<MB>;
+  const buffer_rsrc qrs = make_rsrc(qx, (uint32_t)M * (uint32_t)K);
+  const int r16 = lane & 15, g4 = lane >> 4;
+  int ip = i0 - (i0 / P) * P;
+  int issued = 0, signaled = 0;
+  for (int spin = 0; signaled < n && spin < kSpinLds; ++spin) {
+    const bool can_issue =
+        issued < n &&
+        (issued < C::NW ||
+         lds_read_asm(sync + kConsumed + issued % C::NW) >= kS * (issued / C::NW));
+    if (can_issue) {
+      const int slot = issued % C::NW;
+      const int c0 = ip * kS;
+#pragma unroll
+      for (int k = 0; k < C::NF; ++k) {
+        const int f = lw + kLoadWaves * k;
+        const int jc = f / MB, tb = f % MB;
+        const int off = (tb * 16 + r16) * K + (c0 + jc) * 64 + g4 * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            qrs, (__attribute__((address_space(3))) void*)(ring + (slot * C::FRAGS + f) * 1024),
+            16, off, 0, 0, 0);
+      }
+      ++issued;
+      if (++ip == P) ip = 0;
+      continue;
+    }
+    if (issued > signaled) {
+      // the oldest window is complete once at most the later windows' loads
+      // are outstanding (loads complete in issue order)
+      switch (issued - signaled - 1) {
+        case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+        case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::NF)); break;
+        case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (C::NW > 2 ? C::NF : 0))); break;
+        case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * (C::NW > 3 ? C::NF : 0))); break;
+        case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * (C::NW > 4 ? C::NF : 0))); break;
+        case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5 * (C::NW > 5 ? C::NF : 0))); break;
+        case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6 * (C::NW > 6 ? C::NF : 0))); break;
+        default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(7 * (C::NW > 7 ? C::NF : 0))); break;
+      }
+      if (lane == 0) lds_add_asm(sync + kFilled + signaled % C::NW, 1);
+      ++signaled;
+    } else {
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Epilogue role.  Thread et (0..127) owns slots et + 128 k of a tile round:
+// slot s = 64 tb + l is lane l of token block tb, i.e. token 16 tb + l % 16 and
+// the 4 channels 4 (l / 16) .. + 3 of the tile (the MFMA result layout).  No
+// global load waits inside a round: the weight scales of a group are fetched
+// while the streamers are still on it, and the partial sums of the workgroups
+// that own the rest of a finalized group are summed once, before its rounds.
+// ---------------------------------------------------------------------------
+template <int MB>
+__device__ __forceinline__ void wide_epilogue(const float* __restrict__ wscale,
+                                              const float* __restrict__ sx, int M, int N, int P,
+                                              int U, int G, int b, int i0, int n, uint32_t e,
+                                              int et, int lane, const int32_t* red, int* sync,
+                                              int32_t* __restrict__ partials,
+                                              uint16_t* __restrict__ y,
+                                              int32_t* __restrict__ acc_out) {
+  constexpr int KS = (MB + 1) / 2;           // slots per thread and round
+  constexpr int kPartInts = kTG * MB * 256;  // one workgroup's partial sums
+  const int ln = et & 63;
+  float sxv[KS];
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    const int tok = ((et >> 6) + 2 * k) * 16 + (ln & 15);
+    sxv[k] = tok < M ? sx[tok] : 0.0f;
+  }
+  const buffer_rsrc wrs = make_rsrc(wscale, (uint32_t)N * 4u);
+  float ws[kTG][4];  // weight scales of the group's 4 channels per tile of this thread
+  auto fetch_ws = [&](int g) {
+#pragma unroll
+    for (int tt = 0; tt < kTG; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        ws[tt][i] = __int_as_float(load4(wrs, (((g * kTG + tt) * 16) + 4 * (ln >> 4) + i) * 4));
+  };
+  const int g_first = i0 / P, g_last = (i0 + n - 1) / P;
+  fetch_ws(g_first);
+  int round = 0;
+  for (int g = g_first; g <= g_last; ++g) {
+    const bool writer = g == g_first && i0 % P != 0;
+    const bool finalizer = !writer && (i0 + n) < (g + 1) * P;
+    v4i other[kTG][KS];  // partial sums of the other owners of group g
+#pragma unroll
+    for (int tt = 0; tt < kTG; ++tt)
+#pragma unroll
+      for (int k = 0; k < KS; ++k) other[tt][k] = (v4i){0, 0, 0, 0};
+    if (finalizer) {
+      // contributors: the non-empty workgroups after b whose ranges start
+      // inside group g (each wrote its partial sum of g first, then its flag)
+      for (int c = b + 1; c < G && range_start(c, U, G) < (g + 1) * P; ++c) {
+        if (range_start(c + 1, U, G) == range_start(c, U, G)) continue;  // empty range
+        for (int spin = 0; spin < kSpinGlobal; ++spin) {
+          if (__hip_atomic_load(&g_wide_part_flag[c], __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT) == e + 1u)
+            break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        asm volatile("" ::: "memory");  // the partial sums are read after the flag
+        const int32_t* pc = partials + (size_t)c * kPartInts;
+#pragma unroll
+        for (int tt = 0; tt < kTG; ++tt)
+#pragma unroll
+          for (int k = 0; k < KS; ++k) {
+            const int sidx = et + 128 * k;
+            if (sidx < MB * 64)
+              other[tt][k] += *reinterpret_cast<const v4i*>(pc + (tt * MB + (sidx >> 6)) * 256 + ln * 4);
+          }
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < kTG; ++tt) {
+      const int par = round & 1;
+      lds_wait_ge(sync + kRedReady + par, kS * ((round >> 1) + 1));
+      const int n0 = (g * kTG + tt) * 16 + 4 * (ln >> 4);
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const int sidx = et + 128 * k;
+        if (sidx < MB * 64) {
+          const int tb = sidx >> 6;
+          v4i tot = other[tt][k];
+#pragma unroll
+          for (int w = 0; w < kS; ++w)
+            tot += *reinterpret_cast<const v4i*>(red + ((par * kS + w) * MB + tb) * 256 + ln * 4);
+          if (writer) {
+            store16_device(partials + (size_t)b * kPartInts + (tt * MB + tb) * 256 + ln * 4, tot);
+          } else {
+            const int tok = tb * 16 + (ln & 15);
+            if (tok < M && n0 < N) {
+              const int tv[4] = {tot.x, tot.y, tot.z, tot.w};
+              uint32_t o[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                float v = (float)tv[i];  // round to nearest even
+                v = v * sxv[k];
+                v = v * ws[tt][i];
+                o[i] = f32_to_bf16_rne(v);
+              }
+              uint16_t* yr = y + (size_t)tok * N;
+              if (n0 + 3 < N && ((reinterpret_cast<uintptr_t>(yr + n0) & 7) == 0)) {
+                uint2 pk;
+                pk.x = o[0] | (o[1] << 16);
+                pk.y = o[2] | (o[3] << 16);
+                *reinterpret_cast<uint2*>(yr + n0) = pk;
+              } else {
+                for (int i = 0; i < 4 && n0 + i < N; ++i) yr[n0 + i] = (uint16_t)o[i];
+              }
+              if (acc_out)
+                for (int i = 0; i < 4 && n0 + i < N; ++i) acc_out[(size_t)tok * N + n0 + i] = tv[i];
+            }
+          }
+        }
+      }
+      asm volatile("" ::: "memory");  // the reads of this round precede the count
+      if (lane == 0) lds_add(sync + kRedFree + par, 1);
+      ++round;
+    }
+    if (g < g_last) fetch_ws(g + 1);  // lands while the streamers work on g + 1
+    if (writer) {
+      // both epilogue wavefronts' partial-sum stores complete, then one
+      // raises this workgroup's partial flag
+      wait_stores_done();
+      if (lane == 0) lds_add(sync + kPartDone, 1);
+      if (et == 0) {
+        lds_wait_ge(sync + kPartDone, kEpiWaves);
+        __hip_atomic_store(&g_wide_part_flag[b], e + 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The kernel: 4 streamer wavefronts, then 2 loader and 2 epilogue wavefronts
+// (the 4 helpers quantize the workgroup's token row first).
+// ---------------------------------------------------------------------------
+template <int MB>
+__global__ __launch_bounds__(kThreads) void w8a8_linear_wide_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ s, const int8_t* __restrict__ wq,
+    const float* __restrict__ wscale, int M, int N, int K, int tiles, int P, int U,
+    int8_t* __restrict__ qx, float* __restrict__ sx, int32_t* __restrict__ partials,
+    uint16_t* __restrict__ y, int32_t* __restrict__ acc_out) {
+  using C = Wide<MB>;
+  extern __shared__ __align__(16) char smem[];
+  char* ring = smem;
+  int32_t* red = reinterpret_cast<int32_t*>(smem + C::RING);
+  int* sync = reinterpret_cast<int*>(smem + C::RING + C::RED);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = gridDim.x, b = blockIdx.x;
+  const int i0 = range_start(b, U, G);
+  const int n = range_start(b + 1, U, G) - i0;
+  const int nch = (K + 63) >> 6;
+  if (tid < kSyncWords) sync[tid] = 0;  // ordered before use by barrier (1)
+
+  if (wave < kS) {
+    wide_streamer<MB>(wq, tiles, nch, P, i0, n, wave, lane, ring, red, sync);
+    return;
+  }
+
+  // ---- helpers
+  const int ht = tid - 64 * kS, hw = wave - kS;
+  const uint32_t e = __hip_atomic_load(&g_wide_row_flag[b], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  const bool quantizer = b < M;
+  const int units = K >> 3;
+  const bool in_regs = units <= kRowPieces * 64 * kHelpers;
+  v4i xv[kRowPieces], sv[kRowPieces][2];
+  if (quantizer && in_regs) {
+    const buffer_rsrc xrs = make_rsrc(x + (size_t)b * K, (uint32_t)K * 2u);
+    const buffer_rsrc srs = make_rsrc(s, (uint32_t)K * 4u);
+#pragma unroll
+    for (int u = 0; u < kRowPieces; ++u) {
+      const int q = ht + u * 64 * kHelpers;
+      const bool ok = q < units;
+      xv[u] = load16(xrs, ok ? q * 16 : kOutOfRange);
+      sv[u][0] = load16(srs, ok ? q * 32 : kOutOfRange);
+      sv[u][1] = load16(srs, ok ? q * 32 + 16 : kOutOfRange);
+    }
+  }
+  __syncthreads();  // (1)
+
+  // Row codes and scale go out with device-scope stores; once every helper
+  // wavefront's stores have completed, the row flag is raised.
+  if (quantizer) {
+    quantize_row_compute(x, s, b, K, ht, hw, lane, xv, sv, in_regs, qx, sx, sync);
+    wait_stores_done();
+    if (lane == 0) lds_add(sync + kRowDone, 1);
+  }
+  if (ht == 0) {
+    if (quantizer) lds_wait_ge(sync + kRowDone, kHelpers);
+    __hip_atomic_store(&g_wide_row_flag[b], e + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (n == 0) return;
+
+  // Wait for every token row of this launch (helper wavefront 0 polls the
+  // flags with device-scope loads); the rows are read only after this.
+  if (hw == 0) {
+    for (int spin = 0; spin < kSpinGlobal; ++spin) {
+      bool ready = true;
+      for (int m = lane; m < M; m += 64)
+        ready &= __hip_atomic_load(&g_wide_row_flag[m], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT) == e + 1u;
+      if (__builtin_amdgcn_ballot_w64(!ready) == 0) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+    if (lane == 0) lds_add(sync + kGate, 1);
+  } else {
+    lds_wait_ge(sync + kGate, 1);
+  }
+
+  if (hw < kLoadWaves) {
+    wide_loader<MB>(qx, M, K, P, i0, n, hw, lane, ring, sync);
+  } else {
+    wide_epilogue<MB>(wscale, sx, M, N, P, U, G, b, i0, n, e, tid - 64 * (kS + kLoadWaves), lane,
+                      red, sync, partials, y, acc_out);
+  }
+}
+
+template <int MB>
+hipError_t launch_wide_mb(const WidePlan& p, const uint16_t* x, const float* s, const int8_t* wq,
+                          const float* w_scale, uint16_t* y, int32_t* acc_out, int8_t* qx,
+                          float* sx, int32_t* partials, hipStream_t st) {
+  auto kernel = &w8a8_linear_wide_kernel<MB>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+      Wide<MB>::LDS);
+  if (attr != hipSuccess) return attr;
+  kernel<<<dim3(p.grid), dim3(kThreads), Wide<MB>::LDS, st>>>(
+      x, s, wq, w_scale, (int)p.M, (int)p.N, (int)p.K, p.tiles, p.P, p.U, qx, sx, partials, y,
+      acc_out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int wide_lds_bytes(int mb) {
+  switch (mb) {
+    case 1: return Wide<1>::LDS;
+    case 2: return Wide<2>::LDS;
+    case 3: return Wide<3>::LDS;
+    case 4: return Wide<4>::LDS;
+    case 5: return Wide<5>::LDS;
+    case 6: return Wide<6>::LDS;
+    case 7: return Wide<7>::LDS;
+    default: return Wide<8>::LDS;
+  }
+}
+
+WidePlan plan_wide(int64_t M, int64_t N, int64_t K, int grid) {
+  WidePlan p{};
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.mb = (int)((M + 15) / 16);
+  p.tiles = (int)((N + 15) / 16);
+  p.nch = (int)((K + 63) / 64);
+  p.groups = (p.tiles + kTG - 1) / kTG;
+  p.P = (p.nch + kS - 1) / kS;
+  p.U = p.groups * p.P;
+  p.grid = grid;
+  p.lds = wide_lds_bytes(p.mb);
+  size_t off = 0;
+  p.off_qx = off;
+  off = align_up(off + (size_t)(M * K), kWsAlign);
+  p.off_sx = off;
+  off = align_up(off + (size_t)M * sizeof(float), kWsAlign);
+  p.off_partials = off;
+  off = align_up(off + (size_t)kWideMaxGrid * kTG * p.mb * 1024, kWsAlign);
+  p.bytes = off;
+  return p;
+}
+
+const char* wide_kernel_name(int mb) {
+  static const char* const names[8] = {
+      "w8a8_linear_wide_kernel<1>", "w8a8_linear_wide_kernel<2>", "w8a8_linear_wide_kernel<3>",
+      "w8a8_linear_wide_kernel<4>", "w8a8_linear_wide_kernel<5>", "w8a8_linear_wide_kernel<6>",
+      "w8a8_linear_wide_kernel<7>", "w8a8_linear_wide_kernel<8>"};
+  return names[(mb < 1 ? 1 : (mb > 8 ? 8 : mb)) - 1];
+}
+
+hipError_t launch_wide(const WidePlan& p, const uint16_t* x, const float* s, const int8_t* wq,
+                       const float* w_scale, uint16_t* y, int32_t* acc_out, void* workspace,
+                       hipStream_t st) {
+  char* ws = static_cast<char*>(workspace);
+  int8_t* qx = reinterpret_cast<int8_t*>(ws + p.off_qx);
+  float* sx = reinterpret_cast<float*>(ws + p.off_sx);
+  int32_t* partials = reinterpret_cast<int32_t*>(ws + p.off_partials);
+  switch (p.mb) {
+    case 1: return launch_wide_mb<1>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
+    case 2: return launch_wide_mb<2>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
+    case 3: return launch_wide_mb<3>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
+    case 4: return launch_wide_mb<4>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
+    case 5: return launch_wide_mb<5>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
+    case 6: return launch_wide_mb<6>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
+    case 7: return launch_wide_mb<7>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
+    case 8: return launch_wide_mb<8>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Workgroups the wide kernel launches on the current device: one per compute
+// unit, at most kWideMaxGrid; 0 if one workgroup does not fit a compute unit.
+// Fixed per device for the life of the process (the launch counters rely on
+// every launch using the same grid).
+int wide_grid_for_current_device() {
+  static int cache[64];
+  static bool init[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (!init[dev]) {
+    int cus = 0, occ = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 0;
+    // every instantiation has the same block size; the largest LDS decides
+    int lds = 0, mb_max = 1;
+    for (int mb = 1; mb <= 8; ++mb)
+      if (wide_lds_bytes(mb) > lds) {
+        lds = wide_lds_bytes(mb);
+        mb_max = mb;
+      }
+    static_assert(Wide<6>::LDS >= Wide<5>::LDS && Wide<6>::LDS >= Wide<7>::LDS &&
+                      Wide<6>::LDS >= Wide<8>::LDS && Wide<6>::LDS >= Wide<4>::LDS,
+                  "the MB = 6 variant has the largest LDS");
+    (void)mb_max;
+    auto kernel = &w8a8_linear_wide_kernel<6>;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kThreads, lds) != hipSuccess)
+      occ = 0;
+    cache[dev] = occ >= 1 ? (cus < kWideMaxGrid ? cus : kWideMaxGrid) : 0;
+    init[dev] = true;
+  }
+  return cache[dev];
+}
+
+}  // namespace quasar
