@@ -148,11 +148,14 @@ def test_kernel_name_names_the_launch_plan(L):
     assert name(1, 16, 16) == "w8a8_linear_fused_kernel<2, 4, 2>"
     assert name(8, 4096, 8192) == "w8a8_linear_fused_kernel<8, 4, 4>"
     # wider windows (or K > 12288): one launch over ceil(M / 16) token blocks
-    assert name(48, 4096, 4096) == "w8a8_linear_wide_kernel<3>"
-    assert name(96, 4096, 12288) == "w8a8_linear_wide_kernel<6>"
-    assert name(9, 16, 16) == "w8a8_linear_wide_kernel<1>"
-    assert name(6, 64, 16384) == "w8a8_linear_wide_kernel<1>"
-    assert name(128, 151936, 4096) == "w8a8_linear_wide_kernel<8>"
+    # <token blocks, tiles per group>: one tile per group up to 512 tiles
+    assert name(48, 4096, 4096) == "w8a8_linear_wide_kernel<3, 1>"
+    assert name(96, 4096, 12288) == "w8a8_linear_wide_kernel<6, 1>"
+    assert name(96, 6144, 4096) == "w8a8_linear_wide_kernel<6, 1>"
+    assert name(96, 24576, 4096) == "w8a8_linear_wide_kernel<6, 4>"
+    assert name(9, 16, 16) == "w8a8_linear_wide_kernel<1, 1>"
+    assert name(6, 64, 16384) == "w8a8_linear_wide_kernel<1, 1>"
+    assert name(128, 151936, 4096) == "w8a8_linear_wide_kernel<8, 4>"
     # invalid or unsupported sizes
     assert name(0, 16, 16) == "" and name(6, 16, 17) == "" and name(129, 16, 16) == ""
 

@@ -84,7 +84,8 @@ const char* quasar_w8a8_kernel_name(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || check_k(K) != QUASAR_OK || M > QUASAR_MAX_M || N > kMaxRowsPerCall)
     return "";
   if (fused_supported(M, K)) return fused_kernel_name(plan_fused(M, N, K));
-  return wide_kernel_name(plan_wide(M, N, K, kWideMaxGrid).mb);
+  const WidePlan p = plan_wide(M, N, K, kWideMaxGrid);
+  return wide_kernel_name(p.mb, p.tg);
 }
 
 quasar_status quasar_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {

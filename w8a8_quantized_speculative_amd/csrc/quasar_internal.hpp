@@ -44,7 +44,7 @@ hipError_t launch_fused(const FusedPlan& p, const uint16_t* x, const float* s, c
 // Wide-window plan (9 <= M <= 128, or K > 12288): one launch of a persistent
 // grid (one workgroup per compute unit, all resident at once) that quantizes
 // the token rows into the workspace, passes a one-way grid barrier, and
-// streams (group of 64 channels, 256 K positions) items in equal contiguous
+// streams (group of tg tiles, 256 K positions) items in equal contiguous
 // ranges per workgroup, finishing groups shared by two ranges through INT32
 // partial sums in the workspace.
 // ---------------------------------------------------------------------------
@@ -53,9 +53,10 @@ constexpr int kWideMaxGrid = 256;
 struct WidePlan {
   int64_t M, N, K;
   int mb;      // 16-token blocks: ceil(M / 16), 1..8
+  int tg;      // 16-channel tiles per group: 1 or 4
   int tiles;   // ceil(N / 16)
   int nch;     // ceil(K / 64)
-  int groups;  // ceil(tiles / 4)
+  int groups;  // ceil(tiles / tg)
   int P;       // items per group: ceil(nch / 4)
   int U;       // groups * P
   int grid;    // workgroups (<= kWideMaxGrid, >= M)
@@ -66,8 +67,8 @@ struct WidePlan {
 
 // `grid` only enters the launch; the workspace is sized for kWideMaxGrid.
 WidePlan plan_wide(int64_t M, int64_t N, int64_t K, int grid);
-const char* wide_kernel_name(int mb);
-int wide_lds_bytes(int mb);
+const char* wide_kernel_name(int mb, int tg);
+int wide_tiles_per_group(int64_t N, int grid);
 // Workgroups of a wide launch on the current device (0: cannot run there).
 int wide_grid_for_current_device();
 hipError_t launch_wide(const WidePlan& p, const uint16_t* x, const float* s, const int8_t* wq,

@@ -8,7 +8,7 @@
 // which keeps the whole quantized activation matrix in every compute unit's
 // LDS (96 tokens x 4096 K positions is 384 KB; LDS is 160 KB).  Here the
 // quantized activations go to global memory once and are streamed through a
-// small LDS ring next to the weights:
+// small LDS area next to the weights:
 //
 //   1. Rows.  Workgroup m < M smooths and quantizes token row m
 //      (xs = RN32(x * s), absmax, scale, codes) into the workspace, then
@@ -22,12 +22,16 @@
 //      (stream-K): every workgroup streams the same number of weight bytes
 //      whatever N and K are.
 //   3. Per item, each of the 4 streamer wavefronts loads one 1 KB chunk of
-//      each of the group's 4 tiles (16 KB in flight per wavefront over 4
-//      register buffers) and multiplies it against the item's activation
-//      codes: 16 x 64 fragments of the M-token matrix, one per 16-token
-//      block, read from the LDS ring and reused for the 4 tiles.  Two loader
-//      wavefronts fill the ring with direct-to-LDS buffer loads from the
-//      workspace, several items ahead.
+//      each of the group's 4 tiles into registers and, right behind them, the
+//      activation codes of that K chunk -- one 16 x 64 fragment per 16-token
+//      block -- with direct-to-LDS buffer loads into a slot of its own, then
+//      multiplies each fragment against the 4 tiles.  Weights and codes of
+//      NBUF items are in flight per wavefront.  A compute unit holds only a
+//      bounded number of outstanding vector-memory requests and later
+//      requests wait at issue, so codes loaded by a separate wavefront would
+//      queue behind the weight stream and starve it; issued by the streamer
+//      right behind its weights, they land with them and one in-order wait
+//      count covers both.
 //   4. At the end of a group (or of the range) the streamers hand their
 //      partial sums to two epilogue wavefronts, one tile at a time through a
 //      double-buffered LDS area.  The epilogue sums the 4 partials (exact
@@ -39,7 +43,10 @@
 //
 // Synchronisation inside a workgroup uses monotonic LDS counters (no
 // workgroup barrier after the first), so a stalled role never stalls
-// another.  Across workgroups it uses one flag word per workgroup in module
+// another.  The streamers touch LDS only through inline assembly: the
+// compiler cannot tell their LDS words from the slots the direct-to-LDS loads
+// write and would otherwise wait for every load in flight before each access,
+// while LDS executes a wavefront's accesses in issue order anyway.  Across workgroups it uses one flag word per workgroup in module
 // memory: each launch bumps every workgroup's flag by exactly one, so a flag
 // equal to its owner's pre-launch value plus one marks this launch's data.
 // The grid is one workgroup per compute unit and all of them must be resident
@@ -59,12 +66,9 @@ __device__ uint32_t g_wide_part_flag[kWideMaxGrid];
 
 namespace {
 
-constexpr int kS = 4;          // streamer wavefronts (one 64-wide K chunk each per item)
-constexpr int kTG = 4;         // 16-channel tiles per group
-constexpr int kNBUF = 4;       // items of weights in flight per streamer (4 x 4 KB)
-constexpr int kLoadWaves = 2;  // loader wavefronts
-constexpr int kEpiWaves = 2;   // epilogue wavefronts
-constexpr int kHelpers = kLoadWaves + kEpiWaves;
+constexpr int kS = 4;        // streamer wavefronts (one 64-wide K chunk each per item)
+constexpr int kMaxTG = 4;    // 16-channel tiles per group: 1 or 4
+constexpr int kHelpers = 4;  // row quantizer, then epilogue wavefronts
 constexpr int kThreads = 64 * (kS + kHelpers);
 constexpr int kRowPieces = 8;  // 8-element pieces per helper thread kept in registers
 constexpr int kSpinLds = 1 << 22;
@@ -75,29 +79,36 @@ constexpr int kSpinGlobal = 1 << 20;
 // maxima so they are not waited for).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-// Ring depth by 16-token blocks: the ring (NW windows of 4 MB KB) and the
-// partial-sum area (2 x 4 MB KB) stay within 144 KB of LDS.
-template <int MB>
+// Items in flight per streamer (NBUF) for MB 16-token blocks and TG tiles per
+// group: the code slots (4 streamers x NBUF items x MB KB) and the partial-sum
+// area (2 x 4 x MB KB) stay within 150 KB of LDS, and the loads in flight per
+// wavefront ((NBUF - 1) items of TG + MB, plus one item's MB code loads)
+// within what the 6-bit vmcnt counter can wait for.  At most 8.
+constexpr int wide_nbuf(int MB, int TG) {
+  int nb = 8;
+  while (nb > 2 && (kS * nb * MB + 2 * kS * MB > 150 || (nb - 1) * (TG + MB) + MB > 63)) --nb;
+  return nb;
+}
+template <int MB, int TG>
 struct Wide {
-  static constexpr int NW = MB <= 3 ? 8 : (MB == 4 ? 6 : (MB == 5 ? 5 : (MB == 6 ? 4 : (MB == 7 ? 3 : 2))));
-  static constexpr int FRAGS = kS * MB;          // 1 KB fragments per window (item)
-  static constexpr int NF = FRAGS / kLoadWaves;  // fragments per loader wavefront
-  static constexpr int RING = NW * FRAGS * 1024;
+  static constexpr int NBUF = wide_nbuf(MB, TG);
+  static constexpr int SLOTS = kS * NBUF * MB * 1024;
   static constexpr int RED = 2 * kS * MB * 1024;
   static constexpr int SYNC = 256;
-  static constexpr int LDS = RING + RED + SYNC;
+  static constexpr int LDS = SLOTS + RED + SYNC;
 };
-static_assert(Wide<6>::LDS <= 150 * 1024 && Wide<8>::LDS <= 150 * 1024 &&
-                  Wide<4>::LDS <= 150 * 1024 && Wide<5>::LDS <= 150 * 1024,
-              "LDS budget");
-static_assert((Wide<3>::NW - 1) * Wide<3>::NF <= 63 && (Wide<6>::NW - 1) * Wide<6>::NF <= 63 &&
-                  (Wide<4>::NW - 1) * Wide<4>::NF <= 63 && (Wide<8>::NW - 1) * Wide<8>::NF <= 63,
-              "loader waits fit the 6-bit vmcnt");
+template <int MB>
+constexpr bool wide_fits() {
+  return Wide<MB, 1>::LDS <= 150 * 1024 && Wide<MB, 4>::LDS <= 150 * 1024 &&
+         (Wide<MB, 1>::NBUF - 1) * (1 + MB) + MB <= 63 &&
+         (Wide<MB, 4>::NBUF - 1) * (4 + MB) + MB <= 63;
+}
+static_assert(wide_fits<1>() && wide_fits<2>() && wide_fits<3>() && wide_fits<4>() &&
+                  wide_fits<5>() && wide_fits<6>() && wide_fits<7>() && wide_fits<8>(),
+              "LDS budget, and in-flight loads within the 6-bit vmcnt");
 
 // LDS synchronisation words (int indices into the SYNC area)
 enum : int {
-  kFilled = 0,     // [8] per ring slot: loader wavefronts that filled it (monotonic)
-  kConsumed = 8,   // [8] per ring slot: streamers that finished reading it
   kRedReady = 16,  // [2] per parity: streamers that published a tile round
   kRedFree = 18,   // [2] per parity: epilogue wavefronts that consumed a round
   kRowDone = 20,   // helper wavefronts whose row codes are stored
@@ -105,27 +116,46 @@ enum : int {
   kGate = 22,      // 1 once every token row of the launch is in the workspace
   kPartDone = 23,  // epilogue wavefronts whose partial sums are stored
   kAmax = 24,      // float [4] per-helper row maxima
+  kFlagOut = 28,   // 1 once this workgroup's row flag store has been issued
   kSyncWords = 32
 };
 
-// LDS word read for the wavefronts that also issue direct-to-LDS loads: the
-// compiler cannot tell these words from the ring the loads write, and would
-// wait for every load in flight before a plain read.  LDS executes a
-// wavefront's accesses in order, so no wait is needed.
-__device__ __forceinline__ int lds_read_asm(const int* p) {
-  const uint32_t addr = (uint32_t)reinterpret_cast<uintptr_t>(
-      (__attribute__((address_space(3))) const int*)p);
+// LDS accesses of the streamer wavefronts (see the note above), by LDS byte
+// address.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p);
+}
+
+__device__ __forceinline__ int lds_read_asm(uint32_t addr) {
   int v;
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
   return v;
 }
 
-// LDS counter increment for the same wavefronts (no compiler-inserted wait for
-// the direct-to-LDS loads in flight).
-__device__ __forceinline__ void lds_add_asm(int* p, int v) {
-  const uint32_t addr = (uint32_t)reinterpret_cast<uintptr_t>(
-      (__attribute__((address_space(3))) int*)p);
+__device__ __forceinline__ void lds_add_asm(uint32_t addr, int v) {
   asm volatile("ds_add_u32 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
+__device__ __forceinline__ v4i lds_read16_asm(uint32_t addr) {  // no wait: see lds_wait_reads
+  v4i v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+
+__device__ __forceinline__ void lds_write16_asm(uint32_t addr, v4i v) {
+  asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
+__device__ __forceinline__ void lds_wait_reads() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// Bounded wait until an LDS counter reaches `target`, for the streamers.
+__device__ __forceinline__ void lds_wait_ge_asm(uint32_t addr, int target) {
+  for (int spin = 0; spin < kSpinLds; ++spin) {
+    if (lds_read_asm(addr) >= target) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
 }
 
 __device__ __forceinline__ int lds_load(const int* p) {
@@ -175,84 +205,138 @@ __host__ __device__ inline int range_start(int b, int U, int G) {
 }
 
 // ---------------------------------------------------------------------------
-// Streamer role: weights -> MFMA against the ring -> per-tile partial rounds.
+// Streamer role: weights and codes -> MFMA -> per-tile partial rounds.
 // ---------------------------------------------------------------------------
-template <int MB>
-__device__ __forceinline__ void wide_streamer(const int8_t* __restrict__ wq, int tiles, int nch,
-                                              int P, int i0, int n, int w, int lane,
-                                              const char* ring, int32_t* red, int* sync) {
-  using C = Wide<MB>;
-  v4i a[kNBUF][kTG];
-  // issue pointer: item i0 + j as (group, item within group)
-  int ig = i0 / P, ip = i0 - (i0 / P) * P;
-  int issued = 0;
+template <int MB, int TG>
+__device__ __forceinline__ void wide_streamer(const int8_t* __restrict__ wq,
+                                              const int8_t* __restrict__ qx, int M, int K,
+                                              int tiles, int nch, int P, int i0, int n, int w,
+                                              int lane, bool quantizer, char* slots,
+                                              int32_t* red, int* sync) {
+  using C = Wide<MB, TG>;
+  constexpr int NB = C::NBUF;
   const int voff = lane * 16;
-  auto issue = [&](int bb) {
-    const bool live = issued < n;
+
+  // Weights of the next item into register buffer bb: chunk (item * 4 + w) of
+  // the group's 4 tiles, 1 KB each, zeros past the range, N or K.
+  v4i a[NB][TG];
+  int ig = i0 / P, ip = i0 - (i0 / P) * P, wissued = 0;
+  auto issue_weights = [&](int bb) {
+    const bool live = wissued < n;
     const int c = ip * kS + w;
 #pragma unroll
-    for (int tt = 0; tt < kTG; ++tt) {
-      const int t = ig * kTG + tt;
+    for (int tt = 0; tt < TG; ++tt) {
+      const int t = ig * TG + tt;
       const bool ok = live && t < tiles && c < nch;
       const buffer_rsrc rs =
           make_rsrc(wq + ((size_t)(ok ? t : 0) * nch + (ok ? c : 0)) * 1024, ok ? 1024u : 0u);
       a[bb][tt] = load16<kNonTemporal>(rs, voff);
     }
-    ++issued;
+    ++wissued;
     if (++ip == P) {
       ip = 0;
       ++ig;
     }
   };
+  // Codes of the next item into this streamer's LDS slot bb: fragment tb holds
+  // token block tb at K chunk (item * 4 + w); lane l = 16 g + r reads 16 codes
+  // of token 16 tb + r at K positions 64 c + 16 g, and the direct-to-LDS load
+  // stores them at l * 16.  Token rows >= M read as zero (buffer bound); K
+  // positions past K read the next row's codes or zero, which meet zero
+  // weights.
+  const buffer_rsrc qrs = make_rsrc(qx, (uint32_t)M * (uint32_t)K);
+  const int lane_off = (lane & 15) * K + (lane >> 4) * 16;
+  char* my_slots = slots + w * NB * MB * 1024;
+  int cp_issue = i0 - (i0 / P) * P, cissued = 0;
+  auto issue_codes = [&](int bb) {
+    const bool live = cissued < n;
+    const int c = cp_issue * kS + w;
+#pragma unroll
+    for (int tb = 0; tb < MB; ++tb)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          qrs, (__attribute__((address_space(3))) void*)(my_slots + (bb * MB + tb) * 1024), 16,
+          live ? lane_off + tb * 16 * K + c * 64 : kOutOfRange, 0, 0, 0);
+    ++cissued;
+    if (++cp_issue == P) cp_issue = 0;
+  };
 
   __syncthreads();  // (1) the row quantizer's activation loads are queued first
+  if (n == 0) return;
+  // A compute unit serves its vector-memory requests in order, and the row
+  // quantizer's code stores, its flag and every flag poll sit on the critical
+  // path of the launch: in a workgroup that quantizes a row, the weight stream
+  // starts once the row is out, so those stores do not queue behind it.  (The
+  // other workgroups' first weights have landed by the time the flags are
+  // polled.)
+  if (quantizer) lds_wait_ge_asm(lds_address(sync + kFlagOut), 1);
 #pragma unroll
-  for (int bb = 0; bb < kNBUF; ++bb) issue(bb);
+  for (int bb = 0; bb < NB; ++bb) issue_weights(bb);
+  // the codes exist once every token row of the launch is in the workspace
+  lds_wait_ge_asm(lds_address(sync + kGate), 1);
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) issue_codes(bb);
   __builtin_amdgcn_sched_barrier(0);  // keep the loop below from rotating into the issues
 
-  v4i acc[kTG][MB];
+  v4i acc[TG][MB];
 #pragma unroll
-  for (int tt = 0; tt < kTG; ++tt)
+  for (int tt = 0; tt < TG; ++tt)
 #pragma unroll
     for (int tb = 0; tb < MB; ++tb) acc[tt][tb] = (v4i){0, 0, 0, 0};
 
+  const uint32_t slot_addr = lds_address(my_slots) + lane * 16;
+  const uint32_t red_addr = lds_address(red) + w * MB * 1024 + lane * 16;
   int cp = i0 - (i0 / P) * P;  // consume pointer: item within its group
   int round = 0;
-  for (int jb = 0; jb < n; jb += kNBUF) {
+  for (int jb = 0; jb < n; jb += NB) {
 #pragma unroll
-    for (int bb = 0; bb < kNBUF; ++bb) {
+    for (int bb = 0; bb < NB; ++bb) {
       const int j = jb + bb;
       if (j < n) {
-        const int slot = j % C::NW;
-        lds_wait_ge(sync + kFilled + slot, kLoadWaves * (j / C::NW + 1));
-        const char* frag = ring + (slot * C::FRAGS + w * MB) * 1024 + lane * 16;
+        // Item j's weights and codes have landed once at most the loads issued
+        // after its codes are outstanding (loads complete in issue order):
+        // (NB - 1) MB code loads of later items, plus the weights of the items
+        // issued since -- (NB - 1) MB + min(j, NB - 1) TG in all.
+        switch (j < NB - 1 ? j : NB - 1) {
+          case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * MB)); break;
+          case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * MB + 1 * TG)); break;
+          case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * MB + 2 * TG)); break;
+          case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * MB + 3 * TG)); break;
+          case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * MB + 4 * TG)); break;
+          case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * MB + 5 * TG)); break;
+          case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * MB + 6 * TG)); break;
+          default: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * MB + 7 * TG)); break;
+        }
         v4i bf[MB];
 #pragma unroll
-        for (int tb = 0; tb < MB; ++tb) bf[tb] = *reinterpret_cast<const v4i*>(frag + tb * 1024);
+        for (int tb = 0; tb < MB; ++tb)
+          bf[tb] = lds_read16_asm(slot_addr + (bb * MB + tb) * 1024);
+        lds_wait_reads();
 #pragma unroll
-        for (int tt = 0; tt < kTG; ++tt)
+        for (int tb = 0; tb < MB; ++tb) asm volatile("" : "+v"(bf[tb]));
 #pragma unroll
-          for (int tb = 0; tb < MB; ++tb) acc[tt][tb] = mfma_i8_16x16x64(a[bb][tt], bf[tb], acc[tt][tb]);
-        // the fragment reads above precede this count in LDS order
-        asm volatile("" ::: "memory");
-        if (lane == 0) lds_add(sync + kConsumed + slot, 1);
+        for (int tt = 0; tt < TG; ++tt)
+#pragma unroll
+          for (int tb = 0; tb < MB; ++tb)
+            acc[tt][tb] = mfma_i8_16x16x64(a[bb][tt], bf[tb], acc[tt][tb]);
       }
-      issue(bb);  // item j + kNBUF, or zeros past the range
+      // item j + NB into buffer bb and slot bb (slot bb's codes are in
+      // registers now), or zeros past the range
+      issue_weights(bb);
+      issue_codes(bb);
       if (j < n) {
         const bool group_end = cp == P - 1 || j == n - 1;
         if (group_end) {
 #pragma unroll
-          for (int tt = 0; tt < kTG; ++tt) {
+          for (int tt = 0; tt < TG; ++tt) {
             const int par = round & 1;
-            if (round >= 2) lds_wait_ge(sync + kRedFree + par, kEpiWaves * (round >> 1));
-            int32_t* dst = red + ((par * kS + w) * MB) * 256 + lane * 4;
+            if (round >= 2)
+              lds_wait_ge_asm(lds_address(sync + kRedFree + par), kHelpers * (round >> 1));
 #pragma unroll
             for (int tb = 0; tb < MB; ++tb) {
-              *reinterpret_cast<v4i*>(dst + tb * 256) = acc[tt][tb];
+              lds_write16_asm(red_addr + (par * kS * MB + tb) * 1024, acc[tt][tb]);
               acc[tt][tb] = (v4i){0, 0, 0, 0};
             }
-            asm volatile("" ::: "memory");
-            if (lane == 0) lds_add(sync + kRedReady + par, 1);
+            if (lane == 0) lds_add_asm(lds_address(sync + kRedReady + par), 1);
             ++round;
           }
         }
@@ -348,73 +432,14 @@ __device__ __forceinline__ void quantize_row_compute(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Loader role: fill ring slots with the item's activation fragments.
-// Fragment f = jc * MB + tb of an item holds token block tb at K chunk
-// (item * 4 + jc): lane l = 16 g + r reads 16 codes of token 16 tb + r at K
-// positions 64 c + 16 g, and the direct-to-LDS load stores them at l * 16.
-// Token rows >= M read as zero (buffer bound); K positions past K read the
-// next row's codes or zero, which meet zero weights.
-// ---------------------------------------------------------------------------
-template <int MB>
-__device__ __forceinline__ void wide_loader(const int8_t* __restrict__ qx, int M, int K, int P,
-                                            int i0, int n, int lw, int lane, char* ring,
-                                            int* sync) {
-  using C = Wide<MB>;
-  const buffer_rsrc qrs = make_rsrc(qx, (uint32_t)M * (uint32_t)K);
-  const int r16 = lane & 15, g4 = lane >> 4;
-  int ip = i0 - (i0 / P) * P;
-  int issued = 0, signaled = 0;
-  for (int spin = 0; signaled < n && spin < kSpinLds; ++spin) {
-    const bool can_issue =
-        issued < n &&
-        (issued < C::NW ||
-         lds_read_asm(sync + kConsumed + issued % C::NW) >= kS * (issued / C::NW));
-    if (can_issue) {
-      const int slot = issued % C::NW;
-      const int c0 = ip * kS;
-#pragma unroll
-      for (int k = 0; k < C::NF; ++k) {
-        const int f = lw + kLoadWaves * k;
-        const int jc = f / MB, tb = f % MB;
-        const int off = (tb * 16 + r16) * K + (c0 + jc) * 64 + g4 * 16;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            qrs, (__attribute__((address_space(3))) void*)(ring + (slot * C::FRAGS + f) * 1024),
-            16, off, 0, 0, 0);
-      }
-      ++issued;
-      if (++ip == P) ip = 0;
-      continue;
-    }
-    if (issued > signaled) {
-      // the oldest window is complete once at most the later windows' loads
-      // are outstanding (loads complete in issue order)
-      switch (issued - signaled - 1) {
-        case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
-        case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::NF)); break;
-        case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (C::NW > 2 ? C::NF : 0))); break;
-        case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * (C::NW > 3 ? C::NF : 0))); break;
-        case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * (C::NW > 4 ? C::NF : 0))); break;
-        case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5 * (C::NW > 5 ? C::NF : 0))); break;
-        case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6 * (C::NW > 6 ? C::NF : 0))); break;
-        default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(7 * (C::NW > 7 ? C::NF : 0))); break;
-      }
-      if (lane == 0) lds_add_asm(sync + kFilled + signaled % C::NW, 1);
-      ++signaled;
-    } else {
-      __builtin_amdgcn_s_sleep(1);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Epilogue role.  Thread et (0..127) owns slots et + 128 k of a tile round:
+// Epilogue role.  Thread et (0..255) owns slots et + 256 k of a tile round:
 // slot s = 64 tb + l is lane l of token block tb, i.e. token 16 tb + l % 16 and
 // the 4 channels 4 (l / 16) .. + 3 of the tile (the MFMA result layout).  No
 // global load waits inside a round: the weight scales of a group are fetched
 // while the streamers are still on it, and the partial sums of the workgroups
 // that own the rest of a finalized group are summed once, before its rounds.
 // ---------------------------------------------------------------------------
-template <int MB>
+template <int MB, int TG>
 __device__ __forceinline__ void wide_epilogue(const float* __restrict__ wscale,
                                               const float* __restrict__ sx, int M, int N, int P,
                                               int U, int G, int b, int i0, int n, uint32_t e,
@@ -422,23 +447,23 @@ __device__ __forceinline__ void wide_epilogue(const float* __restrict__ wscale,
                                               int32_t* __restrict__ partials,
                                               uint16_t* __restrict__ y,
                                               int32_t* __restrict__ acc_out) {
-  constexpr int KS = (MB + 1) / 2;           // slots per thread and round
-  constexpr int kPartInts = kTG * MB * 256;  // one workgroup's partial sums
+  constexpr int KS = (MB + 3) / 4;           // slots per thread and round
+  constexpr int kPartInts = kMaxTG * MB * 256;  // one workgroup's partial-sum slot
   const int ln = et & 63;
   float sxv[KS];
 #pragma unroll
   for (int k = 0; k < KS; ++k) {
-    const int tok = ((et >> 6) + 2 * k) * 16 + (ln & 15);
+    const int tok = ((et >> 6) + 4 * k) * 16 + (ln & 15);
     sxv[k] = tok < M ? sx[tok] : 0.0f;
   }
   const buffer_rsrc wrs = make_rsrc(wscale, (uint32_t)N * 4u);
-  float ws[kTG][4];  // weight scales of the group's 4 channels per tile of this thread
+  float ws[TG][4];  // weight scales of the group's 4 channels per tile of this thread
   auto fetch_ws = [&](int g) {
 #pragma unroll
-    for (int tt = 0; tt < kTG; ++tt)
+    for (int tt = 0; tt < TG; ++tt)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        ws[tt][i] = __int_as_float(load4(wrs, (((g * kTG + tt) * 16) + 4 * (ln >> 4) + i) * 4));
+        ws[tt][i] = __int_as_float(load4(wrs, (((g * TG + tt) * 16) + 4 * (ln >> 4) + i) * 4));
   };
   const int g_first = i0 / P, g_last = (i0 + n - 1) / P;
   fetch_ws(g_first);
@@ -446,9 +471,9 @@ __device__ __forceinline__ void wide_epilogue(const float* __restrict__ wscale,
   for (int g = g_first; g <= g_last; ++g) {
     const bool writer = g == g_first && i0 % P != 0;
     const bool finalizer = !writer && (i0 + n) < (g + 1) * P;
-    v4i other[kTG][KS];  // partial sums of the other owners of group g
+    v4i other[TG][KS];  // partial sums of the other owners of group g
 #pragma unroll
-    for (int tt = 0; tt < kTG; ++tt)
+    for (int tt = 0; tt < TG; ++tt)
 #pragma unroll
       for (int k = 0; k < KS; ++k) other[tt][k] = (v4i){0, 0, 0, 0};
     if (finalizer) {
@@ -465,23 +490,23 @@ __device__ __forceinline__ void wide_epilogue(const float* __restrict__ wscale,
         asm volatile("" ::: "memory");  // the partial sums are read after the flag
         const int32_t* pc = partials + (size_t)c * kPartInts;
 #pragma unroll
-        for (int tt = 0; tt < kTG; ++tt)
+        for (int tt = 0; tt < TG; ++tt)
 #pragma unroll
           for (int k = 0; k < KS; ++k) {
-            const int sidx = et + 128 * k;
+            const int sidx = et + 256 * k;
             if (sidx < MB * 64)
               other[tt][k] += *reinterpret_cast<const v4i*>(pc + (tt * MB + (sidx >> 6)) * 256 + ln * 4);
           }
       }
     }
 #pragma unroll
-    for (int tt = 0; tt < kTG; ++tt) {
+    for (int tt = 0; tt < TG; ++tt) {
       const int par = round & 1;
       lds_wait_ge(sync + kRedReady + par, kS * ((round >> 1) + 1));
-      const int n0 = (g * kTG + tt) * 16 + 4 * (ln >> 4);
+      const int n0 = (g * TG + tt) * 16 + 4 * (ln >> 4);
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
-        const int sidx = et + 128 * k;
+        const int sidx = et + 256 * k;
         if (sidx < MB * 64) {
           const int tb = sidx >> 6;
           v4i tot = other[tt][k];
@@ -528,7 +553,7 @@ __device__ __forceinline__ void wide_epilogue(const float* __restrict__ wscale,
       wait_stores_done();
       if (lane == 0) lds_add(sync + kPartDone, 1);
       if (et == 0) {
-        lds_wait_ge(sync + kPartDone, kEpiWaves);
+        lds_wait_ge(sync + kPartDone, kHelpers);
         __hip_atomic_store(&g_wide_part_flag[b], e + 1u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
       }
@@ -537,20 +562,20 @@ __device__ __forceinline__ void wide_epilogue(const float* __restrict__ wscale,
 }
 
 // ---------------------------------------------------------------------------
-// The kernel: 4 streamer wavefronts, then 2 loader and 2 epilogue wavefronts
-// (the 4 helpers quantize the workgroup's token row first).
+// The kernel: 4 streamer wavefronts, then 4 helper wavefronts (they quantize
+// the workgroup's token row, then run the epilogue).
 // ---------------------------------------------------------------------------
-template <int MB>
+template <int MB, int TG>
 __global__ __launch_bounds__(kThreads) void w8a8_linear_wide_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ s, const int8_t* __restrict__ wq,
     const float* __restrict__ wscale, int M, int N, int K, int tiles, int P, int U,
     int8_t* __restrict__ qx, float* __restrict__ sx, int32_t* __restrict__ partials,
     uint16_t* __restrict__ y, int32_t* __restrict__ acc_out) {
-  using C = Wide<MB>;
+  using C = Wide<MB, TG>;
   extern __shared__ __align__(16) char smem[];
-  char* ring = smem;
-  int32_t* red = reinterpret_cast<int32_t*>(smem + C::RING);
-  int* sync = reinterpret_cast<int*>(smem + C::RING + C::RED);
+  char* slots = smem;
+  int32_t* red = reinterpret_cast<int32_t*>(smem + C::SLOTS);
+  int* sync = reinterpret_cast<int*>(smem + C::SLOTS + C::RED);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -561,7 +586,8 @@ __global__ __launch_bounds__(kThreads) void w8a8_linear_wide_kernel(
   if (tid < kSyncWords) sync[tid] = 0;  // ordered before use by barrier (1)
 
   if (wave < kS) {
-    wide_streamer<MB>(wq, tiles, nch, P, i0, n, wave, lane, ring, red, sync);
+    wide_streamer<MB, TG>(wq, qx, M, K, tiles, nch, P, i0, n, wave, lane, b < M, slots, red,
+                          sync);
     return;
   }
 
@@ -597,6 +623,8 @@ __global__ __launch_bounds__(kThreads) void w8a8_linear_wide_kernel(
   if (ht == 0) {
     if (quantizer) lds_wait_ge(sync + kRowDone, kHelpers);
     __hip_atomic_store(&g_wide_row_flag[b], e + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("" ::: "memory");
+    lds_add(sync + kFlagOut, 1);  // the flag is queued ahead of the weight stream
   }
   if (n == 0) return;
 
@@ -617,42 +645,59 @@ __global__ __launch_bounds__(kThreads) void w8a8_linear_wide_kernel(
     lds_wait_ge(sync + kGate, 1);
   }
 
-  if (hw < kLoadWaves) {
-    wide_loader<MB>(qx, M, K, P, i0, n, hw, lane, ring, sync);
-  } else {
-    wide_epilogue<MB>(wscale, sx, M, N, P, U, G, b, i0, n, e, tid - 64 * (kS + kLoadWaves), lane,
-                      red, sync, partials, y, acc_out);
-  }
+  wide_epilogue<MB, TG>(wscale, sx, M, N, P, U, G, b, i0, n, e, ht, lane, red, sync, partials, y,
+                        acc_out);
 }
 
-template <int MB>
+template <int MB, int TG>
 hipError_t launch_wide_mb(const WidePlan& p, const uint16_t* x, const float* s, const int8_t* wq,
                           const float* w_scale, uint16_t* y, int32_t* acc_out, int8_t* qx,
                           float* sx, int32_t* partials, hipStream_t st) {
-  auto kernel = &w8a8_linear_wide_kernel<MB>;
+  auto kernel = &w8a8_linear_wide_kernel<MB, TG>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-      Wide<MB>::LDS);
+      Wide<MB, TG>::LDS);
   if (attr != hipSuccess) return attr;
-  kernel<<<dim3(p.grid), dim3(kThreads), Wide<MB>::LDS, st>>>(
+  kernel<<<dim3(p.grid), dim3(kThreads), Wide<MB, TG>::LDS, st>>>(
       x, s, wq, w_scale, (int)p.M, (int)p.N, (int)p.K, p.tiles, p.P, p.U, qx, sx, partials, y,
       acc_out);
   return hipGetLastError();
 }
 
+template <int TG>
+hipError_t launch_wide_tg(const WidePlan& p, const uint16_t* x, const float* s, const int8_t* wq,
+                          const float* w_scale, uint16_t* y, int32_t* acc_out, int8_t* qx,
+                          float* sx, int32_t* partials, hipStream_t st) {
+  switch (p.mb) {
+    case 1: return launch_wide_mb<1, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
+    case 2: return launch_wide_mb<2, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
+    case 3: return launch_wide_mb<3, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
+    case 4: return launch_wide_mb<4, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
+    case 5: return launch_wide_mb<5, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
+    case 6: return launch_wide_mb<6, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
+    case 7: return launch_wide_mb<7, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
+    case 8: return launch_wide_mb<8, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+constexpr int wide_lds_of(int mb, int tg) {
+  return kS * wide_nbuf(mb, tg) * mb * 1024 + 2 * kS * mb * 1024 + 256;
+}
+static_assert(wide_lds_of(6, 4) == Wide<6, 4>::LDS && wide_lds_of(3, 1) == Wide<3, 1>::LDS,
+              "host LDS size matches the kernel's");
+
 }  // namespace
 
-int wide_lds_bytes(int mb) {
-  switch (mb) {
-    case 1: return Wide<1>::LDS;
-    case 2: return Wide<2>::LDS;
-    case 3: return Wide<3>::LDS;
-    case 4: return Wide<4>::LDS;
-    case 5: return Wide<5>::LDS;
-    case 6: return Wide<6>::LDS;
-    case 7: return Wide<7>::LDS;
-    default: return Wide<8>::LDS;
-  }
+// Tiles per group: groups of 4 tiles let each 16 x 64 activation fragment
+// serve 4 tiles (a quarter of the code bytes per weight byte), but leave a
+// linear with few tiles with fewer groups than workgroups, so that a group's
+// K range is split across several workgroups that must hand INT32 partial
+// sums to each other at the end.  Up to 2 tiles per workgroup, groups of one
+// tile are used instead.
+int wide_tiles_per_group(int64_t N, int grid) {
+  const int64_t tiles = (N + 15) / 16;
+  return tiles <= 2 * (int64_t)(grid > 0 ? grid : kWideMaxGrid) ? 1 : kMaxTG;
 }
 
 WidePlan plan_wide(int64_t M, int64_t N, int64_t K, int grid) {
@@ -661,30 +706,36 @@ WidePlan plan_wide(int64_t M, int64_t N, int64_t K, int grid) {
   p.N = N;
   p.K = K;
   p.mb = (int)((M + 15) / 16);
+  p.tg = wide_tiles_per_group(N, grid);
   p.tiles = (int)((N + 15) / 16);
   p.nch = (int)((K + 63) / 64);
-  p.groups = (p.tiles + kTG - 1) / kTG;
+  p.groups = (p.tiles + p.tg - 1) / p.tg;
   p.P = (p.nch + kS - 1) / kS;
   p.U = p.groups * p.P;
   p.grid = grid;
-  p.lds = wide_lds_bytes(p.mb);
+  p.lds = wide_lds_of(p.mb, p.tg);
   size_t off = 0;
   p.off_qx = off;
   off = align_up(off + (size_t)(M * K), kWsAlign);
   p.off_sx = off;
   off = align_up(off + (size_t)M * sizeof(float), kWsAlign);
   p.off_partials = off;
-  off = align_up(off + (size_t)kWideMaxGrid * kTG * p.mb * 1024, kWsAlign);
+  off = align_up(off + (size_t)kWideMaxGrid * kMaxTG * p.mb * 1024, kWsAlign);
   p.bytes = off;
   return p;
 }
 
-const char* wide_kernel_name(int mb) {
-  static const char* const names[8] = {
-      "w8a8_linear_wide_kernel<1>", "w8a8_linear_wide_kernel<2>", "w8a8_linear_wide_kernel<3>",
-      "w8a8_linear_wide_kernel<4>", "w8a8_linear_wide_kernel<5>", "w8a8_linear_wide_kernel<6>",
-      "w8a8_linear_wide_kernel<7>", "w8a8_linear_wide_kernel<8>"};
-  return names[(mb < 1 ? 1 : (mb > 8 ? 8 : mb)) - 1];
+const char* wide_kernel_name(int mb, int tg) {
+  static const char* const names[2][8] = {
+      {"w8a8_linear_wide_kernel<1, 1>", "w8a8_linear_wide_kernel<2, 1>",
+       "w8a8_linear_wide_kernel<3, 1>", "w8a8_linear_wide_kernel<4, 1>",
+       "w8a8_linear_wide_kernel<5, 1>", "w8a8_linear_wide_kernel<6, 1>",
+       "w8a8_linear_wide_kernel<7, 1>", "w8a8_linear_wide_kernel<8, 1>"},
+      {"w8a8_linear_wide_kernel<1, 4>", "w8a8_linear_wide_kernel<2, 4>",
+       "w8a8_linear_wide_kernel<3, 4>", "w8a8_linear_wide_kernel<4, 4>",
+       "w8a8_linear_wide_kernel<5, 4>", "w8a8_linear_wide_kernel<6, 4>",
+       "w8a8_linear_wide_kernel<7, 4>", "w8a8_linear_wide_kernel<8, 4>"}};
+  return names[tg == 1 ? 0 : 1][(mb < 1 ? 1 : (mb > 8 ? 8 : mb)) - 1];
 }
 
 hipError_t launch_wide(const WidePlan& p, const uint16_t* x, const float* s, const int8_t* wq,
@@ -694,17 +745,10 @@ hipError_t launch_wide(const WidePlan& p, const uint16_t* x, const float* s, con
   int8_t* qx = reinterpret_cast<int8_t*>(ws + p.off_qx);
   float* sx = reinterpret_cast<float*>(ws + p.off_sx);
   int32_t* partials = reinterpret_cast<int32_t*>(ws + p.off_partials);
-  switch (p.mb) {
-    case 1: return launch_wide_mb<1>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
-    case 2: return launch_wide_mb<2>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
-    case 3: return launch_wide_mb<3>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
-    case 4: return launch_wide_mb<4>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
-    case 5: return launch_wide_mb<5>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
-    case 6: return launch_wide_mb<6>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
-    case 7: return launch_wide_mb<7>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
-    case 8: return launch_wide_mb<8>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
-    default: return hipErrorInvalidValue;
-  }
+  if (p.tg == 1) return launch_wide_tg<1>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
+  if (p.tg == kMaxTG)
+    return launch_wide_tg<kMaxTG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
+  return hipErrorInvalidValue;
 }
 
 // Workgroups the wide kernel launches on the current device: one per compute
@@ -721,17 +765,10 @@ int wide_grid_for_current_device() {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       cus = 0;
     // every instantiation has the same block size; the largest LDS decides
-    int lds = 0, mb_max = 1;
+    int lds = 0;
     for (int mb = 1; mb <= 8; ++mb)
-      if (wide_lds_bytes(mb) > lds) {
-        lds = wide_lds_bytes(mb);
-        mb_max = mb;
-      }
-    static_assert(Wide<6>::LDS >= Wide<5>::LDS && Wide<6>::LDS >= Wide<7>::LDS &&
-                      Wide<6>::LDS >= Wide<8>::LDS && Wide<6>::LDS >= Wide<4>::LDS,
-                  "the MB = 6 variant has the largest LDS");
-    (void)mb_max;
-    auto kernel = &w8a8_linear_wide_kernel<6>;
+      for (int tg : {1, kMaxTG}) lds = wide_lds_of(mb, tg) > lds ? wide_lds_of(mb, tg) : lds;
+    auto kernel = &w8a8_linear_wide_kernel<6, kMaxTG>;
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kThreads, lds) != hipSuccess)
