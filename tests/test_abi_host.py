@@ -148,9 +148,11 @@ def test_kernel_name_names_the_launch_plan(L):
     assert name(1, 16, 16) == "w8a8_linear_fused_kernel<2, 4, 2>"
     assert name(8, 4096, 8192) == "w8a8_linear_fused_kernel<8, 4, 4>"
     # wider windows (or K > 12288): one launch over ceil(M / 16) token blocks
-    # <token blocks, tiles per group>: one tile per group up to 512 tiles
+    # <token blocks, tiles per group>: one tile per group up to 512 tiles while
+    # the code matrix is at most 96 x 4096 bytes
     assert name(48, 4096, 4096) == "w8a8_linear_wide_kernel<3, 1>"
-    assert name(96, 4096, 12288) == "w8a8_linear_wide_kernel<6, 1>"
+    assert name(96, 4096, 12288) == "w8a8_linear_wide_kernel<6, 4>"
+    assert name(48, 4096, 12288) == "w8a8_linear_wide_kernel<3, 4>"
     assert name(96, 6144, 4096) == "w8a8_linear_wide_kernel<6, 1>"
     assert name(96, 24576, 4096) == "w8a8_linear_wide_kernel<6, 4>"
     assert name(9, 16, 16) == "w8a8_linear_wide_kernel<1, 1>"

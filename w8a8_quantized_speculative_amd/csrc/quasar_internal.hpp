@@ -68,7 +68,7 @@ struct WidePlan {
 // `grid` only enters the launch; the workspace is sized for kWideMaxGrid.
 WidePlan plan_wide(int64_t M, int64_t N, int64_t K, int grid);
 const char* wide_kernel_name(int mb, int tg);
-int wide_tiles_per_group(int64_t N, int grid);
+int wide_tiles_per_group(int64_t M, int64_t N, int64_t K, int grid);
 // Workgroups of a wide launch on the current device (0: cannot run there).
 int wide_grid_for_current_device();
 hipError_t launch_wide(const WidePlan& p, const uint16_t* x, const float* s, const int8_t* wq,

@@ -693,11 +693,15 @@ static_assert(wide_lds_of(6, 4) == Wide<6, 4>::LDS && wide_lds_of(3, 1) == Wide<
 // serve 4 tiles (a quarter of the code bytes per weight byte), but leave a
 // linear with few tiles with fewer groups than workgroups, so that a group's
 // K range is split across several workgroups that must hand INT32 partial
-// sums to each other at the end.  Up to 2 tiles per workgroup, groups of one
-// tile are used instead.
-int wide_tiles_per_group(int64_t N, int grid) {
+// sums to each other at the end (a few microseconds at the end of the launch).
+// With groups of one tile each workgroup instead reads the whole M x K code
+// matrix per tile.  Measured on MI355X: one-tile groups are faster up to 2
+// tiles per workgroup while the code matrix is at most 384 KB (96 x 4096);
+// beyond that (e.g. 96 x 12288) the code bytes cost more than the hand-over.
+int wide_tiles_per_group(int64_t M, int64_t N, int64_t K, int grid) {
   const int64_t tiles = (N + 15) / 16;
-  return tiles <= 2 * (int64_t)(grid > 0 ? grid : kWideMaxGrid) ? 1 : kMaxTG;
+  const bool few_tiles = tiles <= 2 * (int64_t)(grid > 0 ? grid : kWideMaxGrid);
+  return few_tiles && M * K <= 96 * 4096 ? 1 : kMaxTG;
 }
 
 WidePlan plan_wide(int64_t M, int64_t N, int64_t K, int grid) {
@@ -706,7 +710,7 @@ WidePlan plan_wide(int64_t M, int64_t N, int64_t K, int grid) {
   p.N = N;
   p.K = K;
   p.mb = (int)((M + 15) / 16);
-  p.tg = wide_tiles_per_group(N, grid);
+  p.tg = wide_tiles_per_group(M, N, K, grid);
   p.tiles = (int)((N + 15) / 16);
   p.nch = (int)((K + 63) / 64);
   p.groups = (p.tiles + p.tg - 1) / p.tg;
