@@ -70,6 +70,14 @@ RAGGED = [
     (112, 77, 3072), (128, 300, 4096), (16, 64, 4096), (40, 8000, 512), (24, 6144, 4096),
     # K beyond the one-launch small-window kernel, up to the largest supported K
     (6, 64, 16384), (1, 40, 65536), (50, 48, 20480),
+    # 4 to 5 tiles per workgroup: groups of 4 tiles split across workgroups
+    (20, 16400, 320), (100, 16384, 1040), (128, 16500, 2112), (9, 16390, 4160),
+    (70, 20000, 576),
+    # at least 16 tiles per workgroup: groups of 16 (8 above 96 tokens) whose
+    # activation fragments all four streamers share; every token-block count,
+    # ragged N and K (odd chunk counts), groups split across workgroups
+    (9, 65600, 320), (20, 66000, 208), (48, 70000, 208), (33, 66000, 96), (64, 65540, 576),
+    (70, 65600, 1040), (96, 65600, 64), (100, 65536, 192), (128, 66000, 320),
 ]
 
 
@@ -132,9 +140,10 @@ def test_qwen3_layer_linear_full_size_sampled(name, K, N, M):
     assert np.array_equal(unpack_weights(wq, N, K)[cols], ref["qw"])
 
 
-def test_lm_head_full_size_sampled():
-    """W8A8 LM head 4096 -> 151936 at M = 6."""
-    K, N, M = 4096, synth.QWEN3_8B_VOCAB, 6
+@pytest.mark.parametrize("M", [6, 48, 96, 128])
+def test_lm_head_full_size_sampled(M):
+    """W8A8 LM head 4096 -> 151936 at the verify window M = 6, 48, 96, 128."""
+    K, N = 4096, synth.QWEN3_8B_VOCAB
     announce("lm_head", M, N, K)
     key = (3, 0, 0)
     x = synth.activations(M, K, key)
@@ -145,7 +154,8 @@ def test_lm_head_full_size_sampled():
     check_against_oracle(x, s, w, y, acc, cols)
 
 
-@pytest.mark.parametrize("M,N,K", [(5, 33, 12288), (96, 300, 4096), (48, 6144, 4096)])
+@pytest.mark.parametrize("M,N,K", [(5, 33, 12288), (96, 300, 4096), (48, 6144, 4096),
+                                   (40, 17000, 1040), (96, 66000, 128)])
 def test_repeated_calls_are_bit_identical(M, N, K):
     """Partial sums shared between workgroups and LDS reductions are integer
     sums, and every launch of the wide kernel waits for its own token rows:
@@ -191,7 +201,8 @@ def test_interleaved_wide_shapes_on_one_stream():
     with no synchronisation between them, each against the oracle; a second
     round with new activations checks that no launch reads the rows of the
     one before it."""
-    cases = [(48, 500, 4096), (96, 130, 2048), (17, 2000, 1024), (128, 64, 4096), (9, 40, 12288)]
+    cases = [(48, 500, 4096), (96, 130, 2048), (17, 2000, 1024), (128, 64, 4096), (9, 40, 12288),
+             (40, 17000, 1024), (64, 66000, 64)]
     for rnd in range(2):
         outs = []
         for i, (M, N, K) in enumerate(cases):
