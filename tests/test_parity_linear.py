@@ -64,6 +64,12 @@ RAGGED = [
     (4, 520, 12288),
     # many tiles per compute unit: uneven contiguous tile ranges per workgroup
     (6, 9000, 1024), (2, 8336, 80), (8, 12000, 256),
+    # 1.5 tiles per workgroup (QKV-like), one more tile for the first
+    # workgroups and a last tile half past N, one tile per workgroup
+    (6, 6144, 512), (6, 6152, 512), (5, 24, 64), (3, 4104, 1024),
+    # 4 to 16 tiles per workgroup, ragged N, every K variant
+    (6, 16400, 512), (3, 20008, 1040), (8, 40000, 128), (1, 65536, 64), (4, 16400, 8000),
+    (6, 16400, 12288),
     # wide windows: every 16-token block count (1..8), ragged N and K, groups
     # shared by several workgroups (partial sums), and ranges that are empty
     (9, 100, 1024), (20, 64, 4096), (33, 1000, 2112), (64, 520, 4096), (80, 260, 1040),
@@ -155,7 +161,7 @@ def test_lm_head_full_size_sampled(M):
 
 
 @pytest.mark.parametrize("M,N,K", [(5, 33, 12288), (96, 300, 4096), (48, 6144, 4096),
-                                   (40, 17000, 1040), (96, 66000, 128)])
+                                   (40, 17000, 1040), (96, 66000, 128), (6, 16400, 256)])
 def test_repeated_calls_are_bit_identical(M, N, K):
     """Partial sums shared between workgroups and LDS reductions are integer
     sums, and every launch of the wide kernel waits for its own token rows:
@@ -202,7 +208,7 @@ def test_interleaved_wide_shapes_on_one_stream():
     round with new activations checks that no launch reads the rows of the
     one before it."""
     cases = [(48, 500, 4096), (96, 130, 2048), (17, 2000, 1024), (128, 64, 4096), (9, 40, 12288),
-             (40, 17000, 1024), (64, 66000, 64)]
+             (40, 17000, 1024), (64, 66000, 64), (5, 20000, 512), (6, 66000, 64)]
     for rnd in range(2):
         outs = []
         for i, (M, N, K) in enumerate(cases):

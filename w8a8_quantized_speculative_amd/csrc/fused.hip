@@ -14,8 +14,18 @@
 // Work decomposition (persistent grid, one workgroup per compute unit):
 //   * a tile is 16 output channels x all of K; workgroup b handles the
 //     contiguous tiles [floor(b*tiles/G), floor((b+1)*tiles/G)) (G = grid
-//     size): a workgroup streams one contiguous run of weights, which measured
-//     ~5% faster on the LM head than tiles G apart;
+//     size), computed as b q + floor(b r / G) with q, r = tiles / G, tiles % G
+//     from the host so that every term fits 32 bits: a workgroup
+//     streams one contiguous run of weights, which measured ~5% faster on the
+//     LM head than tiles G apart.  The 64-bit form of this division cost
+//     ~0.4 us per launch.  Measured alternatives: q = tiles / G tiles each
+//     plus one for the first tiles % G workgroups was as fast except on the
+//     LM head (3% slower); half tiles at the range ends (to balance QKV's 384
+//     tiles on 256 workgroups) were no faster, since a load with half its
+//     lanes masked costs the memory pipeline as much as a full one; and
+//     handing the last quarter of the tiles out from a device counter (the
+//     8 XCDs stream at rates up to 25% apart within a launch) was slower on
+//     every linear;
 //   * wavefronts are specialized.  A compute unit keeps only ~32-64 KB of
 //     vector-memory misses in flight, and a wavefront that issues beyond that
 //     stalls at issue until data returns.  So S *streamer* wavefronts own the
@@ -396,8 +406,8 @@ __device__ __forceinline__ void helper(const uint16_t* __restrict__ x, const flo
 template <int MT, int S, int NPH>
 __global__ __launch_bounds__(64 * (S + (NPH == 2 ? 4 : 8))) void w8a8_linear_fused_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ s, const int8_t* __restrict__ wq,
-    const float* __restrict__ wscale, int M, int N, int K, int tiles, uint16_t* __restrict__ y,
-    int32_t* __restrict__ acc_out) {
+    const float* __restrict__ wscale, int M, int N, int K, int tq, int tr, int G,
+    uint16_t* __restrict__ y, int32_t* __restrict__ acc_out) {
   using Var = Variant<NPH == 2 ? 0 : (NPH == 4 ? 1 : 2)>;
   static_assert(Var::S == S && Var::NPH == NPH, "variant");
   extern __shared__ __align__(16) char smem[];
@@ -417,9 +427,11 @@ __global__ __launch_bounds__(64 * (S + (NPH == 2 ? 4 : 8))) void w8a8_linear_fus
     if (tid == 0) *cnt = 0;
     ready[tid] = 0;
   }
-  const int G = gridDim.x;  // <= tiles, so every workgroup has at least one tile
-  const int first = (int)((int64_t)blockIdx.x * tiles / G);
-  const int T = (int)((int64_t)(blockIdx.x + 1) * tiles / G) - first;
+  // G (the grid size) <= tiles, so tq >= 1 and every workgroup has a tile;
+  // b tq < tiles and b tr < 256 G stay far inside 32 bits
+  const int b = blockIdx.x;
+  const int first = b * tq + (int)((unsigned int)(b * tr) / (unsigned int)G);
+  const int T = (b + 1) * tq + (int)((unsigned int)((b + 1) * tr) / (unsigned int)G) - first;
   if (wave < S) {
     streamer<MT, S, NPH, Var::NBUF, Var::NH>(wq, wscale, N, K, first, T, wave, lane, codes, Ks,
                                              red, wsl, ready);
@@ -440,7 +452,8 @@ hipError_t launch_variant(const FusedPlan& p, const uint16_t* x, const float* s,
                           smem_layout(Var::KMAX, MT, Var::S).bytes);
   if (attr != hipSuccess) return attr;
   kernel<<<dim3(p.grid), dim3(64 * Var::WAVES), p.lds, st>>>(
-      x, s, wq, w_scale, (int)p.M, (int)p.N, (int)p.K, p.tiles, y, acc_out);
+      x, s, wq, w_scale, (int)p.M, (int)p.N, (int)p.K, p.tiles / p.grid, p.tiles % p.grid, p.grid,
+      y, acc_out);
   return hipGetLastError();
 }
 
