@@ -183,6 +183,58 @@ def test_rejection_small_vocab_temperatures(T):
     assert band <= 2
 
 
+def chi_square_pvalue(counts, p):
+    """Pearson chi-square p-value; bins expecting fewer than 5 draws are pooled."""
+    from scipy.stats import chi2
+    n = counts.sum()
+    expected = n * np.asarray(p, np.float64)
+    small = expected < 5
+    obs = np.append(counts[~small], counts[small].sum())
+    exp_ = np.append(expected[~small], expected[small].sum())
+    if exp_[-1] < 5:  # the pooled bin joins the least likely remaining one
+        j = int(np.argmin(exp_[:-1]))
+        obs[j] += obs[-1]
+        exp_[j] += exp_[-1]
+        obs, exp_ = obs[:-1], exp_[:-1]
+    return float(chi2.sf(((obs - exp_) ** 2 / exp_).sum(), len(obs) - 1))
+
+
+@pytest.mark.parametrize("T", [0.5, 1.0])
+def test_rejection_is_lossless_chi_square(T):
+    """Losslessness of the GPU's speculative sampling with a one-hot draft.
+
+    Accepting draft d with probability p(d), and otherwise drawing from p with
+    d removed and renormalised, emits a first token distributed exactly as p.
+    After an accept, the bonus token is drawn from the next position's p.
+    12000 seeded sequences share one logits row.  For a likely, an unlikely
+    and a middling draft token, both distributions must pass a chi-square
+    test at p > 1e-6.  The seeds are fixed, so the outcome is deterministic.
+    """
+    V, n = 12, 12000
+    base = synth.logits(1, 1, V, (35, int(T * 10)), sigma=1.0)      # [1, 2, V]
+    probs = []
+    for pos in range(2):
+        v = orc.bf16_to_f32(base[0, pos]).astype(np.float64) / T
+        e = np.exp(v - v.max())
+        probs.append(e / e.sum())
+    lg = np.repeat(base, n, axis=0)
+    for d in (int(np.argmax(probs[0])), int(np.argmin(probs[0])), 5):
+        announce("rejection_lossless", T, d, n, V)
+        draft = np.full((n, 1), d, np.int32)
+        u = synth.uniforms(n, 1, (35, int(T * 10), d))
+        L, nxt, _, pd = gpu_accept(lg, draft, T, u)
+        assert np.allclose(pd[:, 0], probs[0][d], rtol=1e-4)
+        first = np.where(L >= 1, d, nxt)
+        assert chi_square_pvalue(np.bincount(first, minlength=V), probs[0]) > 1e-6
+        # the acceptance rate is p(d) (binomial, 5 standard deviations)
+        acc = int((L >= 1).sum())
+        sd = np.sqrt(n * probs[0][d] * (1 - probs[0][d]))
+        assert abs(acc - n * probs[0][d]) <= 5 * sd + 1
+        if acc >= 2000:
+            bonus = np.bincount(nxt[L >= 1], minlength=V)
+            assert chi_square_pvalue(bonus, probs[1]) > 1e-6
+
+
 def test_rejection_out_of_range_draft_rejected_with_full_residual():
     B, k, V = 2, 2, 3000
     lg = synth.logits(B, k, V, (33, 0))
