@@ -98,12 +98,17 @@ class Stack:
         self.V = V
         self.logits = self.linears[-1]["y"].view(self.B, self.k + 1, V)
         self.acc_ws = binding.new_workspace(binding.workspace_bytes_accept(self.B, self.k, V))
+        self.lmh_ws = binding.new_workspace(
+            binding.workspace_bytes_lm_head_verify(self.B, self.k, V, self.linears[-1]["K"]))
         self.draft = torch.zeros((self.B, self.k), dtype=torch.int32, device="cuda")
         self.accept_len = torch.zeros((self.B,), dtype=torch.int32, device="cuda")
         self.next_token = torch.zeros((self.B,), dtype=torch.int32, device="cuda")
         self.argmax = torch.zeros((self.B, self.k + 1), dtype=torch.int32, device="cuda")
         self.bytes_linear = [algorithmic_bytes(M, e["N"], e["K"]) for e in self.linears]
-        self.bytes_step = sum(self.bytes_linear) + 2 * M * V + 4 * self.B * self.k + 8 * self.B
+        # the linears, the drafts read and the accept lengths and next tokens
+        # written; the logits are not read back (at M <= 8 the LM head's own
+        # epilogue reduces them, so no pass over them is algorithmically needed)
+        self.bytes_step = sum(self.bytes_linear) + 4 * self.B * self.k + 8 * self.B
 
     def linear_call(self, e):
         from w8a8_quantized_speculative_amd import binding
@@ -121,10 +126,26 @@ class Stack:
         if st != 0:
             raise binding.QuasarError("quasar_verify_accept", st)
 
+    def lm_head_verify_call(self):
+        """The LM head and the greedy accept step in one library call."""
+        import ctypes
+        from w8a8_quantized_speculative_amd import binding
+        e = self.linears[-1]
+        L = binding.lib()
+        P = ctypes.c_void_p
+        st = L.quasar_lm_head_verify(
+            P(e["x"].data_ptr()), P(e["s"].data_ptr()), P(e["wq"].data_ptr()),
+            P(e["sw"].data_ptr()), self.B, self.k, self.V, e["K"], P(self.draft.data_ptr()), 0.0,
+            None, P(e["y"].data_ptr()), P(self.accept_len.data_ptr()),
+            P(self.next_token.data_ptr()), P(self.argmax.data_ptr()), None,
+            P(self.lmh_ws.data_ptr()), self.lmh_ws.numel(), binding._stream())
+        if st != 0:
+            raise binding.QuasarError("quasar_lm_head_verify", st)
+
     def step(self):
-        for e in self.linears:
+        for e in self.linears[:-1]:
             self.linear_call(e)
-        self.accept_call()
+        self.lm_head_verify_call()
 
 
 def plant_drafts(stack, n_sets: int):
@@ -445,6 +466,10 @@ def main():
             "weights_int8_gb": round(sum(e["N"] * e["K"] for e in stack.linears) / 1e9, 3),
             "timing": "HIP-graph replay of the whole step, new drafts per step; host clock "
                       "between torch.cuda.synchronize() calls",
+            "lm_head_and_accept": "one quasar_lm_head_verify call" + (
+                " (the LM head kernel's epilogue reduces the logits; one finalize kernel)"
+                if binding.workspace_bytes_linear(args.m, stack.V, 4096) == 0 else
+                " (LM head, then both accept passes)"),
         },
         "hbm_frac_of_peak": round(value / PEAK_HBM_GBS, 4),
         "verified_tokens_per_s": round(stack.B * tau_many / (ms * 1e-3), 1),

@@ -217,6 +217,45 @@ quasar_status quasar_verify_accept(const uint16_t* logits, const int32_t* draft,
                                    float* p_draft_out, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
+/* Workspace bytes quasar_lm_head_verify needs (pure host function); 0 for
+ * invalid or unsupported sizes. */
+size_t quasar_lm_head_verify_workspace_bytes(int64_t B, int64_t k, int64_t V, int64_t K);
+
+/*
+ * quasar_lm_head_verify -- the W8A8 LM head over the 1+k verify positions of B
+ * sequences, then the verification decision on its logits, in one call.
+ *
+ * The final logits come out of the quantized LM head dequantized to BF16
+ * [Quasar, zh page §2 item 3] and go straight to the accept step [pt page §2
+ * item 4].  The results are those of quasar_w8a8_linear with M = B (k+1),
+ * N = V (written to `logits`), followed by quasar_verify_accept on those
+ * logits, with the same arithmetic.  When M <= 8 and K <= 12288 the LM head
+ * kernel itself reduces each of its workgroups' channel ranges of every
+ * logits row to (max, lowest argmax) and, at T > 0, the range's sum of
+ * exp((l - max) / T), so the separate pass over the logits is skipped and one
+ * small kernel takes the decisions; other shapes run the linear and both
+ * accept passes.  (At T > 0 the sums are accumulated in another order than
+ * quasar_verify_accept's, so p_draft may differ from its value in the last
+ * binary32 bits.)
+ *
+ *   x, s, wq, w_scale  the LM head's inputs, as for quasar_w8a8_linear with
+ *                      M = B (k+1) rows of x ordered [B, k+1] and N = V
+ *   B, k, V, K  B >= 0, 0 <= k <= QUASAR_MAX_DRAFT, B (k+1) <= QUASAR_MAX_M,
+ *               V >= 1, 16 <= K <= QUASAR_MAX_K, K % 16 == 0
+ *   draft, temperature, uniforms, accept_len, next_token, argmax_out,
+ *   p_draft_out   as for quasar_verify_accept
+ *   logits      [B, k+1, V] bf16 bits (out)
+ *   workspace   at least quasar_lm_head_verify_workspace_bytes(B, k, V, K)
+ *               bytes, 256-byte aligned, any contents
+ * B == 0 is a no-op.  Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
+ */
+quasar_status quasar_lm_head_verify(const uint16_t* x, const float* s, const int8_t* wq,
+                                    const float* w_scale, int64_t B, int64_t k, int64_t V,
+                                    int64_t K, const int32_t* draft, float temperature,
+                                    const float* uniforms, uint16_t* logits, int32_t* accept_len,
+                                    int32_t* next_token, int32_t* argmax_out, float* p_draft_out,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * quasar_stream_copy -- diagnostic, not part of the method: copies `bytes`
  * bytes from src to dst (device pointers, 16-byte aligned, bytes a multiple of

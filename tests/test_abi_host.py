@@ -52,7 +52,7 @@ def test_status_strings(L):
     for code in range(5):
         assert L.quasar_status_string(code).decode().startswith("QUASAR_")
     assert b"UNKNOWN" in L.quasar_status_string(99)
-    assert L.quasar_abi_version() == 4
+    assert L.quasar_abi_version() == 5
 
 
 def test_workspace_queries_are_pure_host_and_monotone(L):
@@ -130,6 +130,43 @@ def test_accept_argument_errors(L):
     assert accept(L, nxt=FAKE + 2) == INVALID
     assert accept(L, ws=None) == WORKSPACE
     assert accept(L, wsb=16) == WORKSPACE
+
+
+def lm_head_verify(L, x=FAKE, s=FAKE, wq=FAKE, sw=FAKE, B=1, k=5, V=1000, K=64, draft=FAKE,
+                   T=0.0, u=None, logits=FAKE, acc=FAKE, nxt=FAKE, ws=FAKE, wsb=1 << 20):
+    return L.quasar_lm_head_verify(x, s, wq, sw, B, k, V, K, draft, T, u, logits, acc, nxt, None,
+                                   None, ws, wsb, None)
+
+
+def test_lm_head_verify_argument_errors(L):
+    assert lm_head_verify(L, B=-1) == INVALID
+    assert lm_head_verify(L, V=0) == INVALID
+    assert lm_head_verify(L, K=72) == INVALID
+    assert lm_head_verify(L, T=-1.0) == INVALID
+    assert lm_head_verify(L, T=float("nan")) == INVALID
+    assert lm_head_verify(L, T=1.0, u=None) == INVALID
+    assert lm_head_verify(L, draft=None) == INVALID
+    assert lm_head_verify(L, x=FAKE + 8) == INVALID
+    assert lm_head_verify(L, logits=None) == INVALID
+    assert lm_head_verify(L, k=64) == UNSUPPORTED
+    assert lm_head_verify(L, B=22, k=5) == UNSUPPORTED       # 132 token rows > 128
+    assert lm_head_verify(L, K=65536 + 16) == UNSUPPORTED
+    assert lm_head_verify(L, B=0) == OK
+    assert lm_head_verify(L, ws=None) == WORKSPACE
+    need = L.quasar_lm_head_verify_workspace_bytes(1, 5, 1000, 64)
+    assert need > 0 and lm_head_verify(L, wsb=need - 1) == WORKSPACE
+
+
+def test_lm_head_verify_workspace(L):
+    q = L.quasar_lm_head_verify_workspace_bytes
+    assert q(0, 5, 1000, 64) == 0 and q(1, 64, 1000, 64) == 0 and q(22, 5, 1000, 64) == 0
+    # fused: three [rows][workgroups] arrays of 4-byte partials
+    fused = q(1, 5, 151936, 4096)
+    assert 3 * 6 * 256 * 4 <= fused <= 3 * 6 * 256 * 4 + 3 * 256
+    # fallbacks: the linear's workspace plus the accept step's
+    for B, k, V, K in [(3, 5, 20000, 512), (1, 5, 3000, 16384), (1, 1, 600000, 64)]:
+        assert q(B, k, V, K) >= L.quasar_w8a8_workspace_bytes(B * (k + 1), V, K) + \
+            L.quasar_accept_workspace_bytes(B, k, V)
 
 
 def test_packed_weight_bytes(L):

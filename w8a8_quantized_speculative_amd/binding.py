@@ -42,6 +42,10 @@ _SIGNATURES = {
     "quasar_accept_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "quasar_verify_accept": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P,
                                             _P, _P, _P, _SZ, _P]),
+    "quasar_lm_head_verify_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64]),
+    "quasar_lm_head_verify": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P,
+                                             ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                                             _P]),
     "quasar_w8a8_kernel_name": (ctypes.c_char_p, [_I64, _I64, _I64]),
     "quasar_stream_copy": (ctypes.c_int, [_P, _P, _SZ, _P]),
 }
@@ -217,3 +221,49 @@ def quasar_verify_accept(logits: torch.Tensor, draft: torch.Tensor | None, tempe
         _ptr(logits), _ptr(draft), B, k, V, float(temperature), _ptr(uniforms), _ptr(acc_len),
         _ptr(nxt), _ptr(g), _ptr(pd), _ptr(workspace), nbytes, _stream()))
     return acc_len, nxt, g, pd
+
+
+def workspace_bytes_lm_head_verify(B: int, k: int, V: int, K: int) -> int:
+    return int(lib().quasar_lm_head_verify_workspace_bytes(B, k, V, K))
+
+
+def quasar_lm_head_verify(x: torch.Tensor, s: torch.Tensor, wq: PackedWeights,
+                          w_scale: torch.Tensor, B: int, draft: torch.Tensor | None,
+                          temperature: float = 0.0, uniforms: torch.Tensor | None = None,
+                          want_argmax: bool = False, want_p_draft: bool = False,
+                          logits: torch.Tensor | None = None,
+                          workspace: torch.Tensor | None = None):
+    """LM head over x [B*(k+1), K] bf16, then the accept step on its logits ->
+    (logits [B, k+1, V] bf16, accept_len [B], next_token [B], argmax or None,
+    p_draft or None)."""
+    M, K = x.shape
+    if B <= 0 or M % B:
+        raise ValueError("x must hold B * (k+1) rows")
+    kp1 = M // B
+    k = kp1 - 1
+    V = wq.N
+    if not isinstance(wq, PackedWeights) or wq.K != K:
+        raise ValueError("wq must be the PackedWeights of a linear with the same K")
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(s, torch.float32, (K,), "s")
+    _need(w_scale, torch.float32, (V,), "w_scale")
+    if k > 0 or draft is not None:
+        _need(draft, torch.int32, (B, k), "draft")
+    if uniforms is not None:
+        _need(uniforms, torch.float32, (B, kp1), "uniforms")
+    dev = x.device
+    if logits is None:
+        logits = torch.empty((B, kp1, V), dtype=torch.bfloat16, device=dev)
+    _need(logits, torch.bfloat16, (B, kp1, V), "logits")
+    acc_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    nxt = torch.empty((B,), dtype=torch.int32, device=dev)
+    g = torch.empty((B, kp1), dtype=torch.int32, device=dev) if want_argmax else None
+    pd = torch.empty((B, k), dtype=torch.float32, device=dev) if want_p_draft else None
+    if workspace is None:
+        workspace = new_workspace(workspace_bytes_lm_head_verify(B, k, V, K), dev)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("quasar_lm_head_verify", lib().quasar_lm_head_verify(
+        _ptr(x), _ptr(s), _ptr(wq), _ptr(w_scale), B, k, V, K, _ptr(draft), float(temperature),
+        _ptr(uniforms), _ptr(logits), _ptr(acc_len), _ptr(nxt), _ptr(g), _ptr(pd),
+        _ptr(workspace), nbytes, _stream()))
+    return logits, acc_len, nxt, g, pd

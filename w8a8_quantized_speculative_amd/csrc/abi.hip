@@ -23,6 +23,53 @@ quasar_status check_k(int64_t K) {
 
 constexpr int64_t kMaxRowsPerCall = (int64_t)1 << 30;
 
+// quasar_lm_head_verify's plan.  Fused: the one-launch linear's epilogue
+// writes the accept partials (one chunk per workgroup) and only the accept
+// finalize runs after it; the workspace holds the partials.  Otherwise the
+// linear and both accept passes run as in the two separate calls, and the
+// workspace is the linear's followed by the accept step's.
+struct LmHeadPlan {
+  bool fused;
+  FusedPlan fp;
+  AcceptPlan ap;
+  size_t off_pmax, off_pidx, off_psum;  // fused
+  size_t lin_bytes, off_acc;            // otherwise
+  size_t bytes;
+};
+
+LmHeadPlan plan_lm_head(int64_t B, int64_t k, int64_t V, int64_t K) {
+  LmHeadPlan p{};
+  const int64_t M = B * (k + 1);
+  p.ap = plan_accept(B, k, V);
+  p.fused = fused_supported(M, K);
+  if (p.fused) {
+    p.fp = plan_fused(M, V, K);
+    // a workgroup's channel range must fit one finalize scan
+    p.fused = 16 * (p.fp.tiles / p.fp.grid + 1) <= kAcceptChunk;
+  }
+  if (p.fused) {
+    p.ap.chunks = p.fp.grid;
+    p.ap.unit = 16;
+    p.ap.cq = p.fp.tiles / p.fp.grid;
+    p.ap.cr = p.fp.tiles % p.fp.grid;
+    p.ap.cG = p.fp.grid;
+    const size_t slots = (size_t)M * p.fp.grid;
+    size_t off = 0;
+    p.off_pmax = off;
+    off = align_up(off + slots * sizeof(float), kWsAlign);
+    p.off_pidx = off;
+    off = align_up(off + slots * sizeof(int32_t), kWsAlign);
+    p.off_psum = off;
+    off = align_up(off + slots * sizeof(float), kWsAlign);
+    p.bytes = off;
+  } else {
+    p.lin_bytes = fused_supported(M, K) ? 0 : plan_wide(M, V, K, kWideMaxGrid).bytes;
+    p.off_acc = align_up(p.lin_bytes, kWsAlign);
+    p.bytes = p.off_acc + p.ap.bytes;
+  }
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -38,7 +85,7 @@ const char* quasar_status_string(quasar_status status) {
   return "QUASAR_ERR_UNKNOWN";
 }
 
-int quasar_abi_version(void) { return 4; }
+int quasar_abi_version(void) { return 5; }
 
 quasar_status quasar_quantize_weights(const uint16_t* w, const float* s, int64_t N, int64_t K,
                                       int8_t* wq, float* w_scale, void* stream) {
@@ -146,6 +193,62 @@ quasar_status quasar_verify_accept(const uint16_t* logits, const int32_t* draft,
     return QUASAR_ERR_WORKSPACE;
   return hip_status(launch_accept(p, logits, draft, temperature, uniforms, accept_len, next_token,
                                   argmax_out, p_draft_out, workspace, (hipStream_t)stream));
+}
+
+size_t quasar_lm_head_verify_workspace_bytes(int64_t B, int64_t k, int64_t V, int64_t K) {
+  if (B <= 0 || k < 0 || k > QUASAR_MAX_DRAFT || V <= 0 || V > kMaxRowsPerCall ||
+      check_k(K) != QUASAR_OK || B * (k + 1) > QUASAR_MAX_M)
+    return 0;
+  return plan_lm_head(B, k, V, K).bytes;
+}
+
+quasar_status quasar_lm_head_verify(const uint16_t* x, const float* s, const int8_t* wq,
+                                    const float* w_scale, int64_t B, int64_t k, int64_t V,
+                                    int64_t K, const int32_t* draft, float temperature,
+                                    const float* uniforms, uint16_t* logits, int32_t* accept_len,
+                                    int32_t* next_token, int32_t* argmax_out, float* p_draft_out,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || k < 0 || V <= 0) return QUASAR_ERR_INVALID_ARG;
+  if (!(temperature >= 0.0f) || isinf(temperature)) return QUASAR_ERR_INVALID_ARG;  // NaN too
+  quasar_status st = check_k(K);
+  if (st != QUASAR_OK) return st;
+  if (k > QUASAR_MAX_DRAFT || V > kMaxRowsPerCall || B > QUASAR_MAX_M ||
+      B * (k + 1) > QUASAR_MAX_M)
+    return QUASAR_ERR_UNSUPPORTED;
+  if (B == 0) return QUASAR_OK;
+  if (!x || !s || !wq || !w_scale || !logits || !accept_len || !next_token)
+    return QUASAR_ERR_INVALID_ARG;
+  if (k > 0 && !draft) return QUASAR_ERR_INVALID_ARG;
+  if (temperature > 0.0f && !uniforms) return QUASAR_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(s, 16) || !aligned(wq, 16) || !aligned(w_scale, 4) ||
+      !aligned(logits, 2) || (draft && !aligned(draft, 4)) || !aligned(accept_len, 4) ||
+      !aligned(next_token, 4) || (uniforms && !aligned(uniforms, 4)) ||
+      (argmax_out && !aligned(argmax_out, 4)) || (p_draft_out && !aligned(p_draft_out, 4)))
+    return QUASAR_ERR_INVALID_ARG;
+  const LmHeadPlan p = plan_lm_head(B, k, V, K);
+  if (!workspace || workspace_bytes < p.bytes || !aligned(workspace, kWsAlign))
+    return QUASAR_ERR_WORKSPACE;
+  hipStream_t hs = (hipStream_t)stream;
+  char* ws = static_cast<char*>(workspace);
+  const int64_t M = B * (k + 1);
+  if (!p.fused) {
+    st = quasar_w8a8_linear(x, s, wq, w_scale, M, V, K, logits, nullptr,
+                            p.lin_bytes ? ws : nullptr, p.lin_bytes, stream);
+    if (st != QUASAR_OK) return st;
+    return quasar_verify_accept(logits, draft, B, k, V, temperature, uniforms, accept_len,
+                                next_token, argmax_out, p_draft_out, ws + p.off_acc, p.ap.bytes,
+                                stream);
+  }
+  float* pmax = reinterpret_cast<float*>(ws + p.off_pmax);
+  int32_t* pidx = reinterpret_cast<int32_t*>(ws + p.off_pidx);
+  float* psum = reinterpret_cast<float*>(ws + p.off_psum);
+  const bool sample = temperature > 0.0f;
+  const AcceptPartials parts{pmax, pidx, sample ? psum : nullptr, sample ? 1.0f / temperature : 0.0f};
+  hipError_t e = launch_fused(p.fp, x, s, wq, w_scale, logits, nullptr, hs, &parts);
+  if (e != hipSuccess) return QUASAR_ERR_HIP;
+  return hip_status(launch_accept_finalize(p.ap, logits, draft, temperature, uniforms, accept_len,
+                                           next_token, argmax_out, p_draft_out, pmax, pidx, psum,
+                                           hs));
 }
 
 }  // extern "C"

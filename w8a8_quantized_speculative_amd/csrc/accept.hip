@@ -9,6 +9,11 @@
 // Pass 2 (grid B): one workgroup per sequence merges the chunk partials of its
 // k+1 rows, takes the accept decisions in draft order and picks the next token
 // (argmax, or an inverse-CDF draw over the residual in index order).
+//
+// Pass 2 also serves the LM head whose own epilogue produced the partials
+// (one chunk per workgroup of that kernel): chunk c then starts at logit
+// 16 (c q + floor(c r / G)) instead of 2048 c.  Chunks are at most 2048 wide
+// either way.
 #include <float.h>
 #include <limits.h>
 
@@ -19,7 +24,7 @@ namespace quasar {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChunk = 2048;  // logits per pass-1 workgroup (8 per thread)
+constexpr int kChunk = kAcceptChunk;  // logits per pass-1 workgroup (8 per thread)
 constexpr int kMaxRows = 64;  // k + 1 <= 64
 
 struct ArgMax {
@@ -110,10 +115,32 @@ __global__ __launch_bounds__(kThreads) void accept_partial_kernel(
   }
 }
 
+// Chunk c covers logits [start(c), start(c + 1)) of a row: start(c) =
+// unit (c q + floor(c r / G)), capped at V.
+struct ChunkGeometry {
+  int unit, q, r, G;
+};
+
+__device__ __forceinline__ int64_t chunk_start(const ChunkGeometry& cg, int c, int64_t V) {
+  const int64_t u = (int64_t)c * cg.q + (int64_t)c * cg.r / cg.G;
+  return min(V, u * cg.unit);
+}
+
+// the chunk holding logit j (0 <= j < V): the last c with start(c) <= j
+__device__ __forceinline__ int chunk_of(const ChunkGeometry& cg, int chunks, int64_t j, int64_t V) {
+  int lo = 0, hi = chunks - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (chunk_start(cg, mid, V) <= j) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
 template <bool kSample>
 __global__ __launch_bounds__(kThreads) void accept_finalize_kernel(
     const uint16_t* __restrict__ logits, const int32_t* __restrict__ draft, int k, int64_t V,
-    int chunks, float inv_t, const float* __restrict__ uniforms, const float* __restrict__ pmax,
+    int chunks, ChunkGeometry cg, float inv_t, const float* __restrict__ uniforms,
+    const float* __restrict__ pmax,
     const int32_t* __restrict__ pidx, const float* __restrict__ psum,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ next_token,
     int32_t* __restrict__ argmax_out, float* __restrict__ p_draft_out) {
@@ -185,13 +212,13 @@ __global__ __launch_bounds__(kThreads) void accept_finalize_kernel(
     const int d = draft[(int64_t)b * k + L];
     if (d >= 0 && d < V) d_ex = d;
   }
-  const int c_ex = d_ex >= 0 ? d_ex / kChunk : -1;
+  const int c_ex = d_ex >= 0 ? chunk_of(cg, chunks, d_ex, V) : -1;
   // the chunk holding the rejected draft: its sum without that token
   float ex_sum = 0.0f;
   if (c_ex >= 0) {
     float part = 0.0f;
-    const int64_t j1 = min(V, (int64_t)(c_ex + 1) * kChunk);
-    for (int64_t j = (int64_t)c_ex * kChunk + threadIdx.x; j < j1; j += kThreads)
+    const int64_t j1 = chunk_start(cg, c_ex + 1, V);
+    for (int64_t j = chunk_start(cg, c_ex, V) + threadIdx.x; j < j1; j += kThreads)
       if (j != d_ex) part += expf((bf16_to_f32(logits[row * V + j]) - m) * inv_t);
     ex_sum = block_sum(part, sv);
   }
@@ -225,7 +252,8 @@ __global__ __launch_bounds__(kThreads) void accept_finalize_kernel(
   }
   __syncthreads();
   // ---- scan the chosen chunk in index order: thread t owns 8 consecutive logits
-  const int64_t base = (int64_t)s_cstar * kChunk;
+  const int64_t base = chunk_start(cg, s_cstar, V);
+  const int64_t end = chunk_start(cg, s_cstar + 1, V);  // at most kChunk past base
   constexpr int E = kChunk / kThreads;
   float rr[E];
   float run = 0.0f;
@@ -233,7 +261,7 @@ __global__ __launch_bounds__(kThreads) void accept_finalize_kernel(
   for (int e = 0; e < E; ++e) {
     const int64_t j = base + (int64_t)threadIdx.x * E + e;
     rr[e] = 0.0f;
-    if (j < V && j != d_ex) rr[e] = expf((bf16_to_f32(logits[row * V + j]) - m) * inv_t);
+    if (j < end && j != d_ex) rr[e] = expf((bf16_to_f32(logits[row * V + j]) - m) * inv_t);
     run += rr[e];
   }
   s_run[threadIdx.x] = run;
@@ -278,6 +306,10 @@ AcceptPlan plan_accept(int64_t B, int64_t k, int64_t V) {
   p.rows = B * (k + 1);
   p.chunk_len = kChunk;
   p.chunks = (int)((V + kChunk - 1) / kChunk);
+  p.unit = kChunk;
+  p.cq = 1;
+  p.cr = 0;
+  p.cG = 1;
   const size_t slots = (size_t)p.rows * p.chunks;
   size_t off = 0;
   p.off_max = off;
@@ -307,15 +339,28 @@ hipError_t launch_accept(const AcceptPlan& p, const uint16_t* logits, const int3
     accept_partial_kernel<false><<<g1, blk, 0, st>>>(logits, p.V, p.chunks, inv_t, pmax, pidx, psum);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 g2((unsigned)p.B);
+  return launch_accept_finalize(p, logits, draft, temperature, uniforms, accept_len, next_token,
+                                argmax_out, p_draft_out, pmax, pidx, psum, st);
+}
+
+hipError_t launch_accept_finalize(const AcceptPlan& p, const uint16_t* logits,
+                                  const int32_t* draft, float temperature, const float* uniforms,
+                                  int32_t* accept_len, int32_t* next_token, int32_t* argmax_out,
+                                  float* p_draft_out, const float* pmax, const int32_t* pidx,
+                                  const float* psum, hipStream_t st) {
+  const bool sample = temperature > 0.0f;
+  const float inv_t = sample ? 1.0f / temperature : 0.0f;
+  const ChunkGeometry cg{p.unit, p.cq, p.cr, p.cG};
+  const dim3 g2((unsigned)p.B), blk(kThreads);
   if (sample)
-    accept_finalize_kernel<true><<<g2, blk, 0, st>>>(logits, draft, (int)p.k, p.V, p.chunks, inv_t,
-                                                     uniforms, pmax, pidx, psum, accept_len,
+    accept_finalize_kernel<true><<<g2, blk, 0, st>>>(logits, draft, (int)p.k, p.V, p.chunks, cg,
+                                                     inv_t, uniforms, pmax, pidx, psum, accept_len,
                                                      next_token, argmax_out, p_draft_out);
   else
-    accept_finalize_kernel<false><<<g2, blk, 0, st>>>(logits, draft, (int)p.k, p.V, p.chunks, inv_t,
-                                                      uniforms, pmax, pidx, psum, accept_len,
-                                                      next_token, argmax_out, p_draft_out);
+    accept_finalize_kernel<false><<<g2, blk, 0, st>>>(logits, draft, (int)p.k, p.V, p.chunks, cg,
+                                                      inv_t, uniforms, pmax, pidx, psum,
+                                                      accept_len, next_token, argmax_out,
+                                                      p_draft_out);
   return hipGetLastError();
 }
 

@@ -52,6 +52,9 @@
 //     scales, fetched by streamer 0 with its last phase) go to LDS, and 64
 //     helper threads apply the dequant epilogue, 4 channels (8 bytes) per
 //     store.
+#include <float.h>
+#include <limits.h>
+
 #include "quasar_device.hpp"
 #include "quasar_internal.hpp"
 
@@ -240,7 +243,8 @@ __device__ __forceinline__ void helper(const uint16_t* __restrict__ x, const flo
                                        int lane,
                                        int8_t* codes, int Ks, const int32_t* red, const float* wsl,
                                        float* amax_part, float* qp, int* cnt, int* ready,
-                                       uint16_t* __restrict__ y, int32_t* __restrict__ acc_out) {
+                                       uint16_t* __restrict__ y, int32_t* __restrict__ acc_out,
+                                       AcceptPartials ap, int G) {
   constexpr int HT = 64 * NH;  // helper threads
   const int units = K >> 3;    // pieces of 8 K positions per token row
   v4i xv[UP][MT];
@@ -359,6 +363,20 @@ __device__ __forceinline__ void helper(const uint16_t* __restrict__ x, const flo
       __hip_atomic_fetch_add(ready + u, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
 
+  // LM-head epilogue: this thread's running (max, lowest argmax, sum of
+  // exp((l - max) / T)) over the logits it writes, in increasing channel order
+  float am_v = -FLT_MAX, am_s = 0.0f;
+  int am_i = INT_MAX;
+  auto track = [&](float v, int j) {
+    if (v > am_v) {
+      if (ap.psum) am_s = am_s * expf((am_v - v) * ap.inv_t) + 1.0f;
+      am_v = v;
+      am_i = j;
+    } else if (ap.psum) {
+      am_s += expf((v - am_v) * ap.inv_t);
+    }
+  };
+
   for (int t = 0; t < T; ++t) {
     const int tile = first + t;
     const int buf = t & 1;
@@ -392,7 +410,28 @@ __device__ __forceinline__ void helper(const uint16_t* __restrict__ x, const flo
         }
         if (acc_out)
           for (int i = 0; i < 4 && n0 + i < N; ++i) acc_out[(size_t)tt * N + n0 + i] = tv[i];
+        if (ap.pmax)
+          for (int i = 0; i < 4 && n0 + i < N; ++i) track(bf16_to_f32(o[i]), n0 + i);
       }
+    }
+  }
+  if (ap.pmax && ht < 64) {
+    // the four threads of token tt are lanes tt, tt + 16, tt + 32, tt + 48
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+      const float ov = __shfl_xor(am_v, off, kWave);
+      const int oi = __shfl_xor(am_i, off, kWave);
+      const float os = __shfl_xor(am_s, off, kWave);
+      const float m = fmaxf(am_v, ov);
+      if (ap.psum) am_s = am_s * expf((am_v - m) * ap.inv_t) + os * expf((ov - m) * ap.inv_t);
+      if (ov > am_v || (ov == am_v && oi < am_i)) am_i = oi;
+      am_v = m;
+    }
+    if (ht < M) {
+      const size_t slot = (size_t)ht * G + blockIdx.x;
+      ap.pmax[slot] = am_v;
+      ap.pidx[slot] = am_i;
+      if (ap.psum) ap.psum[slot] = am_s;
     }
   }
 }
@@ -407,7 +446,7 @@ template <int MT, int S, int NPH>
 __global__ __launch_bounds__(64 * (S + (NPH == 2 ? 4 : 8))) void w8a8_linear_fused_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ s, const int8_t* __restrict__ wq,
     const float* __restrict__ wscale, int M, int N, int K, int tq, int tr, int G,
-    uint16_t* __restrict__ y, int32_t* __restrict__ acc_out) {
+    uint16_t* __restrict__ y, int32_t* __restrict__ acc_out, AcceptPartials ap) {
   using Var = Variant<NPH == 2 ? 0 : (NPH == 4 ? 1 : 2)>;
   static_assert(Var::S == S && Var::NPH == NPH, "variant");
   extern __shared__ __align__(16) char smem[];
@@ -437,13 +476,14 @@ __global__ __launch_bounds__(64 * (S + (NPH == 2 ? 4 : 8))) void w8a8_linear_fus
                                              red, wsl, ready);
   } else {
     helper<MT, S, Var::NH, Var::UP>(x, s, M, N, K, first, T, tid - 64 * S, wave - S, lane, codes,
-                                    Ks, red, wsl, amax_part, qp, cnt, ready, y, acc_out);
+                                    Ks, red, wsl, amax_part, qp, cnt, ready, y, acc_out, ap, G);
   }
 }
 
 template <int MT, int V>
 hipError_t launch_variant(const FusedPlan& p, const uint16_t* x, const float* s, const int8_t* wq,
-                          const float* w_scale, uint16_t* y, int32_t* acc_out, hipStream_t st) {
+                          const float* w_scale, uint16_t* y, int32_t* acc_out, hipStream_t st,
+                          const AcceptPartials& ap) {
   using Var = Variant<V>;
   auto kernel = &w8a8_linear_fused_kernel<MT, Var::S, Var::NPH>;
   static const hipError_t attr =
@@ -453,17 +493,18 @@ hipError_t launch_variant(const FusedPlan& p, const uint16_t* x, const float* s,
   if (attr != hipSuccess) return attr;
   kernel<<<dim3(p.grid), dim3(64 * Var::WAVES), p.lds, st>>>(
       x, s, wq, w_scale, (int)p.M, (int)p.N, (int)p.K, p.tiles / p.grid, p.tiles % p.grid, p.grid,
-      y, acc_out);
+      y, acc_out, ap);
   return hipGetLastError();
 }
 
 template <int MT>
 hipError_t launch_mt(const FusedPlan& p, const uint16_t* x, const float* s, const int8_t* wq,
-                     const float* w_scale, uint16_t* y, int32_t* acc_out, hipStream_t st) {
+                     const float* w_scale, uint16_t* y, int32_t* acc_out, hipStream_t st,
+                     const AcceptPartials& ap) {
   switch (p.variant) {
-    case 0: return launch_variant<MT, 0>(p, x, s, wq, w_scale, y, acc_out, st);
-    case 1: return launch_variant<MT, 1>(p, x, s, wq, w_scale, y, acc_out, st);
-    default: return launch_variant<MT, 2>(p, x, s, wq, w_scale, y, acc_out, st);
+    case 0: return launch_variant<MT, 0>(p, x, s, wq, w_scale, y, acc_out, st, ap);
+    case 1: return launch_variant<MT, 1>(p, x, s, wq, w_scale, y, acc_out, st, ap);
+    default: return launch_variant<MT, 2>(p, x, s, wq, w_scale, y, acc_out, st, ap);
   }
 }
 
@@ -506,12 +547,14 @@ const char* fused_kernel_name(const FusedPlan& p) {
 }
 
 hipError_t launch_fused(const FusedPlan& p, const uint16_t* x, const float* s, const int8_t* wq,
-                        const float* w_scale, uint16_t* y, int32_t* acc_out, hipStream_t st) {
+                        const float* w_scale, uint16_t* y, int32_t* acc_out, hipStream_t st,
+                        const AcceptPartials* partials) {
+  const AcceptPartials ap = partials ? *partials : AcceptPartials{nullptr, nullptr, nullptr, 0.0f};
   switch (p.mt) {
-    case 2: return launch_mt<2>(p, x, s, wq, w_scale, y, acc_out, st);
-    case 4: return launch_mt<4>(p, x, s, wq, w_scale, y, acc_out, st);
-    case 6: return launch_mt<6>(p, x, s, wq, w_scale, y, acc_out, st);
-    default: return launch_mt<8>(p, x, s, wq, w_scale, y, acc_out, st);
+    case 2: return launch_mt<2>(p, x, s, wq, w_scale, y, acc_out, st, ap);
+    case 4: return launch_mt<4>(p, x, s, wq, w_scale, y, acc_out, st, ap);
+    case 6: return launch_mt<6>(p, x, s, wq, w_scale, y, acc_out, st, ap);
+    default: return launch_mt<8>(p, x, s, wq, w_scale, y, acc_out, st, ap);
   }
 }
 

@@ -33,12 +33,24 @@ struct FusedPlan {
   int lds;    // dynamic LDS bytes
 };
 
+// Optional epilogue of the one-launch linear when it computes an LM head: per
+// workgroup (a contiguous range of output channels) and token row, the
+// (max, lowest argmax) of the BF16 logits it wrote and, when inv_t > 0, the
+// sum of exp((l - max) * inv_t).  Written at [row * grid + workgroup].
+struct AcceptPartials {
+  float* pmax;
+  int32_t* pidx;
+  float* psum;  // NULL at T = 0
+  float inv_t;
+};
+
 bool fused_supported(int64_t M, int64_t K);
 // Name of the kernel of a one-launch plan (static storage).
 const char* fused_kernel_name(const FusedPlan& p);
 FusedPlan plan_fused(int64_t M, int64_t N, int64_t K);
 hipError_t launch_fused(const FusedPlan& p, const uint16_t* x, const float* s, const int8_t* wq,
-                        const float* w_scale, uint16_t* y, int32_t* acc_out, hipStream_t st);
+                        const float* w_scale, uint16_t* y, int32_t* acc_out, hipStream_t st,
+                        const AcceptPartials* partials = nullptr);
 
 // ---------------------------------------------------------------------------
 // Wide-window plan (9 <= M <= 128, or K > 12288): one launch of a persistent
@@ -78,9 +90,15 @@ hipError_t launch_wide(const WidePlan& p, const uint16_t* x, const float* s, con
 // ---------------------------------------------------------------------------
 // Accept plan: each logits row is cut into `chunks` pieces of `chunk_len`.
 // ---------------------------------------------------------------------------
+constexpr int kAcceptChunk = 2048;  // widest chunk the accept finalize scans (8 per thread)
+
 struct AcceptPlan {
   int64_t B, k, V, rows;
   int chunk_len, chunks;
+  // chunk c covers logits [unit (c cq + floor(c cr / cG)), ...) of a row:
+  // 2048 c for the accept kernels' own partials, a workgroup's tile range when
+  // an LM-head launch produced them
+  int unit, cq, cr, cG;
   size_t off_max, off_idx, off_sum, bytes;
 };
 
@@ -99,6 +117,13 @@ hipError_t launch_accept(const AcceptPlan& p, const uint16_t* logits, const int3
                          float temperature, const float* uniforms, int32_t* accept_len,
                          int32_t* next_token, int32_t* argmax_out, float* p_draft_out,
                          void* workspace, hipStream_t st);
+
+// Pass 2 alone, over partials [rows][p.chunks] made elsewhere (the LM head).
+hipError_t launch_accept_finalize(const AcceptPlan& p, const uint16_t* logits,
+                                  const int32_t* draft, float temperature, const float* uniforms,
+                                  int32_t* accept_len, int32_t* next_token, int32_t* argmax_out,
+                                  float* p_draft_out, const float* pmax, const int32_t* pidx,
+                                  const float* psum, hipStream_t st);
 
 // Diagnostic plain copy (16-byte vectors), bytes % 16 == 0.
 hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
