@@ -56,10 +56,11 @@ __all__ = [
     "smooth_weights", "quantize_weights", "smooth_activations",
     "quantize_activations", "int_matmul", "dequantize", "dequantize_f64",
     "w8a8_linear", "w8a8_linear_rows", "argmax_lowest", "greedy_accept",
-    "softmax_f64", "rejection_accept",
+    "softmax_f64", "rejection_accept", "QMAX_W4", "quantize_weights_w4", "w4a8_linear_rows",
 ]
 
 QMAX = 127  # symmetric INT8: codes in [-127, 127]
+QMAX_W4 = 7  # symmetric INT4 weights (the 4-bit variant): codes in [-7, 7]
 
 
 # --------------------------------------------------------------------------
@@ -95,12 +96,13 @@ def rn32_reciprocal(s: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 # symmetric per-row quantizer   [pt §2: symmetric uniform quantization]
 # --------------------------------------------------------------------------
-def quantize_rows(v: np.ndarray):
-    """Per-row symmetric INT8 quantization of a float32 matrix.
+def quantize_rows(v: np.ndarray, qmax: int = QMAX):
+    """Per-row symmetric quantization of a float32 matrix to [-qmax, qmax].
 
     For each row: A = max |v| (exact); if A == 0 the codes are 0 and the scale
-    is 0; otherwise scale = RN32(A / 127), inv = RN32(127 / A) and
-    code = clamp(round_half_even(RN32(v * inv)), -127, 127).
+    is 0; otherwise scale = RN32(A / qmax), inv = RN32(qmax / A) and
+    code = clamp(round_half_even(RN32(v * inv)), -qmax, qmax).  qmax = 127 is
+    INT8; the 4-bit weight variant uses qmax = 7.
     Returns (codes int8 [R, C], scale float32 [R]).
     """
     v = np.asarray(v, dtype=np.float32)
@@ -112,11 +114,11 @@ def quantize_rows(v: np.ndarray):
         a = np.float32(np.max(np.abs(row))) if row.size else np.float32(0)
         if a == 0:
             continue
-        scale[r] = np.float32(np.float64(a) / QMAX)
-        inv = np.float32(QMAX / np.float64(a))
+        scale[r] = np.float32(np.float64(a) / qmax)
+        inv = np.float32(qmax / np.float64(a))
         prod = row * inv                      # binary32 product, one rounding
         q = np.rint(prod)                     # ties to even
-        codes[r] = np.clip(q, -QMAX, QMAX).astype(np.int8)
+        codes[r] = np.clip(q, -qmax, qmax).astype(np.int8)
     return codes, scale
 
 
@@ -132,6 +134,15 @@ def smooth_weights(w_bits: np.ndarray, s: np.ndarray) -> np.ndarray:
 def quantize_weights(w_bits: np.ndarray, s: np.ndarray):
     """Smoothed weights -> (INT8 codes [N, K], per-output-channel scale [N])."""
     return quantize_rows(smooth_weights(w_bits, s))
+
+
+def quantize_weights_w4(w_bits: np.ndarray, s: np.ndarray):
+    """4-bit verifier weights [pt §5 and zh §5: lower-bit verification as future
+    work].  The pages give no group size, zero point or range, so this reads
+    them as the INT8 rule at qmax = 7: the same smoothed weights, one symmetric
+    scale per output channel, codes in [-7, 7].
+    Returns (codes int8 [N, K] in [-7, 7], scale float32 [N])."""
+    return quantize_rows(smooth_weights(w_bits, s), qmax=QMAX_W4)
 
 
 # --------------------------------------------------------------------------
@@ -199,6 +210,15 @@ def w8a8_linear_rows(x_bits: np.ndarray, s: np.ndarray, w_rows_bits: np.ndarray)
     and multiplied exactly as it would be inside the full matrix.
     """
     qw, sw = quantize_weights(w_rows_bits, s)
+    out = w8a8_linear(x_bits, s, qw, sw)
+    out["qw"], out["sw"] = qw, sw
+    return out
+
+
+def w4a8_linear_rows(x_bits: np.ndarray, s: np.ndarray, w_rows_bits: np.ndarray):
+    """The linear with 4-bit weights: INT4 weight codes (quantize_weights_w4),
+    the same dynamic INT8 activations, exact integer accumulation and dequant."""
+    qw, sw = quantize_weights_w4(w_rows_bits, s)
     out = w8a8_linear(x_bits, s, qw, sw)
     out["qw"], out["sw"] = qw, sw
     return out

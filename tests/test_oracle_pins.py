@@ -123,18 +123,20 @@ def test_smoothing_balances_channel_maxima(literal):
 
 
 # ---------------------------------------------------------------- P3 / P4: quantizer
-def test_quantizer_invariants():
+@pytest.mark.parametrize("qmax", [127, 7])
+def test_quantizer_invariants(qmax):
+    """INT8 (qmax 127) and the 4-bit weight variant (qmax 7)."""
     g = np.random.default_rng(7)
     v = (g.standard_normal((50, 333)) * g.uniform(0.01, 100, (50, 1))).astype(np.float32)
     v[3] = 0.0
-    q, sc = orc.quantize_rows(v)
+    q, sc = orc.quantize_rows(v, qmax=qmax)
     assert q.dtype == np.int8 and sc.dtype == np.float32
-    assert q.min() >= -127 and q.max() <= 127
+    assert q.min() >= -qmax and q.max() <= qmax
     for r in range(v.shape[0]):
         if not np.any(v[r]):
             assert sc[r] == 0 and not np.any(q[r])
             continue
-        assert np.max(np.abs(q[r].astype(np.int32))) == 127
+        assert np.max(np.abs(q[r].astype(np.int32))) == qmax
         err = np.abs(q[r].astype(np.float64) * np.float64(sc[r]) - v[r].astype(np.float64))
         assert np.all(err <= np.float64(sc[r]) * (0.5 + 2.0**-14))
         order = np.argsort(v[r], kind="stable")
@@ -150,6 +152,55 @@ def test_quantizer_rounds_half_to_even_when_scale_is_one():
     assert sc[0] == 1.0
     assert q[0, 0] == 127
     assert list(q[0, 1:].astype(int)) == [c[1] for c in cases]
+
+
+def test_w4_quantizer_rounds_half_to_even_when_scale_is_one():
+    """absmax = 7 makes inv = 1 and scale = 1 at qmax 7: codes are round-half-even(v)."""
+    vals = np.array([7.0, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 3.49, -6.5, 6.5], np.float32)
+    q, sc = orc.quantize_rows(vals[None, :], qmax=7)
+    assert sc[0] == 1.0
+    assert q[0].tolist() == [7, 0, 2, 2, 0, -2, -2, 3, -6, 6]
+
+
+def test_w4_textbook_case_unit_smoothing_integer_inputs():
+    """s = 1, integer weights in [-7, 7] with row absmax 7 and integer activations
+    with row absmax 127: the 4-bit codes are the weights, both scales are 1, acc
+    is the integer matrix product and Y its bf16 rounding."""
+    g = np.random.default_rng(18)
+    M, N, K = 6, 29, 256
+    xi = g.integers(-127, 128, (M, K)); xi[:, 3] = -127
+    wi = g.integers(-7, 8, (N, K)); wi[:, 5] = 7
+    s = np.ones(K, np.float32)
+    out = orc.w4a8_linear_rows(bf16(xi), s, bf16(wi))
+    assert np.array_equal(out["qw"], wi.astype(np.int8)) and np.all(out["sw"] == 1)
+    want = xi.astype(np.int64) @ wi.astype(np.int64).T
+    assert np.array_equal(out["acc"], want)
+    assert np.array_equal(out["y"], torch.from_numpy(want.astype(np.float32)).to(torch.bfloat16)
+                          .view(torch.int16).numpy().view(np.uint16))
+
+
+def test_w4_output_stays_within_the_quantization_error_bound():
+    """Each product term of the 4-bit linear is within the two quantizers' error
+    bounds: |acc sx sw - xs . w'| <= sum_k (|xs_k| eps_w + |w'_k| eps_x + eps_x eps_w)
+    with eps = scale (1/2 + 2^-14) per operand; Y is within one bf16 rounding of
+    acc sx sw."""
+    x, w, s = synth.linear_case(6, 512, 64, (0, 2), n_outliers=3, fixed_scale=40.0)
+    out = orc.w4a8_linear_rows(x, s, w)
+    xs = orc.smooth_activations(x, s).astype(np.float64)
+    wp = orc.smooth_weights(w, s).astype(np.float64)
+    ex = np.float64(out["sx"])[:, None] * (0.5 + 2.0**-14)
+    ew = np.float64(out["sw"])[:, None] * (0.5 + 2.0**-14)
+    bound = np.abs(xs) @ np.broadcast_to(ew, wp.shape).T + ex * np.abs(wp).sum(1)[None, :] \
+        + ex * ew.T * xs.shape[1]
+    exact = orc.dequantize_f64(out["acc"], out["sx"], out["sw"])
+    assert np.all(np.abs(exact - xs @ wp.T) <= bound * (1 + 1e-6) + 1e-30)
+    got = f(out["y"]).astype(np.float64)
+    assert np.all(np.abs(got - exact) <= np.abs(exact) * 2.0**-8 * 1.0001 + 1e-37)
+    # and 4 bits cost accuracy: the INT8 result is the closer one on most entries
+    out8 = orc.w8a8_linear_rows(x, s, w)
+    e4 = np.abs(f(out["y"]).astype(np.float64) - xs @ wp.T)
+    e8 = np.abs(f(out8["y"]).astype(np.float64) - xs @ wp.T)
+    assert np.mean(e8 < e4) > 0.8
 
 
 def test_hand_worked_linear():
