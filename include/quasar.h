@@ -257,6 +257,55 @@ quasar_status quasar_lm_head_verify(const uint16_t* x, const float* s, const int
                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * 4-bit weight variant.  The pages name verification with fewer bits (4 or 2)
+ * as future work [Quasar, pt page §5; zh page §5] without fixing a scheme; this
+ * library reads it as the INT8 weight rule at 4 bits: the same smoothed
+ * weights W diag(s)^-1, one symmetric scale per output channel,
+ * scale = RN32(absmax / 7), codes = clamp(rint(RN32(w' * RN32(7 / absmax))),
+ * -7, 7); the activations stay dynamic per-token INT8, and the product is the
+ * same exact integer accumulation and dequant as quasar_w8a8_linear.  It halves
+ * the resident weight bytes that bound a verify step.
+ *
+ * Layout of wq4 (K % 128 == 0): per 16-row tile t and pair of 64-wide chunks
+ * (2c, 2c+1), a 1 KB block; byte ((t*CP + c)*64 + g*16 + r)*16 + b (CP = K/128)
+ * holds the code of row 16t + r at K position 64(2c) + 16g + b in its low
+ * nibble and at 64(2c+1) + 16g + b in its high nibble, as 4-bit two's
+ * complement.  Rows past N hold 0.  quasar_packed_weight_bytes_w4 gives the
+ * size.
+ */
+size_t quasar_packed_weight_bytes_w4(int64_t N, int64_t K);
+
+/*
+ * quasar_quantize_weights_w4 -- offline 4-bit weight preparation (see above).
+ *   w, s, N, K, w_scale  as for quasar_quantize_weights; K % 128 == 0
+ *   wq4      packed 4-bit codes, quasar_packed_weight_bytes_w4(N, K) bytes,
+ *            16-byte aligned (out)
+ * Errors: INVALID_ARG (including K % 128 != 0), UNSUPPORTED, HIP.
+ */
+quasar_status quasar_quantize_weights_w4(const uint16_t* w, const float* s, int64_t N, int64_t K,
+                                         int8_t* wq4, float* w_scale, void* stream);
+
+/*
+ * quasar_w4a8_linear -- the verify linear with 4-bit weights: y = BF16(
+ * RN32(RN32(RN32(acc) * sx_m) * sw_n)) with acc = sum_k qx[m,k] * qw4[n,k]
+ * exact, qx the dynamic per-token INT8 codes of RN32(x * s) as in
+ * quasar_w8a8_linear.  One kernel launch, no workspace.
+ *   x, s, y, acc_out  as for quasar_w8a8_linear
+ *   wq4, w_scale      from quasar_quantize_weights_w4
+ *   M, N, K           1 <= M <= 8 (the verify window of one to a few
+ *                     sequences), N >= 0, 128 <= K <= 12288, K % 128 == 0
+ * M == 0 or N == 0 is a no-op.  Errors: INVALID_ARG (including K % 128 != 0),
+ * UNSUPPORTED (M > 8 or K > 12288), HIP.
+ */
+quasar_status quasar_w4a8_linear(const uint16_t* x, const float* s, const int8_t* wq4,
+                                 const float* w_scale, int64_t M, int64_t N, int64_t K,
+                                 uint16_t* y, int32_t* acc_out, void* stream);
+
+/* Profiler name of the kernel quasar_w4a8_linear launches for M x N x K ("" if
+ * unsupported); a diagnostic for the benchmark and profiles. */
+const char* quasar_w4a8_kernel_name(int64_t M, int64_t N, int64_t K);
+
+/*
  * quasar_stream_copy -- diagnostic, not part of the method: copies `bytes`
  * bytes from src to dst (device pointers, 16-byte aligned, bytes a multiple of
  * 16, non-overlapping) with 16-byte streaming loads and stores.  A copy of B

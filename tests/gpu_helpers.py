@@ -44,3 +44,27 @@ def unpack_weights(packed, N: int, K: int, keep_padding: bool = False) -> np.nda
     a = np.asarray(packed, dtype=np.int8)[: T * C * 1024].reshape(T, C, 4, 16, 16)
     w = a.transpose(0, 3, 1, 2, 4).reshape(T * 16, C * 64)
     return w if keep_padding else w[:N, :K]
+
+
+def unpack_weights_w4(packed, N: int, K: int, keep_padding: bool = False) -> np.ndarray:
+    """4-bit packed weights (include/quasar.h layout) -> row-major int8 [N, K].
+
+    Byte ((t*CP + c)*64 + g*16 + r)*16 + b holds row 16t + r: column
+    128c + 16g + b in its low nibble, 128c + 64 + 16g + b in its high nibble,
+    as 4-bit two's complement.
+    """
+    if hasattr(packed, "codes"):
+        packed = packed.codes
+    if isinstance(packed, torch.Tensor):
+        packed = packed.cpu().numpy()
+    T, CP = (N + 15) // 16, K // 128
+    a = np.asarray(packed, dtype=np.uint8)[: T * CP * 1024].reshape(T, CP, 4, 16, 16)
+    lo = (a & 0x0F).astype(np.int16)
+    hi = (a >> 4).astype(np.int16)
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    w = np.empty((T, 16, CP, 2, 4, 16), np.int16)        # [t, r, c, half, g, b]
+    w[:, :, :, 0] = lo.transpose(0, 3, 1, 2, 4)
+    w[:, :, :, 1] = hi.transpose(0, 3, 1, 2, 4)
+    w = w.reshape(T * 16, K).astype(np.int8)
+    return w if keep_padding else w[:N, :K]

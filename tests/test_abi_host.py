@@ -52,7 +52,7 @@ def test_status_strings(L):
     for code in range(5):
         assert L.quasar_status_string(code).decode().startswith("QUASAR_")
     assert b"UNKNOWN" in L.quasar_status_string(99)
-    assert L.quasar_abi_version() == 5
+    assert L.quasar_abi_version() == 6
 
 
 def test_workspace_queries_are_pure_host_and_monotone(L):
@@ -167,6 +167,29 @@ def test_lm_head_verify_workspace(L):
     for B, k, V, K in [(3, 5, 20000, 512), (1, 5, 3000, 16384), (1, 1, 600000, 64)]:
         assert q(B, k, V, K) >= L.quasar_w8a8_workspace_bytes(B * (k + 1), V, K) + \
             L.quasar_accept_workspace_bytes(B, k, V)
+
+
+def test_w4_argument_errors_and_sizes(L):
+    qw4 = L.quasar_quantize_weights_w4
+    assert qw4(FAKE, FAKE, 10, 64, FAKE, FAKE, None) == INVALID     # K % 128 != 0
+    assert qw4(FAKE, FAKE, 10, 8, FAKE, FAKE, None) == INVALID
+    assert qw4(FAKE, FAKE, 0, 128, None, None, None) == OK
+    assert qw4(FAKE, FAKE + 4, 10, 128, FAKE, FAKE, None) == INVALID
+    lin4 = lambda M=6, N=32, K=128, x=FAKE, y=FAKE: L.quasar_w4a8_linear(
+        x, FAKE, FAKE, FAKE, M, N, K, y, None, None)
+    assert lin4(K=192) == INVALID
+    assert lin4(M=9) == UNSUPPORTED                                 # the 4-bit kernel is M <= 8
+    assert lin4(K=12288 + 128) == UNSUPPORTED
+    assert lin4(M=0) == OK and lin4(N=0) == OK
+    assert lin4(x=None) == INVALID and lin4(y=FAKE + 1) == INVALID
+    assert L.quasar_packed_weight_bytes_w4(4096, 4096) == 4096 * 4096 // 2
+    assert L.quasar_packed_weight_bytes_w4(17, 256) == 2 * 2 * 1024
+    assert L.quasar_packed_weight_bytes_w4(16, 192) == 0
+    name = lambda M, N, K: L.quasar_w4a8_kernel_name(M, N, K).decode()
+    assert name(6, 4096, 4096) == "w4a8_linear_fused_kernel<6, 4, 1>"
+    assert name(6, 4096, 12288) == "w4a8_linear_fused_kernel<6, 4, 3>"
+    assert name(1, 16, 8192) == "w4a8_linear_fused_kernel<2, 4, 2>"
+    assert name(9, 16, 128) == "" and name(6, 16, 192) == ""
 
 
 def test_packed_weight_bytes(L):

@@ -47,6 +47,10 @@ _SIGNATURES = {
                                              ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _SZ,
                                              _P]),
     "quasar_w8a8_kernel_name": (ctypes.c_char_p, [_I64, _I64, _I64]),
+    "quasar_packed_weight_bytes_w4": (_SZ, [_I64, _I64]),
+    "quasar_quantize_weights_w4": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P]),
+    "quasar_w4a8_linear": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P]),
+    "quasar_w4a8_kernel_name": (ctypes.c_char_p, [_I64, _I64, _I64]),
     "quasar_stream_copy": (ctypes.c_int, [_P, _P, _SZ, _P]),
 }
 
@@ -135,10 +139,11 @@ def packed_weight_bytes(N: int, K: int) -> int:
 
 
 class PackedWeights:
-    """Tile-packed INT8 codes of an N x K linear (layout in include/quasar.h)."""
+    """Tile-packed INT8 (bits = 8) or 4-bit (bits = 4) codes of an N x K linear
+    (layouts in include/quasar.h)."""
 
-    def __init__(self, codes: torch.Tensor, N: int, K: int):
-        self.codes, self.N, self.K = codes, N, K
+    def __init__(self, codes: torch.Tensor, N: int, K: int, bits: int = 8):
+        self.codes, self.N, self.K, self.bits = codes, N, K, bits
 
     def data_ptr(self):
         return self.codes.data_ptr()
@@ -177,8 +182,8 @@ def quasar_w8a8_linear(x: torch.Tensor, s: torch.Tensor, wq: PackedWeights, w_sc
     """Y [M, N] bf16 = dequant(quant(X diag(s)) @ W8^T) for X [M, K] bf16."""
     M, K = x.shape
     N = wq.N
-    if not isinstance(wq, PackedWeights) or wq.K != K:
-        raise ValueError("wq must be the PackedWeights of a linear with the same K")
+    if not isinstance(wq, PackedWeights) or wq.K != K or wq.bits != 8:
+        raise ValueError("wq must be the INT8 PackedWeights of a linear with the same K")
     _need(x, torch.bfloat16, (M, K), "x")
     _need(s, torch.float32, (K,), "s")
     _need(w_scale, torch.float32, (N,), "w_scale")
@@ -242,8 +247,8 @@ def quasar_lm_head_verify(x: torch.Tensor, s: torch.Tensor, wq: PackedWeights,
     kp1 = M // B
     k = kp1 - 1
     V = wq.N
-    if not isinstance(wq, PackedWeights) or wq.K != K:
-        raise ValueError("wq must be the PackedWeights of a linear with the same K")
+    if not isinstance(wq, PackedWeights) or wq.K != K or wq.bits != 8:
+        raise ValueError("wq must be the INT8 PackedWeights of a linear with the same K")
     _need(x, torch.bfloat16, (M, K), "x")
     _need(s, torch.float32, (K,), "s")
     _need(w_scale, torch.float32, (V,), "w_scale")
@@ -267,3 +272,47 @@ def quasar_lm_head_verify(x: torch.Tensor, s: torch.Tensor, wq: PackedWeights,
         _ptr(uniforms), _ptr(logits), _ptr(acc_len), _ptr(nxt), _ptr(g), _ptr(pd),
         _ptr(workspace), nbytes, _stream()))
     return logits, acc_len, nxt, g, pd
+
+
+# ------------------------------------------------------- 4-bit weight variant
+def packed_weight_bytes_w4(N: int, K: int) -> int:
+    return int(lib().quasar_packed_weight_bytes_w4(N, K))
+
+
+def w4a8_kernel_name(M: int, N: int, K: int) -> str:
+    return lib().quasar_w4a8_kernel_name(M, N, K).decode()
+
+
+def quasar_quantize_weights_w4(w: torch.Tensor, s: torch.Tensor):
+    """W [N, K] bf16, s [K] f32 (K % 128 == 0) -> (4-bit PackedWeights, w_scale f32 [N])."""
+    N, K = w.shape
+    _need(w, torch.bfloat16, (N, K), "w")
+    _need(s, torch.float32, (K,), "s")
+    nbytes = packed_weight_bytes_w4(N, K) if N > 0 else 0
+    codes = torch.empty((max(nbytes, 16),), dtype=torch.int8, device=w.device)
+    wq = PackedWeights(codes, N, K, bits=4)
+    sw = torch.empty((N,), dtype=torch.float32, device=w.device)
+    _check("quasar_quantize_weights_w4", lib().quasar_quantize_weights_w4(
+        _ptr(w), _ptr(s), N, K, _ptr(wq), _ptr(sw), _stream()))
+    return wq, sw
+
+
+def quasar_w4a8_linear(x: torch.Tensor, s: torch.Tensor, wq: PackedWeights, w_scale: torch.Tensor,
+                       out: torch.Tensor | None = None,
+                       acc_out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y [M, N] bf16 = dequant(quant(X diag(s)) @ W4^T) for X [M, K] bf16, M <= 8."""
+    M, K = x.shape
+    N = wq.N
+    if not isinstance(wq, PackedWeights) or wq.K != K or wq.bits != 4:
+        raise ValueError("wq must be the 4-bit PackedWeights of a linear with the same K")
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(s, torch.float32, (K,), "s")
+    _need(w_scale, torch.float32, (N,), "w_scale")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(out, torch.bfloat16, (M, N), "out")
+    if acc_out is not None:
+        _need(acc_out, torch.int32, (M, N), "acc_out")
+    _check("quasar_w4a8_linear", lib().quasar_w4a8_linear(
+        _ptr(x), _ptr(s), _ptr(wq), _ptr(w_scale), M, N, K, _ptr(out), _ptr(acc_out), _stream()))
+    return out

@@ -85,7 +85,7 @@ const char* quasar_status_string(quasar_status status) {
   return "QUASAR_ERR_UNKNOWN";
 }
 
-int quasar_abi_version(void) { return 5; }
+int quasar_abi_version(void) { return 6; }
 
 quasar_status quasar_quantize_weights(const uint16_t* w, const float* s, int64_t N, int64_t K,
                                       int8_t* wq, float* w_scale, void* stream) {
@@ -193,6 +193,49 @@ quasar_status quasar_verify_accept(const uint16_t* logits, const int32_t* draft,
     return QUASAR_ERR_WORKSPACE;
   return hip_status(launch_accept(p, logits, draft, temperature, uniforms, accept_len, next_token,
                                   argmax_out, p_draft_out, workspace, (hipStream_t)stream));
+}
+
+size_t quasar_packed_weight_bytes_w4(int64_t N, int64_t K) {
+  if (N <= 0 || check_k(K) != QUASAR_OK || K % 128 != 0 || N > kMaxRowsPerCall) return 0;
+  return w4_packed_weight_bytes(N, K);
+}
+
+quasar_status quasar_quantize_weights_w4(const uint16_t* w, const float* s, int64_t N, int64_t K,
+                                         int8_t* wq4, float* w_scale, void* stream) {
+  if (N < 0) return QUASAR_ERR_INVALID_ARG;
+  quasar_status st = check_k(K);
+  if (st != QUASAR_OK) return st;
+  if (K % 128 != 0) return QUASAR_ERR_INVALID_ARG;
+  if (N > kMaxRowsPerCall) return QUASAR_ERR_UNSUPPORTED;
+  if (N == 0) return QUASAR_OK;
+  if (!w || !s || !wq4 || !w_scale) return QUASAR_ERR_INVALID_ARG;
+  if (!aligned(w, 16) || !aligned(s, 16) || !aligned(wq4, 16) || !aligned(w_scale, 4))
+    return QUASAR_ERR_INVALID_ARG;
+  return hip_status(launch_quantize_weights_w4(w, s, N, K, wq4, w_scale, (hipStream_t)stream));
+}
+
+quasar_status quasar_w4a8_linear(const uint16_t* x, const float* s, const int8_t* wq4,
+                                 const float* w_scale, int64_t M, int64_t N, int64_t K,
+                                 uint16_t* y, int32_t* acc_out, void* stream) {
+  if (M < 0 || N < 0) return QUASAR_ERR_INVALID_ARG;
+  quasar_status st = check_k(K);
+  if (st != QUASAR_OK) return st;
+  if (K % 128 != 0) return QUASAR_ERR_INVALID_ARG;
+  if (N > kMaxRowsPerCall || !w4_supported(M > 0 ? M : 1, K)) return QUASAR_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return QUASAR_OK;
+  if (!x || !s || !wq4 || !w_scale || !y) return QUASAR_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(s, 16) || !aligned(wq4, 16) || !aligned(w_scale, 4) ||
+      !aligned(y, 2) || (acc_out && !aligned(acc_out, 4)))
+    return QUASAR_ERR_INVALID_ARG;
+  return hip_status(launch_fused_w4(plan_fused(M, N, K), x, s, wq4, w_scale, y, acc_out,
+                                    (hipStream_t)stream));
+}
+
+const char* quasar_w4a8_kernel_name(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || check_k(K) != QUASAR_OK || K % 128 != 0 || !w4_supported(M, K) ||
+      N > kMaxRowsPerCall)
+    return "";
+  return fused_w4_kernel_name(plan_fused(M, N, K));
 }
 
 size_t quasar_lm_head_verify_workspace_bytes(int64_t B, int64_t k, int64_t V, int64_t K) {

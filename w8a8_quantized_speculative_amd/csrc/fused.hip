@@ -237,7 +237,7 @@ __device__ __forceinline__ void streamer(const int8_t* __restrict__ wq,
 // Helper role: smooth and quantize the activation rows into the LDS code
 // matrix, then finish every tile: sum the streamers' partials (exact INT32) and
 // dequantize to BF16.
-template <int MT, int S, int NH, int UP>
+template <int MT, int S, int NH, int UP, int kAccShift = 0>
 __device__ __forceinline__ void helper(const uint16_t* __restrict__ x, const float* __restrict__ s,
                                        int M, int N, int K, int first, int T, int ht, int hwave,
                                        int lane,
@@ -390,7 +390,9 @@ __device__ __forceinline__ void helper(const uint16_t* __restrict__ x, const flo
         for (int w = 0; w < S; ++w)
           tot += *reinterpret_cast<const v4i*>(red + (buf * S + w) * 256 + ht * 4);
         const float sxt = qp[tt];
-        const int tv[4] = {tot.x, tot.y, tot.z, tot.w};
+        // the 4-bit streamers accumulate 16x the sums (exact: shift back)
+        const int tv[4] = {tot.x >> kAccShift, tot.y >> kAccShift, tot.z >> kAccShift,
+                           tot.w >> kAccShift};
         uint32_t o[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -480,6 +482,174 @@ __global__ __launch_bounds__(64 * (S + (NPH == 2 ? 4 : 8))) void w8a8_linear_fus
   }
 }
 
+// ---------------------------------------------------------------------------
+// 4-bit weight variant [pt page §5, zh page §5: lower-bit verification named
+// as future work].  Same roles, plan and helpers as the kernel above; the
+// weights are the 4-bit layout of w4_packed_offset, so each 16-byte load per
+// lane carries the A operands of two 64-wide chunks:
+//   lo = (v << 4) & 0xF0F0F0F0 (chunk 2c), hi = v & 0xF0F0F0F0 (chunk 2c + 1)
+// are each byte's nibble times 16, an exact int8.  The MFMAs then accumulate
+// 16x the INT32 sums (|16 acc| <= 16 * 7 * 127 * 12288 < 2^31) and the
+// helpers shift the tile's total right by 4.
+// Streamer w's phase ph of a tile is packed chunks ph * 8S + 8w .. + 7 (an 8 KB
+// run per wavefront, 4096 K positions per phase for the 4 streamers).  Units
+// u = tile * NPH4 + phase alternate between two register buffers, issued two
+// units ahead (across tiles when a tile has one phase): as many loads in
+// flight per compute unit as the INT8 streamer, i.e. twice its K span.
+// ---------------------------------------------------------------------------
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+template <int MT, int S, int NPH4, int NH>
+__device__ __forceinline__ void streamer_w4(const int8_t* __restrict__ wq4,
+                                            const float* __restrict__ wscale, int N, int K,
+                                            int first, int T, int wave, int lane,
+                                            const int8_t* codes, int Ks, int32_t* red, float* wsl,
+                                            const int* ready) {
+  constexpr int NB = 2;
+  const int r = lane & 15, g = lane >> 4;
+  const int ncp = K >> 7;  // 128-wide pairs of chunks
+  const int nch = K >> 6;
+  const int U = T * NPH4;
+  v4i a[NB][kPH];
+  float wsv[NB];
+  const int voff = lane * 16;
+  auto issue = [&](int b, int u) {  // u >= U: nothing left, read zeros
+    const bool valid = u < U;
+    const int t = valid ? u / NPH4 : 0;
+    const int ph = valid ? u - t * NPH4 : 0;
+    const int tl = first + t;
+    const int8_t* tbase = wq4 + (size_t)tl * ncp * 1024;
+#pragma unroll
+    for (int j = 0; j < kPH; ++j) {
+      const int pc = ph * (S * kPH) + wave * kPH + j;
+      const buffer_rsrc rs =
+          make_rsrc(tbase + (size_t)pc * 1024, (valid && pc < ncp) ? 1024u : 0u);
+      a[b][j] = load16<kNonTemporal>(rs, voff);
+    }
+    const int rows = (valid && ph == NPH4 - 1) ? min(16, N - tl * 16) : 0;
+    const buffer_rsrc ss = make_rsrc(wscale + (size_t)tl * 16, (uint32_t)rows * 4u);
+    wsv[b] = __int_as_float(load4(ss, (wave == 0 && lane < 16) ? lane * 4 : kOutOfRange));
+  };
+
+  __syncthreads();  // (1) the helpers' activation loads are queued first
+  issue(0, 0);
+  issue(1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+
+  const int8_t* brow = codes + (r < MT ? r : MT - 1) * Ks + g * 16;
+  auto bfrag = [&](int c) -> v4i {
+    return *reinterpret_cast<const v4i*>(brow + min(c, nch - 1) * 64);
+  };
+  // the codes of phase ph's K range exist once every helper has finished the
+  // quantization step holding its last position (helpers finish steps in order)
+  auto wait_codes = [&](int ph) {
+    const int kend = min(K, (ph + 1) * S * kPH * 128) - 1;
+    const int* step_done = ready + kend / (512 * NH);
+    for (int spin = 0; spin < (1 << 22); ++spin) {
+      if (__hip_atomic_load(step_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= NH) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+  };
+  const v4u hi_mask = {0xF0F0F0F0u, 0xF0F0F0F0u, 0xF0F0F0F0u, 0xF0F0F0F0u};
+  v4i acc = {0, 0, 0, 0};
+  for (int ub = 0; ub < U; ub += NB) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int u = ub + b;
+      const bool live = u < U;
+      const int t = u / NPH4;
+      const int ph = u - t * NPH4;
+      const bool last = live && ph == NPH4 - 1;
+      if (live) {
+        if (t == 0) wait_codes(ph);
+#pragma unroll
+        for (int j = 0; j < kPH; ++j) {
+          const int pc = ph * (S * kPH) + wave * kPH + j;
+          const v4u v = __builtin_bit_cast(v4u, a[b][j]);
+          const v4i lo = __builtin_bit_cast(v4i, (v << 4u) & hi_mask);
+          const v4i hi = __builtin_bit_cast(v4i, v & hi_mask);
+          acc = mfma_i8_16x16x64(lo, bfrag(2 * pc), acc);
+          acc = mfma_i8_16x16x64(hi, bfrag(2 * pc + 1), acc);
+        }
+        if (last) {
+          const int buf = t & 1;
+          *reinterpret_cast<v4i*>(red + (buf * S + wave) * 256 + lane * 4) = acc;
+          if (wave == 0 && lane < 16) wsl[buf * 16 + lane] = wsv[b];
+        }
+      }
+      issue(b, u + NB);
+      if (last) {
+        acc = (v4i){0, 0, 0, 0};
+        __syncthreads();  // partials of tile t published
+      }
+    }
+  }
+}
+
+template <int MT, int S, int NPH4>
+__global__ __launch_bounds__(64 * (S + (NPH4 == 1 ? 4 : 8))) void w4a8_linear_fused_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ s, const int8_t* __restrict__ wq4,
+    const float* __restrict__ wscale, int M, int N, int K, int tq, int tr, int G,
+    uint16_t* __restrict__ y, int32_t* __restrict__ acc_out) {
+  using Var = Variant<NPH4 == 1 ? 0 : (NPH4 == 2 ? 1 : 2)>;
+  static_assert(Var::S == S && Var::NPH == 2 * NPH4, "variant");
+  extern __shared__ __align__(16) char smem[];
+  const Smem L = smem_layout(K, MT, S);
+  int8_t* codes = reinterpret_cast<int8_t*>(smem + L.codes);
+  int32_t* red = reinterpret_cast<int32_t*>(smem + L.red);
+  float* wsl = reinterpret_cast<float*>(smem + L.wsl);
+  float* amax_part = reinterpret_cast<float*>(smem + L.amax);
+  float* qp = reinterpret_cast<float*>(smem + L.qp);
+  int* cnt = reinterpret_cast<int*>(smem + L.cnt);
+  int* ready = reinterpret_cast<int*>(smem + L.ready);
+  const int Ks = K + 16;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (tid < 4) {
+    if (tid == 0) *cnt = 0;
+    ready[tid] = 0;
+  }
+  const int b = blockIdx.x;
+  const int first = b * tq + (int)((unsigned int)(b * tr) / (unsigned int)G);
+  const int T = (b + 1) * tq + (int)((unsigned int)((b + 1) * tr) / (unsigned int)G) - first;
+  if (wave < S) {
+    streamer_w4<MT, S, NPH4, Var::NH>(wq4, wscale, N, K, first, T, wave, lane, codes, Ks, red,
+                                      wsl, ready);
+  } else {
+    helper<MT, S, Var::NH, Var::UP, 4>(x, s, M, N, K, first, T, tid - 64 * S, wave - S, lane,
+                                       codes, Ks, red, wsl, amax_part, qp, cnt, ready, y, acc_out,
+                                       AcceptPartials{nullptr, nullptr, nullptr, 0.0f}, G);
+  }
+}
+
+template <int MT, int NPH4>
+hipError_t launch_w4(const FusedPlan& p, const uint16_t* x, const float* s, const int8_t* wq4,
+                     const float* w_scale, uint16_t* y, int32_t* acc_out, hipStream_t st) {
+  constexpr int S = 4;
+  auto kernel = &w4a8_linear_fused_kernel<MT, S, NPH4>;
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize,
+                          smem_layout(Variant<NPH4 - 1>::KMAX, MT, S).bytes);
+  if (attr != hipSuccess) return attr;
+  kernel<<<dim3(p.grid), dim3(64 * (S + (NPH4 == 1 ? 4 : 8))), p.lds, st>>>(
+      x, s, wq4, w_scale, (int)p.M, (int)p.N, (int)p.K, p.tiles / p.grid, p.tiles % p.grid,
+      p.grid, y, acc_out);
+  return hipGetLastError();
+}
+
+template <int MT>
+hipError_t launch_w4_mt(const FusedPlan& p, const uint16_t* x, const float* s, const int8_t* wq4,
+                        const float* w_scale, uint16_t* y, int32_t* acc_out, hipStream_t st) {
+  switch (p.variant) {
+    case 0: return launch_w4<MT, 1>(p, x, s, wq4, w_scale, y, acc_out, st);
+    case 1: return launch_w4<MT, 2>(p, x, s, wq4, w_scale, y, acc_out, st);
+    default: return launch_w4<MT, 3>(p, x, s, wq4, w_scale, y, acc_out, st);
+  }
+}
+
 template <int MT, int V>
 hipError_t launch_variant(const FusedPlan& p, const uint16_t* x, const float* s, const int8_t* wq,
                           const float* w_scale, uint16_t* y, int32_t* acc_out, hipStream_t st,
@@ -530,6 +700,35 @@ FusedPlan plan_fused(int64_t M, int64_t N, int64_t K) {
   const int cap = kNumCU;  // one persistent workgroup per compute unit
   p.grid = p.tiles < cap ? p.tiles : cap;
   return p;
+}
+
+bool w4_supported(int64_t M, int64_t K) {
+  return fused_supported(M, K) && K % 128 == 0;
+}
+
+const char* fused_w4_kernel_name(const FusedPlan& p) {
+  // <token rows, streamer wavefronts, 8 KB phases per streamer and tile>
+  static const char* const names[4][3] = {
+      {"w4a8_linear_fused_kernel<2, 4, 1>", "w4a8_linear_fused_kernel<2, 4, 2>",
+       "w4a8_linear_fused_kernel<2, 4, 3>"},
+      {"w4a8_linear_fused_kernel<4, 4, 1>", "w4a8_linear_fused_kernel<4, 4, 2>",
+       "w4a8_linear_fused_kernel<4, 4, 3>"},
+      {"w4a8_linear_fused_kernel<6, 4, 1>", "w4a8_linear_fused_kernel<6, 4, 2>",
+       "w4a8_linear_fused_kernel<6, 4, 3>"},
+      {"w4a8_linear_fused_kernel<8, 4, 1>", "w4a8_linear_fused_kernel<8, 4, 2>",
+       "w4a8_linear_fused_kernel<8, 4, 3>"}};
+  return names[p.mt / 2 - 1][p.variant];
+}
+
+hipError_t launch_fused_w4(const FusedPlan& p, const uint16_t* x, const float* s,
+                           const int8_t* wq4, const float* w_scale, uint16_t* y, int32_t* acc_out,
+                           hipStream_t st) {
+  switch (p.mt) {
+    case 2: return launch_w4_mt<2>(p, x, s, wq4, w_scale, y, acc_out, st);
+    case 4: return launch_w4_mt<4>(p, x, s, wq4, w_scale, y, acc_out, st);
+    case 6: return launch_w4_mt<6>(p, x, s, wq4, w_scale, y, acc_out, st);
+    default: return launch_w4_mt<8>(p, x, s, wq4, w_scale, y, acc_out, st);
+  }
 }
 
 const char* fused_kernel_name(const FusedPlan& p) {

@@ -134,6 +134,59 @@ __global__ __launch_bounds__(kRowThreads) void zero_pad_rows_kernel(int8_t* __re
     *reinterpret_cast<uint4*>(wq + packed_offset(row, k, nch)) = make_uint4(0, 0, 0, 0);
 }
 
+// 4-bit weights [pt page §5, zh page §5: lower-bit verification as future
+// work; read as the INT8 rule at qmax = 7]: code = clamp(rint(RN32(w' inv)),
+// -7, 7) with inv = RN32(7 / absmax).  Two passes over the row (absmax, then
+// codes); thread i packs the 8 positions 128 c + 8 j and 128 c + 64 + 8 j
+// (j < 8) of pair unit i into 8 bytes of the 4-bit layout (w4_packed_offset).
+__device__ __forceinline__ uint32_t w4_nibble(float v, float inv) {
+  float r = __builtin_rintf(v * inv);
+  r = fminf(fmaxf(r, -kQmaxW4), kQmaxW4);
+  return (uint32_t)(int)r & 0xfu;
+}
+
+__global__ __launch_bounds__(kRowThreads) void quantize_rows_w4_kernel(
+    const uint16_t* __restrict__ w, const float* __restrict__ s, int64_t K,
+    int8_t* __restrict__ wq4, float* __restrict__ scales) {
+  __shared__ float red[kRowThreads / kWave];
+  const int64_t row = blockIdx.x;
+  const uint16_t* wr = w + row * K;
+  const int64_t units = K / 8;
+  float amax = 0.0f;
+  for (int64_t q = threadIdx.x; q < units; q += kRowThreads) {
+    float v[8];
+    load_unit<true>(wr, s, q, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+  }
+  amax = block_max(amax, red);
+  const QParams qp = row_qparams(amax, kQmaxW4);
+  const int64_t ncp = K / 128;
+  for (int64_t p = threadIdx.x; p < K / 16; p += kRowThreads) {
+    const int64_t qlo = (p >> 3) * 16 + (p & 7);  // unit of the chunk-2c half
+    float lo[8], hi[8];
+    load_unit<true>(wr, s, qlo, lo);
+    load_unit<true>(wr, s, qlo + 8, hi);  // 64 positions on: chunk 2c + 1
+    uint32_t by[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) by[e] = w4_nibble(lo[e], qp.inv) | (w4_nibble(hi[e], qp.inv) << 4);
+    uint2 pk;
+    pk.x = by[0] | (by[1] << 8) | (by[2] << 16) | (by[3] << 24);
+    pk.y = by[4] | (by[5] << 8) | (by[6] << 16) | (by[7] << 24);
+    *reinterpret_cast<uint2*>(wq4 + w4_packed_offset(row, qlo * 8, ncp)) = pk;
+  }
+  if (threadIdx.x == 0) scales[row] = qp.scale;
+}
+
+// Rows past N in the last tile of the 4-bit layout hold zero codes.
+__global__ __launch_bounds__(kRowThreads) void zero_pad_rows_w4_kernel(int8_t* __restrict__ wq4,
+                                                                       int64_t N, int64_t ncp) {
+  const int64_t row = N + blockIdx.x;  // N <= row < 16 * tiles
+  for (int64_t i = threadIdx.x; i < ncp * 4; i += kRowThreads)  // 16 bytes per (pair, K group)
+    *reinterpret_cast<uint4*>(wq4 + w4_packed_offset(row, (i >> 2) * 128 + (i & 3) * 16, ncp)) =
+        make_uint4(0, 0, 0, 0);
+}
+
 template <bool kWeights>
 hipError_t launch_rows(const uint16_t* src, const float* s, int64_t rows, int64_t K, int8_t* codes,
                        float* scales, float* xs_out, hipStream_t st) {
@@ -161,6 +214,17 @@ hipError_t launch_quantize_weights(const uint16_t* w, const float* s, int64_t N,
   const int64_t pad_rows = (N + 15) / 16 * 16 - N;
   if (e != hipSuccess || pad_rows == 0) return e;
   zero_pad_rows_kernel<<<dim3((unsigned)pad_rows), dim3(kRowThreads), 0, st>>>(wq, N, (K + 63) / 64);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_weights_w4(const uint16_t* w, const float* s, int64_t N, int64_t K,
+                                      int8_t* wq4, float* w_scale, hipStream_t st) {
+  if (N == 0) return hipSuccess;
+  quantize_rows_w4_kernel<<<dim3((unsigned)N), dim3(kRowThreads), 0, st>>>(w, s, K, wq4, w_scale);
+  hipError_t e = hipGetLastError();
+  const int64_t pad_rows = (N + 15) / 16 * 16 - N;
+  if (e != hipSuccess || pad_rows == 0) return e;
+  zero_pad_rows_w4_kernel<<<dim3((unsigned)pad_rows), dim3(kRowThreads), 0, st>>>(wq4, N, K / 128);
   return hipGetLastError();
 }
 

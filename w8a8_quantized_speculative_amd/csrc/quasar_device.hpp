@@ -34,14 +34,14 @@ struct QParams {
   float inv;
 };
 
-__device__ __forceinline__ QParams row_qparams(float amax) {
+__device__ __forceinline__ QParams row_qparams(float amax, float qmax = kQmax) {
   QParams p;
   if (amax == 0.0f) {
     p.scale = 0.0f;
     p.inv = 0.0f;
   } else {
-    p.scale = amax / kQmax;
-    p.inv = kQmax / amax;
+    p.scale = amax / qmax;
+    p.inv = qmax / amax;
   }
   return p;
 }
@@ -120,6 +120,19 @@ __host__ __device__ __forceinline__ int64_t packed_offset(int64_t n, int64_t k, 
   const int64_t t = n >> 4, r = n & 15, c = k >> 6, g = (k >> 4) & 3, b = k & 15;
   return ((t * nch + c) * 64 + g * 16 + r) * 16 + b;
 }
+
+// 4-bit weight layout (the INT4 verifier variant): the codes (two's complement
+// nibbles) of 64-wide chunks 2c and 2c + 1 of a tile share one 1 KB block, the
+// chunk 2c code in the low nibble and the chunk 2c + 1 code in the high nibble
+// of the byte the INT8 layout gives K position 64 (2c) + j.  So one 16-byte
+// load per lane carries the A operands of two chunks: (v << 4) & 0xF0F0F0F0
+// and v & 0xF0F0F0F0 are the chunks' codes times 16, as int8 bytes.
+// k must lie in the low half of its 128-block (k % 128 < 64); ncp = K / 128.
+__host__ __device__ __forceinline__ int64_t w4_packed_offset(int64_t n, int64_t k, int64_t ncp) {
+  const int64_t t = n >> 4, r = n & 15, cp = k >> 7, g = (k >> 4) & 3, b = k & 15;
+  return ((t * ncp + cp) * 64 + g * 16 + r) * 16 + b;
+}
+constexpr float kQmaxW4 = 7.0f;  // 4-bit weight codes in [-7, 7]
 
 // Block-wide max; `red` must hold blockDim.x / 64 floats.  Ends with a barrier
 // so `red` can be reused afterwards.

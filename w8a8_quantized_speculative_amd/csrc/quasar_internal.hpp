@@ -18,6 +18,10 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline size_t packed_weight_bytes(int64_t N, int64_t K) {
   return (size_t)((N + 15) / 16) * (size_t)((K + 63) / 64) * 1024u;
 }
+// 4-bit weights (K % 128 == 0): a 1 KB block per tile and pair of 64-wide chunks
+inline size_t w4_packed_weight_bytes(int64_t N, int64_t K) {
+  return (size_t)((N + 15) / 16) * (size_t)(K / 128) * 1024u;
+}
 
 // ---------------------------------------------------------------------------
 // One-launch plan (M <= 8, K <= 12288): quantize + GEMM + dequant in one
@@ -45,6 +49,13 @@ struct AcceptPartials {
 };
 
 bool fused_supported(int64_t M, int64_t K);
+// The 4-bit weight variant of the one-launch linear (M <= 8, K <= 12288,
+// K % 128 == 0), on the same plan.
+bool w4_supported(int64_t M, int64_t K);
+const char* fused_w4_kernel_name(const FusedPlan& p);
+hipError_t launch_fused_w4(const FusedPlan& p, const uint16_t* x, const float* s,
+                           const int8_t* wq4, const float* w_scale, uint16_t* y, int32_t* acc_out,
+                           hipStream_t st);
 // Name of the kernel of a one-launch plan (static storage).
 const char* fused_kernel_name(const FusedPlan& p);
 FusedPlan plan_fused(int64_t M, int64_t N, int64_t K);
@@ -109,6 +120,9 @@ AcceptPlan plan_accept(int64_t B, int64_t k, int64_t V);
 // ---------------------------------------------------------------------------
 hipError_t launch_quantize_weights(const uint16_t* w, const float* s, int64_t N, int64_t K,
                                    int8_t* wq, float* w_scale, hipStream_t st);
+
+hipError_t launch_quantize_weights_w4(const uint16_t* w, const float* s, int64_t N, int64_t K,
+                                      int8_t* wq4, float* w_scale, hipStream_t st);
 
 hipError_t launch_quantize_activations(const uint16_t* x, const float* s, int64_t M, int64_t K,
                                        int8_t* qx, float* sx, float* xs_out, hipStream_t st);
