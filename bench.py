@@ -41,6 +41,11 @@ def pmc_file(M: int) -> str:
     return os.path.join(PROFILES, f"w8a8_linear_fused_kernel_qwen3_stack_m{M}_pmc.json")
 
 
+def algorithmic_bytes_w4(M: int, N: int, K: int) -> int:
+    """The same with 4-bit weights: N*K/2 weight bytes."""
+    return N * K // 2 + 4 * N + 4 * K + 2 * M * K + 2 * M * N
+
+
 def algorithmic_bytes(M: int, N: int, K: int) -> int:
     """INT8 weights + weight scales + smoothing vector + BF16 input + BF16 output."""
     return N * K + 4 * N + 4 * K + 2 * M * K + 2 * M * N
@@ -147,6 +152,24 @@ class Stack:
             self.linear_call(e)
         self.lm_head_verify_call()
 
+    def build_w4(self):
+        """4-bit copies of every linear's weights, from the kept BF16 weights."""
+        import torch
+        from w8a8_quantized_speculative_amd import binding
+        for e in self.linears:
+            e["wq4"], e["sw4"] = binding.quasar_quantize_weights_w4(e["w_bf16"], e["s"])
+        torch.cuda.synchronize()
+        self.bytes_step_w4 = sum(algorithmic_bytes_w4(self.M, e["N"], e["K"]) for e in self.linears) \
+            + 4 * self.B * self.k + 8 * self.B
+
+    def step_w4(self):
+        """The same step with 4-bit weights: every linear through quasar_w4a8_linear,
+        then the greedy accept on the LM head's logits."""
+        from w8a8_quantized_speculative_amd import binding
+        for e in self.linears:
+            binding.quasar_w4a8_linear(e["x"], e["s"], e["wq4"], e["sw4"], out=e["y"])
+        self.accept_call()
+
 
 def plant_drafts(stack, n_sets: int):
     """Seeded draft sets planted against the verifier's argmax (p = 0.3 each)."""
@@ -160,18 +183,19 @@ def plant_drafts(stack, n_sets: int):
     return torch.from_numpy(np.stack(sets)).cuda()
 
 
-def time_graph_steps(stack, drafts, warmup: int, steps: int):
+def time_graph_steps(stack, drafts, warmup: int, steps: int, step=None):
     """Capture one step in a HIP graph; replay it `steps` times (new drafts each)."""
     import torch
+    step = step or stack.step
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        stack.step()  # prime everything once outside capture
+        step()  # prime everything once outside capture
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        stack.step()
+        step()
     lens = torch.zeros((warmup + steps, stack.B), dtype=torch.int32, device="cuda")
     for i in range(warmup):
         stack.draft.copy_(drafts[i])
@@ -507,6 +531,33 @@ def main():
             "ms_per_step": round(bms, 4),
             "gbs": round(bbytes / (bms * 1e-3) / 1e9, 1),
             "w8a8_speedup": round(bms / lin_ms, 3),
+        }
+    if not args.no_bf16 and args.m <= 8:
+        # the 4-bit weight variant of the same stack (its own planted drafts and tau)
+        print("[bench] 4-bit weight variant", file=sys.stderr, flush=True)
+        import numpy as np
+        from w8a8_quantized_speculative_amd import synth
+        stack.build_w4()
+        stack.step_w4()
+        torch.cuda.synchronize()
+        g4 = stack.argmax.cpu().numpy()
+        drafts4 = torch.from_numpy(np.stack([synth.draft_tokens(g4[:, :stack.k], stack.V, 0.3, (6, i))
+                                             for i in range(args.warmup + args.steps)])).cuda()
+        tau4 = measure_tau(stack, args.tau_sets)
+        ms4, ms4_ev, _, _g4 = time_graph_steps(stack, drafts4, args.warmup, args.steps,
+                                               step=stack.step_w4)
+        del _g4
+        out["w4a8_variant"] = {
+            "what": "same stack and LM head with 4-bit per-channel weights (quasar_w4a8_linear), "
+                    "then the greedy accept; HIP graph",
+            "kernel": binding.w4a8_kernel_name(args.m, 4096, 4096),
+            "ms_per_step": round(ms4, 4),
+            "ms_per_step_events": round(ms4_ev, 4),
+            "gbs": round(stack.bytes_step_w4 / (ms4 * 1e-3) / 1e9, 1),
+            "weights_int4_gb": round(sum(e["N"] * e["K"] for e in stack.linears) / 2e9, 3),
+            "verified_tokens_per_s": round(stack.B * tau4 / (ms4 * 1e-3), 1),
+            "mean_tau": round(tau4, 4),
+            "speedup_vs_w8a8": round(ms / ms4, 3),
         }
     if not args.no_cpu_baseline:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
