@@ -136,71 +136,131 @@ __device__ __forceinline__ int chunk_of(const ChunkGeometry& cg, int chunks, int
   return lo;
 }
 
+// Inclusive prefix sum over the workgroup (thread order); `wsum` holds one
+// float per wavefront.  Ends with a barrier, so `wsum` can be reused.
+__device__ float block_incl_scan(float v, float* wsum) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const float o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  if (lane == kWave - 1) wsum[wave] = v;
+  __syncthreads();
+  float add = 0.0f;
+  for (int w = 0; w < wave; ++w) add += wsum[w];
+  __syncthreads();
+  return v + add;
+}
+
 template <bool kSample>
 __global__ __launch_bounds__(kThreads) void accept_finalize_kernel(
     const uint16_t* __restrict__ logits, const int32_t* __restrict__ draft, int k, int64_t V,
     int chunks, ChunkGeometry cg, float inv_t, const float* __restrict__ uniforms,
-    const float* __restrict__ pmax,
-    const int32_t* __restrict__ pidx, const float* __restrict__ psum,
-    int32_t* __restrict__ accept_len, int32_t* __restrict__ next_token,
-    int32_t* __restrict__ argmax_out, float* __restrict__ p_draft_out) {
+    const float* __restrict__ pmax, const int32_t* __restrict__ pidx,
+    const float* __restrict__ psum, int32_t* __restrict__ accept_len,
+    int32_t* __restrict__ next_token, int32_t* __restrict__ argmax_out,
+    float* __restrict__ p_draft_out) {
   __shared__ float sv[kThreads / kWave];
   __shared__ int si[kThreads / kWave];
-  __shared__ int s_g[kMaxRows];
-  __shared__ float s_m[kMaxRows], s_z[kMaxRows];
+  __shared__ int s_g[kMaxRows], s_d[kMaxRows];
+  __shared__ float s_m[kMaxRows], s_z[kMaxRows], s_p[kMaxRows], s_u[kMaxRows];
   __shared__ int s_L, s_cstar, s_found, s_fallback;
   __shared__ float s_before, s_target;
   __shared__ float s_run[kThreads];
 
-  const int b = blockIdx.x;
+  const int b = blockIdx.x, tid = threadIdx.x;
   const int kp1 = k + 1;
+  // the sequence's drafts and uniforms, loaded in parallel
+  if (tid < k) s_d[tid] = draft[(int64_t)b * k + tid];
+  if (kSample && tid < kp1) s_u[tid] = uniforms[(int64_t)b * kp1 + tid];
+
   // ---- merge the chunk partials of every verify position
-  for (int i = 0; i < kp1; ++i) {
-    const int64_t row = (int64_t)b * kp1 + i;
-    ArgMax a{-FLT_MAX, INT_MAX};
-    for (int c = threadIdx.x; c < chunks; c += kThreads)
-      a = better(a, ArgMax{pmax[row * chunks + c], pidx[row * chunks + c]});
-    a = block_argmax(a, sv, si);
-    float z = 0.0f;
-    if (kSample) {
-      float part = 0.0f;
-      for (int c = threadIdx.x; c < chunks; c += kThreads)
-        part += psum[row * chunks + c] * expf((pmax[row * chunks + c] - a.v) * inv_t);
-      z = block_sum(part, sv);
+  if (kp1 <= 8 && chunks <= kThreads) {
+    // thread c holds chunk c of every row: all loads are issued before any
+    // reduction, so their latency is paid once rather than once per row
+    float vm[8], vs[8];
+    int vi[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      vm[i] = -FLT_MAX;
+      vi[i] = INT_MAX;
+      vs[i] = 0.0f;
+      if (i < kp1 && tid < chunks) {
+        const int64_t slot = ((int64_t)b * kp1 + i) * chunks + tid;
+        vm[i] = pmax[slot];
+        vi[i] = pidx[slot];
+        if (kSample) vs[i] = psum[slot];
+      }
     }
-    if (threadIdx.x == 0) {
-      s_g[i] = a.idx;
-      s_m[i] = a.v;
-      s_z[i] = z;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i < kp1) {
+        const ArgMax a = block_argmax(ArgMax{vm[i], vi[i]}, sv, si);
+        float z = 0.0f;
+        if (kSample) z = block_sum(tid < chunks ? vs[i] * expf((vm[i] - a.v) * inv_t) : 0.0f, sv);
+        if (tid == 0) {
+          s_g[i] = a.idx;
+          s_m[i] = a.v;
+          s_z[i] = z;
+        }
+      }
+    }
+  } else {
+    for (int i = 0; i < kp1; ++i) {
+      const int64_t row = (int64_t)b * kp1 + i;
+      ArgMax a{-FLT_MAX, INT_MAX};
+      for (int c = tid; c < chunks; c += kThreads)
+        a = better(a, ArgMax{pmax[row * chunks + c], pidx[row * chunks + c]});
+      a = block_argmax(a, sv, si);
+      float z = 0.0f;
+      if (kSample) {
+        float part = 0.0f;
+        for (int c = tid; c < chunks; c += kThreads)
+          part += psum[row * chunks + c] * expf((pmax[row * chunks + c] - a.v) * inv_t);
+        z = block_sum(part, sv);
+      }
+      if (tid == 0) {
+        s_g[i] = a.idx;
+        s_m[i] = a.v;
+        s_z[i] = z;
+      }
     }
   }
   __syncthreads();
 
   if (!kSample) {
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
       int L = 0;
-      while (L < k && draft[(int64_t)b * k + L] == s_g[L]) ++L;
+      while (L < k && s_d[L] == s_g[L]) ++L;
       accept_len[b] = L;
       next_token[b] = s_g[L];
     }
     if (argmax_out)
-      for (int i = threadIdx.x; i < kp1; i += kThreads) argmax_out[(int64_t)b * kp1 + i] = s_g[i];
+      for (int i = tid; i < kp1; i += kThreads) argmax_out[(int64_t)b * kp1 + i] = s_g[i];
     return;
   }
 
-  // ---- rejection: accept decisions in draft order
-  if (threadIdx.x == 0) {
-    int L = k;
-    for (int i = 0; i < k; ++i) {
-      const int d = draft[(int64_t)b * k + i];
-      float p = 0.0f;
-      if (d >= 0 && d < V) {
-        const float l = bf16_to_f32(logits[((int64_t)b * kp1 + i) * V + d]);
-        p = expf((l - s_m[i]) * inv_t) / s_z[i];
-      }
-      if (p_draft_out) p_draft_out[(int64_t)b * k + i] = p;
-      if (L == k && !(uniforms[(int64_t)b * kp1 + i] < p)) L = i;
+  // ---- rejection: p_i(draft i) for every draft in parallel, then the
+  // accept decisions in draft order
+  if (tid < k) {
+    const int d = s_d[tid];
+    float p = 0.0f;
+    if (d >= 0 && d < V) {
+      const float l = bf16_to_f32(logits[((int64_t)b * kp1 + tid) * V + d]);
+      p = expf((l - s_m[tid]) * inv_t) / s_z[tid];
     }
+    s_p[tid] = p;
+    if (p_draft_out) p_draft_out[(int64_t)b * k + tid] = p;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int L = k;
+    for (int i = 0; i < k; ++i)
+      if (!(s_u[i] < s_p[i])) {
+        L = i;
+        break;
+      }
     s_L = L;
   }
   __syncthreads();
@@ -209,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void accept_finalize_kernel(
   const float m = s_m[L];
   int d_ex = -1;  // token removed from the residual (the rejected draft)
   if (L < k) {
-    const int d = draft[(int64_t)b * k + L];
+    const int d = s_d[L];
     if (d >= 0 && d < V) d_ex = d;
   }
   const int c_ex = d_ex >= 0 ? chunk_of(cg, chunks, d_ex, V) : -1;
@@ -218,16 +278,51 @@ __global__ __launch_bounds__(kThreads) void accept_finalize_kernel(
   if (c_ex >= 0) {
     float part = 0.0f;
     const int64_t j1 = chunk_start(cg, c_ex + 1, V);
-    for (int64_t j = chunk_start(cg, c_ex, V) + threadIdx.x; j < j1; j += kThreads)
+    for (int64_t j = chunk_start(cg, c_ex, V) + tid; j < j1; j += kThreads)
       if (j != d_ex) part += expf((bf16_to_f32(logits[row * V + j]) - m) * inv_t);
     ex_sum = block_sum(part, sv);
   }
-  // ---- walk the chunk sums (rescaled to the row max) to the chunk holding the draw
-  if (threadIdx.x == 0) {
+  // ---- the chunk holding the draw: the first whose running sum of chunk sums
+  // (rescaled to the row max) passes u * total
+  if (tid == 0) {
+    s_found = INT_MAX;
+    s_fallback = -1;
+  }
+  if (chunks <= kThreads) {
+    float sc = 0.0f;
+    if (tid < chunks)
+      sc = (tid == c_ex) ? ex_sum
+                         : psum[row * chunks + tid] * expf((pmax[row * chunks + tid] - m) * inv_t);
+    const float incl = block_incl_scan(sc, sv);  // ends with a barrier
+    s_run[tid] = incl;
+    __syncthreads();
+    const float total = s_run[chunks - 1];
+    const float target = s_u[k] * total;
+    if (tid < chunks) {
+      if (incl > target) atomicMin(&s_found, tid);
+      if (sc > 0.0f) atomicMax(&s_fallback, tid);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int cstar = s_found;
+      float before;
+      if (cstar != INT_MAX) {
+        before = cstar > 0 ? s_run[cstar - 1] : 0.0f;
+      } else {  // rounding pushed the target past the last chunk
+        cstar = s_fallback >= 0 ? s_fallback : 0;
+        before = total;
+      }
+      s_cstar = cstar;
+      s_before = before;
+      s_target = target;
+      s_found = INT_MAX;
+      s_fallback = -1;
+    }
+  } else if (tid == 0) {
     float total = 0.0f;
     for (int c = 0; c < chunks; ++c)
       total += (c == c_ex) ? ex_sum : psum[row * chunks + c] * expf((pmax[row * chunks + c] - m) * inv_t);
-    const float target = uniforms[(int64_t)b * kp1 + k] * total;
+    const float target = s_u[k] * total;
     float cum = 0.0f;
     int cstar = -1, last_nz = 0;
     float before = 0.0f;
@@ -259,28 +354,18 @@ __global__ __launch_bounds__(kThreads) void accept_finalize_kernel(
   float run = 0.0f;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int64_t j = base + (int64_t)threadIdx.x * E + e;
+    const int64_t j = base + (int64_t)tid * E + e;
     rr[e] = 0.0f;
     if (j < end && j != d_ex) rr[e] = expf((bf16_to_f32(logits[row * V + j]) - m) * inv_t);
     run += rr[e];
   }
-  s_run[threadIdx.x] = run;
-  __syncthreads();
-  if (threadIdx.x == 0) {  // exclusive prefix of the per-thread sums
-    float acc = 0.0f;
-    for (int t = 0; t < kThreads; ++t) {
-      const float v = s_run[t];
-      s_run[t] = acc;
-      acc += v;
-    }
-  }
-  __syncthreads();
-  float cum = s_before + s_run[threadIdx.x];
+  const float excl = block_incl_scan(run, sv) - run;  // this thread's exclusive prefix
+  float cum = s_before + excl;
   const float target = s_target;
   int found = INT_MAX, nz = -1;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int j = (int)(base + threadIdx.x * E + e);
+    const int j = (int)(base + tid * E + e);
     cum += rr[e];
     if (rr[e] > 0.0f) {
       nz = j;
@@ -290,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void accept_finalize_kernel(
   if (found != INT_MAX) atomicMin(&s_found, found);
   if (nz >= 0) atomicMax(&s_fallback, nz);
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     accept_len[b] = L;
     next_token[b] = s_found != INT_MAX ? s_found : (s_fallback >= 0 ? s_fallback : 0);
   }
