@@ -109,6 +109,7 @@ class Stack:
         self.accept_len = torch.zeros((self.B,), dtype=torch.int32, device="cuda")
         self.next_token = torch.zeros((self.B,), dtype=torch.int32, device="cuda")
         self.argmax = torch.zeros((self.B, self.k + 1), dtype=torch.int32, device="cuda")
+        self.uniforms = torch.zeros((self.B, self.k + 1), dtype=torch.float32, device="cuda")
         self.bytes_linear = [algorithmic_bytes(M, e["N"], e["K"]) for e in self.linears]
         # the linears, the drafts read and the accept lengths and next tokens
         # written; the logits are not read back (at M <= 8 the LM head's own
@@ -131,18 +132,21 @@ class Stack:
         if st != 0:
             raise binding.QuasarError("quasar_verify_accept", st)
 
-    def lm_head_verify_call(self):
-        """The LM head and the greedy accept step in one library call."""
+    def lm_head_verify_call(self, temperature: float = 0.0):
+        """The LM head and the accept step in one library call: greedy, or
+        rejection sampling with the uniforms in self.uniforms at T > 0."""
         import ctypes
         from w8a8_quantized_speculative_amd import binding
         e = self.linears[-1]
         L = binding.lib()
         P = ctypes.c_void_p
+        greedy = temperature == 0.0
         st = L.quasar_lm_head_verify(
             P(e["x"].data_ptr()), P(e["s"].data_ptr()), P(e["wq"].data_ptr()),
-            P(e["sw"].data_ptr()), self.B, self.k, self.V, e["K"], P(self.draft.data_ptr()), 0.0,
-            None, P(e["y"].data_ptr()), P(self.accept_len.data_ptr()),
-            P(self.next_token.data_ptr()), P(self.argmax.data_ptr()), None,
+            P(e["sw"].data_ptr()), self.B, self.k, self.V, e["K"], P(self.draft.data_ptr()),
+            float(temperature), None if greedy else P(self.uniforms.data_ptr()),
+            P(e["y"].data_ptr()), P(self.accept_len.data_ptr()), P(self.next_token.data_ptr()),
+            P(self.argmax.data_ptr()) if greedy else None, None,
             P(self.lmh_ws.data_ptr()), self.lmh_ws.numel(), binding._stream())
         if st != 0:
             raise binding.QuasarError("quasar_lm_head_verify", st)
@@ -151,6 +155,12 @@ class Stack:
         for e in self.linears[:-1]:
             self.linear_call(e)
         self.lm_head_verify_call()
+
+    def step_t1(self):
+        """The step with rejection-sampling verification at T = 1."""
+        for e in self.linears[:-1]:
+            self.linear_call(e)
+        self.lm_head_verify_call(1.0)
 
     def build_w4(self):
         """4-bit copies of every linear's weights, from the kept BF16 weights."""
@@ -183,8 +193,9 @@ def plant_drafts(stack, n_sets: int):
     return torch.from_numpy(np.stack(sets)).cuda()
 
 
-def time_graph_steps(stack, drafts, warmup: int, steps: int, step=None):
-    """Capture one step in a HIP graph; replay it `steps` times (new drafts each)."""
+def time_graph_steps(stack, drafts, warmup: int, steps: int, step=None, uniforms=None):
+    """Capture one step in a HIP graph; replay it `steps` times (new drafts, and
+    new uniforms when given, each)."""
     import torch
     step = step or stack.step
     s = torch.cuda.Stream()
@@ -199,6 +210,8 @@ def time_graph_steps(stack, drafts, warmup: int, steps: int, step=None):
     lens = torch.zeros((warmup + steps, stack.B), dtype=torch.int32, device="cuda")
     for i in range(warmup):
         stack.draft.copy_(drafts[i])
+        if uniforms is not None:
+            stack.uniforms.copy_(uniforms[i])
         graph.replay()
         lens[i].copy_(stack.accept_len)
     t0 = torch.cuda.Event(enable_timing=True)
@@ -208,6 +221,8 @@ def time_graph_steps(stack, drafts, warmup: int, steps: int, step=None):
     t0.record()
     for i in range(warmup, warmup + steps):
         stack.draft.copy_(drafts[i])
+        if uniforms is not None:
+            stack.uniforms.copy_(uniforms[i])
         graph.replay()
         lens[i].copy_(stack.accept_len)
     t1.record()
@@ -248,18 +263,39 @@ def measure_tau(stack, n_sets: int):
     return (lens.float() + 1).mean().item()
 
 
-def time_eager_step(stack, steps: int) -> float:
-    """Plain eager step time (host-issued calls, no graph)."""
+def time_eager_steps(stack, drafts, warmup: int, steps: int, step=None, uniforms=None):
+    """The same steps issued as plain stream launches (no graph): new drafts per
+    step, host clock between torch.cuda.synchronize() calls, HIP events beside.
+    A graph replay adds a per-node cost on this stack (~0.4 us per launch); plain
+    launches avoid it as long as the host issues faster than the GPU runs."""
     import torch
-    torch.cuda.synchronize()
+    step = step or stack.step
+    lens = torch.zeros((warmup + steps, stack.B), dtype=torch.int32, device="cuda")
+    for i in range(warmup):
+        stack.draft.copy_(drafts[i])
+        if uniforms is not None:
+            stack.uniforms.copy_(uniforms[i])
+        step()
+        lens[i].copy_(stack.accept_len)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
     t0.record()
-    for _ in range(steps):
-        stack.step()
+    for i in range(warmup, warmup + steps):
+        stack.draft.copy_(drafts[i])
+        if uniforms is not None:
+            stack.uniforms.copy_(uniforms[i])
+        step()
+        lens[i].copy_(stack.accept_len)
     t1.record()
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps
+    ms = (time.perf_counter() - w0) * 1e3 / steps
+    ms_events = t0.elapsed_time(t1) / steps
+    if abs(ms - ms_events) > 0.1 * ms:
+        raise RuntimeError(f"eager step time disagrees between host clock ({ms:.4f} ms) and "
+                           f"HIP events ({ms_events:.4f} ms)")
+    return ms, ms_events, (lens[warmup:].float() + 1).mean().item()
 
 
 def time_kernels(stack, reps: int):
@@ -325,7 +361,17 @@ def time_bf16_comparator(stack, warmup: int, steps: int):
         graph.replay()
     t1.record()
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
+    ms_graph = t0.elapsed_time(t1) / steps
+    # plain launches of the same calls, as for the W8A8 step; the faster counts
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = min(ms_graph, t0.elapsed_time(t1) / steps)
     bf16_bytes = sum(2 * e["N"] * e["K"] + 2 * stack.M * e["K"] + 2 * stack.M * e["N"]
                      for e in stack.linears)
     return ms, bf16_bytes
@@ -430,8 +476,25 @@ def main():
     drafts = plant_drafts(stack, args.warmup + args.steps)
     print("[bench] graph replay timing", file=sys.stderr, flush=True)
     ms, ms_events, tau, _graph = time_graph_steps(stack, drafts, args.warmup, args.steps)
+    print("[bench] rejection-verify step (T = 1)", file=sys.stderr, flush=True)
+    import numpy as np
+    from w8a8_quantized_speculative_amd import synth as _synth
+    unis = torch.from_numpy(np.stack([_synth.uniforms(stack.B, stack.k, (8, i))
+                                      for i in range(args.warmup + args.steps)])).cuda()
+    ms_t1, ms_t1_ev, tau_t1, _gt1 = time_graph_steps(stack, drafts, args.warmup, args.steps,
+                                                     step=stack.step_t1, uniforms=unis)
+    del _gt1
+    e_t1 = time_eager_steps(stack, drafts, args.warmup, args.steps, step=stack.step_t1,
+                            uniforms=unis)
+    if e_t1[0] < ms_t1:
+        ms_t1, ms_t1_ev, tau_t1 = e_t1
     print("[bench] eager step and per-kernel timing", file=sys.stderr, flush=True)
-    eager_ms = time_eager_step(stack, args.steps)
+    eager_ms, eager_ms_events, eager_tau = time_eager_steps(stack, drafts, args.warmup, args.steps)
+    graph_ms, graph_ms_events = ms, ms_events
+    # the step time is the faster of the two ways of issuing the same step
+    timing_mode = "graph" if graph_ms <= eager_ms else "eager"
+    if timing_mode == "eager":
+        ms, ms_events, tau = eager_ms, eager_ms_events, eager_tau
     per_shape = time_kernels(stack, max(2, args.steps // 4))
     tau_many = measure_tau(stack, args.tau_sets)
 
@@ -488,8 +551,9 @@ def main():
             "M": args.m, "B": stack.B, "k": stack.k, "layers": args.layers, "hidden": 4096,
             "intermediate": 12288, "vocab": stack.V, "linears_per_step": n,
             "weights_int8_gb": round(sum(e["N"] * e["K"] for e in stack.linears) / 1e9, 3),
-            "timing": "HIP-graph replay of the whole step, new drafts per step; host clock "
-                      "between torch.cuda.synchronize() calls",
+            "timing": f"the faster of a HIP-graph replay and plain stream launches of the whole "
+                      f"step ({timing_mode} here), new drafts per step; host clock between "
+                      f"torch.cuda.synchronize() calls, HIP events beside",
             "lm_head_and_accept": "one quasar_lm_head_verify call" + (
                 " (the LM head kernel's epilogue reduces the logits; one finalize kernel)"
                 if binding.workspace_bytes_linear(args.m, stack.V, 4096) == 0 else
@@ -502,6 +566,16 @@ def main():
         "tau_note": f"tau = accepted drafts + 1; mean over {args.tau_sets} seeded draft sets "
                     "(p=0.3, k=5; closed form 1.4275), greedy accept kernel on the step's logits",
         "bytes_per_step": stack.bytes_step,
+        "rejection_t1": {
+            "what": "the same step with rejection-sampling verification at T = 1 (seeded "
+                    "float32 uniforms, new per step; drafts planted against the greedy argmax)",
+            "ms_per_step": round(ms_t1, 4),
+            "ms_per_step_events": round(ms_t1_ev, 4),
+            "gbs": round(stack.bytes_step / (ms_t1 * 1e-3) / 1e9, 1),
+            "mean_tau_timed_steps": round(tau_t1, 4),
+            "verified_tokens_per_s": round(stack.B * tau_t1 / (ms_t1 * 1e-3), 1),
+        },
+        "graph_ms_per_step": round(graph_ms, 4),
         "eager_ms_per_step": round(eager_ms, 4),
         "roofline": {
             "bound": "hbm",
@@ -527,7 +601,8 @@ def main():
         bms, bbytes = time_bf16_comparator(stack, args.warmup, args.steps)
         lin_ms = ms  # the W8A8 step also includes the accept kernel (tiny)
         out["bf16_comparator"] = {
-            "what": "same linear stack + LM head, BF16 weights, torch.matmul (hipBLASLt), HIP graph",
+            "what": "same linear stack + LM head, BF16 weights, torch.matmul (hipBLASLt); the "
+                    "faster of a HIP graph and plain launches",
             "ms_per_step": round(bms, 4),
             "gbs": round(bbytes / (bms * 1e-3) / 1e9, 1),
             "w8a8_speedup": round(bms / lin_ms, 3),
@@ -547,9 +622,12 @@ def main():
         ms4, ms4_ev, _, _g4 = time_graph_steps(stack, drafts4, args.warmup, args.steps,
                                                step=stack.step_w4)
         del _g4
+        e4 = time_eager_steps(stack, drafts4, args.warmup, args.steps, step=stack.step_w4)
+        if e4[0] < ms4:
+            ms4, ms4_ev = e4[0], e4[1]
         out["w4a8_variant"] = {
             "what": "same stack and LM head with 4-bit per-channel weights (quasar_w4a8_linear), "
-                    "then the greedy accept; HIP graph",
+                    "then the greedy accept; the faster of a HIP graph and plain launches",
             "kernel": binding.w4a8_kernel_name(args.m, 4096, 4096),
             "ms_per_step": round(ms4, 4),
             "ms_per_step_events": round(ms4_ev, 4),
