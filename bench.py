@@ -116,9 +116,24 @@ class Stack:
         # epilogue reduces them, so no pass over them is algorithmically needed)
         self.bytes_step = sum(self.bytes_linear) + 4 * self.B * self.k + 8 * self.B
 
-    def linear_call(self, e):
+    def linear_call(self, e, bits: int = 8):
+        """One linear through the C ABI with its arguments marshalled once (the
+        shapes and buffers were checked when the stack was built): a step issues
+        145 of these, and plain launches must stay ahead of the GPU."""
+        import ctypes
         from w8a8_quantized_speculative_amd import binding
-        binding.quasar_w8a8_linear(e["x"], e["s"], e["wq"], e["sw"], out=e["y"], workspace=self.ws)
+        key = "_args%d" % bits
+        if key not in e:
+            P = ctypes.c_void_p
+            wq, sw = (e["wq"], e["sw"]) if bits == 8 else (e["wq4"], e["sw4"])
+            head = (P(e["x"].data_ptr()), P(e["s"].data_ptr()), P(wq.data_ptr()),
+                    P(sw.data_ptr()), self.M, e["N"], e["K"], P(e["y"].data_ptr()), None)
+            e[key] = head + ((P(self.ws.data_ptr()), self.ws.numel()) if bits == 8 else ())
+        L = binding.lib()
+        fn = L.quasar_w8a8_linear if bits == 8 else L.quasar_w4a8_linear
+        st = fn(*e[key], binding._stream())
+        if st != 0:
+            raise binding.QuasarError(fn.__name__, st)
 
     def accept_call(self):
         import ctypes
@@ -175,9 +190,8 @@ class Stack:
     def step_w4(self):
         """The same step with 4-bit weights: every linear through quasar_w4a8_linear,
         then the greedy accept on the LM head's logits."""
-        from w8a8_quantized_speculative_amd import binding
         for e in self.linears:
-            binding.quasar_w4a8_linear(e["x"], e["s"], e["wq4"], e["sw4"], out=e["y"])
+            self.linear_call(e, bits=4)
         self.accept_call()
 
 
