@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 METRIC = ("W8A8 verify-linear HBM GB/s (% of peak) + verified tokens/s at M=6, "
           "Qwen3-8B shape")
 PEAK_HBM_GBS = 8000.0
+PEAK_INT8_TOPS = 5000.0  # MI355X dense INT8 MFMA peak (no sparsity)
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 512 << 20  # calibration copy: plain copy kernel of a known size
 BLOCKER_COPIES = 100    # copies queued ahead of each event-timed step (~20 ms of GPU work)
@@ -518,19 +519,23 @@ def main():
     groups = {}
     for i, e in enumerate(stack.linears):
         name = binding.w8a8_kernel_name(args.m, e["N"], e["K"])
-        g = groups.setdefault(name, {"launches_per_step": 0, "bytes": 0, "ms": 0.0})
+        g = groups.setdefault(name, {"launches_per_step": 0, "bytes": 0, "ms": 0.0, "ops": 0})
         g["launches_per_step"] += 1
         g["bytes"] += stack.bytes_linear[i]
+        g["ops"] += 2 * args.m * e["N"] * e["K"]
         g["ms"] += per_shape[(e["N"], e["K"])]
     kernels = []
     for name, g in groups.items():
         n_l = g["launches_per_step"]
         launch_ms = g["ms"] / n_l
         bpl = g["bytes"] / n_l
+        opl = g["ops"] / n_l
         kernels.append({"kernel": name, "launches_per_step": n_l,
                         "algorithmic_bytes_per_launch": int(bpl),
+                        "algorithmic_int8_ops_per_launch": int(opl),
                         "launch_avg_us": round(launch_ms * 1e3, 2),
                         "gbs": round(bpl / (launch_ms * 1e-3) / 1e9, 1),
+                        "tops": round(opl / (launch_ms * 1e-3) / 1e12, 2),
                         "bytes_share": round(g["bytes"] / sum(stack.bytes_linear), 4)})
     kernels.sort(key=lambda k: -k["bytes_share"])
     dom = kernels[0]
@@ -605,6 +610,15 @@ def main():
             "timing": ("HIP events on the launch stream around back-to-back batches of the "
                        "kernel's launches, in the step's mix of shapes"),
             "traffic_note": traffic_note,
+        },
+        "mfma": {
+            "kernel": dom["kernel"],
+            "achieved_tops": dom["tops"],
+            "peak_tops": PEAK_INT8_TOPS,
+            "frac": round(dom["tops"] / PEAK_INT8_TOPS, 4),
+            "note": "algorithmic 2*M*N*K INT8 ops per launch / launch time, against MI355X's "
+                    "dense INT8 MFMA peak; executed MFMA ops and busy cycles come from a "
+                    "rocprofv3 counter pass (profiling.py mfma)",
         },
         "kernels": kernels,
         "linears": linears,

@@ -12,10 +12,17 @@ Two kinds of run are summarised (the commands are recorded in each summary):
   number of bytes), and the scaled HBM bytes per launch of the roofline kernel
   are written to a JSON file that ``bench.py`` reports as ``roofline.traffic``
   while the kernel sources still hash to the recorded value.
+* ``mfma``: one ``rocprofv3 --pmc`` run of the bench with the INT8 MFMA counters
+  ``SQ_INSTS_VALU_MFMA_MOPS_I8 SQ_INSTS_VALU_MFMA_I8 SQ_VALU_MFMA_BUSY_CYCLES
+  GRBM_GUI_ACTIVE``.  Per linear kernel: MFMA instructions and executed INT8
+  ops per dispatch (MOPS x 512), ops per instruction (32768 for the 16x16x64
+  INT8 MFMA: a check of the scaling), the MFMA busy share of the SIMDs' cycles
+  while the GPU was active, and the executed TOP/s at the bench's launch time.
 
     python -m w8a8_quantized_speculative_amd.profiling stats STATS_CSV BENCH_JSON OUT_MD --command CMD
     python -m w8a8_quantized_speculative_amd.profiling pmc FETCH_CSV WRITE_CSV BENCH_JSON OUT_JSON OUT_MD \\
         --command-fetch CMD --command-write CMD
+    python -m w8a8_quantized_speculative_amd.profiling mfma PMC_CSV BENCH_JSON OUT_MD --command CMD
 """
 from __future__ import annotations
 
@@ -188,6 +195,55 @@ def summarize_pmc(fetch_csv: str, write_csv: str, bench_json: str, out_json: str
     return res
 
 
+SIMDS = 1024        # MI355X: 256 compute units x 4 SIMDs
+PEAK_INT8_TOPS = 5000.0
+
+
+def summarize_mfma(pmc_csv: str, bench_json: str, out_md: str, command: str) -> dict:
+    bench = _bench_line(bench_json)
+    mops = _counter_means(pmc_csv, "SQ_INSTS_VALU_MFMA_MOPS_I8")
+    insts = _counter_means(pmc_csv, "SQ_INSTS_VALU_MFMA_I8")
+    busy = _counter_means(pmc_csv, "SQ_VALU_MFMA_BUSY_CYCLES")
+    active = _counter_means(pmc_csv, "GRBM_GUI_ACTIVE")
+    launch_us = {k["kernel"]: k for k in bench.get("kernels", [])}
+    rows, res = [], {}
+    for name in sorted(mops, key=lambda n: -mops[n][0] * mops[n][1]):
+        if not (name.startswith("w8a8_linear") or name.startswith("w4a8_linear")):
+            continue
+        ops = mops[name][0] * 512
+        ni = insts.get(name, (0, 0))[0]
+        b = busy.get(name, (0, 0))[0]
+        a = active.get(name, (0, 0))[0]
+        util = b / (a * SIMDS) if a else 0.0
+        k = launch_us.get(name)
+        tops = ops / (k["launch_avg_us"] * 1e-6) / 1e12 if k else None
+        alg = k.get("algorithmic_int8_ops_per_launch") if k else None
+        res[name] = {"dispatches": mops[name][1], "mfma_insts_per_dispatch": round(ni),
+                     "executed_int8_ops_per_dispatch": round(ops),
+                     "ops_per_inst": round(ops / ni, 1) if ni else None,
+                     "mfma_busy_frac": round(util, 4),
+                     "executed_tops": round(tops, 2) if tops else None,
+                     "algorithmic_int8_ops_per_launch_in_step": alg}
+        rows.append(f"| `{_cell(name)}` | {mops[name][1]} | {ni:.0f} | {ops:.3e} | "
+                    f"{(ops / ni) if ni else 0:.0f} | {100 * util:.2f}% | "
+                    f"{(f'{tops:.1f}') if tops else '-'} | {(f'{alg:.3e}') if alg else '-'} |")
+    out = ["# INT8 MFMA use (rocprofv3 PMC): " + bench["config"]["workload"], "",
+           "Profiled command (paths relative to the repository root of the GPU run):", "",
+           "```", command, "```", "", "Summary written by:", "", "```", _self_command(), "```", "",
+           "Per dispatch, mean over every launch of the kernel in the run (the bench's mix of "
+           "shapes).  Executed ops = SQ_INSTS_VALU_MFMA_MOPS_I8 x 512; they include the MFMA "
+           "work on padding (token columns past M, channels past N), so they exceed the "
+           "algorithmic 2*M*N*K.  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x "
+           f"{SIMDS} SIMDs).  TOP/s = executed ops / the bench's mean launch time "
+           f"(dense INT8 peak {PEAK_INT8_TOPS:.0f} TOP/s).", "",
+           "| kernel | dispatches | MFMA insts | executed INT8 ops | ops/inst | MFMA busy | "
+           "executed TOP/s | algorithmic ops/launch (step mix) |",
+           "|---|---:|---:|---:|---:|---:|---:|---:|"] + rows + [""]
+    with open(out_md, "w") as f:
+        f.write("\n".join(out))
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -205,8 +261,16 @@ def main():
     b.add_argument("out_md")
     b.add_argument("--command-fetch", required=True)
     b.add_argument("--command-write", required=True)
+    c = sub.add_parser("mfma")
+    c.add_argument("pmc_csv")
+    c.add_argument("bench_json")
+    c.add_argument("out_md")
+    c.add_argument("--command", required=True)
     args = ap.parse_args()
-    if args.cmd == "stats":
+    if args.cmd == "mfma":
+        print(json.dumps(summarize_mfma(args.pmc_csv, args.bench_json, args.out_md,
+                                        args.command)))
+    elif args.cmd == "stats":
         print(json.dumps(summarize_stats(args.stats_csv, args.bench_json, args.out_md,
                                          args.command)))
     else:
