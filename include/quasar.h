@@ -9,6 +9,12 @@
  * arXiv 2603.01399; pt, nl, zh and ko pages).  Citations below name the page
  * and the numbered section of its technical summary.
  *
+ * Calls: quasar_quantize_weights (offline INT8 weights), quasar_w8a8_linear
+ * (the verify linear), quasar_verify_accept (greedy or rejection accept), and
+ * quasar_lm_head_verify (the LM head and the accept step in one call); the
+ * 4-bit weight variant quasar_quantize_weights_w4 / quasar_w4a8_linear; size
+ * queries and diagnostics.
+ *
  * Conventions for every call
  *   - Tensors are row-major and contiguous.  BF16 values travel as uint16_t bit
  *     patterns.  Every tensor pointer is a DEVICE pointer (hipMalloc or torch
