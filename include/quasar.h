@@ -130,8 +130,8 @@ quasar_status quasar_quantize_activations(const uint16_t* x, const float* s, int
  * verify windows of M <= 8 tokens with K <= 12288, which keep the quantized
  * activations in on-chip memory; other shapes stage the quantized activations
  * and the INT32 partial sums of output groups shared by two workgroups in the
- * workspace (M*K + 4*M bytes plus 4 KB per 16-token block and compute unit,
- * each part rounded up to 256). */
+ * workspace (1 KB per 16-token block and 64-wide K chunk, 4*M bytes, and
+ * 16 KB per 16-token block and compute unit, each part rounded up to 256). */
 size_t quasar_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Diagnostic: the kernel(s) quasar_w8a8_linear launches for an M x N x K

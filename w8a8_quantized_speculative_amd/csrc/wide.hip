@@ -12,7 +12,14 @@
 //
 //   1. Rows.  Workgroup m < M smooths and quantizes token row m
 //      (xs = RN32(x * s), absmax, scale, codes) into the workspace, then
-//      publishes a per-workgroup flag.  Every workgroup waits until the M row
+//      publishes a per-workgroup flag.  The codes are stored fragment-major:
+//      the 16 x 64 fragment of token block tb at K chunk c is one contiguous
+//      1 KB at (tb * nch + c) KB, lane l = 16 g + r holding the 16 codes of
+//      token 16 tb + r at K positions 64 c + 16 g .. + 15 (the MFMA B operand
+//      order), so a fragment load is one contiguous 1 KB read.  Measured on
+//      MI355X with every compute unit reading the same L2-resident 384 KB:
+//      128 GB/s per compute unit this way, 37 GB/s with the 16 rows of a
+//      fragment K bytes apart (row-major codes).  Every workgroup waits until the M row
 //      flags are set -- a one-way grid barrier.  Meanwhile its streamer
 //      wavefronts already have their first weights in flight.
 //   2. Items.  The output channels are cut into groups of 4 tiles of 16
@@ -239,13 +246,12 @@ __device__ __forceinline__ void wide_streamer(const int8_t* __restrict__ wq,
     }
   };
   // Codes of the next item into this streamer's LDS slot bb: fragment tb holds
-  // token block tb at K chunk (item * 4 + w); lane l = 16 g + r reads 16 codes
-  // of token 16 tb + r at K positions 64 c + 16 g, and the direct-to-LDS load
-  // stores them at l * 16.  Token rows >= M read as zero (buffer bound); K
-  // positions past K read the next row's codes or zero, which meet zero
-  // weights.
-  const buffer_rsrc qrs = make_rsrc(qx, (uint32_t)M * (uint32_t)K);
-  const int lane_off = (lane & 15) * K + (lane >> 4) * 16;
+  // token block tb at K chunk (item * 4 + w), one contiguous 1 KB of the
+  // fragment-major codes, which the direct-to-LDS load stores in lane order.
+  // Token rows >= M hold whatever the workspace held: they only reach output
+  // rows that are never stored.  A chunk past K meets zero weights.
+  const buffer_rsrc qrs = make_rsrc(qx, (uint32_t)MB * (uint32_t)nch * 1024u);
+  const int lane_off = lane * 16;
   char* my_slots = slots + w * NB * MB * 1024;
   int cp_issue = i0 - (i0 / P) * P, cissued = 0;
   auto issue_codes = [&](int bb) {
@@ -255,7 +261,7 @@ __device__ __forceinline__ void wide_streamer(const int8_t* __restrict__ wq,
     for (int tb = 0; tb < MB; ++tb)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           qrs, (__attribute__((address_space(3))) void*)(my_slots + (bb * MB + tb) * 1024), 16,
-          live ? lane_off + tb * 16 * K + c * 64 : kOutOfRange, 0, 0, 0);
+          live ? lane_off + (tb * nch + c) * 1024 : kOutOfRange, 0, 0, 0);
     ++cissued;
     if (++cp_issue == P) cp_issue = 0;
   };
@@ -400,7 +406,11 @@ __device__ __forceinline__ void quantize_row_compute(const uint16_t* __restrict_
   for (int h = 0; h < kHelpers; ++h) row_amax = fmaxf(row_amax, amax_part[h]);
   const QParams qp = row_qparams(row_amax);
 
-  int8_t* qrow = qx + (size_t)m * K;
+  // piece q (K positions 8 q .. 8 q + 7) of token m: byte 8 (q % 2) of lane
+  // 16 g + m % 16 of the fragment of token block m / 16 at K chunk q / 8,
+  // g = (q / 2) % 4
+  const int nch = (K + 63) >> 6;
+  int8_t* qblk = qx + (size_t)(m >> 4) * nch * 1024 + (m & 15) * 16;
   auto emit = [&](int q, const float v[8]) {
     uint32_t cb[8];
 #pragma unroll
@@ -408,7 +418,7 @@ __device__ __forceinline__ void quantize_row_compute(const uint16_t* __restrict_
     uint2 pk;
     pk.x = pack4_low_bytes(cb[0], cb[1], cb[2], cb[3]);
     pk.y = pack4_low_bytes(cb[4], cb[5], cb[6], cb[7]);
-    store8_device(qrow + q * 8, pk);
+    store8_device(qblk + (q >> 3) * 1024 + ((q >> 1) & 3) * 256 + (q & 1) * 8, pk);
   };
   if (in_regs) {
 #pragma unroll
@@ -749,8 +759,8 @@ __device__ __forceinline__ void wide_shared_streamer(const int8_t* __restrict__ 
   // f = w, w + 4, ...; loads past the item's FR fragments, or past the range
   // (the slot may still be read by another streamer), go to a dummy area, so
   // that every streamer issues NBS loads per item.
-  const buffer_rsrc qrs = make_rsrc(qx, (uint32_t)M * (uint32_t)K);
-  const int lane_off = (lane & 15) * K + (lane >> 4) * 16;
+  const buffer_rsrc qrs = make_rsrc(qx, (uint32_t)MB * (uint32_t)nch * 1024u);
+  const int lane_off = lane * 16;
   int cpi = i0 - (i0 / P) * P, cissued = 0;
   auto issue_codes = [&](int bb) {
     const bool live = cissued < n;
@@ -762,7 +772,8 @@ __device__ __forceinline__ void wide_shared_streamer(const int8_t* __restrict__ 
       char* dst = (live && real) ? lds + (bb * C::FR + f) * 1024 : lds + C::O_DUMMY;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           qrs, (__attribute__((address_space(3))) void*)dst, 16,
-          (live && real) ? lane_off + tb * 16 * K + (cpi * kIC + ic) * 64 : kOutOfRange, 0, 0, 0);
+          (live && real) ? lane_off + (tb * nch + cpi * kIC + ic) * 1024 : kOutOfRange, 0, 0,
+          0);
     }
     ++cissued;
     if (++cpi == P) cpi = 0;
@@ -1081,8 +1092,8 @@ WidePlan plan_wide(int64_t M, int64_t N, int64_t K, int grid) {
   p.grid = grid;
   p.lds = p.tg >= 8 ? 0 : wide_lds_of(p.mb, p.tg);  // the shared mode sets its own
   size_t off = 0;
-  p.off_qx = off;
-  off = align_up(off + (size_t)(M * K), kWsAlign);
+  p.off_qx = off;  // fragment-major codes: 1 KB per 16-token block and 64-wide K chunk
+  off = align_up(off + (size_t)p.mb * p.nch * 1024, kWsAlign);
   p.off_sx = off;
   off = align_up(off + (size_t)M * sizeof(float), kWsAlign);
   p.off_partials = off;
