@@ -209,19 +209,18 @@ def test_kernel_name_names_the_launch_plan(L):
     assert name(8, 4096, 8192) == "w8a8_linear_fused_kernel<8, 4, 4>"
     # wider windows (or K > 12288): one launch over ceil(M / 16) token blocks
     # <token blocks, tiles per group>: one tile per group up to 512 tiles while
-    # the code matrix is at most 96 x 4096 bytes
+    # the code matrix is at most 96 x 12288 bytes, groups of 4 tiles otherwise
     assert name(48, 4096, 4096) == "w8a8_linear_wide_kernel<3, 1>"
-    assert name(96, 4096, 12288) == "w8a8_linear_wide_kernel<6, 4>"
-    assert name(48, 4096, 12288) == "w8a8_linear_wide_kernel<3, 4>"
+    assert name(96, 4096, 12288) == "w8a8_linear_wide_kernel<6, 1>"
+    assert name(48, 4096, 12288) == "w8a8_linear_wide_kernel<3, 1>"
+    assert name(128, 4096, 12288) == "w8a8_linear_wide_kernel<8, 4>"
     assert name(96, 6144, 4096) == "w8a8_linear_wide_kernel<6, 1>"
     assert name(9, 16, 16) == "w8a8_linear_wide_kernel<1, 1>"
     assert name(6, 64, 16384) == "w8a8_linear_wide_kernel<1, 1>"
     assert name(96, 24576, 4096) == "w8a8_linear_wide_kernel<6, 4>"
-    # at least 16 tiles per workgroup: groups of 16 (8 above 96 tokens) whose
-    # activation fragments the four streamers share
-    assert name(48, 151936, 4096) == "w8a8_linear_wide_shared_kernel<3, 16>"
-    assert name(96, 151936, 4096) == "w8a8_linear_wide_shared_kernel<6, 16>"
-    assert name(128, 151936, 4096) == "w8a8_linear_wide_shared_kernel<8, 8>"
+    assert name(48, 151936, 4096) == "w8a8_linear_wide_kernel<3, 4>"
+    assert name(96, 151936, 4096) == "w8a8_linear_wide_kernel<6, 4>"
+    assert name(128, 151936, 4096) == "w8a8_linear_wide_kernel<8, 4>"
     # invalid or unsupported sizes
     assert name(0, 16, 16) == "" and name(6, 16, 17) == "" and name(129, 16, 16) == ""
 

@@ -74,14 +74,15 @@ RAGGED = [
     # shared by several workgroups (partial sums), and ranges that are empty
     (9, 100, 1024), (20, 64, 4096), (33, 1000, 2112), (64, 520, 4096), (80, 260, 1040),
     (112, 77, 3072), (128, 300, 4096), (16, 64, 4096), (40, 8000, 512), (24, 6144, 4096),
+    # one-tile groups over a 96 x 12288 code matrix; groups of 4 just past it
+    (96, 520, 12288), (128, 300, 12288),
     # K beyond the one-launch small-window kernel, up to the largest supported K
     (6, 64, 16384), (1, 40, 65536), (50, 48, 20480),
     # 4 to 5 tiles per workgroup: groups of 4 tiles split across workgroups
     (20, 16400, 320), (100, 16384, 1040), (128, 16500, 2112), (9, 16390, 4160),
     (70, 20000, 576),
-    # at least 16 tiles per workgroup: groups of 16 (8 above 96 tokens) whose
-    # activation fragments all four streamers share; every token-block count,
-    # ragged N and K (odd chunk counts), groups split across workgroups
+    # at least 16 tiles per workgroup (groups of 4 tiles): every token-block
+    # count, ragged N and K (odd chunk counts), groups split across workgroups
     (9, 65600, 320), (20, 66000, 208), (48, 70000, 208), (33, 66000, 96), (64, 65540, 576),
     (70, 65600, 1040), (96, 65600, 64), (100, 65536, 192), (128, 66000, 320),
 ]

@@ -1,8 +1,8 @@
 """GPU parity on seeded random shapes, every element against the oracle.
 
 40 (M, N, K) drawn once from a fixed seed: M from 1 to the 128-token limit
-(every path: the one-launch kernel, the wide kernel's one- and four-tile
-groups and its shared-fragment mode), K any multiple of 16 up to 16384, N from
+(every path: the one-launch kernel and the wide kernel's one- and four-tile
+groups), K any multiple of 16 up to 16384, N from
 1 to 70000; N*K <= 1.2e8 and M*N*K <= 2e9 keep the oracle within seconds.
 The 4-bit path gets 15 shapes of its own (M <= 8, K a multiple of 128 up to
 12288).

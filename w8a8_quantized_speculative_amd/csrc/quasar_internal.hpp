@@ -76,7 +76,7 @@ constexpr int kWideMaxGrid = 256;
 struct WidePlan {
   int64_t M, N, K;
   int mb;      // 16-token blocks: ceil(M / 16), 1..8
-  int tg;      // 16-channel tiles per group: 1 or 4 (fragments per streamer), 8 or 16 (shared)
+  int tg;      // 16-channel tiles per group: 1 or 4
   int tiles;   // ceil(N / 16)
   int nch;     // ceil(K / 64)
   int groups;  // ceil(tiles / tg)

@@ -442,9 +442,9 @@ __device__ __forceinline__ void quantize_row_compute(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Helper prologue of both wide kernels: quantize token row b (b < M) into the
-// workspace and raise this workgroup's row flag, then wait until every token
-// row of the launch is there (helper wavefront 0 polls the flags with
+// Helper prologue: quantize token row b (b < M) into the workspace and raise
+// this workgroup's row flag, then wait until every token row of the launch is
+// there (helper wavefront 0 polls the flags with
 // device-scope loads; the rows are read only after this).  Contains the
 // workgroup barrier (1).  Returns false when the workgroup has no items; `e`
 // is this workgroup's launch count before the launch.
@@ -673,347 +673,6 @@ __global__ __launch_bounds__(kThreads) void w8a8_linear_wide_kernel(
                         acc_out);
 }
 
-// ===========================================================================
-// Shared-fragment mode, for linears with many tiles (gate_up, the LM head).
-// Groups are TG = 8 or 16 tiles and streamer w owns the TG / 4 tiles
-// [w TG/4, (w+1) TG/4) of a group over all of K, so each activation fragment is
-// fetched once per workgroup and used by all four streamers: M / (16 TG) code
-// bytes per weight byte instead of M / 64.  An item is 2 chunks (128 K
-// positions); its 2 MB fragments are fetched a quarter by each streamer into a
-// slot shared by all four, which count the fragments landed and read on two
-// LDS counters per slot.  At a group end each streamer writes the complete
-// sums of its tiles to an LDS area, where the helpers dequantize them (or hand
-// a shared group's partial sums to the workspace).
-// ===========================================================================
-constexpr int kIC = 2;  // 64-wide K chunks per item in the shared-fragment mode
-
-template <int MB, int TG>
-struct WideShared {
-  static constexpr int TGW = TG / kS;             // tiles per streamer
-  static constexpr int FR = kIC * MB;             // fragments per item
-  static constexpr int NBS = (FR + kS - 1) / kS;  // fragment loads per streamer and item
-  static constexpr int ALD = TGW * kIC;           // weight loads per streamer and item
-  static constexpr int NBUF = TG == 16 ? 2 : 4;   // items in flight (16 KB of weights per streamer)
-  static constexpr int SLOTS = NBUF * FR * 1024;
-  static constexpr int DUMMY = 1024;              // target of the padding loads
-  static constexpr int PART = TG * MB * 1024;     // one group's sums, [tile][token block][lane][4]
-  static constexpr int WS = 2 * TG * 16 * 4;      // weight scales of two groups
-  static constexpr int SYNC = 256;
-  static constexpr int O_DUMMY = SLOTS;
-  static constexpr int O_PART = O_DUMMY + DUMMY;
-  static constexpr int O_WS = O_PART + PART;
-  static constexpr int O_SYNC = O_WS + WS;
-  static constexpr int LDS = O_SYNC + SYNC;
-};
-template <int MB, int TG>
-constexpr bool wide_shared_fits() {
-  using C = WideShared<MB, TG>;
-  return C::LDS <= 150 * 1024 && (C::NBUF - 1) * (C::ALD + C::NBS) + C::NBS <= 63;
-}
-static_assert(wide_shared_fits<6, 16>() && wide_shared_fits<8, 8>() && wide_shared_fits<1, 16>(),
-              "shared-fragment mode: LDS budget and in-flight loads");
-
-// LDS synchronisation words of the shared-fragment mode (besides kRowDone,
-// kAmaxCnt, kGate, kPartDone, kAmax and kFlagOut of the prologue)
-enum : int {
-  kSFilled = 0,     // [4] per slot: streamers whose fragment loads of it have landed
-  kSConsumed = 8,   // [4] per slot: streamers that read it
-  kSPartReady = 16, // streamers that wrote a group's sums to LDS
-  kSPartFree = 17   // helper wavefronts done with the group's sums in LDS
-};
-
-template <int MB, int TG>
-__device__ __forceinline__ void wide_shared_streamer(const int8_t* __restrict__ wq,
-                                                     const int8_t* __restrict__ qx, int M, int K,
-                                                     int tiles, int nch, int P, int i0, int n,
-                                                     int w, int lane, bool quantizer, char* lds,
-                                                     int* sync) {
-  using C = WideShared<MB, TG>;
-  constexpr int NB = C::NBUF, TGW = C::TGW;
-  const int voff = lane * 16;
-
-  // weights of the next item into buffer bb: chunks 2 ip, 2 ip + 1 of this
-  // streamer's tiles
-  v4i a[NB][TGW][kIC];
-  int ig = i0 / P, ip = i0 - (i0 / P) * P, wissued = 0;
-  auto issue_weights = [&](int bb) {
-    const bool live = wissued < n;
-#pragma unroll
-    for (int tt = 0; tt < TGW; ++tt)
-#pragma unroll
-      for (int ic = 0; ic < kIC; ++ic) {
-        const int t = ig * TG + w * TGW + tt, c = ip * kIC + ic;
-        const bool ok = live && t < tiles && c < nch;
-        const buffer_rsrc rs =
-            make_rsrc(wq + ((size_t)(ok ? t : 0) * nch + (ok ? c : 0)) * 1024, ok ? 1024u : 0u);
-        a[bb][tt][ic] = load16<kNonTemporal>(rs, voff);
-      }
-    ++wissued;
-    if (++ip == P) {
-      ip = 0;
-      ++ig;
-    }
-  };
-  // This streamer's quarter of the next item's fragments into slot bb:
-  // fragment f = ic * MB + tb (token block tb at K chunk 2 item + ic) for
-  // f = w, w + 4, ...; loads past the item's FR fragments, or past the range
-  // (the slot may still be read by another streamer), go to a dummy area, so
-  // that every streamer issues NBS loads per item.
-  const buffer_rsrc qrs = make_rsrc(qx, (uint32_t)MB * (uint32_t)nch * 1024u);
-  const int lane_off = lane * 16;
-  int cpi = i0 - (i0 / P) * P, cissued = 0;
-  auto issue_codes = [&](int bb) {
-    const bool live = cissued < n;
-#pragma unroll
-    for (int q = 0; q < C::NBS; ++q) {
-      const int f = w + kS * q;
-      const bool real = f < C::FR;
-      const int ic = f / MB, tb = f - (f / MB) * MB;
-      char* dst = (live && real) ? lds + (bb * C::FR + f) * 1024 : lds + C::O_DUMMY;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          qrs, (__attribute__((address_space(3))) void*)dst, 16,
-          (live && real) ? lane_off + (tb * nch + cpi * kIC + ic) * 1024 : kOutOfRange, 0, 0,
-          0);
-    }
-    ++cissued;
-    if (++cpi == P) cpi = 0;
-  };
-
-  __syncthreads();  // (1) the row quantizer's activation loads are queued first
-  if (n == 0) return;
-  if (quantizer) lds_wait_ge_asm(lds_address(sync + kFlagOut), 1);
-#pragma unroll
-  for (int bb = 0; bb < NB; ++bb) issue_weights(bb);
-  lds_wait_ge_asm(lds_address(sync + kGate), 1);
-#pragma unroll
-  for (int bb = 0; bb < NB; ++bb) issue_codes(bb);
-  __builtin_amdgcn_sched_barrier(0);
-
-  v4i acc[TGW][MB];
-#pragma unroll
-  for (int tt = 0; tt < TGW; ++tt)
-#pragma unroll
-    for (int tb = 0; tb < MB; ++tb) acc[tt][tb] = (v4i){0, 0, 0, 0};
-
-  const uint32_t slot_addr = lds_address(lds) + lane * 16;
-  const uint32_t part_addr = lds_address(lds + C::O_PART) + w * TGW * MB * 1024 + lane * 16;
-  const uint32_t sync_addr = lds_address(sync);
-  int cp = i0 - (i0 / P) * P;
-  int gk = 0;  // groups handed to the helpers
-  for (int jb = 0; jb < n; jb += NB) {
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-      const int j = jb + bb;
-      if (j < n) {
-        // own weights and fragment loads of item j have landed: (NB - 1) NBS
-        // fragment loads of later items plus the weights issued since remain
-        switch (j < NB - 1 ? j : NB - 1) {
-          case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * C::NBS)); break;
-          case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * C::NBS + 1 * C::ALD)); break;
-          case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * C::NBS + 2 * C::ALD)); break;
-          default: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * C::NBS + 3 * C::ALD)); break;
-        }
-        if (lane == 0) lds_add_asm(sync_addr + (kSFilled + bb) * 4, 1);
-        lds_wait_ge_asm(sync_addr + (kSFilled + bb) * 4, kS * (j / NB + 1));
-#pragma unroll
-        for (int ic = 0; ic < kIC; ++ic) {
-          v4i bf[MB];
-#pragma unroll
-          for (int tb = 0; tb < MB; ++tb)
-            bf[tb] = lds_read16_asm(slot_addr + (bb * C::FR + ic * MB + tb) * 1024);
-          lds_wait_reads();
-#pragma unroll
-          for (int tb = 0; tb < MB; ++tb) asm volatile("" : "+v"(bf[tb]));
-#pragma unroll
-          for (int tt = 0; tt < TGW; ++tt)
-#pragma unroll
-            for (int tb = 0; tb < MB; ++tb)
-              acc[tt][tb] = mfma_i8_16x16x64(a[bb][tt][ic], bf[tb], acc[tt][tb]);
-        }
-        if (lane == 0) lds_add_asm(sync_addr + (kSConsumed + bb) * 4, 1);
-      }
-      issue_weights(bb);
-      // the slot is refilled once all four streamers have read item j from it
-      if (j < n) lds_wait_ge_asm(sync_addr + (kSConsumed + bb) * 4, kS * (j / NB + 1));
-      issue_codes(bb);
-      if (j < n) {
-        if (cp == P - 1 || j == n - 1) {  // group end: sums to the helpers
-          // the helpers are done with the previous group (and, for the
-          // first, have staged its weight scales)
-          lds_wait_ge_asm(sync_addr + kSPartFree * 4, kHelpers * (gk + 1));
-#pragma unroll
-          for (int tt = 0; tt < TGW; ++tt)
-#pragma unroll
-            for (int tb = 0; tb < MB; ++tb) {
-              lds_write16_asm(part_addr + (tt * MB + tb) * 1024, acc[tt][tb]);
-              acc[tt][tb] = (v4i){0, 0, 0, 0};
-            }
-          if (lane == 0) lds_add_asm(sync_addr + kSPartReady * 4, 1);
-          ++gk;
-        }
-        if (++cp == P) cp = 0;
-      }
-    }
-  }
-}
-
-// Helpers of the shared-fragment mode after the prologue, group by group:
-// stage the next group's weight scales in LDS, then take the group's sums from
-// LDS and either store them as this workgroup's partial sums (a first group
-// shared with the workgroup that owns its first item) or add the other owners'
-// partial sums (a last group whose later items other workgroups own) and
-// dequantize.  Thread ht owns slots ht + 256 k; slot s is lane s % 64 of token
-// block (s / 64) % MB of tile s / (64 MB), i.e. token 16 tb + l % 16 and
-// channels 4 (l / 16) .. + 3 of the tile.
-template <int MB, int TG>
-__device__ __forceinline__ void wide_shared_helper(
-    const float* __restrict__ wscale, const float* __restrict__ sx, int M, int N, int P, int U,
-    int G, int b, int i0, int n, uint32_t e, int ht, int lane, char* lds, int* sync,
-    int32_t* __restrict__ partials, uint16_t* __restrict__ y, int32_t* __restrict__ acc_out) {
-  using C = WideShared<MB, TG>;
-  constexpr int HT = 64 * kHelpers;
-  constexpr int SLOTS = TG * MB * 64;
-  constexpr int KS = (SLOTS + HT - 1) / HT;
-  constexpr int kPartInts = 16 * MB * 256;  // a workgroup's partial-sum slot
-  const int ln = ht & 63;
-  float* wsl = reinterpret_cast<float*>(lds + C::O_WS);
-  const v4i* part = reinterpret_cast<const v4i*>(lds + C::O_PART);
-  const buffer_rsrc wrs = make_rsrc(wscale, (uint32_t)N * 4u);
-  const int g_first = i0 / P, g_last = (i0 + n - 1) / P;
-  auto stage_ws = [&](int g, int par) {
-    for (int i = ht; i < TG * 16; i += HT)
-      wsl[par * TG * 16 + i] = __int_as_float(load4(wrs, (g * TG * 16 + i) * 4));
-  };
-  // kSPartFree counts helper rounds: the first group's scales staged, then
-  // each group done
-  stage_ws(g_first, 0);
-  asm volatile("" ::: "memory");
-  if (lane == 0) lds_add(sync + kSPartFree, 1);
-  for (int g = g_first, k = 0; g <= g_last; ++g, ++k) {
-    const int par = k & 1;
-    const bool writer = g == g_first && i0 % P != 0;
-    const bool finalizer = !writer && (i0 + n) < (g + 1) * P;
-    // the next group's scales, into the buffer group k - 1 used, once every
-    // helper wavefront is done with group k - 1
-    if (g < g_last) {
-      lds_wait_ge(sync + kSPartFree, kHelpers * (k + 1));
-      stage_ws(g + 1, par ^ 1);
-    }
-    if (finalizer) {
-      for (int c = b + 1; c < G && range_start(c, U, G) < (g + 1) * P; ++c) {
-        if (range_start(c + 1, U, G) == range_start(c, U, G)) continue;  // empty range
-        for (int spin = 0; spin < kSpinGlobal; ++spin) {
-          if (__hip_atomic_load(&g_wide_part_flag[c], __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT) == e + 1u)
-            break;
-          __builtin_amdgcn_s_sleep(1);
-        }
-      }
-      asm volatile("" ::: "memory");  // the partial sums are read after the flags
-    }
-    lds_wait_ge(sync + kSPartReady, kS * (k + 1));
-#pragma unroll 1
-    for (int kk = 0; kk < KS; ++kk) {
-      const int sidx = ht + HT * kk;
-      if (sidx >= SLOTS) break;
-      v4i tot = part[sidx];
-      if (writer) {
-        store16_device(partials + (size_t)b * kPartInts + sidx * 4, tot);
-        continue;
-      }
-      if (finalizer) {
-        for (int c = b + 1; c < G && range_start(c, U, G) < (g + 1) * P; ++c)
-          if (range_start(c + 1, U, G) != range_start(c, U, G))
-            tot += *reinterpret_cast<const v4i*>(partials + (size_t)c * kPartInts + sidx * 4);
-      }
-      const int tile = sidx / (MB * 64), tb = (sidx / 64) % MB;
-      const int tok = tb * 16 + (ln & 15);
-      const int nl = tile * 16 + 4 * (ln >> 4);  // channel within the group
-      const int n0 = g * TG * 16 + nl;
-      if (tok < M && n0 < N) {
-        const float sxt = sx[tok];
-        const int tv[4] = {tot.x, tot.y, tot.z, tot.w};
-        uint32_t o[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = (float)tv[i];  // round to nearest even
-          v = v * sxt;
-          v = v * wsl[par * TG * 16 + nl + i];
-          o[i] = f32_to_bf16_rne(v);
-        }
-        uint16_t* yr = y + (size_t)tok * N;
-        if (n0 + 3 < N && ((reinterpret_cast<uintptr_t>(yr + n0) & 7) == 0)) {
-          uint2 pk;
-          pk.x = o[0] | (o[1] << 16);
-          pk.y = o[2] | (o[3] << 16);
-          *reinterpret_cast<uint2*>(yr + n0) = pk;
-        } else {
-          for (int i = 0; i < 4 && n0 + i < N; ++i) yr[n0 + i] = (uint16_t)o[i];
-        }
-        if (acc_out)
-          for (int i = 0; i < 4 && n0 + i < N; ++i) acc_out[(size_t)tok * N + n0 + i] = tv[i];
-      }
-    }
-    asm volatile("" ::: "memory");  // this group's LDS reads precede the count
-    if (writer) {
-      // the shared group's partial sums are out: raise this workgroup's flag
-      wait_stores_done();
-      if (lane == 0) lds_add(sync + kPartDone, 1);
-      if (ht == 0) {
-        lds_wait_ge(sync + kPartDone, kHelpers);
-        __hip_atomic_store(&g_wide_part_flag[b], e + 1u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    if (lane == 0) lds_add(sync + kSPartFree, 1);
-  }
-}
-
-template <int MB, int TG>
-__global__ __launch_bounds__(kThreads) void w8a8_linear_wide_shared_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ s, const int8_t* __restrict__ wq,
-    const float* __restrict__ wscale, int M, int N, int K, int tiles, int P, int U,
-    int8_t* __restrict__ qx, float* __restrict__ sx, int32_t* __restrict__ partials,
-    uint16_t* __restrict__ y, int32_t* __restrict__ acc_out) {
-  using C = WideShared<MB, TG>;
-  extern __shared__ __align__(16) char smem[];
-  int* sync = reinterpret_cast<int*>(smem + C::O_SYNC);
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int G = gridDim.x, b = blockIdx.x;
-  const int i0 = range_start(b, U, G);
-  const int n = range_start(b + 1, U, G) - i0;
-  const int nch = (K + 63) >> 6;
-  if (tid < kSyncWords) sync[tid] = 0;  // ordered before use by barrier (1)
-
-  if (wave < kS) {
-    wide_shared_streamer<MB, TG>(wq, qx, M, K, tiles, nch, P, i0, n, wave, lane, b < M, smem,
-                                 sync);
-    return;
-  }
-  const int ht = tid - 64 * kS;
-  uint32_t e;
-  if (!wide_rows_and_gate(x, s, M, K, b, n, ht, wave - kS, lane, qx, sx, sync, e)) return;
-  wide_shared_helper<MB, TG>(wscale, sx, M, N, P, U, G, b, i0, n, e, ht, lane, smem, sync,
-                             partials, y, acc_out);
-}
-
-template <int MB, int TG>
-hipError_t launch_wide_shared_mb(const WidePlan& p, const uint16_t* x, const float* s,
-                                 const int8_t* wq, const float* w_scale, uint16_t* y,
-                                 int32_t* acc_out, int8_t* qx, float* sx, int32_t* partials,
-                                 hipStream_t st) {
-  auto kernel = &w8a8_linear_wide_shared_kernel<MB, TG>;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-      WideShared<MB, TG>::LDS);
-  if (attr != hipSuccess) return attr;
-  kernel<<<dim3(p.grid), dim3(kThreads), WideShared<MB, TG>::LDS, st>>>(
-      x, s, wq, w_scale, (int)p.M, (int)p.N, (int)p.K, p.tiles, p.P, p.U, qx, sx, partials, y,
-      acc_out);
-  return hipGetLastError();
-}
-
 template <int MB, int TG>
 hipError_t launch_wide_mb(const WidePlan& p, const uint16_t* x, const float* s, const int8_t* wq,
                           const float* w_scale, uint16_t* y, int32_t* acc_out, int8_t* qx,
@@ -1058,21 +717,18 @@ static_assert(wide_lds_of(6, 4) == Wide<6, 4>::LDS && wide_lds_of(3, 1) == Wide<
 // serve 4 tiles (a quarter of the code bytes per weight byte), but leave a
 // linear with few tiles with fewer groups than workgroups, so that a group's
 // K range is split across several workgroups that must hand INT32 partial
-// sums to each other at the end (a few microseconds at the end of the launch).
-// With groups of one tile each workgroup instead reads the whole M x K code
-// matrix per tile.  Measured on MI355X: one-tile groups are faster up to 2
-// tiles per workgroup while the code matrix is at most 384 KB (96 x 4096);
-// beyond that (e.g. 96 x 12288) the code bytes cost more than the hand-over.
-// With at least 16 tiles per workgroup (an LM head) the shared-fragment mode
-// takes groups of 16 tiles (8 above 96 tokens, for LDS): at 96 tokens it cuts
-// the 4096 -> 151936 LM head from 197 to 163 us.  Below that it lost to
-// groups of 4 (gate_up 4096 -> 24576: 46 against 42 us at 96 tokens, 34
-// against 30 us at 48): the four streamers wait for each other on every item.
+// sums to each other at the end of the launch.  With groups of one tile each
+// workgroup instead reads the whole code matrix per tile, at the L2 read rate
+// of contiguous 1 KB fragments.  Measured on MI355X (16 to 128 tokens): one-tile
+// groups are faster up to 2 tiles per workgroup (QKV, O, down) while the code
+// matrix is at most 96 x 12288; groups of 4 are faster beyond (gate_up, the LM
+// head; down at 128 tokens).  Sharing each fragment among 16 tiles through LDS
+// no longer paid once fragments were contiguous: 164 against 163 us on the
+// 4096 -> 151936 LM head at 96 tokens, 206 against 183 at 128.
 int wide_tiles_per_group(int64_t M, int64_t N, int64_t K, int grid) {
   const int64_t tiles = (N + 15) / 16;
   const int64_t g = grid > 0 ? grid : kWideMaxGrid;
-  if (tiles <= 2 * g && M * K <= 96 * 4096) return 1;
-  if (tiles >= 16 * g) return M <= 96 ? 16 : 8;
+  if (tiles <= 2 * g && M * K <= 96 * 12288) return 1;
   return kMaxTG;
 }
 
@@ -1086,30 +742,22 @@ WidePlan plan_wide(int64_t M, int64_t N, int64_t K, int grid) {
   p.tiles = (int)((N + 15) / 16);
   p.nch = (int)((K + 63) / 64);
   p.groups = (p.tiles + p.tg - 1) / p.tg;
-  const int item_chunks = p.tg >= 8 ? kIC : kS;  // 64-wide K chunks per item
-  p.P = (p.nch + item_chunks - 1) / item_chunks;
+  p.P = (p.nch + kS - 1) / kS;  // items of 4 64-wide K chunks
   p.U = p.groups * p.P;
   p.grid = grid;
-  p.lds = p.tg >= 8 ? 0 : wide_lds_of(p.mb, p.tg);  // the shared mode sets its own
+  p.lds = wide_lds_of(p.mb, p.tg);
   size_t off = 0;
   p.off_qx = off;  // fragment-major codes: 1 KB per 16-token block and 64-wide K chunk
   off = align_up(off + (size_t)p.mb * p.nch * 1024, kWsAlign);
   p.off_sx = off;
   off = align_up(off + (size_t)M * sizeof(float), kWsAlign);
   p.off_partials = off;
-  off = align_up(off + (size_t)kWideMaxGrid * 16 * p.mb * 1024, kWsAlign);  // up to 16 tiles
+  off = align_up(off + (size_t)kWideMaxGrid * kMaxTG * p.mb * 1024, kWsAlign);
   p.bytes = off;
   return p;
 }
 
 const char* wide_kernel_name(int mb, int tg) {
-  // shared-fragment mode: groups of 16 up to 6 token blocks, of 8 above
-  static const char* const shared_names[8] = {
-      "w8a8_linear_wide_shared_kernel<1, 16>", "w8a8_linear_wide_shared_kernel<2, 16>",
-      "w8a8_linear_wide_shared_kernel<3, 16>", "w8a8_linear_wide_shared_kernel<4, 16>",
-      "w8a8_linear_wide_shared_kernel<5, 16>", "w8a8_linear_wide_shared_kernel<6, 16>",
-      "w8a8_linear_wide_shared_kernel<7, 8>",  "w8a8_linear_wide_shared_kernel<8, 8>"};
-  if (tg >= 8) return shared_names[(mb < 1 ? 1 : (mb > 8 ? 8 : mb)) - 1];
   static const char* const names[2][8] = {
       {"w8a8_linear_wide_kernel<1, 1>", "w8a8_linear_wide_kernel<2, 1>",
        "w8a8_linear_wide_kernel<3, 1>", "w8a8_linear_wide_kernel<4, 1>",
@@ -1130,15 +778,6 @@ hipError_t launch_wide(const WidePlan& p, const uint16_t* x, const float* s, con
   float* sx = reinterpret_cast<float*>(ws + p.off_sx);
   int32_t* partials = reinterpret_cast<int32_t*>(ws + p.off_partials);
   if (p.tg == 1) return launch_wide_tg<1>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
-  if (p.tg == 8 || p.tg == 16) {
-#define QUASAR_SHARED(MB_, TG_)                                                                  \
-  if (p.mb == MB_ && p.tg == TG_)                                                                \
-    return launch_wide_shared_mb<MB_, TG_>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
-    QUASAR_SHARED(1, 16) QUASAR_SHARED(2, 16) QUASAR_SHARED(3, 16) QUASAR_SHARED(4, 16)
-    QUASAR_SHARED(5, 16) QUASAR_SHARED(6, 16) QUASAR_SHARED(7, 8) QUASAR_SHARED(8, 8)
-#undef QUASAR_SHARED
-    return hipErrorInvalidValue;
-  }
   if (p.tg == kMaxTG)
     return launch_wide_tg<kMaxTG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
   return hipErrorInvalidValue;
@@ -1161,8 +800,6 @@ int wide_grid_for_current_device() {
     int lds = 0;
     for (int mb = 1; mb <= 8; ++mb)
       for (int tg : {1, kMaxTG}) lds = wide_lds_of(mb, tg) > lds ? wide_lds_of(mb, tg) : lds;
-    lds = WideShared<6, 16>::LDS > lds ? WideShared<6, 16>::LDS : lds;
-    lds = WideShared<8, 8>::LDS > lds ? WideShared<8, 8>::LDS : lds;
     auto kernel = &w8a8_linear_wide_kernel<6, kMaxTG>;
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess ||
