@@ -311,6 +311,96 @@ quasar_status quasar_w4a8_linear(const uint16_t* x, const float* s, const int8_t
  * unsupported); a diagnostic for the benchmark and profiles. */
 const char* quasar_w4a8_kernel_name(int64_t M, int64_t N, int64_t K);
 
+/* ---------------------------------------------------------------------------
+ * Decoder steps around the W8A8 linears, for a synthetic full verify step of a
+ * Qwen3-8B-shaped target model [Quasar, pt page §2 execution pipeline: the
+ * verifier runs the target model once over the drafted positions; zh page §2].
+ * They are not part of the quantized linear and not what the method changes;
+ * they put every dependency between the linears in place, so that the
+ * linears' share of a whole verify step can be measured.  Token m = b*T + i is
+ * position i of the T = 1 + k verify positions of sequence b; every sequence
+ * of a call sits at the same position pos0 (its cached context length).
+ * Arithmetic is binary32 with one rounding per operation; tensors leaving a
+ * call are BF16 except the residual stream h (float32).  Errors:
+ * INVALID_ARG for null pointers, misalignment or bad sizes, UNSUPPORTED for
+ * shapes outside the stated limits, HIP.
+ * --------------------------------------------------------------------------- */
+
+/*
+ * quasar_embed -- h[m, :] = float(table[tokens[m], :]); a token outside [0, V)
+ * gives a zero row.
+ *   tokens  [M] int32 (in)      table  [V, H] bf16 (in)      h  [M, H] f32 (out)
+ *   M >= 0, V >= 1, 1 <= H <= 65536
+ */
+quasar_status quasar_embed(const int32_t* tokens, const uint16_t* table, int64_t M, int64_t V,
+                           int64_t H, float* h, void* stream);
+
+/*
+ * quasar_rmsnorm -- the residual add (when delta is not NULL) and RMSNorm:
+ *     h[m, j] = RN32(h[m, j] + float(delta[m, j]))
+ *     r_m     = RN32(1 / RN32(sqrt(RN32(sum_j h[m, j]^2 / H) + eps)))  (binary32 sum)
+ *     out     = BF16(RN32(RN32(h[m, j] * r_m) * gamma[j]))
+ *   h      [M, H] f32 (in/out)   delta [M, H] bf16 or NULL (in)
+ *   gamma  [H] f32 (in)          out   [M, H] bf16 (out)
+ *   M >= 0, 1 <= H <= 65536, eps > 0 and finite
+ */
+quasar_status quasar_rmsnorm(float* h, const uint16_t* delta, const float* gamma, int64_t M,
+                             int64_t H, float eps, uint16_t* out, void* stream);
+
+/*
+ * quasar_qk_rope_cache -- after the QKV linear: per-head RMSNorm of q and k
+ * (as quasar_rmsnorm over the D values of a head, weights q_gamma / k_gamma),
+ * rotate-half rotary embedding of q and k at position pos0 + i (the pair
+ * (j, j + D/2) turns by (pos0 + i) * rope_base^(-2j / D) radians; the angle
+ * and its reduction to [0, 2 pi) are computed in binary64, its sine and
+ * cosine in binary32), then k and v written into the caches at that position
+ * and q into q_out.
+ *   qkv      [B*T, (Hq + 2 Hkv) D] bf16: q heads, then k heads, then v heads (in)
+ *   q_gamma, k_gamma  [D] f32 (in)
+ *   q_out    [B*T, Hq D] bf16 (out)
+ *   k_cache, v_cache  [B, Hkv, Lmax, D] bf16 (in/out: positions pos0 .. pos0+T-1
+ *            written)
+ *   D == 128, Hq % Hkv == 0, 0 <= pos0, pos0 + T <= Lmax, rope_base > 1
+ */
+quasar_status quasar_qk_rope_cache(const uint16_t* qkv, const float* q_gamma,
+                                   const float* k_gamma, int64_t B, int64_t T, int64_t Hq,
+                                   int64_t Hkv, int64_t D, int64_t pos0, int64_t Lmax,
+                                   float rope_base, float eps, uint16_t* q_out,
+                                   uint16_t* k_cache, uint16_t* v_cache, void* stream);
+
+/* Workspace bytes of quasar_attention (0 for invalid sizes). */
+size_t quasar_attention_workspace_bytes(int64_t B, int64_t T, int64_t Hq, int64_t pos0);
+
+/*
+ * quasar_attention -- causal grouped-query attention of the verify positions
+ * over the cache: query i of sequence b, head h, sees cached positions
+ * 0 .. pos0 + i of KV head h / (Hq / Hkv);
+ *     out = BF16(sum_t softmax_t(RN32(q . k_t) / sqrt(D)) v_t)
+ * in binary32, the softmax split into 64-position chunks merged by their
+ * maxima (the result differs from one pass by rounding only).
+ *   q        [B*T, Hq D] bf16 from quasar_qk_rope_cache (in)
+ *   k_cache, v_cache  as above, positions 0 .. pos0+T-1 filled (in)
+ *   out      [B*T, Hq D] bf16 (out)
+ *   workspace  quasar_attention_workspace_bytes(B, T, Hq, pos0) bytes,
+ *            256-byte aligned
+ *   D == 128, Hq % Hkv == 0, (Hq / Hkv) * T <= 64, pos0 + T <= Lmax
+ */
+quasar_status quasar_attention(const uint16_t* q, const uint16_t* k_cache,
+                               const uint16_t* v_cache, int64_t B, int64_t T, int64_t Hq,
+                               int64_t Hkv, int64_t D, int64_t pos0, int64_t Lmax, uint16_t* out,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * quasar_silu_mul -- the MLP activation between gate_up and down:
+ *     out[m, j] = BF16(RN32(RN32(g / RN32(1 + RN32(exp(-g)))) * u)),
+ *     g = gate_up[m, j], u = gate_up[m, I + j]
+ *   gate_up  [M, 2I] bf16: the gate half, then the up half (in)
+ *   out      [M, I] bf16 (out)
+ *   M >= 0, I >= 1
+ */
+quasar_status quasar_silu_mul(const uint16_t* gate_up, int64_t M, int64_t I, uint16_t* out,
+                              void* stream);
+
 /*
  * quasar_stream_copy -- diagnostic, not part of the method: copies `bytes`
  * bytes from src to dst (device pointers, 16-byte aligned, bytes a multiple of

@@ -52,6 +52,14 @@ _SIGNATURES = {
     "quasar_w4a8_linear": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P]),
     "quasar_w4a8_kernel_name": (ctypes.c_char_p, [_I64, _I64, _I64]),
     "quasar_stream_copy": (ctypes.c_int, [_P, _P, _SZ, _P]),
+    "quasar_embed": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _P, _P]),
+    "quasar_rmsnorm": (ctypes.c_int, [_P, _P, _P, _I64, _I64, ctypes.c_float, _P, _P]),
+    "quasar_qk_rope_cache": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
+                                            ctypes.c_float, ctypes.c_float, _P, _P, _P, _P]),
+    "quasar_attention_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64]),
+    "quasar_attention": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64, _P,
+                                        _P, _SZ, _P]),
+    "quasar_silu_mul": (ctypes.c_int, [_P, _I64, _I64, _P, _P]),
 }
 
 
@@ -215,8 +223,10 @@ def quasar_verify_accept(logits: torch.Tensor, draft: torch.Tensor | None, tempe
     if uniforms is not None:
         _need(uniforms, torch.float32, (B, kp1), "uniforms")
     dev = logits.device
-    acc_len = torch.empty((B,), dtype=torch.int32, device=dev)
-    nxt = torch.empty((B,), dtype=torch.int32, device=dev)
+    acc_len = torch.empty((B,), dtype=torch.int32, device=dev) if accept_len is None else accept_len
+    nxt = torch.empty((B,), dtype=torch.int32, device=dev) if next_token is None else next_token
+    _need(acc_len, torch.int32, (B,), "accept_len")
+    _need(nxt, torch.int32, (B,), "next_token")
     g = torch.empty((B, kp1), dtype=torch.int32, device=dev) if want_argmax else None
     pd = torch.empty((B, k), dtype=torch.float32, device=dev) if want_p_draft else None
     if workspace is None:
@@ -237,7 +247,9 @@ def quasar_lm_head_verify(x: torch.Tensor, s: torch.Tensor, wq: PackedWeights,
                           temperature: float = 0.0, uniforms: torch.Tensor | None = None,
                           want_argmax: bool = False, want_p_draft: bool = False,
                           logits: torch.Tensor | None = None,
-                          workspace: torch.Tensor | None = None):
+                          workspace: torch.Tensor | None = None,
+                          accept_len: torch.Tensor | None = None,
+                          next_token: torch.Tensor | None = None):
     """LM head over x [B*(k+1), K] bf16, then the accept step on its logits ->
     (logits [B, k+1, V] bf16, accept_len [B], next_token [B], argmax or None,
     p_draft or None)."""
@@ -260,8 +272,10 @@ def quasar_lm_head_verify(x: torch.Tensor, s: torch.Tensor, wq: PackedWeights,
     if logits is None:
         logits = torch.empty((B, kp1, V), dtype=torch.bfloat16, device=dev)
     _need(logits, torch.bfloat16, (B, kp1, V), "logits")
-    acc_len = torch.empty((B,), dtype=torch.int32, device=dev)
-    nxt = torch.empty((B,), dtype=torch.int32, device=dev)
+    acc_len = torch.empty((B,), dtype=torch.int32, device=dev) if accept_len is None else accept_len
+    nxt = torch.empty((B,), dtype=torch.int32, device=dev) if next_token is None else next_token
+    _need(acc_len, torch.int32, (B,), "accept_len")
+    _need(nxt, torch.int32, (B,), "next_token")
     g = torch.empty((B, kp1), dtype=torch.int32, device=dev) if want_argmax else None
     pd = torch.empty((B, k), dtype=torch.float32, device=dev) if want_p_draft else None
     if workspace is None:
@@ -315,4 +329,101 @@ def quasar_w4a8_linear(x: torch.Tensor, s: torch.Tensor, wq: PackedWeights, w_sc
         _need(acc_out, torch.int32, (M, N), "acc_out")
     _check("quasar_w4a8_linear", lib().quasar_w4a8_linear(
         _ptr(x), _ptr(s), _ptr(wq), _ptr(w_scale), M, N, K, _ptr(out), _ptr(acc_out), _stream()))
+    return out
+
+
+# ------------------------------------------------- decoder steps around the linears
+def quasar_embed(tokens: torch.Tensor, table: torch.Tensor, out: torch.Tensor | None = None):
+    """tokens int32 [M], table bf16 [V, H] -> h f32 [M, H]."""
+    M = tokens.numel()
+    V, H = table.shape
+    _need(tokens, torch.int32, (M,), "tokens")
+    _need(table, torch.bfloat16, (V, H), "table")
+    if out is None:
+        out = torch.empty((M, H), dtype=torch.float32, device=table.device)
+    _need(out, torch.float32, (M, H), "out")
+    _check("quasar_embed", lib().quasar_embed(_ptr(tokens), _ptr(table), M, V, H, _ptr(out),
+                                              _stream()))
+    return out
+
+
+def quasar_rmsnorm(h: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6,
+                   delta: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """h f32 [M, H] (updated in place by += delta when given) -> bf16 [M, H]."""
+    M, H = h.shape
+    _need(h, torch.float32, (M, H), "h")
+    _need(gamma, torch.float32, (H,), "gamma")
+    if delta is not None:
+        _need(delta, torch.bfloat16, (M, H), "delta")
+    if out is None:
+        out = torch.empty((M, H), dtype=torch.bfloat16, device=h.device)
+    _need(out, torch.bfloat16, (M, H), "out")
+    _check("quasar_rmsnorm", lib().quasar_rmsnorm(_ptr(h), _ptr(delta), _ptr(gamma), M, H, eps,
+                                                  _ptr(out), _stream()))
+    return out
+
+
+def quasar_qk_rope_cache(qkv: torch.Tensor, q_gamma: torch.Tensor, k_gamma: torch.Tensor,
+                         k_cache: torch.Tensor, v_cache: torch.Tensor, B: int, Hq: int, pos0: int,
+                         rope_base: float = 1e6, eps: float = 1e-6,
+                         q_out: torch.Tensor | None = None):
+    """qkv bf16 [B*T, (Hq + 2 Hkv) D]; caches bf16 [B, Hkv, Lmax, D] -> q bf16 [B*T, Hq D]."""
+    Bc, Hkv, Lmax, D = k_cache.shape
+    M = qkv.shape[0]
+    T = M // max(B, 1)
+    if Bc != B or T * B != M:
+        raise ValueError("qkv rows must be B*T and the caches' first dimension B")
+    _need(qkv, torch.bfloat16, (M, (Hq + 2 * Hkv) * D), "qkv")
+    _need(q_gamma, torch.float32, (D,), "q_gamma")
+    _need(k_gamma, torch.float32, (D,), "k_gamma")
+    _need(k_cache, torch.bfloat16, (B, Hkv, Lmax, D), "k_cache")
+    _need(v_cache, torch.bfloat16, (B, Hkv, Lmax, D), "v_cache")
+    if q_out is None:
+        q_out = torch.empty((M, Hq * D), dtype=torch.bfloat16, device=qkv.device)
+    _need(q_out, torch.bfloat16, (M, Hq * D), "q_out")
+    _check("quasar_qk_rope_cache", lib().quasar_qk_rope_cache(
+        _ptr(qkv), _ptr(q_gamma), _ptr(k_gamma), B, T, Hq, Hkv, D, pos0, Lmax, rope_base, eps,
+        _ptr(q_out), _ptr(k_cache), _ptr(v_cache), _stream()))
+    return q_out
+
+
+def workspace_bytes_attention(B: int, T: int, Hq: int, pos0: int) -> int:
+    return int(lib().quasar_attention_workspace_bytes(B, T, Hq, pos0))
+
+
+def quasar_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, Hq: int,
+                     pos0: int, out: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None):
+    """q bf16 [B*T, Hq D], caches bf16 [B, Hkv, Lmax, D] -> bf16 [B*T, Hq D]."""
+    B, Hkv, Lmax, D = k_cache.shape
+    M = q.shape[0]
+    T = M // max(B, 1)
+    if T * B != M:
+        raise ValueError("q rows must be B*T")
+    _need(q, torch.bfloat16, (M, Hq * D), "q")
+    _need(k_cache, torch.bfloat16, (B, Hkv, Lmax, D), "k_cache")
+    _need(v_cache, torch.bfloat16, (B, Hkv, Lmax, D), "v_cache")
+    if out is None:
+        out = torch.empty((M, Hq * D), dtype=torch.bfloat16, device=q.device)
+    _need(out, torch.bfloat16, (M, Hq * D), "out")
+    need = workspace_bytes_attention(B, T, Hq, pos0)
+    if workspace is None:
+        workspace = new_workspace(need, q.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("quasar_attention", lib().quasar_attention(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), B, T, Hq, Hkv, D, pos0, Lmax, _ptr(out),
+        _ptr(workspace), nbytes, _stream()))
+    return out
+
+
+def quasar_silu_mul(gate_up: torch.Tensor, out: torch.Tensor | None = None):
+    """gate_up bf16 [M, 2I] -> bf16 [M, I] = silu(gate) * up."""
+    M, I2 = gate_up.shape
+    if I2 % 2:
+        raise ValueError("gate_up must have an even number of columns")
+    _need(gate_up, torch.bfloat16, (M, I2), "gate_up")
+    if out is None:
+        out = torch.empty((M, I2 // 2), dtype=torch.bfloat16, device=gate_up.device)
+    _need(out, torch.bfloat16, (M, I2 // 2), "out")
+    _check("quasar_silu_mul", lib().quasar_silu_mul(_ptr(gate_up), M, I2 // 2, _ptr(out), _stream()))
     return out

@@ -85,7 +85,7 @@ const char* quasar_status_string(quasar_status status) {
   return "QUASAR_ERR_UNKNOWN";
 }
 
-int quasar_abi_version(void) { return 6; }
+int quasar_abi_version(void) { return 7; }
 
 quasar_status quasar_quantize_weights(const uint16_t* w, const float* s, int64_t N, int64_t K,
                                       int8_t* wq, float* w_scale, void* stream) {
@@ -292,6 +292,92 @@ quasar_status quasar_lm_head_verify(const uint16_t* x, const float* s, const int
   return hip_status(launch_accept_finalize(p.ap, logits, draft, temperature, uniforms, accept_len,
                                            next_token, argmax_out, p_draft_out, pmax, pidx, psum,
                                            hs));
+}
+
+// ---------------------------------------------------------------------------
+// Decoder steps around the linears.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int64_t kMaxHidden = 65536;
+constexpr int64_t kMaxGridY = 65535;
+}  // namespace
+
+quasar_status quasar_embed(const int32_t* tokens, const uint16_t* table, int64_t M, int64_t V,
+                           int64_t H, float* h, void* stream) {
+  if (M < 0 || V <= 0 || H <= 0) return QUASAR_ERR_INVALID_ARG;
+  if (H > kMaxHidden || M > kMaxRowsPerCall || V > kMaxRowsPerCall) return QUASAR_ERR_UNSUPPORTED;
+  if (M == 0) return QUASAR_OK;
+  if (!tokens || !table || !h || !aligned(tokens, 4) || !aligned(table, 2) || !aligned(h, 4))
+    return QUASAR_ERR_INVALID_ARG;
+  return hip_status(launch_embed(tokens, table, M, V, H, h, (hipStream_t)stream));
+}
+
+quasar_status quasar_rmsnorm(float* h, const uint16_t* delta, const float* gamma, int64_t M,
+                             int64_t H, float eps, uint16_t* out, void* stream) {
+  if (M < 0 || H <= 0 || !(eps > 0.0f) || isinf(eps)) return QUASAR_ERR_INVALID_ARG;
+  if (H > kMaxHidden || M > kMaxRowsPerCall) return QUASAR_ERR_UNSUPPORTED;
+  if (M == 0) return QUASAR_OK;
+  if (!h || !gamma || !out || !aligned(h, 4) || !aligned(gamma, 4) || !aligned(out, 2) ||
+      (delta && !aligned(delta, 2)))
+    return QUASAR_ERR_INVALID_ARG;
+  return hip_status(launch_rmsnorm(h, delta, gamma, M, H, eps, out, (hipStream_t)stream));
+}
+
+quasar_status quasar_qk_rope_cache(const uint16_t* qkv, const float* q_gamma,
+                                   const float* k_gamma, int64_t B, int64_t T, int64_t Hq,
+                                   int64_t Hkv, int64_t D, int64_t pos0, int64_t Lmax,
+                                   float rope_base, float eps, uint16_t* q_out,
+                                   uint16_t* k_cache, uint16_t* v_cache, void* stream) {
+  if (B < 0 || T <= 0 || Hq <= 0 || Hkv <= 0 || pos0 < 0 || Lmax <= 0 || !(eps > 0.0f) ||
+      isinf(eps) || !(rope_base > 1.0f) || isinf(rope_base))
+    return QUASAR_ERR_INVALID_ARG;
+  if (D != 128 || Hq % Hkv != 0 || pos0 + T > Lmax) return QUASAR_ERR_UNSUPPORTED;
+  if (B * T > kMaxRowsPerCall || Hq + 2 * Hkv > kMaxGridY || Lmax > kMaxRowsPerCall)
+    return QUASAR_ERR_UNSUPPORTED;
+  if (B == 0) return QUASAR_OK;
+  if (!qkv || !q_gamma || !k_gamma || !q_out || !k_cache || !v_cache || !aligned(qkv, 2) ||
+      !aligned(q_gamma, 4) || !aligned(k_gamma, 4) || !aligned(q_out, 2) || !aligned(k_cache, 2) ||
+      !aligned(v_cache, 2))
+    return QUASAR_ERR_INVALID_ARG;
+  return hip_status(launch_qk_rope_cache(qkv, q_gamma, k_gamma, B, T, Hq, Hkv, D, pos0, Lmax,
+                                         log2((double)rope_base), eps, q_out, k_cache, v_cache,
+                                         (hipStream_t)stream));
+}
+
+size_t quasar_attention_workspace_bytes(int64_t B, int64_t T, int64_t Hq, int64_t pos0) {
+  if (B <= 0 || T <= 0 || Hq <= 0 || pos0 < 0 || B * T > kMaxRowsPerCall ||
+      pos0 > kMaxRowsPerCall)
+    return 0;
+  return attn_workspace_bytes(B, T, Hq, pos0);
+}
+
+quasar_status quasar_attention(const uint16_t* q, const uint16_t* k_cache,
+                               const uint16_t* v_cache, int64_t B, int64_t T, int64_t Hq,
+                               int64_t Hkv, int64_t D, int64_t pos0, int64_t Lmax, uint16_t* out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || T <= 0 || Hq <= 0 || Hkv <= 0 || pos0 < 0 || Lmax <= 0)
+    return QUASAR_ERR_INVALID_ARG;
+  if (!attn_supported(Hq, Hkv, D, T) || pos0 + T > Lmax || B > kMaxGridY ||
+      Hq > kMaxGridY || B * T > kMaxRowsPerCall || Lmax > kMaxRowsPerCall)
+    return QUASAR_ERR_UNSUPPORTED;
+  if (B == 0) return QUASAR_OK;
+  if (!q || !k_cache || !v_cache || !out || !aligned(q, 2) || !aligned(k_cache, 2) ||
+      !aligned(v_cache, 2) || !aligned(out, 2))
+    return QUASAR_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < attn_workspace_bytes(B, T, Hq, pos0) ||
+      !aligned(workspace, kWsAlign))
+    return QUASAR_ERR_WORKSPACE;
+  return hip_status(launch_attention(q, k_cache, v_cache, B, T, Hq, Hkv, pos0, Lmax, out,
+                                     workspace, (hipStream_t)stream));
+}
+
+quasar_status quasar_silu_mul(const uint16_t* gate_up, int64_t M, int64_t I, uint16_t* out,
+                              void* stream) {
+  if (M < 0 || I <= 0) return QUASAR_ERR_INVALID_ARG;
+  if (M > kMaxGridY || I > kMaxRowsPerCall) return QUASAR_ERR_UNSUPPORTED;
+  if (M == 0) return QUASAR_OK;
+  if (!gate_up || !out || !aligned(gate_up, 2) || !aligned(out, 2)) return QUASAR_ERR_INVALID_ARG;
+  return hip_status(launch_silu_mul(gate_up, M, I, out, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -139,6 +139,24 @@ hipError_t launch_accept_finalize(const AcceptPlan& p, const uint16_t* logits,
                                   float* p_draft_out, const float* pmax, const int32_t* pidx,
                                   const float* psum, hipStream_t st);
 
+// Decoder steps around the linears (decoder.hip).
+int attn_chunks(int64_t pos0, int64_t T);
+size_t attn_workspace_bytes(int64_t B, int64_t T, int64_t Hq, int64_t pos0);
+bool attn_supported(int64_t Hq, int64_t Hkv, int64_t D, int64_t T);
+hipError_t launch_embed(const int32_t* tok, const uint16_t* table, int64_t M, int64_t V, int64_t H,
+                        float* h, hipStream_t st);
+hipError_t launch_rmsnorm(float* h, const uint16_t* delta, const float* gamma, int64_t M, int64_t H,
+                          float eps, uint16_t* out, hipStream_t st);
+hipError_t launch_qk_rope_cache(const uint16_t* qkv, const float* q_gamma, const float* k_gamma,
+                                int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D,
+                                int64_t pos0, int64_t Lmax, double log2_base, float eps,
+                                uint16_t* q_out, uint16_t* k_cache, uint16_t* v_cache,
+                                hipStream_t st);
+hipError_t launch_attention(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                            int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t pos0, int64_t Lmax,
+                            uint16_t* out, void* workspace, hipStream_t st);
+hipError_t launch_silu_mul(const uint16_t* gu, int64_t M, int64_t I, uint16_t* out, hipStream_t st);
+
 // Diagnostic plain copy (16-byte vectors), bytes % 16 == 0.
 hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
 
