@@ -61,6 +61,10 @@ def parse():
     ap.add_argument("--layers", type=int, default=36)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true", help="skip the BF16-weight comparator")
+    ap.add_argument("--no-decoder", action="store_true",
+                    help="skip the whole-decoder verify step (norms, attention, SiLU around the linears)")
+    ap.add_argument("--context", type=int, default=2048,
+                    help="cached context length of the whole-decoder verify step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     ap.add_argument("--tau-sets", type=int, default=2048,
                     help="seeded draft sets for the mean accepted length")
@@ -258,6 +262,87 @@ def time_graph_steps(stack, drafts, warmup: int, steps: int, step=None, uniforms
         raise RuntimeError(f"step time disagrees between host clock ({ms:.4f} ms) and "
                            f"HIP events ({ms_events:.4f} ms)")
     return ms, ms_events, tau, graph
+
+
+def time_decoder_step(stack, args, linear_graph_ms: float):
+    """A whole Qwen3-8B-shaped decoder verify step around the same W8A8
+    linears (w8a8_quantized_speculative_amd/decoder.py): embedding, per layer
+    RMSNorm -> QKV -> q/k norm + RoPE + KV append -> attention over a cached
+    context -> O -> residual + RMSNorm -> gate_up -> SiLU * up -> down ->
+    residual, then the final RMSNorm and the LM head with greedy accept.
+    Drafts come from the N-gram drafter on synthetic histories.  Captured in
+    a HIP graph and replayed (about 365 launches per step; issued from Python
+    one by one the host would not keep up)."""
+    import numpy as np
+    import torch
+    from dataclasses import replace
+    from w8a8_quantized_speculative_amd.decoder import (QWEN3_8B, DecoderStep, Linear,
+                                                         ngram_history, random_norms)
+    from w8a8_quantized_speculative_amd.drafter import ngram_draft
+    cfg = replace(QWEN3_8B, layers=args.layers)
+    layers = []
+    for e in stack.linears[:-1]:
+        if e["name"] == "qkv":
+            layers.append({})
+        layers[-1][e["name"]] = Linear(e["wq"], e["sw"], e["s"], e["N"], e["K"])
+    lm = stack.linears[-1]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(12345)
+    table = torch.randn((cfg.vocab, cfg.hidden), generator=g, device="cuda").to(torch.bfloat16)
+    step = DecoderStep(cfg, layers, Linear(lm["wq"], lm["sw"], lm["s"], lm["N"], lm["K"]), table,
+                       random_norms(cfg, "cuda"), stack.B, stack.k, args.context)
+    step.fill_context(seed=1)
+    hist = [ngram_history(max(args.context, 16), cfg.vocab, seed=b) for b in range(stack.B)]
+    d0 = time.perf_counter()
+    drafts = [ngram_draft(h, stack.k) for h in hist]
+    draft_us = (time.perf_counter() - d0) * 1e6 / stack.B
+    tokens = np.concatenate([np.concatenate([h[-1:], d]) for h, d in zip(hist, drafts)])
+    step.tokens.copy_(torch.from_numpy(tokens.astype(np.int32)).cuda())
+    step.draft.copy_(torch.from_numpy(np.stack(drafts).astype(np.int32)).cuda())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step.run()  # prime once outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step.run()
+    for _ in range(args.warmup):
+        graph.replay()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - w0) * 1e3 / args.steps
+    ms_ev = t0.elapsed_time(t1) / args.steps
+    step.logits.zero_()
+    graph.replay()
+    torch.cuda.synchronize()
+    if not bool((step.logits != 0).any()):
+        raise RuntimeError("the captured decoder step did not recompute its logits on replay")
+    if abs(ms - ms_ev) > 0.1 * ms:
+        raise RuntimeError(f"decoder step time disagrees: host {ms:.4f} ms, events {ms_ev:.4f} ms")
+    kv_bytes = 2 * cfg.layers * stack.B * cfg.heads_kv * (args.context + stack.k + 1) * cfg.head_dim * 2
+    del graph
+    return {
+        "what": "whole Qwen3-8B-shaped decoder verify step around the same W8A8 linears: "
+                "embedding, RMSNorm, q/k norm + RoPE + KV append, GQA attention over the cached "
+                "context, residual adds, SiLU*up, final RMSNorm, LM head + greedy accept; "
+                "random weights, N-gram drafts; HIP graph replay",
+        "context": args.context,
+        "ms_per_step": round(ms, 4),
+        "ms_per_step_events": round(ms_ev, 4),
+        "linear_stack_ms_per_step": round(linear_graph_ms, 4),
+        "linear_share": round(linear_graph_ms / ms, 4),
+        "kv_cache_read_gb": round(kv_bytes / 1e9, 4),
+        "drafter_us_per_sequence": round(draft_us, 1),
+    }
 
 
 def measure_tau(stack, n_sets: int):
@@ -665,6 +750,9 @@ def main():
             "mean_tau": round(tau4, 4),
             "speedup_vs_w8a8": round(ms / ms4, 3),
         }
+    if not args.no_decoder:
+        print("[bench] whole-decoder verify step", file=sys.stderr, flush=True)
+        out["decoder_step"] = time_decoder_step(stack, args, graph_ms)
     if not args.no_cpu_baseline:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_oracle_baseline(args.m, args.cpu_seconds)

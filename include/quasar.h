@@ -340,8 +340,10 @@ quasar_status quasar_embed(const int32_t* tokens, const uint16_t* table, int64_t
  *     h[m, j] = RN32(h[m, j] + float(delta[m, j]))
  *     r_m     = RN32(1 / RN32(sqrt(RN32(sum_j h[m, j]^2 / H) + eps)))  (binary32 sum)
  *     out     = BF16(RN32(RN32(h[m, j] * r_m) * gamma[j]))
- *   h      [M, H] f32 (in/out)   delta [M, H] bf16 or NULL (in)
- *   gamma  [H] f32 (in)          out   [M, H] bf16 (out)
+ *   h      [M, H] f32, 16-byte aligned (in/out)
+ *   delta  [M, H] bf16, 8-byte aligned, or NULL (in)
+ *   gamma  [H] f32, 16-byte aligned (in)
+ *   out    [M, H] bf16, 8-byte aligned (out)
  *   M >= 0, 1 <= H <= 65536, eps > 0 and finite
  */
 quasar_status quasar_rmsnorm(float* h, const uint16_t* delta, const float* gamma, int64_t M,
@@ -378,8 +380,9 @@ size_t quasar_attention_workspace_bytes(int64_t B, int64_t T, int64_t Hq, int64_
  *     out = BF16(sum_t softmax_t(RN32(q . k_t) / sqrt(D)) v_t)
  * in binary32, the softmax split into 64-position chunks merged by their
  * maxima (the result differs from one pass by rounding only).
- *   q        [B*T, Hq D] bf16 from quasar_qk_rope_cache (in)
- *   k_cache, v_cache  as above, positions 0 .. pos0+T-1 filled (in)
+ *   q        [B*T, Hq D] bf16 from quasar_qk_rope_cache, 16-byte aligned (in)
+ *   k_cache, v_cache  as above, positions 0 .. pos0+T-1 filled, 16-byte
+ *            aligned (in)
  *   out      [B*T, Hq D] bf16 (out)
  *   workspace  quasar_attention_workspace_bytes(B, T, Hq, pos0) bytes,
  *            256-byte aligned

@@ -317,8 +317,8 @@ quasar_status quasar_rmsnorm(float* h, const uint16_t* delta, const float* gamma
   if (M < 0 || H <= 0 || !(eps > 0.0f) || isinf(eps)) return QUASAR_ERR_INVALID_ARG;
   if (H > kMaxHidden || M > kMaxRowsPerCall) return QUASAR_ERR_UNSUPPORTED;
   if (M == 0) return QUASAR_OK;
-  if (!h || !gamma || !out || !aligned(h, 4) || !aligned(gamma, 4) || !aligned(out, 2) ||
-      (delta && !aligned(delta, 2)))
+  if (!h || !gamma || !out || !aligned(h, 16) || !aligned(gamma, 16) || !aligned(out, 8) ||
+      (delta && !aligned(delta, 8)))
     return QUASAR_ERR_INVALID_ARG;
   return hip_status(launch_rmsnorm(h, delta, gamma, M, H, eps, out, (hipStream_t)stream));
 }
@@ -361,8 +361,8 @@ quasar_status quasar_attention(const uint16_t* q, const uint16_t* k_cache,
       Hq > kMaxGridY || B * T > kMaxRowsPerCall || Lmax > kMaxRowsPerCall)
     return QUASAR_ERR_UNSUPPORTED;
   if (B == 0) return QUASAR_OK;
-  if (!q || !k_cache || !v_cache || !out || !aligned(q, 2) || !aligned(k_cache, 2) ||
-      !aligned(v_cache, 2) || !aligned(out, 2))
+  if (!q || !k_cache || !v_cache || !out || !aligned(q, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(out, 2))
     return QUASAR_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < attn_workspace_bytes(B, T, Hq, pos0) ||
       !aligned(workspace, kWsAlign))

@@ -53,29 +53,87 @@ __global__ __launch_bounds__(kNormThreads) void embed_kernel(const int32_t* __re
     h[(size_t)m * H + j] = ok ? bf16_to_f32(row[j]) : 0.0f;
 }
 
-// One block per row.  mean(h^2) is a binary32 sum of squares in a fixed
-// order per thread, then across the block.
+// One block per row.  mean(h^2) is a binary32 sum of squares, per thread in
+// index order, then across the block.  Rows of up to 16 values per thread
+// (H % 4 == 0) stay in registers between the two passes, loaded 4 at a time.
+constexpr int kNormPerThread = 16;
+
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(float* __restrict__ h,
                                                                const uint16_t* __restrict__ delta,
                                                                const float* __restrict__ gamma,
                                                                int H, float eps,
                                                                uint16_t* __restrict__ out) {
   __shared__ float red[kNormThreads / kWave];
-  const int m = blockIdx.x;
+  const int m = blockIdx.x, tid = threadIdx.x;
   float* hr = h + (size_t)m * H;
+  const uint16_t* dr = delta ? delta + (size_t)m * H : nullptr;
+  uint16_t* orow = out + (size_t)m * H;
+  if ((H & 3) == 0 && H <= kNormThreads * kNormPerThread) {
+    // 4 values per 16-byte load, every load of the row issued before the
+    // first use (the rows and gamma are 16-byte aligned, the BF16 rows 8)
+    constexpr int kVec = kNormPerThread / 4;
+    float4 v[kVec];
+#pragma unroll
+    for (int k = 0; k < kVec; ++k) {
+      const int j = (tid + k * kNormThreads) * 4;
+      const float4 x = *reinterpret_cast<const float4*>(hr + (j < H ? j : 0));
+      v[k] = j < H ? x : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+    if (dr) {
+      uint2 dv[kVec];
+#pragma unroll
+      for (int k = 0; k < kVec; ++k) {
+        const int j = (tid + k * kNormThreads) * 4;
+        dv[k] = *reinterpret_cast<const uint2*>(dr + (j < H ? j : 0));
+      }
+#pragma unroll
+      for (int k = 0; k < kVec; ++k) {
+        if ((tid + k * kNormThreads) * 4 < H) {
+          v[k].x = v[k].x + bf16_to_f32(dv[k].x & 0xffffu);
+          v[k].y = v[k].y + bf16_to_f32(dv[k].x >> 16);
+          v[k].z = v[k].z + bf16_to_f32(dv[k].y & 0xffffu);
+          v[k].w = v[k].w + bf16_to_f32(dv[k].y >> 16);
+        }
+      }
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kVec; ++k) {
+      ss = ss + v[k].x * v[k].x;
+      ss = ss + v[k].y * v[k].y;
+      ss = ss + v[k].z * v[k].z;
+      ss = ss + v[k].w * v[k].w;
+    }
+    const float tot = block_sum(ss, red);
+    const float r = 1.0f / sqrtf(tot / (float)H + eps);
+#pragma unroll
+    for (int k = 0; k < kVec; ++k) {
+      const int j = (tid + k * kNormThreads) * 4;
+      if (j < H) {
+        if (dr) *reinterpret_cast<float4*>(hr + j) = v[k];
+        const float4 gm = *reinterpret_cast<const float4*>(gamma + j);
+        uint2 o;
+        o.x = f32_to_bf16_rne(v[k].x * r * gm.x) | (f32_to_bf16_rne(v[k].y * r * gm.y) << 16);
+        o.y = f32_to_bf16_rne(v[k].z * r * gm.z) | (f32_to_bf16_rne(v[k].w * r * gm.w) << 16);
+        *reinterpret_cast<uint2*>(orow + j) = o;
+      }
+    }
+    return;
+  }
+  // wider rows: the residual add first, then the two passes over memory
   float ss = 0.0f;
-  for (int j = threadIdx.x; j < H; j += blockDim.x) {
+  for (int j = tid; j < H; j += kNormThreads) {
     float v = hr[j];
-    if (delta) {
-      v = v + bf16_to_f32(delta[(size_t)m * H + j]);
+    if (dr) {
+      v = v + bf16_to_f32(dr[j]);
       hr[j] = v;
     }
     ss = ss + v * v;
   }
   const float tot = block_sum(ss, red);
   const float r = 1.0f / sqrtf(tot / (float)H + eps);
-  for (int j = threadIdx.x; j < H; j += blockDim.x)
-    out[(size_t)m * H + j] = (uint16_t)f32_to_bf16_rne(hr[j] * r * gamma[j]);
+  for (int j = tid; j < H; j += kNormThreads)
+    orow[j] = (uint16_t)f32_to_bf16_rne(hr[j] * r * gamma[j]);
 }
 
 // One block of D threads per (token, head of q, k or v).  Token m = b T + i sits
@@ -126,10 +184,30 @@ __global__ void qk_rope_cache_kernel(const uint16_t* __restrict__ qkv, const flo
 // query rows of the group (row r = head-in-group * T + i) against cached
 // positions [64 c, 64 c + 64), causal: query i sees positions < pos0 + i + 1.
 // Scores are binary32 dot products in d order, scaled by 1/sqrt(D).
+//
+// Layout: the chunk's keys go to LDS transposed in BF16 pairs, kT2[d/2][t] =
+// (K[t][d], K[t][d+1]) (rows padded to 65 words against bank conflicts on the
+// transposing writes), so lane t of a wavefront reads two of key t's values
+// per 32-bit access; values stay row-major as pairs, vs2[t][d/2], and so do the
+// query rows, qs2[r][d/2], read as 4-byte broadcasts (a 16-byte binary32
+// broadcast moves four times the bytes through the LDS crossbar, and scalar
+// loads of the rows from memory were slower still).  Wavefront w of 8 owns
+// rows w, w + 8, ...: it
+// takes them four at a time through scores (lane = key), softmax (wavefront
+// reductions) and P V (lane = a pair of d), so after the one barrier no
+// wavefront waits for another.  The loops run over the whole chunk (keys
+// past the window carry p = 0 and zero values).
 constexpr int kAttnChunk = 64;
-constexpr int kAttnThreads = 256;
+constexpr int kAttnThreads = 512;
+constexpr int kAttnKTStride = kAttnChunk + 1;  // words per kT2 row
 constexpr int kAttnMaxRows = 64;  // (Hq / Hkv) * T
 constexpr int kAttnD = 128;
+constexpr int kAttnRowGroup = 4;
+
+__host__ __device__ constexpr int attn_lds_bytes(int R) {
+  return (kAttnD / 2) * kAttnKTStride * 4 + kAttnChunk * kAttnD * 2 + R * kAttnD * 2 +
+         R * kAttnChunk * 4;
+}
 
 __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
@@ -142,69 +220,115 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(
   const int klen = pos0 + T;  // keys after this step's append
   const int t0 = c * kAttnChunk;
   const int nt = min(kAttnChunk, klen - t0);
-  float* qs = reinterpret_cast<float*>(smem);          // [R][D]
-  float* ks = qs + kAttnMaxRows * kAttnD;              // [64][D + 1]
-  float* vs = ks + kAttnChunk * (kAttnD + 1);          // [64][D]
-  float* ps = vs + kAttnChunk * kAttnD;                // [R][64]
+  uint32_t* kT2 = reinterpret_cast<uint32_t*>(smem);                       // [D/2][65]
+  uint32_t* vs2 = kT2 + (kAttnD / 2) * kAttnKTStride;                      // [64][D/2]
+  uint32_t* qs2 = vs2 + kAttnChunk * (kAttnD / 2);                         // [R][D/2]
+  float* ps = reinterpret_cast<float*>(qs2 + R * (kAttnD / 2));             // [R][64]
   const int tid = threadIdx.x;
-  for (int e = tid; e < R * kAttnD; e += kAttnThreads) {
-    const int r = e / kAttnD, d = e - r * kAttnD;
-    const int hh = r / T, i = r - hh * T;
-    const int m = b * T + i, h = g * G + hh;
-    qs[e] = bf16_to_f32(q[((size_t)m * Hq + h) * kAttnD + d]);
-  }
+
+  // the chunk's keys and values (buffer resources: reads past its nt keys
+  // return zero, with no branch), 16 bytes = 8 values per load
   const size_t kv0 = (((size_t)b * Hkv + g) * Lmax + t0) * kAttnD;
-  for (int e = tid; e < nt * kAttnD; e += kAttnThreads) {
-    const int t = e / kAttnD, d = e - t * kAttnD;
-    ks[t * (kAttnD + 1) + d] = bf16_to_f32(k_cache[kv0 + e]);
-    vs[e] = bf16_to_f32(v_cache[kv0 + e]);
+  const buffer_rsrc krs = make_rsrc(k_cache + kv0, (uint32_t)nt * kAttnD * 2u);
+  const buffer_rsrc vrs = make_rsrc(v_cache + kv0, (uint32_t)nt * kAttnD * 2u);
+  const buffer_rsrc qrs = make_rsrc(q + (size_t)b * T * Hq * kAttnD, (uint32_t)(T * Hq * kAttnD * 2));
+  v4i kreg[2], vreg[2], qreg[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int u = tid + kAttnThreads * k;  // 1024 units of a 64 x 128 chunk
+    const int t = u >> 4, d0 = (u & 15) * 8;
+    kreg[k] = load16(krs, (t * kAttnD + d0) * 2);
+    vreg[k] = load16(vrs, (t * kAttnD + d0) * 2);
+    const int r = u >> 4;  // query row r (of R <= 64), 8 values at d0
+    const int hh = r / T, i = r - hh * T;
+    qreg[k] = load16(qrs, r < R ? ((i * Hq + g * G + hh) * kAttnD + d0) * 2 : kOutOfRange);
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int u = tid + kAttnThreads * k;
+    const int t = u >> 4, d0 = (u & 15) * 8;
+    kT2[(d0 / 2 + 0) * kAttnKTStride + t] = (uint32_t)kreg[k].x;
+    kT2[(d0 / 2 + 1) * kAttnKTStride + t] = (uint32_t)kreg[k].y;
+    kT2[(d0 / 2 + 2) * kAttnKTStride + t] = (uint32_t)kreg[k].z;
+    kT2[(d0 / 2 + 3) * kAttnKTStride + t] = (uint32_t)kreg[k].w;
+    *reinterpret_cast<v4i*>(vs2 + t * (kAttnD / 2) + d0 / 2) = vreg[k];
+    if (t < R) *reinterpret_cast<v4i*>(qs2 + t * (kAttnD / 2) + d0 / 2) = qreg[k];
   }
   __syncthreads();
-  // scores: thread pairs (row, key)
-  for (int e = tid; e < R * kAttnChunk; e += kAttnThreads) {
-    const int r = e / kAttnChunk, t = e - r * kAttnChunk;
-    const int i = r % T;
-    float sc = -INFINITY;
-    if (t < nt && t0 + t <= pos0 + i) {
-      float acc = 0.0f;
-      const float* qr = qs + r * kAttnD;
-      const float* kr = ks + t * (kAttnD + 1);
-      for (int d = 0; d < kAttnD; ++d) acc = acc + qr[d] * kr[d];
-      sc = acc * scale;
+
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  for (int r0 = wave; r0 < R; r0 += kAttnRowGroup * (kAttnThreads / kWave)) {
+    // rows past R are computed on row R - 1 and dropped: no branch inside the
+    // loops, so the scheduler can issue LDS reads iterations ahead
+    int rows[kAttnRowGroup], rc[kAttnRowGroup];
+#pragma unroll
+    for (int j = 0; j < kAttnRowGroup; ++j) {
+      rows[j] = r0 + j * (kAttnThreads / kWave);
+      rc[j] = rows[j] < R ? rows[j] : R - 1;
     }
-    ps[e] = sc;
-  }
-  __syncthreads();
-  // per row: max, exp, sum (one wavefront per row, rows round-robin)
-  const int wave = tid / kWave, lane = tid % kWave;
-  for (int r = wave; r < R; r += kAttnThreads / kWave) {
-    float* pr = ps + r * kAttnChunk;
-    float mx = -INFINITY;
-    for (int t = lane; t < kAttnChunk; t += kWave) mx = fmaxf(mx, pr[t]);
-    mx = wave_max(mx);
-    float sum = 0.0f;
-    for (int t = lane; t < kAttnChunk; t += kWave) {
-      const float p = mx == -INFINITY ? 0.0f : expf(pr[t] - mx);
-      pr[t] = p;
-      sum = sum + p;
+    // scores: lane = key
+    float acc[kAttnRowGroup] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
+    for (int dp = 0; dp < kAttnD / 2; ++dp) {
+      const uint32_t kw = kT2[dp * kAttnKTStride + lane];
+      const float k0 = bf16_to_f32(kw & 0xffffu), k1 = bf16_to_f32(kw >> 16);
+#pragma unroll
+      for (int j = 0; j < kAttnRowGroup; ++j) {
+        const uint32_t qw = qs2[rc[j] * (kAttnD / 2) + dp];
+        acc[j] = acc[j] + bf16_to_f32(qw & 0xffffu) * k0;
+        acc[j] = acc[j] + bf16_to_f32(qw >> 16) * k1;
+      }
+    }
+    // softmax pieces of each row
+#pragma unroll
+    for (int j = 0; j < kAttnRowGroup; ++j) {
+      const int r = rows[j];
+      if (r >= R) continue;
+      const int i = r % T;
+      const bool valid = lane < nt && t0 + lane <= pos0 + i;
+      const float sc = valid ? acc[j] * scale : -INFINITY;
+      const float mx = wave_max(sc);
+      const float p = mx == -INFINITY ? 0.0f : expf(sc - mx);
+      float sum = p;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, kWave);
+      ps[r * kAttnChunk + lane] = p;
+      if (lane == 0) {
+        const size_t pi = (((size_t)b * Hq + g * G + r / T) * T + i) * nchunks + c;
+        pm[pi] = mx;
+        pl[pi] = sum;
+      }
+    }
+    // this wavefront's own p rows are read back below: LDS executes a
+    // wavefront's accesses in order; keep the compiler from reordering
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // P V: lane = d pair (2 lane, 2 lane + 1), keys in order, 4 per step
+    float o[kAttnRowGroup][2] = {};
+#pragma unroll 4
+    for (int t = 0; t < kAttnChunk; t += 4) {
+      uint32_t vw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vw[e] = vs2[(t + e) * (kAttnD / 2) + lane];
+#pragma unroll
+      for (int j = 0; j < kAttnRowGroup; ++j) {
+        const float4 p4 = *reinterpret_cast<const float4*>(ps + rc[j] * kAttnChunk + t);
+        const float pe[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[j][0] = o[j][0] + pe[e] * bf16_to_f32(vw[e] & 0xffffu);
+          o[j][1] = o[j][1] + pe[e] * bf16_to_f32(vw[e] >> 16);
+        }
+      }
     }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, kWave);
-    if (lane == 0) {
+    for (int j = 0; j < kAttnRowGroup; ++j) {
+      const int r = rows[j];
+      if (r >= R) continue;
       const size_t pi = (((size_t)b * Hq + g * G + r / T) * T + r % T) * nchunks + c;
-      pm[pi] = mx;
-      pl[pi] = sum;
+      *reinterpret_cast<float2*>(po + pi * kAttnD + 2 * lane) = make_float2(o[j][0], o[j][1]);
     }
-  }
-  __syncthreads();
-  // unnormalised outputs: thread pairs (row, d), keys in order
-  for (int e = tid; e < R * kAttnD; e += kAttnThreads) {
-    const int r = e / kAttnD, d = e - r * kAttnD;
-    const float* pr = ps + r * kAttnChunk;
-    float acc = 0.0f;
-    for (int t = 0; t < nt; ++t) acc = acc + pr[t] * vs[t * kAttnD + d];
-    const size_t pi = (((size_t)b * Hq + g * G + r / T) * T + r % T) * nchunks + c;
-    po[pi * kAttnD + d] = acc;
   }
 }
 
@@ -216,12 +340,13 @@ __global__ void attn_combine_kernel(const float* __restrict__ pm, const float* _
   const int b = m / T, i = m - b * T;
   const size_t base = (((size_t)b * Hq + h) * T + i) * nchunks;
   float mx = -INFINITY;
+#pragma unroll 8
   for (int c = 0; c < nchunks; ++c) mx = fmaxf(mx, pm[base + c]);
   float l = 0.0f, o = 0.0f;
+#pragma unroll 8
   for (int c = 0; c < nchunks; ++c) {
     const float mc = pm[base + c];
-    if (mc == -INFINITY) continue;
-    const float w = expf(mc - mx);
+    const float w = mc == -INFINITY ? 0.0f : expf(mc - mx);
     l = l + pl[base + c] * w;
     o = o + po[(base + c) * kAttnD + d] * w;
   }
@@ -275,24 +400,22 @@ hipError_t launch_qk_rope_cache(const uint16_t* qkv, const float* q_gamma, const
   return hipGetLastError();
 }
 
-constexpr int kAttnLds =
-    (kAttnMaxRows * kAttnD + kAttnChunk * (kAttnD + 1) + kAttnChunk * kAttnD +
-     kAttnMaxRows * kAttnChunk) * 4;
 
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
                             int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t pos0, int64_t Lmax,
                             uint16_t* out, void* workspace, hipStream_t st) {
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&attn_chunk_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-      kAttnLds);
+      attn_lds_bytes(kAttnMaxRows));
   if (attr != hipSuccess) return attr;
+  const int lds = attn_lds_bytes((int)((Hq / Hkv) * T));
   const int nch = attn_chunks(pos0, T);
   const size_t rows = (size_t)B * Hq * T * nch;
   char* ws = static_cast<char*>(workspace);
   float* pm = reinterpret_cast<float*>(ws);
   float* pl = reinterpret_cast<float*>(ws + align_up(rows * 4, kWsAlign));
   float* po = reinterpret_cast<float*>(ws + 2 * align_up(rows * 4, kWsAlign));
-  attn_chunk_kernel<<<dim3((unsigned)nch, (unsigned)Hkv, (unsigned)B), dim3(kAttnThreads), kAttnLds,
+  attn_chunk_kernel<<<dim3((unsigned)nch, (unsigned)Hkv, (unsigned)B), dim3(kAttnThreads), lds,
                       st>>>(q, k_cache, v_cache, (int)T, (int)Hq, (int)Hkv, (int)pos0, (int)Lmax, nch,
                             1.0f / sqrtf((float)kAttnD), pm, pl, po);
   hipError_t e = hipGetLastError();
