@@ -223,10 +223,8 @@ def quasar_verify_accept(logits: torch.Tensor, draft: torch.Tensor | None, tempe
     if uniforms is not None:
         _need(uniforms, torch.float32, (B, kp1), "uniforms")
     dev = logits.device
-    acc_len = torch.empty((B,), dtype=torch.int32, device=dev) if accept_len is None else accept_len
-    nxt = torch.empty((B,), dtype=torch.int32, device=dev) if next_token is None else next_token
-    _need(acc_len, torch.int32, (B,), "accept_len")
-    _need(nxt, torch.int32, (B,), "next_token")
+    acc_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    nxt = torch.empty((B,), dtype=torch.int32, device=dev)
     g = torch.empty((B, kp1), dtype=torch.int32, device=dev) if want_argmax else None
     pd = torch.empty((B, k), dtype=torch.float32, device=dev) if want_p_draft else None
     if workspace is None:
