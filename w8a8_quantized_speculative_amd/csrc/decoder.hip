@@ -332,6 +332,127 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(
   }
 }
 
+// The same partials on the matrix cores, for groups of at most 32 query rows
+// (the Qwen3-8B window: 4 heads per KV head x 6 positions = 24).  Eight
+// wavefronts:
+//   scores  wavefront w computes the 16 x 16 tile (row tile w / 4, key tile
+//           w % 4) of Q K^T with four v_mfma_f32_16x16x32_bf16 over D = 128,
+//           its operands read straight from memory (16 contiguous bytes of a
+//           q row and of a key row per lane); products of BF16 values are
+//           exact in binary32;
+//   softmax per row over the 64 keys in LDS (lane = key);
+//   P V     wavefront w owns output dimensions 16 w .. 16 w + 15 of both row
+//           tiles: sixteen v_mfma_f32_16x16x4_f32 over the keys, P in binary32
+//           (not rounded to BF16), V from LDS.
+// Operand layout of both MFMAs: lane l supplies row (or column) l % 16 at the
+// k positions of group l / 16; result register j of lane l is row
+// 4 (l / 16) + j, column l % 16.
+constexpr int kMfmaRows = 32;
+constexpr int kSsStride = kAttnChunk + 1;  // floats per score row in LDS
+constexpr int kVsStride = kAttnD + 8;      // BF16 per value row in LDS
+
+typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kAttnThreads) void attn_chunk_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
+    const uint16_t* __restrict__ v_cache, int T, int Hq, int Hkv, int pos0, int Lmax,
+    int nchunks, float scale, float* __restrict__ pm, float* __restrict__ pl,
+    float* __restrict__ po) {
+  __shared__ float ss[kMfmaRows * kSsStride];
+  __shared__ __align__(16) uint16_t vs[kAttnChunk * kVsStride];
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int G = Hq / Hkv, R = G * T;
+  const int klen = pos0 + T;
+  const int t0 = c * kAttnChunk;
+  const int nt = min(kAttnChunk, klen - t0);
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int rl = lane & 15, grp = lane >> 4;
+
+  // loads first: the value chunk (for LDS), this wavefront's q and key operands
+  const size_t kv0 = (((size_t)b * Hkv + g) * Lmax + t0) * kAttnD;
+  const buffer_rsrc krs = make_rsrc(k_cache + kv0, (uint32_t)nt * kAttnD * 2u);
+  const buffer_rsrc vrs = make_rsrc(v_cache + kv0, (uint32_t)nt * kAttnD * 2u);
+  const buffer_rsrc qrs = make_rsrc(q + (size_t)b * T * Hq * kAttnD, (uint32_t)(T * Hq * kAttnD * 2));
+  v4i vreg[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int u = tid + kAttnThreads * k;
+    vreg[k] = load16(vrs, ((u >> 4) * kAttnD + (u & 15) * 8) * 2);
+  }
+  const int rt = wave >> 2, kt = wave & 3;
+  const int qr = rt * 16 + rl;  // A row: query row of the group
+  const int qhh = qr / T, qi = qr - qhh * T;
+  const int qbase = qr < R ? (qi * Hq + g * G + qhh) * kAttnD * 2 : kOutOfRange;
+  const int kkey = kt * 16 + rl;  // B column: key of the chunk
+  v4i qa[4], kb[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int d = kk * 32 + grp * 8;
+    qa[kk] = load16(qrs, qr < R ? qbase + d * 2 : kOutOfRange);
+    kb[kk] = load16(krs, (kkey * kAttnD + d) * 2);
+  }
+  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf16, qa[kk]),
+                                                  __builtin_bit_cast(v8bf16, kb[kk]), acc, 0, 0, 0);
+  // scaled, masked scores into LDS
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = rt * 16 + grp * 4 + j;
+    const int i = row % T;
+    const bool valid = row < R && kkey < nt && t0 + kkey <= pos0 + i;
+    ss[row * kSsStride + kkey] = valid ? acc[j] * scale : -INFINITY;
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int u = tid + kAttnThreads * k;
+    *reinterpret_cast<v4i*>(vs + (u >> 4) * kVsStride + (u & 15) * 8) = vreg[k];
+  }
+  __syncthreads();
+  // softmax pieces, lane = key
+  for (int row = wave; row < R; row += kAttnThreads / kWave) {
+    const float sc = ss[row * kSsStride + lane];
+    const float mx = wave_max(sc);
+    const float p = mx == -INFINITY ? 0.0f : expf(sc - mx);
+    float sum = p;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, kWave);
+    ss[row * kSsStride + lane] = p;
+    if (lane == 0) {
+      const size_t pi = (((size_t)b * Hq + g * G + row / T) * T + row % T) * nchunks + c;
+      pm[pi] = mx;
+      pl[pi] = sum;
+    }
+  }
+  __syncthreads();
+  // P V: output dimensions 16 wave .. + 15, both row tiles
+  const int dcol = wave * 16 + rl;
+#pragma unroll
+  for (int rt2 = 0; rt2 < kMfmaRows / 16; ++rt2) {
+    if (rt2 * 16 >= R) break;
+    const int prow = rt2 * 16 + rl;
+    v4f o = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < kAttnChunk / 4; ++kk) {
+      const int key = kk * 4 + grp;
+      const float pa = prow < R ? ss[prow * kSsStride + key] : 0.0f;
+      const float vb = bf16_to_f32(vs[key * kVsStride + dcol]);
+      o = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vb, o, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = rt2 * 16 + grp * 4 + j;
+      if (row < R) {
+        const size_t pi = (((size_t)b * Hq + g * G + row / T) * T + row % T) * nchunks + c;
+        po[pi * kAttnD + dcol] = o[j];
+      }
+    }
+  }
+}
+
 // One block of D threads per (token, q head): out = sum_c o_c e^(m_c - M) / sum_c l_c e^(m_c - M).
 __global__ void attn_combine_kernel(const float* __restrict__ pm, const float* __restrict__ pl,
                                     const float* __restrict__ po, int T, int Hq, int nchunks,
@@ -415,6 +536,11 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k_cache, const ui
   float* pm = reinterpret_cast<float*>(ws);
   float* pl = reinterpret_cast<float*>(ws + align_up(rows * 4, kWsAlign));
   float* po = reinterpret_cast<float*>(ws + 2 * align_up(rows * 4, kWsAlign));
+  if ((Hq / Hkv) * T <= kMfmaRows)
+    attn_chunk_mfma_kernel<<<dim3((unsigned)nch, (unsigned)Hkv, (unsigned)B), dim3(kAttnThreads), 0,
+                             st>>>(q, k_cache, v_cache, (int)T, (int)Hq, (int)Hkv, (int)pos0, (int)Lmax,
+                                   nch, 1.0f / sqrtf((float)kAttnD), pm, pl, po);
+  else
   attn_chunk_kernel<<<dim3((unsigned)nch, (unsigned)Hkv, (unsigned)B), dim3(kAttnThreads), lds,
                       st>>>(q, k_cache, v_cache, (int)T, (int)Hq, (int)Hkv, (int)pos0, (int)Lmax, nch,
                             1.0f / sqrtf((float)kAttnD), pm, pl, po);
