@@ -233,3 +233,55 @@ def test_stream_copy_argument_errors(L):
     assert L.quasar_stream_copy(None, aligned, 16, None) == 1          # null source
     assert L.quasar_stream_copy(aligned, aligned, 15, None) == 1       # not a multiple of 16
     assert L.quasar_stream_copy(aligned + 1, aligned, 16, None) == 1   # misaligned
+
+
+# ------------------------------------------------------- decoder steps (host checks)
+def test_embed_and_rmsnorm_argument_errors(L):
+    emb = lambda tok=FAKE, tab=FAKE, M=6, V=100, H=64, h=FAKE: L.quasar_embed(tok, tab, M, V, H, h, None)
+    assert emb(M=0) == OK
+    assert emb(M=-1) == INVALID and emb(V=0) == INVALID and emb(H=0) == INVALID
+    assert emb(H=65537) == UNSUPPORTED
+    assert emb(tok=None) == INVALID and emb(h=FAKE + 2) == INVALID
+    rms = lambda h=FAKE, d=None, g=FAKE, M=6, H=64, eps=1e-6, o=FAKE: L.quasar_rmsnorm(
+        h, d, g, M, H, eps, o, None)
+    assert rms(M=0) == OK
+    assert rms(eps=0.0) == INVALID and rms(eps=float("nan")) == INVALID
+    assert rms(eps=float("inf")) == INVALID and rms(H=0) == INVALID
+    assert rms(h=FAKE + 4) == INVALID and rms(g=FAKE + 8) == INVALID  # 16-byte aligned
+    assert rms(o=FAKE + 2) == INVALID and rms(d=FAKE + 4) == INVALID  # 8-byte aligned
+    assert rms(g=None) == INVALID and rms(H=65537) == UNSUPPORTED
+
+
+def test_rope_attention_silu_argument_errors(L):
+    def rope(qkv=FAKE, B=1, T=6, Hq=32, Hkv=8, D=128, pos0=10, Lmax=16, base=1e6, eps=1e-6,
+             kc=FAKE, vc=FAKE):
+        return L.quasar_qk_rope_cache(qkv, FAKE, FAKE, B, T, Hq, Hkv, D, pos0, Lmax, base, eps,
+                                      FAKE, kc, vc, None)
+    assert rope(B=0) == OK
+    assert rope(D=64) == UNSUPPORTED                 # head dim 128 only
+    assert rope(Hq=30) == UNSUPPORTED                # Hq % Hkv != 0
+    assert rope(pos0=11) == UNSUPPORTED              # pos0 + T > Lmax
+    assert rope(base=1.0) == INVALID and rope(pos0=-1) == INVALID and rope(T=0) == INVALID
+    assert rope(qkv=None) == INVALID and rope(kc=FAKE + 1) == INVALID
+
+    assert L.quasar_attention_workspace_bytes(1, 6, 32, 2048) > 0
+    assert L.quasar_attention_workspace_bytes(0, 6, 32, 2048) == 0
+    need = L.quasar_attention_workspace_bytes(1, 6, 32, 10)
+
+    def attn(q=FAKE, B=1, T=6, Hq=32, Hkv=8, D=128, pos0=10, Lmax=16, ws=FAKE, wsb=None,
+             kc=FAKE):
+        return L.quasar_attention(q, kc, FAKE, B, T, Hq, Hkv, D, pos0, Lmax, FAKE, ws,
+                                  need if wsb is None else wsb, None)
+    assert attn(B=0) == OK
+    assert attn(D=96) == UNSUPPORTED
+    assert attn(T=17) == UNSUPPORTED                 # (Hq / Hkv) * T > 64 rows per KV head
+    assert attn(pos0=11) == UNSUPPORTED              # the window passes Lmax
+    assert attn(wsb=need - 1) == WORKSPACE and attn(ws=None) == WORKSPACE
+    assert attn(ws=FAKE + 16) == WORKSPACE           # 256-byte aligned
+    assert attn(q=FAKE + 8) == INVALID and attn(kc=FAKE + 2) == INVALID  # 16-byte aligned
+    assert attn(q=None) == INVALID
+
+    silu = lambda gu=FAKE, M=6, I=12288, o=FAKE: L.quasar_silu_mul(gu, M, I, o, None)
+    assert silu(M=0) == OK
+    assert silu(I=0) == INVALID and silu(M=-1) == INVALID and silu(gu=None) == INVALID
+    assert silu(M=65536) == UNSUPPORTED and silu(o=FAKE + 1) == INVALID
