@@ -347,6 +347,41 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(
 // Operand layout of both MFMAs: lane l supplies row (or column) l % 16 at the
 // k positions of group l / 16; result register j of lane l is row
 // 4 (l / 16) + j, column l % 16.
+// Wavefront max and sum by DPP row operations (no LDS permutes): butterflies
+// within rows of 16 lanes, then row broadcasts carry the totals to lane 63,
+// read back as a scalar.  For the sum, lanes outside a broadcast's row mask
+// add zero.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_fmax(float v) {
+  const float o = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v),
+                                                             kCtrl, kRowMask, 0xf, false));
+  return fmaxf(v, o);
+}
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_fadd(float v) {
+  const float o = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask,
+                                                             0xf, false));
+  return v + o;
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = dpp_fmax<0xB1, 0xf>(v);   // quad_perm [1,0,3,2]
+  v = dpp_fmax<0x4E, 0xf>(v);   // quad_perm [2,3,0,1]
+  v = dpp_fmax<0x141, 0xf>(v);  // row_half_mirror
+  v = dpp_fmax<0x140, 0xf>(v);  // row_mirror
+  v = dpp_fmax<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_fmax<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v = dpp_fadd<0xB1, 0xf>(v);
+  v = dpp_fadd<0x4E, 0xf>(v);
+  v = dpp_fadd<0x141, 0xf>(v);
+  v = dpp_fadd<0x140, 0xf>(v);
+  v = dpp_fadd<0x142, 0xa>(v);
+  v = dpp_fadd<0x143, 0xc>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 constexpr int kMfmaRows = 32;
 constexpr int kSsStride = kAttnChunk + 1;  // floats per score row in LDS
 constexpr int kVsStride = kAttnD + 8;      // BF16 per value row in LDS
@@ -415,11 +450,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_mfma_kernel(
   // softmax pieces, lane = key
   for (int row = wave; row < R; row += kAttnThreads / kWave) {
     const float sc = ss[row * kSsStride + lane];
-    const float mx = wave_max(sc);
+    const float mx = wave_max_dpp(sc);
     const float p = mx == -INFINITY ? 0.0f : expf(sc - mx);
-    float sum = p;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, kWave);
+    const float sum = wave_sum_dpp(p);
     ss[row * kSsStride + lane] = p;
     if (lane == 0) {
       const size_t pi = (((size_t)b * Hq + g * G + row / T) * T + row % T) * nchunks + c;
@@ -428,26 +461,29 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_mfma_kernel(
     }
   }
   __syncthreads();
-  // P V: output dimensions 16 wave .. + 15, both row tiles
+  // P V: output dimensions 16 wave .. + 15; the two row tiles' MFMA chains
+  // interleave and share each value read
   const int dcol = wave * 16 + rl;
+  v4f o[kMfmaRows / 16] = {};
+#pragma unroll
+  for (int kk = 0; kk < kAttnChunk / 4; ++kk) {
+    const int key = kk * 4 + grp;
+    const float vb = bf16_to_f32(vs[key * kVsStride + dcol]);
+#pragma unroll
+    for (int rt2 = 0; rt2 < kMfmaRows / 16; ++rt2) {
+      const int prow = rt2 * 16 + rl;
+      const float pa = prow < R ? ss[prow * kSsStride + key] : 0.0f;
+      o[rt2] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vb, o[rt2], 0, 0, 0);
+    }
+  }
 #pragma unroll
   for (int rt2 = 0; rt2 < kMfmaRows / 16; ++rt2) {
-    if (rt2 * 16 >= R) break;
-    const int prow = rt2 * 16 + rl;
-    v4f o = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int kk = 0; kk < kAttnChunk / 4; ++kk) {
-      const int key = kk * 4 + grp;
-      const float pa = prow < R ? ss[prow * kSsStride + key] : 0.0f;
-      const float vb = bf16_to_f32(vs[key * kVsStride + dcol]);
-      o = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vb, o, 0, 0, 0);
-    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = rt2 * 16 + grp * 4 + j;
       if (row < R) {
         const size_t pi = (((size_t)b * Hq + g * G + row / T) * T + row % T) * nchunks + c;
-        po[pi * kAttnD + dcol] = o[j];
+        po[pi * kAttnD + dcol] = o[rt2][j];
       }
     }
   }
