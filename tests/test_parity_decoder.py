@@ -137,11 +137,13 @@ def test_qk_rope_cache(B, pos0):
         assert np.all(rest == 0x3F80)
 
 
-@pytest.mark.parametrize("B,pos0", [(1, 0), (1, 63), (1, 64), (1, 1000), (1, 2047), (8, 200),
-                                    (16, 130)])
-def test_attention(B, pos0):
-    T = 6
-    announce("attention", B, pos0)
+# T = 6: 24 query rows per KV head (the matrix-core kernel); T = 9 and 16: 36 and
+# 64 rows (the vector-ALU kernel for groups wider than 32)
+@pytest.mark.parametrize("B,pos0,T", [(1, 0, 6), (1, 63, 6), (1, 64, 6), (1, 1000, 6), (1, 2047, 6),
+                                      (8, 200, 6), (16, 130, 6), (1, 100, 9), (2, 64, 16),
+                                      (1, 0, 16)])
+def test_attention(B, pos0, T):
+    announce("attention", B, pos0, T)
     Lmax = pos0 + T + 5
     kc = bf16_normal((B, HKV, Lmax, D), (63, B, pos0, 0))
     vc = bf16_normal((B, HKV, Lmax, D), (63, B, pos0, 1))

@@ -14,9 +14,11 @@
 //   rmsnorm_kernel       (h += delta), out = BF16(h * rsqrt(mean(h^2) + eps) * gamma)
 //   qk_rope_cache_kernel per-head RMSNorm of q and k, rotate-half RoPE, k and v
 //                        appended to the cache, q written for the attention
-//   attn_chunk_kernel    one KV head x 64 cached positions: partial softmax
+//   attn_chunk_mfma_kernel  one KV head x 64 cached positions: partial softmax
 //                        (max, sum of exp, unnormalised output) of the group's
-//                        query rows
+//                        query rows, both products on the matrix cores (groups
+//                        of at most 32 query rows)
+//   attn_chunk_kernel    the same on the vector ALUs, for wider groups
 //   attn_combine_kernel  merges the chunks of a query row
 //   silu_mul_kernel      out = BF16(silu(gate) * up) over the gate_up output
 #include "quasar_device.hpp"
@@ -192,10 +194,9 @@ __global__ void qk_rope_cache_kernel(const uint16_t* __restrict__ qkv, const flo
 // query rows, qs2[r][d/2], read as 4-byte broadcasts (a 16-byte binary32
 // broadcast moves four times the bytes through the LDS crossbar, and scalar
 // loads of the rows from memory were slower still).  Wavefront w of 8 owns
-// rows w, w + 8, ...: it
-// takes them four at a time through scores (lane = key), softmax (wavefront
-// reductions) and P V (lane = a pair of d), so after the one barrier no
-// wavefront waits for another.  The loops run over the whole chunk (keys
+// rows w, w + 8, ...: it takes them four at a time through scores (lane =
+// key), softmax (wavefront reductions) and P V (lane = a pair of d), so after
+// the one barrier no wavefront waits for another.  The loops run over the whole chunk (keys
 // past the window carry p = 0 and zero values).
 constexpr int kAttnChunk = 64;
 constexpr int kAttnThreads = 512;
@@ -332,21 +333,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(
   }
 }
 
-// The same partials on the matrix cores, for groups of at most 32 query rows
-// (the Qwen3-8B window: 4 heads per KV head x 6 positions = 24).  Eight
-// wavefronts:
-//   scores  wavefront w computes the 16 x 16 tile (row tile w / 4, key tile
-//           w % 4) of Q K^T with four v_mfma_f32_16x16x32_bf16 over D = 128,
-//           its operands read straight from memory (16 contiguous bytes of a
-//           q row and of a key row per lane); products of BF16 values are
-//           exact in binary32;
-//   softmax per row over the 64 keys in LDS (lane = key);
-//   P V     wavefront w owns output dimensions 16 w .. 16 w + 15 of both row
-//           tiles: sixteen v_mfma_f32_16x16x4_f32 over the keys, P in binary32
-//           (not rounded to BF16), V from LDS.
-// Operand layout of both MFMAs: lane l supplies row (or column) l % 16 at the
-// k positions of group l / 16; result register j of lane l is row
-// 4 (l / 16) + j, column l % 16.
 // Wavefront max and sum by DPP row operations (no LDS permutes): butterflies
 // within rows of 16 lanes, then row broadcasts carry the totals to lane 63,
 // read back as a scalar.  For the sum, lanes outside a broadcast's row mask
@@ -382,6 +368,21 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// The same partials on the matrix cores, for groups of at most 32 query rows
+// (the Qwen3-8B window: 4 heads per KV head x 6 positions = 24).  Eight
+// wavefronts:
+//   scores  wavefront w computes the 16 x 16 tile (row tile w / 4, key tile
+//           w % 4) of Q K^T with four v_mfma_f32_16x16x32_bf16 over D = 128,
+//           its operands read straight from memory (16 contiguous bytes of a
+//           q row and of a key row per lane); products of BF16 values are
+//           exact in binary32;
+//   softmax per row over the 64 keys in LDS (lane = key);
+//   P V     wavefront w owns output dimensions 16 w .. 16 w + 15 of both row
+//           tiles: sixteen v_mfma_f32_16x16x4_f32 over the keys, P in binary32
+//           (not rounded to BF16), V from LDS.
+// Operand layout of both MFMAs: lane l supplies row (or column) l % 16 at the
+// k positions of group l / 16; result register j of lane l is row
+// 4 (l / 16) + j, column l % 16.
 constexpr int kMfmaRows = 32;
 constexpr int kSsStride = kAttnChunk + 1;  // floats per score row in LDS
 constexpr int kVsStride = kAttnD + 8;      // BF16 per value row in LDS
