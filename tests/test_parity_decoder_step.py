@@ -9,9 +9,10 @@ W8A8 linears bit-exact, residual adds bit-exact, RMSNorm / RoPE / attention
 error bound, nearly all elements identical), and the accept decision exact
 on the GPU's logits.
 Two windows: one sequence (6 tokens: the one-launch linear) and two
-sequences (12 tokens: the wide linear).  The cached context (70 positions)
-crosses an attention chunk edge; the drafts come from the N-gram drafter on a
-synthetic history.
+sequences (12 tokens: the wide linear), with a 70-position cached context that
+crosses an attention chunk edge; and one layer at Qwen3-8B's dimensions (hidden
+4096, 32 / 8 heads, intermediate 12288) over a 2048-position context.  The drafts
+come from the N-gram drafter on a synthetic history.
 """
 import numpy as np
 import pytest
@@ -30,6 +31,10 @@ pytestmark = pytest.mark.gpu
 
 CFG = DecoderConfig(hidden=512, heads_q=4, heads_kv=2, head_dim=128, intermediate=1024, layers=2,
                     vocab=1000)
+# one layer at Qwen3-8B's dimensions (vocabulary cut to 1000 to keep the oracle's
+# LM head small), a 2048-position context
+QWEN3_LAYER = DecoderConfig(hidden=4096, heads_q=32, heads_kv=8, head_dim=128, intermediate=12288,
+                            layers=1, vocab=1000)
 
 
 def make_linear(N, K, key):
@@ -44,12 +49,13 @@ def bits(t):
     return host_bf16(t)
 
 
-@pytest.mark.parametrize("B", [1, 2])
-def test_decoder_step_link_by_link(B):
-    c = CFG
-    k, pos0 = 5, 70
+@pytest.mark.parametrize("cfg_name,B,pos0", [("small", 1, 70), ("small", 2, 70),
+                                              ("qwen3_layer", 1, 2048)])
+def test_decoder_step_link_by_link(cfg_name, B, pos0):
+    c = CFG if cfg_name == "small" else QWEN3_LAYER
+    k = 5
     T = k + 1
-    announce("decoder_step", B, k, pos0)
+    announce("decoder_step", cfg_name, B, k, pos0)
     H, D, I = c.hidden, c.head_dim, c.intermediate
     qkv_n = (c.heads_q + 2 * c.heads_kv) * D
     layers, host_w = [], []
