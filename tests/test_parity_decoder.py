@@ -138,10 +138,12 @@ def test_qk_rope_cache(B, pos0):
 
 
 # T = 6: 24 query rows per KV head (the matrix-core kernel); T = 9 and 16: 36 and
-# 64 rows (the vector-ALU kernel for groups wider than 32)
+# 64 rows (the vector-ALU kernel for groups wider than 32).  Batches whose chunk
+# workgroups exceed ~1024 walk several chunks per workgroup: 8 x 1100 (2 per
+# workgroup) and 16 x 2047 (5 per workgroup, the 96-token window at a 2048 context).
 @pytest.mark.parametrize("B,pos0,T", [(1, 0, 6), (1, 63, 6), (1, 64, 6), (1, 1000, 6), (1, 2047, 6),
-                                      (8, 200, 6), (16, 130, 6), (1, 100, 9), (2, 64, 16),
-                                      (1, 0, 16)])
+                                      (8, 200, 6), (16, 130, 6), (8, 1100, 6), (16, 2047, 6),
+                                      (1, 100, 9), (2, 64, 16), (1, 0, 16)])
 def test_attention(B, pos0, T):
     announce("attention", B, pos0, T)
     Lmax = pos0 + T + 5

@@ -384,6 +384,7 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
 // k positions of group l / 16; result register j of lane l is row
 // 4 (l / 16) + j, column l % 16.
 constexpr int kMfmaRows = 32;
+constexpr int kAttnResidentWgs = 1024;  // chunk workgroups resident at once: ~4 per CU on 256 CUs
 constexpr int kSsStride = kAttnChunk + 1;  // floats per score row in LDS
 constexpr int kVsStride = kAttnD + 8;      // BF16 per value row in LDS
 
@@ -392,89 +393,123 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kAttnThreads) void attn_chunk_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
-    const uint16_t* __restrict__ v_cache, int T, int Hq, int Hkv, int pos0, int Lmax,
-    int nchunks, float scale, float* __restrict__ pm, float* __restrict__ pl,
-    float* __restrict__ po) {
+    const uint16_t* __restrict__ v_cache, int T, int Hq, int Hkv, int pos0, int Lmax, int nparts,
+    int cpw, float scale, float* __restrict__ pm, float* __restrict__ pl, float* __restrict__ po) {
   __shared__ float ss[kMfmaRows * kSsStride];
+  __shared__ float sfac[kMfmaRows];  // per-row rescale of the running output, this chunk
   __shared__ __align__(16) uint16_t vs[kAttnChunk * kVsStride];
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv, R = G * T;
   const int klen = pos0 + T;
-  const int t0 = c * kAttnChunk;
-  const int nt = min(kAttnChunk, klen - t0);
+  const int nch = (klen + kAttnChunk - 1) / kAttnChunk;
+  const int c_begin = part * cpw, c_end = min(c_begin + cpw, nch);
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int rl = lane & 15, grp = lane >> 4;
 
-  // loads first: the value chunk (for LDS), this wavefront's q and key operands
-  const size_t kv0 = (((size_t)b * Hkv + g) * Lmax + t0) * kAttnD;
-  const buffer_rsrc krs = make_rsrc(k_cache + kv0, (uint32_t)nt * kAttnD * 2u);
-  const buffer_rsrc vrs = make_rsrc(v_cache + kv0, (uint32_t)nt * kAttnD * 2u);
+  // this wavefront's q operands, once for all of the workgroup's chunks
   const buffer_rsrc qrs = make_rsrc(q + (size_t)b * T * Hq * kAttnD, (uint32_t)(T * Hq * kAttnD * 2));
-  v4i vreg[2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int u = tid + kAttnThreads * k;
-    vreg[k] = load16(vrs, ((u >> 4) * kAttnD + (u & 15) * 8) * 2);
-  }
   const int rt = wave >> 2, kt = wave & 3;
   const int qr = rt * 16 + rl;  // A row: query row of the group
   const int qhh = qr / T, qi = qr - qhh * T;
   const int qbase = qr < R ? (qi * Hq + g * G + qhh) * kAttnD * 2 : kOutOfRange;
   const int kkey = kt * 16 + rl;  // B column: key of the chunk
-  v4i qa[4], kb[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int d = kk * 32 + grp * 8;
-    qa[kk] = load16(qrs, qr < R ? qbase + d * 2 : kOutOfRange);
-    kb[kk] = load16(krs, (kkey * kAttnD + d) * 2);
-  }
-  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  v4i qa[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf16, qa[kk]),
-                                                  __builtin_bit_cast(v8bf16, kb[kk]), acc, 0, 0, 0);
-  // scaled, masked scores into LDS
+    qa[kk] = load16(qrs, qr < R ? qbase + (kk * 32 + grp * 8) * 2 : kOutOfRange);
+
+  // running softmax of the rows this wavefront owns (rows wave + 8 jr), and the
+  // running unnormalised output of its 16 dimensions for both row tiles
+  constexpr int kRowsPerWave = kMfmaRows / (kAttnThreads / kWave);
+  float m_run[kRowsPerWave], l_run[kRowsPerWave];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = rt * 16 + grp * 4 + j;
-    const int i = row % T;
-    const bool valid = row < R && kkey < nt && t0 + kkey <= pos0 + i;
-    ss[row * kSsStride + kkey] = valid ? acc[j] * scale : -INFINITY;
+  for (int jr = 0; jr < kRowsPerWave; ++jr) {
+    m_run[jr] = -INFINITY;
+    l_run[jr] = 0.0f;
   }
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int u = tid + kAttnThreads * k;
-    *reinterpret_cast<v4i*>(vs + (u >> 4) * kVsStride + (u & 15) * 8) = vreg[k];
-  }
-  __syncthreads();
-  // softmax pieces, lane = key
-  for (int row = wave; row < R; row += kAttnThreads / kWave) {
-    const float sc = ss[row * kSsStride + lane];
-    const float mx = wave_max_dpp(sc);
-    const float p = mx == -INFINITY ? 0.0f : expf(sc - mx);
-    const float sum = wave_sum_dpp(p);
-    ss[row * kSsStride + lane] = p;
-    if (lane == 0) {
-      const size_t pi = (((size_t)b * Hq + g * G + row / T) * T + row % T) * nchunks + c;
-      pm[pi] = mx;
-      pl[pi] = sum;
-    }
-  }
-  __syncthreads();
-  // P V: output dimensions 16 wave .. + 15; the two row tiles' MFMA chains
-  // interleave and share each value read
   const int dcol = wave * 16 + rl;
   v4f o[kMfmaRows / 16] = {};
+
+  for (int c = c_begin; c < c_end; ++c) {
+    const int t0 = c * kAttnChunk;
+    const int nt = min(kAttnChunk, klen - t0);
+    const size_t kv0 = (((size_t)b * Hkv + g) * Lmax + t0) * kAttnD;
+    const buffer_rsrc krs = make_rsrc(k_cache + kv0, (uint32_t)nt * kAttnD * 2u);
+    const buffer_rsrc vrs = make_rsrc(v_cache + kv0, (uint32_t)nt * kAttnD * 2u);
+    v4i vreg[2], kb[4];
 #pragma unroll
-  for (int kk = 0; kk < kAttnChunk / 4; ++kk) {
-    const int key = kk * 4 + grp;
-    const float vb = bf16_to_f32(vs[key * kVsStride + dcol]);
+    for (int k = 0; k < 2; ++k) {
+      const int u = tid + kAttnThreads * k;
+      vreg[k] = load16(vrs, ((u >> 4) * kAttnD + (u & 15) * 8) * 2);
+    }
 #pragma unroll
-    for (int rt2 = 0; rt2 < kMfmaRows / 16; ++rt2) {
-      const int prow = rt2 * 16 + rl;
-      const float pa = prow < R ? ss[prow * kSsStride + key] : 0.0f;
-      o[rt2] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vb, o[rt2], 0, 0, 0);
+    for (int kk = 0; kk < 4; ++kk) kb[kk] = load16(krs, (kkey * kAttnD + kk * 32 + grp * 8) * 2);
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf16, qa[kk]),
+                                                    __builtin_bit_cast(v8bf16, kb[kk]), acc, 0, 0,
+                                                    0);
+    __syncthreads();  // the previous chunk's P V reads of ss and vs are done
+    // scaled, masked scores and the value chunk into LDS
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = rt * 16 + grp * 4 + j;
+      const int i = row % T;
+      const bool valid = row < R && kkey < nt && t0 + kkey <= pos0 + i;
+      ss[row * kSsStride + kkey] = valid ? acc[j] * scale : -INFINITY;
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int u = tid + kAttnThreads * k;
+      *reinterpret_cast<v4i*>(vs + (u >> 4) * kVsStride + (u & 15) * 8) = vreg[k];
+    }
+    __syncthreads();
+    // softmax pieces, lane = key, folded into the running maximum and sum
+#pragma unroll
+    for (int jr = 0; jr < kRowsPerWave; ++jr) {
+      const int row = wave + jr * (kAttnThreads / kWave);
+      if (row >= R) continue;
+      const float sc = ss[row * kSsStride + lane];
+      const float new_m = fmaxf(m_run[jr], wave_max_dpp(sc));
+      const float fac = m_run[jr] == -INFINITY ? 0.0f : expf(m_run[jr] - new_m);
+      const float p = new_m == -INFINITY ? 0.0f : expf(sc - new_m);
+      l_run[jr] = l_run[jr] * fac + wave_sum_dpp(p);
+      m_run[jr] = new_m;
+      ss[row * kSsStride + lane] = p;
+      if (lane == 0) sfac[row] = fac;
+    }
+    __syncthreads();
+    // P V: rescale the running output rows, then add this chunk's keys; the two
+    // row tiles' MFMA chains interleave and share each value read
+#pragma unroll
+    for (int rt2 = 0; rt2 < kMfmaRows / 16; ++rt2)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = rt2 * 16 + grp * 4 + j;
+        o[rt2][j] = o[rt2][j] * (row < R ? sfac[row] : 0.0f);
+      }
+#pragma unroll
+    for (int kk = 0; kk < kAttnChunk / 4; ++kk) {
+      const int key = kk * 4 + grp;
+      const float vb = bf16_to_f32(vs[key * kVsStride + dcol]);
+#pragma unroll
+      for (int rt2 = 0; rt2 < kMfmaRows / 16; ++rt2) {
+        const int prow = rt2 * 16 + rl;
+        const float pa = prow < R ? ss[prow * kSsStride + key] : 0.0f;
+        o[rt2] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vb, o[rt2], 0, 0, 0);
+      }
+    }
+  }
+  // the workgroup's partials
+#pragma unroll
+  for (int jr = 0; jr < kRowsPerWave; ++jr) {
+    const int row = wave + jr * (kAttnThreads / kWave);
+    if (row < R && lane == 0) {
+      const size_t pi = (((size_t)b * Hq + g * G + row / T) * T + row % T) * nparts + part;
+      pm[pi] = m_run[jr];
+      pl[pi] = l_run[jr];
     }
   }
 #pragma unroll
@@ -483,7 +518,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_mfma_kernel(
     for (int j = 0; j < 4; ++j) {
       const int row = rt2 * 16 + grp * 4 + j;
       if (row < R) {
-        const size_t pi = (((size_t)b * Hq + g * G + row / T) * T + row % T) * nchunks + c;
+        const size_t pi = (((size_t)b * Hq + g * G + row / T) * T + row % T) * nparts + part;
         po[pi * kAttnD + dcol] = o[rt2][j];
       }
     }
@@ -573,18 +608,27 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k_cache, const ui
   float* pm = reinterpret_cast<float*>(ws);
   float* pl = reinterpret_cast<float*>(ws + align_up(rows * 4, kWsAlign));
   float* po = reinterpret_cast<float*>(ws + 2 * align_up(rows * 4, kWsAlign));
-  if ((Hq / Hkv) * T <= kMfmaRows)
-    attn_chunk_mfma_kernel<<<dim3((unsigned)nch, (unsigned)Hkv, (unsigned)B), dim3(kAttnThreads), 0,
-                             st>>>(q, k_cache, v_cache, (int)T, (int)Hq, (int)Hkv, (int)pos0, (int)Lmax,
-                                   nch, 1.0f / sqrtf((float)kAttnD), pm, pl, po);
-  else
-  attn_chunk_kernel<<<dim3((unsigned)nch, (unsigned)Hkv, (unsigned)B), dim3(kAttnThreads), lds,
-                      st>>>(q, k_cache, v_cache, (int)T, (int)Hq, (int)Hkv, (int)pos0, (int)Lmax, nch,
-                            1.0f / sqrtf((float)kAttnD), pm, pl, po);
+  int nparts = nch;
+  if ((Hq / Hkv) * T <= kMfmaRows) {
+    // chunks per workgroup: one while the chunk workgroups fit the device at
+    // about four per compute unit, more (walked with a running softmax) when a
+    // batch of sequences would need several rounds of them
+    const int64_t chunk_wgs = (int64_t)nch * Hkv * B;
+    const int cpw = (int)((chunk_wgs + kAttnResidentWgs - 1) / kAttnResidentWgs);
+    nparts = (nch + cpw - 1) / cpw;
+    attn_chunk_mfma_kernel<<<dim3((unsigned)nparts, (unsigned)Hkv, (unsigned)B), dim3(kAttnThreads),
+                             0, st>>>(q, k_cache, v_cache, (int)T, (int)Hq, (int)Hkv, (int)pos0,
+                                      (int)Lmax, nparts, cpw, 1.0f / sqrtf((float)kAttnD), pm, pl,
+                                      po);
+  } else {
+    attn_chunk_kernel<<<dim3((unsigned)nch, (unsigned)Hkv, (unsigned)B), dim3(kAttnThreads), lds,
+                        st>>>(q, k_cache, v_cache, (int)T, (int)Hq, (int)Hkv, (int)pos0, (int)Lmax,
+                              nch, 1.0f / sqrtf((float)kAttnD), pm, pl, po);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   attn_combine_kernel<<<dim3((unsigned)(B * T), (unsigned)Hq), dim3(kAttnD), 0, st>>>(
-      pm, pl, po, (int)T, (int)Hq, nch, out);
+      pm, pl, po, (int)T, (int)Hq, nparts, out);
   return hipGetLastError();
 }
 
