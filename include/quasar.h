@@ -371,20 +371,21 @@ quasar_status quasar_qk_rope_cache(const uint16_t* qkv, const float* q_gamma,
                                    uint16_t* k_cache, uint16_t* v_cache, void* stream);
 
 /* Workspace bytes of quasar_attention (0 for invalid sizes). */
-size_t quasar_attention_workspace_bytes(int64_t B, int64_t T, int64_t Hq, int64_t pos0);
+size_t quasar_attention_workspace_bytes(int64_t B, int64_t T, int64_t Hq, int64_t Hkv,
+                                        int64_t pos0);
 
 /*
  * quasar_attention -- causal grouped-query attention of the verify positions
  * over the cache: query i of sequence b, head h, sees cached positions
  * 0 .. pos0 + i of KV head h / (Hq / Hkv);
  *     out = BF16(sum_t softmax_t(RN32(q . k_t) / sqrt(D)) v_t)
- * in binary32, the softmax split into 64-position chunks merged by their
+ * in binary32, the softmax split into ranges of positions merged by their
  * maxima (the result differs from one pass by rounding only).
  *   q        [B*T, Hq D] bf16 from quasar_qk_rope_cache, 16-byte aligned (in)
  *   k_cache, v_cache  as above, positions 0 .. pos0+T-1 filled, 16-byte
  *            aligned (in)
  *   out      [B*T, Hq D] bf16 (out)
- *   workspace  quasar_attention_workspace_bytes(B, T, Hq, pos0) bytes,
+ *   workspace  quasar_attention_workspace_bytes(B, T, Hq, Hkv, pos0) bytes,
  *            256-byte aligned
  *   D == 128, Hq % Hkv == 0, (Hq / Hkv) * T <= 64, pos0 + T <= Lmax
  */

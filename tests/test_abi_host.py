@@ -52,7 +52,7 @@ def test_status_strings(L):
     for code in range(5):
         assert L.quasar_status_string(code).decode().startswith("QUASAR_")
     assert b"UNKNOWN" in L.quasar_status_string(99)
-    assert L.quasar_abi_version() == 7
+    assert L.quasar_abi_version() == 8
 
 
 def test_workspace_queries_are_pure_host_and_monotone(L):
@@ -264,9 +264,10 @@ def test_rope_attention_silu_argument_errors(L):
     assert rope(base=1.0) == INVALID and rope(pos0=-1) == INVALID and rope(T=0) == INVALID
     assert rope(qkv=None) == INVALID and rope(kc=FAKE + 1) == INVALID
 
-    assert L.quasar_attention_workspace_bytes(1, 6, 32, 2048) > 0
-    assert L.quasar_attention_workspace_bytes(0, 6, 32, 2048) == 0
-    need = L.quasar_attention_workspace_bytes(1, 6, 32, 10)
+    assert L.quasar_attention_workspace_bytes(1, 6, 32, 8, 2048) > 0
+    assert L.quasar_attention_workspace_bytes(0, 6, 32, 8, 2048) == 0
+    assert L.quasar_attention_workspace_bytes(1, 6, 32, 5, 2048) == 0  # Hq % Hkv != 0
+    need = L.quasar_attention_workspace_bytes(1, 6, 32, 8, 10)
 
     def attn(q=FAKE, B=1, T=6, Hq=32, Hkv=8, D=128, pos0=10, Lmax=16, ws=FAKE, wsb=None,
              kc=FAKE):

@@ -56,7 +56,7 @@ _SIGNATURES = {
     "quasar_rmsnorm": (ctypes.c_int, [_P, _P, _P, _I64, _I64, ctypes.c_float, _P, _P]),
     "quasar_qk_rope_cache": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
                                             ctypes.c_float, ctypes.c_float, _P, _P, _P, _P]),
-    "quasar_attention_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64]),
+    "quasar_attention_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64]),
     "quasar_attention": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64, _P,
                                         _P, _SZ, _P]),
     "quasar_silu_mul": (ctypes.c_int, [_P, _I64, _I64, _P, _P]),
@@ -385,8 +385,8 @@ def quasar_qk_rope_cache(qkv: torch.Tensor, q_gamma: torch.Tensor, k_gamma: torc
     return q_out
 
 
-def workspace_bytes_attention(B: int, T: int, Hq: int, pos0: int) -> int:
-    return int(lib().quasar_attention_workspace_bytes(B, T, Hq, pos0))
+def workspace_bytes_attention(B: int, T: int, Hq: int, Hkv: int, pos0: int) -> int:
+    return int(lib().quasar_attention_workspace_bytes(B, T, Hq, Hkv, pos0))
 
 
 def quasar_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, Hq: int,
@@ -404,7 +404,7 @@ def quasar_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
     if out is None:
         out = torch.empty((M, Hq * D), dtype=torch.bfloat16, device=q.device)
     _need(out, torch.bfloat16, (M, Hq * D), "out")
-    need = workspace_bytes_attention(B, T, Hq, pos0)
+    need = workspace_bytes_attention(B, T, Hq, Hkv, pos0)
     if workspace is None:
         workspace = new_workspace(need, q.device)
     nbytes = workspace.numel() * workspace.element_size()

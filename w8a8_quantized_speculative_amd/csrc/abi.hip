@@ -85,7 +85,7 @@ const char* quasar_status_string(quasar_status status) {
   return "QUASAR_ERR_UNKNOWN";
 }
 
-int quasar_abi_version(void) { return 7; }
+int quasar_abi_version(void) { return 8; }
 
 quasar_status quasar_quantize_weights(const uint16_t* w, const float* s, int64_t N, int64_t K,
                                       int8_t* wq, float* w_scale, void* stream) {
@@ -344,11 +344,12 @@ quasar_status quasar_qk_rope_cache(const uint16_t* qkv, const float* q_gamma,
                                          (hipStream_t)stream));
 }
 
-size_t quasar_attention_workspace_bytes(int64_t B, int64_t T, int64_t Hq, int64_t pos0) {
-  if (B <= 0 || T <= 0 || Hq <= 0 || pos0 < 0 || B * T > kMaxRowsPerCall ||
+size_t quasar_attention_workspace_bytes(int64_t B, int64_t T, int64_t Hq, int64_t Hkv,
+                                        int64_t pos0) {
+  if (B <= 0 || T <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || pos0 < 0 || B * T > kMaxRowsPerCall ||
       pos0 > kMaxRowsPerCall)
     return 0;
-  return attn_workspace_bytes(B, T, Hq, pos0);
+  return attn_workspace_bytes(B, T, Hq, Hkv, pos0);
 }
 
 quasar_status quasar_attention(const uint16_t* q, const uint16_t* k_cache,
@@ -364,7 +365,7 @@ quasar_status quasar_attention(const uint16_t* q, const uint16_t* k_cache,
   if (!q || !k_cache || !v_cache || !out || !aligned(q, 16) || !aligned(k_cache, 16) ||
       !aligned(v_cache, 16) || !aligned(out, 2))
     return QUASAR_ERR_INVALID_ARG;
-  if (!workspace || workspace_bytes < attn_workspace_bytes(B, T, Hq, pos0) ||
+  if (!workspace || workspace_bytes < attn_workspace_bytes(B, T, Hq, Hkv, pos0) ||
       !aligned(workspace, kWsAlign))
     return QUASAR_ERR_WORKSPACE;
   return hip_status(launch_attention(q, k_cache, v_cache, B, T, Hq, Hkv, pos0, Lmax, out,

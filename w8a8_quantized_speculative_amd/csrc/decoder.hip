@@ -14,13 +14,17 @@
 //   rmsnorm_kernel       (h += delta), out = BF16(h * rsqrt(mean(h^2) + eps) * gamma)
 //   qk_rope_cache_kernel per-head RMSNorm of q and k, rotate-half RoPE, k and v
 //                        appended to the cache, q written for the attention
-//   attn_chunk_mfma_kernel  one KV head x 64 cached positions: partial softmax
-//                        (max, sum of exp, unnormalised output) of the group's
-//                        query rows, both products on the matrix cores (groups
-//                        of at most 32 query rows)
-//   attn_chunk_kernel    the same on the vector ALUs, for wider groups
+//   attn_wave_kernel     one KV head x a range of cached positions per
+//                        wavefront: partial softmax (max, sum of exp,
+//                        unnormalised output) of the group's query rows, both
+//                        products on the matrix cores (groups of at most 32
+//                        query rows)
+//   attn_chunk_kernel    the same per 64 positions on the vector ALUs, for
+//                        wider groups
 //   attn_combine_kernel  merges the chunks of a query row
 //   silu_mul_kernel      out = BF16(silu(gate) * up) over the gate_up output
+#include <algorithm>
+
 #include "quasar_device.hpp"
 #include "quasar_internal.hpp"
 
@@ -333,217 +337,270 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(
   }
 }
 
-// Wavefront max and sum by DPP row operations (no LDS permutes): butterflies
-// within rows of 16 lanes, then row broadcasts carry the totals to lane 63,
-// read back as a scalar.  For the sum, lanes outside a broadcast's row mask
-// add zero.
-template <int kCtrl, int kRowMask>
-__device__ __forceinline__ float dpp_fmax(float v) {
-  const float o = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v),
-                                                             kCtrl, kRowMask, 0xf, false));
-  return fmaxf(v, o);
-}
-template <int kCtrl, int kRowMask>
-__device__ __forceinline__ float dpp_fadd(float v) {
-  const float o = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask,
-                                                             0xf, false));
-  return v + o;
-}
-__device__ __forceinline__ float wave_max_dpp(float v) {
-  v = dpp_fmax<0xB1, 0xf>(v);   // quad_perm [1,0,3,2]
-  v = dpp_fmax<0x4E, 0xf>(v);   // quad_perm [2,3,0,1]
-  v = dpp_fmax<0x141, 0xf>(v);  // row_half_mirror
-  v = dpp_fmax<0x140, 0xf>(v);  // row_mirror
-  v = dpp_fmax<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
-  v = dpp_fmax<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-  v = dpp_fadd<0xB1, 0xf>(v);
-  v = dpp_fadd<0x4E, 0xf>(v);
-  v = dpp_fadd<0x141, 0xf>(v);
-  v = dpp_fadd<0x140, 0xf>(v);
-  v = dpp_fadd<0x142, 0xa>(v);
-  v = dpp_fadd<0x143, 0xc>(v);
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-
-// The same partials on the matrix cores, for groups of at most 32 query rows
-// (the Qwen3-8B window: 4 heads per KV head x 6 positions = 24).  Eight
-// wavefronts:
-//   scores  wavefront w computes the 16 x 16 tile (row tile w / 4, key tile
-//           w % 4) of Q K^T with four v_mfma_f32_16x16x32_bf16 over D = 128,
-//           its operands read straight from memory (16 contiguous bytes of a
-//           q row and of a key row per lane); products of BF16 values are
-//           exact in binary32;
-//   softmax per row over the 64 keys in LDS (lane = key);
-//   P V     wavefront w owns output dimensions 16 w .. 16 w + 15 of both row
-//           tiles: sixteen v_mfma_f32_16x16x4_f32 over the keys, P in binary32
-//           (not rounded to BF16), V from LDS.
-// Operand layout of both MFMAs: lane l supplies row (or column) l % 16 at the
-// k positions of group l / 16; result register j of lane l is row
-// 4 (l / 16) + j, column l % 16.
+// The partials on the matrix cores, one wavefront per range of positions, for
+// groups of at most 32 query rows (the Qwen3-8B window: 4 heads per KV head x 6
+// positions = 24).  A wavefront walks `spw` steps of 32 keys with a running
+// softmax per query row; each step
+//   scores  S^T = K Q^T, four tiles (2 key tiles x 2 query-row tiles) of
+//           v_mfma_f32_16x16x32_bf16 over D = 128, operands straight from memory
+//           (16 contiguous bytes of a key row and of a q row per lane).  Products
+//           of BF16 values are exact in binary32.  Result register j of lane l is
+//           key 4 (l / 16) + j of the tile, query row l % 16;
+//   softmax per query row: the row's 32 scores sit in the four lanes l % 16 + 16 g
+//           (8 each), so its maximum is a local max and two lane exchanges, and
+//           every exponential is computed in the lane that holds the score;
+//   P V     O^T += V^T P^T by v_mfma_f32_16x16x32_bf16.  The B operand of lane l is
+//           query row l % 16 at the 8 keys this lane already holds (key slots
+//           0..3 = keys 4 (l / 16) + j of the first key tile, 4..7 of the second),
+//           so P never leaves the registers; the A operand is V^T at the same key
+//           slots: two 8-byte LDS reads from this wavefront's transposed copy of
+//           the values (dimension-major, keys contiguous), written there with
+//           16-bit stores.  P (binary32, in [0, 1]) is split exactly into three BF16 parts
+//           hi + mid + lo (truncations: 8 + 8 + 8 significant bits), each
+//           multiplied in its own MFMA, so no product rounds P to BF16.
+// The next step's keys and values are loaded before the current step's softmax.
+// Result register j of the P V tiles is output dimension 4 (l / 16) + j of the
+// tile for query row l % 16: the running output is rescaled per lane.
+constexpr int kWaveKeys = 32;
+// BF16 per row of the transposed values (one output dimension, 32 keys): rows
+// 8 apart start 16 banks apart, so a store instruction (16 keys x 4 rows 8 apart)
+// touches 32 distinct banks, and every row start is 8-byte aligned
+constexpr int kWaveVtStride = 36;
+constexpr int kAttnResidentWaves = 2048;  // two wavefronts per SIMD on 256 compute units
 constexpr int kMfmaRows = 32;
-constexpr int kAttnResidentWgs = 1024;  // chunk workgroups resident at once: ~4 per CU on 256 CUs
-constexpr int kSsStride = kAttnChunk + 1;  // floats per score row in LDS
-constexpr int kVsStride = kAttnD + 8;      // BF16 per value row in LDS
 
 typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(kAttnThreads) void attn_chunk_mfma_kernel(
+// Steps of 32 keys per wavefront: one while the wavefronts of a launch are
+// resident at once, more when a batch would need several rounds of them.
+int attn_wave_steps(int64_t B, int64_t Hkv, int64_t klen) {
+  const int64_t steps = (klen + kWaveKeys - 1) / kWaveKeys;
+  const int64_t waves = steps * Hkv * B;
+  return (int)std::max<int64_t>(1, (waves + kAttnResidentWaves - 1) / kAttnResidentWaves);
+}
+
+__device__ __forceinline__ uint32_t pack_hi16(float a, float b) {
+  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+}
+
+__global__ __launch_bounds__(kWave, 2) void attn_wave_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, int T, int Hq, int Hkv, int pos0, int Lmax, int nparts,
-    int cpw, float scale, float* __restrict__ pm, float* __restrict__ pl, float* __restrict__ po) {
-  __shared__ float ss[kMfmaRows * kSsStride];
-  __shared__ float sfac[kMfmaRows];  // per-row rescale of the running output, this chunk
-  __shared__ __align__(16) uint16_t vs[kAttnChunk * kVsStride];
+    int spw, float scale, float* __restrict__ pm, float* __restrict__ pl, float* __restrict__ po) {
+  __shared__ __align__(16) uint16_t vt[kAttnD * kWaveVtStride];
   const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int G = Hq / Hkv, R = G * T;
-  const int klen = pos0 + T;
-  const int nch = (klen + kAttnChunk - 1) / kAttnChunk;
-  const int c_begin = part * cpw, c_end = min(c_begin + cpw, nch);
-  const int tid = threadIdx.x, lane = tid % kWave;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int rl = lane & 15, grp = lane >> 4;
+  const int lane = threadIdx.x, rl = lane & 15, grp = lane >> 4;
+  const int G = Hq / Hkv, R = G * T, klen = pos0 + T;
+  const int t_begin = part * spw * kWaveKeys;
+  const int t_end = min(t_begin + spw * kWaveKeys, klen);
 
-  // this wavefront's q operands, once for all of the workgroup's chunks
+  // B operands of the scores: query row rt * 16 + rl of the group at D values
+  // 32 kk + 8 grp .. + 7; `vis` is the last key the row sees (-1: padding row)
   const buffer_rsrc qrs = make_rsrc(q + (size_t)b * T * Hq * kAttnD, (uint32_t)(T * Hq * kAttnD * 2));
-  const int rt = wave >> 2, kt = wave & 3;
-  const int qr = rt * 16 + rl;  // A row: query row of the group
-  const int qhh = qr / T, qi = qr - qhh * T;
-  const int qbase = qr < R ? (qi * Hq + g * G + qhh) * kAttnD * 2 : kOutOfRange;
-  const int kkey = kt * 16 + rl;  // B column: key of the chunk
-  v4i qa[4];
+  v4i qb[2][4];
+  int vis[2];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    qa[kk] = load16(qrs, qr < R ? qbase + (kk * 32 + grp * 8) * 2 : kOutOfRange);
+  for (int rt = 0; rt < 2; ++rt) {
+    const int r = rt * 16 + rl;
+    const int hh = r / T, i = r - hh * T;
+    const int base = ((i * Hq + g * G + hh) * kAttnD + grp * 8) * 2;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qb[rt][kk] = load16(qrs, r < R ? base + kk * 64 : kOutOfRange);
+    vis[rt] = r < R ? pos0 + i : -1;
+  }
 
-  // running softmax of the rows this wavefront owns (rows wave + 8 jr), and the
-  // running unnormalised output of its 16 dimensions for both row tiles
-  constexpr int kRowsPerWave = kMfmaRows / (kAttnThreads / kWave);
-  float m_run[kRowsPerWave], l_run[kRowsPerWave];
+  const size_t kv_head = ((size_t)b * Hkv + g) * Lmax * kAttnD;
+  const int vkey = lane & 15, vcol8 = lane >> 4;
+  v4i ka[2][4], vr[8];
+  auto load_step = [&](int t0) {
+    // keys t0 .. t0 + 31; those at or past klen read as zero (masked below)
+    const uint32_t bytes = (uint32_t)min(kWaveKeys, klen - t0) * kAttnD * 2u;
+    const buffer_rsrc krs = make_rsrc(k_cache + kv_head + (size_t)t0 * kAttnD, bytes);
+    const buffer_rsrc vrs = make_rsrc(v_cache + kv_head + (size_t)t0 * kAttnD, bytes);
 #pragma unroll
-  for (int jr = 0; jr < kRowsPerWave; ++jr) {
-    m_run[jr] = -INFINITY;
-    l_run[jr] = 0.0f;
-  }
-  const int dcol = wave * 16 + rl;
-  v4f o[kMfmaRows / 16] = {};
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        ka[kt][kk] = load16(krs, ((kt * 16 + rl) * kAttnD + kk * 32 + grp * 8) * 2);
+    // value piece i of this lane: key vkey + 16 (i & 1), dimensions 8 vcol8 .. + 7
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      vr[i] = load16(vrs, ((vkey + 16 * (i & 1)) * kAttnD + (vcol8 + 4 * (i >> 1)) * 8) * 2);
+  };
+  load_step(t_begin);
 
-  for (int c = c_begin; c < c_end; ++c) {
-    const int t0 = c * kAttnChunk;
-    const int nt = min(kAttnChunk, klen - t0);
-    const size_t kv0 = (((size_t)b * Hkv + g) * Lmax + t0) * kAttnD;
-    const buffer_rsrc krs = make_rsrc(k_cache + kv0, (uint32_t)nt * kAttnD * 2u);
-    const buffer_rsrc vrs = make_rsrc(v_cache + kv0, (uint32_t)nt * kAttnD * 2u);
-    v4i vreg[2], kb[4];
+  float m_run[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.0f, 0.0f};
+  v4f o[8][2] = {};
+  for (int t0 = t_begin; t0 < t_end; t0 += kWaveKeys) {
+    v4f s[2][2];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int u = tid + kAttnThreads * k;
-      vreg[k] = load16(vrs, ((u >> 4) * kAttnD + (u & 15) * 8) * 2);
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        s[rt][kt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          s[rt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(v8bf16, ka[kt][kk]), __builtin_bit_cast(v8bf16, qb[rt][kk]),
+              s[rt][kt], 0, 0, 0);
+      }
+    __syncthreads();  // the previous step's reads of vt are done
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint16_t* dst = vt + (vcol8 + 4 * (i >> 1)) * 8 * kWaveVtStride + vkey + 16 * (i & 1);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t w = (uint32_t)vr[i][c];
+        dst[(2 * c) * kWaveVtStride] = (uint16_t)w;
+        dst[(2 * c + 1) * kWaveVtStride] = (uint16_t)(w >> 16);
+      }
     }
+    if (t0 + kWaveKeys < t_end) load_step(t0 + kWaveKeys);
+
+    // softmax pieces of query rows rt * 16 + rl; P split into BF16 parts
+    v4i ph[2][3];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) kb[kk] = load16(krs, (kkey * kAttnD + kk * 32 + grp * 8) * 2);
-    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int rt = 0; rt < 2; ++rt) {
+      float sv[8];
+      float mx = -INFINITY;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf16, qa[kk]),
-                                                    __builtin_bit_cast(v8bf16, kb[kk]), acc, 0, 0,
-                                                    0);
-    __syncthreads();  // the previous chunk's P V reads of ss and vs are done
-    // scaled, masked scores and the value chunk into LDS
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = rt * 16 + grp * 4 + j;
-      const int i = row % T;
-      const bool valid = row < R && kkey < nt && t0 + kkey <= pos0 + i;
-      ss[row * kSsStride + kkey] = valid ? acc[j] * scale : -INFINITY;
-    }
+        for (int j = 0; j < 4; ++j) {
+          const int key = t0 + kt * 16 + grp * 4 + j;
+          sv[kt * 4 + j] = key <= vis[rt] ? s[rt][kt][j] * scale : -INFINITY;
+          mx = fmaxf(mx, sv[kt * 4 + j]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float m_new = fmaxf(m_run[rt], mx);
+      const float fac = m_run[rt] == -INFINITY ? 0.0f : expf(m_run[rt] - m_new);
+      float p[8], hi[8], mid[8], lo[8];
+      float ls = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int u = tid + kAttnThreads * k;
-      *reinterpret_cast<v4i*>(vs + (u >> 4) * kVsStride + (u & 15) * 8) = vreg[k];
-    }
-    __syncthreads();
-    // softmax pieces, lane = key, folded into the running maximum and sum
+      for (int e = 0; e < 8; ++e) {
+        p[e] = m_new == -INFINITY ? 0.0f : expf(sv[e] - m_new);
+        ls = ls + p[e];
+        hi[e] = __uint_as_float(__float_as_uint(p[e]) & 0xffff0000u);
+        const float r1 = p[e] - hi[e];
+        mid[e] = __uint_as_float(__float_as_uint(r1) & 0xffff0000u);
+        lo[e] = r1 - mid[e];
+      }
+      l_part[rt] = l_part[rt] * fac + ls;
+      m_run[rt] = m_new;
 #pragma unroll
-    for (int jr = 0; jr < kRowsPerWave; ++jr) {
-      const int row = wave + jr * (kAttnThreads / kWave);
-      if (row >= R) continue;
-      const float sc = ss[row * kSsStride + lane];
-      const float new_m = fmaxf(m_run[jr], wave_max_dpp(sc));
-      const float fac = m_run[jr] == -INFINITY ? 0.0f : expf(m_run[jr] - new_m);
-      const float p = new_m == -INFINITY ? 0.0f : expf(sc - new_m);
-      l_run[jr] = l_run[jr] * fac + wave_sum_dpp(p);
-      m_run[jr] = new_m;
-      ss[row * kSsStride + lane] = p;
-      if (lane == 0) sfac[row] = fac;
-    }
-    __syncthreads();
-    // P V: rescale the running output rows, then add this chunk's keys; the two
-    // row tiles' MFMA chains interleave and share each value read
-#pragma unroll
-    for (int rt2 = 0; rt2 < kMfmaRows / 16; ++rt2)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = rt2 * 16 + grp * 4 + j;
-        o[rt2][j] = o[rt2][j] * (row < R ? sfac[row] : 0.0f);
+      for (int d = 0; d < 4; ++d) {
+        ph[rt][0][d] = (int)pack_hi16(hi[2 * d], hi[2 * d + 1]);
+        ph[rt][1][d] = (int)pack_hi16(mid[2 * d], mid[2 * d + 1]);
+        ph[rt][2][d] = (int)pack_hi16(lo[2 * d], lo[2 * d + 1]);
       }
 #pragma unroll
-    for (int kk = 0; kk < kAttnChunk / 4; ++kk) {
-      const int key = kk * 4 + grp;
-      const float vb = bf16_to_f32(vs[key * kVsStride + dcol]);
+      for (int dt = 0; dt < 8; ++dt) o[dt][rt] = o[dt][rt] * fac;
+    }
+    __syncthreads();  // this step's values are in vt
+    // A operands: V^T row dt * 16 + rl at key slots 0..7 of this lane's group
+    // (keys 4 grp .. + 3 and 16 + 4 grp .. + 3)
+    v4i va[8];
 #pragma unroll
-      for (int rt2 = 0; rt2 < kMfmaRows / 16; ++rt2) {
-        const int prow = rt2 * 16 + rl;
-        const float pa = prow < R ? ss[prow * kSsStride + key] : 0.0f;
-        o[rt2] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vb, o[rt2], 0, 0, 0);
-      }
+    for (int dt = 0; dt < 8; ++dt) {
+      const uint16_t* row = vt + (dt * 16 + rl) * kWaveVtStride + grp * 4;
+      const int2 a = *reinterpret_cast<const int2*>(row);
+      const int2 c = *reinterpret_cast<const int2*>(row + 16);
+      va[dt] = v4i{a.x, a.y, c.x, c.y};
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int part3 = 0; part3 < 3; ++part3)
+          o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(v8bf16, va[dt]), __builtin_bit_cast(v8bf16, ph[rt][part3]), o[dt][rt],
+              0, 0, 0);
     }
   }
-  // the workgroup's partials
+
+  // the wavefront's partials: row maximum, sum of exponentials, output
 #pragma unroll
-  for (int jr = 0; jr < kRowsPerWave; ++jr) {
-    const int row = wave + jr * (kAttnThreads / kWave);
-    if (row < R && lane == 0) {
-      const size_t pi = (((size_t)b * Hq + g * G + row / T) * T + row % T) * nparts + part;
-      pm[pi] = m_run[jr];
-      pl[pi] = l_run[jr];
-    }
-  }
-#pragma unroll
-  for (int rt2 = 0; rt2 < kMfmaRows / 16; ++rt2) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = rt2 * 16 + grp * 4 + j;
-      if (row < R) {
-        const size_t pi = (((size_t)b * Hq + g * G + row / T) * T + row % T) * nparts + part;
-        po[pi * kAttnD + dcol] = o[rt2][j];
+  for (int rt = 0; rt < 2; ++rt) {
+    float l = l_part[rt];
+    l = l + __shfl_xor(l, 16, kWave);
+    l = l + __shfl_xor(l, 32, kWave);
+    const int r = rt * 16 + rl;
+    if (r < R) {
+      const size_t pi = (((size_t)b * Hq + g * G + r / T) * T + r % T) * nparts + part;
+      if (grp == 0) {
+        pm[pi] = m_run[rt];
+        pl[pi] = l;
       }
+      float* dst = po + pi * kAttnD + grp * 4;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<float4*>(dst + dt * 16) =
+            make_float4(o[dt][rt][0], o[dt][rt][1], o[dt][rt][2], o[dt][rt][3]);
     }
   }
 }
 
-// One block of D threads per (token, q head): out = sum_c o_c e^(m_c - M) / sum_c l_c e^(m_c - M).
-__global__ void attn_combine_kernel(const float* __restrict__ pm, const float* __restrict__ pl,
-                                    const float* __restrict__ po, int T, int Hq, int nchunks,
-                                    uint16_t* __restrict__ out) {
-  const int m = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+// One block per (token, q head): out = sum_c o_c e^(m_c - M) / sum_c l_c e^(m_c - M)
+// over the row's partials c, M their largest maximum.  G groups of 32 threads
+// (G = blockDim.x / 32, 2 to 16: about four partials per group) take every G-th
+// partial, 4 dimensions per thread with 16-byte loads, so that a row's loads are
+// issued together; the groups' sums are then added in LDS in group order.
+constexpr int kCombMaxThreads = 512;
+constexpr int kCombMaxGroups = kCombMaxThreads / (kAttnD / 4);
+
+int attn_combine_threads(int64_t nparts) {
+  int g = 1;
+  while (g < kCombMaxGroups && 4 * g < nparts) g *= 2;
+  return std::max(g * (kAttnD / 4), kWave);
+}
+
+__global__ __launch_bounds__(kCombMaxThreads) void attn_combine_kernel(
+    const float* __restrict__ pm, const float* __restrict__ pl, const float* __restrict__ po, int T,
+    int Hq, int nparts, uint16_t* __restrict__ out) {
+  __shared__ float red[kCombMaxThreads / kWave];
+  __shared__ float4 osum[kCombMaxGroups][kAttnD / 4];
+  __shared__ float lsum[kCombMaxGroups];
+  const int m = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int nthreads = blockDim.x, ngroups = nthreads / (kAttnD / 4), nwaves = nthreads / kWave;
   const int b = m / T, i = m - b * T;
-  const size_t base = (((size_t)b * Hq + h) * T + i) * nchunks;
+  const size_t base = (((size_t)b * Hq + h) * T + i) * nparts;
   float mx = -INFINITY;
-#pragma unroll 8
-  for (int c = 0; c < nchunks; ++c) mx = fmaxf(mx, pm[base + c]);
-  float l = 0.0f, o = 0.0f;
-#pragma unroll 8
-  for (int c = 0; c < nchunks; ++c) {
+  for (int c = tid; c < nparts; c += nthreads) mx = fmaxf(mx, pm[base + c]);
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
+  if (tid % kWave == 0) red[tid / kWave] = mx;
+  __syncthreads();
+  mx = red[0];
+  for (int w = 1; w < nwaves; ++w) mx = fmaxf(mx, red[w]);
+  const int grp = tid / (kAttnD / 4), d4 = tid % (kAttnD / 4);
+  float l = 0.0f;
+  float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll 4
+  for (int c = grp; c < nparts; c += ngroups) {
     const float mc = pm[base + c];
     const float w = mc == -INFINITY ? 0.0f : expf(mc - mx);
     l = l + pl[base + c] * w;
-    o = o + po[(base + c) * kAttnD + d] * w;
+    const float4 v = *reinterpret_cast<const float4*>(po + (base + c) * kAttnD + d4 * 4);
+    o.x = o.x + v.x * w;
+    o.y = o.y + v.y * w;
+    o.z = o.z + v.z * w;
+    o.w = o.w + v.w * w;
   }
-  out[((size_t)m * Hq + h) * kAttnD + d] = (uint16_t)f32_to_bf16_rne(o / l);
+  osum[grp][d4] = o;
+  if (d4 == 0) lsum[grp] = l;
+  __syncthreads();
+  const float* os = reinterpret_cast<const float*>(&osum[0][0]);
+  for (int d = tid; d < kAttnD; d += nthreads) {
+    float acc = 0.0f, L = 0.0f;
+    for (int g2 = 0; g2 < ngroups; ++g2) {
+      acc = acc + os[g2 * kAttnD + d];
+      L = L + lsum[g2];
+    }
+    out[((size_t)m * Hq + h) * kAttnD + d] = (uint16_t)f32_to_bf16_rne(acc / L);
+  }
 }
 
 __global__ __launch_bounds__(kNormThreads) void silu_mul_kernel(const uint16_t* __restrict__ gu,
@@ -561,8 +618,18 @@ __global__ __launch_bounds__(kNormThreads) void silu_mul_kernel(const uint16_t* 
 
 int attn_chunks(int64_t pos0, int64_t T) { return (int)((pos0 + T + kAttnChunk - 1) / kAttnChunk); }
 
-size_t attn_workspace_bytes(int64_t B, int64_t T, int64_t Hq, int64_t pos0) {
-  const size_t rows = (size_t)B * Hq * T * attn_chunks(pos0, T);
+// Partials per query row: position ranges of the wavefront kernel, or 64-position
+// chunks of the vector-ALU kernel.
+static int64_t attn_parts(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t pos0) {
+  const int64_t klen = pos0 + T;
+  if ((Hq / Hkv) * T > kMfmaRows) return attn_chunks(pos0, T);
+  const int64_t steps = (klen + kWaveKeys - 1) / kWaveKeys;
+  const int spw = attn_wave_steps(B, Hkv, klen);
+  return (steps + spw - 1) / spw;
+}
+
+size_t attn_workspace_bytes(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t pos0) {
+  const size_t rows = (size_t)B * Hq * T * attn_parts(B, T, Hq, Hkv, pos0);
   return align_up(rows * 4, kWsAlign) * 2 + align_up(rows * kAttnD * 4, kWsAlign);
 }
 
@@ -602,33 +669,28 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k_cache, const ui
       attn_lds_bytes(kAttnMaxRows));
   if (attr != hipSuccess) return attr;
   const int lds = attn_lds_bytes((int)((Hq / Hkv) * T));
-  const int nch = attn_chunks(pos0, T);
-  const size_t rows = (size_t)B * Hq * T * nch;
+  const int64_t nparts = attn_parts(B, T, Hq, Hkv, pos0);
+  const size_t rows = (size_t)B * Hq * T * nparts;
   char* ws = static_cast<char*>(workspace);
   float* pm = reinterpret_cast<float*>(ws);
   float* pl = reinterpret_cast<float*>(ws + align_up(rows * 4, kWsAlign));
   float* po = reinterpret_cast<float*>(ws + 2 * align_up(rows * 4, kWsAlign));
-  int nparts = nch;
+  const float scale = 1.0f / sqrtf((float)kAttnD);
   if ((Hq / Hkv) * T <= kMfmaRows) {
-    // chunks per workgroup: one while the chunk workgroups fit the device at
-    // about four per compute unit, more (walked with a running softmax) when a
-    // batch of sequences would need several rounds of them
-    const int64_t chunk_wgs = (int64_t)nch * Hkv * B;
-    const int cpw = (int)((chunk_wgs + kAttnResidentWgs - 1) / kAttnResidentWgs);
-    nparts = (nch + cpw - 1) / cpw;
-    attn_chunk_mfma_kernel<<<dim3((unsigned)nparts, (unsigned)Hkv, (unsigned)B), dim3(kAttnThreads),
-                             0, st>>>(q, k_cache, v_cache, (int)T, (int)Hq, (int)Hkv, (int)pos0,
-                                      (int)Lmax, nparts, cpw, 1.0f / sqrtf((float)kAttnD), pm, pl,
-                                      po);
+    const int spw = attn_wave_steps(B, Hkv, pos0 + T);
+    attn_wave_kernel<<<dim3((unsigned)nparts, (unsigned)Hkv, (unsigned)B), dim3(kWave), 0, st>>>(
+        q, k_cache, v_cache, (int)T, (int)Hq, (int)Hkv, (int)pos0, (int)Lmax, (int)nparts, spw,
+        scale, pm, pl, po);
   } else {
-    attn_chunk_kernel<<<dim3((unsigned)nch, (unsigned)Hkv, (unsigned)B), dim3(kAttnThreads), lds,
+    attn_chunk_kernel<<<dim3((unsigned)nparts, (unsigned)Hkv, (unsigned)B), dim3(kAttnThreads), lds,
                         st>>>(q, k_cache, v_cache, (int)T, (int)Hq, (int)Hkv, (int)pos0, (int)Lmax,
-                              nch, 1.0f / sqrtf((float)kAttnD), pm, pl, po);
+                              (int)nparts, scale, pm, pl, po);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  attn_combine_kernel<<<dim3((unsigned)(B * T), (unsigned)Hq), dim3(kAttnD), 0, st>>>(
-      pm, pl, po, (int)T, (int)Hq, nparts, out);
+  attn_combine_kernel<<<dim3((unsigned)(B * T), (unsigned)Hq),
+                        dim3((unsigned)attn_combine_threads(nparts)), 0, st>>>(
+      pm, pl, po, (int)T, (int)Hq, (int)nparts, out);
   return hipGetLastError();
 }
 

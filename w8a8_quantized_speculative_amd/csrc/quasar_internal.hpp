@@ -141,7 +141,7 @@ hipError_t launch_accept_finalize(const AcceptPlan& p, const uint16_t* logits,
 
 // Decoder steps around the linears (decoder.hip).
 int attn_chunks(int64_t pos0, int64_t T);
-size_t attn_workspace_bytes(int64_t B, int64_t T, int64_t Hq, int64_t pos0);
+size_t attn_workspace_bytes(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t pos0);
 bool attn_supported(int64_t Hq, int64_t Hkv, int64_t D, int64_t T);
 hipError_t launch_embed(const int32_t* tok, const uint16_t* table, int64_t M, int64_t V, int64_t H,
                         float* h, hipStream_t st);

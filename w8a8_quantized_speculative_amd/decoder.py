@@ -97,7 +97,7 @@ class DecoderStep:
                      for L in layers for l in L.values())
         self.ws_lin = binding.new_workspace(lin_ws, dev)
         self.ws_att = binding.new_workspace(
-            binding.workspace_bytes_attention(B, self.T, c.heads_q, pos0), dev)
+            binding.workspace_bytes_attention(B, self.T, c.heads_q, c.heads_kv, pos0), dev)
         self.ws_head = binding.new_workspace(
             binding.workspace_bytes_lm_head_verify(B, k, c.vocab, H), dev)
 
