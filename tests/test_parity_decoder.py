@@ -158,6 +158,26 @@ def test_attention(B, pos0, T):
     assert_bf16_close(host_bf16(out).reshape(B * T, HQ, D), ref, 0.99, allow)
 
 
+# other head groupings: one query head per KV head, eight per KV head, a one-token
+# decode (T = 1), and group widths R = (Hq / Hkv) T of 1, 4, 32 (the widest the
+# matrix-core kernel takes) and 40 (the vector-ALU kernel)
+@pytest.mark.parametrize("Hq,Hkv,B,pos0,T", [(8, 8, 2, 100, 1), (8, 8, 1, 300, 4), (16, 2, 1, 95, 4),
+                                             (32, 8, 3, 33, 1), (4, 4, 2, 40, 32), (16, 4, 1, 70, 8),
+                                             (8, 1, 1, 200, 5)])
+def test_attention_head_groupings(Hq, Hkv, B, pos0, T):
+    announce("attention_groupings", Hq, Hkv, B, pos0, T)
+    Lmax = pos0 + T + 2
+    kc = bf16_normal((B, Hkv, Lmax, D), (66, Hq, Hkv, T, 0))
+    vc = bf16_normal((B, Hkv, Lmax, D), (66, Hq, Hkv, T, 1))
+    q = bf16_normal((B * T, Hq * D), (66, Hq, Hkv, T, 2), 1.5)
+    out = binding.quasar_attention(dev_bf16(q), dev_bf16(kc), dev_bf16(vc), Hq, pos0)
+    torch.cuda.synchronize()
+    qf = f32(q).reshape(B * T, Hq, D)
+    ref = dec.attention(qf, f32(kc), f32(vc), B, T, Hq, pos0)
+    allow = attention_allow(qf, f32(kc), f32(vc), B, T, Hq, pos0)
+    assert_bf16_close(host_bf16(out).reshape(B * T, Hq, D), ref, 0.99, allow)
+
+
 def test_attention_ignores_positions_past_the_window():
     """Cache positions >= pos0 + T (not yet written in a real step) never
     reach the output: filling them with large values changes nothing."""
