@@ -340,7 +340,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(
 // The partials on the matrix cores, one wavefront per range of positions, for
 // groups of at most 32 query rows (the Qwen3-8B window: 4 heads per KV head x 6
 // positions = 24).  A wavefront walks `spw` steps of 32 keys with a running
-// softmax per query row; each step
+// softmax per query row, and the four wavefronts of a workgroup (consecutive
+// ranges) merge their maxima, sums and outputs in LDS at the end, so one
+// partial per workgroup reaches memory; each step
 //   scores  S^T = K Q^T, four tiles (2 key tiles x 2 query-row tiles) of
 //           v_mfma_f32_16x16x32_bf16 over D = 128, operands straight from memory
 //           (16 contiguous bytes of a key row and of a q row per lane).  Products
@@ -368,6 +370,11 @@ constexpr int kWaveKeys = 32;
 constexpr int kWaveVtStride = 36;
 constexpr int kAttnResidentWaves = 2048;  // two wavefronts per SIMD on 256 compute units
 constexpr int kMfmaRows = 32;
+constexpr int kAttnWaves = 4;                // wavefronts per workgroup, merged before the write
+constexpr int kMergeStride = kAttnD + 4;     // floats per output row in the merge buffer
+constexpr int kAttnWaveLds =
+    std::max(kAttnWaves * kAttnD * kWaveVtStride * 2,
+             (2 * kAttnWaves * kMfmaRows + (kAttnWaves - 1) * kMfmaRows * kMergeStride) * 4);
 
 typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -384,16 +391,28 @@ __device__ __forceinline__ uint32_t pack_hi16(float a, float b) {
   return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
 }
 
-__global__ __launch_bounds__(kWave, 2) void attn_wave_kernel(
+// Orders this wavefront's LDS stores before its later LDS loads (other lanes'
+// data): LDS runs a wavefront's accesses in issue order, so only the compiler
+// must keep them in place.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__global__ __launch_bounds__(kAttnWaves * kWave, 2) void attn_wave_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
-    const uint16_t* __restrict__ v_cache, int T, int Hq, int Hkv, int pos0, int Lmax, int nparts,
-    int spw, float scale, float* __restrict__ pm, float* __restrict__ pl, float* __restrict__ po) {
-  __shared__ __align__(16) uint16_t vt[kAttnD * kWaveVtStride];
-  const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x, rl = lane & 15, grp = lane >> 4;
+    const uint16_t* __restrict__ v_cache, int T, int Hq, int Hkv, int pos0, int Lmax, int spw,
+    float scale, float* __restrict__ pm, float* __restrict__ pl, float* __restrict__ po) {
+  // per wavefront: its transposed values; after the walk, reused for the merge
+  __shared__ __align__(16) char lds[kAttnWaveLds];
+  const int part = blockIdx.x, nparts = gridDim.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x % kWave, rl = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  uint16_t* vt = reinterpret_cast<uint16_t*>(lds) + wave * kAttnD * kWaveVtStride;
   const int G = Hq / Hkv, R = G * T, klen = pos0 + T;
-  const int t_begin = part * spw * kWaveKeys;
-  const int t_end = min(t_begin + spw * kWaveKeys, klen);
+  const int t_begin = (part * kAttnWaves + wave) * spw * kWaveKeys;
+  const int t_end = min(t_begin + spw * kWaveKeys, klen);  // t_end <= t_begin: no steps
 
   // B operands of the scores: query row rt * 16 + rl of the group at D values
   // 32 kk + 8 grp .. + 7; `vis` is the last key the row sees (-1: padding row)
@@ -428,7 +447,7 @@ __global__ __launch_bounds__(kWave, 2) void attn_wave_kernel(
     for (int i = 0; i < 8; ++i)
       vr[i] = load16(vrs, ((vkey + 16 * (i & 1)) * kAttnD + (vcol8 + 4 * (i >> 1)) * 8) * 2);
   };
-  load_step(t_begin);
+  if (t_begin < t_end) load_step(t_begin);
 
   float m_run[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.0f, 0.0f};
   v4f o[8][2] = {};
@@ -445,7 +464,7 @@ __global__ __launch_bounds__(kWave, 2) void attn_wave_kernel(
               __builtin_bit_cast(v8bf16, ka[kt][kk]), __builtin_bit_cast(v8bf16, qb[rt][kk]),
               s[rt][kt], 0, 0, 0);
       }
-    __syncthreads();  // the previous step's reads of vt are done
+    wave_lds_sync();  // the previous step's reads of vt are done
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       uint16_t* dst = vt + (vcol8 + 4 * (i >> 1)) * 8 * kWaveVtStride + vkey + 16 * (i & 1);
@@ -498,7 +517,7 @@ __global__ __launch_bounds__(kWave, 2) void attn_wave_kernel(
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) o[dt][rt] = o[dt][rt] * fac;
     }
-    __syncthreads();  // this step's values are in vt
+    wave_lds_sync();  // this step's values are in vt
     // A operands: V^T row dt * 16 + rl at key slots 0..7 of this lane's group
     // (keys 4 grp .. + 3 and 16 + 4 grp .. + 3)
     v4i va[8];
@@ -521,24 +540,69 @@ __global__ __launch_bounds__(kWave, 2) void attn_wave_kernel(
     }
   }
 
-  // the wavefront's partials: row maximum, sum of exponentials, output
+  // merge the workgroup's wavefronts: a common maximum per row, each
+  // wavefront's sum and output rescaled to it; wavefronts 1.. hand theirs to
+  // wavefront 0 through LDS, which adds them in wavefront order and writes
+  float* mw = reinterpret_cast<float*>(lds);  // [waves][32] maxima
+  float* lw = mw + kAttnWaves * kMfmaRows;    // [waves][32] rescaled sums
+  float* ow = lw + kAttnWaves * kMfmaRows;    // [waves - 1][32][kMergeStride] outputs
+  float l[2], mx[2];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
-    float l = l_part[rt];
-    l = l + __shfl_xor(l, 16, kWave);
-    l = l + __shfl_xor(l, 32, kWave);
+    l[rt] = l_part[rt];
+    l[rt] = l[rt] + __shfl_xor(l[rt], 16, kWave);
+    l[rt] = l[rt] + __shfl_xor(l[rt], 32, kWave);
+  }
+  __syncthreads();  // every wavefront is done with its vt
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+    if (grp == 0) mw[wave * kMfmaRows + rt * 16 + rl] = m_run[rt];
+  __syncthreads();
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
     const int r = rt * 16 + rl;
-    if (r < R) {
-      const size_t pi = (((size_t)b * Hq + g * G + r / T) * T + r % T) * nparts + part;
-      if (grp == 0) {
-        pm[pi] = m_run[rt];
-        pl[pi] = l;
-      }
-      float* dst = po + pi * kAttnD + grp * 4;
+    mx[rt] = mw[r];
+#pragma unroll
+    for (int w = 1; w < kAttnWaves; ++w) mx[rt] = fmaxf(mx[rt], mw[w * kMfmaRows + r]);
+    const float f = m_run[rt] == -INFINITY ? 0.0f : expf(m_run[rt] - mx[rt]);
+    if (grp == 0) lw[wave * kMfmaRows + r] = l[rt] * f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt][rt] = o[dt][rt] * f;
+    if (wave > 0) {
+      float* dst = ow + ((wave - 1) * kMfmaRows + r) * kMergeStride + grp * 4;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
         *reinterpret_cast<float4*>(dst + dt * 16) =
             make_float4(o[dt][rt][0], o[dt][rt][1], o[dt][rt][2], o[dt][rt][3]);
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int r = rt * 16 + rl;
+    if (r >= R) continue;
+    const size_t pi = (((size_t)b * Hq + g * G + r / T) * T + r % T) * nparts + part;
+    if (grp == 0) {
+      float ls = lw[r];
+#pragma unroll
+      for (int w = 1; w < kAttnWaves; ++w) ls = ls + lw[w * kMfmaRows + r];
+      pm[pi] = mx[rt];
+      pl[pi] = ls;
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      float4 acc = make_float4(o[dt][rt][0], o[dt][rt][1], o[dt][rt][2], o[dt][rt][3]);
+#pragma unroll
+      for (int w = 1; w < kAttnWaves; ++w) {
+        const float4 v = *reinterpret_cast<const float4*>(
+            ow + ((w - 1) * kMfmaRows + r) * kMergeStride + grp * 4 + dt * 16);
+        acc.x = acc.x + v.x;
+        acc.y = acc.y + v.y;
+        acc.z = acc.z + v.z;
+        acc.w = acc.w + v.w;
+      }
+      *reinterpret_cast<float4*>(po + pi * kAttnD + grp * 4 + dt * 16) = acc;
     }
   }
 }
@@ -624,8 +688,9 @@ static int64_t attn_parts(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t
   const int64_t klen = pos0 + T;
   if ((Hq / Hkv) * T > kMfmaRows) return attn_chunks(pos0, T);
   const int64_t steps = (klen + kWaveKeys - 1) / kWaveKeys;
-  const int spw = attn_wave_steps(B, Hkv, klen);
-  return (steps + spw - 1) / spw;
+  const int64_t spw = attn_wave_steps(B, Hkv, klen);
+  const int64_t wave_parts = (steps + spw - 1) / spw;
+  return (wave_parts + kAttnWaves - 1) / kAttnWaves;
 }
 
 size_t attn_workspace_bytes(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t pos0) {
@@ -678,9 +743,9 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k_cache, const ui
   const float scale = 1.0f / sqrtf((float)kAttnD);
   if ((Hq / Hkv) * T <= kMfmaRows) {
     const int spw = attn_wave_steps(B, Hkv, pos0 + T);
-    attn_wave_kernel<<<dim3((unsigned)nparts, (unsigned)Hkv, (unsigned)B), dim3(kWave), 0, st>>>(
-        q, k_cache, v_cache, (int)T, (int)Hq, (int)Hkv, (int)pos0, (int)Lmax, (int)nparts, spw,
-        scale, pm, pl, po);
+    attn_wave_kernel<<<dim3((unsigned)nparts, (unsigned)Hkv, (unsigned)B), dim3(kAttnWaves * kWave),
+                       0, st>>>(q, k_cache, v_cache, (int)T, (int)Hq, (int)Hkv, (int)pos0,
+                                (int)Lmax, spw, scale, pm, pl, po);
   } else {
     attn_chunk_kernel<<<dim3((unsigned)nparts, (unsigned)Hkv, (unsigned)B), dim3(kAttnThreads), lds,
                         st>>>(q, k_cache, v_cache, (int)T, (int)Hq, (int)Hkv, (int)pos0, (int)Lmax,
