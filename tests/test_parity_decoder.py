@@ -178,6 +178,33 @@ def test_attention_head_groupings(Hq, Hkv, B, pos0, T):
     assert_bf16_close(host_bf16(out).reshape(B * T, Hq, D), ref, 0.99, allow)
 
 
+def test_attention_repeated_calls_of_different_shapes():
+    """Calls of different batch sizes and contexts in turn, each into a zeroed
+    output and reusing the library's per-call state: a repeated call must give
+    the same bits as the first, and each first call matches the oracle."""
+    announce("attention_repeats")
+    cases = [(1, 2047), (16, 130), (3, 700), (1, 2047), (16, 130)]
+    seen = {}
+    for B, pos0 in cases:
+        T = 6
+        Lmax = pos0 + T
+        kc = bf16_normal((B, HKV, Lmax, D), (67, B, pos0, 0))
+        vc = bf16_normal((B, HKV, Lmax, D), (67, B, pos0, 1))
+        q = bf16_normal((B * T, HQ * D), (67, B, pos0, 2), 1.5)
+        out = torch.zeros((B * T, HQ * D), dtype=torch.bfloat16, device="cuda")
+        binding.quasar_attention(dev_bf16(q), dev_bf16(kc), dev_bf16(vc), HQ, pos0, out=out)
+        torch.cuda.synchronize()
+        got = host_bf16(out)
+        if (B, pos0) in seen:
+            assert np.array_equal(got, seen[(B, pos0)])
+            continue
+        seen[(B, pos0)] = got
+        qf = f32(q).reshape(B * T, HQ, D)
+        ref = dec.attention(qf, f32(kc), f32(vc), B, T, HQ, pos0)
+        allow = attention_allow(qf, f32(kc), f32(vc), B, T, HQ, pos0)
+        assert_bf16_close(got.reshape(B * T, HQ, D), ref, 0.99, allow)
+
+
 def test_attention_ignores_positions_past_the_window():
     """Cache positions >= pos0 + T (not yet written in a real step) never
     reach the output: filling them with large values changes nothing."""
