@@ -96,6 +96,8 @@ class Stack:
             x = torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
             ent = dict(layer=layer, name=name, N=N, K=K, x=x, s=s_d, wq=wq, sw=sw,
                        y=torch.empty((M, N), dtype=torch.bfloat16, device="cuda"))
+            if name == "gate_up":  # the decoder step runs gate_up with SiLU fused
+                ent["wqg"], ent["swg"] = binding.quasar_quantize_weights_gated(w, s_d)
             if keep_bf16:
                 ent["w_bf16"] = w
             else:
@@ -270,9 +272,10 @@ def time_decoder_step(stack, args, linear_graph_ms: float):
     RMSNorm -> QKV -> q/k norm + RoPE + KV append -> attention over a cached
     context -> O -> residual + RMSNorm -> gate_up -> SiLU * up -> down ->
     residual, then the final RMSNorm and the LM head with greedy accept.
-    Drafts come from the N-gram drafter on synthetic histories.  Captured in
-    a HIP graph and replayed (about 365 launches per step; issued from Python
-    one by one the host would not keep up)."""
+    Drafts come from the N-gram drafter on synthetic histories.  gate_up runs
+    with silu(gate) * up in its epilogue (weights in the gated order).
+    Captured in a HIP graph and replayed (about 330 launches per step; issued
+    from Python one by one the host would not keep up)."""
     import numpy as np
     import torch
     from dataclasses import replace
@@ -284,7 +287,10 @@ def time_decoder_step(stack, args, linear_graph_ms: float):
     for e in stack.linears[:-1]:
         if e["name"] == "qkv":
             layers.append({})
-        layers[-1][e["name"]] = Linear(e["wq"], e["sw"], e["s"], e["N"], e["K"])
+        if e["name"] == "gate_up":
+            layers[-1][e["name"]] = Linear(e["wqg"], e["swg"], e["s"], e["N"], e["K"], gated=True)
+        else:
+            layers[-1][e["name"]] = Linear(e["wq"], e["sw"], e["s"], e["N"], e["K"])
     lm = stack.linears[-1]
     g = torch.Generator(device="cuda")
     g.manual_seed(12345)

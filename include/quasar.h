@@ -103,6 +103,18 @@ quasar_status quasar_quantize_weights(const uint16_t* w, const float* s, int64_t
                                       int8_t* wq, float* w_scale, void* stream);
 
 /*
+ * quasar_quantize_weights_gated -- quasar_quantize_weights for the stacked
+ * gate and up projections of a gated MLP, w = [W_gate; W_up] ([2I, K]), with
+ * the rows stored in the gated order that quasar_w8a8_linear_swiglu expects:
+ * packed row 16t + i is gate row 8t + i for i < 8 and up row 8t + i - 8
+ * otherwise; w_scale follows the packed rows.  Each row is quantized exactly
+ * as by quasar_quantize_weights.  N = 2I, N % 16 == 0; other arguments and
+ * errors as there.
+ */
+quasar_status quasar_quantize_weights_gated(const uint16_t* w, const float* s, int64_t N,
+                                            int64_t K, int8_t* wq, float* w_scale, void* stream);
+
+/*
  * quasar_quantize_activations -- the online half of one linear, on its own.
  *
  * BF16 activations are smoothed by diag(s) and quantized dynamically, one
@@ -393,6 +405,30 @@ quasar_status quasar_attention(const uint16_t* q, const uint16_t* k_cache,
                                const uint16_t* v_cache, int64_t B, int64_t T, int64_t Hq,
                                int64_t Hkv, int64_t D, int64_t pos0, int64_t Lmax, uint16_t* out,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of quasar_w8a8_linear_swiglu (0 when it needs none or for
+ * invalid sizes). */
+size_t quasar_w8a8_linear_swiglu_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * quasar_w8a8_linear_swiglu -- the gate_up W8A8 linear followed by the gated
+ * MLP's activation, act = silu(gate) * up, for weights from
+ * quasar_quantize_weights_gated.  The result equals quasar_w8a8_linear on the
+ * same rows in [gate | up] order followed by quasar_silu_mul, bit for bit.
+ * Windows of M <= 8 tokens with K <= 12288 run as one launch (the linear's
+ * epilogue applies the activation: no [M, N] product is written); other shapes
+ * run the wide linear into the workspace, then the activation.
+ *   x, s, wq, w_scale, M, K  as for quasar_w8a8_linear
+ *   N        2I, the product's width; N % 16 == 0
+ *   act      [M, N / 2] bf16, 8-byte aligned (out)
+ *   workspace  quasar_w8a8_linear_swiglu_workspace_bytes(M, N, K) bytes,
+ *            256-byte aligned (may be NULL when that is 0)
+ * Errors as quasar_w8a8_linear; INVALID_ARG for N % 16 != 0.
+ */
+quasar_status quasar_w8a8_linear_swiglu(const uint16_t* x, const float* s, const int8_t* wq,
+                                        const float* w_scale, int64_t M, int64_t N, int64_t K,
+                                        uint16_t* act, void* workspace, size_t workspace_bytes,
+                                        void* stream);
 
 /*
  * quasar_silu_mul -- the MLP activation between gate_up and down:

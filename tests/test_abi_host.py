@@ -52,7 +52,7 @@ def test_status_strings(L):
     for code in range(5):
         assert L.quasar_status_string(code).decode().startswith("QUASAR_")
     assert b"UNKNOWN" in L.quasar_status_string(99)
-    assert L.quasar_abi_version() == 8
+    assert L.quasar_abi_version() == 9
 
 
 def test_workspace_queries_are_pure_host_and_monotone(L):

@@ -10,9 +10,12 @@ error bound, nearly all elements identical), and the accept decision exact
 on the GPU's logits.
 Two windows: one sequence (6 tokens: the one-launch linear) and two
 sequences (12 tokens: the wide linear), with a 70-position cached context that
-crosses an attention chunk edge; and one layer at Qwen3-8B's dimensions (hidden
-4096, 32 / 8 heads, intermediate 12288) over a 2048-position context.  The drafts
-come from the N-gram drafter on a synthetic history.
+crosses an attention step edge; and one layer at Qwen3-8B's dimensions (hidden
+4096, 32 / 8 heads, intermediate 12288) over a 2048-position context.  Each runs
+twice: gate_up then SiLU as two calls, and gate_up in the gated order with SiLU
+applied in the linear's epilogue (6 tokens) or by the gated SiLU kernel (12
+tokens), where the activation is checked against the oracle linear of the GPU's
+input.  The drafts come from the N-gram drafter on a synthetic history.
 """
 import numpy as np
 import pytest
@@ -37,21 +40,24 @@ QWEN3_LAYER = DecoderConfig(hidden=4096, heads_q=32, heads_kv=8, head_dim=128, i
                             layers=1, vocab=1000)
 
 
-def make_linear(N, K, key):
+def make_linear(N, K, key, gated=False):
     w = synth.weights(N, K, key)
     prof = synth.activations(64, K, key + (9,))
     s = synth.smoothing_vector(synth.col_absmax_bf16(prof), synth.col_absmax_bf16(w))
-    wq, sw = binding.quasar_quantize_weights(dev_bf16(w), dev(s))
-    return Linear(wq, sw, dev(s), N, K), (w, s)
+    pack = binding.quasar_quantize_weights_gated if gated else binding.quasar_quantize_weights
+    wq, sw = pack(dev_bf16(w), dev(s))
+    return Linear(wq, sw, dev(s), N, K, gated=gated), (w, s)
 
 
 def bits(t):
     return host_bf16(t)
 
 
-@pytest.mark.parametrize("cfg_name,B,pos0", [("small", 1, 70), ("small", 2, 70),
-                                              ("qwen3_layer", 1, 2048)])
-def test_decoder_step_link_by_link(cfg_name, B, pos0):
+@pytest.mark.parametrize("cfg_name,B,pos0,gated", [("small", 1, 70, False), ("small", 2, 70, False),
+                                                    ("qwen3_layer", 1, 2048, False),
+                                                    ("small", 1, 70, True), ("small", 2, 70, True),
+                                                    ("qwen3_layer", 1, 2048, True)])
+def test_decoder_step_link_by_link(cfg_name, B, pos0, gated):
     c = CFG if cfg_name == "small" else QWEN3_LAYER
     k = 5
     T = k + 1
@@ -63,7 +69,8 @@ def test_decoder_step_link_by_link(cfg_name, B, pos0):
         L, Lh = {}, {}
         for name, N, K in (("qkv", qkv_n, H), ("o", H, c.heads_q * D), ("gate_up", 2 * I, H),
                            ("down", H, I)):
-            L[name], Lh[name] = make_linear(N, K, (70, B, li, len(L)))
+            L[name], Lh[name] = make_linear(N, K, (70, B, li, len(L)),
+                                            gated=gated and name == "gate_up")
         layers.append(L)
         host_w.append(Lh)
     lm, lm_host = make_linear(c.vocab, H, (70, B, 99))
@@ -119,8 +126,13 @@ def test_decoder_step_link_by_link(cfg_name, B, pos0):
         assert np.array_equal(host(rec["h_before_down"][li]), h)
         ref = dec.rmsnorm(h, g["post"][li], c.eps)[1]
         assert_bf16_close(bits(rec["x_mlp_in"][li]), ref, 0.99, (H + 8) * U * np.abs(ref))
-        lin_check(rec["x_mlp_in"][li], rec["gu"][li], Lh["gate_up"])
-        gu = orc.bf16_to_f32(bits(rec["gu"][li])).astype(np.float64)
+        if gated:  # no product is written: the oracle linear of the GPU's input
+            gu_bits = orc.w8a8_linear_rows(bits(rec["x_mlp_in"][li]), Lh["gate_up"][1],
+                                           Lh["gate_up"][0])["y"]
+        else:
+            lin_check(rec["x_mlp_in"][li], rec["gu"][li], Lh["gate_up"])
+            gu_bits = bits(rec["gu"][li])
+        gu = orc.bf16_to_f32(gu_bits).astype(np.float64)
         ref = dec.silu_mul(gu)
         assert_bf16_close(bits(rec["act"][li]), ref, 0.99, 8 * U * np.abs(ref))
         lin_check(rec["act"][li], rec["dn"][li], Lh["down"])

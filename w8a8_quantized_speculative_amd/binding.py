@@ -35,6 +35,10 @@ _SIGNATURES = {
     "quasar_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "quasar_abi_version": (ctypes.c_int, []),
     "quasar_quantize_weights": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P]),
+    "quasar_quantize_weights_gated": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P]),
+    "quasar_w8a8_linear_swiglu_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "quasar_w8a8_linear_swiglu": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ,
+                                                 _P]),
     "quasar_quantize_activations": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P, _P]),
     "quasar_packed_weight_bytes": (_SZ, [_I64, _I64]),
     "quasar_w8a8_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
@@ -171,6 +175,21 @@ def quasar_quantize_weights(w: torch.Tensor, s: torch.Tensor):
     return wq, sw
 
 
+def quasar_quantize_weights_gated(w: torch.Tensor, s: torch.Tensor):
+    """[W_gate; W_up] [2I, K] bf16, s [K] f32 -> (PackedWeights in the gated row
+    order, w_scale f32 [2I] in that order), for quasar_w8a8_linear_swiglu."""
+    N, K = w.shape
+    _need(w, torch.bfloat16, (N, K), "w")
+    _need(s, torch.float32, (K,), "s")
+    nbytes = packed_weight_bytes(N, K) if N > 0 else 0
+    codes = torch.empty((max(nbytes, 16),), dtype=torch.int8, device=w.device)
+    wq = PackedWeights(codes, N, K)
+    sw = torch.empty((N,), dtype=torch.float32, device=w.device)
+    _check("quasar_quantize_weights_gated", lib().quasar_quantize_weights_gated(
+        _ptr(w), _ptr(s), N, K, _ptr(wq), _ptr(sw), _stream()))
+    return wq, sw
+
+
 def quasar_quantize_activations(x: torch.Tensor, s: torch.Tensor, want_xs: bool = False):
     """X [M, K] bf16 -> (qx int8 [M, K], x_scale f32 [M], xs f32 [M, K] or None)."""
     M, K = x.shape
@@ -207,6 +226,35 @@ def quasar_w8a8_linear(x: torch.Tensor, s: torch.Tensor, wq: PackedWeights, w_sc
     _check("quasar_w8a8_linear", lib().quasar_w8a8_linear(
         _ptr(x), _ptr(s), _ptr(wq), _ptr(w_scale), M, N, K, _ptr(out), _ptr(acc_out),
         _ptr(workspace), nbytes, _stream()))
+    return out
+
+
+def workspace_bytes_linear_swiglu(M: int, N: int, K: int) -> int:
+    return int(lib().quasar_w8a8_linear_swiglu_workspace_bytes(M, N, K))
+
+
+def quasar_w8a8_linear_swiglu(x: torch.Tensor, s: torch.Tensor, wq: PackedWeights,
+                              w_scale: torch.Tensor, out: torch.Tensor | None = None,
+                              workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """act [M, N/2] bf16 = silu(gate) * up of the gate_up linear, for weights from
+    quasar_quantize_weights_gated."""
+    M, K = x.shape
+    N = wq.N
+    if not isinstance(wq, PackedWeights) or wq.K != K or wq.bits != 8:
+        raise ValueError("wq must be the INT8 PackedWeights of a linear with the same K")
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(s, torch.float32, (K,), "s")
+    _need(w_scale, torch.float32, (N,), "w_scale")
+    if out is None:
+        out = torch.empty((M, N // 2), dtype=torch.bfloat16, device=x.device)
+    _need(out, torch.bfloat16, (M, N // 2), "out")
+    need = workspace_bytes_linear_swiglu(M, N, K)
+    if workspace is None and need > 0:
+        workspace = new_workspace(need, x.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("quasar_w8a8_linear_swiglu", lib().quasar_w8a8_linear_swiglu(
+        _ptr(x), _ptr(s), _ptr(wq), _ptr(w_scale), M, N, K, _ptr(out), _ptr(workspace), nbytes,
+        _stream()))
     return out
 
 

@@ -85,7 +85,7 @@ const char* quasar_status_string(quasar_status status) {
   return "QUASAR_ERR_UNKNOWN";
 }
 
-int quasar_abi_version(void) { return 8; }
+int quasar_abi_version(void) { return 9; }
 
 quasar_status quasar_quantize_weights(const uint16_t* w, const float* s, int64_t N, int64_t K,
                                       int8_t* wq, float* w_scale, void* stream) {
@@ -98,6 +98,20 @@ quasar_status quasar_quantize_weights(const uint16_t* w, const float* s, int64_t
   if (!aligned(w, 16) || !aligned(s, 16) || !aligned(wq, 16) || !aligned(w_scale, 4))
     return QUASAR_ERR_INVALID_ARG;
   return hip_status(launch_quantize_weights(w, s, N, K, wq, w_scale, (hipStream_t)stream));
+}
+
+quasar_status quasar_quantize_weights_gated(const uint16_t* w, const float* s, int64_t N,
+                                            int64_t K, int8_t* wq, float* w_scale, void* stream) {
+  if (N < 0 || N % 16 != 0) return QUASAR_ERR_INVALID_ARG;
+  quasar_status st = check_k(K);
+  if (st != QUASAR_OK) return st;
+  if (N > kMaxRowsPerCall) return QUASAR_ERR_UNSUPPORTED;
+  if (N == 0) return QUASAR_OK;
+  if (!w || !s || !wq || !w_scale) return QUASAR_ERR_INVALID_ARG;
+  if (!aligned(w, 16) || !aligned(s, 16) || !aligned(wq, 16) || !aligned(w_scale, 4))
+    return QUASAR_ERR_INVALID_ARG;
+  return hip_status(
+      launch_quantize_weights(w, s, N, K, wq, w_scale, (hipStream_t)stream, /*gated=*/true));
 }
 
 quasar_status quasar_quantize_activations(const uint16_t* x, const float* s, int64_t M, int64_t K,
@@ -164,6 +178,46 @@ quasar_status quasar_w8a8_linear(const uint16_t* x, const float* s, const int8_t
   p.grid = wide_grid_for_current_device();
   if (p.grid < M) return QUASAR_ERR_UNSUPPORTED;  // one resident workgroup per token row
   return hip_status(launch_wide(p, x, s, wq, w_scale, y, acc_out, workspace, hs));
+}
+
+size_t quasar_w8a8_linear_swiglu_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || N % 16 != 0 || check_k(K) != QUASAR_OK || M > QUASAR_MAX_M ||
+      N > kMaxRowsPerCall)
+    return 0;
+  if (fused_supported(M, K)) return 0;
+  // the wide kernel's workspace, then the gated product [M, N] BF16
+  return align_up(plan_wide(M, N, K, kWideMaxGrid).bytes, kWsAlign) +
+         align_up((size_t)M * N * 2, kWsAlign);
+}
+
+quasar_status quasar_w8a8_linear_swiglu(const uint16_t* x, const float* s, const int8_t* wq,
+                                        const float* w_scale, int64_t M, int64_t N, int64_t K,
+                                        uint16_t* act, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  if (M < 0 || N < 0 || N % 16 != 0) return QUASAR_ERR_INVALID_ARG;
+  quasar_status st = check_k(K);
+  if (st != QUASAR_OK) return st;
+  if (M > QUASAR_MAX_M || N > kMaxRowsPerCall) return QUASAR_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return QUASAR_OK;
+  if (!x || !s || !wq || !w_scale || !act) return QUASAR_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(s, 16) || !aligned(wq, 16) || !aligned(w_scale, 4) ||
+      !aligned(act, 8))
+    return QUASAR_ERR_INVALID_ARG;
+  hipStream_t hs = (hipStream_t)stream;
+  if (fused_supported(M, K))  // one launch: the product's epilogue applies silu(gate) * up
+    return hip_status(launch_fused(plan_fused(M, N, K), x, s, wq, w_scale, act, nullptr, hs,
+                                   nullptr, /*swiglu=*/true));
+  WidePlan p = plan_wide(M, N, K, kWideMaxGrid);
+  const size_t lin = align_up(p.bytes, kWsAlign);
+  if (!workspace || workspace_bytes < lin + align_up((size_t)M * N * 2, kWsAlign) ||
+      !aligned(workspace, kWsAlign))
+    return QUASAR_ERR_WORKSPACE;
+  p.grid = wide_grid_for_current_device();
+  if (p.grid < M) return QUASAR_ERR_UNSUPPORTED;
+  uint16_t* gu = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + lin);
+  hipError_t e = launch_wide(p, x, s, wq, w_scale, gu, nullptr, workspace, hs);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(launch_silu_mul_gated(gu, M, N / 2, act, hs));
 }
 
 size_t quasar_accept_workspace_bytes(int64_t B, int64_t k, int64_t V) {

@@ -667,13 +667,18 @@ __global__ __launch_bounds__(kCombMaxThreads) void attn_combine_kernel(
   }
 }
 
+// kGated: the columns of gu are in the gated order (16-column tiles of 8 gate
+// then 8 up columns) instead of [gate | up].
+template <bool kGated>
 __global__ __launch_bounds__(kNormThreads) void silu_mul_kernel(const uint16_t* __restrict__ gu,
                                                                 int I, uint16_t* __restrict__ out) {
   const int m = blockIdx.y;
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= I) return;
-  const float g = bf16_to_f32(gu[(size_t)m * 2 * I + j]);
-  const float u = bf16_to_f32(gu[(size_t)m * 2 * I + I + j]);
+  const int gc = kGated ? (j >> 3) * 16 + (j & 7) : j;
+  const int uc = kGated ? gc + 8 : I + j;
+  const float g = bf16_to_f32(gu[(size_t)m * 2 * I + gc]);
+  const float u = bf16_to_f32(gu[(size_t)m * 2 * I + uc]);
   const float s = g / (1.0f + expf(-g));
   out[(size_t)m * I + j] = (uint16_t)f32_to_bf16_rne(s * u);
 }
@@ -760,8 +765,15 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k_cache, const ui
 }
 
 hipError_t launch_silu_mul(const uint16_t* gu, int64_t M, int64_t I, uint16_t* out, hipStream_t st) {
-  silu_mul_kernel<<<dim3((unsigned)((I + kNormThreads - 1) / kNormThreads), (unsigned)M),
-                    dim3(kNormThreads), 0, st>>>(gu, (int)I, out);
+  silu_mul_kernel<false><<<dim3((unsigned)((I + kNormThreads - 1) / kNormThreads), (unsigned)M),
+                           dim3(kNormThreads), 0, st>>>(gu, (int)I, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_mul_gated(const uint16_t* gu, int64_t M, int64_t I, uint16_t* out,
+                                 hipStream_t st) {
+  silu_mul_kernel<true><<<dim3((unsigned)((I + kNormThreads - 1) / kNormThreads), (unsigned)M),
+                          dim3(kNormThreads), 0, st>>>(gu, (int)I, out);
   return hipGetLastError();
 }
 

@@ -244,7 +244,7 @@ __device__ __forceinline__ void helper(const uint16_t* __restrict__ x, const flo
                                        int8_t* codes, int Ks, const int32_t* red, const float* wsl,
                                        float* amax_part, float* qp, int* cnt, int* ready,
                                        uint16_t* __restrict__ y, int32_t* __restrict__ acc_out,
-                                       AcceptPartials ap, int G) {
+                                       AcceptPartials ap, int G, int swiglu) {
   constexpr int HT = 64 * NH;  // helper threads
   const int units = K >> 3;    // pieces of 8 K positions per token row
   v4i xv[UP][MT];
@@ -401,6 +401,29 @@ __device__ __forceinline__ void helper(const uint16_t* __restrict__ x, const flo
           v = v * wsl[buf * 16 + 4 * (ht >> 4) + i];
           o[i] = f32_to_bf16_rne(v);
         }
+        if (swiglu) {
+          // gated weight order: channels 0..7 of the tile are the gate and 8..15
+          // the up projections of outputs 8 tile .. + 7; the up values of this
+          // thread's 4 outputs sit 32 lanes on.  silu(g) u as quasar_silu_mul:
+          // BF16 g and u, binary32 arithmetic, one BF16 rounding.
+          uint32_t up[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) up[i] = (uint32_t)__shfl_xor((int)o[i], 32, kWave);
+          if ((ht >> 4) < 2) {
+            uint32_t a[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float g = bf16_to_f32(o[i]), u = bf16_to_f32(up[i]);
+              const float sg = g / (1.0f + expf(-g));
+              a[i] = f32_to_bf16_rne(sg * u);
+            }
+            uint2 pk;
+            pk.x = a[0] | (a[1] << 16);
+            pk.y = a[2] | (a[3] << 16);
+            *reinterpret_cast<uint2*>(y + (size_t)tt * (N / 2) + tile * 8 + 4 * (ht >> 4)) = pk;
+          }
+          continue;
+        }
         uint16_t* yr = y + (size_t)tt * N;
         if (n0 + 3 < N && ((reinterpret_cast<uintptr_t>(yr + n0) & 7) == 0)) {
           uint2 pk;
@@ -448,7 +471,7 @@ template <int MT, int S, int NPH>
 __global__ __launch_bounds__(64 * (S + (NPH == 2 ? 4 : 8))) void w8a8_linear_fused_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ s, const int8_t* __restrict__ wq,
     const float* __restrict__ wscale, int M, int N, int K, int tq, int tr, int G,
-    uint16_t* __restrict__ y, int32_t* __restrict__ acc_out, AcceptPartials ap) {
+    uint16_t* __restrict__ y, int32_t* __restrict__ acc_out, AcceptPartials ap, int swiglu) {
   using Var = Variant<NPH == 2 ? 0 : (NPH == 4 ? 1 : 2)>;
   static_assert(Var::S == S && Var::NPH == NPH, "variant");
   extern __shared__ __align__(16) char smem[];
@@ -478,7 +501,8 @@ __global__ __launch_bounds__(64 * (S + (NPH == 2 ? 4 : 8))) void w8a8_linear_fus
                                              red, wsl, ready);
   } else {
     helper<MT, S, Var::NH, Var::UP>(x, s, M, N, K, first, T, tid - 64 * S, wave - S, lane, codes,
-                                    Ks, red, wsl, amax_part, qp, cnt, ready, y, acc_out, ap, G);
+                                    Ks, red, wsl, amax_part, qp, cnt, ready, y, acc_out, ap, G,
+                                    swiglu);
   }
 }
 
@@ -620,7 +644,7 @@ __global__ __launch_bounds__(64 * (S + (NPH4 == 1 ? 4 : 8))) void w4a8_linear_fu
   } else {
     helper<MT, S, Var::NH, Var::UP, 4>(x, s, M, N, K, first, T, tid - 64 * S, wave - S, lane,
                                        codes, Ks, red, wsl, amax_part, qp, cnt, ready, y, acc_out,
-                                       AcceptPartials{nullptr, nullptr, nullptr, 0.0f}, G);
+                                       AcceptPartials{nullptr, nullptr, nullptr, 0.0f}, G, 0);
   }
 }
 
@@ -653,7 +677,7 @@ hipError_t launch_w4_mt(const FusedPlan& p, const uint16_t* x, const float* s, c
 template <int MT, int V>
 hipError_t launch_variant(const FusedPlan& p, const uint16_t* x, const float* s, const int8_t* wq,
                           const float* w_scale, uint16_t* y, int32_t* acc_out, hipStream_t st,
-                          const AcceptPartials& ap) {
+                          const AcceptPartials& ap, int swiglu) {
   using Var = Variant<V>;
   auto kernel = &w8a8_linear_fused_kernel<MT, Var::S, Var::NPH>;
   static const hipError_t attr =
@@ -663,18 +687,18 @@ hipError_t launch_variant(const FusedPlan& p, const uint16_t* x, const float* s,
   if (attr != hipSuccess) return attr;
   kernel<<<dim3(p.grid), dim3(64 * Var::WAVES), p.lds, st>>>(
       x, s, wq, w_scale, (int)p.M, (int)p.N, (int)p.K, p.tiles / p.grid, p.tiles % p.grid, p.grid,
-      y, acc_out, ap);
+      y, acc_out, ap, swiglu);
   return hipGetLastError();
 }
 
 template <int MT>
 hipError_t launch_mt(const FusedPlan& p, const uint16_t* x, const float* s, const int8_t* wq,
                      const float* w_scale, uint16_t* y, int32_t* acc_out, hipStream_t st,
-                     const AcceptPartials& ap) {
+                     const AcceptPartials& ap, int swiglu) {
   switch (p.variant) {
-    case 0: return launch_variant<MT, 0>(p, x, s, wq, w_scale, y, acc_out, st, ap);
-    case 1: return launch_variant<MT, 1>(p, x, s, wq, w_scale, y, acc_out, st, ap);
-    default: return launch_variant<MT, 2>(p, x, s, wq, w_scale, y, acc_out, st, ap);
+    case 0: return launch_variant<MT, 0>(p, x, s, wq, w_scale, y, acc_out, st, ap, swiglu);
+    case 1: return launch_variant<MT, 1>(p, x, s, wq, w_scale, y, acc_out, st, ap, swiglu);
+    default: return launch_variant<MT, 2>(p, x, s, wq, w_scale, y, acc_out, st, ap, swiglu);
   }
 }
 
@@ -747,13 +771,14 @@ const char* fused_kernel_name(const FusedPlan& p) {
 
 hipError_t launch_fused(const FusedPlan& p, const uint16_t* x, const float* s, const int8_t* wq,
                         const float* w_scale, uint16_t* y, int32_t* acc_out, hipStream_t st,
-                        const AcceptPartials* partials) {
+                        const AcceptPartials* partials, bool swiglu) {
   const AcceptPartials ap = partials ? *partials : AcceptPartials{nullptr, nullptr, nullptr, 0.0f};
+  const int sw = swiglu ? 1 : 0;
   switch (p.mt) {
-    case 2: return launch_mt<2>(p, x, s, wq, w_scale, y, acc_out, st, ap);
-    case 4: return launch_mt<4>(p, x, s, wq, w_scale, y, acc_out, st, ap);
-    case 6: return launch_mt<6>(p, x, s, wq, w_scale, y, acc_out, st, ap);
-    default: return launch_mt<8>(p, x, s, wq, w_scale, y, acc_out, st, ap);
+    case 2: return launch_mt<2>(p, x, s, wq, w_scale, y, acc_out, st, ap, sw);
+    case 4: return launch_mt<4>(p, x, s, wq, w_scale, y, acc_out, st, ap, sw);
+    case 6: return launch_mt<6>(p, x, s, wq, w_scale, y, acc_out, st, ap, sw);
+    default: return launch_mt<8>(p, x, s, wq, w_scale, y, acc_out, st, ap, sw);
   }
 }
 

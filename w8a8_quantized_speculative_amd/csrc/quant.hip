@@ -61,16 +61,27 @@ __device__ __forceinline__ void zero_k_padding(int8_t* __restrict__ wq, int64_t 
     *reinterpret_cast<uint4*>(wq + packed_offset(row, k, nch)) = make_uint4(0, 0, 0, 0);
 }
 
+// Row of the source matrix behind output row `row`.  In the gated order
+// (gated_half = I > 0, the rows of a [gate; up] matrix of 2I rows), output rows
+// 16 t .. 16 t + 7 are gate rows 8 t .. 8 t + 7 and 16 t + 8 .. 16 t + 15 are up
+// rows 8 t .. 8 t + 7, so one 16-channel tile holds both factors of 8 outputs.
+__device__ __forceinline__ int64_t source_row(int64_t row, int64_t gated_half) {
+  if (gated_half == 0) return row;
+  const int64_t t = row >> 4, i = row & 15;
+  return (i < 8 ? 0 : gated_half) + t * 8 + (i & 7);
+}
+
 // Register-resident variant: the smoothed row stays in registers between the
 // absmax pass and the quantize pass (K <= kUPT * 256 * 8).
 template <bool kWeights, int kUPT>
 __global__ __launch_bounds__(kRowThreads) void quantize_rows_reg_kernel(
     const uint16_t* __restrict__ src, const float* __restrict__ s, int64_t K,
-    int8_t* __restrict__ codes, float* __restrict__ scales, float* __restrict__ xs_out) {
+    int8_t* __restrict__ codes, float* __restrict__ scales, float* __restrict__ xs_out,
+    int64_t gated_half) {
   __shared__ float red[kRowThreads / kWave];
   const int64_t row = blockIdx.x;
   const int64_t units = K / 8;
-  const uint16_t* xr = src + row * K;
+  const uint16_t* xr = src + source_row(row, gated_half) * K;
   float v[kUPT][8];
   float amax = 0.0f;
 #pragma unroll
@@ -100,11 +111,12 @@ __global__ __launch_bounds__(kRowThreads) void quantize_rows_reg_kernel(
 template <bool kWeights>
 __global__ __launch_bounds__(kRowThreads) void quantize_rows_stream_kernel(
     const uint16_t* __restrict__ src, const float* __restrict__ s, int64_t K,
-    int8_t* __restrict__ codes, float* __restrict__ scales, float* __restrict__ xs_out) {
+    int8_t* __restrict__ codes, float* __restrict__ scales, float* __restrict__ xs_out,
+    int64_t gated_half) {
   __shared__ float red[kRowThreads / kWave];
   const int64_t row = blockIdx.x;
   const int64_t units = K / 8;
-  const uint16_t* xr = src + row * K;
+  const uint16_t* xr = src + source_row(row, gated_half) * K;
   float amax = 0.0f;
   for (int64_t q = threadIdx.x; q < units; q += kRowThreads) {
     float v[8];
@@ -189,28 +201,33 @@ __global__ __launch_bounds__(kRowThreads) void zero_pad_rows_w4_kernel(int8_t* _
 
 template <bool kWeights>
 hipError_t launch_rows(const uint16_t* src, const float* s, int64_t rows, int64_t K, int8_t* codes,
-                       float* scales, float* xs_out, hipStream_t st) {
+                       float* scales, float* xs_out, hipStream_t st, int64_t gated_half = 0) {
   if (rows == 0) return hipSuccess;
   const dim3 grid((unsigned)rows), block(kRowThreads);
   const int64_t upt = (K / 8 + kRowThreads - 1) / kRowThreads;
   if (upt <= 1)
-    quantize_rows_reg_kernel<kWeights, 1><<<grid, block, 0, st>>>(src, s, K, codes, scales, xs_out);
+    quantize_rows_reg_kernel<kWeights, 1><<<grid, block, 0, st>>>(src, s, K, codes, scales, xs_out,
+                                                               gated_half);
   else if (upt <= 2)
-    quantize_rows_reg_kernel<kWeights, 2><<<grid, block, 0, st>>>(src, s, K, codes, scales, xs_out);
+    quantize_rows_reg_kernel<kWeights, 2><<<grid, block, 0, st>>>(src, s, K, codes, scales, xs_out,
+                                                               gated_half);
   else if (upt <= 4)
-    quantize_rows_reg_kernel<kWeights, 4><<<grid, block, 0, st>>>(src, s, K, codes, scales, xs_out);
+    quantize_rows_reg_kernel<kWeights, 4><<<grid, block, 0, st>>>(src, s, K, codes, scales, xs_out,
+                                                               gated_half);
   else if (upt <= 8)
-    quantize_rows_reg_kernel<kWeights, 8><<<grid, block, 0, st>>>(src, s, K, codes, scales, xs_out);
+    quantize_rows_reg_kernel<kWeights, 8><<<grid, block, 0, st>>>(src, s, K, codes, scales, xs_out,
+                                                               gated_half);
   else
-    quantize_rows_stream_kernel<kWeights><<<grid, block, 0, st>>>(src, s, K, codes, scales, xs_out);
+    quantize_rows_stream_kernel<kWeights><<<grid, block, 0, st>>>(src, s, K, codes, scales, xs_out,
+                                                               gated_half);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_quantize_weights(const uint16_t* w, const float* s, int64_t N, int64_t K,
-                                   int8_t* wq, float* w_scale, hipStream_t st) {
-  hipError_t e = launch_rows<true>(w, s, N, K, wq, w_scale, nullptr, st);
+                                   int8_t* wq, float* w_scale, hipStream_t st, bool gated) {
+  hipError_t e = launch_rows<true>(w, s, N, K, wq, w_scale, nullptr, st, gated ? N / 2 : 0);
   const int64_t pad_rows = (N + 15) / 16 * 16 - N;
   if (e != hipSuccess || pad_rows == 0) return e;
   zero_pad_rows_kernel<<<dim3((unsigned)pad_rows), dim3(kRowThreads), 0, st>>>(wq, N, (K + 63) / 64);

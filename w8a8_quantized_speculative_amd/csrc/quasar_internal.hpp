@@ -59,9 +59,11 @@ hipError_t launch_fused_w4(const FusedPlan& p, const uint16_t* x, const float* s
 // Name of the kernel of a one-launch plan (static storage).
 const char* fused_kernel_name(const FusedPlan& p);
 FusedPlan plan_fused(int64_t M, int64_t N, int64_t K);
+// swiglu: the weights are in the gated order and y receives silu(gate) * up,
+// [M, N / 2] (N % 16 == 0, no partials)
 hipError_t launch_fused(const FusedPlan& p, const uint16_t* x, const float* s, const int8_t* wq,
                         const float* w_scale, uint16_t* y, int32_t* acc_out, hipStream_t st,
-                        const AcceptPartials* partials = nullptr);
+                        const AcceptPartials* partials = nullptr, bool swiglu = false);
 
 // ---------------------------------------------------------------------------
 // Wide-window plan (9 <= M <= 128, or K > 12288): one launch of a persistent
@@ -118,8 +120,10 @@ AcceptPlan plan_accept(int64_t B, int64_t k, int64_t V);
 // ---------------------------------------------------------------------------
 // Launchers (return the hipError_t of the launch).
 // ---------------------------------------------------------------------------
+// gated: the rows of a [gate; up] matrix (N = 2I) in the gated order (packed
+// row 16 t + i is gate row 8 t + i for i < 8, up row 8 t + i - 8 otherwise)
 hipError_t launch_quantize_weights(const uint16_t* w, const float* s, int64_t N, int64_t K,
-                                   int8_t* wq, float* w_scale, hipStream_t st);
+                                   int8_t* wq, float* w_scale, hipStream_t st, bool gated = false);
 
 hipError_t launch_quantize_weights_w4(const uint16_t* w, const float* s, int64_t N, int64_t K,
                                       int8_t* wq4, float* w_scale, hipStream_t st);
@@ -155,6 +159,9 @@ hipError_t launch_qk_rope_cache(const uint16_t* qkv, const float* q_gamma, const
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
                             int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t pos0, int64_t Lmax,
                             uint16_t* out, void* workspace, hipStream_t st);
+// silu(gate) * up from a [M, 2I] product whose columns are in the gated order
+hipError_t launch_silu_mul_gated(const uint16_t* gu, int64_t M, int64_t I, uint16_t* out,
+                                 hipStream_t st);
 hipError_t launch_silu_mul(const uint16_t* gu, int64_t M, int64_t I, uint16_t* out, hipStream_t st);
 
 // Diagnostic plain copy (16-byte vectors), bytes % 16 == 0.

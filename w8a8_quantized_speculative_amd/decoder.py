@@ -6,7 +6,8 @@ embedding of the last accepted token and the k drafts, then per layer
 
     x = RMSNorm(h)                  -> QKV (W8A8) -> q/k norm, RoPE, KV append
       -> attention over the cache   -> O (W8A8)   -> h += o
-    x = RMSNorm(h)                  -> gate_up (W8A8) -> silu(gate) * up
+    x = RMSNorm(h)                  -> gate_up (W8A8) -> silu(gate) * up (in the
+                                       linear's epilogue for gated weights)
       -> down (W8A8)                -> h += down
 
 then the final RMSNorm and the W8A8 LM head with the accept step
@@ -45,12 +46,15 @@ QWEN3_8B = DecoderConfig(hidden=4096, heads_q=32, heads_kv=8, head_dim=128, inte
 
 @dataclass
 class Linear:
-    """One W8A8 linear: packed INT8 weights, per-channel scales, smoothing s."""
+    """One W8A8 linear: packed INT8 weights, per-channel scales, smoothing s.
+    ``gated``: a gate_up linear packed by quasar_quantize_weights_gated, run as
+    quasar_w8a8_linear_swiglu (the activation in the linear's epilogue)."""
     wq: binding.PackedWeights
     sw: torch.Tensor
     s: torch.Tensor
     N: int
     K: int
+    gated: bool = False
 
 
 class DecoderStep:
@@ -93,7 +97,8 @@ class DecoderStep:
                         for _ in range(c.layers)]
         self.v_cache = [torch.zeros((B, c.heads_kv, self.Lmax, D), dtype=bf, device=dev)
                         for _ in range(c.layers)]
-        lin_ws = max(binding.workspace_bytes_linear(M, l.N, l.K)
+        lin_ws = max((binding.workspace_bytes_linear_swiglu if l.gated else
+                      binding.workspace_bytes_linear)(M, l.N, l.K)
                      for L in layers for l in L.values())
         self.ws_lin = binding.new_workspace(lin_ws, dev)
         self.ws_att = binding.new_workspace(
@@ -141,9 +146,14 @@ class DecoderStep:
             rec("h_before_o", self.h)
             binding.quasar_rmsnorm(self.h, self.norms["post"][li], c.eps, delta=self.o, out=self.x)
             rec("x_mlp_in", self.x)
-            self._linear(self.x, L["gate_up"], self.gu)
-            rec("gu", self.gu)
-            binding.quasar_silu_mul(self.gu, out=self.act)
+            gu = L["gate_up"]
+            if gu.gated:
+                binding.quasar_w8a8_linear_swiglu(self.x, gu.s, gu.wq, gu.sw, out=self.act,
+                                                  workspace=self.ws_lin)
+            else:
+                self._linear(self.x, gu, self.gu)
+                rec("gu", self.gu)
+                binding.quasar_silu_mul(self.gu, out=self.act)
             rec("act", self.act)
             self._linear(self.act, L["down"], self.dn)
             rec("dn", self.dn)
