@@ -21,16 +21,26 @@
  *     CUDA memory) unless stated otherwise; sizes are element counts.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
  *     validate their arguments on the host, then enqueue kernels on `stream`
- *     and return without synchronising.  Nothing is allocated, and no state
- *     is kept between calls apart from the launch counters of the wide linear
- *     kernel (device words of this library, one per workgroup): the caller owns
+ *     and return without synchronising.  Nothing is allocated: the caller owns
  *     every buffer, including workspaces sized by the *_workspace_bytes
- *     queries.  Two calls may run concurrently
- *     on different streams only with different workspaces (and see
- *     quasar_w8a8_linear for the one kind of call that must not overlap).
+ *     queries.  The only library state is one status word per device (see
+ *     quasar_device_check).  Two calls may run concurrently on different
+ *     streams as long as they use different workspaces.
+ *   - Workspaces.  Kernels whose workgroups hand data to each other within a
+ *     launch keep their flags in the first quasar_workspace_header_bytes()
+ *     bytes of the workspace.  That header must be all zero before the
+ *     workspace's first use (allocate it zero-filled, or call
+ *     quasar_workspace_init once); the calls maintain it afterwards and never
+ *     need it reset.  A workspace belongs to one device, and to one call at a
+ *     time.  The rest of a workspace may hold anything.
  *   - Argument errors are reported before any launch, as a status code; the
  *     outputs are then untouched.  A launch failure returns QUASAR_ERR_HIP.
  *     Device faults surface at the caller's next synchronisation.
+ *   - Every wait of one workgroup for another is bounded.  If one gives up (a
+ *     grid that could not be resident at once, e.g. next to another process's
+ *     kernels, or a workspace header that was not zeroed), the kernel still
+ *     finishes, that call's outputs are undefined, and the next
+ *     quasar_device_check() returns QUASAR_ERR_INCOMPLETE.
  *   - Inputs must be finite.  A non-finite input is outside the contract.
  */
 #ifndef QUASAR_H
@@ -48,8 +58,15 @@ typedef enum quasar_status {
   QUASAR_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size or value  */
   QUASAR_ERR_UNSUPPORTED = 2, /* valid in principle, outside this build's limits */
   QUASAR_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required  */
-  QUASAR_ERR_HIP = 4          /* the HIP runtime rejected a launch           */
+  QUASAR_ERR_HIP = 4,         /* the HIP runtime rejected a launch           */
+  QUASAR_ERR_INCOMPLETE = 5   /* quasar_device_check: a bounded wait gave up */
 } quasar_status;
+
+/* Detail bits of quasar_device_check: which kind of wait gave up. */
+#define QUASAR_WAIT_LDS 1u       /* between wavefronts of one workgroup            */
+#define QUASAR_WAIT_ROWS 2u      /* for other workgroups' quantized token rows      */
+#define QUASAR_WAIT_PARTIALS 4u  /* for other workgroups' INT32 partial sums        */
+#define QUASAR_WAIT_CHAIN 8u     /* for an earlier link of a chained call           */
 
 /* Limits of this build. */
 #define QUASAR_MAX_M 128      /* verify-window rows per linear call            */
@@ -61,6 +78,42 @@ const char* quasar_status_string(quasar_status status);
 
 /* ABI version of this library (bumped on any change of the exported set). */
 int quasar_abi_version(void);
+
+/*
+ * quasar_device_check -- waits until the current device is idle, then reads
+ * and clears its status word.  QUASAR_OK if no bounded wait gave up since the
+ * last check; QUASAR_ERR_INCOMPLETE otherwise, with *detail (if not NULL) the
+ * QUASAR_WAIT_* bits of the waits that did (the outputs of the calls in between
+ * are undefined); QUASAR_ERR_HIP if the device reports an error.  Not meant for
+ * the hot loop: it synchronises the whole device.  A kernel that gives up
+ * between this call's synchronisation and its read of the word (another host
+ * thread launching meanwhile) is reported by the next check.
+ */
+quasar_status quasar_device_check(uint32_t* detail);
+
+/*
+ * quasar_debug_force_wait_expiry -- test hook, not for production: while `on`
+ * is nonzero, kernels launched by this process get wait targets that can never
+ * be reached and a short spin bound, so that every cross-workgroup and
+ * cross-wavefront wait gives up at once and is reported by
+ * quasar_device_check, while every kernel still runs to its end.  Outputs of
+ * such launches are undefined (all memory accesses stay inside the call's
+ * buffers).
+ */
+void quasar_debug_force_wait_expiry(int on);
+
+/* Bytes of the flag header at the start of every workspace (see the
+ * conventions above): 2048. */
+size_t quasar_workspace_header_bytes(void);
+
+/*
+ * quasar_workspace_init -- zero the flag header of a workspace with a small
+ * kernel on `stream` (not a memset, so it may be captured in a graph).  Needed
+ * once per workspace before its first use unless it was allocated zeroed.
+ *   workspace  device pointer, 256-byte aligned; workspace_bytes >= the header
+ * Errors: WORKSPACE, HIP.
+ */
+quasar_status quasar_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * quasar_packed_weight_bytes -- size of the INT8 weight buffer of an N x K
@@ -140,10 +193,11 @@ quasar_status quasar_quantize_activations(const uint16_t* x, const float* s, int
 /* Workspace bytes quasar_w8a8_linear needs for this shape.  Pure host
  * function, deterministic in (M, N, K).  It is 0 for an empty call and for
  * verify windows of M <= 8 tokens with K <= 12288, which keep the quantized
- * activations in on-chip memory; other shapes stage the quantized activations
- * and the INT32 partial sums of output groups shared by two workgroups in the
- * workspace (1 KB per 16-token block and 64-wide K chunk, 4*M bytes, and
- * 16 KB per 16-token block and compute unit, each part rounded up to 256). */
+ * activations in on-chip memory; other shapes need the flag header (2 KB) and
+ * stage the quantized activations and the INT32 partial sums of output groups
+ * shared by two workgroups in the workspace (1 KB per 16-token block and
+ * 64-wide K chunk, 4*M bytes, and 16 KB per 16-token block and compute unit,
+ * each part rounded up to 256). */
 size_t quasar_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Diagnostic: the kernel(s) quasar_w8a8_linear launches for an M x N x K
@@ -172,17 +226,18 @@ const char* quasar_w8a8_kernel_name(int64_t M, int64_t N, int64_t K);
  *   acc_out  [M, N] int32 or NULL                      (out, optional: the exact
  *            accumulators, for tests)
  *   workspace, workspace_bytes: device scratch of at least
- *            quasar_w8a8_workspace_bytes(M, N, K) bytes, 256-byte aligned; any
- *            contents; overwritten.  May be NULL when that size is 0.
+ *            quasar_w8a8_workspace_bytes(M, N, K) bytes, 256-byte aligned, its
+ *            flag header zeroed before first use (see the conventions above).
+ *            May be NULL when that size is 0.
  * Every shape runs as one kernel launch on `stream` (quantize, GEMM and
  * dequant fused).  Windows of M <= 8 tokens with K <= 12288 use a kernel that
  * keeps the codes in on-chip memory.  Other shapes use a kernel whose grid is
  * one workgroup per compute unit, all resident at once: its workgroups hand the
- * quantized token rows and partial sums to each other through the workspace
- * and through per-workgroup launch counters kept in the library's device
- * memory.  Two such calls on one device must not run at the same time (each
- * needs every compute unit); calls ordered on one stream never do.  The result
- * does not depend on the workspace's previous contents.
+ * quantized token rows and partial sums to each other through the workspace,
+ * with flags in its header.  Such calls on different streams with different
+ * workspaces may overlap; a wait that gives up because the grid could not be
+ * resident is reported by quasar_device_check.  The result does not depend on
+ * the previous contents of the workspace beyond its header.
  * M == 0 or N == 0 is a no-op.  Errors: INVALID_ARG, UNSUPPORTED (M or K
  * beyond the limits, or a device with fewer than M compute units),
  * WORKSPACE, HIP.
@@ -264,7 +319,7 @@ size_t quasar_lm_head_verify_workspace_bytes(int64_t B, int64_t k, int64_t V, in
  *   p_draft_out   as for quasar_verify_accept
  *   logits      [B, k+1, V] bf16 bits (out)
  *   workspace   at least quasar_lm_head_verify_workspace_bytes(B, k, V, K)
- *               bytes, 256-byte aligned, any contents
+ *               bytes, 256-byte aligned, its flag header zeroed before first use
  * B == 0 is a no-op.  Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
  */
 quasar_status quasar_lm_head_verify(const uint16_t* x, const float* s, const int8_t* wq,
@@ -273,6 +328,109 @@ quasar_status quasar_lm_head_verify(const uint16_t* x, const float* s, const int
                                     const float* uniforms, uint16_t* logits, int32_t* accept_len,
                                     int32_t* next_token, int32_t* argmax_out, float* p_draft_out,
                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Chained linears: the linears of a verify step in one launch.
+ *
+ * A verify step runs the target model's linears over the 1+k verify positions
+ * one after the other, each reading what an earlier one wrote [Quasar, pt page
+ * §2 execution pipeline: the verifier runs the target model once over the
+ * drafts; items 2-4 for each linear].  quasar_w8a8_chain runs a list of such
+ * W8A8 linears ("links") over one window of M <= 8 tokens as ONE persistent
+ * kernel.  Link i computes exactly what quasar_w8a8_linear (or
+ * quasar_w8a8_linear_swiglu, with QUASAR_LINK_SWIGLU) computes on its
+ * arguments.  A link whose input is (a column slice of) the previous link's
+ * output says so with dep = i - 1: it starts reading its input only once the
+ * previous link is complete in every workgroup.  Weights do not depend on any
+ * input, so the kernel keeps streaming the next link's weights from HBM across
+ * each such wait: the weight stream, which bounds the step [pt page §1], does
+ * not stop between links.  (On MI355X at 6 tokens the wait -- a grid-wide
+ * hand-off, then every workgroup loading and quantizing the input -- costs
+ * more than a kernel boundary does, so per-linear launches are faster; the
+ * chain is kept for callers that cannot launch per linear.)
+ * The grid is one workgroup per compute unit, all resident at once (see the
+ * conventions on bounded waits).
+ * --------------------------------------------------------------------------- */
+#define QUASAR_LINK_SWIGLU 1u  /* weights from quasar_quantize_weights_gated;
+                                  y receives silu(gate) * up, [M, N/2] */
+#define QUASAR_CHAIN_MAX_LINKS 4096
+
+typedef struct quasar_chain_link {
+  const uint16_t* x;      /* [M, ldx] bf16 input rows; 16-byte aligned                    */
+  const float* s;         /* [K] smoothing vector; 16-byte aligned                         */
+  const int8_t* wq;       /* packed INT8 weights (quasar_quantize_weights, or _gated); 16 B */
+  const float* w_scale;   /* [N] weight scales; 4-byte aligned                             */
+  uint16_t* y;            /* [M, N] bf16 output ([M, N/2] with SWIGLU); 8-byte aligned     */
+  int32_t* acc_out;       /* [M, N] int32 accumulators or NULL (tests); NULL with SWIGLU  */
+  int64_t N;              /* output channels: 16 <= N, N % 16 == 0                         */
+  int64_t K;              /* 16 <= K <= 12288, K % 16 == 0                                 */
+  int64_t ldx;            /* row stride of x in elements: ldx >= K, ldx % 8 == 0           */
+  int32_t dep;            /* -1: x is ready before the call; i - 1: x is a column slice
+                             of the previous link's y (x = y_prev + col0 with col0 % 16
+                             == 0, ldx = the row length of y_prev), written in this call */
+  uint32_t flags;         /* 0 or QUASAR_LINK_SWIGLU                                       */
+} quasar_chain_link;
+
+/* Workspace bytes of quasar_w8a8_chain for these links (0 if they are invalid):
+ * the flag header. */
+size_t quasar_w8a8_chain_workspace_bytes(const quasar_chain_link* links, int64_t n_links,
+                                         int64_t M);
+
+/*
+ * quasar_w8a8_chain -- run n_links W8A8 linears over the same M-token window
+ * in one launch, in order, each as quasar_w8a8_linear would (bit for bit).
+ *   links      HOST array of n_links descriptors: validated here, and used to
+ *              plan the launch
+ *   links_dev  DEVICE copy of the same n_links descriptors (same bytes), read by
+ *              the kernel; 8-byte aligned; must stay unchanged until the call
+ *              has run (a graph that captures the call keeps reading it)
+ *   n_links    0 <= n_links <= QUASAR_CHAIN_MAX_LINKS (0 is a no-op)
+ *   M          1 <= M <= 8 (one to a few sequences' 1+k verify positions)
+ *   workspace  quasar_w8a8_chain_workspace_bytes(links, n_links, M) bytes,
+ *              256-byte aligned, flag header zeroed before first use
+ * The links' y and acc_out must not overlap each other or any link's x, except
+ * that a link with dep = i - 1 reads (a slice of) the previous link's y (the
+ * library does not check overlaps).  Errors: INVALID_ARG (a link that breaks a
+ * rule above; nothing is launched), UNSUPPORTED (M > 8, K > 12288, too many links, a device with too
+ * few compute units, or a link feeding the next one with more than 32 tiles of
+ * 16 channels per compute unit), WORKSPACE, HIP.
+ */
+quasar_status quasar_w8a8_chain(const quasar_chain_link* links, const quasar_chain_link* links_dev,
+                                int64_t n_links, int64_t M, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of quasar_chain_verify for these links (0 if invalid). */
+size_t quasar_chain_verify_workspace_bytes(const quasar_chain_link* links, int64_t n_links,
+                                           int64_t B, int64_t k);
+
+/*
+ * quasar_chain_verify -- a whole verify step's linears and its decision: the
+ * chain as quasar_w8a8_chain, whose LAST link is the LM head (M = B (k+1)
+ * rows ordered [B, k+1], N = V, no SWIGLU; its y receives the logits), then
+ * the accept step on those logits, as quasar_lm_head_verify does it: the LM
+ * head's epilogue reduces each workgroup's channel range of every logits row
+ * to (max, lowest argmax) and, at T > 0, its sum of exp((l - max) / T), and one
+ * small kernel takes the decisions.  Results equal quasar_w8a8_chain followed
+ * by quasar_verify_accept (at T > 0, p_draft up to the last binary32 bits).
+ *   links, links_dev, n_links  as for quasar_w8a8_chain (n_links >= 1)
+ *   B, k        B >= 1, 0 <= k <= QUASAR_MAX_DRAFT, B (k+1) <= 8
+ *   draft, temperature, uniforms, accept_len, next_token, argmax_out,
+ *   p_draft_out   as for quasar_verify_accept
+ *   workspace   quasar_chain_verify_workspace_bytes(links, n_links, B, k) bytes,
+ *               256-byte aligned, flag header zeroed before first use
+ * Errors: as quasar_w8a8_chain and quasar_verify_accept; UNSUPPORTED when a
+ * workgroup's channel range of the LM head exceeds 2048.
+ */
+quasar_status quasar_chain_verify(const quasar_chain_link* links,
+                                  const quasar_chain_link* links_dev, int64_t n_links, int64_t B,
+                                  int64_t k, const int32_t* draft, float temperature,
+                                  const float* uniforms, int32_t* accept_len, int32_t* next_token,
+                                  int32_t* argmax_out, float* p_draft_out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* Profiler name of the kernel quasar_w8a8_chain launches for M tokens ("" if
+ * unsupported); a diagnostic for the benchmark and profiles. */
+const char* quasar_w8a8_chain_kernel_name(int64_t M);
 
 /*
  * 4-bit weight variant.  The pages name verification with fewer bits (4 or 2)

@@ -49,10 +49,22 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for code in range(5):
+    for code in range(6):
         assert L.quasar_status_string(code).decode().startswith("QUASAR_")
     assert b"UNKNOWN" in L.quasar_status_string(99)
-    assert L.quasar_abi_version() == 9
+    assert L.quasar_abi_version() == 10
+
+
+def test_workspace_header_and_init_errors(L):
+    hdr = L.quasar_workspace_header_bytes()
+    assert hdr == 2048
+    # every workspace that carries flags starts with the header
+    for M, N, K in [(96, 4096, 12288), (9, 16, 16), (6, 64, 16384)]:
+        assert L.quasar_w8a8_workspace_bytes(M, N, K) >= hdr + M * K
+    init = L.quasar_workspace_init
+    assert init(None, 1 << 20, None) == WORKSPACE
+    assert init(FAKE, hdr - 1, None) == WORKSPACE
+    assert init(FAKE + 16, 1 << 20, None) == WORKSPACE
 
 
 def test_workspace_queries_are_pure_host_and_monotone(L):
@@ -286,3 +298,71 @@ def test_rope_attention_silu_argument_errors(L):
     assert silu(M=0) == OK
     assert silu(I=0) == INVALID and silu(M=-1) == INVALID and silu(gu=None) == INVALID
     assert silu(M=65536) == UNSUPPORTED and silu(o=FAKE + 1) == INVALID
+
+
+def chain_links(n=2, **over):
+    """n links of 64 x 64; link i > 0 reads link i - 1's output (x = y_prev)."""
+    arr = (binding.ChainLink * n)()
+    for i in range(n):
+        x = FAKE if i == 0 else FAKE + 0x1000 * i
+        arr[i] = binding.ChainLink(x, FAKE, FAKE, FAKE, FAKE + 0x1000 * (i + 1), None, 64, 64, 64,
+                                   i - 1, 0)
+    for k, v in over.items():
+        i, field = k.split("_", 1)
+        setattr(arr[int(i[1:])], field, v)
+    return arr
+
+
+def chain(L, links, n=None, dev=FAKE, M=6, ws=FAKE, wsb=1 << 24):
+    n = len(links) if n is None else n
+    return L.quasar_w8a8_chain(ctypes.cast(links, ctypes.c_void_p), dev, n, M, ws, wsb, None)
+
+
+def test_chain_argument_errors(L):
+    P = lambda a: ctypes.cast(a, ctypes.c_void_p)
+    hdr = L.quasar_workspace_header_bytes()
+    lk = chain_links()
+    assert L.quasar_w8a8_chain_workspace_bytes(P(lk), 2, 6) == hdr  # the flag header
+    assert L.quasar_w8a8_chain_workspace_bytes(P(chain_links(l1_dep=-1)), 2, 6) == hdr
+    assert L.quasar_w8a8_chain_workspace_bytes(P(lk), 2, 9) == 0
+    assert L.quasar_w8a8_chain_kernel_name(6).decode().startswith("w8a8_chain_kernel<6")
+    assert chain(L, chain_links(), n=0) == OK                       # empty chain: no-op
+    assert chain(L, chain_links(), M=0) == INVALID
+    assert chain(L, chain_links(), M=9) == UNSUPPORTED
+    assert chain(L, chain_links(l0_N=40)) == INVALID                 # N % 16 != 0
+    assert chain(L, chain_links(l1_K=12304, l1_ldx=12304, l1_dep=-1)) == UNSUPPORTED
+    assert chain(L, chain_links(l1_ldx=48)) == INVALID               # ldx < K
+    assert chain(L, chain_links(l1_ldx=68, l1_dep=-1)) == INVALID    # ldx % 8 != 0
+    assert chain(L, chain_links(l0_dep=0)) == INVALID                # a link cannot wait for itself
+    assert chain(L, chain_links(3, l2_dep=0)) == INVALID             # only the previous link
+    assert chain(L, chain_links(l1_dep=-2)) == INVALID
+    assert chain(L, chain_links(l1_x=FAKE + 0x1000 + 16)) == INVALID  # slice past the row end
+    assert chain(L, chain_links(l1_x=FAKE + 0x1000 + 8, l1_K=48)) == INVALID  # col0 % 16 != 0
+    assert chain(L, chain_links(l1_ldx=128, l0_N=64)) == INVALID     # ldx != the row length
+    assert chain(L, chain_links(l1_flags=2)) == INVALID
+    assert chain(L, chain_links(l1_flags=1, l1_acc_out=FAKE)) == INVALID  # SWIGLU without acc
+    assert chain(L, chain_links(l0_x=FAKE + 8)) == INVALID
+    assert chain(L, chain_links(l0_y=FAKE + 4)) == INVALID
+    assert chain(L, chain_links(l1_s=None)) == INVALID
+    assert chain(L, chain_links(), dev=None) == INVALID
+    assert chain(L, chain_links(), ws=None) == WORKSPACE
+    assert chain(L, chain_links(), wsb=hdr - 256) == WORKSPACE
+    assert chain(L, chain_links(), n=5000) == UNSUPPORTED
+
+
+def test_chain_verify_argument_errors(L):
+    links = chain_links()
+    cv = lambda n=2, B=1, k=5, T=0.0, u=None, draft=FAKE, lk=links: L.quasar_chain_verify(
+        ctypes.cast(lk, ctypes.c_void_p), FAKE, n, B, k, draft, T, u, FAKE, FAKE, None, None,
+        FAKE, 1 << 24, None)
+    P = lambda a: ctypes.cast(a, ctypes.c_void_p)
+    assert L.quasar_chain_verify_workspace_bytes(P(links), 2, 1, 5) > \
+        L.quasar_w8a8_chain_workspace_bytes(P(links), 2, 6)          # + the accept partials
+    assert L.quasar_chain_verify_workspace_bytes(P(links), 2, 2, 5) == 0  # 12 rows > 8
+    assert cv(n=0) == INVALID
+    assert cv(B=2) == UNSUPPORTED
+    assert cv(T=-1.0) == INVALID
+    assert cv(T=float("nan")) == INVALID
+    assert cv(T=1.0, u=None) == INVALID
+    assert cv(draft=None) == INVALID
+    assert cv(lk=chain_links(l1_flags=1)) == INVALID                 # the head is not gated

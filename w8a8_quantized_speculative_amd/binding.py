@@ -22,6 +22,11 @@ QUASAR_ERR_INVALID_ARG = 1
 QUASAR_ERR_UNSUPPORTED = 2
 QUASAR_ERR_WORKSPACE = 3
 QUASAR_ERR_HIP = 4
+QUASAR_ERR_INCOMPLETE = 5
+QUASAR_WAIT_LDS = 1
+QUASAR_WAIT_ROWS = 2
+QUASAR_WAIT_PARTIALS = 4
+QUASAR_WAIT_CHAIN = 8
 QUASAR_MAX_M = 128
 QUASAR_MAX_K = 65536
 QUASAR_MAX_DRAFT = 63
@@ -34,6 +39,10 @@ _SZ = ctypes.c_size_t
 _SIGNATURES = {
     "quasar_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "quasar_abi_version": (ctypes.c_int, []),
+    "quasar_device_check": (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint32)]),
+    "quasar_debug_force_wait_expiry": (None, [ctypes.c_int]),
+    "quasar_workspace_header_bytes": (_SZ, []),
+    "quasar_workspace_init": (ctypes.c_int, [_P, _SZ, _P]),
     "quasar_quantize_weights": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P]),
     "quasar_quantize_weights_gated": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P]),
     "quasar_w8a8_linear_swiglu_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
@@ -64,7 +73,25 @@ _SIGNATURES = {
     "quasar_attention": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64, _P,
                                         _P, _SZ, _P]),
     "quasar_silu_mul": (ctypes.c_int, [_P, _I64, _I64, _P, _P]),
+    "quasar_w8a8_chain_workspace_bytes": (_SZ, [_P, _I64, _I64]),
+    "quasar_w8a8_chain": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _SZ, _P]),
+    "quasar_chain_verify_workspace_bytes": (_SZ, [_P, _I64, _I64, _I64]),
+    "quasar_chain_verify": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _P, ctypes.c_float, _P, _P,
+                                           _P, _P, _P, _P, _SZ, _P]),
+    "quasar_w8a8_chain_kernel_name": (ctypes.c_char_p, [_I64]),
 }
+
+QUASAR_LINK_SWIGLU = 1
+
+
+class ChainLink(ctypes.Structure):
+    """struct quasar_chain_link (include/quasar.h)."""
+    _fields_ = [("x", _P), ("s", _P), ("wq", _P), ("w_scale", _P), ("y", _P), ("acc_out", _P),
+                ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("ldx", ctypes.c_int64),
+                ("dep", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+assert ctypes.sizeof(ChainLink) == 80
 
 
 class QuasarError(RuntimeError):
@@ -125,9 +152,28 @@ def workspace_bytes_accept(B: int, k: int, V: int) -> int:
 
 
 def new_workspace(nbytes: int, device=None) -> torch.Tensor:
-    """A device byte buffer for the *_workspace_bytes sizes (256-byte aligned)."""
-    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8,
+    """A zero-filled device byte buffer for the *_workspace_bytes sizes (256-byte
+    aligned): the flag header at its start must be zero before first use."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8,
                        device=device if device is not None else "cuda")
+
+
+def workspace_init(workspace: torch.Tensor) -> None:
+    """Zero a workspace's flag header with the library's kernel (graph-safe)."""
+    _check("quasar_workspace_init", lib().quasar_workspace_init(
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
+
+
+def device_check():
+    """Wait for the device, read and clear its status word: (status, detail bits)."""
+    bits = ctypes.c_uint32(0)
+    st = lib().quasar_device_check(ctypes.byref(bits))
+    return int(st), int(bits.value)
+
+
+def force_wait_expiry(on: bool) -> None:
+    """Test hook: every bounded wait of kernels launched while on gives up."""
+    lib().quasar_debug_force_wait_expiry(1 if on else 0)
 
 
 def w8a8_kernel_name(M: int, N: int, K: int) -> str:
@@ -473,3 +519,104 @@ def quasar_silu_mul(gate_up: torch.Tensor, out: torch.Tensor | None = None):
     _need(out, torch.bfloat16, (M, I2 // 2), "out")
     _check("quasar_silu_mul", lib().quasar_silu_mul(_ptr(gate_up), M, I2 // 2, _ptr(out), _stream()))
     return out
+
+
+class Chain:
+    """A list of W8A8 linears over one M-token window, run as one launch
+    (quasar_w8a8_chain), or with the accept step after its last link, the LM
+    head (quasar_chain_verify).  Links are added once; finalize() makes the
+    host array and its device copy, which later runs reuse (the tensors passed
+    to add() are kept alive by this object)."""
+
+    def __init__(self, M: int, device=None):
+        self.M = int(M)
+        self.device = device if device is not None else "cuda"
+        self.links = []
+        self._keep = []
+        self.host = None
+        self.dev = None
+        self.workspace = None
+
+    def add(self, x: torch.Tensor, s: torch.Tensor, wq, w_scale: torch.Tensor, y: torch.Tensor,
+            dep: int = -1, swiglu: bool = False, acc_out: torch.Tensor | None = None) -> int:
+        """Append a link; returns its index.  x is [M, K] bf16 with unit column
+        stride (a column slice of an earlier link's y is fine: its row stride is
+        passed as ldx); y is [M, N] bf16 ([M, N/2] with swiglu), contiguous."""
+        if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[0] != self.M or x.stride(1) != 1:
+            raise ValueError("x must be a [M, K] bf16 matrix with unit column stride")
+        K = x.shape[1]
+        N = wq.N
+        _need(s, torch.float32, (K,), "s")
+        _need(w_scale, torch.float32, (N,), "w_scale")
+        _need(y, torch.bfloat16, (self.M, N // 2 if swiglu else N), "y")
+        if acc_out is not None:
+            _need(acc_out, torch.int32, (self.M, N), "acc_out")
+        lk = ChainLink(x.data_ptr(), s.data_ptr(), wq.data_ptr(), w_scale.data_ptr(), y.data_ptr(),
+                       None if acc_out is None else acc_out.data_ptr(), N, K, x.stride(0),
+                       int(dep), QUASAR_LINK_SWIGLU if swiglu else 0)
+        self.links.append(lk)
+        self._keep.append((x, s, wq, w_scale, y, acc_out))
+        self.host = None
+        return len(self.links) - 1
+
+    def finalize(self):
+        n = len(self.links)
+        self.host = (ChainLink * max(n, 1))(*self.links)
+        raw = torch.frombuffer(bytearray(bytes(self.host)), dtype=torch.uint8)
+        self.dev = raw.to(self.device)
+        need = int(lib().quasar_w8a8_chain_workspace_bytes(ctypes.cast(self.host, _P), n, self.M))
+        if n and need == 0:
+            raise QuasarError("quasar_w8a8_chain_workspace_bytes", QUASAR_ERR_INVALID_ARG)
+        # a zero-filled workspace of this chain's own (its exchange areas depend on the links)
+        self.workspace = new_workspace(need, self.device)
+        return self
+
+    def run(self, workspace: torch.Tensor | None = None) -> None:
+        if self.host is None:
+            self.finalize()
+        ws = self.workspace if workspace is None else workspace
+        _check("quasar_w8a8_chain", lib().quasar_w8a8_chain(
+            ctypes.cast(self.host, _P), _ptr(self.dev), len(self.links), self.M, _ptr(ws),
+            ws.numel() * ws.element_size(), _stream()))
+
+    def verify_workspace(self, B: int, k: int) -> torch.Tensor:
+        if self.host is None:
+            self.finalize()
+        need = int(lib().quasar_chain_verify_workspace_bytes(ctypes.cast(self.host, _P),
+                                                              len(self.links), B, k))
+        if need == 0:
+            raise QuasarError("quasar_chain_verify_workspace_bytes", QUASAR_ERR_INVALID_ARG)
+        return new_workspace(need, self.device)
+
+    def run_verify(self, B: int, k: int, draft: torch.Tensor | None, temperature: float = 0.0,
+                   uniforms: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                   want_argmax: bool = False, want_p_draft: bool = False, out=None):
+        """The chain, then the accept step on its last link's logits.  Returns
+        (accept_len [B], next_token [B], argmax [B, k+1] or None, p_draft [B, k] or None)."""
+        if self.host is None:
+            self.finalize()
+        if workspace is None:
+            if getattr(self, "_verify_ws", None) is None or self._verify_key != (B, k):
+                self._verify_ws, self._verify_key = self.verify_workspace(B, k), (B, k)
+            workspace = self._verify_ws
+        dev = self.device
+        if out is None:
+            acc = torch.empty((B,), dtype=torch.int32, device=dev)
+            nxt = torch.empty((B,), dtype=torch.int32, device=dev)
+            g = torch.empty((B, k + 1), dtype=torch.int32, device=dev) if want_argmax else None
+            pd = torch.empty((B, k), dtype=torch.float32, device=dev) if want_p_draft else None
+        else:
+            acc, nxt, g, pd = out
+        if draft is not None:
+            _need(draft, torch.int32, (B, k), "draft")
+        if uniforms is not None:
+            _need(uniforms, torch.float32, (B, k + 1), "uniforms")
+        _check("quasar_chain_verify", lib().quasar_chain_verify(
+            ctypes.cast(self.host, _P), _ptr(self.dev), len(self.links), B, k, _ptr(draft),
+            float(temperature), _ptr(uniforms), _ptr(acc), _ptr(nxt), _ptr(g), _ptr(pd),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
+        return acc, nxt, g, pd
+
+
+def chain_kernel_name(M: int) -> str:
+    return lib().quasar_w8a8_chain_kernel_name(M).decode()

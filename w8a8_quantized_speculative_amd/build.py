@@ -21,7 +21,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libquasar.so")
 ARCH = "gfx950"
 
-SOURCES = ["quant.hip", "fused.hip", "wide.hip", "accept.hip", "decoder.hip", "diag.hip", "abi.hip"]
+SOURCES = ["quant.hip", "fused.hip", "wide.hip", "chain.hip", "accept.hip", "decoder.hip", "diag.hip",
+           "abi.hip"]
 
 # -ffp-contract=off: every binary32 multiply and add rounds on its own (the
 #   quantizer and the dequant epilogue are specified operation by operation).

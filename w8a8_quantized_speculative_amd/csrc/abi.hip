@@ -3,6 +3,7 @@
 // never reaches the GPU, then enqueues its kernels on the caller's stream.
 #include "../../include/quasar.h"
 #include "quasar_internal.hpp"
+#include "quasar_sync.hpp"
 
 #include <math.h>
 
@@ -70,6 +71,64 @@ LmHeadPlan plan_lm_head(int64_t B, int64_t k, int64_t V, int64_t K) {
   return p;
 }
 
+// Chained linears: validate every link on the host; the widest K sizes the
+// LDS code matrix.  A link with dep = i - 1 must read a column slice of link
+// i - 1's output.
+quasar_status check_chain(const quasar_chain_link* links, int64_t n, int64_t M, int* kmax) {
+  if (M < 1 || n < 0) return QUASAR_ERR_INVALID_ARG;
+  if (M > 8 || n > QUASAR_CHAIN_MAX_LINKS) return QUASAR_ERR_UNSUPPORTED;
+  if (n > 0 && !links) return QUASAR_ERR_INVALID_ARG;
+  int km = 16;
+  for (int64_t i = 0; i < n; ++i) {
+    const quasar_chain_link& L = links[i];
+    if (L.N < 16 || L.N % 16 != 0 || L.K < 16 || L.K % 16 != 0) return QUASAR_ERR_INVALID_ARG;
+    if (L.K > kChainMaxK || L.N > kMaxRowsPerCall) return QUASAR_ERR_UNSUPPORTED;
+    if (L.ldx < L.K || L.ldx % 8 != 0) return QUASAR_ERR_INVALID_ARG;
+    if ((M - 1) * L.ldx + L.K > ((int64_t)1 << 29)) return QUASAR_ERR_UNSUPPORTED;
+    if (L.dep != -1 && L.dep != i - 1) return QUASAR_ERR_INVALID_ARG;
+    if (L.flags & ~QUASAR_LINK_SWIGLU) return QUASAR_ERR_INVALID_ARG;
+    const bool swiglu = (L.flags & QUASAR_LINK_SWIGLU) != 0;
+    if (!L.x || !L.s || !L.wq || !L.w_scale || !L.y || (swiglu && L.acc_out))
+      return QUASAR_ERR_INVALID_ARG;
+    if (!aligned(L.x, 16) || !aligned(L.s, 16) || !aligned(L.wq, 16) || !aligned(L.w_scale, 4) ||
+        !aligned(L.y, 8) || (L.acc_out && !aligned(L.acc_out, 4)))
+      return QUASAR_ERR_INVALID_ARG;
+    if (L.dep >= 0) {
+      // x = y of the previous link + col0, same row stride, whole columns
+      const quasar_chain_link& P = links[i - 1];
+      const int64_t width = (P.flags & QUASAR_LINK_SWIGLU) ? P.N / 2 : P.N;
+      const int64_t col0 = (int64_t)(L.x - P.y);
+      if (col0 < 0 || col0 % 16 != 0 || col0 + L.K > width || L.ldx != width)
+        return QUASAR_ERR_INVALID_ARG;
+    }
+    if (L.K > km) km = (int)L.K;
+  }
+  *kmax = km;
+  return QUASAR_OK;
+}
+
+size_t chain_workspace_bytes(const quasar_chain_link*, int64_t) { return kFlagHeaderBytes; }
+
+// quasar_chain_verify's workspace: the flag header, then the LM head's accept
+// partials [M][kWideMaxGrid] (max, argmax, sum of exp).
+struct ChainVerifyPlan {
+  size_t off_pmax, off_pidx, off_psum, bytes;
+};
+
+ChainVerifyPlan plan_chain_verify(const quasar_chain_link* links, int64_t n, int64_t M) {
+  ChainVerifyPlan p{};
+  const size_t slots = (size_t)M * kWideMaxGrid;
+  size_t off = chain_workspace_bytes(links, n);
+  p.off_pmax = off;
+  off = align_up(off + slots * sizeof(float), kWsAlign);
+  p.off_pidx = off;
+  off = align_up(off + slots * sizeof(int32_t), kWsAlign);
+  p.off_psum = off;
+  off = align_up(off + slots * sizeof(float), kWsAlign);
+  p.bytes = off;
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -81,11 +140,31 @@ const char* quasar_status_string(quasar_status status) {
     case QUASAR_ERR_UNSUPPORTED: return "QUASAR_ERR_UNSUPPORTED: size outside this build's limits";
     case QUASAR_ERR_WORKSPACE: return "QUASAR_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case QUASAR_ERR_HIP: return "QUASAR_ERR_HIP: the HIP runtime rejected a launch";
+    case QUASAR_ERR_INCOMPLETE:
+      return "QUASAR_ERR_INCOMPLETE: a bounded wait between workgroups gave up; outputs since the "
+             "last check are undefined";
   }
   return "QUASAR_ERR_UNKNOWN";
 }
 
-int quasar_abi_version(void) { return 9; }
+int quasar_abi_version(void) { return 10; }
+
+quasar_status quasar_device_check(uint32_t* detail) {
+  uint32_t bits = 0;
+  if (read_and_clear_status(&bits) != hipSuccess) return QUASAR_ERR_HIP;
+  if (detail) *detail = bits;
+  return bits ? QUASAR_ERR_INCOMPLETE : QUASAR_OK;
+}
+
+void quasar_debug_force_wait_expiry(int on) { set_forced_wait_expiry(on != 0); }
+
+size_t quasar_workspace_header_bytes(void) { return kFlagHeaderBytes; }
+
+quasar_status quasar_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace || workspace_bytes < kFlagHeaderBytes || !aligned(workspace, kWsAlign))
+    return QUASAR_ERR_WORKSPACE;
+  return hip_status(launch_zero_flag_header(workspace, (hipStream_t)stream));
+}
 
 quasar_status quasar_quantize_weights(const uint16_t* w, const float* s, int64_t N, int64_t K,
                                       int8_t* wq, float* w_scale, void* stream) {
@@ -344,6 +423,94 @@ quasar_status quasar_lm_head_verify(const uint16_t* x, const float* s, const int
   hipError_t e = launch_fused(p.fp, x, s, wq, w_scale, logits, nullptr, hs, &parts);
   if (e != hipSuccess) return QUASAR_ERR_HIP;
   return hip_status(launch_accept_finalize(p.ap, logits, draft, temperature, uniforms, accept_len,
+                                           next_token, argmax_out, p_draft_out, pmax, pidx, psum,
+                                           hs));
+}
+
+size_t quasar_w8a8_chain_workspace_bytes(const quasar_chain_link* links, int64_t n_links,
+                                         int64_t M) {
+  int kmax = 0;
+  if (check_chain(links, n_links, M, &kmax) != QUASAR_OK) return 0;
+  return chain_workspace_bytes(links, n_links);
+}
+
+const char* quasar_w8a8_chain_kernel_name(int64_t M) {
+  if (M < 1 || M > 8) return "";
+  return chain_kernel_name((int)M);
+}
+
+quasar_status quasar_w8a8_chain(const quasar_chain_link* links, const quasar_chain_link* links_dev,
+                                int64_t n_links, int64_t M, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  int kmax = 0;
+  quasar_status st = check_chain(links, n_links, M, &kmax);
+  if (st != QUASAR_OK) return st;
+  if (n_links == 0) return QUASAR_OK;
+  if (!links_dev || !aligned(links_dev, 8)) return QUASAR_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < chain_workspace_bytes(links, n_links) ||
+      !aligned(workspace, kWsAlign))
+    return QUASAR_ERR_WORKSPACE;
+  const int G = wide_grid_for_current_device();
+  if (G < 1) return QUASAR_ERR_UNSUPPORTED;
+  return hip_status(launch_chain(links_dev, (int)n_links, (int)M, kmax, G, workspace, nullptr,
+                                 (hipStream_t)stream));
+}
+
+size_t quasar_chain_verify_workspace_bytes(const quasar_chain_link* links, int64_t n_links,
+                                           int64_t B, int64_t k) {
+  if (B < 1 || k < 0 || k > QUASAR_MAX_DRAFT || B * (k + 1) > 8 || n_links < 1) return 0;
+  int kmax = 0;
+  if (check_chain(links, n_links, B * (k + 1), &kmax) != QUASAR_OK) return 0;
+  return plan_chain_verify(links, n_links, B * (k + 1)).bytes;
+}
+
+quasar_status quasar_chain_verify(const quasar_chain_link* links,
+                                  const quasar_chain_link* links_dev, int64_t n_links, int64_t B,
+                                  int64_t k, const int32_t* draft, float temperature,
+                                  const float* uniforms, int32_t* accept_len, int32_t* next_token,
+                                  int32_t* argmax_out, float* p_draft_out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (B < 1 || k < 0 || n_links < 1) return QUASAR_ERR_INVALID_ARG;
+  if (!(temperature >= 0.0f) || isinf(temperature)) return QUASAR_ERR_INVALID_ARG;  // NaN too
+  if (k > QUASAR_MAX_DRAFT || B * (k + 1) > 8) return QUASAR_ERR_UNSUPPORTED;
+  const int64_t M = B * (k + 1);
+  int kmax = 0;
+  quasar_status st = check_chain(links, n_links, M, &kmax);
+  if (st != QUASAR_OK) return st;
+  const quasar_chain_link& head = links[n_links - 1];
+  if (head.flags & QUASAR_LINK_SWIGLU) return QUASAR_ERR_INVALID_ARG;
+  if (!accept_len || !next_token) return QUASAR_ERR_INVALID_ARG;
+  if (k > 0 && !draft) return QUASAR_ERR_INVALID_ARG;
+  if (temperature > 0.0f && !uniforms) return QUASAR_ERR_INVALID_ARG;
+  if ((draft && !aligned(draft, 4)) || !aligned(accept_len, 4) || !aligned(next_token, 4) ||
+      (uniforms && !aligned(uniforms, 4)) || (argmax_out && !aligned(argmax_out, 4)) ||
+      (p_draft_out && !aligned(p_draft_out, 4)))
+    return QUASAR_ERR_INVALID_ARG;
+  if (!links_dev || !aligned(links_dev, 8)) return QUASAR_ERR_INVALID_ARG;
+  const int64_t V = head.N;
+  const ChainVerifyPlan cp = plan_chain_verify(links, n_links, M);
+  if (!workspace || workspace_bytes < cp.bytes || !aligned(workspace, kWsAlign))
+    return QUASAR_ERR_WORKSPACE;
+  const int G = wide_grid_for_current_device();
+  if (G < 1) return QUASAR_ERR_UNSUPPORTED;
+  AcceptPlan ap = plan_accept(B, k, V);
+  const int tiles = (int)((V + 15) / 16);
+  if (16 * (tiles / G + 1) > kAcceptChunk) return QUASAR_ERR_UNSUPPORTED;
+  ap.chunks = G;
+  ap.unit = 16;
+  ap.cq = tiles / G;
+  ap.cr = tiles % G;
+  ap.cG = G;
+  char* ws = static_cast<char*>(workspace);
+  float* pmax = reinterpret_cast<float*>(ws + cp.off_pmax);
+  int32_t* pidx = reinterpret_cast<int32_t*>(ws + cp.off_pidx);
+  float* psum = reinterpret_cast<float*>(ws + cp.off_psum);
+  const bool sample = temperature > 0.0f;
+  const AcceptPartials parts{pmax, pidx, sample ? psum : nullptr, sample ? 1.0f / temperature : 0.0f};
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = launch_chain(links_dev, (int)n_links, (int)M, kmax, G, workspace, &parts, hs);
+  if (e != hipSuccess) return QUASAR_ERR_HIP;
+  return hip_status(launch_accept_finalize(ap, head.y, draft, temperature, uniforms, accept_len,
                                            next_token, argmax_out, p_draft_out, pmax, pidx, psum,
                                            hs));
 }

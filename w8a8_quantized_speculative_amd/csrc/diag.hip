@@ -1,11 +1,37 @@
-// Diagnostic kernel: a plain device-to-device copy with 16-byte vector loads
-// and stores.  It is the reference workload for reading hardware byte
-// counters: a copy of B bytes fetches and writes exactly B bytes.
+// Diagnostics of libquasar: the device status word that reports bounded waits
+// that gave up (see quasar_sync.hpp), the forced-expiry test hook, and a plain
+// device-to-device copy with 16-byte vector loads and stores -- the reference
+// workload for reading hardware byte counters (a copy of B bytes fetches and
+// writes exactly B bytes).
+#include <atomic>
+#include <mutex>
+
 #include "quasar_device.hpp"
 #include "quasar_internal.hpp"
+#include "quasar_sync.hpp"
 
 namespace quasar {
+
+// One word per device (each device that loads the library holds its own copy).
+__device__ uint32_t g_wait_status;
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_status_mutex;
+uint32_t* g_status_ptr[kMaxDevices];
+std::atomic<bool> g_forced{false};
+
+uint32_t* status_word_for_device(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_status_mutex);
+  if (!g_status_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_wait_status)) != hipSuccess) return nullptr;
+    g_status_ptr[dev] = static_cast<uint32_t*>(p);
+  }
+  return g_status_ptr[dev];
+}
 
 __global__ __launch_bounds__(256) void stream_copy_kernel(const v4i* __restrict__ src,
                                                           v4i* __restrict__ dst, size_t n16) {
@@ -24,7 +50,52 @@ __global__ __launch_bounds__(256) void stream_copy_kernel(const v4i* __restrict_
   for (; i < n16; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
+// Zero fill of a workspace's flag header by a kernel (not a memset node), so
+// that it can sit inside a captured graph.
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
 }  // namespace
+
+WaitCtl wait_ctl_for_current_device() {
+  int dev = -1;
+  WaitCtl w{nullptr, 0u, kSpinLdsDefault, kSpinGlobalDefault};
+  if (hipGetDevice(&dev) != hipSuccess) return w;
+  w.status = status_word_for_device(dev);
+  if (g_forced.load()) {
+    w.bias = kForcedBias;
+    w.spin_lds = kSpinForced;
+    w.spin_global = kSpinForced;
+  }
+  return w;
+}
+
+void set_forced_wait_expiry(bool on) { g_forced.store(on); }
+
+hipError_t read_and_clear_status(uint32_t* bits) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (!status_word_for_device(dev)) return hipErrorInvalidSymbol;
+  e = hipDeviceSynchronize();
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_status_mutex);
+  uint32_t v = 0;
+  e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_wait_status), sizeof(v), 0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return e;
+  const uint32_t zero = 0;
+  e = hipMemcpyToSymbol(HIP_SYMBOL(g_wait_status), &zero, sizeof(zero), 0, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return e;
+  *bits = v;
+  return hipSuccess;
+}
+
+hipError_t launch_zero_flag_header(void* workspace, hipStream_t st) {
+  zero_words_kernel<<<dim3(1), dim3(256), 0, st>>>(static_cast<uint32_t*>(workspace),
+                                                   (int)(kFlagHeaderBytes / sizeof(uint32_t)));
+  return hipGetLastError();
+}
 
 hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t st) {
   const size_t n16 = bytes / 16;

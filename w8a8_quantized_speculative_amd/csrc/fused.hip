@@ -57,6 +57,7 @@
 
 #include "quasar_device.hpp"
 #include "quasar_internal.hpp"
+#include "quasar_sync.hpp"
 
 namespace quasar {
 namespace {
@@ -135,7 +136,7 @@ __device__ __forceinline__ void streamer(const int8_t* __restrict__ wq,
                                          const float* __restrict__ wscale, int N, int K,
                                          int first, int T, int wave, int lane,
                                          const int8_t* codes, int Ks, int32_t* red, float* wsl,
-                                         const int* ready) {
+                                         const int* ready, const WaitCtl& wc) {
   static_assert(NPH % NBUF == 0, "phase p of every tile uses buffer p % NBUF");
   // helper quantization step u covers K positions [u * 512 NH, (u + 1) * 512 NH):
   // PPS = NH / 4 phases of 8S chunks of 64
@@ -192,15 +193,9 @@ __device__ __forceinline__ void streamer(const int8_t* __restrict__ wq,
   // executes a wavefront's accesses in order, so a relaxed load plus a
   // compiler barrier suffices; an acquire would also wait for this
   // wavefront's weight loads in flight.  All helpers are resident and finish
-  // every step unconditionally; the spin is bounded all the same.
-  auto wait_codes = [&](int ph) {
-    const int* step_done = ready + ph / PPS;
-    for (int spin = 0; spin < (1 << 22); ++spin) {
-      if (__hip_atomic_load(step_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= NH) break;
-      __builtin_amdgcn_s_sleep(1);
-    }
-    asm volatile("" ::: "memory");  // keep the code reads below the wait
-  };
+  // every step unconditionally; the spin is bounded all the same (an expiry
+  // is reported in the device status word).
+  auto wait_codes = [&](int ph) { lds_wait_at_least(ready + ph / PPS, NH, wc); };
   v4i acc = {0, 0, 0, 0};
   for (int t = 0; t < T; ++t) {
     const int tile = first + t;
@@ -244,7 +239,7 @@ __device__ __forceinline__ void helper(const uint16_t* __restrict__ x, const flo
                                        int8_t* codes, int Ks, const int32_t* red, const float* wsl,
                                        float* amax_part, float* qp, int* cnt, int* ready,
                                        uint16_t* __restrict__ y, int32_t* __restrict__ acc_out,
-                                       AcceptPartials ap, int G, int swiglu) {
+                                       AcceptPartials ap, int G, int swiglu, const WaitCtl& wc) {
   constexpr int HT = 64 * NH;  // helper threads
   const int units = K >> 3;    // pieces of 8 K positions per token row
   v4i xv[UP][MT];
@@ -315,10 +310,7 @@ __device__ __forceinline__ void helper(const uint16_t* __restrict__ x, const flo
   // streamers are stalled issuing weight loads and must not gate this.  All
   // helpers are resident in this workgroup and publish unconditionally, so the
   // count is reached; the spin is bounded all the same.
-  for (int spin = 0; spin < (1 << 22); ++spin) {
-    if (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= NH) break;
-    __builtin_amdgcn_s_sleep(1);
-  }
+  lds_wait_at_least(cnt, NH, wc);
   // every helper forms the row parameters itself: lane m holds row m's
   float row_amax = 0.0f;
   if (lane < MT) {
@@ -471,7 +463,8 @@ template <int MT, int S, int NPH>
 __global__ __launch_bounds__(64 * (S + (NPH == 2 ? 4 : 8))) void w8a8_linear_fused_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ s, const int8_t* __restrict__ wq,
     const float* __restrict__ wscale, int M, int N, int K, int tq, int tr, int G,
-    uint16_t* __restrict__ y, int32_t* __restrict__ acc_out, AcceptPartials ap, int swiglu) {
+    uint16_t* __restrict__ y, int32_t* __restrict__ acc_out, AcceptPartials ap, int swiglu,
+    WaitCtl wc) {
   using Var = Variant<NPH == 2 ? 0 : (NPH == 4 ? 1 : 2)>;
   static_assert(Var::S == S && Var::NPH == NPH, "variant");
   extern __shared__ __align__(16) char smem[];
@@ -498,11 +491,11 @@ __global__ __launch_bounds__(64 * (S + (NPH == 2 ? 4 : 8))) void w8a8_linear_fus
   const int T = (b + 1) * tq + (int)((unsigned int)((b + 1) * tr) / (unsigned int)G) - first;
   if (wave < S) {
     streamer<MT, S, NPH, Var::NBUF, Var::NH>(wq, wscale, N, K, first, T, wave, lane, codes, Ks,
-                                             red, wsl, ready);
+                                             red, wsl, ready, wc);
   } else {
     helper<MT, S, Var::NH, Var::UP>(x, s, M, N, K, first, T, tid - 64 * S, wave - S, lane, codes,
                                     Ks, red, wsl, amax_part, qp, cnt, ready, y, acc_out, ap, G,
-                                    swiglu);
+                                    swiglu, wc);
   }
 }
 
@@ -528,7 +521,7 @@ __device__ __forceinline__ void streamer_w4(const int8_t* __restrict__ wq4,
                                             const float* __restrict__ wscale, int N, int K,
                                             int first, int T, int wave, int lane,
                                             const int8_t* codes, int Ks, int32_t* red, float* wsl,
-                                            const int* ready) {
+                                            const int* ready, const WaitCtl& wc) {
   constexpr int NB = 2;
   const int r = lane & 15, g = lane >> 4;
   const int ncp = K >> 7;  // 128-wide pairs of chunks
@@ -568,12 +561,7 @@ __device__ __forceinline__ void streamer_w4(const int8_t* __restrict__ wq4,
   // quantization step holding its last position (helpers finish steps in order)
   auto wait_codes = [&](int ph) {
     const int kend = min(K, (ph + 1) * S * kPH * 128) - 1;
-    const int* step_done = ready + kend / (512 * NH);
-    for (int spin = 0; spin < (1 << 22); ++spin) {
-      if (__hip_atomic_load(step_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= NH) break;
-      __builtin_amdgcn_s_sleep(1);
-    }
-    asm volatile("" ::: "memory");
+    lds_wait_at_least(ready + kend / (512 * NH), NH, wc);
   };
   const v4u hi_mask = {0xF0F0F0F0u, 0xF0F0F0F0u, 0xF0F0F0F0u, 0xF0F0F0F0u};
   v4i acc = {0, 0, 0, 0};
@@ -615,7 +603,7 @@ template <int MT, int S, int NPH4>
 __global__ __launch_bounds__(64 * (S + (NPH4 == 1 ? 4 : 8))) void w4a8_linear_fused_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ s, const int8_t* __restrict__ wq4,
     const float* __restrict__ wscale, int M, int N, int K, int tq, int tr, int G,
-    uint16_t* __restrict__ y, int32_t* __restrict__ acc_out) {
+    uint16_t* __restrict__ y, int32_t* __restrict__ acc_out, WaitCtl wc) {
   using Var = Variant<NPH4 == 1 ? 0 : (NPH4 == 2 ? 1 : 2)>;
   static_assert(Var::S == S && Var::NPH == 2 * NPH4, "variant");
   extern __shared__ __align__(16) char smem[];
@@ -640,11 +628,11 @@ __global__ __launch_bounds__(64 * (S + (NPH4 == 1 ? 4 : 8))) void w4a8_linear_fu
   const int T = (b + 1) * tq + (int)((unsigned int)((b + 1) * tr) / (unsigned int)G) - first;
   if (wave < S) {
     streamer_w4<MT, S, NPH4, Var::NH>(wq4, wscale, N, K, first, T, wave, lane, codes, Ks, red,
-                                      wsl, ready);
+                                      wsl, ready, wc);
   } else {
     helper<MT, S, Var::NH, Var::UP, 4>(x, s, M, N, K, first, T, tid - 64 * S, wave - S, lane,
                                        codes, Ks, red, wsl, amax_part, qp, cnt, ready, y, acc_out,
-                                       AcceptPartials{nullptr, nullptr, nullptr, 0.0f}, G, 0);
+                                       AcceptPartials{nullptr, nullptr, nullptr, 0.0f}, G, 0, wc);
   }
 }
 
@@ -658,9 +646,11 @@ hipError_t launch_w4(const FusedPlan& p, const uint16_t* x, const float* s, cons
                           hipFuncAttributeMaxDynamicSharedMemorySize,
                           smem_layout(Variant<NPH4 - 1>::KMAX, MT, S).bytes);
   if (attr != hipSuccess) return attr;
+  const WaitCtl wc = wait_ctl_for_current_device();
+  if (!wc.status) return hipErrorInvalidSymbol;
   kernel<<<dim3(p.grid), dim3(64 * (S + (NPH4 == 1 ? 4 : 8))), p.lds, st>>>(
       x, s, wq4, w_scale, (int)p.M, (int)p.N, (int)p.K, p.tiles / p.grid, p.tiles % p.grid,
-      p.grid, y, acc_out);
+      p.grid, y, acc_out, wc);
   return hipGetLastError();
 }
 
@@ -685,9 +675,11 @@ hipError_t launch_variant(const FusedPlan& p, const uint16_t* x, const float* s,
                           hipFuncAttributeMaxDynamicSharedMemorySize,
                           smem_layout(Var::KMAX, MT, Var::S).bytes);
   if (attr != hipSuccess) return attr;
+  const WaitCtl wc = wait_ctl_for_current_device();
+  if (!wc.status) return hipErrorInvalidSymbol;
   kernel<<<dim3(p.grid), dim3(64 * Var::WAVES), p.lds, st>>>(
       x, s, wq, w_scale, (int)p.M, (int)p.N, (int)p.K, p.tiles / p.grid, p.tiles % p.grid, p.grid,
-      y, acc_out, ap, swiglu);
+      y, acc_out, ap, swiglu, wc);
   return hipGetLastError();
 }
 

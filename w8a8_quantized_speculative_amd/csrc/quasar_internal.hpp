@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+struct quasar_chain_link;
+
 namespace quasar {
 
 constexpr int kNumCU = 256;          // MI355X: 256 compute units in 8 XCDs
@@ -101,6 +103,19 @@ hipError_t launch_wide(const WidePlan& p, const uint16_t* x, const float* s, con
                        hipStream_t st);
 
 // ---------------------------------------------------------------------------
+// Chained linears (M <= 8): one persistent launch over a list of links
+// (quasar_chain_link), each waiting for the link that writes its input.
+// ---------------------------------------------------------------------------
+constexpr int kChainMaxK = 12288;
+int chain_lds_bytes(int M, int Kmax);
+const char* chain_kernel_name(int M);
+// `partials` (optional) receive the accept partials of the LAST link, as the
+// one-launch kernel's LM-head epilogue writes them ([row * G + workgroup]).
+// links_dev: a device copy of the links; workspace: its flag header first.
+hipError_t launch_chain(const struct quasar_chain_link* links_dev, int n, int M, int Kmax, int G,
+                        void* workspace, const AcceptPartials* partials, hipStream_t st);
+
+// ---------------------------------------------------------------------------
 // Accept plan: each logits row is cut into `chunks` pieces of `chunk_len`.
 // ---------------------------------------------------------------------------
 constexpr int kAcceptChunk = 2048;  // widest chunk the accept finalize scans (8 per thread)
@@ -166,5 +181,8 @@ hipError_t launch_silu_mul(const uint16_t* gu, int64_t M, int64_t I, uint16_t* o
 
 // Diagnostic plain copy (16-byte vectors), bytes % 16 == 0.
 hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
+// Zero the flag header at the start of a workspace (a kernel, so it can be
+// captured in a graph).
+hipError_t launch_zero_flag_header(void* workspace, hipStream_t st);
 
 }  // namespace quasar

@@ -53,24 +53,25 @@
 // another.  The streamers touch LDS only through inline assembly: the
 // compiler cannot tell their LDS words from the slots the direct-to-LDS loads
 // write and would otherwise wait for every load in flight before each access,
-// while LDS executes a wavefront's accesses in issue order anyway.  Across workgroups it uses one flag word per workgroup in module
-// memory: each launch bumps every workgroup's flag by exactly one, so a flag
-// equal to its owner's pre-launch value plus one marks this launch's data.
-// The grid is one workgroup per compute unit and all of them must be resident
-// at once; every wait is bounded, so a grid that cannot be co-resident ends
-// (with undefined outputs) instead of hanging.
+// while LDS executes a wavefront's accesses in issue order anyway.
+//
+// Across workgroups it uses the flag header of the caller's workspace (the
+// protocol of quasar_sync.hpp): row flags (word b: workgroup b's token row is
+// in the workspace) and partial flags (word 256 + b: its partial sum of a
+// shared group is).  Workgroup b reads its row flag e at the start and raises
+// it to e + 1 once per launch, so a flag equal to e + 1 marks this launch's
+// data; the header must hold equal words (zeros) before the workspace's first
+// use and is never reset.  The grid is one workgroup per compute unit and all
+// of them must be resident at once; every wait is bounded, and one that gives
+// up sets a bit of the device status word (undefined outputs) instead of
+// hanging.
+#include <mutex>
+
 #include "quasar_device.hpp"
 #include "quasar_internal.hpp"
+#include "quasar_sync.hpp"
 
 namespace quasar {
-
-// Per-workgroup launch counters: row flags (the workgroup's token row is in
-// the workspace) and partial flags (its partial sum of a shared group is).
-// Zero at module load; launch e (0-based) leaves both at e + 1 for every
-// workgroup b < grid (the partial flag only for workgroups that wrote one).
-__device__ uint32_t g_wide_row_flag[kWideMaxGrid];
-__device__ uint32_t g_wide_part_flag[kWideMaxGrid];
-
 namespace {
 
 constexpr int kS = 4;        // streamer wavefronts (one 64-wide K chunk each per item)
@@ -78,8 +79,6 @@ constexpr int kMaxTG = 4;    // 16-channel tiles per group: 1 or 4
 constexpr int kHelpers = 4;  // row quantizer, then epilogue wavefronts
 constexpr int kThreads = 64 * (kS + kHelpers);
 constexpr int kRowPieces = 8;  // 8-element pieces per helper thread kept in registers
-constexpr int kSpinLds = 1 << 22;
-constexpr int kSpinGlobal = 1 << 20;
 
 // s_waitcnt immediate for "at most n vector-memory operations outstanding"
 // (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt at their
@@ -157,10 +156,18 @@ __device__ __forceinline__ void lds_wait_reads() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
-// Bounded wait until an LDS counter reaches `target`, for the streamers.
-__device__ __forceinline__ void lds_wait_ge_asm(uint32_t addr, int target) {
-  for (int spin = 0; spin < kSpinLds; ++spin) {
-    if (lds_read_asm(addr) >= target) break;
+// Bounded wait until an LDS counter reaches `target`, for the streamers.  On
+// expiry the status word is set with a global atomic: it counts as one more
+// outstanding vector-memory operation, which only makes the streamers' exact
+// waits below wait for one more load.
+__device__ __forceinline__ void lds_wait_ge_asm(uint32_t addr, int target, const WaitCtl& wc) {
+  const int t = target + (int)wc.bias;
+  for (int spin = 0;; ++spin) {
+    if (lds_read_asm(addr) >= t) break;
+    if (spin >= wc.spin_lds) {
+      note_expired(wc, kWaitLds);
+      break;
+    }
     __builtin_amdgcn_s_sleep(1);
   }
 }
@@ -173,10 +180,9 @@ __device__ __forceinline__ void lds_add(int* p, int v) {
   __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// Stores another workgroup reads during the same launch: device-scope
-// (write-through) stores, so a workgroup on another XCD -- whose L2 does not
-// hold the line, as every launch starts with invalidated caches and the line is
-// read only after its flag -- fetches the new value.
+// Stores another workgroup reads during the same launch: agent-scope
+// (write-through) stores, ordered before the flag that publishes them by a
+// release fence (quasar_sync.hpp).
 __device__ __forceinline__ void store8_device(void* p, uint2 v) {
   __hip_atomic_store(reinterpret_cast<uint64_t*>(p),
                      (uint64_t)v.x | ((uint64_t)v.y << 32), __ATOMIC_RELAXED,
@@ -196,14 +202,6 @@ __device__ __forceinline__ void wait_stores_done() {
   asm volatile("" ::: "memory");
 }
 
-// Bounded wait until an LDS counter reaches `target` (plain-read wavefronts).
-__device__ __forceinline__ void lds_wait_ge(const int* p, int target) {
-  for (int spin = 0; spin < kSpinLds; ++spin) {
-    if (lds_load(p) >= target) break;
-    __builtin_amdgcn_s_sleep(1);
-  }
-  asm volatile("" ::: "memory");  // later LDS reads stay below the wait
-}
 
 // Item ranges: the (group, item) sequence of U items is split into G equal
 // contiguous ranges.
@@ -219,7 +217,7 @@ __device__ __forceinline__ void wide_streamer(const int8_t* __restrict__ wq,
                                               const int8_t* __restrict__ qx, int M, int K,
                                               int tiles, int nch, int P, int i0, int n, int w,
                                               int lane, bool quantizer, char* slots,
-                                              int32_t* red, int* sync) {
+                                              int32_t* red, int* sync, const WaitCtl& wc) {
   using C = Wide<MB, TG>;
   constexpr int NB = C::NBUF;
   const int voff = lane * 16;
@@ -261,7 +259,7 @@ __device__ __forceinline__ void wide_streamer(const int8_t* __restrict__ wq,
     for (int tb = 0; tb < MB; ++tb)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           qrs, (__attribute__((address_space(3))) void*)(my_slots + (bb * MB + tb) * 1024), 16,
-          live ? lane_off + (tb * nch + c) * 1024 : kOutOfRange, 0, 0, 0);
+          live ? lane_off + (tb * nch + c) * 1024 : kOutOfRange, 0, 0, kCoherent);
     ++cissued;
     if (++cp_issue == P) cp_issue = 0;
   };
@@ -274,11 +272,11 @@ __device__ __forceinline__ void wide_streamer(const int8_t* __restrict__ wq,
   // starts once the row is out, so those stores do not queue behind it.  (The
   // other workgroups' first weights have landed by the time the flags are
   // polled.)
-  if (quantizer) lds_wait_ge_asm(lds_address(sync + kFlagOut), 1);
+  if (quantizer) lds_wait_ge_asm(lds_address(sync + kFlagOut), 1, wc);
 #pragma unroll
   for (int bb = 0; bb < NB; ++bb) issue_weights(bb);
   // the codes exist once every token row of the launch is in the workspace
-  lds_wait_ge_asm(lds_address(sync + kGate), 1);
+  lds_wait_ge_asm(lds_address(sync + kGate), 1, wc);
 #pragma unroll
   for (int bb = 0; bb < NB; ++bb) issue_codes(bb);
   __builtin_amdgcn_sched_barrier(0);  // keep the loop below from rotating into the issues
@@ -336,7 +334,7 @@ __device__ __forceinline__ void wide_streamer(const int8_t* __restrict__ wq,
           for (int tt = 0; tt < TG; ++tt) {
             const int par = round & 1;
             if (round >= 2)
-              lds_wait_ge_asm(lds_address(sync + kRedFree + par), kHelpers * (round >> 1));
+              lds_wait_ge_asm(lds_address(sync + kRedFree + par), kHelpers * (round >> 1), wc);
 #pragma unroll
             for (int tb = 0; tb < MB; ++tb) {
               lds_write16_asm(red_addr + (par * kS * MB + tb) * 1024, acc[tt][tb]);
@@ -360,7 +358,7 @@ __device__ __forceinline__ void quantize_row_compute(const uint16_t* __restrict_
                                                      int ht, int hw, int lane, const v4i (&xv)[kRowPieces],
                                                      const v4i (&sv)[kRowPieces][2], bool in_regs,
                                                      int8_t* __restrict__ qx, float* __restrict__ sx,
-                                                     int* sync) {
+                                                     int* sync, const WaitCtl& wc) {
   const int units = K >> 3;
   const buffer_rsrc xrs = make_rsrc(x + (size_t)m * K, (uint32_t)K * 2u);
   const buffer_rsrc srs = make_rsrc(s, (uint32_t)K * 4u);
@@ -400,7 +398,7 @@ __device__ __forceinline__ void quantize_row_compute(const uint16_t* __restrict_
     asm volatile("" ::: "memory");
     lds_add(sync + kAmaxCnt, 1);
   }
-  lds_wait_ge(sync + kAmaxCnt, kHelpers);
+  lds_wait_at_least(sync + kAmaxCnt, kHelpers, wc);
   float row_amax = 0.0f;
 #pragma unroll
   for (int h = 0; h < kHelpers; ++h) row_amax = fmaxf(row_amax, amax_part[h]);
@@ -444,17 +442,18 @@ __device__ __forceinline__ void quantize_row_compute(const uint16_t* __restrict_
 // ---------------------------------------------------------------------------
 // Helper prologue: quantize token row b (b < M) into the workspace and raise
 // this workgroup's row flag, then wait until every token row of the launch is
-// there (helper wavefront 0 polls the flags with
-// device-scope loads; the rows are read only after this).  Contains the
-// workgroup barrier (1).  Returns false when the workgroup has no items; `e`
-// is this workgroup's launch count before the launch.
+// there (helper wavefront 0 polls the flags with agent-scope loads, then
+// acquires; the rows are read only after this).  Contains the workgroup
+// barrier (1).  Returns false when the workgroup has no items; `e` is this
+// workgroup's row flag before the launch.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bool wide_rows_and_gate(const uint16_t* __restrict__ x,
                                                    const float* __restrict__ s, int M, int K, int b,
                                                    int n, int ht, int hw, int lane,
                                                    int8_t* __restrict__ qx, float* __restrict__ sx,
-                                                   int* sync, uint32_t& e) {
-  e = __hip_atomic_load(&g_wide_row_flag[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                                                   uint32_t* row_flag, int* sync, uint32_t& e,
+                                                   const WaitCtl& wc) {
+  e = load_flag(row_flag + b);
   const bool quantizer = b < M;
   const int units = K >> 3;
   const bool in_regs = units <= kRowPieces * 64 * kHelpers;
@@ -473,34 +472,40 @@ __device__ __forceinline__ bool wide_rows_and_gate(const uint16_t* __restrict__ 
   }
   __syncthreads();  // (1)
 
-  // Row codes and scale go out with device-scope stores; once every helper
-  // wavefront's stores have completed, the row flag is raised.
+  // Row codes and scale go out with agent-scope stores; once every helper
+  // wavefront's stores have completed, the row flag is raised behind a
+  // release fence.
   if (quantizer) {
-    quantize_row_compute(x, s, b, K, ht, hw, lane, xv, sv, in_regs, qx, sx, sync);
+    quantize_row_compute(x, s, b, K, ht, hw, lane, xv, sv, in_regs, qx, sx, sync, wc);
     wait_stores_done();
     if (lane == 0) lds_add(sync + kRowDone, 1);
   }
   if (ht == 0) {
-    if (quantizer) lds_wait_ge(sync + kRowDone, kHelpers);
-    __hip_atomic_store(&g_wide_row_flag[b], e + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (quantizer) lds_wait_at_least(sync + kRowDone, kHelpers, wc);
+    store_flag(row_flag + b, e + 1u);
     asm volatile("" ::: "memory");
     lds_add(sync + kFlagOut, 1);  // the flag is queued ahead of the weight stream
   }
   if (n == 0) return false;
 
   if (hw == 0) {
-    for (int spin = 0; spin < kSpinGlobal; ++spin) {
+    const uint32_t target = e + 1u + wc.bias;
+    bool ok = false;
+    for (int spin = 0;; ++spin) {
       bool ready = true;
-      for (int m = lane; m < M; m += 64)
-        ready &= __hip_atomic_load(&g_wide_row_flag[m], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT) == e + 1u;
-      if (__builtin_amdgcn_ballot_w64(!ready) == 0) break;
+      for (int m = lane; m < M; m += 64) ready &= load_flag(row_flag + m) == target;
+      if (__builtin_amdgcn_ballot_w64(!ready) == 0) {
+        ok = true;
+        break;
+      }
+      if (spin >= wc.spin_global) break;
       __builtin_amdgcn_s_sleep(1);
     }
-    asm volatile("" ::: "memory");
+    if (!ok && lane == 0) note_expired(wc, kWaitRows);
+    after_poll();
     if (lane == 0) lds_add(sync + kGate, 1);
   } else {
-    lds_wait_ge(sync + kGate, 1);
+    lds_wait_at_least(sync + kGate, 1, wc);
   }
   return true;
 }
@@ -518,9 +523,9 @@ __device__ __forceinline__ void wide_epilogue(const float* __restrict__ wscale,
                                               const float* __restrict__ sx, int M, int N, int P,
                                               int U, int G, int b, int i0, int n, uint32_t e,
                                               int et, int lane, const int32_t* red, int* sync,
-                                              int32_t* __restrict__ partials,
+                                              int32_t* __restrict__ partials, uint32_t* part_flag,
                                               uint16_t* __restrict__ y,
-                                              int32_t* __restrict__ acc_out) {
+                                              int32_t* __restrict__ acc_out, const WaitCtl& wc) {
   constexpr int KS = (MB + 3) / 4;           // slots per thread and round
   constexpr int kPartInts = kMaxTG * MB * 256;  // one workgroup's partial-sum slot
   const int ln = et & 63;
@@ -528,7 +533,7 @@ __device__ __forceinline__ void wide_epilogue(const float* __restrict__ wscale,
 #pragma unroll
   for (int k = 0; k < KS; ++k) {
     const int tok = ((et >> 6) + 4 * k) * 16 + (ln & 15);
-    sxv[k] = tok < M ? sx[tok] : 0.0f;
+    sxv[k] = tok < M ? load_coherent(sx + tok) : 0.0f;  // written by workgroup tok
   }
   const buffer_rsrc wrs = make_rsrc(wscale, (uint32_t)N * 4u);
   float ws[TG][4];  // weight scales of the group's 4 channels per tile of this thread
@@ -555,28 +560,31 @@ __device__ __forceinline__ void wide_epilogue(const float* __restrict__ wscale,
       // inside group g (each wrote its partial sum of g first, then its flag)
       for (int c = b + 1; c < G && range_start(c, U, G) < (g + 1) * P; ++c) {
         if (range_start(c + 1, U, G) == range_start(c, U, G)) continue;  // empty range
-        for (int spin = 0; spin < kSpinGlobal; ++spin) {
-          if (__hip_atomic_load(&g_wide_part_flag[c], __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT) == e + 1u)
+        for (int spin = 0;; ++spin) {
+          if (load_flag(part_flag + c) == e + 1u + wc.bias) break;
+          if (spin >= wc.spin_global) {
+            if (lane == 0) note_expired(wc, kWaitPartials);
             break;
+          }
           __builtin_amdgcn_s_sleep(1);
         }
-        asm volatile("" ::: "memory");  // the partial sums are read after the flag
-        const int32_t* pc = partials + (size_t)c * kPartInts;
+        after_poll();  // the partial sums are read after the flag, agent-scope
+        const buffer_rsrc prs =
+            make_rsrc(partials + (size_t)c * kPartInts, (uint32_t)kPartInts * 4u);
 #pragma unroll
         for (int tt = 0; tt < TG; ++tt)
 #pragma unroll
           for (int k = 0; k < KS; ++k) {
             const int sidx = et + 256 * k;
             if (sidx < MB * 64)
-              other[tt][k] += *reinterpret_cast<const v4i*>(pc + (tt * MB + (sidx >> 6)) * 256 + ln * 4);
+              other[tt][k] += load16<kCoherent>(prs, ((tt * MB + (sidx >> 6)) * 256 + ln * 4) * 4);
           }
       }
     }
 #pragma unroll
     for (int tt = 0; tt < TG; ++tt) {
       const int par = round & 1;
-      lds_wait_ge(sync + kRedReady + par, kS * ((round >> 1) + 1));
+      lds_wait_at_least(sync + kRedReady + par, kS * ((round >> 1) + 1), wc);
       const int n0 = (g * TG + tt) * 16 + 4 * (ln >> 4);
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
@@ -627,9 +635,8 @@ __device__ __forceinline__ void wide_epilogue(const float* __restrict__ wscale,
       wait_stores_done();
       if (lane == 0) lds_add(sync + kPartDone, 1);
       if (et == 0) {
-        lds_wait_ge(sync + kPartDone, kHelpers);
-        __hip_atomic_store(&g_wide_part_flag[b], e + 1u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        lds_wait_at_least(sync + kPartDone, kHelpers, wc);
+        store_flag(part_flag + b, e + 1u);
       }
     }
   }
@@ -644,7 +651,8 @@ __global__ __launch_bounds__(kThreads) void w8a8_linear_wide_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ s, const int8_t* __restrict__ wq,
     const float* __restrict__ wscale, int M, int N, int K, int tiles, int P, int U,
     int8_t* __restrict__ qx, float* __restrict__ sx, int32_t* __restrict__ partials,
-    uint16_t* __restrict__ y, int32_t* __restrict__ acc_out) {
+    uint32_t* __restrict__ flags, uint16_t* __restrict__ y, int32_t* __restrict__ acc_out,
+    WaitCtl wc) {
   using C = Wide<MB, TG>;
   extern __shared__ __align__(16) char smem[];
   char* slots = smem;
@@ -661,46 +669,49 @@ __global__ __launch_bounds__(kThreads) void w8a8_linear_wide_kernel(
 
   if (wave < kS) {
     wide_streamer<MB, TG>(wq, qx, M, K, tiles, nch, P, i0, n, wave, lane, b < M, slots, red,
-                          sync);
+                          sync, wc);
     return;
   }
 
   // ---- helpers
   const int ht = tid - 64 * kS;
   uint32_t e;
-  if (!wide_rows_and_gate(x, s, M, K, b, n, ht, wave - kS, lane, qx, sx, sync, e)) return;
-  wide_epilogue<MB, TG>(wscale, sx, M, N, P, U, G, b, i0, n, e, ht, lane, red, sync, partials, y,
-                        acc_out);
+  if (!wide_rows_and_gate(x, s, M, K, b, n, ht, wave - kS, lane, qx, sx, flags, sync, e, wc))
+    return;
+  wide_epilogue<MB, TG>(wscale, sx, M, N, P, U, G, b, i0, n, e, ht, lane, red, sync, partials,
+                        flags + kFlagSlots, y, acc_out, wc);
 }
 
 template <int MB, int TG>
 hipError_t launch_wide_mb(const WidePlan& p, const uint16_t* x, const float* s, const int8_t* wq,
                           const float* w_scale, uint16_t* y, int32_t* acc_out, int8_t* qx,
-                          float* sx, int32_t* partials, hipStream_t st) {
+                          float* sx, int32_t* partials, uint32_t* flags, const WaitCtl& wc,
+                          hipStream_t st) {
   auto kernel = &w8a8_linear_wide_kernel<MB, TG>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
       Wide<MB, TG>::LDS);
   if (attr != hipSuccess) return attr;
   kernel<<<dim3(p.grid), dim3(kThreads), Wide<MB, TG>::LDS, st>>>(
-      x, s, wq, w_scale, (int)p.M, (int)p.N, (int)p.K, p.tiles, p.P, p.U, qx, sx, partials, y,
-      acc_out);
+      x, s, wq, w_scale, (int)p.M, (int)p.N, (int)p.K, p.tiles, p.P, p.U, qx, sx, partials, flags,
+      y, acc_out, wc);
   return hipGetLastError();
 }
 
 template <int TG>
 hipError_t launch_wide_tg(const WidePlan& p, const uint16_t* x, const float* s, const int8_t* wq,
                           const float* w_scale, uint16_t* y, int32_t* acc_out, int8_t* qx,
-                          float* sx, int32_t* partials, hipStream_t st) {
+                          float* sx, int32_t* partials, uint32_t* flags, const WaitCtl& wc,
+                          hipStream_t st) {
   switch (p.mb) {
-    case 1: return launch_wide_mb<1, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
-    case 2: return launch_wide_mb<2, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
-    case 3: return launch_wide_mb<3, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
-    case 4: return launch_wide_mb<4, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
-    case 5: return launch_wide_mb<5, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
-    case 6: return launch_wide_mb<6, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
-    case 7: return launch_wide_mb<7, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
-    case 8: return launch_wide_mb<8, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
+    case 1: return launch_wide_mb<1, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st);
+    case 2: return launch_wide_mb<2, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st);
+    case 3: return launch_wide_mb<3, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st);
+    case 4: return launch_wide_mb<4, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st);
+    case 5: return launch_wide_mb<5, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st);
+    case 6: return launch_wide_mb<6, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st);
+    case 7: return launch_wide_mb<7, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st);
+    case 8: return launch_wide_mb<8, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -746,7 +757,7 @@ WidePlan plan_wide(int64_t M, int64_t N, int64_t K, int grid) {
   p.U = p.groups * p.P;
   p.grid = grid;
   p.lds = wide_lds_of(p.mb, p.tg);
-  size_t off = 0;
+  size_t off = kFlagHeaderBytes;  // the flag header (quasar_sync.hpp) comes first
   p.off_qx = off;  // fragment-major codes: 1 KB per 16-token block and 64-wide K chunk
   off = align_up(off + (size_t)p.mb * p.nch * 1024, kWsAlign);
   p.off_sx = off;
@@ -777,21 +788,28 @@ hipError_t launch_wide(const WidePlan& p, const uint16_t* x, const float* s, con
   int8_t* qx = reinterpret_cast<int8_t*>(ws + p.off_qx);
   float* sx = reinterpret_cast<float*>(ws + p.off_sx);
   int32_t* partials = reinterpret_cast<int32_t*>(ws + p.off_partials);
-  if (p.tg == 1) return launch_wide_tg<1>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
+  uint32_t* flags = reinterpret_cast<uint32_t*>(ws);
+  const WaitCtl wc = wait_ctl_for_current_device();
+  if (!wc.status) return hipErrorInvalidSymbol;
+  if (p.tg == 1)
+    return launch_wide_tg<1>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st);
   if (p.tg == kMaxTG)
-    return launch_wide_tg<kMaxTG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, st);
+    return launch_wide_tg<kMaxTG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc,
+                                  st);
   return hipErrorInvalidValue;
 }
 
 // Workgroups the wide kernel launches on the current device: one per compute
 // unit, at most kWideMaxGrid; 0 if one workgroup does not fit a compute unit.
-// Fixed per device for the life of the process (the launch counters rely on
+// Fixed per device for the life of the process (the workspace flags rely on
 // every launch using the same grid).
 int wide_grid_for_current_device() {
+  static std::mutex mu;
   static int cache[64];
   static bool init[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lock(mu);
   if (!init[dev]) {
     int cus = 0, occ = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
