@@ -247,6 +247,25 @@ quasar_status quasar_w8a8_linear(const uint16_t* x, const float* s, const int8_t
                                  uint16_t* y, int32_t* acc_out, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/*
+ * quasar_w8a8_linear_noalloc -- for callers that cannot allocate memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): quasar_w8a8_linear with the same arguments minus the
+ * workspace, and the same results bit for bit.  Shapes that need a workspace
+ * use a scratch array the library holds in device memory instead, one per
+ * device, QUASAR_NOALLOC_SCRATCH_BYTES (12 MiB) large, kept until the process
+ * ends; the call allocates nothing.  Every call on a device shares that
+ * device's array: two such calls whose kernels overlap in time (on different
+ * streams) race and their results are undefined; calls ordered on one stream
+ * are safe.  Errors: as quasar_w8a8_linear, and UNSUPPORTED when the shape's
+ * workspace (quasar_w8a8_workspace_bytes) exceeds the scratch -- every
+ * M <= 128 with K <= 16384 fits.
+ */
+#define QUASAR_NOALLOC_SCRATCH_BYTES (12u << 20)
+quasar_status quasar_w8a8_linear_noalloc(const uint16_t* x, const float* s, const int8_t* wq,
+                                         const float* w_scale, int64_t M, int64_t N, int64_t K,
+                                         uint16_t* y, int32_t* acc_out, void* stream);
+
 /* Workspace bytes quasar_verify_accept needs (pure host function). */
 size_t quasar_accept_workspace_bytes(int64_t B, int64_t k, int64_t V);
 

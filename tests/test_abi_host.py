@@ -366,3 +366,17 @@ def test_chain_verify_argument_errors(L):
     assert cv(T=1.0, u=None) == INVALID
     assert cv(draft=None) == INVALID
     assert cv(lk=chain_links(l1_flags=1)) == INVALID                 # the head is not gated
+
+
+def test_noalloc_argument_errors(L):
+    na = lambda M=16, N=32, K=64, x=FAKE, y=FAKE: L.quasar_w8a8_linear_noalloc(
+        x, FAKE, FAKE, FAKE, M, N, K, y, None, None)
+    assert na(M=-1) == INVALID
+    assert na(K=72) == INVALID
+    assert na(M=0) == OK
+    assert na(x=None) == INVALID
+    assert na(y=FAKE + 1) == INVALID
+    assert na(M=129) == UNSUPPORTED
+    # the scratch holds the workspace of M <= 128 at K <= 16384, not more
+    assert na(M=128, N=64, K=65536) == UNSUPPORTED
+    assert L.quasar_w8a8_workspace_bytes(128, 151936, 16384) <= 12 << 20

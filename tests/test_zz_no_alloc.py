@@ -1,0 +1,51 @@
+"""quasar_w8a8_linear_noalloc (the entry point for callers that cannot
+allocate) against quasar_w8a8_linear on the same inputs: bit-identical outputs
+and INT32 accumulators, on two calls in a row -- the second with a smaller
+input, so the library's scratch still holds the first call's contents -- for
+wide windows (the kernel that uses the scratch), and on a small window (no
+scratch).  The first case is also checked against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import quasar_oracle as orc
+from w8a8_quantized_speculative_amd import binding, synth
+from tests.gpu_helpers import announce, dev, dev_bf16, host, host_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def both(M, N, K, key):
+    x, w, s = synth.linear_case(M, K, N, key)
+    wq, sw = binding.quasar_quantize_weights(dev_bf16(w), dev(s))
+    xd, sd = dev_bf16(x), dev(s)
+    acc_a = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    acc_b = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    y_a = binding.quasar_w8a8_linear(xd, sd, wq, sw, acc_out=acc_a)
+    y_b = binding.quasar_w8a8_linear_noalloc(xd, sd, wq, sw, acc_out=acc_b)
+    torch.cuda.synchronize()
+    return x, w, s, host_bf16(y_a), host(acc_a), host_bf16(y_b), host(acc_b)
+
+
+def test_noalloc_matches_the_workspace_call_on_calls_in_a_row():
+    binding.device_check()
+    for i, (M, N, K) in enumerate([(96, 4096, 4096), (40, 1000, 2112), (17, 300, 1024),
+                                   (6, 2048, 4096)]):
+        announce("noalloc", M, N, K)
+        x, w, s, y_a, acc_a, y_b, acc_b = both(M, N, K, (97, i))
+        assert np.array_equal(y_a, y_b) and np.array_equal(acc_a, acc_b), (M, N, K)
+        if i == 1:
+            ref = orc.w8a8_linear_rows(x, s, w)
+            assert np.array_equal(acc_b, ref["acc"].astype(np.int32))
+            assert np.array_equal(y_b, ref["y"])
+    assert binding.device_check() == (binding.QUASAR_OK, 0)
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch():
+    x = torch.zeros((128, 65536), dtype=torch.bfloat16, device="cuda")
+    s = torch.ones(65536, dtype=torch.float32, device="cuda")
+    wq = binding.PackedWeights(torch.zeros(1024 * 1024, dtype=torch.int8, device="cuda"), 16, 65536)
+    sw = torch.ones(16, dtype=torch.float32, device="cuda")
+    with pytest.raises(binding.QuasarError) as e:
+        binding.quasar_w8a8_linear_noalloc(x, s, wq, sw)
+    assert e.value.status == binding.QUASAR_ERR_UNSUPPORTED

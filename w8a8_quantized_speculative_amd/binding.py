@@ -52,6 +52,7 @@ _SIGNATURES = {
     "quasar_packed_weight_bytes": (_SZ, [_I64, _I64]),
     "quasar_w8a8_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "quasar_w8a8_linear": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _SZ, _P]),
+    "quasar_w8a8_linear_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P]),
     "quasar_accept_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "quasar_verify_accept": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P,
                                             _P, _P, _P, _SZ, _P]),
@@ -272,6 +273,25 @@ def quasar_w8a8_linear(x: torch.Tensor, s: torch.Tensor, wq: PackedWeights, w_sc
     _check("quasar_w8a8_linear", lib().quasar_w8a8_linear(
         _ptr(x), _ptr(s), _ptr(wq), _ptr(w_scale), M, N, K, _ptr(out), _ptr(acc_out),
         _ptr(workspace), nbytes, _stream()))
+    return out
+
+
+def quasar_w8a8_linear_noalloc(x: torch.Tensor, s: torch.Tensor, wq: PackedWeights,
+                               w_scale: torch.Tensor, out: torch.Tensor | None = None,
+                               acc_out: torch.Tensor | None = None) -> torch.Tensor:
+    """quasar_w8a8_linear without a workspace (the library's own scratch)."""
+    M, K = x.shape
+    N = wq.N
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(s, torch.float32, (K,), "s")
+    _need(w_scale, torch.float32, (N,), "w_scale")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(out, torch.bfloat16, (M, N), "out")
+    if acc_out is not None:
+        _need(acc_out, torch.int32, (M, N), "acc_out")
+    _check("quasar_w8a8_linear_noalloc", lib().quasar_w8a8_linear_noalloc(
+        _ptr(x), _ptr(s), _ptr(wq), _ptr(w_scale), M, N, K, _ptr(out), _ptr(acc_out), _stream()))
     return out
 
 

@@ -259,6 +259,30 @@ quasar_status quasar_w8a8_linear(const uint16_t* x, const float* s, const int8_t
   return hip_status(launch_wide(p, x, s, wq, w_scale, y, acc_out, workspace, hs));
 }
 
+quasar_status quasar_w8a8_linear_noalloc(const uint16_t* x, const float* s, const int8_t* wq,
+                                         const float* w_scale, int64_t M, int64_t N, int64_t K,
+                                         uint16_t* y, int32_t* acc_out, void* stream) {
+  if (M < 0 || N < 0) return QUASAR_ERR_INVALID_ARG;
+  quasar_status st = check_k(K);
+  if (st != QUASAR_OK) return st;
+  if (M > QUASAR_MAX_M || N > kMaxRowsPerCall) return QUASAR_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return QUASAR_OK;
+  if (!x || !s || !wq || !w_scale || !y) return QUASAR_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(s, 16) || !aligned(wq, 16) || !aligned(w_scale, 4) ||
+      !aligned(y, 2) || (acc_out && !aligned(acc_out, 4)))
+    return QUASAR_ERR_INVALID_ARG;
+  hipStream_t hs = (hipStream_t)stream;
+  if (fused_supported(M, K))  // no scratch needed
+    return hip_status(launch_fused(plan_fused(M, N, K), x, s, wq, w_scale, y, acc_out, hs));
+  WidePlan p = plan_wide(M, N, K, kWideMaxGrid);
+  if (p.bytes > kNoAllocScratchBytes) return QUASAR_ERR_UNSUPPORTED;
+  void* scratch = noalloc_scratch_for_current_device();
+  if (!scratch) return QUASAR_ERR_HIP;
+  p.grid = wide_grid_for_current_device();
+  if (p.grid < M) return QUASAR_ERR_UNSUPPORTED;
+  return hip_status(launch_wide(p, x, s, wq, w_scale, y, acc_out, scratch, hs));
+}
+
 size_t quasar_w8a8_linear_swiglu_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || N % 16 != 0 || check_k(K) != QUASAR_OK || M > QUASAR_MAX_M ||
       N > kMaxRowsPerCall)

@@ -98,6 +98,10 @@ const char* wide_kernel_name(int mb, int tg);
 int wide_tiles_per_group(int64_t M, int64_t N, int64_t K, int grid);
 // Workgroups of a wide launch on the current device (0: cannot run there).
 int wide_grid_for_current_device();
+// quasar_w8a8_linear_noalloc: the wide kernel's workspace in library device
+// memory (one array per device); its address on the current device, or null.
+constexpr size_t kNoAllocScratchBytes = (size_t)12 << 20;
+void* noalloc_scratch_for_current_device();
 hipError_t launch_wide(const WidePlan& p, const uint16_t* x, const float* s, const int8_t* wq,
                        const float* w_scale, uint16_t* y, int32_t* acc_out, void* workspace,
                        hipStream_t st);

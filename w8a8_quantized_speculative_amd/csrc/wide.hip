@@ -799,6 +799,28 @@ hipError_t launch_wide(const WidePlan& p, const uint16_t* x, const float* s, con
   return hipErrorInvalidValue;
 }
 
+// Scratch of quasar_w8a8_linear_noalloc: the wide kernel's workspace (flag
+// header, quantized rows, token scales, INT32 partials) in a file-scope device
+// array, one per device, zero at load (so its flag header starts valid) and
+// held until the process ends.  Host code never passes the array's name to a
+// kernel: it takes the device address from hipGetSymbolAddress once per
+// device and uses that.
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+void* noalloc_scratch_for_current_device() {
+  static std::mutex mu;
+  static void* ptr[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptr[dev] = p;
+  }
+  return ptr[dev];
+}
+
 // Workgroups the wide kernel launches on the current device: one per compute
 // unit, at most kWideMaxGrid; 0 if one workgroup does not fit a compute unit.
 // Fixed per device for the life of the process (the workspace flags rely on
