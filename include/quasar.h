@@ -103,7 +103,7 @@ quasar_status quasar_device_check(uint32_t* detail);
 void quasar_debug_force_wait_expiry(int on);
 
 /* Bytes of the flag header at the start of every workspace (see the
- * conventions above): 2048. */
+ * conventions above): 65536 (each flag word alone in a 128-byte line). */
 size_t quasar_workspace_header_bytes(void);
 
 /*
@@ -193,7 +193,7 @@ quasar_status quasar_quantize_activations(const uint16_t* x, const float* s, int
 /* Workspace bytes quasar_w8a8_linear needs for this shape.  Pure host
  * function, deterministic in (M, N, K).  It is 0 for an empty call and for
  * verify windows of M <= 8 tokens with K <= 12288, which keep the quantized
- * activations in on-chip memory; other shapes need the flag header (2 KB) and
+ * activations in on-chip memory; other shapes need the flag header (64 KB) and
  * stage the quantized activations and the INT32 partial sums of output groups
  * shared by two workgroups in the workspace (1 KB per 16-token block and
  * 64-wide K chunk, 4*M bytes, and 16 KB per 16-token block and compute unit,
@@ -626,6 +626,15 @@ quasar_status quasar_silu_mul(const uint16_t* gate_up, int64_t M, int64_t I, uin
  * reading the hardware's memory byte counters.  Errors: INVALID_ARG, HIP.
  */
 quasar_status quasar_stream_copy(const void* src, void* dst, size_t bytes, void* stream);
+
+/*
+ * quasar_stream_read -- diagnostic, not part of the method: reads `bytes`
+ * bytes at src (16-byte aligned, a multiple of 16) with 16-byte streaming loads
+ * and writes nothing meaningful (sink: 1024 words of scratch, device memory).
+ * The reference rate of a read-only HBM stream, the shape of the verify
+ * linears' traffic.  Errors: INVALID_ARG, HIP.
+ */
+quasar_status quasar_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -57,7 +57,7 @@ def test_status_strings(L):
 
 def test_workspace_header_and_init_errors(L):
     hdr = L.quasar_workspace_header_bytes()
-    assert hdr == 2048
+    assert hdr == 65536
     # every workspace that carries flags starts with the header
     for M, N, K in [(96, 4096, 12288), (9, 16, 16), (6, 64, 16384)]:
         assert L.quasar_w8a8_workspace_bytes(M, N, K) >= hdr + M * K
@@ -220,15 +220,18 @@ def test_kernel_name_names_the_launch_plan(L):
     assert name(1, 16, 16) == "w8a8_linear_fused_kernel<2, 4, 2>"
     assert name(8, 4096, 8192) == "w8a8_linear_fused_kernel<8, 4, 4>"
     # wider windows (or K > 12288): one launch over ceil(M / 16) token blocks
-    # <token blocks, tiles per group>: one tile per group up to 512 tiles while
-    # the code matrix is at most 96 x 12288 bytes, groups of 4 tiles otherwise
+    # <token blocks, tiles per group>: up to 512 tiles while the code matrix is
+    # at most 96 x 12288 bytes, one tile per group, or two for K > 8192 or for
+    # more tiles than workgroups above 64 tokens; groups of 4 tiles otherwise
     assert name(48, 4096, 4096) == "w8a8_linear_wide_kernel<3, 1>"
-    assert name(96, 4096, 12288) == "w8a8_linear_wide_kernel<6, 1>"
-    assert name(48, 4096, 12288) == "w8a8_linear_wide_kernel<3, 1>"
+    assert name(96, 4096, 4096) == "w8a8_linear_wide_kernel<6, 1>"
+    assert name(96, 4096, 12288) == "w8a8_linear_wide_kernel<6, 2>"
+    assert name(48, 4096, 12288) == "w8a8_linear_wide_kernel<3, 2>"
     assert name(128, 4096, 12288) == "w8a8_linear_wide_kernel<8, 4>"
-    assert name(96, 6144, 4096) == "w8a8_linear_wide_kernel<6, 1>"
+    assert name(96, 6144, 4096) == "w8a8_linear_wide_kernel<6, 2>"
+    assert name(48, 6144, 4096) == "w8a8_linear_wide_kernel<3, 1>"
     assert name(9, 16, 16) == "w8a8_linear_wide_kernel<1, 1>"
-    assert name(6, 64, 16384) == "w8a8_linear_wide_kernel<1, 1>"
+    assert name(6, 64, 16384) == "w8a8_linear_wide_kernel<1, 2>"
     assert name(96, 24576, 4096) == "w8a8_linear_wide_kernel<6, 4>"
     assert name(48, 151936, 4096) == "w8a8_linear_wide_kernel<3, 4>"
     assert name(96, 151936, 4096) == "w8a8_linear_wide_kernel<6, 4>"

@@ -81,6 +81,10 @@ RAGGED = [
     # 4 to 5 tiles per workgroup: groups of 4 tiles split across workgroups
     (20, 16400, 320), (100, 16384, 1040), (128, 16500, 2112), (9, 16390, 4160),
     (70, 20000, 576),
+    # pairs of tiles per group in the wide kernel: K past 8192 (ragged N and K),
+    # and more tiles than workgroups at more than 64 tokens (an odd tile count:
+    # the last group holds one tile)
+    (20, 1000, 8208), (90, 200, 10000), (96, 6152, 4096), (72, 4104, 2048),
     # at least 16 tiles per workgroup (groups of 4 tiles): every token-block
     # count, ragged N and K (odd chunk counts), groups split across workgroups
     (9, 65600, 320), (20, 66000, 208), (48, 70000, 208), (33, 66000, 96), (64, 65540, 576),

@@ -66,6 +66,7 @@ _SIGNATURES = {
     "quasar_w4a8_linear": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P]),
     "quasar_w4a8_kernel_name": (ctypes.c_char_p, [_I64, _I64, _I64]),
     "quasar_stream_copy": (ctypes.c_int, [_P, _P, _SZ, _P]),
+    "quasar_stream_read": (ctypes.c_int, [_P, _SZ, _P, _P]),
     "quasar_embed": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _P, _P]),
     "quasar_rmsnorm": (ctypes.c_int, [_P, _P, _P, _I64, _I64, ctypes.c_float, _P, _P]),
     "quasar_qk_rope_cache": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
@@ -180,6 +181,12 @@ def force_wait_expiry(on: bool) -> None:
 def w8a8_kernel_name(M: int, N: int, K: int) -> str:
     """Profiler name of the kernel(s) quasar_w8a8_linear launches for M x N x K."""
     return lib().quasar_w8a8_kernel_name(M, N, K).decode()
+
+
+def quasar_stream_read(src: torch.Tensor, sink: torch.Tensor) -> None:
+    """Diagnostic read-only stream of src's bytes (sink: 1024 int32 words)."""
+    _check("quasar_stream_read", lib().quasar_stream_read(
+        _ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream()))
 
 
 def quasar_stream_copy(src: torch.Tensor, dst: torch.Tensor) -> None:

@@ -228,6 +228,13 @@ const char* quasar_w8a8_kernel_name(int64_t M, int64_t N, int64_t K) {
   return wide_kernel_name(p.mb, p.tg);
 }
 
+quasar_status quasar_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (bytes == 0) return QUASAR_OK;
+  if (!src || !sink || bytes % 16 != 0 || !aligned(src, 16) || !aligned(sink, 4))
+    return QUASAR_ERR_INVALID_ARG;
+  return hip_status(launch_stream_read(src, bytes, sink, (hipStream_t)stream));
+}
+
 quasar_status quasar_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
   if (bytes == 0) return QUASAR_OK;
   if (!src || !dst || bytes % 16 != 0 || !aligned(src, 16) || !aligned(dst, 16))

@@ -257,7 +257,7 @@ __device__ __forceinline__ void chain_helper(const quasar_chain_link* __restrict
                                              float* amax_part, float* qp, int* cnt, int* ready,
                                              int* gate, const int* expired, uint32_t* progress,
                                              AcceptPartials ap, const WaitCtl& wc) {
-  const uint32_t base = load_flag(progress + b);
+  const uint32_t base = load_flag(flag_word(progress, 0, b));
   int qseq = 0;    // links quantized here (LDS counter cnt)
   int dseq = 0;    // dependency waits passed (LDS counter gate)
   int tcount = 0;  // tiles finished (partial-buffer parity)
@@ -290,7 +290,7 @@ __device__ __forceinline__ void chain_helper(const quasar_chain_link* __restrict
           bool ok = false;
           for (int spin = 0;; ++spin) {
             bool all = true;
-            for (int c = lane; c < G; c += 64) all &= reached(load_flag(progress + c), target);
+            for (int c = lane; c < G; c += 64) all &= reached(load_flag(flag_word(progress, 0, c)), target);
             if (__builtin_amdgcn_ballot_w64(!all) == 0) {
               ok = true;
               break;
@@ -515,7 +515,7 @@ __device__ __forceinline__ void chain_helper(const quasar_chain_link* __restrict
     // (after the stores have completed when the next link reads them)
     if (hwave == 0) {
       if (consumed && T > 0) wait_stores_complete();
-      if (lane == 0) store_flag(progress + b, base + (uint32_t)li + 1u);
+      if (lane == 0) store_flag(flag_word(progress, 0, b), base + (uint32_t)li + 1u);
     }
   }
   if (!started) __syncthreads();  // (1): no link had tiles here

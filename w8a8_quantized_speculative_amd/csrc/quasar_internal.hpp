@@ -185,6 +185,8 @@ hipError_t launch_silu_mul(const uint16_t* gu, int64_t M, int64_t I, uint16_t* o
 
 // Diagnostic plain copy (16-byte vectors), bytes % 16 == 0.
 hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
+// Diagnostic read-only stream of `bytes` (% 16 == 0); sink holds 1024 words.
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);
 // Zero the flag header at the start of a workspace (a kernel, so it can be
 // captured in a graph).
 hipError_t launch_zero_flag_header(void* workspace, hipStream_t st);

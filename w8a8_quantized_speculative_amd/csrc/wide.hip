@@ -105,8 +105,9 @@ struct Wide {
 };
 template <int MB>
 constexpr bool wide_fits() {
-  return Wide<MB, 1>::LDS <= 150 * 1024 && Wide<MB, 4>::LDS <= 150 * 1024 &&
-         (Wide<MB, 1>::NBUF - 1) * (1 + MB) + MB <= 63 &&
+  return Wide<MB, 1>::LDS <= 150 * 1024 && Wide<MB, 2>::LDS <= 150 * 1024 &&
+         Wide<MB, 4>::LDS <= 150 * 1024 && (Wide<MB, 1>::NBUF - 1) * (1 + MB) + MB <= 63 &&
+         (Wide<MB, 2>::NBUF - 1) * (2 + MB) + MB <= 63 &&
          (Wide<MB, 4>::NBUF - 1) * (4 + MB) + MB <= 63;
 }
 static_assert(wide_fits<1>() && wide_fits<2>() && wide_fits<3>() && wide_fits<4>() &&
@@ -451,9 +452,9 @@ __device__ __forceinline__ bool wide_rows_and_gate(const uint16_t* __restrict__ 
                                                    const float* __restrict__ s, int M, int K, int b,
                                                    int n, int ht, int hw, int lane,
                                                    int8_t* __restrict__ qx, float* __restrict__ sx,
-                                                   uint32_t* row_flag, int* sync, uint32_t& e,
+                                                   uint32_t* flags, int* sync, uint32_t& e,
                                                    const WaitCtl& wc) {
-  e = load_flag(row_flag + b);
+  e = load_flag(flag_word(flags, 0, b));
   const bool quantizer = b < M;
   const int units = K >> 3;
   const bool in_regs = units <= kRowPieces * 64 * kHelpers;
@@ -482,7 +483,7 @@ __device__ __forceinline__ bool wide_rows_and_gate(const uint16_t* __restrict__ 
   }
   if (ht == 0) {
     if (quantizer) lds_wait_at_least(sync + kRowDone, kHelpers, wc);
-    store_flag(row_flag + b, e + 1u);
+    store_flag(flag_word(flags, 0, b), e + 1u);
     asm volatile("" ::: "memory");
     lds_add(sync + kFlagOut, 1);  // the flag is queued ahead of the weight stream
   }
@@ -493,7 +494,7 @@ __device__ __forceinline__ bool wide_rows_and_gate(const uint16_t* __restrict__ 
     bool ok = false;
     for (int spin = 0;; ++spin) {
       bool ready = true;
-      for (int m = lane; m < M; m += 64) ready &= load_flag(row_flag + m) == target;
+      for (int m = lane; m < M; m += 64) ready &= load_flag(flag_word(flags, 0, m)) == target;
       if (__builtin_amdgcn_ballot_w64(!ready) == 0) {
         ok = true;
         break;
@@ -523,7 +524,7 @@ __device__ __forceinline__ void wide_epilogue(const float* __restrict__ wscale,
                                               const float* __restrict__ sx, int M, int N, int P,
                                               int U, int G, int b, int i0, int n, uint32_t e,
                                               int et, int lane, const int32_t* red, int* sync,
-                                              int32_t* __restrict__ partials, uint32_t* part_flag,
+                                              int32_t* __restrict__ partials, uint32_t* flags,
                                               uint16_t* __restrict__ y,
                                               int32_t* __restrict__ acc_out, const WaitCtl& wc) {
   constexpr int KS = (MB + 3) / 4;           // slots per thread and round
@@ -561,7 +562,7 @@ __device__ __forceinline__ void wide_epilogue(const float* __restrict__ wscale,
       for (int c = b + 1; c < G && range_start(c, U, G) < (g + 1) * P; ++c) {
         if (range_start(c + 1, U, G) == range_start(c, U, G)) continue;  // empty range
         for (int spin = 0;; ++spin) {
-          if (load_flag(part_flag + c) == e + 1u + wc.bias) break;
+          if (load_flag(flag_word(flags, 1, c)) == e + 1u + wc.bias) break;
           if (spin >= wc.spin_global) {
             if (lane == 0) note_expired(wc, kWaitPartials);
             break;
@@ -636,7 +637,7 @@ __device__ __forceinline__ void wide_epilogue(const float* __restrict__ wscale,
       if (lane == 0) lds_add(sync + kPartDone, 1);
       if (et == 0) {
         lds_wait_at_least(sync + kPartDone, kHelpers, wc);
-        store_flag(part_flag + b, e + 1u);
+        store_flag(flag_word(flags, 1, b), e + 1u);
       }
     }
   }
@@ -679,7 +680,7 @@ __global__ __launch_bounds__(kThreads) void w8a8_linear_wide_kernel(
   if (!wide_rows_and_gate(x, s, M, K, b, n, ht, wave - kS, lane, qx, sx, flags, sync, e, wc))
     return;
   wide_epilogue<MB, TG>(wscale, sx, M, N, P, U, G, b, i0, n, e, ht, lane, red, sync, partials,
-                        flags + kFlagSlots, y, acc_out, wc);
+                        flags, y, acc_out, wc);
 }
 
 template <int MB, int TG>
@@ -739,7 +740,14 @@ static_assert(wide_lds_of(6, 4) == Wide<6, 4>::LDS && wide_lds_of(3, 1) == Wide<
 int wide_tiles_per_group(int64_t M, int64_t N, int64_t K, int grid) {
   const int64_t tiles = (N + 15) / 16;
   const int64_t g = grid > 0 ? grid : kWideMaxGrid;
-  if (tiles <= 2 * g && M * K <= 96 * 12288) return 1;
+  if (tiles <= 2 * g && M * K <= 96 * 12288) {
+    // pairs of tiles halve the fragment loads per weight byte; measured faster
+    // for K > 8192 (down at 48 and 96 tokens: 22.2 -> 20.2 and 29.7 -> 26.1 us)
+    // and for more tiles than workgroups at more than 64 tokens (QKV at 96:
+    // 18.8 -> 17.5 us), slower otherwise (O at 96: 15.0 -> 15.5 us)
+    if (K > 8192 || (tiles > g && M > 64)) return 2;
+    return 1;
+  }
   return kMaxTG;
 }
 
@@ -769,16 +777,20 @@ WidePlan plan_wide(int64_t M, int64_t N, int64_t K, int grid) {
 }
 
 const char* wide_kernel_name(int mb, int tg) {
-  static const char* const names[2][8] = {
+  static const char* const names[3][8] = {
       {"w8a8_linear_wide_kernel<1, 1>", "w8a8_linear_wide_kernel<2, 1>",
        "w8a8_linear_wide_kernel<3, 1>", "w8a8_linear_wide_kernel<4, 1>",
        "w8a8_linear_wide_kernel<5, 1>", "w8a8_linear_wide_kernel<6, 1>",
        "w8a8_linear_wide_kernel<7, 1>", "w8a8_linear_wide_kernel<8, 1>"},
+      {"w8a8_linear_wide_kernel<1, 2>", "w8a8_linear_wide_kernel<2, 2>",
+       "w8a8_linear_wide_kernel<3, 2>", "w8a8_linear_wide_kernel<4, 2>",
+       "w8a8_linear_wide_kernel<5, 2>", "w8a8_linear_wide_kernel<6, 2>",
+       "w8a8_linear_wide_kernel<7, 2>", "w8a8_linear_wide_kernel<8, 2>"},
       {"w8a8_linear_wide_kernel<1, 4>", "w8a8_linear_wide_kernel<2, 4>",
        "w8a8_linear_wide_kernel<3, 4>", "w8a8_linear_wide_kernel<4, 4>",
        "w8a8_linear_wide_kernel<5, 4>", "w8a8_linear_wide_kernel<6, 4>",
        "w8a8_linear_wide_kernel<7, 4>", "w8a8_linear_wide_kernel<8, 4>"}};
-  return names[tg == 1 ? 0 : 1][(mb < 1 ? 1 : (mb > 8 ? 8 : mb)) - 1];
+  return names[tg == 1 ? 0 : (tg == 2 ? 1 : 2)][(mb < 1 ? 1 : (mb > 8 ? 8 : mb)) - 1];
 }
 
 hipError_t launch_wide(const WidePlan& p, const uint16_t* x, const float* s, const int8_t* wq,
@@ -793,6 +805,8 @@ hipError_t launch_wide(const WidePlan& p, const uint16_t* x, const float* s, con
   if (!wc.status) return hipErrorInvalidSymbol;
   if (p.tg == 1)
     return launch_wide_tg<1>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st);
+  if (p.tg == 2)
+    return launch_wide_tg<2>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st);
   if (p.tg == kMaxTG)
     return launch_wide_tg<kMaxTG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc,
                                   st);
@@ -839,7 +853,7 @@ int wide_grid_for_current_device() {
     // every instantiation has the same block size; the largest LDS decides
     int lds = 0;
     for (int mb = 1; mb <= 8; ++mb)
-      for (int tg : {1, kMaxTG}) lds = wide_lds_of(mb, tg) > lds ? wide_lds_of(mb, tg) : lds;
+      for (int tg : {1, 2, kMaxTG}) lds = wide_lds_of(mb, tg) > lds ? wide_lds_of(mb, tg) : lds;
     auto kernel = &w8a8_linear_wide_kernel<6, kMaxTG>;
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess ||
