@@ -13,7 +13,10 @@ the verifier's argmax with probability 0.3 each.  All inputs are resident in
 HBM before the timed region; each step reads 7.6 GB of INT8 weights.
 
 Prints one JSON line.  `value` is the algorithmic HBM bytes of a step divided
-by the step time (GB/s); tokens/s = B * mean(accepted + 1) / step time.
+by the step time (GB/s); tokens/s = B * mean(accepted + 1) / step time.  The
+same resident weights also serve the batched windows (M = 48 and 96 tokens),
+the single 1024 x 1024 linear (its launch latency), the chained step (the
+linears in one persistent launch) and the comparators.
 
     python bench.py [--steps 20] [--warmup 3] [--m 6] [--gpus 1]
 """
@@ -39,7 +42,7 @@ BLOCKER_COPIES = 100    # copies queued ahead of each event-timed step (~20 ms o
 
 
 def pmc_file(M: int) -> str:
-    return os.path.join(PROFILES, f"w8a8_linear_fused_kernel_qwen3_stack_m{M}_pmc.json")
+    return os.path.join(PROFILES, f"qwen3_stack_m{M}_pmc.json")
 
 
 def algorithmic_bytes_w4(M: int, N: int, K: int) -> int:
@@ -65,44 +68,69 @@ def parse():
                     help="skip the whole-decoder verify step (norms, attention, SiLU around the linears)")
     ap.add_argument("--context", type=int, default=2048,
                     help="cached context length of the whole-decoder verify step")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=24.0,
+                    help="budget of the oracle samples (all configs and thread counts)")
+    ap.add_argument("--windows", default="48,96",
+                    help="batched verify windows timed over the same weights ('' for none)")
+    ap.add_argument("--no-chain", action="store_true", help="skip the chained (one-launch) step")
+    ap.add_argument("--no-config0", action="store_true", help="skip the single-linear latency")
     ap.add_argument("--tau-sets", type=int, default=2048,
                     help="seeded draft sets for the mean accepted length")
     return ap.parse_args()
 
 
-class Stack:
-    """Resident W8A8 weights, activations and outputs of one verify step."""
+class Weights:
+    """Resident W8A8 weights of the stack: 36 layers' QKV, O, gate_up (also in
+    the gated order) and down, and the LM head, shared by every window size.
+    Each linear's smoothing vector is calibrated on a seeded 64-row activation
+    sample of its width, so it does not depend on the window."""
 
-    def __init__(self, M: int, layers: int, keep_bf16: bool):
+    def __init__(self, layers: int, keep_bf16: bool):
         import numpy as np
         import torch
         from w8a8_quantized_speculative_amd import binding, synth
-
-        self.M, self.B, self.k = M, M // 6, 5
-        self.linears = []     # dicts: name, N, K, x, s, wq, sw, y, (w_bf16)
+        self.layers = layers
+        self.linears = []
         shapes = [(l, name, K, N) for l in range(layers) for (name, K, N) in synth.QWEN3_8B_LINEARS]
         shapes.append((layers, "lm_head", 4096, synth.QWEN3_8B_VOCAB))
         for li, (layer, name, K, N) in enumerate(shapes):
-            key = (4, layer, li % 4 if name != "lm_head" else 4)
-            x_bits = synth.activations(M, K, key)
+            role = li % 4 if name != "lm_head" else 4
             g = torch.Generator(device="cuda")
-            g.manual_seed(1_000_003 * (layer + 1) + 7919 * (li % 5) + M)
+            g.manual_seed(1_000_003 * (layer + 1) + 7919 * (li % 5))
             w = (torch.randn((N, K), generator=g, device="cuda", dtype=torch.float32) * 0.02).to(torch.bfloat16)
             w_colmax = w.abs().amax(dim=0).float().cpu().numpy().astype(np.float64)
-            s = synth.smoothing_vector(synth.col_absmax_bf16(x_bits), w_colmax)
+            x_cal = synth.activations(64, K, (4, layer, role, 99))
+            s = synth.smoothing_vector(synth.col_absmax_bf16(x_cal), w_colmax)
             s_d = torch.from_numpy(s).cuda()
             wq, sw = binding.quasar_quantize_weights(w, s_d)
-            x = torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
-            ent = dict(layer=layer, name=name, N=N, K=K, x=x, s=s_d, wq=wq, sw=sw,
-                       y=torch.empty((M, N), dtype=torch.bfloat16, device="cuda"))
-            if name == "gate_up":  # the decoder step runs gate_up with SiLU fused
+            ent = dict(layer=layer, name=name, role=role, N=N, K=K, s=s_d, wq=wq, sw=sw)
+            if name == "gate_up":  # the decoder step and the chain run gate_up with SiLU fused
                 ent["wqg"], ent["swg"] = binding.quasar_quantize_weights_gated(w, s_d)
             if keep_bf16:
                 ent["w_bf16"] = w
             else:
                 del w
             self.linears.append(ent)
+        torch.cuda.synchronize()
+
+
+class Stack:
+    """One verify window of M tokens over the shared weights: per-linear BF16
+    activations (seeded), outputs, workspaces and the accept buffers."""
+
+    def __init__(self, W: Weights, M: int):
+        import numpy as np
+        import torch
+        from w8a8_quantized_speculative_amd import binding, synth
+
+        self.W = W
+        self.M, self.B, self.k = M, M // 6, 5
+        self.linears = []
+        for e in W.linears:
+            x_bits = synth.activations(M, e["K"], (4, e["layer"], e["role"]))
+            x = torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+            self.linears.append(dict(e, x=x, y=torch.empty((M, e["N"]), dtype=torch.bfloat16,
+                                                            device="cuda")))
         torch.cuda.synchronize()
         self.ws = binding.new_workspace(max(binding.workspace_bytes_linear(M, e["N"], e["K"])
                                             for e in self.linears))
@@ -214,9 +242,11 @@ def plant_drafts(stack, n_sets: int):
     return torch.from_numpy(np.stack(sets)).cuda()
 
 
-def time_graph_steps(stack, drafts, warmup: int, steps: int, step=None, uniforms=None):
+def time_graph_steps(stack, drafts, warmup: int, steps: int, step=None, uniforms=None,
+                     probes=None):
     """Capture one step in a HIP graph; replay it `steps` times (new drafts, and
-    new uniforms when given, each)."""
+    new uniforms when given, each).  `probes`: outputs the step must rewrite on
+    replay (default: the first and the last linear's)."""
     import torch
     step = step or stack.step
     s = torch.cuda.Stream()
@@ -253,7 +283,7 @@ def time_graph_steps(stack, drafts, warmup: int, steps: int, step=None, uniforms
     tau = (lens[warmup:].float() + 1).mean().item()
     # the replay must recompute the step: clear the first and the last linear's
     # outputs, replay once, and require both to be written again
-    probes = (stack.linears[0]["y"], stack.linears[-1]["y"])
+    probes = probes or (stack.linears[0]["y"], stack.linears[-1]["y"])
     for y in probes:
         y.zero_()
     graph.replay()
@@ -431,7 +461,7 @@ def time_eager_steps(stack, drafts, warmup: int, steps: int, step=None, uniforms
     return ms, ms_events, (lens[warmup:].float() + 1).mean().item()
 
 
-def time_kernels(stack, reps: int):
+def time_kernels(stack, reps: int, bits: int = 8):
     """Per-launch time of every linear shape of the step, with HIP events on the
     launch stream.  Each batch -- `reps` passes over all linears of one shape,
     rotating through the layers' weights so nothing is re-read from a cache --
@@ -460,7 +490,8 @@ def time_kernels(stack, reps: int):
         shapes.setdefault((e["N"], e["K"]), []).append(e)
     per_shape = {}
     for (N, K), ents in shapes.items():
-        ms = batch(lambda i, ents=ents: stack.linear_call(ents[i % len(ents)]), reps * len(ents))
+        ms = batch(lambda i, ents=ents: stack.linear_call(ents[i % len(ents)], bits=bits),
+                   reps * len(ents))
         per_shape[(N, K)] = ms
     del blk_src, blk_dst
     return per_shape
@@ -510,59 +541,372 @@ def time_bf16_comparator(stack, warmup: int, steps: int):
     return ms, bf16_bytes
 
 
+def kernel_groups(stack, per_shape, bits: int = 8):
+    """Per kernel symbol: launches of one step, their algorithmic bytes and ops,
+    and the mean launch time (from the per-shape timings); sorted by bytes."""
+    from w8a8_quantized_speculative_amd import binding
+    M = stack.M
+    kname = binding.w8a8_kernel_name if bits == 8 else binding.w4a8_kernel_name
+    abytes = algorithmic_bytes if bits == 8 else algorithmic_bytes_w4
+    groups = {}
+    total = 0
+    for i, e in enumerate(stack.linears):
+        name = kname(M, e["N"], e["K"])
+        g = groups.setdefault(name, {"launches_per_step": 0, "bytes": 0, "ms": 0.0, "ops": 0})
+        g["launches_per_step"] += 1
+        nb = abytes(M, e["N"], e["K"])
+        g["bytes"] += nb
+        total += nb
+        g["ops"] += 2 * M * e["N"] * e["K"]
+        g["ms"] += per_shape[(e["N"], e["K"])]
+    kernels = []
+    for name, g in groups.items():
+        n_l = g["launches_per_step"]
+        launch_ms = g["ms"] / n_l
+        bpl = g["bytes"] / n_l
+        opl = g["ops"] / n_l
+        kernels.append({"kernel": name, "launches_per_step": n_l,
+                        "algorithmic_bytes_per_launch": int(bpl),
+                        "algorithmic_int8_ops_per_launch": int(opl),
+                        "launch_avg_us": round(launch_ms * 1e3, 2),
+                        "gbs": round(bpl / (launch_ms * 1e-3) / 1e9, 1),
+                        "tops": round(opl / (launch_ms * 1e-3) / 1e12, 2),
+                        "bytes_share": round(g["bytes"] / total, 4)})
+    kernels.sort(key=lambda k: -k["bytes_share"])
+    linears = []
+    for (N, K), shape_ms in per_shape.items():
+        e = next(x for x in stack.linears if (x["N"], x["K"]) == (N, K))
+        nb = abytes(M, N, K)
+        linears.append({"linear": e["name"], "N": N, "K": K,
+                        "launch_us": round(shape_ms * 1e3, 2),
+                        "gbs": round(nb / (shape_ms * 1e-3) / 1e9, 1),
+                        "frac_of_hbm_peak": round(nb / (shape_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                        "kernel": kname(M, N, K)})
+    return kernels, linears
+
+
+def time_window(W, M: int, args):
+    """A batched verify window (M = 48 or 96 tokens, B = M / 6 sequences) over
+    the same resident weights: the whole step (faster of graph replay and plain
+    launches), every linear shape's launch time, the dominant kernel's roofline,
+    and the BF16-weight comparator."""
+    import torch
+    st = Stack(W, M)
+    drafts = plant_drafts(st, args.warmup + args.steps)
+    g_ms, g_ev, _, _g = time_graph_steps(st, drafts, args.warmup, args.steps)
+    del _g
+    e_ms, e_ev, _ = time_eager_steps(st, drafts, args.warmup, args.steps)
+    ms, ms_ev, mode = (g_ms, g_ev, "graph") if g_ms <= e_ms else (e_ms, e_ev, "eager")
+    per_shape = time_kernels(st, max(2, args.steps // 4))
+    kernels, linears = kernel_groups(st, per_shape)
+    tau = measure_tau(st, max(64, args.tau_sets // 8))
+    dom = kernels[0]
+    out = {
+        "what": f"the same 36-layer stack + LM head + greedy accept over a window of {M} tokens "
+                f"({st.B} sequences x 1+5), the same resident weights",
+        "M": M, "B": st.B,
+        "ms_per_step": round(ms, 4), "ms_per_step_events": round(ms_ev, 4), "timing": mode,
+        "gbs": round(st.bytes_step / (ms * 1e-3) / 1e9, 1),
+        "hbm_frac_of_peak": round(st.bytes_step / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "bytes_per_step": st.bytes_step,
+        "verified_tokens_per_s": round(st.B * tau / (ms * 1e-3), 1),
+        "mean_tau": round(tau, 4),
+        "roofline": {"bound": "hbm", "kernel": dom["kernel"], "achieved": dom["gbs"],
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(dom["gbs"] / PEAK_HBM_GBS, 4),
+                     "traffic": read_traffic(M, dom["kernel"])[0],
+                     "traffic_note": read_traffic(M, dom["kernel"])[1],
+                     "launch_avg_us": dom["launch_avg_us"],
+                     "algorithmic_bytes_per_launch": dom["algorithmic_bytes_per_launch"],
+                     "launches_per_step": dom["launches_per_step"]},
+        "mfma": {"kernel": dom["kernel"], "achieved_tops": dom["tops"], "peak_tops": PEAK_INT8_TOPS,
+                 "frac": round(dom["tops"] / PEAK_INT8_TOPS, 4)},
+        "kernels": kernels, "linears": linears,
+    }
+    if not args.no_bf16:
+        bms, bbytes = time_bf16_comparator(st, args.warmup, args.steps)
+        out["bf16_comparator"] = {"ms_per_step": round(bms, 4),
+                                  "gbs": round(bbytes / (bms * 1e-3) / 1e9, 1),
+                                  "w8a8_speedup": round(bms / ms, 3)}
+    del st
+    torch.cuda.empty_cache()
+    return out
+
+
+def time_chained_step(stack, drafts, args, per_linear_ms: float):
+    """The same stack as ONE persistent launch (quasar_chain_verify) and the
+    accept finalize.  Each layer's data flow is real: O reads the query columns
+    of QKV's output (attention's stand-in), gate_up (SiLU * up in its epilogue)
+    reads O's output, down reads that activation; each layer's QKV and the LM
+    head read their own seeded activations (the residual stream and the norms
+    between layers are not in the chain).  Every dependent link waits for its
+    predecessor inside the kernel while the weight stream keeps going."""
+    import torch
+    from w8a8_quantized_speculative_amd import binding
+    M = stack.M
+    ch = binding.Chain(M)
+    outs = []
+    y_qkv = y_o = act = None
+    for e in stack.linears:
+        name = e["name"]
+        if name == "qkv":
+            y_qkv = torch.empty((M, e["N"]), dtype=torch.bfloat16, device="cuda")
+            ch.add(e["x"], e["s"], e["wq"], e["sw"], y_qkv, dep=-1)
+        elif name == "o":
+            y_o = torch.empty((M, e["N"]), dtype=torch.bfloat16, device="cuda")
+            ch.add(y_qkv[:, :e["K"]], e["s"], e["wq"], e["sw"], y_o, dep=len(ch.links) - 1)
+        elif name == "gate_up":
+            act = torch.empty((M, e["N"] // 2), dtype=torch.bfloat16, device="cuda")
+            ch.add(y_o, e["s"], e["wqg"], e["swg"], act, dep=len(ch.links) - 1, swiglu=True)
+        elif name == "down":
+            y_d = torch.empty((M, e["N"]), dtype=torch.bfloat16, device="cuda")
+            ch.add(act, e["s"], e["wq"], e["sw"], y_d, dep=len(ch.links) - 1)
+        else:
+            ch.add(e["x"], e["s"], e["wq"], e["sw"], stack.linears[-1]["y"], dep=-1)
+    ch.finalize()
+    ws = ch.verify_workspace(stack.B, stack.k)
+    out = (stack.accept_len, stack.next_token, stack.argmax, None)
+
+    def step():
+        ch.run_verify(stack.B, stack.k, stack.draft, 0.0, None, workspace=ws, out=out)
+
+    g_ms, g_ev, tau, _g = time_graph_steps(stack, drafts, args.warmup, args.steps, step=step,
+                                           probes=(y_qkv, stack.linears[-1]["y"]))
+    del _g
+    e_ms, e_ev, _ = time_eager_steps(stack, drafts, args.warmup, args.steps, step=step)
+    ms, ms_ev, mode = (g_ms, g_ev, "graph") if g_ms <= e_ms else (e_ms, e_ev, "eager")
+    st, bits = binding.device_check()
+    if st != 0:
+        raise RuntimeError(f"chained step: a bounded wait gave up (status bits {bits})")
+    return {
+        "what": "the same linears and LM head + greedy accept as ONE persistent kernel "
+                "(quasar_chain_verify: 145 links, 108 of them waiting for their predecessor "
+                "inside the kernel) and the accept finalize",
+        "kernel": binding.chain_kernel_name(M),
+        "ms_per_step": round(ms, 4), "ms_per_step_events": round(ms_ev, 4), "timing": mode,
+        "gbs": round(stack.bytes_step / (ms * 1e-3) / 1e9, 1),
+        "vs_per_linear_launches": round(per_linear_ms / ms, 3),
+        "note": "slower than one launch per linear on MI355X: each in-kernel hand-off (a "
+                "grid-wide flag wait, then every workgroup loading and quantizing the input) "
+                "costs more than a kernel boundary",
+    }
+
+
+def config0_latency(blocker_bytes: int = COPY_BYTES):
+    """The single 1024 x 1024 W8A8 linear at M = 6 (four outlier channels x50):
+    not a bandwidth configuration.  1024 launches over a rotating pool of 1024
+    weight copies (1 GiB, so no launch reads another's weights from a cache),
+    queued behind ~20 ms of copies so that the events time the GPU."""
+    import numpy as np
+    import torch
+    import ctypes
+    from w8a8_quantized_speculative_amd import binding, synth
+    M, K, N, copies = 6, 1024, 1024, 1024
+    x_bits, w_bits, s = synth.linear_case(M, K, N, (0, 0), n_outliers=4, fixed_scale=50.0)
+    x = torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    w = torch.from_numpy(w_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    s_d = torch.from_numpy(s).cuda()
+    wq, sw = binding.quasar_quantize_weights(w, s_d)
+    pool = wq.codes.repeat(copies)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    L = binding.lib()
+    P = ctypes.c_void_p
+    nbytes = wq.codes.numel()
+    blk_src = torch.empty(blocker_bytes, dtype=torch.uint8, device="cuda")
+    blk_dst = torch.empty_like(blk_src)
+    stream = binding._stream()
+    for i in range(8):
+        L.quasar_w8a8_linear(P(x.data_ptr()), P(s_d.data_ptr()), P(pool.data_ptr() + i * nbytes),
+                             P(sw.data_ptr()), M, N, K, P(y.data_ptr()), None, None, 0, stream)
+    torch.cuda.synchronize()
+    for _ in range(BLOCKER_COPIES):
+        binding.quasar_stream_copy(blk_src, blk_dst)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(copies):
+        st = L.quasar_w8a8_linear(P(x.data_ptr()), P(s_d.data_ptr()),
+                                  P(pool.data_ptr() + i * nbytes), P(sw.data_ptr()), M, N, K,
+                                  P(y.data_ptr()), None, None, 0, stream)
+        if st != 0:
+            raise binding.QuasarError("quasar_w8a8_linear", st)
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / copies
+    nb = algorithmic_bytes(M, N, K)
+    del pool, blk_src, blk_dst
+    torch.cuda.empty_cache()
+    return {"what": "single W8A8 linear, M=6, K=N=1024 (not a bandwidth configuration: its "
+                    "1.08 MB take 0.14 us at 8 TB/s)",
+            "kernel": binding.w8a8_kernel_name(M, N, K),
+            "us_per_launch": round(us, 2), "gbs": round(nb / (us * 1e-6) / 1e9, 1),
+            "algorithmic_bytes": nb,
+            "timing": "1024 back-to-back launches over 1024 weight copies (1 GiB), HIP events, "
+                      "queued behind ~20 ms of copies"}
+
+
+def read_calibration():
+    """A plain read-only 16-byte stream over 1 GiB: the measured ceiling of a
+    read stream, the shape of the verify linears' weight traffic."""
+    import torch
+    from w8a8_quantized_speculative_amd import binding
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(3)
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    binding.quasar_stream_read(src, sink)
+    torch.cuda.synchronize()
+    reps = 10
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        binding.quasar_stream_read(src, sink)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    del src, sink
+    torch.cuda.empty_cache()
+    return {"kernel": "stream_read_kernel", "bytes": 1 << 30,
+            "read_gbs": round((1 << 30) / (ms * 1e-3) / 1e9, 1), "us": round(ms * 1e3, 2)}
+
+
+def read_twin(stack, reps: int = 5):
+    """The step's read-only twin: one plain streaming read over each linear's
+    packed weights, in the step's order, one launch per linear, back to back
+    (queued behind ~20 ms of copies, HIP events).  Its time is what launches of
+    a kernel that only reads the same bytes take: the measured ceiling of a
+    step made of one launch per linear."""
+    import torch
+    from w8a8_quantized_speculative_amd import binding
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    blk_src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    blk_dst = torch.empty_like(blk_src)
+    codes = [e["wq"].codes for e in stack.linears]
+    nbytes = sum(c.numel() for c in codes)
+    for c in codes:
+        binding.quasar_stream_read(c, sink)
+    torch.cuda.synchronize()
+    for _ in range(BLOCKER_COPIES):
+        binding.quasar_stream_copy(blk_src, blk_dst)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        for c in codes:
+            binding.quasar_stream_read(c, sink)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    del blk_src, blk_dst
+    return ms, nbytes
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_oracle_baseline(M: int, budget_s: float):
-    """The CPU oracle as it stands on a bounded sample: the four linears of one
-    Qwen3-8B-shaped layer at the same M, repeated until the budget is spent."""
+    """The CPU oracle as it stands, on bounded samples of three workloads, with
+    its BLAS (the integer products are float64 BLAS products of the codes) on
+    one thread and on all the host threads given (at most 16):
+      config 0: the single 1024 x 1024 linear;
+      config 1: one Qwen3-8B-shaped layer's 4 linears;
+      config 3: the LM head on a 16384-row sample of its 151936 rows plus the
+                greedy accept over full-vocabulary logits of the window.
+    The quantization and dequantization loops are numpy on one thread
+    whatever the BLAS setting."""
     import numpy as np
     from oracle import quasar_oracle as orc
     from w8a8_quantized_speculative_amd import synth
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
-    cases = []
-    for li, (name, K, N) in enumerate(synth.QWEN3_8B_LINEARS):
-        key = (6, 0, li)
-        x = synth.activations(M, K, key)
-        w = synth.weights(N, K, key)
-        s = synth.smoothing_vector(synth.col_absmax_bf16(x), synth.col_absmax_bf16(w))
-        qw, sw = orc.quantize_weights(w, s)
-        del w
-        cases.append((x, s, qw, sw, algorithmic_bytes(M, N, K)))
-    done_bytes, reps = 0, 0
-    t0 = time.perf_counter()
-    while True:
-        for x, s, qw, sw, nb in cases:
-            orc.w8a8_linear(x, s, qw, sw)
-            done_bytes += nb
-        reps += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": round(done_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{reps} pass(es) over one Qwen3-8B-shaped layer's 4 W8A8 linears at M={M} "
-                      f"(weights pre-quantized, untimed), {dt:.1f} s",
-            "ms_per_layer": round(dt / reps * 1e3, 2)}
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover - threadpoolctl is in the image
+        threadpool_limits = None
+    n_all = max(1, min(os.cpu_count() or 1, 16))
+
+    def layer_cases(K_N, key0):
+        cases = []
+        for li, (K, N) in enumerate(K_N):
+            key = (6, key0, li)
+            x = synth.activations(M, K, key)
+            w = synth.weights(N, K, key)
+            s = synth.smoothing_vector(synth.col_absmax_bf16(x), synth.col_absmax_bf16(w))
+            qw, sw = orc.quantize_weights(w, s)
+            del w
+            cases.append((x, s, qw, sw, algorithmic_bytes(M, N, K)))
+        return cases
+
+    configs = {
+        "0": ("one 1024 x 1024 linear", layer_cases([(1024, 1024)], 0), 0),
+        "1": ("one layer's 4 linears (QKV, O, gate_up, down)",
+              layer_cases([(K, N) for (_, K, N) in synth.QWEN3_8B_LINEARS], 1), 0),
+        "3": ("LM head rows 0..16383 of 151936 + greedy accept over full logits",
+              layer_cases([(4096, 16384)], 3), 1),
+    }
+    lg = synth.logits(1, 5, synth.QWEN3_8B_VOCAB, (6, 3)) if M == 6 else None
+    drafts = np.zeros((1, 5), np.int64)
+    per = budget_s / (2 * len(configs))
+    results = {}
+    for cid, (what, cases, with_accept) in configs.items():
+        r = {"what": what}
+        for threads in (1, n_all):
+            ctx = threadpool_limits(limits=threads) if threadpool_limits else None
+            if ctx:
+                ctx.__enter__()
+            try:
+                done, reps = 0, 0
+                t0 = time.perf_counter()
+                while True:
+                    for x, s, qw, sw, nb in cases:
+                        orc.w8a8_linear(x, s, qw, sw)
+                        done += nb
+                    if with_accept and lg is not None:
+                        orc.greedy_accept(lg, drafts)
+                    reps += 1
+                    if time.perf_counter() - t0 >= per:
+                        break
+                dt = time.perf_counter() - t0
+            finally:
+                if ctx:
+                    ctx.__exit__(None, None, None)
+            key = "threads_1" if threads == 1 else f"threads_{threads}"
+            r[key] = {"gbs": round(done / dt / 1e9, 3), "passes": reps, "seconds": round(dt, 2)}
+        results[cid] = r
+    best = results["1"][f"threads_{n_all}"]
+    return {"value": best["gbs"], "unit": "GB/s", "cores": n_all, "kind": "oracle",
+            "sample": f"config 1 (one Qwen3-8B-shaped layer's 4 W8A8 linears at M={M}, weights "
+                      f"pre-quantized, untimed), {best['passes']} pass(es) in {best['seconds']} s "
+                      f"with the BLAS on {n_all} threads; configs 0, 1 and 3 on 1 and "
+                      f"{n_all} threads below",
+            "cpu_model": _cpu_model(), "host_threads": os.cpu_count(),
+            "threads_note": "the integer products run in the BLAS on the stated threads; the "
+                            "quantize and dequantize steps are single-threaded numpy",
+            "configs": results}
 
 
 def read_traffic(M: int, kernel: str):
-    """HBM traffic per launch from the committed rocprofv3 PMC summary, when it
-    was taken on the current kernel sources and for this kernel."""
+    """HBM traffic per launch from the committed rocprofv3 PMC summary of the
+    M-token step, when it was taken on the kernel's current sources."""
     from w8a8_quantized_speculative_amd.profiling import kernel_source_hash
     try:
         with open(pmc_file(M)) as f:
             pmc = json.load(f)
     except (OSError, ValueError):
         return None, "no PMC summary for this workload"
-    if pmc.get("kernel") != kernel:
-        return None, "PMC summary is for another kernel"
-    if pmc.get("kernel_source_hash") != kernel_source_hash():
+    rec = pmc.get("kernels", {}).get(kernel)
+    if rec is None:
+        return None, "the PMC summary does not cover this kernel"
+    if rec.get("kernel_source_hash") != kernel_source_hash(kernel):
         return None, "kernel sources changed since the PMC runs"
-    return pmc.get("traffic_bytes_per_launch"), (
+    return rec.get("traffic_bytes_per_launch"), (
         f"FETCH_SIZE + WRITE_SIZE per launch, scaled by a plain copy; "
-        f"{pmc.get('traffic_over_algorithmic')} x the algorithmic bytes")
+        f"{rec.get('traffic_over_algorithmic')} x the algorithmic bytes")
 
 
 def copy_calibration():
@@ -602,13 +946,17 @@ def main():
     if args.m % 6 != 0 or not 6 <= args.m <= 96:
         sys.exit("--m must be B*(1+5) with 1 <= B <= 16")
 
-    print("[bench] calibration copy", file=sys.stderr, flush=True)
+    print("[bench] calibration copy and read", file=sys.stderr, flush=True)
     copy_cal = copy_calibration()
-    print(f"[bench] building stack: M={args.m} layers={args.layers}", file=sys.stderr, flush=True)
-    stack = Stack(args.m, args.layers, keep_bf16=not args.no_bf16)
+    read_cal = read_calibration()
+    print(f"[bench] building weights ({args.layers} layers) and the M={args.m} window",
+          file=sys.stderr, flush=True)
+    W = Weights(args.layers, keep_bf16=not args.no_bf16)
+    stack = Stack(W, args.m)
     drafts = plant_drafts(stack, args.warmup + args.steps)
     print("[bench] graph replay timing", file=sys.stderr, flush=True)
     ms, ms_events, tau, _graph = time_graph_steps(stack, drafts, args.warmup, args.steps)
+    del _graph
     print("[bench] rejection-verify step (T = 1)", file=sys.stderr, flush=True)
     import numpy as np
     from w8a8_quantized_speculative_amd import synth as _synth
@@ -631,41 +979,12 @@ def main():
     per_shape = time_kernels(stack, max(2, args.steps // 4))
     tau_many = measure_tau(stack, args.tau_sets)
 
-    # per kernel symbol: launches of one step, their algorithmic bytes and time
     from w8a8_quantized_speculative_amd import binding
     n = len(stack.linears)
-    groups = {}
-    for i, e in enumerate(stack.linears):
-        name = binding.w8a8_kernel_name(args.m, e["N"], e["K"])
-        g = groups.setdefault(name, {"launches_per_step": 0, "bytes": 0, "ms": 0.0, "ops": 0})
-        g["launches_per_step"] += 1
-        g["bytes"] += stack.bytes_linear[i]
-        g["ops"] += 2 * args.m * e["N"] * e["K"]
-        g["ms"] += per_shape[(e["N"], e["K"])]
-    kernels = []
-    for name, g in groups.items():
-        n_l = g["launches_per_step"]
-        launch_ms = g["ms"] / n_l
-        bpl = g["bytes"] / n_l
-        opl = g["ops"] / n_l
-        kernels.append({"kernel": name, "launches_per_step": n_l,
-                        "algorithmic_bytes_per_launch": int(bpl),
-                        "algorithmic_int8_ops_per_launch": int(opl),
-                        "launch_avg_us": round(launch_ms * 1e3, 2),
-                        "gbs": round(bpl / (launch_ms * 1e-3) / 1e9, 1),
-                        "tops": round(opl / (launch_ms * 1e-3) / 1e12, 2),
-                        "bytes_share": round(g["bytes"] / sum(stack.bytes_linear), 4)})
-    kernels.sort(key=lambda k: -k["bytes_share"])
+    kernels, linears = kernel_groups(stack, per_shape)
     dom = kernels[0]
-    linears = []
-    for (N, K), shape_ms in per_shape.items():
-        e = next(x for x in stack.linears if (x["N"], x["K"]) == (N, K))
-        nb = algorithmic_bytes(args.m, N, K)
-        linears.append({"linear": e["name"], "N": N, "K": K,
-                        "launch_us": round(shape_ms * 1e3, 2),
-                        "gbs": round(nb / (shape_ms * 1e-3) / 1e9, 1),
-                        "kernel": binding.w8a8_kernel_name(args.m, N, K)})
     achieved = dom["gbs"]
+    twin_ms, twin_bytes = read_twin(stack)
     traffic, traffic_note = read_traffic(args.m, dom["kernel"])
 
     value = stack.bytes_step / (ms * 1e-3) / 1e9
@@ -741,6 +1060,18 @@ def main():
         "kernels": kernels,
         "linears": linears,
         "copy_calibration": copy_cal,
+        "read_calibration": read_cal,
+        "hbm_frac_of_measured_read": round(value / read_cal["read_gbs"], 4),
+        "measured_read_note": "the step's GB/s over a plain 16-byte streaming read of 1 GiB "
+                              "on the same GPU (the measured ceiling of one long read stream)",
+        "read_twin": {
+            "what": "one plain streaming read over each linear's packed weights, one launch "
+                    "per linear in the step's order, back to back: the ceiling of a step made "
+                    "of one launch per linear",
+            "ms": round(twin_ms, 4), "bytes": twin_bytes,
+            "gbs": round(twin_bytes / (twin_ms * 1e-3) / 1e9, 1),
+            "step_over_twin": round(twin_ms / ms, 4),
+        },
     }
     if not args.no_bf16:
         print("[bench] bf16 comparator", file=sys.stderr, flush=True)
@@ -771,6 +1102,8 @@ def main():
         e4 = time_eager_steps(stack, drafts4, args.warmup, args.steps, step=stack.step_w4)
         if e4[0] < ms4:
             ms4, ms4_ev = e4[0], e4[1]
+        k4, l4 = kernel_groups(stack, time_kernels(stack, max(2, args.steps // 4), bits=4), bits=4)
+        t4, t4_note = read_traffic(args.m, k4[0]["kernel"])
         out["w4a8_variant"] = {
             "what": "same stack and LM head with 4-bit per-channel weights (quasar_w4a8_linear), "
                     "then the greedy accept; the faster of a HIP graph and plain launches",
@@ -782,10 +1115,28 @@ def main():
             "verified_tokens_per_s": round(stack.B * tau4 / (ms4 * 1e-3), 1),
             "mean_tau": round(tau4, 4),
             "speedup_vs_w8a8": round(ms / ms4, 3),
+            "roofline": {"bound": "hbm", "kernel": k4[0]["kernel"], "achieved": k4[0]["gbs"],
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(k4[0]["gbs"] / PEAK_HBM_GBS, 4), "traffic": t4,
+                         "traffic_note": t4_note, "launch_avg_us": k4[0]["launch_avg_us"],
+                         "algorithmic_bytes_per_launch": k4[0]["algorithmic_bytes_per_launch"]},
+            "kernels": k4, "linears": l4,
         }
+    if not args.no_chain and args.m <= 8:
+        print("[bench] chained step (one persistent launch)", file=sys.stderr, flush=True)
+        out["chained_step"] = time_chained_step(stack, drafts, args, ms)
     if not args.no_decoder:
         print("[bench] whole-decoder verify step", file=sys.stderr, flush=True)
         out["decoder_step"] = time_decoder_step(stack, args, graph_ms)
+    windows = [int(m) for m in args.windows.split(",") if m.strip()] if args.windows else []
+    for Mw in windows:
+        if Mw == args.m or Mw % 6 or not 6 <= Mw <= 96:
+            continue
+        print(f"[bench] verify window M={Mw}", file=sys.stderr, flush=True)
+        out[f"window_m{Mw}"] = time_window(W, Mw, args)
+    if not args.no_config0:
+        print("[bench] single 1024 x 1024 linear (latency)", file=sys.stderr, flush=True)
+        out["config0_latency"] = config0_latency()
     if not args.no_cpu_baseline:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_oracle_baseline(args.m, args.cpu_seconds)

@@ -36,16 +36,27 @@ import os
 from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-# sources of the one-launch linear kernel (the roofline kernel at M <= 8)
-KERNEL_SOURCES = [os.path.join(PKG, "csrc", f)
-                  for f in ("fused.hip", "quasar_device.hpp", "quasar_internal.hpp")]
+# the file that defines each kernel family; every family also depends on the
+# shared device headers
+_FAMILY_SOURCES = (
+    ("w8a8_linear_fused_kernel", "fused.hip"),
+    ("w4a8_linear_fused_kernel", "fused.hip"),
+    ("w8a8_linear_wide_kernel", "wide.hip"),
+    ("w8a8_chain_kernel", "chain.hip"),
+    ("accept_", "accept.hip"),
+)
+_SHARED_HEADERS = ("quasar_device.hpp", "quasar_internal.hpp", "quasar_sync.hpp")
 COPY_KERNEL = "stream_copy_kernel"
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str = "w8a8_linear_fused_kernel") -> str:
+    """Hash of the sources a kernel is built from (its family's file and the
+    shared device headers): a recorded counter reading stays valid while this
+    hash is unchanged."""
+    files = [f for prefix, f in _FAMILY_SOURCES if kernel.startswith(prefix)][:1]
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
+    for name in files + list(_SHARED_HEADERS):
+        with open(os.path.join(PKG, "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -125,6 +136,28 @@ def summarize_stats(stats_csv: str, bench_json: str, out_md: str, command: str) 
             + (f"{roof['algorithmic_bytes_per_launch'] / (prof_avg_us * 1e3):.1f} GB/s by rocprofv3"
                if prof_avg_us else "n/a"),
             ""]
+    others = []
+    for key in sorted(k for k in bench if k.startswith("window_m")):
+        r = bench[key]["roofline"]
+        others.append((f"{key} roofline kernel", r["kernel"], r["launch_avg_us"],
+                       r["algorithmic_bytes_per_launch"]))
+    if "w4a8_variant" in bench and bench["w4a8_variant"].get("kernels"):
+        k0 = bench["w4a8_variant"]["kernels"][0]
+        others.append(("w4a8_variant dominant kernel", k0["kernel"], k0["launch_avg_us"],
+                       k0["algorithmic_bytes_per_launch"]))
+    if others:
+        out += ["Other measured kernels of the same run (mean per launch; the bench's figure is "
+                "mix-weighted over the shapes of its step, as are rocprofv3's launches):", "",
+                "| section | kernel | rocprofv3 mean us | bench.py events us | GB/s (rocprofv3) |",
+                "|---|---|---:|---:|---:|"]
+        by_name = {r[0]: r for r in rows}
+        for what, name, ev_us, alg in others:
+            pr = by_name.get(name)
+            p_us = pr[3] / 1e3 if pr else None
+            out.append(f"| {what} | `{_cell(name)}` | {p_us:.2f} | {ev_us} | "
+                       f"{alg / (p_us * 1e3):.1f} |" if p_us else
+                       f"| {what} | `{_cell(name)}` | - | {ev_us} | - |")
+        out.append("")
     with open(out_md, "w") as f:
         f.write("\n".join(out))
     return {"rocprof_avg_us": prof_avg_us, "events_avg_us": roof["launch_avg_us"]}
@@ -143,33 +176,47 @@ def _counter_means(path: str, counter: str) -> dict:
 
 def summarize_pmc(fetch_csv: str, write_csv: str, bench_json: str, out_json: str, out_md: str,
                   command_fetch: str, command_write: str) -> dict:
+    """HBM traffic per launch of every linear kernel of the bench's step (and of
+    the 4-bit variant's, when it ran), scaled by the calibration copy."""
     bench = _bench_line(bench_json)
-    kname = bench["roofline"]["kernel"]
     copy_bytes = bench["copy_calibration"]["bytes"]
     fetch = _counter_means(fetch_csv, "FETCH_SIZE")
     write = _counter_means(write_csv, "WRITE_SIZE")
     cf, cw = fetch[COPY_KERNEL][0], write[COPY_KERNEL][0]
     f_scale, w_scale = copy_bytes / cf, copy_bytes / cw  # bytes per counter unit
-    kf, nf = fetch[kname]
-    kw, nw = write[kname]
-    traffic = kf * f_scale + kw * w_scale
-    alg = bench["roofline"]["algorithmic_bytes_per_launch"]
+    step_kernels = list(bench.get("kernels", []))
+    step_kernels += list(bench.get("w4a8_variant", {}).get("kernels", []))
+    kernels = {}
+    for k in step_kernels:
+        name = k["kernel"]
+        if name not in fetch or name not in write:
+            continue
+        kf, nf = fetch[name]
+        kw, nw = write[name]
+        traffic = kf * f_scale + kw * w_scale
+        alg = k["algorithmic_bytes_per_launch"]
+        kernels[name] = {
+            "kernel_source_hash": kernel_source_hash(name),
+            "traffic_bytes_per_launch": round(traffic),
+            "fetch_bytes_per_launch": round(kf * f_scale),
+            "write_bytes_per_launch": round(kw * w_scale),
+            "algorithmic_bytes_per_launch": alg,
+            "traffic_over_algorithmic": round(traffic / alg, 4),
+            "dispatches_averaged": {"FETCH_SIZE": nf, "WRITE_SIZE": nw},
+        }
     res = {
-        "kernel": kname,
-        "kernel_source_hash": kernel_source_hash(),
-        "traffic_bytes_per_launch": round(traffic),
-        "fetch_bytes_per_launch": round(kf * f_scale),
-        "write_bytes_per_launch": round(kw * w_scale),
-        "algorithmic_bytes_per_launch": alg,
-        "traffic_over_algorithmic": round(traffic / alg, 4),
-        "dispatches_averaged": {"FETCH_SIZE": nf, "WRITE_SIZE": nw},
+        "workload": bench["config"]["workload"],
+        "M": bench["config"]["M"],
+        "roofline_kernel": bench["roofline"]["kernel"],
+        "kernels": kernels,
         "calibration": {"kernel": COPY_KERNEL, "bytes": copy_bytes,
                         "FETCH_SIZE": cf, "WRITE_SIZE": cw,
                         "bytes_per_unit_fetch": round(f_scale, 4),
                         "bytes_per_unit_write": round(w_scale, 4)},
         "commands": [command_fetch, command_write],
         "note": "FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by its reading for a "
-                "plain copy of a known size; mean over every launch of the kernel in the run",
+                "plain copy of a known size; mean over every launch of the kernel in the run "
+                "(the step's mix of shapes)",
     }
     with open(out_json, "w") as f:
         json.dump(res, f, indent=1)
@@ -180,13 +227,17 @@ def summarize_pmc(fetch_csv: str, write_csv: str, bench_json: str, out_json: str
            f"Calibration: `{COPY_KERNEL}` copies {copy_bytes} bytes; it reads FETCH_SIZE {cf:.1f} "
            f"and WRITE_SIZE {cw:.1f}, i.e. {f_scale:.2f} and {w_scale:.2f} bytes per counter unit.",
            "",
+           "Linear kernels of the step (mean per launch over the step's mix of shapes):", "",
            "| kernel | dispatches | FETCH bytes/launch | WRITE bytes/launch | traffic | algorithmic | ratio |",
-           "|---|---:|---:|---:|---:|---:|---:|",
-           f"| `{kname}` | {nf} | {kf * f_scale:.0f} | {kw * w_scale:.0f} | {traffic:.0f} | {alg} | "
-           f"{traffic / alg:.4f} |", "",
-           "Other kernels of the run (scaled the same way, bytes per dispatch):", "",
-           "| kernel | dispatches | FETCH | WRITE |", "|---|---:|---:|---:|"]
-    for name in sorted(set(fetch) & set(write), key=lambda n: -fetch[n][0] * fetch[n][1])[:12]:
+           "|---|---:|---:|---:|---:|---:|---:|"]
+    for name, r in kernels.items():
+        out.append(f"| `{name}` | {r['dispatches_averaged']['FETCH_SIZE']} | "
+                   f"{r['fetch_bytes_per_launch']} | {r['write_bytes_per_launch']} | "
+                   f"{r['traffic_bytes_per_launch']} | {r['algorithmic_bytes_per_launch']} | "
+                   f"{r['traffic_over_algorithmic']:.4f} |")
+    out += ["", "Every kernel of the run (scaled the same way, bytes per dispatch):", "",
+            "| kernel | dispatches | FETCH | WRITE |", "|---|---:|---:|---:|"]
+    for name in sorted(set(fetch) & set(write), key=lambda n: -fetch[n][0] * fetch[n][1])[:16]:
         out.append(f"| `{_cell(name)}` | {fetch[name][1]} | {fetch[name][0] * f_scale:.0f} | "
                    f"{write[name][0] * w_scale:.0f} |")
     out.append("")
