@@ -74,6 +74,8 @@ def parse():
                     help="batched verify windows timed over the same weights ('' for none)")
     ap.add_argument("--no-chain", action="store_true", help="skip the chained (one-launch) step")
     ap.add_argument("--no-config0", action="store_true", help="skip the single-linear latency")
+    ap.add_argument("--no-shards", action="store_true",
+                    help="skip the 8-way tensor-parallel shard shapes")
     ap.add_argument("--tau-sets", type=int, default=2048,
                     help="seeded draft sets for the mean accepted length")
     return ap.parse_args()
@@ -745,6 +747,75 @@ def config0_latency(blocker_bytes: int = COPY_BYTES):
                       "queued behind ~20 ms of copies"}
 
 
+TP8_SHARDS = [("qkv/8", 4096, 768), ("o/8", 512, 4096), ("gate_up/8", 4096, 3072),
+              ("down/8", 1536, 4096), ("lm_head/8", 4096, 18992)]
+
+
+def tp8_shard_shapes(M: int, blocker_bytes: int = COPY_BYTES):
+    """One GPU's share of each linear under 8-way tensor parallelism (column-
+    parallel QKV, gate_up and LM head: N / 8; row-parallel O and down: K / 8)
+    at the same window: launch time over 1 GiB of rotating weight copies, queued
+    behind ~20 ms of copies, HIP events.  The single-GPU build runs the shard
+    shapes only; the all-reduce of the row-parallel partial outputs is not in it."""
+    import numpy as np
+    import torch
+    import ctypes
+    from w8a8_quantized_speculative_amd import binding, synth
+    L = binding.lib()
+    P = ctypes.c_void_p
+    blk_src = torch.empty(blocker_bytes, dtype=torch.uint8, device="cuda")
+    blk_dst = torch.empty_like(blk_src)
+    stream = binding._stream()
+    rows = []
+    for name, K, N in TP8_SHARDS:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(77 + N + K)
+        w = (torch.randn((N, K), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+        x_bits = synth.activations(M, K, (9, N, K))
+        x = torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+        s = synth.smoothing_vector(synth.col_absmax_bf16(x_bits),
+                                   w.abs().amax(dim=0).float().cpu().numpy().astype(np.float64))
+        s_d = torch.from_numpy(s).cuda()
+        wq, sw = binding.quasar_quantize_weights(w, s_d)
+        del w
+        nbytes = wq.codes.numel()
+        copies = max(2, -(-(1 << 30) // nbytes))
+        pool = wq.codes.repeat(copies)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        ws = binding.new_workspace(binding.workspace_bytes_linear(M, N, K))
+
+        def launch(i):
+            st = L.quasar_w8a8_linear(P(x.data_ptr()), P(s_d.data_ptr()),
+                                      P(pool.data_ptr() + (i % copies) * nbytes), P(sw.data_ptr()),
+                                      M, N, K, P(y.data_ptr()), None, P(ws.data_ptr()), ws.numel(),
+                                      stream)
+            if st != 0:
+                raise binding.QuasarError("quasar_w8a8_linear", st)
+
+        for i in range(4):
+            launch(i)
+        torch.cuda.synchronize()
+        for _ in range(BLOCKER_COPIES):
+            binding.quasar_stream_copy(blk_src, blk_dst)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        reps = 400
+        t0.record()
+        for i in range(reps):
+            launch(i)
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) * 1e3 / reps
+        nb = algorithmic_bytes(M, N, K)
+        rows.append({"linear": name, "N": N, "K": K, "kernel": binding.w8a8_kernel_name(M, N, K),
+                     "us_per_launch": round(us, 2), "gbs": round(nb / (us * 1e-6) / 1e9, 1),
+                     "frac_of_hbm_peak": round(nb / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)})
+        del pool, wq, sw, ws
+        torch.cuda.empty_cache()
+    del blk_src, blk_dst
+    return rows
+
+
 def read_calibration():
     """A plain read-only 16-byte stream over 1 GiB: the measured ceiling of a
     read stream, the shape of the verify linears' weight traffic."""
@@ -1137,6 +1208,23 @@ def main():
     if not args.no_config0:
         print("[bench] single 1024 x 1024 linear (latency)", file=sys.stderr, flush=True)
         out["config0_latency"] = config0_latency()
+    if not args.no_shards:
+        print("[bench] 8-way tensor-parallel shard shapes", file=sys.stderr, flush=True)
+        shards = tp8_shard_shapes(args.m)
+        floor = out.get("config0_latency", {}).get("us_per_launch")
+        out["tp8_shards"] = {
+            "what": f"one GPU's share of each linear under 8-way tensor parallelism at M={args.m} "
+                    "(column-parallel QKV, gate_up, LM head: N/8; row-parallel O, down: K/8)",
+            "linears": shards,
+            "latency_floor_us": floor,
+            "note": "over_floor: the shard's launch time over the single 1024 x 1024 linear's "
+                    "(1.1 MB), the latency floor of one launch (launch, activation load and "
+                    "quantization, epilogue); a shard near 1 is latency-bound, and no split of "
+                    "its work over more workgroups can shorten it",
+        }
+        if floor:
+            for r in shards:
+                r["over_floor"] = round(r["us_per_launch"] / floor, 3)
     if not args.no_cpu_baseline:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_oracle_baseline(args.m, args.cpu_seconds)

@@ -151,6 +151,27 @@ def test_qwen3_layer_linear_full_size_sampled(name, K, N, M):
     assert np.array_equal(unpack_weights(wq, N, K)[cols], ref["qw"])
 
 
+# One GPU's share of each Qwen3-8B linear under 8-way tensor parallelism:
+# column-parallel QKV, gate_up and LM head (N / 8), row-parallel O and down
+# (K / 8).  (name, K, N)
+TP8_SHARDS = [("qkv/8", 4096, 768), ("o/8", 512, 4096), ("gate_up/8", 4096, 3072),
+              ("down/8", 1536, 4096), ("lm_head/8", 4096, 18992)]
+
+
+@pytest.mark.parametrize("M", [1, 6, 8, 48])
+@pytest.mark.parametrize("name,K,N", TP8_SHARDS)
+def test_tp8_shard_shapes_every_element(name, K, N, M):
+    """The 8-way tensor-parallel shard shapes, every output element (the
+    shard's weights are a slice of the full layer's: any slice must match)."""
+    announce("tp8_shard", name, M, N, K)
+    key = (8, ["qkv/8", "o/8", "gate_up/8", "down/8", "lm_head/8"].index(name))
+    x = synth.activations(M, K, key)
+    w = synth.weights(N, K, key)
+    s = synth.smoothing_vector(synth.col_absmax_bf16(x), synth.col_absmax_bf16(w))
+    y, acc, _, _ = run_gpu(x, s, w)
+    check_against_oracle(x, s, w, y, acc)
+
+
 @pytest.mark.parametrize("M", [6, 48, 96, 128])
 def test_lm_head_full_size_sampled(M):
     """W8A8 LM head 4096 -> 151936 at the verify window M = 6, 48, 96, 128."""

@@ -1,7 +1,7 @@
 // extern "C" entry points of libquasar.so (declared in include/quasar.h).
 // Every call validates its arguments on the host first, so an argument error
 // never reaches the GPU, then enqueues its kernels on the caller's stream.
-#include "../../include/quasar.h"
+#include "quasar.h"
 #include "quasar_internal.hpp"
 #include "quasar_sync.hpp"
 

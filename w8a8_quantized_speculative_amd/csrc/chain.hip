@@ -50,7 +50,7 @@
 #include <float.h>
 #include <limits.h>
 
-#include "../../include/quasar.h"
+#include "quasar.h"
 #include "quasar_device.hpp"
 #include "quasar_internal.hpp"
 #include "quasar_sync.hpp"

@@ -53,8 +53,10 @@ __global__ __launch_bounds__(256) void stream_copy_kernel(const v4i* __restrict_
 // Plain streaming read: each workgroup reads one contiguous range with
 // 16-byte streaming (nt) loads, four per lane in flight, folded into one word
 // so the loads are kept: the reference rate for a read-only stream.  Measured
-// on MI355X over 1 GiB: 7.07 TB/s with 512 workgroups; grid-stride order gave
-// 5.2-5.9 TB/s, and plain (non-streaming) loads about 6.1 TB/s.
+// on MI355X: 7.07 TB/s over 1 GiB; one launch per buffer, back to back, 4.1,
+// 4.9, 5.8, 6.4 and 6.8 TB/s over 16.8, 25.2, 50.3, 100.7 and 622 MB.
+// Grid-stride order gave 5.2-5.9 TB/s over 1 GiB, and plain (non-streaming)
+// loads about 6.1 TB/s.
 __global__ __launch_bounds__(256) void stream_read_kernel(const v4i* __restrict__ src, size_t n16,
                                                           uint32_t* __restrict__ sink) {
   const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
@@ -123,9 +125,12 @@ hipError_t launch_zero_flag_header(void* workspace, hipStream_t st) {
 
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t st) {
   const size_t n16 = bytes / 16;
-  // two workgroups per compute unit, each with at least 16 KB to read
+  // up to eight workgroups per compute unit, each with at least 16 KB to read
+  // (within 3% of the fastest grid at every size measured up to 622 MB); two
+  // per compute unit from 512 MB on (7.07 against 6.7-6.9 TB/s over 1 GiB)
   size_t blocks = (n16 + 1023) / 1024;
-  if (blocks > 2 * (size_t)kNumCU) blocks = 2 * (size_t)kNumCU;
+  const size_t cap = (bytes >= ((size_t)512 << 20) ? 2 : 8) * (size_t)kNumCU;
+  if (blocks > cap) blocks = cap;
   if (blocks == 0) return hipSuccess;
   stream_read_kernel<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(static_cast<const v4i*>(src),
                                                                    n16, sink);
