@@ -108,7 +108,8 @@ class Weights:
             ent = dict(layer=layer, name=name, role=role, N=N, K=K, s=s_d, wq=wq, sw=sw)
             if name == "gate_up":  # the decoder step and the chain run gate_up with SiLU fused
                 ent["wqg"], ent["swg"] = binding.quasar_quantize_weights_gated(w, s_d)
-            if keep_bf16:
+            if keep_bf16:  # the 4-bit variant and the BF16 comparator
+                ent["wq4"], ent["sw4"] = binding.quasar_quantize_weights_w4(w, s_d)
                 ent["w_bf16"] = w
             else:
                 del w
@@ -165,7 +166,8 @@ class Stack:
             wq, sw = (e["wq"], e["sw"]) if bits == 8 else (e["wq4"], e["sw4"])
             head = (P(e["x"].data_ptr()), P(e["s"].data_ptr()), P(wq.data_ptr()),
                     P(sw.data_ptr()), self.M, e["N"], e["K"], P(e["y"].data_ptr()), None)
-            e[key] = head + ((P(self.ws.data_ptr()), self.ws.numel()) if bits == 8 else ())
+            ws = self.ws if bits == 8 else self.ws4
+            e[key] = head + (P(ws.data_ptr()), ws.numel())
         L = binding.lib()
         fn = L.quasar_w8a8_linear if bits == 8 else L.quasar_w4a8_linear
         st = fn(*e[key], binding._stream())
@@ -215,14 +217,14 @@ class Stack:
         self.lm_head_verify_call(1.0)
 
     def build_w4(self):
-        """4-bit copies of every linear's weights, from the kept BF16 weights."""
+        """The 4-bit variant's workspace (the 4-bit weights are shared)."""
         import torch
         from w8a8_quantized_speculative_amd import binding
-        for e in self.linears:
-            e["wq4"], e["sw4"] = binding.quasar_quantize_weights_w4(e["w_bf16"], e["s"])
-        torch.cuda.synchronize()
+        self.ws4 = binding.new_workspace(max(binding.workspace_bytes_w4(self.M, e["N"], e["K"])
+                                             for e in self.linears))
         self.bytes_step_w4 = sum(algorithmic_bytes_w4(self.M, e["N"], e["K"]) for e in self.linears) \
             + 4 * self.B * self.k + 8 * self.B
+        torch.cuda.synchronize()
 
     def step_w4(self):
         """The same step with 4-bit weights: every linear through quasar_w4a8_linear,
@@ -543,6 +545,51 @@ def time_bf16_comparator(stack, warmup: int, steps: int):
     return ms, bf16_bytes
 
 
+def time_w4_variant(stack, args, ms_w8: float):
+    """The same stack and LM head with 4-bit per-channel weights
+    (quasar_w4a8_linear), then the greedy accept: its own planted drafts and
+    mean tau, the faster of a HIP graph and plain launches, every linear's
+    launch time and the dominant kernel's roofline."""
+    import numpy as np
+    import torch
+    from w8a8_quantized_speculative_amd import binding, synth
+    stack.build_w4()
+    stack.step_w4()
+    torch.cuda.synchronize()
+    g4 = stack.argmax.cpu().numpy()
+    drafts4 = torch.from_numpy(np.stack([synth.draft_tokens(g4[:, :stack.k], stack.V, 0.3, (6, i))
+                                         for i in range(args.warmup + args.steps)])).cuda()
+    tau4 = measure_tau(stack, max(64, args.tau_sets // (1 if stack.M <= 8 else 8)))
+    ms4, ms4_ev, _, _g4 = time_graph_steps(stack, drafts4, args.warmup, args.steps,
+                                           step=stack.step_w4)
+    del _g4
+    e4 = time_eager_steps(stack, drafts4, args.warmup, args.steps, step=stack.step_w4)
+    mode = "graph"
+    if e4[0] < ms4:
+        ms4, ms4_ev, mode = e4[0], e4[1], "eager"
+    k4, l4 = kernel_groups(stack, time_kernels(stack, max(2, args.steps // 4), bits=4), bits=4)
+    t4, t4_note = read_traffic(stack.M, k4[0]["kernel"])
+    return {
+        "what": "same stack and LM head with 4-bit per-channel weights (quasar_w4a8_linear), "
+                "then the greedy accept",
+        "kernel": k4[0]["kernel"],
+        "ms_per_step": round(ms4, 4),
+        "ms_per_step_events": round(ms4_ev, 4),
+        "timing": mode,
+        "gbs": round(stack.bytes_step_w4 / (ms4 * 1e-3) / 1e9, 1),
+        "weights_int4_gb": round(sum(e["N"] * e["K"] for e in stack.linears) / 2e9, 3),
+        "verified_tokens_per_s": round(stack.B * tau4 / (ms4 * 1e-3), 1),
+        "mean_tau": round(tau4, 4),
+        "speedup_vs_w8a8": round(ms_w8 / ms4, 3),
+        "roofline": {"bound": "hbm", "kernel": k4[0]["kernel"], "achieved": k4[0]["gbs"],
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(k4[0]["gbs"] / PEAK_HBM_GBS, 4), "traffic": t4,
+                     "traffic_note": t4_note, "launch_avg_us": k4[0]["launch_avg_us"],
+                     "algorithmic_bytes_per_launch": k4[0]["algorithmic_bytes_per_launch"]},
+        "kernels": k4, "linears": l4,
+    }
+
+
 def kernel_groups(stack, per_shape, bits: int = 8):
     """Per kernel symbol: launches of one step, their algorithmic bytes and ops,
     and the mean launch time (from the per-shape timings); sorted by bytes."""
@@ -630,6 +677,8 @@ def time_window(W, M: int, args):
         out["bf16_comparator"] = {"ms_per_step": round(bms, 4),
                                   "gbs": round(bbytes / (bms * 1e-3) / 1e9, 1),
                                   "w8a8_speedup": round(bms / ms, 3)}
+        if M <= 96:
+            out["w4a8_variant"] = time_w4_variant(st, args, ms)
     del st
     torch.cuda.empty_cache()
     return out
@@ -1155,44 +1204,9 @@ def main():
             "gbs": round(bbytes / (bms * 1e-3) / 1e9, 1),
             "w8a8_speedup": round(bms / lin_ms, 3),
         }
-    if not args.no_bf16 and args.m <= 8:
-        # the 4-bit weight variant of the same stack (its own planted drafts and tau)
+    if not args.no_bf16 and args.m <= 96:
         print("[bench] 4-bit weight variant", file=sys.stderr, flush=True)
-        import numpy as np
-        from w8a8_quantized_speculative_amd import synth
-        stack.build_w4()
-        stack.step_w4()
-        torch.cuda.synchronize()
-        g4 = stack.argmax.cpu().numpy()
-        drafts4 = torch.from_numpy(np.stack([synth.draft_tokens(g4[:, :stack.k], stack.V, 0.3, (6, i))
-                                             for i in range(args.warmup + args.steps)])).cuda()
-        tau4 = measure_tau(stack, args.tau_sets)
-        ms4, ms4_ev, _, _g4 = time_graph_steps(stack, drafts4, args.warmup, args.steps,
-                                               step=stack.step_w4)
-        del _g4
-        e4 = time_eager_steps(stack, drafts4, args.warmup, args.steps, step=stack.step_w4)
-        if e4[0] < ms4:
-            ms4, ms4_ev = e4[0], e4[1]
-        k4, l4 = kernel_groups(stack, time_kernels(stack, max(2, args.steps // 4), bits=4), bits=4)
-        t4, t4_note = read_traffic(args.m, k4[0]["kernel"])
-        out["w4a8_variant"] = {
-            "what": "same stack and LM head with 4-bit per-channel weights (quasar_w4a8_linear), "
-                    "then the greedy accept; the faster of a HIP graph and plain launches",
-            "kernel": binding.w4a8_kernel_name(args.m, 4096, 4096),
-            "ms_per_step": round(ms4, 4),
-            "ms_per_step_events": round(ms4_ev, 4),
-            "gbs": round(stack.bytes_step_w4 / (ms4 * 1e-3) / 1e9, 1),
-            "weights_int4_gb": round(sum(e["N"] * e["K"] for e in stack.linears) / 2e9, 3),
-            "verified_tokens_per_s": round(stack.B * tau4 / (ms4 * 1e-3), 1),
-            "mean_tau": round(tau4, 4),
-            "speedup_vs_w8a8": round(ms / ms4, 3),
-            "roofline": {"bound": "hbm", "kernel": k4[0]["kernel"], "achieved": k4[0]["gbs"],
-                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(k4[0]["gbs"] / PEAK_HBM_GBS, 4), "traffic": t4,
-                         "traffic_note": t4_note, "launch_avg_us": k4[0]["launch_avg_us"],
-                         "algorithmic_bytes_per_launch": k4[0]["algorithmic_bytes_per_launch"]},
-            "kernels": k4, "linears": l4,
-        }
+        out["w4a8_variant"] = time_w4_variant(stack, args, ms)
     if not args.no_chain and args.m <= 8:
         print("[bench] chained step (one persistent launch)", file=sys.stderr, flush=True)
         out["chained_step"] = time_chained_step(stack, drafts, args, ms)

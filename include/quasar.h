@@ -481,20 +481,34 @@ quasar_status quasar_quantize_weights_w4(const uint16_t* w, const float* s, int6
                                          int8_t* wq4, float* w_scale, void* stream);
 
 /*
+ * quasar_w4a8_workspace_bytes -- device workspace quasar_w4a8_linear needs for
+ * M x N x K: 0 for windows of at most 8 tokens with K <= 12288 (one launch,
+ * no workspace), else the wide kernel's (flag header first, zero before the
+ * first use, as for quasar_w8a8_workspace_bytes).  0 also for unsupported
+ * sizes (K % 128 != 0, M > 96 with 4-bit weights).
+ */
+size_t quasar_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
  * quasar_w4a8_linear -- the verify linear with 4-bit weights: y = BF16(
  * RN32(RN32(RN32(acc) * sx_m) * sw_n)) with acc = sum_k qx[m,k] * qw4[n,k]
  * exact, qx the dynamic per-token INT8 codes of RN32(x * s) as in
- * quasar_w8a8_linear.  One kernel launch, no workspace.
+ * quasar_w8a8_linear.  One kernel launch.
  *   x, s, y, acc_out  as for quasar_w8a8_linear
  *   wq4, w_scale      from quasar_quantize_weights_w4
- *   M, N, K           1 <= M <= 8 (the verify window of one to a few
- *                     sequences), N >= 0, 128 <= K <= 12288, K % 128 == 0
+ *   M, N, K           1 <= M <= 96, N >= 0, 128 <= K <= 65536, K % 128 == 0
+ *   workspace         quasar_w4a8_workspace_bytes(M, N, K) bytes, 256-byte
+ *                     aligned (may be NULL when that is 0); one call at a
+ *                     time per workspace
  * M == 0 or N == 0 is a no-op.  Errors: INVALID_ARG (including K % 128 != 0),
- * UNSUPPORTED (M > 8 or K > 12288), HIP.
+ * UNSUPPORTED (M > 96, or a window of more than 8 tokens wider than one
+ * workgroup per compute unit), WORKSPACE, HIP; a bounded wait that gave up is
+ * reported by quasar_device_check.
  */
 quasar_status quasar_w4a8_linear(const uint16_t* x, const float* s, const int8_t* wq4,
                                  const float* w_scale, int64_t M, int64_t N, int64_t K,
-                                 uint16_t* y, int32_t* acc_out, void* stream);
+                                 uint16_t* y, int32_t* acc_out, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /* Profiler name of the kernel quasar_w4a8_linear launches for M x N x K ("" if
  * unsupported); a diagnostic for the benchmark and profiles. */

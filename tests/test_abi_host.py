@@ -52,7 +52,7 @@ def test_status_strings(L):
     for code in range(6):
         assert L.quasar_status_string(code).decode().startswith("QUASAR_")
     assert b"UNKNOWN" in L.quasar_status_string(99)
-    assert L.quasar_abi_version() == 10
+    assert L.quasar_abi_version() == 11
 
 
 def test_workspace_header_and_init_errors(L):
@@ -187,13 +187,23 @@ def test_w4_argument_errors_and_sizes(L):
     assert qw4(FAKE, FAKE, 10, 8, FAKE, FAKE, None) == INVALID
     assert qw4(FAKE, FAKE, 0, 128, None, None, None) == OK
     assert qw4(FAKE, FAKE + 4, 10, 128, FAKE, FAKE, None) == INVALID
-    lin4 = lambda M=6, N=32, K=128, x=FAKE, y=FAKE: L.quasar_w4a8_linear(
-        x, FAKE, FAKE, FAKE, M, N, K, y, None, None)
+    lin4 = lambda M=6, N=32, K=128, x=FAKE, y=FAKE, ws=None, nb=0: L.quasar_w4a8_linear(
+        x, FAKE, FAKE, FAKE, M, N, K, y, None, ws, nb, None)
     assert lin4(K=192) == INVALID
-    assert lin4(M=9) == UNSUPPORTED                                 # the 4-bit kernel is M <= 8
-    assert lin4(K=12288 + 128) == UNSUPPORTED
+    assert lin4(M=97) == UNSUPPORTED                                # 4-bit weights: M <= 96
+    assert lin4(M=129) == UNSUPPORTED
+    assert lin4(M=9) == WORKSPACE                                   # the wide kernel needs one
+    assert lin4(K=12288 + 128) == WORKSPACE
+    need = L.quasar_w4a8_workspace_bytes(9, 32, 128)
+    assert need >= L.quasar_workspace_header_bytes()
+    assert lin4(M=9, ws=FAKE, nb=need - 256) == WORKSPACE
+    assert lin4(M=9, ws=FAKE + 16, nb=need) == WORKSPACE             # not 256-byte aligned
     assert lin4(M=0) == OK and lin4(N=0) == OK
     assert lin4(x=None) == INVALID and lin4(y=FAKE + 1) == INVALID
+    ws4 = L.quasar_w4a8_workspace_bytes
+    assert ws4(6, 4096, 4096) == 0 and ws4(8, 4096, 12288) == 0     # one launch, no workspace
+    assert ws4(48, 4096, 4096) > 0 and ws4(96, 24576, 4096) > 0 and ws4(6, 64, 16384) > 0
+    assert ws4(97, 16, 128) == 0 and ws4(48, 16, 192) == 0 and ws4(0, 16, 128) == 0
     assert L.quasar_packed_weight_bytes_w4(4096, 4096) == 4096 * 4096 // 2
     assert L.quasar_packed_weight_bytes_w4(17, 256) == 2 * 2 * 1024
     assert L.quasar_packed_weight_bytes_w4(16, 192) == 0
@@ -201,7 +211,13 @@ def test_w4_argument_errors_and_sizes(L):
     assert name(6, 4096, 4096) == "w4a8_linear_fused_kernel<6, 4, 1>"
     assert name(6, 4096, 12288) == "w4a8_linear_fused_kernel<6, 4, 3>"
     assert name(1, 16, 8192) == "w4a8_linear_fused_kernel<2, 4, 2>"
-    assert name(9, 16, 128) == "" and name(6, 16, 192) == ""
+    # wider windows: the wide kernel with 4-bit weights, <token blocks, tiles per group>
+    assert name(9, 16, 128) == "w4a8_linear_wide_kernel<1, 1>"
+    assert name(48, 4096, 4096) == "w4a8_linear_wide_kernel<3, 1>"
+    assert name(96, 6144, 4096) == "w4a8_linear_wide_kernel<6, 2>"
+    assert name(96, 24576, 4096) == "w4a8_linear_wide_kernel<6, 4>"
+    assert name(6, 64, 16384) == "w4a8_linear_wide_kernel<1, 2>"
+    assert name(97, 16, 128) == "" and name(6, 16, 192) == ""
 
 
 def test_packed_weight_bytes(L):

@@ -51,6 +51,23 @@ def _shapes_w4(n=15, seed=2027):
 SHAPES_W4 = _shapes_w4()
 
 
+def _shapes_w4_wide(n=10, seed=2028):
+    """Random windows of 9 to 96 tokens for the wide kernel's 4-bit path."""
+    g = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        M = int(g.integers(9, 97))
+        K = 128 * int(g.integers(1, 97))
+        N = int(g.choice([g.integers(1, 300), g.integers(300, 5000), g.integers(5000, 40000)]))
+        if N * K > 1.2e8:
+            continue
+        out.append((M, N, K))
+    return out
+
+
+SHAPES_W4_WIDE = _shapes_w4_wide()
+
+
 @pytest.mark.parametrize("i", range(len(SHAPES)), ids=[f"{m}x{n}x{k}" for m, n, k in SHAPES])
 def test_random_shape_every_element(i):
     M, N, K = SHAPES[i]
@@ -71,6 +88,21 @@ def test_random_shape_w4_every_element(i):
     M, N, K = SHAPES_W4[i]
     announce("random_shape_w4", i, M, N, K)
     x, w, s = synth.linear_case(M, K, N, (61, i))
+    wq4, sw4 = binding.quasar_quantize_weights_w4(dev_bf16(w), dev(s))
+    acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    y = binding.quasar_w4a8_linear(dev_bf16(x), dev(s), wq4, sw4, acc_out=acc)
+    torch.cuda.synchronize()
+    ref = orc.w4a8_linear_rows(x, s, w)
+    assert np.array_equal(host(acc), ref["acc"].astype(np.int32))
+    assert np.array_equal(host_bf16(y), ref["y"])
+
+
+@pytest.mark.parametrize("i", range(len(SHAPES_W4_WIDE)),
+                         ids=[f"{m}x{n}x{k}" for m, n, k in SHAPES_W4_WIDE])
+def test_random_shape_w4_wide_every_element(i):
+    M, N, K = SHAPES_W4_WIDE[i]
+    announce("random_shape_w4_wide", i, M, N, K)
+    x, w, s = synth.linear_case(M, K, N, (62, i))
     wq4, sw4 = binding.quasar_quantize_weights_w4(dev_bf16(w), dev(s))
     acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
     y = binding.quasar_w4a8_linear(dev_bf16(x), dev(s), wq4, sw4, acc_out=acc)

@@ -47,6 +47,15 @@ SHAPES = [
     (1, 16, 128), (6, 1000, 1024), (6, 4096, 256), (2, 7, 384), (8, 300, 4096), (3, 40, 6144),
     (7, 100, 8064), (8, 64, 10112), (4, 520, 12288), (6, 9000, 1024), (5, 33, 12288),
     (6, 16400, 512), (1, 143000, 128),
+    # wide windows (and K > 12288): the wide kernel with 4-bit weight blocks --
+    # every token-block count it takes (1..6), an odd number of chunk pairs
+    # (a last item with fewer than 4 pairs), single tiles, tile pairs (K > 8192;
+    # more tiles than workgroups past 64 tokens, odd tile count) and groups of
+    # 4 split across workgroups, empty ranges
+    (9, 100, 1024), (20, 64, 4096), (33, 1000, 2176), (48, 520, 4096), (64, 260, 1152),
+    (80, 300, 4096), (96, 77, 3072), (96, 520, 12288), (40, 8000, 512), (24, 6144, 4096),
+    (96, 6152, 4096), (72, 4104, 2048), (6, 64, 16384), (50, 48, 20480), (20, 16400, 384),
+    (96, 16384, 1024), (9, 16390, 4224), (17, 500, 65536),
 ]
 
 
@@ -78,11 +87,11 @@ def test_w4_zero_rows_and_extreme_codes():
     assert np.abs(unpack_weights_w4(wq, N, K)[9]).min() >= 6
 
 
+@pytest.mark.parametrize("M", [6, 48, 96])
 @pytest.mark.parametrize("name,K,N", synth.QWEN3_8B_LINEARS + (synth.QWEN3_8B_LM_HEAD,))
-def test_w4_qwen3_shapes_sampled(name, K, N):
-    """The Qwen3-8B-shaped layer linears and the LM head at M = 6: every output
-    of sampled channels (the oracle quantizes just those rows)."""
-    M = 6
+def test_w4_qwen3_shapes_sampled(name, K, N, M):
+    """The Qwen3-8B-shaped layer linears and the LM head at M = 6, 48 and 96:
+    every output of sampled channels (the oracle quantizes just those rows)."""
     announce("w4_qwen3", name, M, N, K)
     key = (53, ["qkv", "o", "gate_up", "down", "lm_head"].index(name))
     x = synth.activations(M, K, key)

@@ -63,7 +63,9 @@ _SIGNATURES = {
     "quasar_w8a8_kernel_name": (ctypes.c_char_p, [_I64, _I64, _I64]),
     "quasar_packed_weight_bytes_w4": (_SZ, [_I64, _I64]),
     "quasar_quantize_weights_w4": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P]),
-    "quasar_w4a8_linear": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P]),
+    "quasar_w4a8_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64]),
+    "quasar_w4a8_linear": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P,
+                                          ctypes.c_size_t, _P]),
     "quasar_w4a8_kernel_name": (ctypes.c_char_p, [_I64, _I64, _I64]),
     "quasar_stream_copy": (ctypes.c_int, [_P, _P, _SZ, _P]),
     "quasar_stream_read": (ctypes.c_int, [_P, _SZ, _P, _P]),
@@ -430,10 +432,14 @@ def quasar_quantize_weights_w4(w: torch.Tensor, s: torch.Tensor):
     return wq, sw
 
 
+def workspace_bytes_w4(M: int, N: int, K: int) -> int:
+    return int(lib().quasar_w4a8_workspace_bytes(M, N, K))
+
+
 def quasar_w4a8_linear(x: torch.Tensor, s: torch.Tensor, wq: PackedWeights, w_scale: torch.Tensor,
-                       out: torch.Tensor | None = None,
-                       acc_out: torch.Tensor | None = None) -> torch.Tensor:
-    """Y [M, N] bf16 = dequant(quant(X diag(s)) @ W4^T) for X [M, K] bf16, M <= 8."""
+                       out: torch.Tensor | None = None, acc_out: torch.Tensor | None = None,
+                       workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Y [M, N] bf16 = dequant(quant(X diag(s)) @ W4^T) for X [M, K] bf16, M <= 96."""
     M, K = x.shape
     N = wq.N
     if not isinstance(wq, PackedWeights) or wq.K != K or wq.bits != 4:
@@ -446,8 +452,13 @@ def quasar_w4a8_linear(x: torch.Tensor, s: torch.Tensor, wq: PackedWeights, w_sc
     _need(out, torch.bfloat16, (M, N), "out")
     if acc_out is not None:
         _need(acc_out, torch.int32, (M, N), "acc_out")
+    need = workspace_bytes_w4(M, N, K)
+    if workspace is None and need > 0:
+        workspace = new_workspace(need, x.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("quasar_w4a8_linear", lib().quasar_w4a8_linear(
-        _ptr(x), _ptr(s), _ptr(wq), _ptr(w_scale), M, N, K, _ptr(out), _ptr(acc_out), _stream()))
+        _ptr(x), _ptr(s), _ptr(wq), _ptr(w_scale), M, N, K, _ptr(out), _ptr(acc_out),
+        _ptr(workspace), nbytes, _stream()))
     return out
 
 

@@ -147,7 +147,7 @@ const char* quasar_status_string(quasar_status status) {
   return "QUASAR_ERR_UNKNOWN";
 }
 
-int quasar_abi_version(void) { return 10; }
+int quasar_abi_version(void) { return 11; }
 
 quasar_status quasar_device_check(uint32_t* detail) {
   uint32_t bits = 0;
@@ -378,28 +378,49 @@ quasar_status quasar_quantize_weights_w4(const uint16_t* w, const float* s, int6
   return hip_status(launch_quantize_weights_w4(w, s, N, K, wq4, w_scale, (hipStream_t)stream));
 }
 
+// 4-bit weights: the one-launch kernel of small windows (M <= 8, K <= 12288)
+// without workspace, else the wide kernel (M <= 96) with one.
+static bool w4_shape_ok(int64_t M, int64_t N, int64_t K) {
+  return M > 0 && N > 0 && check_k(K) == QUASAR_OK && K % 128 == 0 && N <= kMaxRowsPerCall &&
+         (w4_supported(M, K) || wide_w4_supported(M));
+}
+
+size_t quasar_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (!w4_shape_ok(M, N, K) || w4_supported(M, K)) return 0;
+  return plan_wide(M, N, K, kWideMaxGrid, 4).bytes;
+}
+
 quasar_status quasar_w4a8_linear(const uint16_t* x, const float* s, const int8_t* wq4,
                                  const float* w_scale, int64_t M, int64_t N, int64_t K,
-                                 uint16_t* y, int32_t* acc_out, void* stream) {
+                                 uint16_t* y, int32_t* acc_out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
   if (M < 0 || N < 0) return QUASAR_ERR_INVALID_ARG;
   quasar_status st = check_k(K);
   if (st != QUASAR_OK) return st;
   if (K % 128 != 0) return QUASAR_ERR_INVALID_ARG;
-  if (N > kMaxRowsPerCall || !w4_supported(M > 0 ? M : 1, K)) return QUASAR_ERR_UNSUPPORTED;
+  if (N > kMaxRowsPerCall || M > QUASAR_MAX_M) return QUASAR_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return QUASAR_OK;
+  if (!w4_shape_ok(M, N, K)) return QUASAR_ERR_UNSUPPORTED;
   if (!x || !s || !wq4 || !w_scale || !y) return QUASAR_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(s, 16) || !aligned(wq4, 16) || !aligned(w_scale, 4) ||
       !aligned(y, 2) || (acc_out && !aligned(acc_out, 4)))
     return QUASAR_ERR_INVALID_ARG;
-  return hip_status(launch_fused_w4(plan_fused(M, N, K), x, s, wq4, w_scale, y, acc_out,
-                                    (hipStream_t)stream));
+  hipStream_t hs = (hipStream_t)stream;
+  if (w4_supported(M, K))  // one launch, no workspace
+    return hip_status(launch_fused_w4(plan_fused(M, N, K), x, s, wq4, w_scale, y, acc_out, hs));
+  WidePlan p = plan_wide(M, N, K, kWideMaxGrid, 4);
+  if (!workspace || workspace_bytes < p.bytes || !aligned(workspace, kWsAlign))
+    return QUASAR_ERR_WORKSPACE;
+  p.grid = wide_grid_for_current_device();
+  if (p.grid < M) return QUASAR_ERR_UNSUPPORTED;  // one resident workgroup per token row
+  return hip_status(launch_wide(p, x, s, wq4, w_scale, y, acc_out, workspace, hs));
 }
 
 const char* quasar_w4a8_kernel_name(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || N <= 0 || check_k(K) != QUASAR_OK || K % 128 != 0 || !w4_supported(M, K) ||
-      N > kMaxRowsPerCall)
-    return "";
-  return fused_w4_kernel_name(plan_fused(M, N, K));
+  if (!w4_shape_ok(M, N, K)) return "";
+  if (w4_supported(M, K)) return fused_w4_kernel_name(plan_fused(M, N, K));
+  const WidePlan p = plan_wide(M, N, K, kWideMaxGrid, 4);
+  return wide_kernel_name(p.mb, p.tg, 4);
 }
 
 size_t quasar_lm_head_verify_workspace_bytes(int64_t B, int64_t k, int64_t V, int64_t K) {

@@ -87,14 +87,17 @@ struct WidePlan {
   int P;       // items per group: ceil(nch / 4)
   int U;       // groups * P
   int grid;    // workgroups (<= kWideMaxGrid, >= M)
+  int wb;      // weight bits: 8 (INT8 layout) or 4 (4-bit layout)
   int lds;     // dynamic LDS bytes
   // workspace layout (byte offsets)
   size_t off_qx, off_sx, off_partials, bytes;
 };
 
 // `grid` only enters the launch; the workspace is sized for kWideMaxGrid.
-WidePlan plan_wide(int64_t M, int64_t N, int64_t K, int grid);
-const char* wide_kernel_name(int mb, int tg);
+WidePlan plan_wide(int64_t M, int64_t N, int64_t K, int grid, int wbits = 8);
+const char* wide_kernel_name(int mb, int tg, int wbits = 8);
+// 4-bit weights in the wide kernel: up to 96 tokens
+bool wide_w4_supported(int64_t M);
 int wide_tiles_per_group(int64_t M, int64_t N, int64_t K, int grid);
 // Workgroups of a wide launch on the current device (0: cannot run there).
 int wide_grid_for_current_device();

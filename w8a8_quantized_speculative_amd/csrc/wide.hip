@@ -66,6 +66,8 @@
 // up sets a bit of the device status word (undefined outputs) instead of
 // hanging.
 #include <mutex>
+#include <string>
+#include <vector>
 
 #include "quasar_device.hpp"
 #include "quasar_internal.hpp"
@@ -84,34 +86,43 @@ constexpr int kRowPieces = 8;  // 8-element pieces per helper thread kept in reg
 // (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt at their
 // maxima so they are not waited for).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
-// Items in flight per streamer (NBUF) for MB 16-token blocks and TG tiles per
-// group: the code slots (4 streamers x NBUF items x MB KB) and the partial-sum
-// area (2 x 4 x MB KB) stay within 150 KB of LDS, and the loads in flight per
-// wavefront ((NBUF - 1) items of TG + MB, plus one item's MB code loads)
+// Items in flight per streamer (NBUF) for MB 16-token blocks, TG tiles per
+// group and F code fragments per token block and item (1 for INT8 weights, 2
+// for 4-bit weights, whose 1 KB weight block holds two 64-wide K chunks): the
+// code slots (4 streamers x NBUF items x F MB KB) and the partial-sum area
+// (2 x 4 x MB KB) stay within 150 KB of LDS, and the loads in flight per
+// wavefront ((NBUF - 1) items of TG + F MB, plus one item's F MB code loads)
 // within what the 6-bit vmcnt counter can wait for.  At most 8.
-constexpr int wide_nbuf(int MB, int TG) {
+constexpr int wide_nbuf(int MB, int TG, int F = 1) {
   int nb = 8;
-  while (nb > 2 && (kS * nb * MB + 2 * kS * MB > 150 || (nb - 1) * (TG + MB) + MB > 63)) --nb;
+  while (nb > 2 && (kS * nb * F * MB + 2 * kS * MB > 150 || (nb - 1) * (TG + F * MB) + F * MB > 63))
+    --nb;
   return nb;
 }
-template <int MB, int TG>
+template <int MB, int TG, int F = 1>
 struct Wide {
-  static constexpr int NBUF = wide_nbuf(MB, TG);
-  static constexpr int SLOTS = kS * NBUF * MB * 1024;
+  static constexpr int NBUF = wide_nbuf(MB, TG, F);
+  static constexpr int SLOTS = kS * NBUF * F * MB * 1024;
   static constexpr int RED = 2 * kS * MB * 1024;
   static constexpr int SYNC = 256;
   static constexpr int LDS = SLOTS + RED + SYNC;
 };
-template <int MB>
+template <int MB, int F>
 constexpr bool wide_fits() {
-  return Wide<MB, 1>::LDS <= 150 * 1024 && Wide<MB, 2>::LDS <= 150 * 1024 &&
-         Wide<MB, 4>::LDS <= 150 * 1024 && (Wide<MB, 1>::NBUF - 1) * (1 + MB) + MB <= 63 &&
-         (Wide<MB, 2>::NBUF - 1) * (2 + MB) + MB <= 63 &&
-         (Wide<MB, 4>::NBUF - 1) * (4 + MB) + MB <= 63;
+  return Wide<MB, 1, F>::LDS <= 150 * 1024 && Wide<MB, 2, F>::LDS <= 150 * 1024 &&
+         Wide<MB, 4, F>::LDS <= 150 * 1024 &&
+         (Wide<MB, 1, F>::NBUF - 1) * (1 + F * MB) + F * MB <= 63 &&
+         (Wide<MB, 2, F>::NBUF - 1) * (2 + F * MB) + F * MB <= 63 &&
+         (Wide<MB, 4, F>::NBUF - 1) * (4 + F * MB) + F * MB <= 63;
 }
-static_assert(wide_fits<1>() && wide_fits<2>() && wide_fits<3>() && wide_fits<4>() &&
-                  wide_fits<5>() && wide_fits<6>() && wide_fits<7>() && wide_fits<8>(),
+// 4-bit weights: up to 6 token blocks (96 tokens)
+constexpr int kWideMaxMbW4 = 6;
+static_assert(wide_fits<1, 1>() && wide_fits<2, 1>() && wide_fits<3, 1>() && wide_fits<4, 1>() &&
+                  wide_fits<5, 1>() && wide_fits<6, 1>() && wide_fits<7, 1>() &&
+                  wide_fits<8, 1>() && wide_fits<1, 2>() && wide_fits<2, 2>() &&
+                  wide_fits<3, 2>() && wide_fits<4, 2>() && wide_fits<5, 2>() && wide_fits<6, 2>(),
               "LDS budget, and in-flight loads within the 6-bit vmcnt");
 
 // LDS synchronisation words (int indices into the SYNC area)
@@ -212,19 +223,24 @@ __host__ __device__ inline int range_start(int b, int U, int G) {
 
 // ---------------------------------------------------------------------------
 // Streamer role: weights and codes -> MFMA -> per-tile partial rounds.
+// WB = 8: a weight block is one 64-wide K chunk of a tile (the INT8 layout);
+// WB = 4: it is the pair of chunks 2c, 2c + 1 of the 4-bit layout, so an item
+// spans 512 K positions and each block meets the codes of two chunks (F = 2).
 // ---------------------------------------------------------------------------
-template <int MB, int TG>
+template <int MB, int TG, int WB>
 __device__ __forceinline__ void wide_streamer(const int8_t* __restrict__ wq,
                                               const int8_t* __restrict__ qx, int M, int K,
                                               int tiles, int nch, int P, int i0, int n, int w,
                                               int lane, bool quantizer, char* slots,
                                               int32_t* red, int* sync, const WaitCtl& wc) {
-  using C = Wide<MB, TG>;
+  constexpr int F = WB == 4 ? 2 : 1;
+  using C = Wide<MB, TG, F>;
   constexpr int NB = C::NBUF;
   const int voff = lane * 16;
+  const int nwc = WB == 4 ? K >> 7 : nch;  // weight blocks per tile
 
-  // Weights of the next item into register buffer bb: chunk (item * 4 + w) of
-  // the group's 4 tiles, 1 KB each, zeros past the range, N or K.
+  // Weights of the next item into register buffer bb: block (item * 4 + w) of
+  // the group's tiles, 1 KB each, zeros past the range, N or K.
   v4i a[NB][TG];
   int ig = i0 / P, ip = i0 - (i0 / P) * P, wissued = 0;
   auto issue_weights = [&](int bb) {
@@ -233,9 +249,9 @@ __device__ __forceinline__ void wide_streamer(const int8_t* __restrict__ wq,
 #pragma unroll
     for (int tt = 0; tt < TG; ++tt) {
       const int t = ig * TG + tt;
-      const bool ok = live && t < tiles && c < nch;
+      const bool ok = live && t < tiles && c < nwc;
       const buffer_rsrc rs =
-          make_rsrc(wq + ((size_t)(ok ? t : 0) * nch + (ok ? c : 0)) * 1024, ok ? 1024u : 0u);
+          make_rsrc(wq + ((size_t)(ok ? t : 0) * nwc + (ok ? c : 0)) * 1024, ok ? 1024u : 0u);
       a[bb][tt] = load16<kNonTemporal>(rs, voff);
     }
     ++wissued;
@@ -244,23 +260,25 @@ __device__ __forceinline__ void wide_streamer(const int8_t* __restrict__ wq,
       ++ig;
     }
   };
-  // Codes of the next item into this streamer's LDS slot bb: fragment tb holds
-  // token block tb at K chunk (item * 4 + w), one contiguous 1 KB of the
-  // fragment-major codes, which the direct-to-LDS load stores in lane order.
-  // Token rows >= M hold whatever the workspace held: they only reach output
-  // rows that are never stored.  A chunk past K meets zero weights.
+  // Codes of the next item into this streamer's LDS slot bb: fragment (f, tb)
+  // holds token block tb at K chunk F (item * 4 + w) + f, one contiguous 1 KB
+  // of the fragment-major codes, which the direct-to-LDS load stores in lane
+  // order.  Token rows >= M hold whatever the workspace held: they only reach
+  // output rows that are never stored.  A chunk past K meets zero weights.
   const buffer_rsrc qrs = make_rsrc(qx, (uint32_t)MB * (uint32_t)nch * 1024u);
   const int lane_off = lane * 16;
-  char* my_slots = slots + w * NB * MB * 1024;
+  char* my_slots = slots + w * NB * F * MB * 1024;
   int cp_issue = i0 - (i0 / P) * P, cissued = 0;
   auto issue_codes = [&](int bb) {
     const bool live = cissued < n;
     const int c = cp_issue * kS + w;
 #pragma unroll
-    for (int tb = 0; tb < MB; ++tb)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          qrs, (__attribute__((address_space(3))) void*)(my_slots + (bb * MB + tb) * 1024), 16,
-          live ? lane_off + (tb * nch + c) * 1024 : kOutOfRange, 0, 0, kCoherent);
+    for (int f = 0; f < F; ++f)
+#pragma unroll
+      for (int tb = 0; tb < MB; ++tb)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            qrs, (__attribute__((address_space(3))) void*)(my_slots + ((bb * F + f) * MB + tb) * 1024),
+            16, live ? lane_off + (tb * nch + F * c + f) * 1024 : kOutOfRange, 0, 0, kCoherent);
     ++cissued;
     if (++cp_issue == P) cp_issue = 0;
   };
@@ -299,30 +317,46 @@ __device__ __forceinline__ void wide_streamer(const int8_t* __restrict__ wq,
       if (j < n) {
         // Item j's weights and codes have landed once at most the loads issued
         // after its codes are outstanding (loads complete in issue order):
-        // (NB - 1) MB code loads of later items, plus the weights of the items
-        // issued since -- (NB - 1) MB + min(j, NB - 1) TG in all.
+        // (NB - 1) F MB code loads of later items, plus the weights of the
+        // items issued since -- (NB - 1) F MB + min(j, NB - 1) TG in all.
         switch (j < NB - 1 ? j : NB - 1) {
-          case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * MB)); break;
-          case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * MB + 1 * TG)); break;
-          case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * MB + 2 * TG)); break;
-          case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * MB + 3 * TG)); break;
-          case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * MB + 4 * TG)); break;
-          case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * MB + 5 * TG)); break;
-          case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * MB + 6 * TG)); break;
-          default: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * MB + 7 * TG)); break;
+          case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * F * MB)); break;
+          case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * F * MB + 1 * TG)); break;
+          case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * F * MB + 2 * TG)); break;
+          case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * F * MB + 3 * TG)); break;
+          case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * F * MB + 4 * TG)); break;
+          case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * F * MB + 5 * TG)); break;
+          case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * F * MB + 6 * TG)); break;
+          default: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * F * MB + 7 * TG)); break;
         }
-        v4i bf[MB];
+        v4i bf[F * MB];
 #pragma unroll
-        for (int tb = 0; tb < MB; ++tb)
-          bf[tb] = lds_read16_asm(slot_addr + (bb * MB + tb) * 1024);
+        for (int i = 0; i < F * MB; ++i)
+          bf[i] = lds_read16_asm(slot_addr + (bb * F * MB + i) * 1024);
         lds_wait_reads();
 #pragma unroll
-        for (int tb = 0; tb < MB; ++tb) asm volatile("" : "+v"(bf[tb]));
+        for (int i = 0; i < F * MB; ++i) asm volatile("" : "+v"(bf[i]));
 #pragma unroll
-        for (int tt = 0; tt < TG; ++tt)
+        for (int tt = 0; tt < TG; ++tt) {
+          if constexpr (WB == 4) {
+            // each byte's low nibble is chunk 2c's code, its high nibble chunk
+            // 2c + 1's: both times 16 as exact int8 values (the epilogue
+            // divides the sums by 16)
+            const v4u v = __builtin_bit_cast(v4u, a[bb][tt]);
+            const v4u hm = {0xF0F0F0F0u, 0xF0F0F0F0u, 0xF0F0F0F0u, 0xF0F0F0F0u};
+            const v4i lo = __builtin_bit_cast(v4i, (v << 4u) & hm);
+            const v4i hi = __builtin_bit_cast(v4i, v & hm);
 #pragma unroll
-          for (int tb = 0; tb < MB; ++tb)
-            acc[tt][tb] = mfma_i8_16x16x64(a[bb][tt], bf[tb], acc[tt][tb]);
+            for (int tb = 0; tb < MB; ++tb) {
+              acc[tt][tb] = mfma_i8_16x16x64(lo, bf[tb], acc[tt][tb]);
+              acc[tt][tb] = mfma_i8_16x16x64(hi, bf[MB + tb], acc[tt][tb]);
+            }
+          } else {
+#pragma unroll
+            for (int tb = 0; tb < MB; ++tb)
+              acc[tt][tb] = mfma_i8_16x16x64(a[bb][tt], bf[tb], acc[tt][tb]);
+          }
+        }
       }
       // item j + NB into buffer bb and slot bb (slot bb's codes are in
       // registers now), or zeros past the range
@@ -519,7 +553,7 @@ __device__ __forceinline__ bool wide_rows_and_gate(const uint16_t* __restrict__ 
 // while the streamers are still on it, and the partial sums of the workgroups
 // that own the rest of a finalized group are summed once, before its rounds.
 // ---------------------------------------------------------------------------
-template <int MB, int TG>
+template <int MB, int TG, int WB>
 __device__ __forceinline__ void wide_epilogue(const float* __restrict__ wscale,
                                               const float* __restrict__ sx, int M, int N, int P,
                                               int U, int G, int b, int i0, int n, uint32_t e,
@@ -601,7 +635,9 @@ __device__ __forceinline__ void wide_epilogue(const float* __restrict__ wscale,
           } else {
             const int tok = tb * 16 + (ln & 15);
             if (tok < M && n0 < N) {
-              const int tv[4] = {tot.x, tot.y, tot.z, tot.w};
+              // 4-bit weights: the sums are 16 times the products (exact shift)
+              constexpr int sh = WB == 4 ? 4 : 0;
+              const int tv[4] = {tot.x >> sh, tot.y >> sh, tot.z >> sh, tot.w >> sh};
               uint32_t o[4];
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
@@ -645,16 +681,17 @@ __device__ __forceinline__ void wide_epilogue(const float* __restrict__ wscale,
 
 // ---------------------------------------------------------------------------
 // The kernel: 4 streamer wavefronts, then 4 helper wavefronts (they quantize
-// the workgroup's token row, then run the epilogue).
+// the workgroup's token row, then run the epilogue).  One body for INT8 (WB =
+// 8) and 4-bit (WB = 4) weights, launched as two kernels.
 // ---------------------------------------------------------------------------
-template <int MB, int TG>
-__global__ __launch_bounds__(kThreads) void w8a8_linear_wide_kernel(
+template <int MB, int TG, int WB>
+__device__ __forceinline__ void wide_body(
     const uint16_t* __restrict__ x, const float* __restrict__ s, const int8_t* __restrict__ wq,
     const float* __restrict__ wscale, int M, int N, int K, int tiles, int P, int U,
     int8_t* __restrict__ qx, float* __restrict__ sx, int32_t* __restrict__ partials,
     uint32_t* __restrict__ flags, uint16_t* __restrict__ y, int32_t* __restrict__ acc_out,
     WaitCtl wc) {
-  using C = Wide<MB, TG>;
+  using C = Wide<MB, TG, WB == 4 ? 2 : 1>;
   extern __shared__ __align__(16) char smem[];
   char* slots = smem;
   int32_t* red = reinterpret_cast<int32_t*>(smem + C::SLOTS);
@@ -669,8 +706,8 @@ __global__ __launch_bounds__(kThreads) void w8a8_linear_wide_kernel(
   if (tid < kSyncWords) sync[tid] = 0;  // ordered before use by barrier (1)
 
   if (wave < kS) {
-    wide_streamer<MB, TG>(wq, qx, M, K, tiles, nch, P, i0, n, wave, lane, b < M, slots, red,
-                          sync, wc);
+    wide_streamer<MB, TG, WB>(wq, qx, M, K, tiles, nch, P, i0, n, wave, lane, b < M, slots, red,
+                              sync, wc);
     return;
   }
 
@@ -679,48 +716,82 @@ __global__ __launch_bounds__(kThreads) void w8a8_linear_wide_kernel(
   uint32_t e;
   if (!wide_rows_and_gate(x, s, M, K, b, n, ht, wave - kS, lane, qx, sx, flags, sync, e, wc))
     return;
-  wide_epilogue<MB, TG>(wscale, sx, M, N, P, U, G, b, i0, n, e, ht, lane, red, sync, partials,
-                        flags, y, acc_out, wc);
+  wide_epilogue<MB, TG, WB>(wscale, sx, M, N, P, U, G, b, i0, n, e, ht, lane, red, sync,
+                            partials, flags, y, acc_out, wc);
+}
+
+#define QUASAR_WIDE_PARAMS                                                                   \
+  const uint16_t *__restrict__ x, const float *__restrict__ s, const int8_t *__restrict__ wq, \
+      const float *__restrict__ wscale, int M, int N, int K, int tiles, int P, int U,       \
+      int8_t *__restrict__ qx, float *__restrict__ sx, int32_t *__restrict__ partials,     \
+      uint32_t *__restrict__ flags, uint16_t *__restrict__ y, int32_t *__restrict__ acc_out, \
+      WaitCtl wc
+#define QUASAR_WIDE_ARGS x, s, wq, wscale, M, N, K, tiles, P, U, qx, sx, partials, flags, y, acc_out, wc
+
+template <int MB, int TG>
+__global__ __launch_bounds__(kThreads) void w8a8_linear_wide_kernel(QUASAR_WIDE_PARAMS) {
+  wide_body<MB, TG, 8>(QUASAR_WIDE_ARGS);
 }
 
 template <int MB, int TG>
+__global__ __launch_bounds__(kThreads) void w4a8_linear_wide_kernel(QUASAR_WIDE_PARAMS) {
+  wide_body<MB, TG, 4>(QUASAR_WIDE_ARGS);
+}
+#undef QUASAR_WIDE_PARAMS
+#undef QUASAR_WIDE_ARGS
+
+template <int MB, int TG, int WB>
 hipError_t launch_wide_mb(const WidePlan& p, const uint16_t* x, const float* s, const int8_t* wq,
                           const float* w_scale, uint16_t* y, int32_t* acc_out, int8_t* qx,
                           float* sx, int32_t* partials, uint32_t* flags, const WaitCtl& wc,
                           hipStream_t st) {
-  auto kernel = &w8a8_linear_wide_kernel<MB, TG>;
+  auto kernel = [] {
+    if constexpr (WB == 4)
+      return &w4a8_linear_wide_kernel<MB, TG>;
+    else
+      return &w8a8_linear_wide_kernel<MB, TG>;
+  }();
+  constexpr int lds = Wide<MB, TG, WB == 4 ? 2 : 1>::LDS;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-      Wide<MB, TG>::LDS);
+      reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  kernel<<<dim3(p.grid), dim3(kThreads), Wide<MB, TG>::LDS, st>>>(
-      x, s, wq, w_scale, (int)p.M, (int)p.N, (int)p.K, p.tiles, p.P, p.U, qx, sx, partials, flags,
-      y, acc_out, wc);
+  kernel<<<dim3(p.grid), dim3(kThreads), lds, st>>>(x, s, wq, w_scale, (int)p.M, (int)p.N,
+                                                    (int)p.K, p.tiles, p.P, p.U, qx, sx, partials,
+                                                    flags, y, acc_out, wc);
   return hipGetLastError();
 }
 
-template <int TG>
+template <int TG, int WB>
 hipError_t launch_wide_tg(const WidePlan& p, const uint16_t* x, const float* s, const int8_t* wq,
                           const float* w_scale, uint16_t* y, int32_t* acc_out, int8_t* qx,
                           float* sx, int32_t* partials, uint32_t* flags, const WaitCtl& wc,
                           hipStream_t st) {
+#define QUASAR_WIDE_CASE(B)                                                                  \
+  case B:                                                                                    \
+    if constexpr (WB == 8 || B <= kWideMaxMbW4)                                              \
+      return launch_wide_mb<B, TG, WB>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials,   \
+                                       flags, wc, st);                                       \
+    return hipErrorInvalidValue;
   switch (p.mb) {
-    case 1: return launch_wide_mb<1, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st);
-    case 2: return launch_wide_mb<2, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st);
-    case 3: return launch_wide_mb<3, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st);
-    case 4: return launch_wide_mb<4, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st);
-    case 5: return launch_wide_mb<5, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st);
-    case 6: return launch_wide_mb<6, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st);
-    case 7: return launch_wide_mb<7, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st);
-    case 8: return launch_wide_mb<8, TG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st);
+    QUASAR_WIDE_CASE(1)
+    QUASAR_WIDE_CASE(2)
+    QUASAR_WIDE_CASE(3)
+    QUASAR_WIDE_CASE(4)
+    QUASAR_WIDE_CASE(5)
+    QUASAR_WIDE_CASE(6)
+    QUASAR_WIDE_CASE(7)
+    QUASAR_WIDE_CASE(8)
     default: return hipErrorInvalidValue;
   }
+#undef QUASAR_WIDE_CASE
 }
 
-constexpr int wide_lds_of(int mb, int tg) {
-  return kS * wide_nbuf(mb, tg) * mb * 1024 + 2 * kS * mb * 1024 + 256;
+constexpr int wide_lds_of(int mb, int tg, int wb = 8) {
+  return kS * wide_nbuf(mb, tg, wb == 4 ? 2 : 1) * (wb == 4 ? 2 : 1) * mb * 1024 +
+         2 * kS * mb * 1024 + 256;
 }
-static_assert(wide_lds_of(6, 4) == Wide<6, 4>::LDS && wide_lds_of(3, 1) == Wide<3, 1>::LDS,
+static_assert(wide_lds_of(6, 4) == Wide<6, 4>::LDS && wide_lds_of(3, 1) == Wide<3, 1>::LDS &&
+                  wide_lds_of(6, 2, 4) == Wide<6, 2, 2>::LDS,
               "host LDS size matches the kernel's");
 
 }  // namespace
@@ -751,20 +822,23 @@ int wide_tiles_per_group(int64_t M, int64_t N, int64_t K, int grid) {
   return kMaxTG;
 }
 
-WidePlan plan_wide(int64_t M, int64_t N, int64_t K, int grid) {
+WidePlan plan_wide(int64_t M, int64_t N, int64_t K, int grid, int wbits) {
   WidePlan p{};
   p.M = M;
   p.N = N;
   p.K = K;
+  p.wb = wbits == 4 ? 4 : 8;
   p.mb = (int)((M + 15) / 16);
   p.tg = wide_tiles_per_group(M, N, K, grid);
   p.tiles = (int)((N + 15) / 16);
   p.nch = (int)((K + 63) / 64);
   p.groups = (p.tiles + p.tg - 1) / p.tg;
-  p.P = (p.nch + kS - 1) / kS;  // items of 4 64-wide K chunks
+  // items of 4 weight blocks: 64-wide K chunks (INT8), pairs of them (4-bit)
+  const int nwc = p.wb == 4 ? (int)(K / 128) : p.nch;
+  p.P = (nwc + kS - 1) / kS;
   p.U = p.groups * p.P;
   p.grid = grid;
-  p.lds = wide_lds_of(p.mb, p.tg);
+  p.lds = wide_lds_of(p.mb, p.tg, p.wb);
   size_t off = kFlagHeaderBytes;  // the flag header (quasar_sync.hpp) comes first
   p.off_qx = off;  // fragment-major codes: 1 KB per 16-token block and 64-wide K chunk
   off = align_up(off + (size_t)p.mb * p.nch * 1024, kWsAlign);
@@ -776,22 +850,23 @@ WidePlan plan_wide(int64_t M, int64_t N, int64_t K, int grid) {
   return p;
 }
 
-const char* wide_kernel_name(int mb, int tg) {
-  static const char* const names[3][8] = {
-      {"w8a8_linear_wide_kernel<1, 1>", "w8a8_linear_wide_kernel<2, 1>",
-       "w8a8_linear_wide_kernel<3, 1>", "w8a8_linear_wide_kernel<4, 1>",
-       "w8a8_linear_wide_kernel<5, 1>", "w8a8_linear_wide_kernel<6, 1>",
-       "w8a8_linear_wide_kernel<7, 1>", "w8a8_linear_wide_kernel<8, 1>"},
-      {"w8a8_linear_wide_kernel<1, 2>", "w8a8_linear_wide_kernel<2, 2>",
-       "w8a8_linear_wide_kernel<3, 2>", "w8a8_linear_wide_kernel<4, 2>",
-       "w8a8_linear_wide_kernel<5, 2>", "w8a8_linear_wide_kernel<6, 2>",
-       "w8a8_linear_wide_kernel<7, 2>", "w8a8_linear_wide_kernel<8, 2>"},
-      {"w8a8_linear_wide_kernel<1, 4>", "w8a8_linear_wide_kernel<2, 4>",
-       "w8a8_linear_wide_kernel<3, 4>", "w8a8_linear_wide_kernel<4, 4>",
-       "w8a8_linear_wide_kernel<5, 4>", "w8a8_linear_wide_kernel<6, 4>",
-       "w8a8_linear_wide_kernel<7, 4>", "w8a8_linear_wide_kernel<8, 4>"}};
-  return names[tg == 1 ? 0 : (tg == 2 ? 1 : 2)][(mb < 1 ? 1 : (mb > 8 ? 8 : mb)) - 1];
+const char* wide_kernel_name(int mb, int tg, int wbits) {
+  // "w8a8_linear_wide_kernel<MB, TG>" / "w4a8_linear_wide_kernel<MB, TG>"
+  static const std::vector<std::string> names = [] {
+    std::vector<std::string> v;
+    for (const char* k : {"w8a8_linear_wide_kernel<", "w4a8_linear_wide_kernel<"})
+      for (int t : {1, 2, kMaxTG})
+        for (int b = 1; b <= 8; ++b)
+          v.push_back(std::string(k) + std::to_string(b) + ", " + std::to_string(t) + ">");
+    return v;
+  }();
+  const int wi = wbits == 4 ? 1 : 0;
+  const int ti = tg == 1 ? 0 : (tg == 2 ? 1 : 2);
+  mb = mb < 1 ? 1 : (mb > 8 ? 8 : mb);
+  return names[(wi * 3 + ti) * 8 + mb - 1].c_str();
 }
+
+bool wide_w4_supported(int64_t M) { return (M + 15) / 16 <= kWideMaxMbW4; }
 
 hipError_t launch_wide(const WidePlan& p, const uint16_t* x, const float* s, const int8_t* wq,
                        const float* w_scale, uint16_t* y, int32_t* acc_out, void* workspace,
@@ -803,13 +878,23 @@ hipError_t launch_wide(const WidePlan& p, const uint16_t* x, const float* s, con
   uint32_t* flags = reinterpret_cast<uint32_t*>(ws);
   const WaitCtl wc = wait_ctl_for_current_device();
   if (!wc.status) return hipErrorInvalidSymbol;
+  if (p.wb == 4) {
+    if (p.tg == 1)
+      return launch_wide_tg<1, 4>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st);
+    if (p.tg == 2)
+      return launch_wide_tg<2, 4>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st);
+    if (p.tg == kMaxTG)
+      return launch_wide_tg<kMaxTG, 4>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags,
+                                       wc, st);
+    return hipErrorInvalidValue;
+  }
   if (p.tg == 1)
-    return launch_wide_tg<1>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st);
+    return launch_wide_tg<1, 8>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st);
   if (p.tg == 2)
-    return launch_wide_tg<2>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st);
+    return launch_wide_tg<2, 8>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st);
   if (p.tg == kMaxTG)
-    return launch_wide_tg<kMaxTG>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc,
-                                  st);
+    return launch_wide_tg<kMaxTG, 8>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc,
+                                     st);
   return hipErrorInvalidValue;
 }
 
@@ -853,7 +938,11 @@ int wide_grid_for_current_device() {
     // every instantiation has the same block size; the largest LDS decides
     int lds = 0;
     for (int mb = 1; mb <= 8; ++mb)
-      for (int tg : {1, 2, kMaxTG}) lds = wide_lds_of(mb, tg) > lds ? wide_lds_of(mb, tg) : lds;
+      for (int tg : {1, 2, kMaxTG})
+        for (int wb : {8, 4}) {
+          if (wb == 4 && mb > kWideMaxMbW4) continue;
+          lds = wide_lds_of(mb, tg, wb) > lds ? wide_lds_of(mb, tg, wb) : lds;
+        }
     auto kernel = &w8a8_linear_wide_kernel<6, kMaxTG>;
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess ||
