@@ -19,7 +19,7 @@ Two kinds of run are summarised (the commands are recorded in each summary):
   INT8 MFMA: a check of the scaling), the MFMA busy share of the SIMDs' cycles
   while the GPU was active, and the executed TOP/s at the bench's launch time.
 
-    python -m w8a8_quantized_speculative_amd.profiling stats STATS_CSV BENCH_JSON OUT_MD --command CMD
+    python -m w8a8_quantized_speculative_amd.profiling stats STATS_CSV BENCH_JSON OUT_MD --command CMD [--trace TRACE_CSV]
     python -m w8a8_quantized_speculative_amd.profiling pmc FETCH_CSV WRITE_CSV BENCH_JSON OUT_JSON OUT_MD \\
         --command-fetch CMD --command-write CMD
     python -m w8a8_quantized_speculative_amd.profiling mfma PMC_CSV BENCH_JSON OUT_MD --command CMD
@@ -104,7 +104,39 @@ def _self_command() -> str:
         shlex.quote(a) for a in sys.argv[1:])
 
 
-def summarize_stats(stats_csv: str, bench_json: str, out_md: str, command: str) -> dict:
+def _trace_means(trace_csv: str, names) -> dict:
+    """Per kernel (short name): the mean duration in ns of its dispatches in the
+    launch configuration (grid size, LDS bytes) it was dispatched with most
+    often, with the count of those dispatches and of all its dispatches.  The
+    step's shapes of a kernel share one configuration, while other sections of
+    the bench (the single 1024 x 1024 linear, the tensor-parallel shards) launch
+    the same kernel with other grids or LDS sizes."""
+    want = set(names)
+    groups = defaultdict(lambda: defaultdict(list))
+    with open(trace_csv) as f:
+        rd = csv.DictReader(f)
+        cols = rd.fieldnames or []
+        gcol = next((c for c in cols if c.startswith("Grid_Size") and c.endswith("X")),
+                    next((c for c in cols if c.startswith("Grid_Size")), None))
+        lcol = next((c for c in cols if c in ("LDS_Block_Size", "Group_Segment_Size",
+                                               "LDS_Size")), None)
+        for r in rd:
+            name = _short(r["Kernel_Name"])
+            if name not in want:
+                continue
+            key = (r.get(gcol, ""), r.get(lcol, ""))
+            groups[name][key].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = {}
+    for name, g in groups.items():
+        key, durs = max(g.items(), key=lambda kv: len(kv[1]))
+        out[name] = {"mean_ns": sum(durs) / len(durs), "dispatches": len(durs),
+                     "all_dispatches": sum(len(v) for v in g.values()),
+                     "grid": key[0], "lds": key[1]}
+    return out
+
+
+def summarize_stats(stats_csv: str, bench_json: str, out_md: str, command: str,
+                    trace_csv: str | None = None) -> dict:
     rows = []
     with open(stats_csv) as f:
         for r in csv.DictReader(f):
@@ -116,6 +148,10 @@ def summarize_stats(stats_csv: str, bench_json: str, out_md: str, command: str) 
     kname = roof["kernel"]
     prof = [r for r in rows if r[0] == kname]
     prof_avg_us = prof[0][3] / 1e3 if prof else None
+    others_names = [bench[k]["roofline"]["kernel"] for k in bench if k.startswith("window_m")]
+    if "w4a8_variant" in bench and bench["w4a8_variant"].get("kernels"):
+        others_names.append(bench["w4a8_variant"]["kernels"][0]["kernel"])
+    tm = _trace_means(trace_csv, [kname] + others_names) if trace_csv else {}
     out = ["# rocprofv3 kernel statistics: " + bench["config"]["workload"], "",
            "Profiled command (paths relative to the repository root of the GPU run):", "",
            "```", command, "```", "", "Summary written by:", "", "```", _self_command(), "```", "",
@@ -126,15 +162,23 @@ def summarize_stats(stats_csv: str, bench_json: str, out_md: str, command: str) 
     for name, calls, tot, avg, mn, mx in rows[:20]:
         out.append(f"| `{_cell(name)}` | {calls} | {tot / 1e6:.3f} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | "
                    f"{mx / 1e3:.2f} |")
-    out += ["", "Roofline kernel, mean duration per launch:", "",
+    t = tm.get(kname)
+    out += ["", "Roofline kernel, mean duration per launch:", ""]
+    if t:
+        lds = f", {t['lds']} B of LDS" if t["lds"] not in ("", "0") else ""
+        out.append(f"- rocprofv3, the {t['dispatches']} of its {t['all_dispatches']} dispatches with the "
+                   f"launch grid of the step's shapes ({t['grid']} threads{lds}; the other dispatches "
+                   f"are smaller grids: the single 1024 x 1024 linear and tensor-parallel shards): "
+                   f"{t['mean_ns'] / 1e3:.2f} us")
+    out += [
             f"- rocprofv3 (all launches in the run, graph replays and eager calls): "
             f"{prof_avg_us:.2f} us" if prof_avg_us is not None else "- rocprofv3: kernel not found",
             f"- bench.py, HIP events around back-to-back batches of its launches, same run: "
             f"{roof['launch_avg_us']} us",
             f"- algorithmic bytes per launch: {roof['algorithmic_bytes_per_launch']} "
             f"-> {roof['achieved']} GB/s by the events, "
-            + (f"{roof['algorithmic_bytes_per_launch'] / (prof_avg_us * 1e3):.1f} GB/s by rocprofv3"
-               if prof_avg_us else "n/a"),
+            + (f"{roof['algorithmic_bytes_per_launch'] / ((t['mean_ns'] if t else prof_avg_us * 1e3)):.1f} "
+               f"GB/s by rocprofv3" if prof_avg_us else "n/a"),
             ""]
     others = []
     for key in sorted(k for k in bench if k.startswith("window_m")):
@@ -154,13 +198,16 @@ def summarize_stats(stats_csv: str, bench_json: str, out_md: str, command: str) 
         for what, name, ev_us, alg in others:
             pr = by_name.get(name)
             p_us = pr[3] / 1e3 if pr else None
+            if name in tm:
+                p_us = tm[name]["mean_ns"] / 1e3
             out.append(f"| {what} | `{_cell(name)}` | {p_us:.2f} | {ev_us} | "
                        f"{alg / (p_us * 1e3):.1f} |" if p_us else
                        f"| {what} | `{_cell(name)}` | - | {ev_us} | - |")
         out.append("")
     with open(out_md, "w") as f:
         f.write("\n".join(out))
-    return {"rocprof_avg_us": prof_avg_us, "events_avg_us": roof["launch_avg_us"]}
+    return {"rocprof_avg_us": prof_avg_us, "events_avg_us": roof["launch_avg_us"],
+            "rocprof_step_config_avg_us": (t["mean_ns"] / 1e3) if t else None}
 
 
 def _counter_means(path: str, counter: str) -> dict:
@@ -304,6 +351,7 @@ def main():
     a.add_argument("bench_json")
     a.add_argument("out_md")
     a.add_argument("--command", required=True)
+    a.add_argument("--trace", default=None, help="kernel_trace.csv of the same run")
     b = sub.add_parser("pmc")
     b.add_argument("fetch_csv")
     b.add_argument("write_csv")
@@ -323,7 +371,7 @@ def main():
                                         args.command)))
     elif args.cmd == "stats":
         print(json.dumps(summarize_stats(args.stats_csv, args.bench_json, args.out_md,
-                                         args.command)))
+                                         args.command, args.trace)))
     else:
         print(json.dumps(summarize_pmc(args.fetch_csv, args.write_csv, args.bench_json,
                                        args.out_json, args.out_md, args.command_fetch,
