@@ -1057,7 +1057,7 @@ def copy_calibration():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
     import torch

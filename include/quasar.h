@@ -56,7 +56,7 @@ extern "C" {
 typedef enum quasar_status {
   QUASAR_OK = 0,
   QUASAR_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size or value  */
-  QUASAR_ERR_UNSUPPORTED = 2, /* valid in principle, outside this build's limits */
+  QUASAR_ERR_UNSUPPORTED = 2, /* valid in principle, outside the library's limits */
   QUASAR_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required  */
   QUASAR_ERR_HIP = 4,         /* the HIP runtime rejected a launch           */
   QUASAR_ERR_INCOMPLETE = 5   /* quasar_device_check: a bounded wait gave up */
@@ -68,7 +68,7 @@ typedef enum quasar_status {
 #define QUASAR_WAIT_PARTIALS 4u  /* for other workgroups' INT32 partial sums        */
 #define QUASAR_WAIT_CHAIN 8u     /* for an earlier link of a chained call           */
 
-/* Limits of this build. */
+/* Limits of the library. */
 #define QUASAR_MAX_M 128      /* verify-window rows per linear call            */
 #define QUASAR_MAX_K 65536    /* keeps |acc| <= K*127^2 < 2^31                 */
 #define QUASAR_MAX_DRAFT 63   /* k, drafts per sequence in quasar_verify_accept */

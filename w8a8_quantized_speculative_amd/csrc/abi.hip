@@ -137,7 +137,7 @@ const char* quasar_status_string(quasar_status status) {
   switch (status) {
     case QUASAR_OK: return "QUASAR_OK";
     case QUASAR_ERR_INVALID_ARG: return "QUASAR_ERR_INVALID_ARG: null or misaligned pointer, or bad size/value";
-    case QUASAR_ERR_UNSUPPORTED: return "QUASAR_ERR_UNSUPPORTED: size outside this build's limits";
+    case QUASAR_ERR_UNSUPPORTED: return "QUASAR_ERR_UNSUPPORTED: size outside the library's limits";
     case QUASAR_ERR_WORKSPACE: return "QUASAR_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case QUASAR_ERR_HIP: return "QUASAR_ERR_HIP: the HIP runtime rejected a launch";
     case QUASAR_ERR_INCOMPLETE:
