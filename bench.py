@@ -886,7 +886,8 @@ def read_calibration():
     del src, sink
     torch.cuda.empty_cache()
     return {"kernel": "stream_read_kernel", "bytes": 1 << 30,
-            "read_gbs": round((1 << 30) / (ms * 1e-3) / 1e9, 1), "us": round(ms * 1e3, 2)}
+            "read_gbs": round((1 << 30) / (ms * 1e-3) / 1e9, 1), "us": round(ms * 1e3, 2),
+            "dispatches": reps + 1}
 
 
 def read_twin(stack, reps: int = 5):
@@ -917,7 +918,7 @@ def read_twin(stack, reps: int = 5):
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / reps
     del blk_src, blk_dst
-    return ms, nbytes
+    return ms, nbytes, reps + 1, len(codes)
 
 
 def _cpu_model() -> str:
@@ -1104,7 +1105,7 @@ def main():
     kernels, linears = kernel_groups(stack, per_shape)
     dom = kernels[0]
     achieved = dom["gbs"]
-    twin_ms, twin_bytes = read_twin(stack)
+    twin_ms, twin_bytes, twin_passes, twin_launches = read_twin(stack)
     traffic, traffic_note = read_traffic(args.m, dom["kernel"])
 
     value = stack.bytes_step / (ms * 1e-3) / 1e9
@@ -1188,7 +1189,8 @@ def main():
             "what": "one plain streaming read over each linear's packed weights, one launch "
                     "per linear in the step's order, back to back: the ceiling of a step made "
                     "of one launch per linear",
-            "ms": round(twin_ms, 4), "bytes": twin_bytes,
+            "ms": round(twin_ms, 4), "bytes": twin_bytes, "passes": twin_passes,
+            "launches_per_pass": twin_launches,
             "gbs": round(twin_bytes / (twin_ms * 1e-3) / 1e9, 1),
             "step_over_twin": round(twin_ms / ms, 4),
         },

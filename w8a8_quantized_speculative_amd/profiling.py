@@ -251,6 +251,19 @@ def summarize_pmc(fetch_csv: str, write_csv: str, bench_json: str, out_json: str
             "traffic_over_algorithmic": round(traffic / alg, 4),
             "dispatches_averaged": {"FETCH_SIZE": nf, "WRITE_SIZE": nw},
         }
+    # cross-check of the FETCH scale on a second kernel of known bytes: the
+    # streaming read kernel (the 1 GiB calibration read and the step's
+    # read-only twin, bench.py's read_calibration and read_twin)
+    rc, rt = bench.get("read_calibration", {}), bench.get("read_twin", {})
+    xcheck = None
+    if "stream_read_kernel" in fetch and rc.get("dispatches") and rt.get("passes"):
+        n_disp = rc["dispatches"] + rt["passes"] * rt["launches_per_pass"]
+        expect = (rc["dispatches"] * rc["bytes"] + rt["passes"] * rt["bytes"]) / n_disp
+        got = fetch["stream_read_kernel"][0] * f_scale
+        xcheck = {"kernel": "stream_read_kernel", "dispatches": fetch["stream_read_kernel"][1],
+                  "expected_dispatches": n_disp, "read_bytes_per_dispatch": round(expect),
+                  "scaled_fetch_per_dispatch": round(got),
+                  "ratio": round(got / expect, 4)}
     res = {
         "workload": bench["config"]["workload"],
         "M": bench["config"]["M"],
@@ -260,6 +273,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, bench_json: str, out_json: str
                         "FETCH_SIZE": cf, "WRITE_SIZE": cw,
                         "bytes_per_unit_fetch": round(f_scale, 4),
                         "bytes_per_unit_write": round(w_scale, 4)},
+        "fetch_cross_check": xcheck,
         "commands": [command_fetch, command_write],
         "note": "FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by its reading for a "
                 "plain copy of a known size; mean over every launch of the kernel in the run "
@@ -273,6 +287,12 @@ def summarize_pmc(fetch_csv: str, write_csv: str, bench_json: str, out_json: str
            _self_command(), "```", "",
            f"Calibration: `{COPY_KERNEL}` copies {copy_bytes} bytes; it reads FETCH_SIZE {cf:.1f} "
            f"and WRITE_SIZE {cw:.1f}, i.e. {f_scale:.2f} and {w_scale:.2f} bytes per counter unit.",
+           "",
+           (f"Cross-check of the FETCH scale on `stream_read_kernel` (the 1 GiB calibration read "
+            f"and the step's read-only twin, {xcheck['dispatches']} dispatches, "
+            f"{xcheck['expected_dispatches']} expected): {xcheck['scaled_fetch_per_dispatch']} B "
+            f"fetched per dispatch against {xcheck['read_bytes_per_dispatch']} B read, ratio "
+            f"{xcheck['ratio']}." if xcheck else "No second calibration kernel in this run."),
            "",
            "Linear kernels of the step (mean per launch over the step's mix of shapes):", "",
            "| kernel | dispatches | FETCH bytes/launch | WRITE bytes/launch | traffic | algorithmic | ratio |",
