@@ -70,6 +70,32 @@ def test_forced_wait_expiry_is_reported_and_the_workspace_recovers():
     assert binding.device_check() == (binding.QUASAR_OK, 0)
 
 
+def test_forced_expiry_with_4bit_weights_is_reported_and_the_workspace_recovers():
+    """The wide kernel's 4-bit instantiation follows the same protocol."""
+    binding.device_check()
+    M, N, K = 40, 700, 1024
+    x, w, s = synth.linear_case(M, K, N, (94, 0))
+    wq4, sw4 = binding.quasar_quantize_weights_w4(dev_bf16(w), dev(s))
+    ws = binding.new_workspace(binding.workspace_bytes_w4(M, N, K))
+    xd, sd = dev_bf16(x), dev(s)
+    announce("forced expiry: wide 4-bit 40x700x1024")
+    binding.force_wait_expiry(True)
+    try:
+        binding.quasar_w4a8_linear(xd, sd, wq4, sw4, workspace=ws)
+    finally:
+        binding.force_wait_expiry(False)
+    st, bits = binding.device_check()
+    assert st == binding.QUASAR_ERR_INCOMPLETE and bits & binding.QUASAR_WAIT_ROWS, bits
+    ref = orc.w4a8_linear_rows(x, s, w)
+    for _ in range(2):
+        acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+        y = binding.quasar_w4a8_linear(xd, sd, wq4, sw4, acc_out=acc, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(acc), ref["acc"].astype(np.int32))
+        assert np.array_equal(host_bf16(y), ref["y"])
+    assert binding.device_check() == (binding.QUASAR_OK, 0)
+
+
 def test_workspace_init_resets_a_junk_header():
     """quasar_workspace_init zeroes the flag header with a kernel: a workspace
     whose header holds junk gives exact results after it."""
