@@ -501,15 +501,10 @@ def time_kernels(stack, reps: int, bits: int = 8):
     return per_shape
 
 
-def time_bf16_comparator(stack, warmup: int, steps: int):
-    """Same linear shapes with BF16 weights through torch.matmul (hipBLASLt)."""
+def time_library_step(step, warmup: int, steps: int) -> float:
+    """ms per call of `step` (a sequence of library calls): the faster of a HIP
+    graph of it and plain launches."""
     import torch
-    outs = [torch.empty((stack.M, e["N"]), dtype=torch.bfloat16, device="cuda") for e in stack.linears]
-
-    def step():
-        for e, o in zip(stack.linears, outs):
-            torch.matmul(e["x"], e["w_bf16"].t(), out=o)
-
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -530,7 +525,7 @@ def time_bf16_comparator(stack, warmup: int, steps: int):
     t1.record()
     torch.cuda.synchronize()
     ms_graph = t0.elapsed_time(t1) / steps
-    # plain launches of the same calls, as for the W8A8 step; the faster counts
+    del graph
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -539,10 +534,80 @@ def time_bf16_comparator(stack, warmup: int, steps: int):
         step()
     t1.record()
     torch.cuda.synchronize()
-    ms = min(ms_graph, t0.elapsed_time(t1) / steps)
+    return min(ms_graph, t0.elapsed_time(t1) / steps)
+
+
+def time_bf16_comparator(stack, warmup: int, steps: int):
+    """Same linear shapes with BF16 weights through torch.matmul (hipBLASLt)."""
+    import torch
+    outs = [torch.empty((stack.M, e["N"]), dtype=torch.bfloat16, device="cuda") for e in stack.linears]
+
+    def step():
+        for e, o in zip(stack.linears, outs):
+            torch.matmul(e["x"], e["w_bf16"].t(), out=o)
+
+    ms = time_library_step(step, warmup, steps)
     bf16_bytes = sum(2 * e["N"] * e["K"] + 2 * stack.M * e["K"] + 2 * stack.M * e["N"]
                      for e in stack.linears)
     return ms, bf16_bytes
+
+
+def time_int8_library_comparator(stack, warmup: int, steps: int, ms_w8: float):
+    """The step's linear shapes as the vendor library's bare INT8 GEMM
+    (torch._int_mm, hipBLASLt): INT8 activations [M, K] times row-major INT8
+    weights [N, K] into INT32 outputs.  The activation quantization and the
+    dequantization that the W8A8 kernels fuse are left out, so this is a lower
+    bound for a step built on the library GEMM.  Operands are seeded random
+    codes (only the shapes matter for the time).  The library takes more than
+    16 rows, so a smaller window is padded to 17 rows, as a step built on it
+    would have to be."""
+    import torch
+    M = max(stack.M, 17)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(8_000_017)
+    ops = []
+    per_linear = {}
+    for e in stack.linears:
+        a = torch.randint(-127, 128, (M, e["K"]), dtype=torch.int8, device="cuda", generator=g)
+        w = torch.randint(-127, 128, (e["N"], e["K"]), dtype=torch.int8, device="cuda", generator=g)
+        o = torch.empty((M, e["N"]), dtype=torch.int32, device="cuda")
+        ops.append((a, w, o))
+        per_linear.setdefault(e["name"], (e["N"], e["K"], len(ops) - 1))
+    try:
+        torch._int_mm(ops[0][0], ops[0][1].t(), out=ops[0][2])
+        torch.cuda.synchronize()
+    except RuntimeError as ex:  # the library has no INT8 GEMM for this shape
+        return {"what": "torch._int_mm (hipBLASLt INT8 GEMM)", "unavailable": str(ex)[:200]}
+
+    def step():
+        for a, w, o in ops:
+            torch._int_mm(a, w.t(), out=o)
+
+    ms = time_library_step(step, warmup, steps)
+    nbytes = sum(e["N"] * e["K"] + M * e["K"] + 4 * M * e["N"] for e in stack.linears)
+    # each shape alone: its calls of the step back to back (over the step's own
+    # weights of that shape), timed like the step
+    shapes = []
+    for name, (N, K, _) in per_linear.items():
+        idx = [i for i, e in enumerate(stack.linears) if e["name"] == name]
+
+        def shape_step(idx=idx):
+            for i in idx:
+                torch._int_mm(ops[i][0], ops[i][1].t(), out=ops[i][2])
+
+        us = time_library_step(shape_step, 2, max(4, 64 // len(idx))) * 1e3 / len(idx)
+        shapes.append({"linear": name, "N": N, "K": K, "launch_us": round(us, 2),
+                       "weight_gbs": round(N * K / (us * 1e-6) / 1e9, 1)})
+    del ops
+    torch.cuda.empty_cache()
+    return {"what": "the step's linear shapes as torch._int_mm (hipBLASLt INT8 GEMM, INT32 "
+                    "out), activation quantization and dequantization left out; the faster "
+                    "of a HIP graph and plain launches",
+            "rows": M, "rows_padded": M != stack.M,
+            "ms_per_step": round(ms, 4),
+            "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "w8a8_speedup": round(ms / ms_w8, 3),
+            "linears": shapes}
 
 
 def time_w4_variant(stack, args, ms_w8: float):
@@ -677,6 +742,7 @@ def time_window(W, M: int, args):
         out["bf16_comparator"] = {"ms_per_step": round(bms, 4),
                                   "gbs": round(bbytes / (bms * 1e-3) / 1e9, 1),
                                   "w8a8_speedup": round(bms / ms, 3)}
+        out["int8_library_comparator"] = time_int8_library_comparator(st, args.warmup, args.steps, ms)
         if M <= 96:
             out["w4a8_variant"] = time_w4_variant(st, args, ms)
     del st
@@ -1206,6 +1272,9 @@ def main():
             "gbs": round(bbytes / (bms * 1e-3) / 1e9, 1),
             "w8a8_speedup": round(bms / lin_ms, 3),
         }
+        print("[bench] int8 library comparator", file=sys.stderr, flush=True)
+        out["int8_library_comparator"] = time_int8_library_comparator(stack, args.warmup,
+                                                                      args.steps, ms)
     if not args.no_bf16 and args.m <= 96:
         print("[bench] 4-bit weight variant", file=sys.stderr, flush=True)
         out["w4a8_variant"] = time_w4_variant(stack, args, ms)
