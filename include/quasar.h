@@ -31,8 +31,10 @@
  *     bytes of the workspace.  That header must be all zero before the
  *     workspace's first use (allocate it zero-filled, or call
  *     quasar_workspace_init once); the calls maintain it afterwards and never
- *     need it reset.  A workspace belongs to one device, and to one call at a
- *     time.  The rest of a workspace may hold anything.
+ *     need it reset, whatever shapes and entry points use the workspace in
+ *     turn (each launch advances every flag slot, whatever its grid).  A
+ *     workspace belongs to one device, and to one call at a time.  The rest of
+ *     a workspace may hold anything.
  *   - Argument errors are reported before any launch, as a status code; the
  *     outputs are then untouched.  A launch failure returns QUASAR_ERR_HIP.
  *     Device faults surface at the caller's next synchronisation.
@@ -231,10 +233,12 @@ const char* quasar_w8a8_kernel_name(int64_t M, int64_t N, int64_t K);
  *            May be NULL when that size is 0.
  * Every shape runs as one kernel launch on `stream` (quantize, GEMM and
  * dequant fused).  Windows of M <= 8 tokens with K <= 12288 use a kernel that
- * keeps the codes in on-chip memory.  Other shapes use a kernel whose grid is
- * one workgroup per compute unit, all resident at once: its workgroups hand the
- * quantized token rows and partial sums to each other through the workspace,
- * with flags in its header.  Such calls on different streams with different
+ * keeps the codes in on-chip memory.  Other shapes use a kernel with at most
+ * one workgroup per compute unit, all resident at once (one per group of one
+ * or two 16-channel weight tiles when those groups fit the device and K <=
+ * 8192, else one per compute unit): its workgroups hand the quantized token
+ * rows and partial sums to each other through the workspace, with flags in its
+ * header.  Such calls on different streams with different
  * workspaces may overlap; a wait that gives up because the grid could not be
  * resident is reported by quasar_device_check.  The result does not depend on
  * the previous contents of the workspace beyond its header.

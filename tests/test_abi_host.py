@@ -245,7 +245,7 @@ def test_kernel_name_names_the_launch_plan(L):
     assert name(48, 4096, 12288) == "w8a8_linear_wide_kernel<3, 2>"
     assert name(128, 4096, 12288) == "w8a8_linear_wide_kernel<8, 4>"
     assert name(96, 6144, 4096) == "w8a8_linear_wide_kernel<6, 2>"
-    assert name(48, 6144, 4096) == "w8a8_linear_wide_kernel<3, 1>"
+    assert name(48, 6144, 4096) == "w8a8_linear_wide_kernel<3, 2>"
     assert name(9, 16, 16) == "w8a8_linear_wide_kernel<1, 1>"
     assert name(6, 64, 16384) == "w8a8_linear_wide_kernel<1, 2>"
     assert name(96, 24576, 4096) == "w8a8_linear_wide_kernel<6, 4>"

@@ -96,6 +96,29 @@ def test_forced_expiry_with_4bit_weights_is_reported_and_the_workspace_recovers(
     assert binding.device_check() == (binding.QUASAR_OK, 0)
 
 
+def test_launches_of_different_grids_share_one_workspace():
+    """Wide launches whose grids differ (one workgroup per group of weight
+    tiles where the groups fit: 100, 192 or 32 workgroups here, else one per
+    compute unit), back to back on ONE workspace, a small grid first and a full
+    one after it, in two rounds: each matches the oracle and no wait gives up.
+    A launch advances the flag slots beyond its own grid too, so the next
+    launch with a larger grid finds every slot counting the same launches."""
+    cases = [(96, 1600, 4096), (48, 4096, 4096), (48, 6144, 4096), (16, 500, 4096),
+             (20, 1000, 8208), (48, 3072, 4096), (96, 4096, 4096)]
+    ws = binding.new_workspace(max(binding.workspace_bytes_linear(M, N, K) for M, N, K in cases))
+    data = [case(M, N, K, (17, i)) for i, (M, N, K) in enumerate(cases)]
+    assert binding.device_check() == (0, 0)
+    for rnd in range(2):
+        outs = []
+        for (M, N, K), (x, w, s, wq, sw) in zip(cases, data):
+            announce("protocol_mixed_grids", rnd, M, N, K)
+            outs.append(run(x, s, wq, sw, N, ws))
+        torch.cuda.synchronize()
+        assert binding.device_check() == (0, 0), f"a wait gave up in round {rnd}"
+        for (x, w, s, wq, sw), (y, acc) in zip(data, outs):
+            assert exact(x, s, w, y, acc)
+
+
 def test_workspace_init_resets_a_junk_header():
     """quasar_workspace_init zeroes the flag header with a kernel: a workspace
     whose header holds junk gives exact results after it."""

@@ -261,7 +261,7 @@ quasar_status quasar_w8a8_linear(const uint16_t* x, const float* s, const int8_t
   WidePlan p = plan_wide(M, N, K, kWideMaxGrid);
   if (!workspace || workspace_bytes < p.bytes || !aligned(workspace, kWsAlign))
     return QUASAR_ERR_WORKSPACE;
-  p.grid = wide_grid_for_current_device();
+  p.grid = wide_launch_grid(p);
   if (p.grid < M) return QUASAR_ERR_UNSUPPORTED;  // one resident workgroup per token row
   return hip_status(launch_wide(p, x, s, wq, w_scale, y, acc_out, workspace, hs));
 }
@@ -285,7 +285,7 @@ quasar_status quasar_w8a8_linear_noalloc(const uint16_t* x, const float* s, cons
   if (p.bytes > kNoAllocScratchBytes) return QUASAR_ERR_UNSUPPORTED;
   void* scratch = noalloc_scratch_for_current_device();
   if (!scratch) return QUASAR_ERR_HIP;
-  p.grid = wide_grid_for_current_device();
+  p.grid = wide_launch_grid(p);
   if (p.grid < M) return QUASAR_ERR_UNSUPPORTED;
   return hip_status(launch_wide(p, x, s, wq, w_scale, y, acc_out, scratch, hs));
 }
@@ -322,7 +322,7 @@ quasar_status quasar_w8a8_linear_swiglu(const uint16_t* x, const float* s, const
   if (!workspace || workspace_bytes < lin + align_up((size_t)M * N * 2, kWsAlign) ||
       !aligned(workspace, kWsAlign))
     return QUASAR_ERR_WORKSPACE;
-  p.grid = wide_grid_for_current_device();
+  p.grid = wide_launch_grid(p);
   if (p.grid < M) return QUASAR_ERR_UNSUPPORTED;
   uint16_t* gu = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + lin);
   hipError_t e = launch_wide(p, x, s, wq, w_scale, gu, nullptr, workspace, hs);
@@ -411,7 +411,7 @@ quasar_status quasar_w4a8_linear(const uint16_t* x, const float* s, const int8_t
   WidePlan p = plan_wide(M, N, K, kWideMaxGrid, 4);
   if (!workspace || workspace_bytes < p.bytes || !aligned(workspace, kWsAlign))
     return QUASAR_ERR_WORKSPACE;
-  p.grid = wide_grid_for_current_device();
+  p.grid = wide_launch_grid(p);
   if (p.grid < M) return QUASAR_ERR_UNSUPPORTED;  // one resident workgroup per token row
   return hip_status(launch_wide(p, x, s, wq4, w_scale, y, acc_out, workspace, hs));
 }

@@ -101,6 +101,8 @@ bool wide_w4_supported(int64_t M);
 int wide_tiles_per_group(int64_t M, int64_t N, int64_t K, int grid);
 // Workgroups of a wide launch on the current device (0: cannot run there).
 int wide_grid_for_current_device();
+// The grid a wide plan launches with on the current device (0 if none fits).
+int wide_launch_grid(const WidePlan& p);
 // quasar_w8a8_linear_noalloc: the wide kernel's workspace in library device
 // memory (one array per device); its address on the current device, or null.
 constexpr size_t kNoAllocScratchBytes = (size_t)12 << 20;

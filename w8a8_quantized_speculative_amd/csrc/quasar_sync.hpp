@@ -23,6 +23,8 @@
 // belongs to one workgroup and only grows: a launch reads its own word first
 // and every target is relative to that value, so the words need to be equal
 // (e.g. all zero) when the workspace is first used and never need a reset.
+// A launch with fewer workgroups than slots advances the slots beyond its grid
+// too, so the words stay equal across launches of different grids.
 //
 // Every wait is bounded.  A wait that gives up sets a bit of the device status
 // word and the kernel continues (with undefined outputs for that call) instead

@@ -484,7 +484,7 @@ __device__ __forceinline__ void quantize_row_compute(const uint16_t* __restrict_
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bool wide_rows_and_gate(const uint16_t* __restrict__ x,
                                                    const float* __restrict__ s, int M, int K, int b,
-                                                   int n, int ht, int hw, int lane,
+                                                   int G, int n, int ht, int hw, int lane,
                                                    int8_t* __restrict__ qx, float* __restrict__ sx,
                                                    uint32_t* flags, int* sync, uint32_t& e,
                                                    const WaitCtl& wc) {
@@ -520,6 +520,10 @@ __device__ __forceinline__ bool wide_rows_and_gate(const uint16_t* __restrict__ 
     store_flag(flag_word(flags, 0, b), e + 1u);
     asm volatile("" ::: "memory");
     lds_add(sync + kFlagOut, 1);  // the flag is queued ahead of the weight stream
+    // The slots beyond this launch's grid advance too (no launch reads them
+    // before it ends), so that every slot's word keeps counting the launches
+    // on this workspace whatever grid each of them had.
+    for (int sl = b + G; sl < kFlagSlots; sl += G) store_flag(flag_word(flags, 0, sl), e + 1u);
   }
   if (n == 0) return false;
 
@@ -714,7 +718,7 @@ __device__ __forceinline__ void wide_body(
   // ---- helpers
   const int ht = tid - 64 * kS;
   uint32_t e;
-  if (!wide_rows_and_gate(x, s, M, K, b, n, ht, wave - kS, lane, qx, sx, flags, sync, e, wc))
+  if (!wide_rows_and_gate(x, s, M, K, b, G, n, ht, wave - kS, lane, qx, sx, flags, sync, e, wc))
     return;
   wide_epilogue<MB, TG, WB>(wscale, sx, M, N, P, U, G, b, i0, n, e, ht, lane, red, sync,
                             partials, flags, y, acc_out, wc);
@@ -800,24 +804,29 @@ static_assert(wide_lds_of(6, 4) == Wide<6, 4>::LDS && wide_lds_of(3, 1) == Wide<
 // serve 4 tiles (a quarter of the code bytes per weight byte), but leave a
 // linear with few tiles with fewer groups than workgroups, so that a group's
 // K range is split across several workgroups that must hand INT32 partial
-// sums to each other at the end of the launch.  With groups of one tile each
-// workgroup instead reads the whole code matrix per tile, at the L2 read rate
-// of contiguous 1 KB fragments.  Measured on MI355X (16 to 128 tokens): one-tile
-// groups are faster up to 2 tiles per workgroup (QKV, O, down) while the code
-// matrix is at most 96 x 12288; groups of 4 are faster beyond (gate_up, the LM
-// head; down at 128 tokens).  Sharing each fragment among 16 tiles through LDS
-// no longer paid once fragments were contiguous: 164 against 163 us on the
-// 4096 -> 151936 LM head at 96 tokens, 206 against 183 at 128.
+// sums to each other at the end of the launch.  With groups of one or two
+// tiles each workgroup instead reads the whole code matrix per group, at the
+// L2 read rate of contiguous 1 KB fragments.  Measured on MI355X (16 to 128
+// tokens):
+//   * up to 2 tiles per CU and K <= 8192 (QKV, O): the smallest group that
+//     gives at most one group per CU, launched one group per workgroup
+//     (wide_launch_grid), so that no K range is split: 4096 -> 6144 at 48 and
+//     96 tokens 14.2 -> 13.2 and 17.5 -> 16.5 us, 4096 -> 3072 at 48 tokens
+//     12.1 -> 11.2 us, 4096 -> 8192 at 48 tokens 16.4 -> 13.7 us, against
+//     single tiles on every CU;
+//   * K > 8192 (down): pairs of tiles on every CU, each K range split in two
+//     (down at 48 and 96 tokens: 20.0 and 26.0 us against 21.3 and 29.5 for
+//     single tiles and 24.7 and 33.1 for one pair per workgroup);
+//   * beyond (gate_up, the LM head; down at 128 tokens): groups of 4 on every CU.
+// Sharing each fragment among 16 tiles through LDS no longer paid once
+// fragments were contiguous: 164 against 163 us on the 4096 -> 151936 LM head
+// at 96 tokens, 206 against 183 at 128.
 int wide_tiles_per_group(int64_t M, int64_t N, int64_t K, int grid) {
   const int64_t tiles = (N + 15) / 16;
   const int64_t g = grid > 0 ? grid : kWideMaxGrid;
   if (tiles <= 2 * g && M * K <= 96 * 12288) {
-    // pairs of tiles halve the fragment loads per weight byte; measured faster
-    // for K > 8192 (down at 48 and 96 tokens: 22.2 -> 20.2 and 29.7 -> 26.1 us)
-    // and for more tiles than workgroups at more than 64 tokens (QKV at 96:
-    // 18.8 -> 17.5 us), slower otherwise (O at 96: 15.0 -> 15.5 us)
-    if (K > 8192 || (tiles > g && M > 64)) return 2;
-    return 1;
+    if (K > 8192) return 2;
+    return tiles <= g ? 1 : 2;
   }
   return kMaxTG;
 }
@@ -952,6 +961,15 @@ int wide_grid_for_current_device() {
     init[dev] = true;
   }
   return cache[dev];
+}
+
+int wide_launch_grid(const WidePlan& p) {
+  const int dev = wide_grid_for_current_device();
+  // one group per workgroup where the groups of one or two tiles fit the
+  // device's grid and K is not split (wide_tiles_per_group); still one
+  // workgroup per token row
+  if (dev > 0 && p.tg <= 2 && p.K <= 8192 && p.groups <= dev && p.groups >= p.M) return p.groups;
+  return dev;
 }
 
 }  // namespace quasar
