@@ -807,27 +807,34 @@ static_assert(wide_lds_of(6, 4) == Wide<6, 4>::LDS && wide_lds_of(3, 1) == Wide<
 // sums to each other at the end of the launch.  With groups of one or two
 // tiles each workgroup instead reads the whole code matrix per group, at the
 // L2 read rate of contiguous 1 KB fragments.  Measured on MI355X (16 to 128
-// tokens):
-//   * up to 2 tiles per CU and K <= 8192 (QKV, O): the smallest group that
-//     gives at most one group per CU, launched one group per workgroup
-//     (wide_launch_grid), so that no K range is split: 4096 -> 6144 at 48 and
-//     96 tokens 14.2 -> 13.2 and 17.5 -> 16.5 us, 4096 -> 3072 at 48 tokens
-//     12.1 -> 11.2 us, 4096 -> 8192 at 48 tokens 16.4 -> 13.7 us, against
-//     single tiles on every CU;
+// tokens, K = 4096 unless stated; us per launch):
+//   * up to 2 tiles per CU (QKV, O): the smallest group that gives at most one
+//     group per CU, launched one group per workgroup (wide_launch_grid), so no
+//     K range is split: 4096 -> 6144 at 48 and 96 tokens 14.2 -> 13.2 and
+//     17.5 -> 16.5, 4096 -> 8192 at 48 tokens 16.4 -> 13.7, against single
+//     tiles on every CU;
+//   * 2 to 4 tiles per CU: pairs on every CU up to 64 tokens (4096 -> 12288 at
+//     48 tokens 20.8 -> 17.4), beyond that groups of 4, one per workgroup (at
+//     96 tokens 24.5 -> 21.6), against groups of 4 on every CU;
+//   * up to 8 tiles per CU at up to 32 tokens: pairs on every CU (gate_up at
+//     16 tokens 23.3 -> 20.9);
 //   * K > 8192 (down): pairs of tiles on every CU, each K range split in two
-//     (down at 48 and 96 tokens: 20.0 and 26.0 us against 21.3 and 29.5 for
+//     (down at 48 and 96 tokens: 20.0 and 26.0 against 21.3 and 29.5 for
 //     single tiles and 24.7 and 33.1 for one pair per workgroup);
-//   * beyond (gate_up, the LM head; down at 128 tokens): groups of 4 on every CU.
+//   * beyond (gate_up from 48 tokens, the LM head; down at 128 tokens): groups
+//     of 4 on every CU.
 // Sharing each fragment among 16 tiles through LDS no longer paid once
 // fragments were contiguous: 164 against 163 us on the 4096 -> 151936 LM head
 // at 96 tokens, 206 against 183 at 128.
 int wide_tiles_per_group(int64_t M, int64_t N, int64_t K, int grid) {
   const int64_t tiles = (N + 15) / 16;
   const int64_t g = grid > 0 ? grid : kWideMaxGrid;
-  if (tiles <= 2 * g && M * K <= 96 * 12288) {
-    if (K > 8192) return 2;
-    return tiles <= g ? 1 : 2;
-  }
+  if (M * K > 96 * 12288) return kMaxTG;
+  if (K > 8192) return tiles <= 2 * g ? 2 : kMaxTG;
+  if (tiles <= g) return 1;
+  if (tiles <= 2 * g) return 2;
+  if (tiles < 4 * g) return M <= 64 ? 2 : kMaxTG;
+  if (tiles <= 8 * g && M <= 32) return 2;
   return kMaxTG;
 }
 
@@ -965,10 +972,9 @@ int wide_grid_for_current_device() {
 
 int wide_launch_grid(const WidePlan& p) {
   const int dev = wide_grid_for_current_device();
-  // one group per workgroup where the groups of one or two tiles fit the
-  // device's grid and K is not split (wide_tiles_per_group); still one
-  // workgroup per token row
-  if (dev > 0 && p.tg <= 2 && p.K <= 8192 && p.groups <= dev && p.groups >= p.M) return p.groups;
+  // one group per workgroup where the groups fit the device's grid and K is
+  // not split (wide_tiles_per_group); still one workgroup per token row
+  if (dev > 0 && p.K <= 8192 && p.groups <= dev && p.groups >= p.M) return p.groups;
   return dev;
 }
 
