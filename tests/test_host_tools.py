@@ -51,7 +51,18 @@ def test_kernel_source_hash_follows_the_kernel_family():
     a = profiling.kernel_source_hash("w8a8_linear_fused_kernel<6, 4, 2>")
     assert a == profiling.kernel_source_hash("w4a8_linear_fused_kernel<6, 4, 1>")  # same file
     assert a != profiling.kernel_source_hash("w8a8_linear_wide_kernel<3, 1>")
+    assert profiling.kernel_source_hash("w4a8_linear_wide_kernel<3, 1>") == \
+        profiling.kernel_source_hash("w8a8_linear_wide_kernel<6, 4>")  # same file
     assert len(a) == 16
+
+
+def test_kernel_source_hash_ignores_comments_and_layout():
+    a = 'int f(int x) {  // twice\n  return 2 * x; /* doubled */ }\nconst char* s = "a // b";'
+    b = 'int f(int x) {\n    return 2 * x;   }\n// a note\nconst char* s = "a // b";'
+    c = 'int f(int x) { return 3 * x; } const char* s = "a // b";'
+    assert profiling.code_only(a) == profiling.code_only(b)
+    assert profiling.code_only(a) != profiling.code_only(c)
+    assert profiling.code_only('char q = \'"\'; // x') == "char q = '\"';"
 
 
 def _write(path, header, rows):

@@ -22,17 +22,19 @@
 //      fragment K bytes apart (row-major codes).  Every workgroup waits until the M row
 //      flags are set -- a one-way grid barrier.  Meanwhile its streamer
 //      wavefronts already have their first weights in flight.
-//   2. Items.  The output channels are cut into groups of 4 tiles of 16
-//      channels (64 channels) and K into items of 256 positions (4 chunks of
-//      64, one per streamer wavefront).  The (group, item) sequence, group
-//      major, is divided into G equal contiguous ranges, one per workgroup
-//      (stream-K): every workgroup streams the same number of weight bytes
-//      whatever N and K are.
+//   2. Items.  The output channels are cut into groups of TG tiles of 16
+//      channels (TG = 1, 2 or 4: wide_tiles_per_group) and K into items of
+//      256 positions (4 chunks of 64, one per streamer wavefront).  The
+//      (group, item) sequence, group major, is divided into G equal
+//      contiguous ranges, one per workgroup (stream-K): every workgroup
+//      streams the same number of weight bytes whatever N and K are.  G is
+//      the number of groups where they fit the device and K <= 8192 (each
+//      workgroup owns one whole group), else one workgroup per compute unit.
 //   3. Per item, each of the 4 streamer wavefronts loads one 1 KB chunk of
-//      each of the group's 4 tiles into registers and, right behind them, the
+//      each of the group's TG tiles into registers and, right behind them, the
 //      activation codes of that K chunk -- one 16 x 64 fragment per 16-token
 //      block -- with direct-to-LDS buffer loads into a slot of its own, then
-//      multiplies each fragment against the 4 tiles.  Weights and codes of
+//      multiplies each fragment against the TG tiles.  Weights and codes of
 //      NBUF items are in flight per wavefront.  A compute unit holds only a
 //      bounded number of outstanding vector-memory requests and later
 //      requests wait at issue, so codes loaded by a separate wavefront would
@@ -40,7 +42,7 @@
 //      right behind its weights, they land with them and one in-order wait
 //      count covers both.
 //   4. At the end of a group (or of the range) the streamers hand their
-//      partial sums to two epilogue wavefronts, one tile at a time through a
+//      partial sums to the four helper wavefronts, one tile at a time through a
 //      double-buffered LDS area.  The epilogue sums the 4 partials (exact
 //      INT32) and either dequantizes to BF16, or -- for a group whose first
 //      item belongs to another workgroup -- stores the INT32 partial to the
@@ -61,8 +63,10 @@
 // shared group is).  Workgroup b reads its row flag e at the start and raises
 // it to e + 1 once per launch, so a flag equal to e + 1 marks this launch's
 // data; the header must hold equal words (zeros) before the workspace's first
-// use and is never reset.  The grid is one workgroup per compute unit and all
-// of them must be resident at once; every wait is bounded, and one that gives
+// use and is never reset (a launch raises the row-flag words beyond its grid
+// as well, so launches of different grids can share a workspace).  The grid
+// is at most one workgroup per compute unit and all of them must be resident
+// at once; every wait is bounded, and one that gives
 // up sets a bit of the device status word (undefined outputs) instead of
 // hanging.
 #include <mutex>
@@ -77,7 +81,7 @@ namespace quasar {
 namespace {
 
 constexpr int kS = 4;        // streamer wavefronts (one 64-wide K chunk each per item)
-constexpr int kMaxTG = 4;    // 16-channel tiles per group: 1 or 4
+constexpr int kMaxTG = 4;    // 16-channel tiles per group: 1, 2 or 4
 constexpr int kHelpers = 4;  // row quantizer, then epilogue wavefronts
 constexpr int kThreads = 64 * (kS + kHelpers);
 constexpr int kRowPieces = 8;  // 8-element pieces per helper thread kept in registers

@@ -42,6 +42,7 @@ _FAMILY_SOURCES = (
     ("w8a8_linear_fused_kernel", "fused.hip"),
     ("w4a8_linear_fused_kernel", "fused.hip"),
     ("w8a8_linear_wide_kernel", "wide.hip"),
+    ("w4a8_linear_wide_kernel", "wide.hip"),
     ("w8a8_chain_kernel", "chain.hip"),
     ("accept_", "accept.hip"),
 )
@@ -49,15 +50,40 @@ _SHARED_HEADERS = ("quasar_device.hpp", "quasar_internal.hpp", "quasar_sync.hpp"
 COPY_KERNEL = "stream_copy_kernel"
 
 
+def code_only(text: str) -> str:
+    """C++ source text without its comments, whitespace runs collapsed to one
+    space (string and character literals kept as written)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash(kernel: str = "w8a8_linear_fused_kernel") -> str:
-    """Hash of the sources a kernel is built from (its family's file and the
-    shared device headers): a recorded counter reading stays valid while this
-    hash is unchanged."""
+    """Hash of the code a kernel is built from (its family's file and the
+    shared device headers, comments and layout left out): a recorded counter
+    reading stays valid while this hash is unchanged."""
     files = [f for prefix, f in _FAMILY_SOURCES if kernel.startswith(prefix)][:1]
     h = hashlib.sha256()
     for name in files + list(_SHARED_HEADERS):
-        with open(os.path.join(PKG, "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(PKG, "csrc", name), encoding="utf-8") as f:
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
