@@ -236,9 +236,10 @@ def test_kernel_name_names_the_launch_plan(L):
     assert name(1, 16, 16) == "w8a8_linear_fused_kernel<2, 4, 2>"
     assert name(8, 4096, 8192) == "w8a8_linear_fused_kernel<8, 4, 4>"
     # wider windows (or K > 12288): one launch over ceil(M / 16) token blocks
-    # <token blocks, tiles per group>: up to 512 tiles while the code matrix is
-    # at most 96 x 12288 bytes, one tile per group, or two for K > 8192 or for
-    # more tiles than workgroups above 64 tokens; groups of 4 tiles otherwise
+    # <token blocks, tiles per group>, while the code matrix is at most
+    # 96 x 12288 bytes: K > 8192 pairs up to 512 tiles; otherwise one tile up to
+    # 256 tiles, pairs up to 512, pairs below 1024 tiles up to 64 tokens, pairs
+    # up to 2048 tiles up to 32 tokens; groups of 4 tiles beyond
     assert name(48, 4096, 4096) == "w8a8_linear_wide_kernel<3, 1>"
     assert name(96, 4096, 4096) == "w8a8_linear_wide_kernel<6, 1>"
     assert name(96, 4096, 12288) == "w8a8_linear_wide_kernel<6, 2>"
@@ -252,6 +253,13 @@ def test_kernel_name_names_the_launch_plan(L):
     assert name(48, 151936, 4096) == "w8a8_linear_wide_kernel<3, 4>"
     assert name(96, 151936, 4096) == "w8a8_linear_wide_kernel<6, 4>"
     assert name(128, 151936, 4096) == "w8a8_linear_wide_kernel<8, 4>"
+    assert name(48, 12288, 4096) == "w8a8_linear_wide_kernel<3, 2>"     # 768 tiles, <= 64 tokens
+    assert name(96, 12288, 4096) == "w8a8_linear_wide_kernel<6, 4>"     # 768 tiles, > 64 tokens
+    assert name(64, 16384, 4096) == "w8a8_linear_wide_kernel<4, 4>"     # 1024 tiles
+    assert name(32, 16384, 4096) == "w8a8_linear_wide_kernel<2, 2>"     # <= 2048 tiles, <= 32 tokens
+    assert name(16, 24576, 4096) == "w8a8_linear_wide_kernel<1, 2>"
+    assert name(48, 24576, 4096) == "w8a8_linear_wide_kernel<3, 4>"
+    assert name(16, 49152, 4096) == "w8a8_linear_wide_kernel<1, 4>"     # 3072 tiles
     # invalid or unsupported sizes
     assert name(0, 16, 16) == "" and name(6, 16, 17) == "" and name(129, 16, 16) == ""
 
