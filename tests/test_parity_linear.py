@@ -89,6 +89,12 @@ RAGGED = [
     # count, ragged N and K (odd chunk counts), groups split across workgroups
     (9, 65600, 320), (20, 66000, 208), (48, 70000, 208), (33, 66000, 96), (64, 65540, 576),
     (70, 65600, 1040), (96, 65600, 64), (100, 65536, 192), (128, 66000, 320),
+    # token blocks split over two workgroups of one XCD (one pair of tiles per
+    # range): 2 + 2, 3 + 3 (a ragged last block) and 4 + 4 blocks, ragged N,
+    # 32 to 128 pairs, K up to 8192; 256 tiles at K > 8192; more codes than
+    # 96 x 12288
+    (64, 2048, 4096), (90, 4090, 4096), (128, 2040, 4096), (64, 3072, 8192), (96, 1530, 2112),
+    (96, 4096, 12288), (128, 2048, 12288), (128, 2048, 16384),
 ]
 
 

@@ -56,6 +56,9 @@ SHAPES = [
     (80, 300, 4096), (96, 77, 3072), (96, 520, 12288), (40, 8000, 512), (24, 6144, 4096),
     (96, 6152, 4096), (72, 4104, 2048), (6, 64, 16384), (50, 48, 20480), (20, 16400, 384),
     (96, 16384, 1024), (9, 16390, 4224), (17, 500, 65536),
+    # token blocks split over two workgroups (3 + 3 blocks with a ragged last
+    # one, 2 + 2), ragged N, K past 8192 with 256 tiles
+    (90, 4090, 4096), (64, 3072, 8192), (96, 4096, 12288),
 ]
 
 

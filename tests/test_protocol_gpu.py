@@ -98,13 +98,14 @@ def test_forced_expiry_with_4bit_weights_is_reported_and_the_workspace_recovers(
 
 def test_launches_of_different_grids_share_one_workspace():
     """Wide launches whose grids differ (one workgroup per group of weight
-    tiles where the groups fit: 100, 192 or 32 workgroups here, else one per
-    compute unit), back to back on ONE workspace, a small grid first and a full
+    tiles where the groups fit: 100, 192 or 32 workgroups here; two per pair
+    of tiles with the token blocks split: 128 or 256; else one per compute
+    unit), back to back on ONE workspace, a small grid first and a full
     one after it, in two rounds: each matches the oracle and no wait gives up.
     A launch advances the flag slots beyond its own grid too, so the next
     launch with a larger grid finds every slot counting the same launches."""
     cases = [(96, 1600, 4096), (48, 4096, 4096), (48, 6144, 4096), (16, 500, 4096),
-             (20, 1000, 8208), (48, 3072, 4096), (96, 4096, 4096)]
+             (64, 2048, 4096), (20, 1000, 8208), (48, 3072, 4096), (96, 4096, 4096)]
     ws = binding.new_workspace(max(binding.workspace_bytes_linear(M, N, K) for M, N, K in cases))
     data = [case(M, N, K, (17, i)) for i, (M, N, K) in enumerate(cases)]
     assert binding.device_check() == (0, 0)

@@ -225,7 +225,7 @@ const char* quasar_w8a8_kernel_name(int64_t M, int64_t N, int64_t K) {
     return "";
   if (fused_supported(M, K)) return fused_kernel_name(plan_fused(M, N, K));
   const WidePlan p = plan_wide(M, N, K, kWideMaxGrid);
-  return wide_kernel_name(p.mb, p.tg);
+  return wide_kernel_name(p.mbl, p.tg, 8, p.ms == 2);
 }
 
 quasar_status quasar_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
@@ -420,7 +420,7 @@ const char* quasar_w4a8_kernel_name(int64_t M, int64_t N, int64_t K) {
   if (!w4_shape_ok(M, N, K)) return "";
   if (w4_supported(M, K)) return fused_w4_kernel_name(plan_fused(M, N, K));
   const WidePlan p = plan_wide(M, N, K, kWideMaxGrid, 4);
-  return wide_kernel_name(p.mb, p.tg, 4);
+  return wide_kernel_name(p.mbl, p.tg, 4, p.ms == 2);
 }
 
 size_t quasar_lm_head_verify_workspace_bytes(int64_t B, int64_t k, int64_t V, int64_t K) {

@@ -225,17 +225,27 @@ __host__ __device__ inline int range_start(int b, int U, int G) {
   return (int)((int64_t)b * U / G);
 }
 
+// Token-block split: the workgroup that runs range c on half `mpart` of the
+// token blocks.  Workgroup b runs on XCD b % 8, so the two workgroups of a
+// range, b and b + 8, share an XCD and read the range's weights through its L2.
+__host__ __device__ inline int wide_split_wg(int c, int mpart) {
+  return (c & 7) | (mpart << 3) | ((c >> 3) << 4);
+}
+
 // ---------------------------------------------------------------------------
 // Streamer role: weights and codes -> MFMA -> per-tile partial rounds.
 // WB = 8: a weight block is one 64-wide K chunk of a tile (the INT8 layout);
 // WB = 4: it is the pair of chunks 2c, 2c + 1 of the 4-bit layout, so an item
 // spans 512 K positions and each block meets the codes of two chunks (F = 2).
+// SPLIT: the workgroup multiplies token blocks tb0 .. tb0 + MB - 1 of the 2 MB
+// blocks of the code matrix (otherwise blocks 0 .. MB - 1 of MB).
 // ---------------------------------------------------------------------------
-template <int MB, int TG, int WB>
+template <int MB, int TG, int WB, bool SPLIT>
 __device__ __forceinline__ void wide_streamer(const int8_t* __restrict__ wq,
                                               const int8_t* __restrict__ qx, int M, int K,
                                               int tiles, int nch, int P, int i0, int n, int w,
-                                              int lane, bool quantizer, char* slots,
+                                              int lane, bool quantizer, int tb0_split,
+                                              char* slots,
                                               int32_t* red, int* sync, const WaitCtl& wc) {
   constexpr int F = WB == 4 ? 2 : 1;
   using C = Wide<MB, TG, F>;
@@ -265,11 +275,14 @@ __device__ __forceinline__ void wide_streamer(const int8_t* __restrict__ wq,
     }
   };
   // Codes of the next item into this streamer's LDS slot bb: fragment (f, tb)
-  // holds token block tb at K chunk F (item * 4 + w) + f, one contiguous 1 KB
+  // holds token block tb0 + tb (of the MBT blocks of the code matrix) at K
+  // chunk F (item * 4 + w) + f, one contiguous 1 KB
   // of the fragment-major codes, which the direct-to-LDS load stores in lane
   // order.  Token rows >= M hold whatever the workspace held: they only reach
   // output rows that are never stored.  A chunk past K meets zero weights.
-  const buffer_rsrc qrs = make_rsrc(qx, (uint32_t)MB * (uint32_t)nch * 1024u);
+  constexpr int MBT = SPLIT ? 2 * MB : MB;
+  const int tb0 = SPLIT ? tb0_split : 0;
+  const buffer_rsrc qrs = make_rsrc(qx, (uint32_t)MBT * (uint32_t)nch * 1024u);
   const int lane_off = lane * 16;
   char* my_slots = slots + w * NB * F * MB * 1024;
   int cp_issue = i0 - (i0 / P) * P, cissued = 0;
@@ -282,7 +295,8 @@ __device__ __forceinline__ void wide_streamer(const int8_t* __restrict__ wq,
       for (int tb = 0; tb < MB; ++tb)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             qrs, (__attribute__((address_space(3))) void*)(my_slots + ((bb * F + f) * MB + tb) * 1024),
-            16, live ? lane_off + (tb * nch + F * c + f) * 1024 : kOutOfRange, 0, 0, kCoherent);
+            16, live ? lane_off + ((tb0 + tb) * nch + F * c + f) * 1024 : kOutOfRange, 0, 0,
+            kCoherent);
     ++cissued;
     if (++cp_issue == P) cp_issue = 0;
   };
@@ -480,15 +494,17 @@ __device__ __forceinline__ void quantize_row_compute(const uint16_t* __restrict_
 
 // ---------------------------------------------------------------------------
 // Helper prologue: quantize token row b (b < M) into the workspace and raise
-// this workgroup's row flag, then wait until every token row of the launch is
-// there (helper wavefront 0 polls the flags with agent-scope loads, then
-// acquires; the rows are read only after this).  Contains the workgroup
+// this workgroup's row flag, then wait until the token rows [mlo, mhi) this
+// workgroup multiplies are there (helper wavefront 0 polls their flags with
+// agent-scope loads; the rows are read only after this).  Contains the workgroup
 // barrier (1).  Returns false when the workgroup has no items; `e` is this
 // workgroup's row flag before the launch.
 // ---------------------------------------------------------------------------
+template <bool SPLIT>
 __device__ __forceinline__ bool wide_rows_and_gate(const uint16_t* __restrict__ x,
                                                    const float* __restrict__ s, int M, int K, int b,
-                                                   int G, int n, int ht, int hw, int lane,
+                                                   int G, int n, int mlo, int mhi, int ht,
+                                                   int hw, int lane,
                                                    int8_t* __restrict__ qx, float* __restrict__ sx,
                                                    uint32_t* flags, int* sync, uint32_t& e,
                                                    const WaitCtl& wc) {
@@ -536,7 +552,8 @@ __device__ __forceinline__ bool wide_rows_and_gate(const uint16_t* __restrict__ 
     bool ok = false;
     for (int spin = 0;; ++spin) {
       bool ready = true;
-      for (int m = lane; m < M; m += 64) ready &= load_flag(flag_word(flags, 0, m)) == target;
+      for (int m = (SPLIT ? mlo : 0) + lane; m < (SPLIT ? mhi : M); m += 64)
+        ready &= load_flag(flag_word(flags, 0, m)) == target;
       if (__builtin_amdgcn_ballot_w64(!ready) == 0) {
         ok = true;
         break;
@@ -555,16 +572,20 @@ __device__ __forceinline__ bool wide_rows_and_gate(const uint16_t* __restrict__ 
 
 // ---------------------------------------------------------------------------
 // Epilogue role.  Thread et (0..255) owns slots et + 256 k of a tile round:
-// slot s = 64 tb + l is lane l of token block tb, i.e. token 16 tb + l % 16 and
-// the 4 channels 4 (l / 16) .. + 3 of the tile (the MFMA result layout).  No
+// slot s = 64 tb + l is lane l of token block tb, i.e. token 16 (tb0 + tb) +
+// l % 16 and the 4 channels 4 (l / 16) .. + 3 of the tile (the MFMA result
+// layout).  Ranges are numbered r = 0..G-1 (G ranges); range c of this
+// workgroup's half of the token blocks belongs to workgroup wg_of(c), whose
+// number also indexes its partial-sum slot and partial flag.  No
 // global load waits inside a round: the weight scales of a group are fetched
 // while the streamers are still on it, and the partial sums of the workgroups
 // that own the rest of a finalized group are summed once, before its rounds.
 // ---------------------------------------------------------------------------
-template <int MB, int TG, int WB>
+template <int MB, int TG, int WB, bool SPLIT>
 __device__ __forceinline__ void wide_epilogue(const float* __restrict__ wscale,
                                               const float* __restrict__ sx, int M, int N, int P,
-                                              int U, int G, int b, int i0, int n, uint32_t e,
+                                              int U, int G, int r, int bp, int tb0, int i0,
+                                              int n, uint32_t e,
                                               int et, int lane, const int32_t* red, int* sync,
                                               int32_t* __restrict__ partials, uint32_t* flags,
                                               uint16_t* __restrict__ y,
@@ -572,10 +593,13 @@ __device__ __forceinline__ void wide_epilogue(const float* __restrict__ wscale,
   constexpr int KS = (MB + 3) / 4;           // slots per thread and round
   constexpr int kPartInts = kMaxTG * MB * 256;  // one workgroup's partial-sum slot
   const int ln = et & 63;
+  if (!SPLIT) tb0 = 0;
+  const int mpart = (bp >> 3) & 1;
+  auto wg_of = [&](int c) { return SPLIT ? wide_split_wg(c, mpart) : c; };
   float sxv[KS];
 #pragma unroll
   for (int k = 0; k < KS; ++k) {
-    const int tok = ((et >> 6) + 4 * k) * 16 + (ln & 15);
+    const int tok = (tb0 + (et >> 6) + 4 * k) * 16 + (ln & 15);
     sxv[k] = tok < M ? load_coherent(sx + tok) : 0.0f;  // written by workgroup tok
   }
   const buffer_rsrc wrs = make_rsrc(wscale, (uint32_t)N * 4u);
@@ -599,12 +623,13 @@ __device__ __forceinline__ void wide_epilogue(const float* __restrict__ wscale,
 #pragma unroll
       for (int k = 0; k < KS; ++k) other[tt][k] = (v4i){0, 0, 0, 0};
     if (finalizer) {
-      // contributors: the non-empty workgroups after b whose ranges start
-      // inside group g (each wrote its partial sum of g first, then its flag)
-      for (int c = b + 1; c < G && range_start(c, U, G) < (g + 1) * P; ++c) {
+      // contributors: the non-empty ranges after r that start inside group g
+      // (each owner wrote its partial sum of g first, then its flag)
+      for (int c = r + 1; c < G && range_start(c, U, G) < (g + 1) * P; ++c) {
         if (range_start(c + 1, U, G) == range_start(c, U, G)) continue;  // empty range
+        const int cw = wg_of(c);
         for (int spin = 0;; ++spin) {
-          if (load_flag(flag_word(flags, 1, c)) == e + 1u + wc.bias) break;
+          if (load_flag(flag_word(flags, 1, cw)) == e + 1u + wc.bias) break;
           if (spin >= wc.spin_global) {
             if (lane == 0) note_expired(wc, kWaitPartials);
             break;
@@ -613,7 +638,7 @@ __device__ __forceinline__ void wide_epilogue(const float* __restrict__ wscale,
         }
         after_poll();  // the partial sums are read after the flag, agent-scope
         const buffer_rsrc prs =
-            make_rsrc(partials + (size_t)c * kPartInts, (uint32_t)kPartInts * 4u);
+            make_rsrc(partials + (size_t)cw * kPartInts, (uint32_t)kPartInts * 4u);
 #pragma unroll
         for (int tt = 0; tt < TG; ++tt)
 #pragma unroll
@@ -639,9 +664,9 @@ __device__ __forceinline__ void wide_epilogue(const float* __restrict__ wscale,
           for (int w = 0; w < kS; ++w)
             tot += *reinterpret_cast<const v4i*>(red + ((par * kS + w) * MB + tb) * 256 + ln * 4);
           if (writer) {
-            store16_device(partials + (size_t)b * kPartInts + (tt * MB + tb) * 256 + ln * 4, tot);
+            store16_device(partials + (size_t)bp * kPartInts + (tt * MB + tb) * 256 + ln * 4, tot);
           } else {
-            const int tok = tb * 16 + (ln & 15);
+            const int tok = (tb0 + tb) * 16 + (ln & 15);
             if (tok < M && n0 < N) {
               // 4-bit weights: the sums are 16 times the products (exact shift)
               constexpr int sh = WB == 4 ? 4 : 0;
@@ -681,7 +706,7 @@ __device__ __forceinline__ void wide_epilogue(const float* __restrict__ wscale,
       if (lane == 0) lds_add(sync + kPartDone, 1);
       if (et == 0) {
         lds_wait_at_least(sync + kPartDone, kHelpers, wc);
-        store_flag(flag_word(flags, 1, b), e + 1u);
+        store_flag(flag_word(flags, 1, bp), e + 1u);
       }
     }
   }
@@ -692,7 +717,7 @@ __device__ __forceinline__ void wide_epilogue(const float* __restrict__ wscale,
 // the workgroup's token row, then run the epilogue).  One body for INT8 (WB =
 // 8) and 4-bit (WB = 4) weights, launched as two kernels.
 // ---------------------------------------------------------------------------
-template <int MB, int TG, int WB>
+template <int MB, int TG, int WB, bool SPLIT>
 __device__ __forceinline__ void wide_body(
     const uint16_t* __restrict__ x, const float* __restrict__ s, const int8_t* __restrict__ wq,
     const float* __restrict__ wscale, int M, int N, int K, int tiles, int P, int U,
@@ -707,25 +732,33 @@ __device__ __forceinline__ void wide_body(
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int G = gridDim.x, b = blockIdx.x;
-  const int i0 = range_start(b, U, G);
-  const int n = range_start(b + 1, U, G) - i0;
+  const int G0 = gridDim.x, b = blockIdx.x;
+  // With the token-block split, workgroups b and b + 8 (one XCD) take the two
+  // halves (MB blocks each) of the token blocks of range r; otherwise range r
+  // is workgroup r and takes all MB blocks.
+  const int G = SPLIT ? G0 >> 1 : G0;
+  const int r = SPLIT ? (b & 7) | ((b >> 4) << 3) : b;
+  const int tb0 = SPLIT ? ((b >> 3) & 1) * MB : 0;
+  const int mlo = tb0 * 16, mhi = SPLIT ? min(M, (tb0 + MB) * 16) : M;
+  const int i0 = range_start(r, U, G);
+  const int n = range_start(r + 1, U, G) - i0;
   const int nch = (K + 63) >> 6;
   if (tid < kSyncWords) sync[tid] = 0;  // ordered before use by barrier (1)
 
   if (wave < kS) {
-    wide_streamer<MB, TG, WB>(wq, qx, M, K, tiles, nch, P, i0, n, wave, lane, b < M, slots, red,
-                              sync, wc);
+    wide_streamer<MB, TG, WB, SPLIT>(wq, qx, M, K, tiles, nch, P, i0, n, wave, lane, b < M, tb0,
+                                     slots, red, sync, wc);
     return;
   }
 
   // ---- helpers
   const int ht = tid - 64 * kS;
   uint32_t e;
-  if (!wide_rows_and_gate(x, s, M, K, b, G, n, ht, wave - kS, lane, qx, sx, flags, sync, e, wc))
+  if (!wide_rows_and_gate<SPLIT>(x, s, M, K, b, G0, n, mlo, mhi, ht, wave - kS, lane, qx, sx, flags,
+                                 sync, e, wc))
     return;
-  wide_epilogue<MB, TG, WB>(wscale, sx, M, N, P, U, G, b, i0, n, e, ht, lane, red, sync,
-                            partials, flags, y, acc_out, wc);
+  wide_epilogue<MB, TG, WB, SPLIT>(wscale, sx, M, N, P, U, G, r, b, tb0, i0, n, e, ht, lane, red,
+                                   sync, partials, flags, y, acc_out, wc);
 }
 
 #define QUASAR_WIDE_PARAMS                                                                   \
@@ -738,23 +771,39 @@ __device__ __forceinline__ void wide_body(
 
 template <int MB, int TG>
 __global__ __launch_bounds__(kThreads) void w8a8_linear_wide_kernel(QUASAR_WIDE_PARAMS) {
-  wide_body<MB, TG, 8>(QUASAR_WIDE_ARGS);
+  wide_body<MB, TG, 8, false>(QUASAR_WIDE_ARGS);
 }
 
 template <int MB, int TG>
 __global__ __launch_bounds__(kThreads) void w4a8_linear_wide_kernel(QUASAR_WIDE_PARAMS) {
-  wide_body<MB, TG, 4>(QUASAR_WIDE_ARGS);
+  wide_body<MB, TG, 4, false>(QUASAR_WIDE_ARGS);
+}
+
+// The token-block split (pairs of tiles, MB of the 2 MB token blocks per
+// workgroup): its own kernels, so that the unsplit ones keep their constants.
+template <int MB>
+__global__ __launch_bounds__(kThreads) void w8a8_linear_wide_split_kernel(QUASAR_WIDE_PARAMS) {
+  wide_body<MB, 2, 8, true>(QUASAR_WIDE_ARGS);
+}
+
+template <int MB>
+__global__ __launch_bounds__(kThreads) void w4a8_linear_wide_split_kernel(QUASAR_WIDE_PARAMS) {
+  wide_body<MB, 2, 4, true>(QUASAR_WIDE_ARGS);
 }
 #undef QUASAR_WIDE_PARAMS
 #undef QUASAR_WIDE_ARGS
 
-template <int MB, int TG, int WB>
+template <int MB, int TG, int WB, bool SPLIT = false>
 hipError_t launch_wide_mb(const WidePlan& p, const uint16_t* x, const float* s, const int8_t* wq,
                           const float* w_scale, uint16_t* y, int32_t* acc_out, int8_t* qx,
                           float* sx, int32_t* partials, uint32_t* flags, const WaitCtl& wc,
                           hipStream_t st) {
   auto kernel = [] {
-    if constexpr (WB == 4)
+    if constexpr (SPLIT && WB == 4)
+      return &w4a8_linear_wide_split_kernel<MB>;
+    else if constexpr (SPLIT)
+      return &w8a8_linear_wide_split_kernel<MB>;
+    else if constexpr (WB == 4)
       return &w4a8_linear_wide_kernel<MB, TG>;
     else
       return &w8a8_linear_wide_kernel<MB, TG>;
@@ -780,7 +829,7 @@ hipError_t launch_wide_tg(const WidePlan& p, const uint16_t* x, const float* s, 
       return launch_wide_mb<B, TG, WB>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials,   \
                                        flags, wc, st);                                       \
     return hipErrorInvalidValue;
-  switch (p.mb) {
+  switch (p.mbl) {
     QUASAR_WIDE_CASE(1)
     QUASAR_WIDE_CASE(2)
     QUASAR_WIDE_CASE(3)
@@ -830,6 +879,27 @@ static_assert(wide_lds_of(6, 4) == Wide<6, 4>::LDS && wide_lds_of(3, 1) == Wide<
 // Sharing each fragment among 16 tiles through LDS no longer paid once
 // fragments were contiguous: 164 against 163 us on the 4096 -> 151936 LM head
 // at 96 tokens, 206 against 183 at 128.
+// Token-block split: at 64 tokens and more, up to one tile pair per range of
+// a full grid, two workgroups of one XCD share each pair of tiles and take
+// half of the token blocks each, so each reads half the code matrix while the
+// pair's weights come from HBM once and from L2 for the second reader; every
+// range owns one whole pair (no K range split).  Measured on MI355X (us per
+// launch, against the tile-group rule below, bit-identical outputs):
+//   * K <= 8192: 4096 -> 4096 at 64, 96 and 128 tokens 13.2 -> 12.2,
+//     14.7 -> 13.5 and 16.2 -> 15.1; 4096 -> 2048 at 96 tokens 14.1 -> 13.1;
+//     4-bit weights at 96 tokens 13.5 -> 12.1;
+//   * K > 8192 only with 256 tiles from 96 tokens (down at 96 tokens
+//     26.0 -> 25.4, 4-bit 22.3 -> 20.9) or beyond 96 x 12288 codes (down at
+//     128 tokens 33.7 -> 28.0): with fewer tiles or at 64 tokens the K-split
+//     pairs of every CU stay faster (12288 -> 2048 at 96 tokens 21.5 against
+//     24.2).
+bool wide_token_split(int64_t M, int64_t N, int64_t K, int grid) {
+  const int64_t mb = (M + 15) / 16, tiles = (N + 15) / 16, pairs = (tiles + 1) / 2;
+  const int64_t g = grid > 0 ? grid : kWideMaxGrid;
+  if (mb < 4 || mb % 2 != 0 || tiles > g || pairs % 8 != 0 || 2 * pairs < M) return false;
+  return K <= 8192 || (tiles == g && mb >= 6) || M * K > 96 * 12288;
+}
+
 int wide_tiles_per_group(int64_t M, int64_t N, int64_t K, int grid) {
   const int64_t tiles = (N + 15) / 16;
   const int64_t g = grid > 0 ? grid : kWideMaxGrid;
@@ -849,7 +919,9 @@ WidePlan plan_wide(int64_t M, int64_t N, int64_t K, int grid, int wbits) {
   p.K = K;
   p.wb = wbits == 4 ? 4 : 8;
   p.mb = (int)((M + 15) / 16);
-  p.tg = wide_tiles_per_group(M, N, K, grid);
+  p.ms = wide_token_split(M, N, K, grid) ? 2 : 1;
+  p.mbl = p.mb / p.ms;
+  p.tg = p.ms == 2 ? 2 : wide_tiles_per_group(M, N, K, grid);
   p.tiles = (int)((N + 15) / 16);
   p.nch = (int)((K + 63) / 64);
   p.groups = (p.tiles + p.tg - 1) / p.tg;
@@ -858,7 +930,7 @@ WidePlan plan_wide(int64_t M, int64_t N, int64_t K, int grid, int wbits) {
   p.P = (nwc + kS - 1) / kS;
   p.U = p.groups * p.P;
   p.grid = grid;
-  p.lds = wide_lds_of(p.mb, p.tg, p.wb);
+  p.lds = wide_lds_of(p.mbl, p.tg, p.wb);
   size_t off = kFlagHeaderBytes;  // the flag header (quasar_sync.hpp) comes first
   p.off_qx = off;  // fragment-major codes: 1 KB per 16-token block and 64-wide K chunk
   off = align_up(off + (size_t)p.mb * p.nch * 1024, kWsAlign);
@@ -870,17 +942,21 @@ WidePlan plan_wide(int64_t M, int64_t N, int64_t K, int grid, int wbits) {
   return p;
 }
 
-const char* wide_kernel_name(int mb, int tg, int wbits) {
-  // "w8a8_linear_wide_kernel<MB, TG>" / "w4a8_linear_wide_kernel<MB, TG>"
+const char* wide_kernel_name(int mb, int tg, int wbits, bool split) {
+  // "w8a8_linear_wide_kernel<MB, TG>" / "w4a8_linear_wide_kernel<MB, TG>", and
+  // "w8a8_linear_wide_split_kernel<MB>" / "w4a8_linear_wide_split_kernel<MB>"
   static const std::vector<std::string> names = [] {
     std::vector<std::string> v;
     for (const char* k : {"w8a8_linear_wide_kernel<", "w4a8_linear_wide_kernel<"})
       for (int t : {1, 2, kMaxTG})
         for (int b = 1; b <= 8; ++b)
           v.push_back(std::string(k) + std::to_string(b) + ", " + std::to_string(t) + ">");
+    for (const char* k : {"w8a8_linear_wide_split_kernel<", "w4a8_linear_wide_split_kernel<"})
+      for (int b = 1; b <= 8; ++b) v.push_back(std::string(k) + std::to_string(b) + ">");
     return v;
   }();
   const int wi = wbits == 4 ? 1 : 0;
+  if (split) return names[48 + wi * 8 + (mb < 1 ? 1 : (mb > 8 ? 8 : mb)) - 1].c_str();
   const int ti = tg == 1 ? 0 : (tg == 2 ? 1 : 2);
   mb = mb < 1 ? 1 : (mb > 8 ? 8 : mb);
   return names[(wi * 3 + ti) * 8 + mb - 1].c_str();
@@ -898,6 +974,22 @@ hipError_t launch_wide(const WidePlan& p, const uint16_t* x, const float* s, con
   uint32_t* flags = reinterpret_cast<uint32_t*>(ws);
   const WaitCtl wc = wait_ctl_for_current_device();
   if (!wc.status) return hipErrorInvalidSymbol;
+  if (p.ms == 2) {  // token-block split: pairs of tiles, 2, 3 or 4 blocks per workgroup
+#define QUASAR_SPLIT_ARGS p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st
+    switch (p.mbl) {
+      case 2:
+        return p.wb == 4 ? launch_wide_mb<2, 2, 4, true>(QUASAR_SPLIT_ARGS)
+                         : launch_wide_mb<2, 2, 8, true>(QUASAR_SPLIT_ARGS);
+      case 3:
+        return p.wb == 4 ? launch_wide_mb<3, 2, 4, true>(QUASAR_SPLIT_ARGS)
+                         : launch_wide_mb<3, 2, 8, true>(QUASAR_SPLIT_ARGS);
+      case 4:
+        return p.wb == 4 ? hipErrorInvalidValue : launch_wide_mb<4, 2, 8, true>(QUASAR_SPLIT_ARGS);
+      default:
+        return hipErrorInvalidValue;
+    }
+#undef QUASAR_SPLIT_ARGS
+  }
   if (p.wb == 4) {
     if (p.tg == 1)
       return launch_wide_tg<1, 4>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st);
@@ -976,6 +1068,13 @@ int wide_grid_for_current_device() {
 
 int wide_launch_grid(const WidePlan& p) {
   const int dev = wide_grid_for_current_device();
+  if (p.ms == 2) {
+    // two workgroups per range, one range per pair of tiles; the pairs of an
+    // XCD need a grid that is a multiple of 16 (fewer ranges split K)
+    if (2 * p.groups <= dev) return 2 * p.groups;
+    const int g16 = dev / 16 * 16;
+    return g16 >= p.M ? g16 : 0;
+  }
   // one group per workgroup where the groups fit the device's grid and K is
   // not split (wide_tiles_per_group); still one workgroup per token row
   if (dev > 0 && p.K <= 8192 && p.groups <= dev && p.groups >= p.M) return p.groups;

@@ -43,6 +43,8 @@ _FAMILY_SOURCES = (
     ("w4a8_linear_fused_kernel", "fused.hip"),
     ("w8a8_linear_wide_kernel", "wide.hip"),
     ("w4a8_linear_wide_kernel", "wide.hip"),
+    ("w8a8_linear_wide_split_kernel", "wide.hip"),
+    ("w4a8_linear_wide_split_kernel", "wide.hip"),
     ("w8a8_chain_kernel", "chain.hip"),
     ("accept_", "accept.hip"),
 )
