@@ -214,9 +214,10 @@ def test_w4_argument_errors_and_sizes(L):
     # wider windows: the wide kernel with 4-bit weights, <token blocks, tiles per group>
     assert name(9, 16, 128) == "w4a8_linear_wide_kernel<1, 1>"
     assert name(48, 4096, 4096) == "w4a8_linear_wide_kernel<3, 1>"
-    assert name(96, 6144, 4096) == "w4a8_linear_wide_kernel<6, 2>"
-    assert name(96, 4096, 4096) == "w4a8_linear_wide_split_kernel<3>"
-    assert name(64, 2048, 4096) == "w4a8_linear_wide_split_kernel<2>"
+    assert name(96, 4096, 4096) == "w4a8_linear_wide_split_kernel<3, 2>"
+    assert name(64, 2048, 4096) == "w4a8_linear_wide_split_kernel<2, 2>"
+    assert name(96, 6144, 4096) == "w4a8_linear_wide_split_kernel<3, 3>"   # triples from 96 tokens
+    assert name(64, 6144, 4096) == "w4a8_linear_wide_kernel<4, 2>"
     assert name(96, 24576, 4096) == "w4a8_linear_wide_kernel<6, 4>"
     assert name(6, 64, 16384) == "w4a8_linear_wide_kernel<1, 2>"
     assert name(97, 16, 128) == "" and name(6, 16, 192) == ""
@@ -247,16 +248,18 @@ def test_kernel_name_names_the_launch_plan(L):
     # 256 tiles, pairs up to 512, pairs below 1024 tiles up to 64 tokens, pairs
     # up to 2048 tiles up to 32 tokens; groups of 4 tiles beyond
     assert name(48, 4096, 4096) == "w8a8_linear_wide_kernel<3, 1>"
-    assert name(96, 4096, 4096) == "w8a8_linear_wide_split_kernel<3>"  # token blocks split in two
-    assert name(96, 4096, 12288) == "w8a8_linear_wide_split_kernel<3>" # split: 256 tiles
+    assert name(96, 4096, 4096) == "w8a8_linear_wide_split_kernel<3, 2>"  # token blocks split in two
+    assert name(96, 4096, 12288) == "w8a8_linear_wide_split_kernel<3, 2>"  # split: 256 tiles
     assert name(48, 4096, 12288) == "w8a8_linear_wide_kernel<3, 2>"
-    assert name(128, 4096, 12288) == "w8a8_linear_wide_split_kernel<4>" # split: beyond 96 x 12288
+    assert name(128, 4096, 12288) == "w8a8_linear_wide_split_kernel<4, 2>"  # beyond 96 x 12288
     assert name(64, 4096, 12288) == "w8a8_linear_wide_kernel<4, 2>"    # no split: K-split pairs
     assert name(96, 2048, 12288) == "w8a8_linear_wide_kernel<6, 2>"    # no split: 128 tiles
-    assert name(64, 2048, 4096) == "w8a8_linear_wide_split_kernel<2>"  # split
+    assert name(64, 2048, 4096) == "w8a8_linear_wide_split_kernel<2, 2>"  # split
     assert name(80, 4096, 4096) == "w8a8_linear_wide_kernel<5, 1>"     # odd block count: no split
     assert name(128, 4000, 4096) == "w8a8_linear_wide_kernel<8, 1>"    # 125 pairs: no split
-    assert name(96, 6144, 4096) == "w8a8_linear_wide_kernel<6, 2>"
+    assert name(96, 6144, 4096) == "w8a8_linear_wide_split_kernel<3, 3>"  # groups of 3 tiles
+    assert name(64, 6144, 4096) == "w8a8_linear_wide_split_kernel<2, 3>"
+    assert name(96, 6152, 4096) == "w8a8_linear_wide_kernel<6, 2>"        # 129 triples
     assert name(48, 6144, 4096) == "w8a8_linear_wide_kernel<3, 2>"
     assert name(9, 16, 16) == "w8a8_linear_wide_kernel<1, 1>"
     assert name(6, 64, 16384) == "w8a8_linear_wide_kernel<1, 2>"

@@ -95,6 +95,8 @@ RAGGED = [
     # 96 x 12288
     (64, 2048, 4096), (90, 4090, 4096), (128, 2040, 4096), (64, 3072, 8192), (96, 1530, 2112),
     (96, 4096, 12288), (128, 2048, 12288), (128, 2048, 16384),
+    # the split with groups of 3 tiles (up to 384 tiles): ragged M, N and K
+    (90, 6130, 4224), (128, 6100, 1024), (64, 6144, 2048),
 ]
 
 

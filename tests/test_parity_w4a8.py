@@ -59,6 +59,8 @@ SHAPES = [
     # token blocks split over two workgroups (3 + 3 blocks with a ragged last
     # one, 2 + 2), ragged N, K past 8192 with 256 tiles
     (90, 4090, 4096), (64, 3072, 8192), (96, 4096, 12288),
+    # groups of 3 tiles split over two workgroups
+    (96, 6100, 2048), (90, 6130, 4224),
 ]
 
 

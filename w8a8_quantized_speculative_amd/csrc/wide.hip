@@ -779,16 +779,17 @@ __global__ __launch_bounds__(kThreads) void w4a8_linear_wide_kernel(QUASAR_WIDE_
   wide_body<MB, TG, 4, false>(QUASAR_WIDE_ARGS);
 }
 
-// The token-block split (pairs of tiles, MB of the 2 MB token blocks per
-// workgroup): its own kernels, so that the unsplit ones keep their constants.
-template <int MB>
+// The token-block split (groups of TG = 2 or 3 tiles, MB of the 2 MB token
+// blocks per workgroup): its own kernels, so that the unsplit ones keep their
+// constants.
+template <int MB, int TG>
 __global__ __launch_bounds__(kThreads) void w8a8_linear_wide_split_kernel(QUASAR_WIDE_PARAMS) {
-  wide_body<MB, 2, 8, true>(QUASAR_WIDE_ARGS);
+  wide_body<MB, TG, 8, true>(QUASAR_WIDE_ARGS);
 }
 
-template <int MB>
+template <int MB, int TG>
 __global__ __launch_bounds__(kThreads) void w4a8_linear_wide_split_kernel(QUASAR_WIDE_PARAMS) {
-  wide_body<MB, 2, 4, true>(QUASAR_WIDE_ARGS);
+  wide_body<MB, TG, 4, true>(QUASAR_WIDE_ARGS);
 }
 #undef QUASAR_WIDE_PARAMS
 #undef QUASAR_WIDE_ARGS
@@ -800,9 +801,9 @@ hipError_t launch_wide_mb(const WidePlan& p, const uint16_t* x, const float* s, 
                           hipStream_t st) {
   auto kernel = [] {
     if constexpr (SPLIT && WB == 4)
-      return &w4a8_linear_wide_split_kernel<MB>;
+      return &w4a8_linear_wide_split_kernel<MB, TG>;
     else if constexpr (SPLIT)
-      return &w8a8_linear_wide_split_kernel<MB>;
+      return &w8a8_linear_wide_split_kernel<MB, TG>;
     else if constexpr (WB == 4)
       return &w4a8_linear_wide_kernel<MB, TG>;
     else
@@ -880,7 +881,7 @@ static_assert(wide_lds_of(6, 4) == Wide<6, 4>::LDS && wide_lds_of(3, 1) == Wide<
 // fragments were contiguous: 164 against 163 us on the 4096 -> 151936 LM head
 // at 96 tokens, 206 against 183 at 128.
 // Token-block split: at 64 tokens and more, up to one tile pair per range of
-// a full grid, two workgroups of one XCD share each pair of tiles and take
+// a full grid, two workgroups of one XCD share each group of tiles and take
 // half of the token blocks each, so each reads half the code matrix while the
 // pair's weights come from HBM once and from L2 for the second reader; every
 // range owns one whole pair (no K range split).  Measured on MI355X (us per
@@ -893,11 +894,23 @@ static_assert(wide_lds_of(6, 4) == Wide<6, 4>::LDS && wide_lds_of(3, 1) == Wide<
 //     128 tokens 33.7 -> 28.0): with fewer tiles or at 64 tokens the K-split
 //     pairs of every CU stay faster (12288 -> 2048 at 96 tokens 21.5 against
 //     24.2).
-bool wide_token_split(int64_t M, int64_t N, int64_t K, int grid) {
-  const int64_t mb = (M + 15) / 16, tiles = (N + 15) / 16, pairs = (tiles + 1) / 2;
+// Between 1 and 1.5 tiles per CU (QKV) the ranges take groups of 3 tiles
+// (K <= 8192): 4096 -> 6144 at 64, 96 and 128 tokens 14.5 -> 14.0, 16.5 ->
+// 16.0 and 18.2 -> 17.7; with 4-bit weights only from 96 tokens (14.9 ->
+// 13.7; at 64 tokens 12.2 -> 13.0).
+// Returns the tiles per group of the split (2 or 3), or 0 for no split.
+int wide_token_split(int64_t M, int64_t N, int64_t K, int grid, int wbits) {
+  const int64_t mb = (M + 15) / 16, tiles = (N + 15) / 16;
+  const int64_t pairs = (tiles + 1) / 2, triples = (tiles + 2) / 3;
   const int64_t g = grid > 0 ? grid : kWideMaxGrid;
-  if (mb < 4 || mb % 2 != 0 || tiles > g || pairs % 8 != 0 || 2 * pairs < M) return false;
-  return K <= 8192 || (tiles == g && mb >= 6) || M * K > 96 * 12288;
+  if (mb < 4 || mb % 2 != 0) return 0;
+  if (tiles <= g && pairs % 8 == 0 && 2 * pairs >= M &&
+      (K <= 8192 || (tiles == g && mb >= 6) || M * K > 96 * 12288))
+    return 2;
+  if (tiles > g && 2 * tiles <= 3 * g && triples % 8 == 0 && 2 * triples >= M && K <= 8192 &&
+      (wbits != 4 || mb >= 6))
+    return 3;
+  return 0;
 }
 
 int wide_tiles_per_group(int64_t M, int64_t N, int64_t K, int grid) {
@@ -919,9 +932,10 @@ WidePlan plan_wide(int64_t M, int64_t N, int64_t K, int grid, int wbits) {
   p.K = K;
   p.wb = wbits == 4 ? 4 : 8;
   p.mb = (int)((M + 15) / 16);
-  p.ms = wide_token_split(M, N, K, grid) ? 2 : 1;
+  const int split_tg = wide_token_split(M, N, K, grid, p.wb);
+  p.ms = split_tg ? 2 : 1;
   p.mbl = p.mb / p.ms;
-  p.tg = p.ms == 2 ? 2 : wide_tiles_per_group(M, N, K, grid);
+  p.tg = split_tg ? split_tg : wide_tiles_per_group(M, N, K, grid);
   p.tiles = (int)((N + 15) / 16);
   p.nch = (int)((K + 63) / 64);
   p.groups = (p.tiles + p.tg - 1) / p.tg;
@@ -943,23 +957,21 @@ WidePlan plan_wide(int64_t M, int64_t N, int64_t K, int grid, int wbits) {
 }
 
 const char* wide_kernel_name(int mb, int tg, int wbits, bool split) {
-  // "w8a8_linear_wide_kernel<MB, TG>" / "w4a8_linear_wide_kernel<MB, TG>", and
-  // "w8a8_linear_wide_split_kernel<MB>" / "w4a8_linear_wide_split_kernel<MB>"
+  // "w8a8_linear_wide_kernel<MB, TG>" / "w4a8_linear_wide_kernel<MB, TG>" (TG 1, 2, 4), and
+  // "w8a8_linear_wide_split_kernel<MB, TG>" / "w4a8_..." (TG 2, 3)
   static const std::vector<std::string> names = [] {
     std::vector<std::string> v;
-    for (const char* k : {"w8a8_linear_wide_kernel<", "w4a8_linear_wide_kernel<"})
-      for (int t : {1, 2, kMaxTG})
+    for (const char* k : {"w8a8_linear_wide_kernel<", "w4a8_linear_wide_kernel<",
+                          "w8a8_linear_wide_split_kernel<", "w4a8_linear_wide_split_kernel<"})
+      for (int t : {1, 2, 3, kMaxTG})
         for (int b = 1; b <= 8; ++b)
           v.push_back(std::string(k) + std::to_string(b) + ", " + std::to_string(t) + ">");
-    for (const char* k : {"w8a8_linear_wide_split_kernel<", "w4a8_linear_wide_split_kernel<"})
-      for (int b = 1; b <= 8; ++b) v.push_back(std::string(k) + std::to_string(b) + ">");
     return v;
   }();
-  const int wi = wbits == 4 ? 1 : 0;
-  if (split) return names[48 + wi * 8 + (mb < 1 ? 1 : (mb > 8 ? 8 : mb)) - 1].c_str();
-  const int ti = tg == 1 ? 0 : (tg == 2 ? 1 : 2);
+  const int ki = (split ? 2 : 0) + (wbits == 4 ? 1 : 0);
+  const int ti = tg <= 1 ? 0 : (tg == 2 ? 1 : (tg == 3 ? 2 : 3));
   mb = mb < 1 ? 1 : (mb > 8 ? 8 : mb);
-  return names[(wi * 3 + ti) * 8 + mb - 1].c_str();
+  return names[(ki * 4 + ti) * 8 + mb - 1].c_str();
 }
 
 bool wide_w4_supported(int64_t M) { return (M + 15) / 16 <= kWideMaxMbW4; }
@@ -974,20 +986,25 @@ hipError_t launch_wide(const WidePlan& p, const uint16_t* x, const float* s, con
   uint32_t* flags = reinterpret_cast<uint32_t*>(ws);
   const WaitCtl wc = wait_ctl_for_current_device();
   if (!wc.status) return hipErrorInvalidSymbol;
-  if (p.ms == 2) {  // token-block split: pairs of tiles, 2, 3 or 4 blocks per workgroup
+  if (p.ms == 2) {  // token-block split: groups of 2 or 3 tiles, 2, 3 or 4 blocks per workgroup
 #define QUASAR_SPLIT_ARGS p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st
-    switch (p.mbl) {
-      case 2:
-        return p.wb == 4 ? launch_wide_mb<2, 2, 4, true>(QUASAR_SPLIT_ARGS)
-                         : launch_wide_mb<2, 2, 8, true>(QUASAR_SPLIT_ARGS);
-      case 3:
-        return p.wb == 4 ? launch_wide_mb<3, 2, 4, true>(QUASAR_SPLIT_ARGS)
-                         : launch_wide_mb<3, 2, 8, true>(QUASAR_SPLIT_ARGS);
-      case 4:
-        return p.wb == 4 ? hipErrorInvalidValue : launch_wide_mb<4, 2, 8, true>(QUASAR_SPLIT_ARGS);
-      default:
-        return hipErrorInvalidValue;
-    }
+#define QUASAR_SPLIT_TG(T)                                                                  \
+  switch (p.mbl) {                                                                          \
+    case 2:                                                                                 \
+      return p.wb == 4 ? launch_wide_mb<2, T, 4, true>(QUASAR_SPLIT_ARGS)                   \
+                       : launch_wide_mb<2, T, 8, true>(QUASAR_SPLIT_ARGS);                  \
+    case 3:                                                                                 \
+      return p.wb == 4 ? launch_wide_mb<3, T, 4, true>(QUASAR_SPLIT_ARGS)                   \
+                       : launch_wide_mb<3, T, 8, true>(QUASAR_SPLIT_ARGS);                  \
+    case 4:                                                                                 \
+      return p.wb == 4 ? hipErrorInvalidValue : launch_wide_mb<4, T, 8, true>(QUASAR_SPLIT_ARGS); \
+    default:                                                                                \
+      return hipErrorInvalidValue;                                                          \
+  }
+    if (p.tg == 2) QUASAR_SPLIT_TG(2)
+    if (p.tg == 3) QUASAR_SPLIT_TG(3)
+    return hipErrorInvalidValue;
+#undef QUASAR_SPLIT_TG
 #undef QUASAR_SPLIT_ARGS
   }
   if (p.wb == 4) {
