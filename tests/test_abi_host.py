@@ -263,16 +263,17 @@ def test_kernel_name_names_the_launch_plan(L):
     assert name(48, 6144, 4096) == "w8a8_linear_wide_kernel<3, 2>"
     assert name(9, 16, 16) == "w8a8_linear_wide_kernel<1, 1>"
     assert name(6, 64, 16384) == "w8a8_linear_wide_kernel<1, 2>"
-    assert name(96, 24576, 4096) == "w8a8_linear_wide_kernel<6, 4>"
-    assert name(48, 151936, 4096) == "w8a8_linear_wide_kernel<3, 4>"
-    assert name(96, 151936, 4096) == "w8a8_linear_wide_kernel<6, 4>"
+    assert name(96, 24576, 4096) == "w8a8_linear_wide_kernel<6, 6>"     # groups of 6 tiles
+    assert name(48, 151936, 4096) == "w8a8_linear_wide_kernel<3, 6>"
+    assert name(96, 151936, 4096) == "w8a8_linear_wide_kernel<6, 6>"
     assert name(128, 151936, 4096) == "w8a8_linear_wide_kernel<8, 4>"
     assert name(48, 12288, 4096) == "w8a8_linear_wide_kernel<3, 2>"     # 768 tiles, <= 64 tokens
     assert name(96, 12288, 4096) == "w8a8_linear_wide_kernel<6, 4>"     # 768 tiles, > 64 tokens
     assert name(64, 16384, 4096) == "w8a8_linear_wide_kernel<4, 4>"     # 1024 tiles
     assert name(32, 16384, 4096) == "w8a8_linear_wide_kernel<2, 2>"     # <= 2048 tiles, <= 32 tokens
     assert name(16, 24576, 4096) == "w8a8_linear_wide_kernel<1, 2>"
-    assert name(48, 24576, 4096) == "w8a8_linear_wide_kernel<3, 4>"
+    assert name(48, 24576, 4096) == "w8a8_linear_wide_kernel<3, 6>"
+    assert name(112, 24576, 4096) == "w8a8_linear_wide_kernel<7, 4>"    # 7 blocks: groups of 4
     assert name(16, 49152, 4096) == "w8a8_linear_wide_kernel<1, 4>"     # 3072 tiles
     # invalid or unsupported sizes
     assert name(0, 16, 16) == "" and name(6, 16, 17) == "" and name(129, 16, 16) == ""

@@ -97,6 +97,10 @@ RAGGED = [
     (96, 4096, 12288), (128, 2048, 12288), (128, 2048, 16384),
     # the split with groups of 3 tiles (up to 384 tiles): ragged M, N and K
     (90, 6130, 4224), (128, 6100, 1024), (64, 6144, 2048),
+    # groups of 6 tiles (beyond 4 tiles per CU, 3 to 6 token blocks): one
+    # group per workgroup, and groups split across workgroups (partial sums
+    # of 6 tiles), ragged N and K
+    (70, 17000, 1040), (48, 20000, 512), (96, 30000, 256), (64, 16400, 2112), (81, 24576, 4160),
 ]
 
 

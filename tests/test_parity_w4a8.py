@@ -61,6 +61,8 @@ SHAPES = [
     (90, 4090, 4096), (64, 3072, 8192), (96, 4096, 12288),
     # groups of 3 tiles split over two workgroups
     (96, 6100, 2048), (90, 6130, 4224),
+    # groups of 6 tiles (3 to 5 token blocks): one per workgroup and split
+    (48, 20000, 512), (80, 17000, 1152), (40, 30000, 256),
 ]
 
 

@@ -82,7 +82,7 @@ struct WidePlan {
   int mb;      // 16-token blocks: ceil(M / 16), 1..8
   int ms;      // token-block split: 1, or 2 (two workgroups share a group, half the blocks each)
   int mbl;     // token blocks per workgroup: mb / ms (the kernel's MB)
-  int tg;      // 16-channel tiles per group: 1, 2 or 4 (2 or 3 with the split)
+  int tg;      // 16-channel tiles per group: 1, 2, 4 or 6 (2 or 3 with the split)
   int tiles;   // ceil(N / 16)
   int nch;     // ceil(K / 64)
   int groups;  // ceil(tiles / tg)
@@ -100,7 +100,7 @@ WidePlan plan_wide(int64_t M, int64_t N, int64_t K, int grid, int wbits = 8);
 const char* wide_kernel_name(int mb, int tg, int wbits = 8, bool split = false);
 // 4-bit weights in the wide kernel: up to 96 tokens
 bool wide_w4_supported(int64_t M);
-int wide_tiles_per_group(int64_t M, int64_t N, int64_t K, int grid);
+int wide_tiles_per_group(int64_t M, int64_t N, int64_t K, int grid, int wbits = 8);
 int wide_token_split(int64_t M, int64_t N, int64_t K, int grid, int wbits);
 // Workgroups of a wide launch on the current device (0: cannot run there).
 int wide_grid_for_current_device();

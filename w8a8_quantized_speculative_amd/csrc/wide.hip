@@ -81,7 +81,8 @@ namespace quasar {
 namespace {
 
 constexpr int kS = 4;        // streamer wavefronts (one 64-wide K chunk each per item)
-constexpr int kMaxTG = 4;    // 16-channel tiles per group: 1, 2 or 4
+constexpr int kMaxTG = 4;    // 16-channel tiles per group: 1, 2 or 4 ...
+constexpr int kWideTG = 6;   // ... or 6 (beyond 4 tiles per CU at 48 to 96 tokens)
 constexpr int kHelpers = 4;  // row quantizer, then epilogue wavefronts
 constexpr int kThreads = 64 * (kS + kHelpers);
 constexpr int kRowPieces = 8;  // 8-element pieces per helper thread kept in registers
@@ -98,9 +99,11 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 // code slots (4 streamers x NBUF items x F MB KB) and the partial-sum area
 // (2 x 4 x MB KB) stay within 150 KB of LDS, and the loads in flight per
 // wavefront ((NBUF - 1) items of TG + F MB, plus one item's F MB code loads)
-// within what the 6-bit vmcnt counter can wait for.  At most 8.
+// within what the 6-bit vmcnt counter can wait for.  At most 8; groups of 6
+// tiles keep 2 items in flight, since their 6 x MB accumulators leave no
+// registers for more.
 constexpr int wide_nbuf(int MB, int TG, int F = 1) {
-  int nb = 8;
+  int nb = TG > kMaxTG ? 2 : 8;
   while (nb > 2 && (kS * nb * F * MB + 2 * kS * MB > 150 || (nb - 1) * (TG + F * MB) + F * MB > 63))
     --nb;
   return nb;
@@ -128,6 +131,16 @@ static_assert(wide_fits<1, 1>() && wide_fits<2, 1>() && wide_fits<3, 1>() && wid
                   wide_fits<8, 1>() && wide_fits<1, 2>() && wide_fits<2, 2>() &&
                   wide_fits<3, 2>() && wide_fits<4, 2>() && wide_fits<5, 2>() && wide_fits<6, 2>(),
               "LDS budget, and in-flight loads within the 6-bit vmcnt");
+// groups of 6 tiles: 3 to 6 token blocks (3 to 5 with 4-bit weights)
+template <int MB, int F>
+constexpr bool wide_fits_tg6() {
+  return Wide<MB, kWideTG, F>::LDS <= 150 * 1024 &&
+         (Wide<MB, kWideTG, F>::NBUF - 1) * (kWideTG + F * MB) + F * MB <= 63;
+}
+static_assert(wide_fits_tg6<3, 1>() && wide_fits_tg6<4, 1>() && wide_fits_tg6<5, 1>() &&
+                  wide_fits_tg6<6, 1>() && wide_fits_tg6<3, 2>() && wide_fits_tg6<4, 2>() &&
+                  wide_fits_tg6<5, 2>(),
+              "groups of 6 tiles: LDS budget and in-flight loads");
 
 // LDS synchronisation words (int indices into the SYNC area)
 enum : int {
@@ -591,7 +604,7 @@ __device__ __forceinline__ void wide_epilogue(const float* __restrict__ wscale,
                                               uint16_t* __restrict__ y,
                                               int32_t* __restrict__ acc_out, const WaitCtl& wc) {
   constexpr int KS = (MB + 3) / 4;           // slots per thread and round
-  constexpr int kPartInts = kMaxTG * MB * 256;  // one workgroup's partial-sum slot
+  constexpr int kPartInts = (TG > kMaxTG ? TG : kMaxTG) * MB * 256;  // one workgroup's partial sums
   const int ln = et & 63;
   if (!SPLIT) tb0 = 0;
   const int mpart = (bp >> 3) & 1;
@@ -875,8 +888,15 @@ static_assert(wide_lds_of(6, 4) == Wide<6, 4>::LDS && wide_lds_of(3, 1) == Wide<
 //   * K > 8192 (down): pairs of tiles on every CU, each K range split in two
 //     (down at 48 and 96 tokens: 20.0 and 26.0 against 21.3 and 29.5 for
 //     single tiles and 24.7 and 33.1 for one pair per workgroup);
-//   * beyond (gate_up from 48 tokens, the LM head; down at 128 tokens): groups
-//     of 4 on every CU.
+//   * beyond 4 tiles per CU from 48 to 96 tokens (3 to 6 token blocks, 3 to 5
+//     with 4-bit weights, whose 6-block streamer would spill): groups of 6
+//     tiles, one per CU for gate_up (no K range split), with two items in
+//     flight per streamer: gate_up at 48, 64, 80 and 96 tokens 26.0, 28.5,
+//     31.3, 32.8 -> 22.7, 24.2, 26.6, 27.9; the LM head at 64 and 96 tokens
+//     131.1 -> 126.1 and 152.5 -> 148.6; 4-bit gate_up at 48 tokens 20.6 ->
+//     16.9, its LM head 78.9 -> 74.6;
+//   * beyond (the LM head above 96 tokens, down at 128 tokens, 4-bit at 96
+//     tokens): groups of 4 on every CU.
 // Sharing each fragment among 16 tiles through LDS no longer paid once
 // fragments were contiguous: 164 against 163 us on the 4096 -> 151936 LM head
 // at 96 tokens, 206 against 183 at 128.
@@ -913,8 +933,8 @@ int wide_token_split(int64_t M, int64_t N, int64_t K, int grid, int wbits) {
   return 0;
 }
 
-int wide_tiles_per_group(int64_t M, int64_t N, int64_t K, int grid) {
-  const int64_t tiles = (N + 15) / 16;
+int wide_tiles_per_group(int64_t M, int64_t N, int64_t K, int grid, int wbits) {
+  const int64_t tiles = (N + 15) / 16, mb = (M + 15) / 16;
   const int64_t g = grid > 0 ? grid : kWideMaxGrid;
   if (M * K > 96 * 12288) return kMaxTG;
   if (K > 8192) return tiles <= 2 * g ? 2 : kMaxTG;
@@ -922,6 +942,7 @@ int wide_tiles_per_group(int64_t M, int64_t N, int64_t K, int grid) {
   if (tiles <= 2 * g) return 2;
   if (tiles < 4 * g) return M <= 64 ? 2 : kMaxTG;
   if (tiles <= 8 * g && M <= 32) return 2;
+  if (tiles > 4 * g && mb >= 3 && mb <= (wbits == 4 ? 5 : 6)) return kWideTG;
   return kMaxTG;
 }
 
@@ -935,7 +956,7 @@ WidePlan plan_wide(int64_t M, int64_t N, int64_t K, int grid, int wbits) {
   const int split_tg = wide_token_split(M, N, K, grid, p.wb);
   p.ms = split_tg ? 2 : 1;
   p.mbl = p.mb / p.ms;
-  p.tg = split_tg ? split_tg : wide_tiles_per_group(M, N, K, grid);
+  p.tg = split_tg ? split_tg : wide_tiles_per_group(M, N, K, grid, p.wb);
   p.tiles = (int)((N + 15) / 16);
   p.nch = (int)((K + 63) / 64);
   p.groups = (p.tiles + p.tg - 1) / p.tg;
@@ -951,7 +972,8 @@ WidePlan plan_wide(int64_t M, int64_t N, int64_t K, int grid, int wbits) {
   p.off_sx = off;
   off = align_up(off + (size_t)M * sizeof(float), kWsAlign);
   p.off_partials = off;
-  off = align_up(off + (size_t)kWideMaxGrid * kMaxTG * p.mb * 1024, kWsAlign);
+  off = align_up(off + (size_t)kWideMaxGrid * (p.tg > kMaxTG ? p.tg : kMaxTG) * p.mb * 1024,
+                 kWsAlign);
   p.bytes = off;
   return p;
 }
@@ -963,19 +985,20 @@ const char* wide_kernel_name(int mb, int tg, int wbits, bool split) {
     std::vector<std::string> v;
     for (const char* k : {"w8a8_linear_wide_kernel<", "w4a8_linear_wide_kernel<",
                           "w8a8_linear_wide_split_kernel<", "w4a8_linear_wide_split_kernel<"})
-      for (int t : {1, 2, 3, kMaxTG})
+      for (int t : {1, 2, 3, kMaxTG, kWideTG})
         for (int b = 1; b <= 8; ++b)
           v.push_back(std::string(k) + std::to_string(b) + ", " + std::to_string(t) + ">");
     return v;
   }();
   const int ki = (split ? 2 : 0) + (wbits == 4 ? 1 : 0);
-  const int ti = tg <= 1 ? 0 : (tg == 2 ? 1 : (tg == 3 ? 2 : 3));
+  const int ti = tg <= 1 ? 0 : (tg == 2 ? 1 : (tg == 3 ? 2 : (tg == kMaxTG ? 3 : 4)));
   mb = mb < 1 ? 1 : (mb > 8 ? 8 : mb);
-  return names[(ki * 4 + ti) * 8 + mb - 1].c_str();
+  return names[(ki * 5 + ti) * 8 + mb - 1].c_str();
 }
 
 bool wide_w4_supported(int64_t M) { return (M + 15) / 16 <= kWideMaxMbW4; }
 
+#define QUASAR_WIDE_LAUNCH_ARGS p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc, st
 hipError_t launch_wide(const WidePlan& p, const uint16_t* x, const float* s, const int8_t* wq,
                        const float* w_scale, uint16_t* y, int32_t* acc_out, void* workspace,
                        hipStream_t st) {
@@ -1015,6 +1038,14 @@ hipError_t launch_wide(const WidePlan& p, const uint16_t* x, const float* s, con
     if (p.tg == kMaxTG)
       return launch_wide_tg<kMaxTG, 4>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags,
                                        wc, st);
+    if (p.tg == kWideTG) {
+      switch (p.mbl) {
+        case 3: return launch_wide_mb<3, kWideTG, 4>(QUASAR_WIDE_LAUNCH_ARGS);
+        case 4: return launch_wide_mb<4, kWideTG, 4>(QUASAR_WIDE_LAUNCH_ARGS);
+        case 5: return launch_wide_mb<5, kWideTG, 4>(QUASAR_WIDE_LAUNCH_ARGS);
+        default: return hipErrorInvalidValue;
+      }
+    }
     return hipErrorInvalidValue;
   }
   if (p.tg == 1)
@@ -1024,8 +1055,18 @@ hipError_t launch_wide(const WidePlan& p, const uint16_t* x, const float* s, con
   if (p.tg == kMaxTG)
     return launch_wide_tg<kMaxTG, 8>(p, x, s, wq, w_scale, y, acc_out, qx, sx, partials, flags, wc,
                                      st);
+  if (p.tg == kWideTG) {
+    switch (p.mbl) {
+      case 3: return launch_wide_mb<3, kWideTG, 8>(QUASAR_WIDE_LAUNCH_ARGS);
+      case 4: return launch_wide_mb<4, kWideTG, 8>(QUASAR_WIDE_LAUNCH_ARGS);
+      case 5: return launch_wide_mb<5, kWideTG, 8>(QUASAR_WIDE_LAUNCH_ARGS);
+      case 6: return launch_wide_mb<6, kWideTG, 8>(QUASAR_WIDE_LAUNCH_ARGS);
+      default: return hipErrorInvalidValue;
+    }
+  }
   return hipErrorInvalidValue;
 }
+#undef QUASAR_WIDE_LAUNCH_ARGS
 
 // Scratch of quasar_w8a8_linear_noalloc: the wide kernel's workspace (flag
 // header, quantized rows, token scales, INT32 partials) in a file-scope device
