@@ -23,13 +23,16 @@
 //      flags are set -- a one-way grid barrier.  Meanwhile its streamer
 //      wavefronts already have their first weights in flight.
 //   2. Items.  The output channels are cut into groups of TG tiles of 16
-//      channels (TG = 1, 2 or 4: wide_tiles_per_group) and K into items of
+//      channels (TG = 1, 2, 4 or 6: wide_tiles_per_group) and K into items of
 //      256 positions (4 chunks of 64, one per streamer wavefront).  The
 //      (group, item) sequence, group major, is divided into G equal
 //      contiguous ranges, one per workgroup (stream-K): every workgroup
 //      streams the same number of weight bytes whatever N and K are.  G is
 //      the number of groups where they fit the device and K <= 8192 (each
 //      workgroup owns one whole group), else one workgroup per compute unit.
+//      With the token-block split (wide_token_split: groups of 2 or 3 tiles
+//      from 64 tokens), each range is run by two workgroups of one XCD, each
+//      on half of the token blocks.
 //   3. Per item, each of the 4 streamer wavefronts loads one 1 KB chunk of
 //      each of the group's TG tiles into registers and, right behind them, the
 //      activation codes of that K chunk -- one 16 x 64 fragment per 16-token
