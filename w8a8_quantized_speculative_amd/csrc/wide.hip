@@ -102,11 +102,16 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 // code slots (4 streamers x NBUF items x F MB KB) and the partial-sum area
 // (2 x 4 x MB KB) stay within 150 KB of LDS, and the loads in flight per
 // wavefront ((NBUF - 1) items of TG + F MB, plus one item's F MB code loads)
-// within what the 6-bit vmcnt counter can wait for.  At most 8; groups of 6
-// tiles keep 2 items in flight, since their 6 x MB accumulators leave no
-// registers for more.
+// within what the 6-bit vmcnt counter can wait for.  4 items with INT8
+// weights and 2 with 4-bit ones (whose items carry twice the code fragments):
+// measured against 8 items, QKV, O and down at 96 tokens 16.0, 13.3, 25.6 ->
+// 15.0, 12.6, 24.9 us, at 48 tokens 13.3, 11.6, 20.2 -> 13.1, 11.3, 19.8, and
+// with 4-bit weights at 96 tokens 13.8, 12.0 -> 12.4, 11.2 (2 or 3 items
+// were slower with INT8 weights, 6 in between).  Groups of 6 tiles keep 2
+// items in flight: their 6 x MB accumulators leave no registers for more (3
+// or 4, where they fit, measured ~1 us slower on gate_up).
 constexpr int wide_nbuf(int MB, int TG, int F = 1) {
-  int nb = TG > kMaxTG ? 2 : 8;
+  int nb = TG > kMaxTG || F == 2 ? 2 : 4;
   while (nb > 2 && (kS * nb * F * MB + 2 * kS * MB > 150 || (nb - 1) * (TG + F * MB) + F * MB > 63))
     --nb;
   return nb;
