@@ -218,7 +218,7 @@ def test_w4_argument_errors_and_sizes(L):
     assert name(64, 2048, 4096) == "w4a8_linear_wide_split_kernel<2, 2>"
     assert name(96, 6144, 4096) == "w4a8_linear_wide_split_kernel<3, 3>"   # triples from 96 tokens
     assert name(64, 6144, 4096) == "w4a8_linear_wide_kernel<4, 2>"
-    assert name(96, 24576, 4096) == "w4a8_linear_wide_kernel<6, 4>"
+    assert name(96, 24576, 4096) == "w4a8_linear_wide_kernel<6, 6>"
     assert name(6, 64, 16384) == "w4a8_linear_wide_kernel<1, 2>"
     assert name(97, 16, 128) == "" and name(6, 16, 192) == ""
 

@@ -139,7 +139,7 @@ static_assert(wide_fits<1, 1>() && wide_fits<2, 1>() && wide_fits<3, 1>() && wid
                   wide_fits<8, 1>() && wide_fits<1, 2>() && wide_fits<2, 2>() &&
                   wide_fits<3, 2>() && wide_fits<4, 2>() && wide_fits<5, 2>() && wide_fits<6, 2>(),
               "LDS budget, and in-flight loads within the 6-bit vmcnt");
-// groups of 6 tiles: 3 to 6 token blocks (3 to 5 with 4-bit weights)
+// groups of 6 tiles: 3 to 6 token blocks
 template <int MB, int F>
 constexpr bool wide_fits_tg6() {
   return Wide<MB, kWideTG, F>::LDS <= 150 * 1024 &&
@@ -147,7 +147,7 @@ constexpr bool wide_fits_tg6() {
 }
 static_assert(wide_fits_tg6<3, 1>() && wide_fits_tg6<4, 1>() && wide_fits_tg6<5, 1>() &&
                   wide_fits_tg6<6, 1>() && wide_fits_tg6<3, 2>() && wide_fits_tg6<4, 2>() &&
-                  wide_fits_tg6<5, 2>(),
+                  wide_fits_tg6<5, 2>() && wide_fits_tg6<6, 2>(),
               "groups of 6 tiles: LDS budget and in-flight loads");
 
 // LDS synchronisation words (int indices into the SYNC area)
@@ -368,6 +368,29 @@ __device__ __forceinline__ void wide_streamer(const int8_t* __restrict__ wq,
           case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * F * MB + 6 * TG)); break;
           default: __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * F * MB + 7 * TG)); break;
         }
+        if constexpr (WB == 4 && TG > kMaxTG) {
+          // groups of 6 tiles with 4-bit weights: chunk 2c's codes first, then
+          // chunk 2c + 1's, so only half of the item's code fragments are in
+          // registers at a time
+          const v4u hm = {0xF0F0F0F0u, 0xF0F0F0F0u, 0xF0F0F0F0u, 0xF0F0F0F0u};
+#pragma unroll
+          for (int f = 0; f < 2; ++f) {
+            v4i bq[MB];
+#pragma unroll
+            for (int tb = 0; tb < MB; ++tb)
+              bq[tb] = lds_read16_asm(slot_addr + ((bb * F + f) * MB + tb) * 1024);
+            lds_wait_reads();
+#pragma unroll
+            for (int tb = 0; tb < MB; ++tb) asm volatile("" : "+v"(bq[tb]));
+#pragma unroll
+            for (int tt = 0; tt < TG; ++tt) {
+              const v4u v = __builtin_bit_cast(v4u, a[bb][tt]);
+              const v4i q = __builtin_bit_cast(v4i, f == 0 ? ((v << 4u) & hm) : (v & hm));
+#pragma unroll
+              for (int tb = 0; tb < MB; ++tb) acc[tt][tb] = mfma_i8_16x16x64(q, bq[tb], acc[tt][tb]);
+            }
+          }
+        } else {
         v4i bf[F * MB];
 #pragma unroll
         for (int i = 0; i < F * MB; ++i)
@@ -395,6 +418,7 @@ __device__ __forceinline__ void wide_streamer(const int8_t* __restrict__ wq,
             for (int tb = 0; tb < MB; ++tb)
               acc[tt][tb] = mfma_i8_16x16x64(a[bb][tt], bf[tb], acc[tt][tb]);
           }
+        }
         }
       }
       // item j + NB into buffer bb and slot bb (slot bb's codes are in
@@ -896,15 +920,15 @@ static_assert(wide_lds_of(6, 4) == Wide<6, 4>::LDS && wide_lds_of(3, 1) == Wide<
 //   * K > 8192 (down): pairs of tiles on every CU, each K range split in two
 //     (down at 48 and 96 tokens: 20.0 and 26.0 against 21.3 and 29.5 for
 //     single tiles and 24.7 and 33.1 for one pair per workgroup);
-//   * beyond 4 tiles per CU from 48 to 96 tokens (3 to 6 token blocks, 3 to 5
-//     with 4-bit weights, whose 6-block streamer would spill): groups of 6
-//     tiles, one per CU for gate_up (no K range split), with two items in
-//     flight per streamer: gate_up at 48, 64, 80 and 96 tokens 26.0, 28.5,
-//     31.3, 32.8 -> 22.7, 24.2, 26.6, 27.9; the LM head at 64 and 96 tokens
-//     131.1 -> 126.1 and 152.5 -> 148.6; 4-bit gate_up at 48 tokens 20.6 ->
-//     16.9, its LM head 78.9 -> 74.6;
-//   * beyond (the LM head above 96 tokens, down at 128 tokens, 4-bit at 96
-//     tokens): groups of 4 on every CU.
+//   * beyond 4 tiles per CU from 48 to 96 tokens (3 to 6 token blocks):
+//     groups of 6 tiles, one per CU for gate_up (no K range split), with two
+//     items in flight per streamer: gate_up at 48, 64, 80 and 96 tokens 26.0,
+//     28.5, 31.3, 32.8 -> 22.7, 24.2, 26.6, 27.9; the LM head at 64 and 96
+//     tokens 131.1 -> 126.1 and 152.5 -> 148.6; 4-bit gate_up at 48 and 96
+//     tokens 20.6 -> 16.9 and 27.7 -> 23.9, its LM head 78.9 -> 74.6 and
+//     117.5 -> 108.5;
+//   * beyond (the LM head above 96 tokens, down at 128 tokens): groups of 4
+//     on every CU.
 // Sharing each fragment among 16 tiles through LDS no longer paid once
 // fragments were contiguous: 164 against 163 us on the 4096 -> 151936 LM head
 // at 96 tokens, 206 against 183 at 128.
@@ -950,7 +974,7 @@ int wide_tiles_per_group(int64_t M, int64_t N, int64_t K, int grid, int wbits) {
   if (tiles <= 2 * g) return 2;
   if (tiles < 4 * g) return M <= 64 ? 2 : kMaxTG;
   if (tiles <= 8 * g && M <= 32) return 2;
-  if (tiles > 4 * g && mb >= 3 && mb <= (wbits == 4 ? 5 : 6)) return kWideTG;
+  if (tiles > 4 * g && mb >= 3 && mb <= 6) return kWideTG;
   return kMaxTG;
 }
 
@@ -1051,6 +1075,7 @@ hipError_t launch_wide(const WidePlan& p, const uint16_t* x, const float* s, con
         case 3: return launch_wide_mb<3, kWideTG, 4>(QUASAR_WIDE_LAUNCH_ARGS);
         case 4: return launch_wide_mb<4, kWideTG, 4>(QUASAR_WIDE_LAUNCH_ARGS);
         case 5: return launch_wide_mb<5, kWideTG, 4>(QUASAR_WIDE_LAUNCH_ARGS);
+        case 6: return launch_wide_mb<6, kWideTG, 4>(QUASAR_WIDE_LAUNCH_ARGS);
         default: return hipErrorInvalidValue;
       }
     }
