@@ -218,6 +218,7 @@ def test_w4_argument_errors_and_sizes(L):
     assert name(64, 2048, 4096) == "w4a8_linear_wide_split_kernel<2, 2>"
     assert name(96, 6144, 4096) == "w4a8_linear_wide_split_kernel<3, 3>"   # triples from 96 tokens
     assert name(64, 6144, 4096) == "w4a8_linear_wide_kernel<4, 2>"
+    assert name(16, 24576, 4096) == "w4a8_linear_wide_kernel<1, 6>"     # 4-bit: groups of 6 below 48 tokens too
     assert name(96, 24576, 4096) == "w4a8_linear_wide_kernel<6, 6>"
     assert name(6, 64, 16384) == "w4a8_linear_wide_kernel<1, 2>"
     assert name(97, 16, 128) == "" and name(6, 16, 192) == ""
@@ -272,6 +273,8 @@ def test_kernel_name_names_the_launch_plan(L):
     assert name(64, 16384, 4096) == "w8a8_linear_wide_kernel<4, 4>"     # 1024 tiles
     assert name(32, 16384, 4096) == "w8a8_linear_wide_kernel<2, 2>"     # <= 2048 tiles, <= 32 tokens
     assert name(16, 24576, 4096) == "w8a8_linear_wide_kernel<1, 2>"
+    assert name(32, 24576, 4096) == "w8a8_linear_wide_kernel<2, 6>"     # 32 tokens: groups of 6
+    assert name(32, 151936, 4096) == "w8a8_linear_wide_kernel<2, 4>"
     assert name(48, 24576, 4096) == "w8a8_linear_wide_kernel<3, 6>"
     assert name(112, 24576, 4096) == "w8a8_linear_wide_kernel<7, 4>"    # 7 blocks: groups of 4
     assert name(16, 49152, 4096) == "w8a8_linear_wide_kernel<1, 4>"     # 3072 tiles

@@ -101,6 +101,7 @@ RAGGED = [
     # group per workgroup, and groups split across workgroups (partial sums
     # of 6 tiles), ragged N and K
     (70, 17000, 1040), (48, 20000, 512), (96, 30000, 256), (64, 16400, 2112), (81, 24576, 4160),
+    (32, 17000, 1040), (20, 24576, 512),
 ]
 
 

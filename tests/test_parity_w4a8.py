@@ -62,7 +62,8 @@ SHAPES = [
     # groups of 3 tiles split over two workgroups
     (96, 6100, 2048), (90, 6130, 4224),
     # groups of 6 tiles (3 to 5 token blocks): one per workgroup and split
-    (48, 20000, 512), (80, 17000, 1152), (40, 30000, 256),
+    (48, 20000, 512), (80, 17000, 1152), (40, 30000, 256), (16, 17000, 512), (30, 20000, 1152),
+    (96, 24576, 1024),
 ]
 
 

@@ -139,13 +139,14 @@ static_assert(wide_fits<1, 1>() && wide_fits<2, 1>() && wide_fits<3, 1>() && wid
                   wide_fits<8, 1>() && wide_fits<1, 2>() && wide_fits<2, 2>() &&
                   wide_fits<3, 2>() && wide_fits<4, 2>() && wide_fits<5, 2>() && wide_fits<6, 2>(),
               "LDS budget, and in-flight loads within the 6-bit vmcnt");
-// groups of 6 tiles: 3 to 6 token blocks
+// groups of 6 tiles: 1 to 6 token blocks
 template <int MB, int F>
 constexpr bool wide_fits_tg6() {
   return Wide<MB, kWideTG, F>::LDS <= 150 * 1024 &&
          (Wide<MB, kWideTG, F>::NBUF - 1) * (kWideTG + F * MB) + F * MB <= 63;
 }
-static_assert(wide_fits_tg6<3, 1>() && wide_fits_tg6<4, 1>() && wide_fits_tg6<5, 1>() &&
+static_assert(wide_fits_tg6<2, 1>() && wide_fits_tg6<1, 2>() && wide_fits_tg6<2, 2>() &&
+                  wide_fits_tg6<3, 1>() && wide_fits_tg6<4, 1>() && wide_fits_tg6<5, 1>() &&
                   wide_fits_tg6<6, 1>() && wide_fits_tg6<3, 2>() && wide_fits_tg6<4, 2>() &&
                   wide_fits_tg6<5, 2>() && wide_fits_tg6<6, 2>(),
               "groups of 6 tiles: LDS budget and in-flight loads");
@@ -927,8 +928,12 @@ static_assert(wide_lds_of(6, 4) == Wide<6, 4>::LDS && wide_lds_of(3, 1) == Wide<
 //     tokens 131.1 -> 126.1 and 152.5 -> 148.6; 4-bit gate_up at 48 and 96
 //     tokens 20.6 -> 16.9 and 27.7 -> 23.9, its LM head 78.9 -> 74.6 and
 //     117.5 -> 108.5;
-//   * beyond (the LM head above 96 tokens, down at 128 tokens): groups of 4
-//     on every CU.
+//     below 48 tokens the same with 4-bit weights (gate_up at 16 and 32 tokens
+//     16.5 -> 15.1 and 20.1 -> 16.2) and at 32 tokens up to 8 tiles per CU
+//     with INT8 (gate_up 23.7 -> 22.6; at 16 tokens pairs stay faster, 20.3
+//     against 21.7);
+//   * beyond (the LM head above 96 tokens or with INT8 below 48 tokens, down
+//     at 128 tokens): groups of 4 on every CU.
 // Sharing each fragment among 16 tiles through LDS no longer paid once
 // fragments were contiguous: 164 against 163 us on the 4096 -> 151936 LM head
 // at 96 tokens, 206 against 183 at 128.
@@ -973,8 +978,9 @@ int wide_tiles_per_group(int64_t M, int64_t N, int64_t K, int grid, int wbits) {
   if (tiles <= g) return 1;
   if (tiles <= 2 * g) return 2;
   if (tiles < 4 * g) return M <= 64 ? 2 : kMaxTG;
+  if (tiles > 4 * g && mb <= 6 && (mb >= 3 || wbits == 4 || (mb == 2 && tiles <= 8 * g)))
+    return kWideTG;
   if (tiles <= 8 * g && M <= 32) return 2;
-  if (tiles > 4 * g && mb >= 3 && mb <= 6) return kWideTG;
   return kMaxTG;
 }
 
@@ -1072,6 +1078,8 @@ hipError_t launch_wide(const WidePlan& p, const uint16_t* x, const float* s, con
                                        wc, st);
     if (p.tg == kWideTG) {
       switch (p.mbl) {
+        case 1: return launch_wide_mb<1, kWideTG, 4>(QUASAR_WIDE_LAUNCH_ARGS);
+        case 2: return launch_wide_mb<2, kWideTG, 4>(QUASAR_WIDE_LAUNCH_ARGS);
         case 3: return launch_wide_mb<3, kWideTG, 4>(QUASAR_WIDE_LAUNCH_ARGS);
         case 4: return launch_wide_mb<4, kWideTG, 4>(QUASAR_WIDE_LAUNCH_ARGS);
         case 5: return launch_wide_mb<5, kWideTG, 4>(QUASAR_WIDE_LAUNCH_ARGS);
@@ -1090,6 +1098,7 @@ hipError_t launch_wide(const WidePlan& p, const uint16_t* x, const float* s, con
                                      st);
   if (p.tg == kWideTG) {
     switch (p.mbl) {
+      case 2: return launch_wide_mb<2, kWideTG, 8>(QUASAR_WIDE_LAUNCH_ARGS);
       case 3: return launch_wide_mb<3, kWideTG, 8>(QUASAR_WIDE_LAUNCH_ARGS);
       case 4: return launch_wide_mb<4, kWideTG, 8>(QUASAR_WIDE_LAUNCH_ARGS);
       case 5: return launch_wide_mb<5, kWideTG, 8>(QUASAR_WIDE_LAUNCH_ARGS);
