@@ -130,3 +130,14 @@ def test_stats_summary_takes_the_step_grid_from_the_trace(tmp_path):
     assert res["rocprof_step_config_avg_us"] == pytest.approx(11.0)
     md = open(tmp_path / "o.md").read()
     assert "the 10 of its 13 dispatches" in md and "11.00 us" in md
+
+
+def test_kernel_launch_times_cover_every_section():
+    line = {"kernels": [{"kernel": "a<6>", "launch_avg_us": 10.0}],
+            "window_m48": {"kernels": [{"kernel": "b<3>", "launch_avg_us": 20.0}],
+                           "w4a8_variant": {"kernels": [{"kernel": "c<3>", "launch_avg_us": 15.0}]}},
+            "w4a8_variant": {"kernels": [{"kernel": "d<6>", "launch_avg_us": 8.0}]},
+            "roofline": {"kernel": "a<6>"}}
+    t = profiling.kernel_launch_times(line)
+    assert {k: v["launch_avg_us"] for k, v in t.items()} == {"a<6>": 10.0, "b<3>": 20.0,
+                                                               "c<3>": 15.0, "d<6>": 8.0}

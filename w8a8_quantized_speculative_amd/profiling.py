@@ -345,13 +345,35 @@ SIMDS = 1024        # MI355X: 256 compute units x 4 SIMDs
 PEAK_INT8_TOPS = 5000.0
 
 
-def summarize_mfma(pmc_csv: str, bench_json: str, out_md: str, command: str) -> dict:
+def kernel_launch_times(bench: dict) -> dict:
+    """kernel name -> its entry (launch_avg_us, algorithmic ops...) from every
+    section of a bench line that lists kernels: the step's, each window's and
+    each 4-bit variant's."""
+    out = {}
+
+    def walk(d):
+        if isinstance(d, dict):
+            for k in d.get("kernels", []) if isinstance(d.get("kernels"), list) else []:
+                if isinstance(k, dict) and "kernel" in k:
+                    out.setdefault(k["kernel"], k)
+            for v in d.values():
+                if isinstance(v, dict):
+                    walk(v)
+    walk(bench)
+    return out
+
+
+def summarize_mfma(pmc_csv: str, bench_json: str, out_md: str, command: str,
+                   timing_json: str = None) -> dict:
+    """MFMA counters per kernel.  Launch times come from `timing_json` (a bench
+    line of a run without counters) when given: the counter runs serialize the
+    dispatches and time each launch several times longer."""
     bench = _bench_line(bench_json)
     mops = _counter_means(pmc_csv, "SQ_INSTS_VALU_MFMA_MOPS_I8")
     insts = _counter_means(pmc_csv, "SQ_INSTS_VALU_MFMA_I8")
     busy = _counter_means(pmc_csv, "SQ_VALU_MFMA_BUSY_CYCLES")
     active = _counter_means(pmc_csv, "GRBM_GUI_ACTIVE")
-    launch_us = {k["kernel"]: k for k in bench.get("kernels", [])}
+    launch_us = kernel_launch_times(_bench_line(timing_json) if timing_json else bench)
     rows, res = [], {}
     for name in sorted(mops, key=lambda n: -mops[n][0] * mops[n][1]):
         if not (name.startswith("w8a8_linear") or name.startswith("w4a8_linear")):
@@ -380,8 +402,9 @@ def summarize_mfma(pmc_csv: str, bench_json: str, out_md: str, command: str) -> 
            "shapes).  Executed ops = SQ_INSTS_VALU_MFMA_MOPS_I8 x 512; they include the MFMA "
            "work on padding (token columns past M, channels past N), so they exceed the "
            "algorithmic 2*M*N*K.  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x "
-           f"{SIMDS} SIMDs).  TOP/s = executed ops / the bench's mean launch time "
-           f"(dense INT8 peak {PEAK_INT8_TOPS:.0f} TOP/s).", "",
+           f"{SIMDS} SIMDs).  TOP/s = executed ops / the kernel's mean launch time in "
+           + ("a bench run without counters" if timing_json else "the same run")
+           + f" (dense INT8 peak {PEAK_INT8_TOPS:.0f} TOP/s).", "",
            "| kernel | dispatches | MFMA insts | executed INT8 ops | ops/inst | MFMA busy | "
            "executed TOP/s | algorithmic ops/launch (step mix) |",
            "|---|---:|---:|---:|---:|---:|---:|---:|"] + rows + [""]
@@ -413,10 +436,12 @@ def main():
     c.add_argument("bench_json")
     c.add_argument("out_md")
     c.add_argument("--command", required=True)
+    c.add_argument("--timing", default=None,
+                   help="bench line of a run without counters, for the launch times")
     args = ap.parse_args()
     if args.cmd == "mfma":
         print(json.dumps(summarize_mfma(args.pmc_csv, args.bench_json, args.out_md,
-                                        args.command)))
+                                        args.command, args.timing)))
     elif args.cmd == "stats":
         print(json.dumps(summarize_stats(args.stats_csv, args.bench_json, args.out_md,
                                          args.command, args.trace)))
