@@ -389,25 +389,32 @@ def summarize_mfma(pmc_csv: str, bench_json: str, out_md: str, command: str,
         res[name] = {"dispatches": mops[name][1], "mfma_insts_per_dispatch": round(ni),
                      "executed_int8_ops_per_dispatch": round(ops),
                      "ops_per_inst": round(ops / ni, 1) if ni else None,
-                     "mfma_busy_frac": round(util, 4),
+                     "mfma_busy_frac_counter_run": round(util, 4),
                      "executed_tops": round(tops, 2) if tops else None,
+                     "executed_frac_of_peak": round(tops / PEAK_INT8_TOPS, 4) if tops else None,
                      "algorithmic_int8_ops_per_launch_in_step": alg}
         rows.append(f"| `{_cell(name)}` | {mops[name][1]} | {ni:.0f} | {ops:.3e} | "
                     f"{(ops / ni) if ni else 0:.0f} | {100 * util:.2f}% | "
-                    f"{(f'{tops:.1f}') if tops else '-'} | {(f'{alg:.3e}') if alg else '-'} |")
+                    f"{(f'{tops:.1f}') if tops else '-'} | "
+                    f"{(f'{100 * tops / PEAK_INT8_TOPS:.1f}%') if tops else '-'} | "
+                    f"{(f'{alg:.3e}') if alg else '-'} |")
     out = ["# INT8 MFMA use (rocprofv3 PMC): " + bench["config"]["workload"], "",
            "Profiled command (paths relative to the repository root of the GPU run):", "",
            "```", command, "```", "", "Summary written by:", "", "```", _self_command(), "```", "",
            "Per dispatch, mean over every launch of the kernel in the run (the bench's mix of "
            "shapes).  Executed ops = SQ_INSTS_VALU_MFMA_MOPS_I8 x 512; they include the MFMA "
            "work on padding (token columns past M, channels past N), so they exceed the "
-           "algorithmic 2*M*N*K.  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x "
-           f"{SIMDS} SIMDs).  TOP/s = executed ops / the kernel's mean launch time in "
+           "algorithmic 2*M*N*K.  TOP/s = executed ops / the kernel's mean launch time in "
            + ("a bench run without counters" if timing_json else "the same run")
-           + f" (dense INT8 peak {PEAK_INT8_TOPS:.0f} TOP/s).", "",
-           "| kernel | dispatches | MFMA insts | executed INT8 ops | ops/inst | MFMA busy | "
-           "executed TOP/s | algorithmic ops/launch (step mix) |",
-           "|---|---:|---:|---:|---:|---:|---:|---:|"] + rows + [""]
+           + f", and its share of the dense INT8 peak ({PEAK_INT8_TOPS:.0f} TOP/s) is the "
+           "matrix units' use.  MFMA busy (counter run) = SQ_VALU_MFMA_BUSY_CYCLES / "
+           f"(GRBM_GUI_ACTIVE x {SIMDS} SIMDs) during the counter run, which serializes the "
+           "dispatches and stretches each several times, so it understates the use by that "
+           "factor.", "",
+           "| kernel | dispatches | MFMA insts | executed INT8 ops | ops/inst | MFMA busy "
+           "(counter run) | executed TOP/s | share of INT8 peak | algorithmic ops/launch "
+           "(step mix) |",
+           "|---|---:|---:|---:|---:|---:|---:|---:|---:|"] + rows + [""]
     with open(out_md, "w") as f:
         f.write("\n".join(out))
     return res
