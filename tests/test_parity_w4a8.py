@@ -47,6 +47,8 @@ SHAPES = [
     (1, 16, 128), (6, 1000, 1024), (6, 4096, 256), (2, 7, 384), (8, 300, 4096), (3, 40, 6144),
     (7, 100, 8064), (8, 64, 10112), (4, 520, 12288), (6, 9000, 1024), (5, 33, 12288),
     (6, 16400, 512), (1, 143000, 128),
+    # K past 8192 with three 4-bit buffers: 2 and 3 tiles per workgroup, ragged N
+    (6, 9000, 12288), (3, 5000, 9216), (8, 4100, 12288),
     # wide windows (and K > 12288): the wide kernel with 4-bit weight blocks --
     # every token-block count it takes (1..6), an odd number of chunk pairs
     # (a last item with fewer than 4 pairs), single tiles, tile pairs (K > 8192;

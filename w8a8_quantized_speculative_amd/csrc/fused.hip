@@ -510,9 +510,13 @@ __global__ __launch_bounds__(64 * (S + (NPH == 2 ? 4 : 8))) void w8a8_linear_fus
 // helpers shift the tile's total right by 4.
 // Streamer w's phase ph of a tile is packed chunks ph * 8S + 8w .. + 7 (an 8 KB
 // run per wavefront, 4096 K positions per phase for the 4 streamers).  Units
-// u = tile * NPH4 + phase alternate between two register buffers, issued two
-// units ahead (across tiles when a tile has one phase): as many loads in
-// flight per compute unit as the INT8 streamer, i.e. twice its K span.
+// u = tile * NPH4 + phase rotate through NB register buffers, issued NB units
+// ahead (across tiles when a tile has one phase).  NB = 2 up to K = 8192; at
+// K > 8192 NB = 3 requests the whole 96 KB tile before the longer quantization
+// prologue ends (a 4096 x 12288 linear at 6 tokens: 9.9 -> 9.2 us per launch;
+// 8 tokens within 0.15 us either way).  Issuing the third buffer only once
+// the activations had landed kept half of that gain, and a fourth INT8
+// buffer at K > 8192 (128 of the 192 KB tile requested) was 0.9 us slower.
 // ---------------------------------------------------------------------------
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
@@ -522,7 +526,9 @@ __device__ __forceinline__ void streamer_w4(const int8_t* __restrict__ wq4,
                                             int first, int T, int wave, int lane,
                                             const int8_t* codes, int Ks, int32_t* red, float* wsl,
                                             const int* ready, const WaitCtl& wc) {
-  constexpr int NB = 2;
+  // three buffers (the whole 96 KB tile) at K > 8192: the stream then waits
+  // for the longer quantization prologue with all of its tile requested
+  constexpr int NB = NPH4 == 3 ? 3 : 2;
   const int r = lane & 15, g = lane >> 4;
   const int ncp = K >> 7;  // 128-wide pairs of chunks
   const int nch = K >> 6;
@@ -549,8 +555,8 @@ __device__ __forceinline__ void streamer_w4(const int8_t* __restrict__ wq4,
   };
 
   __syncthreads();  // (1) the helpers' activation loads are queued first
-  issue(0, 0);
-  issue(1, 1);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) issue(b, b);
   __builtin_amdgcn_sched_barrier(0);
 
   const int8_t* brow = codes + (r < MT ? r : MT - 1) * Ks + g * 16;
