@@ -148,21 +148,20 @@ __device__ __forceinline__ void streamer(const int8_t* __restrict__ wq,
   v4i a[NBUF][kPH];
   float wsv[NBUF];  // wavefront 0, lanes 0..15: weight scales if the buffer holds a last phase
 
-  // One scalar buffer descriptor per 1 KB chunk (size 0 past K or past the last
-  // tile, which reads zeros without touching memory) and one shared vector
-  // offset: no per-chunk vector registers.
+  // One scalar buffer descriptor per tile (size 0 past the last tile) and the
+  // chunk in the vector offset: chunks past K fall outside the tile's range
+  // and read zeros without touching memory.  (A descriptor per chunk needed
+  // 32 scalar registers per issue, and at K > 4096 the compiler spilled
+  // scalars into vector lanes.)
   const int voff = lane * 16;
   auto issue = [&](int b, int tile, int ph) {  // tile < 0: nothing left, read zeros
     const bool valid = tile >= 0;
     const int tl = valid ? tile : 0;
-    const int8_t* tbase = wq + (size_t)tl * nch * 1024;
+    const buffer_rsrc rs =
+        make_rsrc(wq + (size_t)tl * nch * 1024, valid ? (uint32_t)nch * 1024u : 0u);
+    const int pbase = voff + (cw + ph * (S * kPH)) * 1024;
 #pragma unroll
-    for (int j = 0; j < kPH; ++j) {
-      const int c = cw + ph * (S * kPH) + j;
-      const buffer_rsrc rs =
-          make_rsrc(tbase + (size_t)c * 1024, (valid && c < nch) ? 1024u : 0u);
-      a[b][j] = load16<kNonTemporal>(rs, voff);
-    }
+    for (int j = 0; j < kPH; ++j) a[b][j] = load16<kNonTemporal>(rs, pbase + j * 1024);
     const int rows = (valid && ph == NPH - 1) ? min(16, N - tl * 16) : 0;
     const buffer_rsrc ss = make_rsrc(wscale + (size_t)tl * 16, (uint32_t)rows * 4u);
     wsv[b] = __int_as_float(load4(ss, (wave == 0 && lane < 16) ? lane * 4 : kOutOfRange));
