@@ -605,12 +605,17 @@ __device__ __forceinline__ void streamer_w4(const int8_t* __restrict__ wq4,
 }
 
 template <int MT, int S, int NPH4>
-__global__ __launch_bounds__(64 * (S + (NPH4 == 1 ? 4 : 8))) void w4a8_linear_fused_kernel(
+__global__ __launch_bounds__(64 * (S + 8)) void w4a8_linear_fused_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ s, const int8_t* __restrict__ wq4,
     const float* __restrict__ wscale, int M, int N, int K, int tq, int tr, int G,
     uint16_t* __restrict__ y, int32_t* __restrict__ acc_out, WaitCtl wc) {
   using Var = Variant<NPH4 == 1 ? 0 : (NPH4 == 2 ? 1 : 2)>;
   static_assert(Var::S == S && Var::NPH == 2 * NPH4, "variant");
+  // eight helper wavefronts at every K: the 4-bit stream is half as long, so
+  // the codes, not the weights, end the small linears' prologue
+  constexpr int kW4Helpers = 8;
+  constexpr int kW4Up = NPH4 == 1 ? 1 : Var::UP;
+  static_assert(kW4Helpers * 64 * kW4Up * 8 >= Var::KMAX, "helpers cover K");
   extern __shared__ __align__(16) char smem[];
   const Smem L = smem_layout(K, MT, S);
   int8_t* codes = reinterpret_cast<int8_t*>(smem + L.codes);
@@ -632,10 +637,10 @@ __global__ __launch_bounds__(64 * (S + (NPH4 == 1 ? 4 : 8))) void w4a8_linear_fu
   const int first = b * tq + (int)((unsigned int)(b * tr) / (unsigned int)G);
   const int T = (b + 1) * tq + (int)((unsigned int)((b + 1) * tr) / (unsigned int)G) - first;
   if (wave < S) {
-    streamer_w4<MT, S, NPH4, Var::NH>(wq4, wscale, N, K, first, T, wave, lane, codes, Ks, red,
-                                      wsl, ready, wc);
+    streamer_w4<MT, S, NPH4, kW4Helpers>(wq4, wscale, N, K, first, T, wave, lane, codes, Ks, red,
+                                         wsl, ready, wc);
   } else {
-    helper<MT, S, Var::NH, Var::UP, 4>(x, s, M, N, K, first, T, tid - 64 * S, wave - S, lane,
+    helper<MT, S, kW4Helpers, kW4Up, 4>(x, s, M, N, K, first, T, tid - 64 * S, wave - S, lane,
                                        codes, Ks, red, wsl, amax_part, qp, cnt, ready, y, acc_out,
                                        AcceptPartials{nullptr, nullptr, nullptr, 0.0f}, G, 0, wc);
   }
@@ -653,7 +658,7 @@ hipError_t launch_w4(const FusedPlan& p, const uint16_t* x, const float* s, cons
   if (attr != hipSuccess) return attr;
   const WaitCtl wc = wait_ctl_for_current_device();
   if (!wc.status) return hipErrorInvalidSymbol;
-  kernel<<<dim3(p.grid), dim3(64 * (S + (NPH4 == 1 ? 4 : 8))), p.lds, st>>>(
+  kernel<<<dim3(p.grid), dim3(64 * (S + 8)), p.lds, st>>>(
       x, s, wq4, w_scale, (int)p.M, (int)p.N, (int)p.K, p.tiles / p.grid, p.tiles % p.grid,
       p.grid, y, acc_out, wc);
   return hipGetLastError();
