@@ -75,6 +75,11 @@ constexpr int kMaxHelpers = 8;
 //   0        <= 4096  4   2   2     4   2    8     64 KB (the whole tile)
 //   1        <= 8192  4   4   2     8   2   12     64 KB
 //   2        <= 12288 4   6   3     8   3   12     96 KB
+// At K <= 4096 with 6 to 8 token rows the quantization outlasts the tile's
+// arrival, so that variant runs 8 helpers with one piece each (12 waves):
+// per launch at 6 tokens the LM head -2.8 us, gate_up -0.15, O -0.07, QKV
+// +0.09; at 7 and 8 tokens O -0.5 and the LM head -2.5.  (At 6 tokens 8
+// helpers once measured no change; the stream has changed since.)
 // NBUF divides NPH, so phase p of every tile uses buffer p % NBUF.
 template <int V>
 struct Variant {
@@ -84,10 +89,15 @@ struct Variant {
   static constexpr int NH = V == 0 ? 4 : 8;
   static constexpr int UP = V == 2 ? 3 : 2;
   static constexpr int KMAX = S * NPH * kPH * 64;
-  static constexpr int WAVES = S + NH;
+  // helper wavefronts, pieces per thread and row, and wavefronts at MT rows
+  static constexpr int helpers(int MT) { return V == 0 && MT >= 6 ? 8 : NH; }
+  static constexpr int pieces(int MT) { return V == 0 && MT >= 6 ? 1 : UP; }
+  static constexpr int waves(int MT) { return S + helpers(MT); }
 };
 static_assert(Variant<0>::KMAX == 4096 && Variant<1>::KMAX == 8192 && Variant<2>::KMAX == 12288,
               "variant K ranges");
+static_assert(Variant<0>::helpers(8) * 64 * Variant<0>::pieces(8) * 8 >= Variant<0>::KMAX,
+              "helpers cover K at 6 or more rows");
 static_assert(Variant<0>::NH * 64 * Variant<0>::UP * 8 >= Variant<0>::KMAX &&
                   Variant<1>::NH * 64 * Variant<1>::UP * 8 >= Variant<1>::KMAX &&
                   Variant<2>::NH * 64 * Variant<2>::UP * 8 >= Variant<2>::KMAX,
@@ -459,7 +469,8 @@ __device__ __forceinline__ void helper(const uint16_t* __restrict__ x, const flo
 // is rewritten two tiles later, after the helpers have passed the barrier of
 // the tile in between, i.e. after they finished reading it.
 template <int MT, int S, int NPH>
-__global__ __launch_bounds__(64 * (S + (NPH == 2 ? 4 : 8))) void w8a8_linear_fused_kernel(
+__global__ __launch_bounds__(64 * Variant<NPH == 2 ? 0 : (NPH == 4 ? 1 : 2)>::waves(MT)) void
+w8a8_linear_fused_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ s, const int8_t* __restrict__ wq,
     const float* __restrict__ wscale, int M, int N, int K, int tq, int tr, int G,
     uint16_t* __restrict__ y, int32_t* __restrict__ acc_out, AcceptPartials ap, int swiglu,
@@ -489,12 +500,12 @@ __global__ __launch_bounds__(64 * (S + (NPH == 2 ? 4 : 8))) void w8a8_linear_fus
   const int first = b * tq + (int)((unsigned int)(b * tr) / (unsigned int)G);
   const int T = (b + 1) * tq + (int)((unsigned int)((b + 1) * tr) / (unsigned int)G) - first;
   if (wave < S) {
-    streamer<MT, S, NPH, Var::NBUF, Var::NH>(wq, wscale, N, K, first, T, wave, lane, codes, Ks,
-                                             red, wsl, ready, wc);
+    streamer<MT, S, NPH, Var::NBUF, Var::helpers(MT)>(wq, wscale, N, K, first, T, wave, lane,
+                                                      codes, Ks, red, wsl, ready, wc);
   } else {
-    helper<MT, S, Var::NH, Var::UP>(x, s, M, N, K, first, T, tid - 64 * S, wave - S, lane, codes,
-                                    Ks, red, wsl, amax_part, qp, cnt, ready, y, acc_out, ap, G,
-                                    swiglu, wc);
+    helper<MT, S, Var::helpers(MT), Var::pieces(MT)>(
+        x, s, M, N, K, first, T, tid - 64 * S, wave - S, lane, codes, Ks, red, wsl, amax_part, qp,
+        cnt, ready, y, acc_out, ap, G, swiglu, wc);
   }
 }
 
@@ -687,7 +698,7 @@ hipError_t launch_variant(const FusedPlan& p, const uint16_t* x, const float* s,
   if (attr != hipSuccess) return attr;
   const WaitCtl wc = wait_ctl_for_current_device();
   if (!wc.status) return hipErrorInvalidSymbol;
-  kernel<<<dim3(p.grid), dim3(64 * Var::WAVES), p.lds, st>>>(
+  kernel<<<dim3(p.grid), dim3(64 * Var::waves(MT)), p.lds, st>>>(
       x, s, wq, w_scale, (int)p.M, (int)p.N, (int)p.K, p.tiles / p.grid, p.tiles % p.grid, p.grid,
       y, acc_out, ap, swiglu, wc);
   return hipGetLastError();
@@ -719,8 +730,8 @@ FusedPlan plan_fused(int64_t M, int64_t N, int64_t K) {
   p.nch = (int)((K + 63) / 64);
   p.mt = M <= 2 ? 2 : (M <= 4 ? 4 : (M <= 6 ? 6 : 8));
   p.variant = K <= Variant<0>::KMAX ? 0 : (K <= Variant<1>::KMAX ? 1 : 2);
-  p.waves = p.variant == 0 ? Variant<0>::WAVES
-                           : (p.variant == 1 ? Variant<1>::WAVES : Variant<2>::WAVES);
+  p.waves = p.variant == 0 ? Variant<0>::waves(p.mt)
+                           : (p.variant == 1 ? Variant<1>::waves(p.mt) : Variant<2>::waves(p.mt));
   const int S = p.variant == 2 ? Variant<2>::S : Variant<0>::S;
   p.lds = smem_layout((int)K, p.mt, S).bytes;
   const int cap = kNumCU;  // one persistent workgroup per compute unit
