@@ -72,32 +72,26 @@ constexpr int kMaxHelpers = 8;
 // bytes a compute unit requests before the code matrix exists: a larger K
 // means a longer quantization prologue, which the requested bytes must cover.
 //   variant  K        S  NPH NBUF  NH  UP  waves  requested
-//   0        <= 4096  4   2   2     4   2    8     64 KB (the whole tile)
+//   0        <= 4096  4   2   2     8   1   12     64 KB (the whole tile)
 //   1        <= 8192  4   4   2     8   2   12     64 KB
 //   2        <= 12288 4   6   3     8   3   12     96 KB
-// At K <= 4096 with 6 to 8 token rows the quantization outlasts the tile's
-// arrival, so that variant runs 8 helpers with one piece each (12 waves):
-// per launch at 6 tokens the LM head -2.8 us, gate_up -0.15, O -0.07, QKV
-// +0.09; at 7 and 8 tokens O -0.5 and the LM head -2.5.  (At 6 tokens 8
-// helpers once measured no change; the stream has changed since.)
+// Variant 0 ran 4 helpers with 2 pieces each before; 8 with one piece measured
+// faster at every token count: per launch the LM head 2.5-3.8 us, gate_up
+// 0.15-0.25 us, QKV and O up to 0.1 us (at 7 and 8 tokens O 0.5 us), QKV at
+// 6 tokens +0.09 us.
 // NBUF divides NPH, so phase p of every tile uses buffer p % NBUF.
 template <int V>
 struct Variant {
   static constexpr int S = 4;
   static constexpr int NPH = V == 0 ? 2 : (V == 1 ? 4 : 6);
   static constexpr int NBUF = V == 2 ? 3 : 2;
-  static constexpr int NH = V == 0 ? 4 : 8;
-  static constexpr int UP = V == 2 ? 3 : 2;
+  static constexpr int NH = 8;
+  static constexpr int UP = V == 0 ? 1 : (V == 1 ? 2 : 3);
   static constexpr int KMAX = S * NPH * kPH * 64;
-  // helper wavefronts, pieces per thread and row, and wavefronts at MT rows
-  static constexpr int helpers(int MT) { return V == 0 && MT >= 6 ? 8 : NH; }
-  static constexpr int pieces(int MT) { return V == 0 && MT >= 6 ? 1 : UP; }
-  static constexpr int waves(int MT) { return S + helpers(MT); }
+  static constexpr int WAVES = S + NH;
 };
 static_assert(Variant<0>::KMAX == 4096 && Variant<1>::KMAX == 8192 && Variant<2>::KMAX == 12288,
               "variant K ranges");
-static_assert(Variant<0>::helpers(8) * 64 * Variant<0>::pieces(8) * 8 >= Variant<0>::KMAX,
-              "helpers cover K at 6 or more rows");
 static_assert(Variant<0>::NH * 64 * Variant<0>::UP * 8 >= Variant<0>::KMAX &&
                   Variant<1>::NH * 64 * Variant<1>::UP * 8 >= Variant<1>::KMAX &&
                   Variant<2>::NH * 64 * Variant<2>::UP * 8 >= Variant<2>::KMAX,
@@ -469,8 +463,7 @@ __device__ __forceinline__ void helper(const uint16_t* __restrict__ x, const flo
 // is rewritten two tiles later, after the helpers have passed the barrier of
 // the tile in between, i.e. after they finished reading it.
 template <int MT, int S, int NPH>
-__global__ __launch_bounds__(64 * Variant<NPH == 2 ? 0 : (NPH == 4 ? 1 : 2)>::waves(MT)) void
-w8a8_linear_fused_kernel(
+__global__ __launch_bounds__(64 * (S + 8)) void w8a8_linear_fused_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ s, const int8_t* __restrict__ wq,
     const float* __restrict__ wscale, int M, int N, int K, int tq, int tr, int G,
     uint16_t* __restrict__ y, int32_t* __restrict__ acc_out, AcceptPartials ap, int swiglu,
@@ -500,12 +493,12 @@ w8a8_linear_fused_kernel(
   const int first = b * tq + (int)((unsigned int)(b * tr) / (unsigned int)G);
   const int T = (b + 1) * tq + (int)((unsigned int)((b + 1) * tr) / (unsigned int)G) - first;
   if (wave < S) {
-    streamer<MT, S, NPH, Var::NBUF, Var::helpers(MT)>(wq, wscale, N, K, first, T, wave, lane,
-                                                      codes, Ks, red, wsl, ready, wc);
+    streamer<MT, S, NPH, Var::NBUF, Var::NH>(wq, wscale, N, K, first, T, wave, lane, codes, Ks,
+                                             red, wsl, ready, wc);
   } else {
-    helper<MT, S, Var::helpers(MT), Var::pieces(MT)>(
-        x, s, M, N, K, first, T, tid - 64 * S, wave - S, lane, codes, Ks, red, wsl, amax_part, qp,
-        cnt, ready, y, acc_out, ap, G, swiglu, wc);
+    helper<MT, S, Var::NH, Var::UP>(x, s, M, N, K, first, T, tid - 64 * S, wave - S, lane, codes,
+                                    Ks, red, wsl, amax_part, qp, cnt, ready, y, acc_out, ap, G,
+                                    swiglu, wc);
   }
 }
 
@@ -622,11 +615,6 @@ __global__ __launch_bounds__(64 * (S + 8)) void w4a8_linear_fused_kernel(
     uint16_t* __restrict__ y, int32_t* __restrict__ acc_out, WaitCtl wc) {
   using Var = Variant<NPH4 == 1 ? 0 : (NPH4 == 2 ? 1 : 2)>;
   static_assert(Var::S == S && Var::NPH == 2 * NPH4, "variant");
-  // eight helper wavefronts at every K: the 4-bit stream is half as long, so
-  // the codes, not the weights, end the small linears' prologue
-  constexpr int kW4Helpers = 8;
-  constexpr int kW4Up = NPH4 == 1 ? 1 : Var::UP;
-  static_assert(kW4Helpers * 64 * kW4Up * 8 >= Var::KMAX, "helpers cover K");
   extern __shared__ __align__(16) char smem[];
   const Smem L = smem_layout(K, MT, S);
   int8_t* codes = reinterpret_cast<int8_t*>(smem + L.codes);
@@ -648,12 +636,12 @@ __global__ __launch_bounds__(64 * (S + 8)) void w4a8_linear_fused_kernel(
   const int first = b * tq + (int)((unsigned int)(b * tr) / (unsigned int)G);
   const int T = (b + 1) * tq + (int)((unsigned int)((b + 1) * tr) / (unsigned int)G) - first;
   if (wave < S) {
-    streamer_w4<MT, S, NPH4, kW4Helpers>(wq4, wscale, N, K, first, T, wave, lane, codes, Ks, red,
-                                         wsl, ready, wc);
+    streamer_w4<MT, S, NPH4, Var::NH>(wq4, wscale, N, K, first, T, wave, lane, codes, Ks, red,
+                                      wsl, ready, wc);
   } else {
-    helper<MT, S, kW4Helpers, kW4Up, 4>(x, s, M, N, K, first, T, tid - 64 * S, wave - S, lane,
-                                       codes, Ks, red, wsl, amax_part, qp, cnt, ready, y, acc_out,
-                                       AcceptPartials{nullptr, nullptr, nullptr, 0.0f}, G, 0, wc);
+    helper<MT, S, Var::NH, Var::UP, 4>(x, s, M, N, K, first, T, tid - 64 * S, wave - S, lane,
+                                      codes, Ks, red, wsl, amax_part, qp, cnt, ready, y, acc_out,
+                                      AcceptPartials{nullptr, nullptr, nullptr, 0.0f}, G, 0, wc);
   }
 }
 
@@ -698,7 +686,7 @@ hipError_t launch_variant(const FusedPlan& p, const uint16_t* x, const float* s,
   if (attr != hipSuccess) return attr;
   const WaitCtl wc = wait_ctl_for_current_device();
   if (!wc.status) return hipErrorInvalidSymbol;
-  kernel<<<dim3(p.grid), dim3(64 * Var::waves(MT)), p.lds, st>>>(
+  kernel<<<dim3(p.grid), dim3(64 * Var::WAVES), p.lds, st>>>(
       x, s, wq, w_scale, (int)p.M, (int)p.N, (int)p.K, p.tiles / p.grid, p.tiles % p.grid, p.grid,
       y, acc_out, ap, swiglu, wc);
   return hipGetLastError();
@@ -730,8 +718,8 @@ FusedPlan plan_fused(int64_t M, int64_t N, int64_t K) {
   p.nch = (int)((K + 63) / 64);
   p.mt = M <= 2 ? 2 : (M <= 4 ? 4 : (M <= 6 ? 6 : 8));
   p.variant = K <= Variant<0>::KMAX ? 0 : (K <= Variant<1>::KMAX ? 1 : 2);
-  p.waves = p.variant == 0 ? Variant<0>::waves(p.mt)
-                           : (p.variant == 1 ? Variant<1>::waves(p.mt) : Variant<2>::waves(p.mt));
+  p.waves = p.variant == 0 ? Variant<0>::WAVES
+                           : (p.variant == 1 ? Variant<1>::WAVES : Variant<2>::WAVES);
   const int S = p.variant == 2 ? Variant<2>::S : Variant<0>::S;
   p.lds = smem_layout((int)K, p.mt, S).bytes;
   const int cap = kNumCU;  // one persistent workgroup per compute unit
