@@ -62,6 +62,9 @@ RAGGED = [
     # (<= 4096, <= 8192, <= 12288), with ragged N and partial last streamer ranges
     (4, 48, 4096), (8, 300, 4096), (3, 40, 6144), (7, 100, 8000), (8, 64, 10000),
     (4, 520, 12288),
+    # K just past each variant's range start (a last phase nearly all zero
+    # padding) and just past one 2048-wide phase; QKV at 8 token rows
+    (6, 300, 4112), (7, 500, 8208), (2, 1000, 2064), (8, 6144, 4096),
     # many tiles per compute unit: uneven contiguous tile ranges per workgroup
     (6, 9000, 1024), (2, 8336, 80), (8, 12000, 256),
     # 1.5 tiles per workgroup (QKV-like), one more tile for the first
