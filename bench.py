@@ -1310,6 +1310,14 @@ def main():
         if floor:
             for r in shards:
                 r["over_floor"] = round(r["us_per_launch"] / floor, 3)
+        if 96 in windows or args.m == 96:
+            print("[bench] 8-way tensor-parallel shard shapes at M=96", file=sys.stderr, flush=True)
+            out["tp8_shards_m96"] = {
+                "what": "the same shard shapes at M=96 (16 sequences): the wide kernel, whose "
+                        "stream-K ranges split a tile group's K chunks over several workgroups "
+                        "wherever the groups are fewer than the grid (split-K for a small N)",
+                "linears": tp8_shard_shapes(96),
+            }
     if not args.no_cpu_baseline:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_oracle_baseline(args.m, args.cpu_seconds)

@@ -174,7 +174,7 @@ TP8_SHARDS = [("qkv/8", 4096, 768), ("o/8", 512, 4096), ("gate_up/8", 4096, 3072
               ("down/8", 1536, 4096), ("lm_head/8", 4096, 18992)]
 
 
-@pytest.mark.parametrize("M", [1, 6, 8, 48])
+@pytest.mark.parametrize("M", [1, 6, 8, 48, 96])
 @pytest.mark.parametrize("name,K,N", TP8_SHARDS)
 def test_tp8_shard_shapes_every_element(name, K, N, M):
     """The 8-way tensor-parallel shard shapes, every output element (the

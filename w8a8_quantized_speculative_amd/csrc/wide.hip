@@ -668,9 +668,9 @@ __device__ __forceinline__ void wide_epilogue(const float* __restrict__ wscale,
     for (int tt = 0; tt < TG; ++tt)
 #pragma unroll
       for (int k = 0; k < KS; ++k) other[tt][k] = (v4i){0, 0, 0, 0};
-    if (finalizer) {
-      // contributors: the non-empty ranges after r that start inside group g
-      // (each owner wrote its partial sum of g first, then its flag)
+    if (finalizer && TG * KS > 8) {
+      // groups of many tiles and token blocks: the contributors one after the
+      // other (their partial sums fill the registers the streamers leave)
       for (int c = r + 1; c < G && range_start(c, U, G) < (g + 1) * P; ++c) {
         if (range_start(c + 1, U, G) == range_start(c, U, G)) continue;  // empty range
         const int cw = wg_of(c);
@@ -693,6 +693,69 @@ __device__ __forceinline__ void wide_epilogue(const float* __restrict__ wscale,
             if (sidx < MB * 64)
               other[tt][k] += load16<kCoherent>(prs, ((tt * MB + (sidx >> 6)) * 256 + ln * 4) * 4);
           }
+      }
+    } else if (finalizer) {
+      // contributors: the non-empty ranges c_lo .. c_hi - 1 after r that start
+      // inside group g (each owner wrote its partial sum of g first, then its
+      // flag).  Lane j polls contributor c_lo + j, so all flags are waited for
+      // together, and the partial sums are then loaded up to four contributors
+      // at a time (as many as 32 registers hold): a group split over several
+      // workgroups (a small N) pays one hand-off, not one per contributor.
+      constexpr int kBatch = TG * KS <= 2 ? 4 : (TG * KS <= 4 ? 2 : 1);  // <= 32 registers
+      // range c starts before item X = (g + 1) P exactly when c < X G / U
+      const int c_lo = r + 1;
+      const int c_hi =
+          (int)min((int64_t)G, ((int64_t)(g + 1) * P * G + U - 1) / U);
+      const uint32_t target = e + 1u + wc.bias;
+      // one descriptor over every workgroup's partial-sum slot
+      const buffer_rsrc prs =
+          make_rsrc(partials, (uint32_t)kWideMaxGrid * (uint32_t)kPartInts * 4u);
+      for (int c0 = c_lo; c0 < c_hi; c0 += 64) {
+        const int nc = min(64, c_hi - c0);
+        // an empty range writes no partial sums.  Ranges are empty only when
+        // U < G (then (c + 1) U <= 256 * 256 fits 32 bits): range c is not
+        // empty exactly when a multiple of G lies in (c U, (c + 1) U].
+        const int c = c0 + lane;
+        const bool mine = lane < nc && (U >= G || (unsigned)((c + 1) * U) % (unsigned)G <
+                                                      (unsigned)U);
+        const uint64_t live = __builtin_amdgcn_ballot_w64(mine);
+        bool ok = false;
+        for (int spin = 0;; ++spin) {
+          const bool ready = !mine || load_flag(flag_word(flags, 1, wg_of(c))) == target;
+          if (__builtin_amdgcn_ballot_w64(!ready) == 0) {
+            ok = true;
+            break;
+          }
+          if (spin >= wc.spin_global) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        if (!ok && lane == 0) note_expired(wc, kWaitPartials);
+        after_poll();  // the partial sums are read after the flags, agent-scope
+        for (int j0 = 0; j0 < nc; j0 += kBatch) {
+          v4i part[kBatch][TG][KS];
+#pragma unroll
+          for (int j = 0; j < kBatch; ++j) {
+            // an empty range or one past the group reads zeros
+            const bool lv = j0 + j < nc && ((live >> (j0 + j)) & 1u);
+            const int base = (lv ? wg_of(c0 + j0 + j) : 0) * kPartInts;
+#pragma unroll
+            for (int tt = 0; tt < TG; ++tt)
+#pragma unroll
+              for (int k = 0; k < KS; ++k) {
+                const int sidx = et + 256 * k;
+                part[j][tt][k] = load16<kCoherent>(
+                    prs, lv && sidx < MB * 64
+                             ? (base + (tt * MB + (sidx >> 6)) * 256 + ln * 4) * 4
+                             : kOutOfRange);
+              }
+          }
+#pragma unroll
+          for (int j = 0; j < kBatch; ++j)
+#pragma unroll
+            for (int tt = 0; tt < TG; ++tt)
+#pragma unroll
+              for (int k = 0; k < KS; ++k) other[tt][k] += part[j][tt][k];
+        }
       }
     }
 #pragma unroll
