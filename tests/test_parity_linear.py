@@ -81,6 +81,10 @@ RAGGED = [
     (96, 520, 12288), (128, 300, 12288),
     # K beyond the one-launch small-window kernel, up to the largest supported K
     (6, 64, 16384), (1, 40, 65536), (50, 48, 20480),
+    # a tile group's K over many workgroups, all their flags waited for at once:
+    # fewer items than workgroups (empty ranges, 63 contributors), more than 64
+    # contributors (two rounds of lanes), 96 and 33 tokens
+    (16, 16, 16384), (20, 48, 20480), (96, 64, 4096), (33, 100, 8192),
     # 4 to 5 tiles per workgroup: groups of 4 tiles split across workgroups
     (20, 16400, 320), (100, 16384, 1040), (128, 16500, 2112), (9, 16390, 4160),
     (70, 20000, 576),
