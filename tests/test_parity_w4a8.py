@@ -66,6 +66,9 @@ SHAPES = [
     # groups of 6 tiles (3 to 5 token blocks): one per workgroup and split
     (48, 20000, 512), (80, 17000, 1152), (40, 30000, 256), (16, 17000, 512), (30, 20000, 1152),
     (96, 24576, 1024),
+    # a tile group's K over many workgroups: empty ranges and 63 contributors,
+    # more than 64 contributors, 96 tokens
+    (16, 16, 16384), (20, 48, 20480), (96, 64, 4096),
 ]
 
 
