@@ -332,7 +332,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, bench_json: str, out_json: str
                    f"{r['traffic_over_algorithmic']:.4f} |")
     out += ["", "Every kernel of the run (scaled the same way, bytes per dispatch):", "",
             "| kernel | dispatches | FETCH | WRITE |", "|---|---:|---:|---:|"]
-    for name in sorted(set(fetch) & set(write), key=lambda n: -fetch[n][0] * fetch[n][1])[:16]:
+    for name in sorted(set(fetch) & set(write), key=lambda n: -fetch[n][0] * fetch[n][1]):
         out.append(f"| `{_cell(name)}` | {fetch[name][1]} | {fetch[name][0] * f_scale:.0f} | "
                    f"{write[name][0] * w_scale:.0f} |")
     out.append("")
